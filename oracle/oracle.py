@@ -1,0 +1,231 @@
+"""CPU oracle for causal multi-head / grouped-query attention with a per-head
+QK-RMSNorm + rotate_half RoPE prologue, forward and backward.
+
+TEST INFRASTRUCTURE.  Only tests/, the package's smoke() check and the
+benchmark's CPU-baseline leg may import or run this module; the HIP library and
+its Python binding never do, and this module imports nothing from them.
+
+Everything is computed in float64 with numpy.  Each function is the plain
+definition written out, one (batch, head) at a time, with the full S x S score
+matrix materialised; there is no tiling, no online softmax and no fusion.
+
+Sources (titles of the pages and the section each function follows):
+  * "Phase T9: Export to xserv", conventions table and Decision 1: RMSNorm
+    x*rsqrt(mean(x^2)+eps)*gamma with no mean subtraction; QK-norm is a per-head
+    RMSNorm over each [head_dim] vector, one gamma[head_dim] for all Q heads and
+    one for all K heads, applied after the head reshape and before RoPE;
+    rotate_half RoPE with frequency theta^(-2i/hd) and position = token index;
+    scale 1/sqrt(head_dim); causal mask.
+  * Mint documentation (morn.ink), section 5.3.1 (score, causal mask, stable
+    softmax, weighted sum), 5.4.1-5.4.4 (rotation of pairs (i, i+hd/2), angle
+    t*base^(-2i/dk), Q and K rotated but not V, backward = rotation by the
+    negative angle, positions restart at 0 per sequence), 5.5.1-5.5.2 (RMSNorm
+    forward and its backward: dot = sum g*dy*x, dx = g*dy/rms - x*dot/(d*rms^3),
+    dg accumulated across rows).
+  * "Phase T15: GQA", "what is GQA" and Decision 2: query head qh reads KV head
+    qh // group with groups contiguous; the K/V gradient of a shared head is the
+    sum over r < group of the gradients of query heads kvh*group + r.
+  * "Phase T12: bf16 mixed precision", precision table: softmax, RoPE and norm in
+    fp32 on the device; the oracle uses float64 throughout.
+
+Readings where the pages leave a step open (listed with the design notes):
+  * masking: the pages use an additive -1e9 / -1e38 or a causal flag; all three
+    exclude j > i exactly under a finite-input causal square attention, so the
+    oracle excludes those entries exactly (they contribute exp(.) = 0);
+  * lse (the forward's second output) is the natural-log logsumexp of the scaled,
+    masked scores of each query row;
+  * the attention backward is not written on the pages; it is the chain rule of
+    the forward (dP = dO V^T, D = rowsum(P * dP), dS = P * (dP - D),
+    dQ = dS K / sqrt(hd), dK = dS^T Q / sqrt(hd), dV = P^T dO), pinned by
+    finite differences in the tests;
+  * the group sum of K/V gradients runs over r in ascending order.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# RoPE (Mint docs 5.4.1 / 5.4.2; Phase T9 conventions table)
+# --------------------------------------------------------------------------
+def rope_tables(seq_len: int, head_dim: int, theta: float, pos_offset: int = 0):
+    """cos/sin of the rotation angle t * theta^(-2i/hd), t = pos_offset + s for
+    s in [0, seq_len), i in [0, hd/2).  Returns two [seq_len, hd/2] float64 arrays."""
+    if head_dim % 2:
+        raise ValueError("head_dim must be even")
+    half = head_dim // 2
+    i = np.arange(half, dtype=np.float64)
+    inv_freq = np.power(np.float64(theta), -2.0 * i / head_dim)
+    t = np.arange(seq_len, dtype=np.float64) + pos_offset
+    angle = t[:, None] * inv_freq[None, :]
+    return np.cos(angle), np.sin(angle)
+
+
+def rope_apply(n, cos, sin):
+    """rotate_half: pair (i, i + hd/2) rotated by the angle of (position, i).
+    n: [..., S, hd]; cos/sin: [S, hd/2]."""
+    n = _f64(n)
+    half = n.shape[-1] // 2
+    x, y = n[..., :half], n[..., half:]
+    return np.concatenate([x * cos - y * sin, x * sin + y * cos], axis=-1)
+
+
+def rope_apply_inverse(dy, cos, sin):
+    """Rotation by the negative angle (the transpose of the rotation): this is the
+    RoPE backward of Mint docs 5.4.4."""
+    dy = _f64(dy)
+    half = dy.shape[-1] // 2
+    a, b = dy[..., :half], dy[..., half:]
+    return np.concatenate([a * cos + b * sin, -a * sin + b * cos], axis=-1)
+
+
+# --------------------------------------------------------------------------
+# QK-norm = RMSNorm over each head vector (Mint docs 5.5.1, Phase T9 Decision 1)
+# --------------------------------------------------------------------------
+def qk_rmsnorm(x, gamma, eps: float):
+    """n = x * gamma / rms with rms = sqrt(mean(x^2) + eps).  Returns (n, rstd)
+    where rstd = 1/rms has the shape of x without its last axis."""
+    x = _f64(x)
+    gamma = _f64(gamma)
+    d = x.shape[-1]
+    ms = np.sum(x * x, axis=-1) / d
+    rstd = 1.0 / np.sqrt(ms + eps)
+    return x * rstd[..., None] * gamma, rstd
+
+
+def qk_rmsnorm_bwd(dn, x, gamma, rstd):
+    """Mint docs 5.5.2, per row: dot = sum_j g_j dy_j x_j;
+    dx_j = g_j dy_j / rms - x_j dot / (d rms^3); dg_j = sum over rows of dy_j x_j / rms.
+    Returns (dx, dgamma)."""
+    dn, x, gamma, rstd = _f64(dn), _f64(x), _f64(gamma), _f64(rstd)
+    d = x.shape[-1]
+    r = rstd[..., None]
+    dot = np.sum(gamma * dn * x, axis=-1, keepdims=True)
+    dx = gamma * dn * r - x * dot * r ** 3 / d
+    dgamma = np.sum((dn * x * r).reshape(-1, d), axis=0)
+    return dx, dgamma
+
+
+def qknorm_rope_fwd(x, gamma, eps: float, theta: float, pos_offset: int = 0):
+    """Prologue forward on a [rows, S, hd] tensor: y = RoPE(QKnorm(x)).
+    Returns (y, rstd[rows, S])."""
+    x = _f64(x)
+    _, S, hd = x.shape
+    cos, sin = rope_tables(S, hd, theta, pos_offset)
+    n, rstd = qk_rmsnorm(x, gamma, eps)
+    return rope_apply(n, cos, sin), rstd
+
+
+def qknorm_rope_bwd(dy, x, gamma, rstd, theta: float, pos_offset: int = 0):
+    """Prologue backward: dn = RoPE^-1(dy), then the RMSNorm backward.
+    Returns (dx, dgamma)."""
+    x = _f64(x)
+    _, S, hd = x.shape
+    cos, sin = rope_tables(S, hd, theta, pos_offset)
+    dn = rope_apply_inverse(dy, cos, sin)
+    return qk_rmsnorm_bwd(dn, x, gamma, rstd)
+
+
+# --------------------------------------------------------------------------
+# Causal GQA attention (Mint docs 5.3.1; Phase T15 head mapping)
+# --------------------------------------------------------------------------
+def _kv_index(bh: int, num_heads: int, num_kv_heads: int) -> int:
+    b, qh = divmod(bh, num_heads)
+    group = num_heads // num_kv_heads
+    return b * num_kv_heads + qh // group
+
+
+def _probs(qrow, krows, scale):
+    """Scores s_ij = q_i.k_j * scale for j <= i, the rest excluded; returns
+    (P, lse) with P the causal softmax (float64)."""
+    S = qrow.shape[0]
+    s = (qrow @ krows.T) * scale
+    keep = np.tril(np.ones((S, S), dtype=bool))
+    s = np.where(keep, s, -np.inf)
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.where(keep, np.exp(s - m), 0.0)
+    l = np.sum(e, axis=1, keepdims=True)
+    return e / l, (m + np.log(l))[:, 0]
+
+
+def _check_heads(num_heads, num_kv_heads):
+    if num_kv_heads <= 0 or num_heads % num_kv_heads:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+
+
+def attention_fwd(q, k, v, num_heads: int, num_kv_heads: int, heads=None):
+    """q: [B*H, S, hd]; k, v: [B*Hkv, S, hd].  Returns (out [B*H,S,hd], lse [B*H,S]).
+    `heads` optionally restricts the computation to a list of B*H row indices
+    (the others stay zero)."""
+    _check_heads(num_heads, num_kv_heads)
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    BH, S, hd = q.shape
+    scale = 1.0 / np.sqrt(hd)
+    out = np.zeros((BH, S, hd))
+    lse = np.zeros((BH, S))
+    for bh in (range(BH) if heads is None else heads):
+        kv = _kv_index(bh, num_heads, num_kv_heads)
+        p, lse[bh] = _probs(q[bh], k[kv], scale)
+        out[bh] = p @ v[kv]
+    return out, lse
+
+
+def attention_bwd(q, k, v, dout, num_heads: int, num_kv_heads: int, kv_heads=None):
+    """Chain rule of attention_fwd.  Returns (dq, dk, dv) w.r.t. the q, k, v that
+    attention_fwd consumed.  For each KV head the gradients of its `group` query
+    heads are summed in ascending r.  `kv_heads` optionally restricts the work to a
+    list of B*Hkv indices (and their query heads)."""
+    _check_heads(num_heads, num_kv_heads)
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    BH, S, hd = q.shape
+    BKV = k.shape[0]
+    group = num_heads // num_kv_heads
+    scale = 1.0 / np.sqrt(hd)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for kv in (range(BKV) if kv_heads is None else kv_heads):
+        b, kvh = divmod(kv, num_kv_heads)
+        dk_sum = np.zeros((S, hd))
+        dv_sum = np.zeros((S, hd))
+        for r in range(group):
+            bh = b * num_heads + kvh * group + r
+            p, _ = _probs(q[bh], k[kv], scale)
+            dp = dout[bh] @ v[kv].T                        # dP_ij = dO_i . v_j
+            D = np.sum(p * dp, axis=1, keepdims=True)      # D_i = sum_j p_ij dP_ij
+            ds = p * (dp - D)                              # dS_ij = p_ij (dP_ij - D_i)
+            dq[bh] = (ds @ k[kv]) * scale
+            dk_sum = dk_sum + (ds.T @ q[bh]) * scale
+            dv_sum = dv_sum + p.T @ dout[bh]
+        dk[kv] = dk_sum
+        dv[kv] = dv_sum
+    return dq, dk, dv
+
+
+# --------------------------------------------------------------------------
+# Whole path: prologue on Q and K, then attention
+# --------------------------------------------------------------------------
+def forward(xq, xk, v, gamma_q, gamma_k, num_heads, num_kv_heads, eps, theta,
+            heads=None, pos_offset: int = 0):
+    """Returns a dict with yq, rstd_q, yk, rstd_k, out, lse."""
+    yq, rq = qknorm_rope_fwd(xq, gamma_q, eps, theta, pos_offset)
+    yk, rk = qknorm_rope_fwd(xk, gamma_k, eps, theta, pos_offset)
+    out, lse = attention_fwd(yq, yk, v, num_heads, num_kv_heads, heads)
+    return dict(yq=yq, rstd_q=rq, yk=yk, rstd_k=rk, out=out, lse=lse)
+
+
+def backward(xq, xk, v, gamma_q, gamma_k, dout, num_heads, num_kv_heads, eps, theta,
+             kv_heads=None, pos_offset: int = 0):
+    """Gradients of sum(dout * out) w.r.t. the raw inputs.  Returns a dict with
+    dyq, dyk (w.r.t. the post-RoPE q, k), dxq, dxk, dv, dgamma_q, dgamma_k."""
+    f = forward(xq, xk, v, gamma_q, gamma_k, num_heads, num_kv_heads, eps, theta,
+                heads=[], pos_offset=pos_offset)
+    dyq, dyk, dv = attention_bwd(f["yq"], f["yk"], v, dout, num_heads, num_kv_heads,
+                                 kv_heads)
+    dxq, dgq = qknorm_rope_bwd(dyq, xq, gamma_q, f["rstd_q"], theta, pos_offset)
+    dxk, dgk = qknorm_rope_bwd(dyk, xk, gamma_k, f["rstd_k"], theta, pos_offset)
+    return dict(dyq=dyq, dyk=dyk, dxq=dxq, dxk=dxk, dv=dv, dgamma_q=dgq, dgamma_k=dgk)
