@@ -1,0 +1,279 @@
+"""Python binding of libxattn: causal GQA attention with a QK-norm + RoPE prologue on
+MI355X (gfx950).
+
+This module only marshals arguments: it checks tensor placement, dtype and shape,
+allocates outputs and workspaces with torch (device memory and streams are all torch is
+used for) and calls the C ABI declared in include/xattn.h.  Every computation runs in
+the HIP kernels of libxattn.so; there is no fallback path.  If the library has not been
+built, every call raises.
+
+The functions named xattn_* mirror the C entry points one to one (same argument order,
+torch tensors in place of device pointers).  The short helpers below them (rope_cache,
+qknorm_rope_fwd, ...) allocate the outputs and call those.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "XattnError", "library_path", "load_library",
+    "xattn_rope_cache", "xattn_qknorm_rope_fwd", "xattn_qknorm_rope_bwd_workspace_bytes",
+    "xattn_qknorm_rope_bwd", "xattn_fwd", "xattn_bwd_workspace_bytes", "xattn_bwd",
+    "xattn_status_string", "xattn_last_error", "xattn_version",
+    "rope_cache", "qknorm_rope_fwd", "qknorm_rope_bwd", "attn_fwd", "attn_bwd",
+]
+
+XATTN_F32 = 0
+XATTN_BF16 = 1
+_DTYPES = {torch.float32: XATTN_F32, torch.bfloat16: XATTN_BF16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class XattnError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({detail})")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64),
+                ("num_heads", ctypes.c_int64), ("num_kv_heads", ctypes.c_int64),
+                ("head_dim", ctypes.c_int64), ("dtype", ctypes.c_int32)]
+
+
+class Prologue(ctypes.Structure):
+    _fields_ = [("xq", ctypes.c_void_p), ("xk", ctypes.c_void_p),
+                ("gamma_q", ctypes.c_void_p), ("gamma_k", ctypes.c_void_p),
+                ("rstd_q", ctypes.c_void_p), ("rstd_k", ctypes.c_void_p),
+                ("cos_tab", ctypes.c_void_p), ("sin_tab", ctypes.c_void_p),
+                ("dgamma_q", ctypes.c_void_p), ("dgamma_k", ctypes.c_void_p)]
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libxattn.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libxattn.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m causal_gqa_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    sigs = {
+        "xattn_rope_cache": (i32, [vp, vp, i64, i64, ctypes.c_double, vp]),
+        "xattn_qknorm_rope_fwd": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_float,
+                                        i32, vp]),
+        "xattn_qknorm_rope_bwd_workspace_bytes": (sz, [i64, i64, i64]),
+        "xattn_qknorm_rope_bwd": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64,
+                                        i32, vp]),
+        "xattn_fwd": (i32, [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp]),
+        "xattn_bwd_workspace_bytes": (sz, [ctypes.POINTER(Dims), ctypes.c_int]),
+        "xattn_bwd": (i32, [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                            ctypes.POINTER(Prologue), vp, sz, vp]),
+        "xattn_status_string": (ctypes.c_char_p, [i32]),
+        "xattn_last_error": (ctypes.c_char_p, []),
+        "xattn_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+# ----------------------------------------------------------------------------------------
+# marshalling helpers
+# ----------------------------------------------------------------------------------------
+def _ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _io(t, name):
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"{name} must be float32 or bfloat16, got {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status, where):
+    if status != 0:
+        lib = load_library()
+        detail = lib.xattn_last_error().decode() or lib.xattn_status_string(status).decode()
+        raise XattnError(status, where, detail)
+
+
+# ----------------------------------------------------------------------------------------
+# one-to-one wrappers of the C entry points
+# ----------------------------------------------------------------------------------------
+def xattn_version() -> str:
+    return load_library().xattn_version().decode()
+
+
+def xattn_status_string(status: int) -> str:
+    return load_library().xattn_status_string(status).decode()
+
+
+def xattn_last_error() -> str:
+    return load_library().xattn_last_error().decode()
+
+
+def xattn_rope_cache(cos_tab, sin_tab, seq_len, head_dim, theta, stream=None):
+    _check(load_library().xattn_rope_cache(
+        _ptr(cos_tab, "cos_tab", torch.float32), _ptr(sin_tab, "sin_tab", torch.float32),
+        seq_len, head_dim, float(theta), _stream(stream)), "xattn_rope_cache")
+
+
+def xattn_qknorm_rope_fwd(x, gamma, cos_tab, sin_tab, y, rstd, rows, seq_len, head_dim, eps,
+                          stream=None):
+    _check(load_library().xattn_qknorm_rope_fwd(
+        _ptr(x, "x"), _ptr(gamma, "gamma", torch.float32), _ptr(cos_tab, "cos_tab", torch.float32),
+        _ptr(sin_tab, "sin_tab", torch.float32), _ptr(y, "y", x.dtype),
+        _ptr(rstd, "rstd", torch.float32), rows, seq_len, head_dim, float(eps), _io(x, "x"),
+        _stream(stream)), "xattn_qknorm_rope_fwd")
+
+
+def xattn_qknorm_rope_bwd_workspace_bytes(rows, seq_len, head_dim) -> int:
+    return int(load_library().xattn_qknorm_rope_bwd_workspace_bytes(rows, seq_len, head_dim))
+
+
+def xattn_qknorm_rope_bwd(dy, x, gamma, rstd, cos_tab, sin_tab, dx, dgamma, workspace, rows,
+                          seq_len, head_dim, stream=None):
+    _check(load_library().xattn_qknorm_rope_bwd(
+        _ptr(dy, "dy", x.dtype), _ptr(x, "x"), _ptr(gamma, "gamma", torch.float32),
+        _ptr(rstd, "rstd", torch.float32), _ptr(cos_tab, "cos_tab", torch.float32),
+        _ptr(sin_tab, "sin_tab", torch.float32), _ptr(dx, "dx", x.dtype),
+        _ptr(dgamma, "dgamma", torch.float32), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), rows, seq_len, head_dim, _io(x, "x"),
+        _stream(stream)), "xattn_qknorm_rope_bwd")
+
+
+def make_dims(q, num_heads, num_kv_heads) -> Dims:
+    bh, S, hd = q.shape
+    if bh % num_heads:
+        raise ValueError("q.shape[0] must be batch * num_heads")
+    return Dims(bh // num_heads, S, num_heads, num_kv_heads, hd, _io(q, "q"))
+
+
+def xattn_fwd(dims: Dims, q, k, v, out, lse, stream=None):
+    _check(load_library().xattn_fwd(
+        ctypes.byref(dims), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype),
+        _ptr(out, "out", q.dtype), _ptr(lse, "lse", torch.float32), _stream(stream)),
+        "xattn_fwd")
+
+
+def xattn_bwd_workspace_bytes(dims: Dims, with_prologue: bool) -> int:
+    return int(load_library().xattn_bwd_workspace_bytes(ctypes.byref(dims), int(with_prologue)))
+
+
+def xattn_bwd(dims: Dims, q, k, v, out, lse, dout, dq, dk, dv, prologue, workspace,
+              stream=None):
+    """prologue: None or a dict with xq, xk, gamma_q, gamma_k, rstd_q, rstd_k, cos_tab,
+    sin_tab, dgamma_q, dgamma_k tensors."""
+    pro = None
+    if prologue is not None:
+        p = prologue
+        pro = Prologue(_ptr(p["xq"], "xq", q.dtype), _ptr(p["xk"], "xk", q.dtype),
+                       _ptr(p["gamma_q"], "gamma_q", torch.float32),
+                       _ptr(p["gamma_k"], "gamma_k", torch.float32),
+                       _ptr(p["rstd_q"], "rstd_q", torch.float32),
+                       _ptr(p["rstd_k"], "rstd_k", torch.float32),
+                       _ptr(p["cos_tab"], "cos_tab", torch.float32),
+                       _ptr(p["sin_tab"], "sin_tab", torch.float32),
+                       _ptr(p["dgamma_q"], "dgamma_q", torch.float32),
+                       _ptr(p["dgamma_k"], "dgamma_k", torch.float32))
+    _check(load_library().xattn_bwd(
+        ctypes.byref(dims), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype),
+        _ptr(out, "out", q.dtype), _ptr(lse, "lse", torch.float32),
+        _ptr(dout, "dout", q.dtype), _ptr(dq, "dq", q.dtype), _ptr(dk, "dk", q.dtype),
+        _ptr(dv, "dv", q.dtype), ctypes.byref(pro) if pro is not None else None,
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "xattn_bwd")
+
+
+# ----------------------------------------------------------------------------------------
+# allocating helpers
+# ----------------------------------------------------------------------------------------
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def rope_cache(seq_len, head_dim, theta, device="cuda", stream=None):
+    cos_tab = torch.empty(seq_len, head_dim // 2, dtype=torch.float32, device=device)
+    sin_tab = torch.empty_like(cos_tab)
+    xattn_rope_cache(cos_tab, sin_tab, seq_len, head_dim, theta, stream)
+    return cos_tab, sin_tab
+
+
+def qknorm_rope_fwd(x, gamma, cos_tab, sin_tab, eps, stream=None):
+    rows, S, hd = x.shape
+    y = torch.empty_like(x)
+    rstd = torch.empty(rows * S, dtype=torch.float32, device=x.device)
+    xattn_qknorm_rope_fwd(x, gamma, cos_tab, sin_tab, y, rstd, rows, S, hd, eps, stream)
+    return y, rstd
+
+
+def qknorm_rope_bwd(dy, x, gamma, rstd, cos_tab, sin_tab, stream=None, workspace=None):
+    rows, S, hd = x.shape
+    dx = torch.empty_like(x)
+    dgamma = torch.empty(hd, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = _workspace(xattn_qknorm_rope_bwd_workspace_bytes(rows, S, hd), x.device)
+    xattn_qknorm_rope_bwd(dy, x, gamma, rstd, cos_tab, sin_tab, dx, dgamma, workspace, rows, S,
+                          hd, stream)
+    return dx, dgamma
+
+
+def attn_fwd(q, k, v, num_heads, num_kv_heads, stream=None):
+    dims = make_dims(q, num_heads, num_kv_heads)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[0] * q.shape[1], dtype=torch.float32, device=q.device)
+    xattn_fwd(dims, q, k, v, out, lse, stream)
+    return out, lse
+
+
+def attn_bwd(q, k, v, out, lse, dout, num_heads, num_kv_heads, prologue=None, stream=None,
+             workspace=None):
+    """Returns (dq, dk, dv); with a prologue dict (see xattn_bwd, without the dgamma
+    entries) returns (dxq, dxk, dv, dgamma_q, dgamma_k)."""
+    dims = make_dims(q, num_heads, num_kv_heads)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    pro = None
+    if prologue is not None:
+        hd = q.shape[-1]
+        pro = dict(prologue)
+        pro["dgamma_q"] = torch.empty(hd, dtype=torch.float32, device=q.device)
+        pro["dgamma_k"] = torch.empty(hd, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = _workspace(xattn_bwd_workspace_bytes(dims, pro is not None), q.device)
+    xattn_bwd(dims, q, k, v, out, lse, dout, dq, dk, dv, pro, workspace, stream)
+    if pro is None:
+        return dq, dk, dv
+    return dq, dk, dv, pro["dgamma_q"], pro["dgamma_k"]

@@ -1,0 +1,546 @@
+// Causal GQA attention, forward and backward, on gfx950 MFMA.
+//
+// What is computed (Mint documentation 5.3.1; xtrain "Phase T9: Export to xserv"
+// conventions table; xtrain "Phase T15: GQA"):
+//   s_ij = q_i . k_j / sqrt(hd) for j <= i (later keys excluded), p = softmax_j(s) in fp32,
+//   out_i = sum_j p_ij v_j, lse_i = ln sum_j exp(s_ij); query head qh of batch b reads KV
+//   head b*Hkv + qh/group.  The backward is the chain rule with D_i = dO_i . out_i:
+//   dS = P (dP - D), dq = dS K / sqrt(hd), dk = sum_r dS^T Q / sqrt(hd), dv = sum_r P^T dO,
+//   where r runs over the group's query heads; each dk/dv tile has exactly one owning
+//   workgroup that sums the group in ascending r with no atomics.
+//
+// Design (MI355X-first, not a translation of the pages' CUDA kernels):
+//   * Tiles of 32 x 32 on v_mfma_f32_32x32x16_bf16 (fp32 io: v_mfma_f32_32x32x2_f32).
+//     A wave owns 32 rows of the "resident" side (queries in the forward and dq kernels,
+//     keys in the dk/dv kernel); its operand fragments stay in registers for the whole
+//     kernel, while the streamed side goes HBM -> LDS in 16-byte coalesced chunks.
+//   * Products are arranged so the score tile comes out with the resident index on the
+//     lane (column) axis: per-row softmax statistics are then per-lane scalars, the row
+//     max needs a single cross-half exchange, and the probability tile can be fed back to
+//     the next MFMA straight from the accumulator registers.
+//   * The operand that must be contracted over the streamed index (V in P.V, K in dS.K,
+//     Q and dO in the dk/dv products) is read from the row-major LDS tile with gfx950's
+//     transposing LDS read, so no transposed copy is ever stored.
+//   * Online softmax in the exp2 domain with log2(e)/sqrt(hd) folded into one multiply.
+//   * Work order: the heaviest causal tiles are dispatched first.
+#include <type_traits>
+
+#include "xattn_device.h"
+#include "xattn_internal.h"
+
+namespace xattn {
+
+template <typename T, int HD>
+struct Tile {
+  static constexpr int VEC = V16<T>::n;            // elements per 16-byte chunk
+  static constexpr int HDP = HD < 32 ? 32 : HD;    // LDS row length, padded to one MFMA tile
+  static constexpr int LDS_ROW = HDP + VEC;        // +16 bytes per row against bank conflicts
+  static constexpr int NCH = HD / (2 * VEC);       // 16-byte chunks per lane in a hd-contraction
+  static constexpr int NDT = HDP / 32;             // 32-row MFMA tiles along hd
+  static constexpr int CPR = HDP / VEC;            // 16-byte chunks per padded row
+  static constexpr bool kBf16 = std::is_same<T, bf16>::value;
+};
+
+__device__ __forceinline__ bf16x8 pack8_bf16(const float* p) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (bf16)p[j];
+  return r;
+}
+
+// A operand of a product contracted over the streamed (row) index of an LDS tile:
+// rows kb..kb+3 and kb+8..kb+11 (kb = row0 + 16*c2 + 4*h), column d = col0 + c32, as the
+// eight k-slots of this lane.  Matches the accumulator rows 8*(i/4) + 4*h + (i%4) for
+// i in [8*c2, 8*c2 + 8), i.e. the probabilities this lane packs for the same MFMA.
+template <int LDS_ROW>
+__device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int row0, int c2, int col0,
+                                             int lane) {
+  const int g = lane >> 4, li = lane & 15, h = lane >> 5;
+  const int row = row0 + 16 * c2 + 4 * h + (li >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (li & 3);
+  const bf16x4 lo = lds_read_tr16(tile + row * LDS_ROW + col);
+  const bf16x4 hi = lds_read_tr16(tile + (row + 8) * LDS_ROW + col);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// acc[dt] += (tile rows row0..row0+31, transposed) x (probability-like values in the
+// accumulator layout of the 32x32 score tile).
+template <typename T, int HD, int NDT>
+__device__ __forceinline__ void accumulate_transposed(f32x16 (&acc)[NDT], const T* tile,
+                                                      int row0, const float (&pv)[16],
+                                                      int lane) {
+  using C = Tile<T, HD>;
+  static_assert(NDT == C::NDT, "accumulator tiles must cover the padded head dim");
+  if constexpr (C::kBf16) {
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const bf16x8 b = pack8_bf16(pv + 8 * c2);
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) {
+        const bf16x8 a = tr_operand<C::LDS_ROW>(tile, row0, c2, 32 * dt, lane);
+        acc[dt] = mfma_bf16(a, b, acc[dt]);
+      }
+    }
+  } else {
+    const int c32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int r = row0 + 8 * (t >> 2) + 4 * h + (t & 3);
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+        acc[dt] = mfma_f32(tile[r * C::LDS_ROW + 32 * dt + c32], pv[t], acc[dt]);
+    }
+  }
+}
+
+// Score-like tile: sum over hd of tile[row0 + c32][:] (A, from LDS) with the lane's
+// register fragment (B).
+template <typename T, int HD, int NCH>
+__device__ __forceinline__ f32x16 contract_hd(const T* tile, int row0,
+                                              const vec16_t<T> (&frag)[NCH], int lane) {
+  using C = Tile<T, HD>;
+  static_assert(NCH == C::NCH, "fragment must cover head_dim");
+  const int c32 = lane & 31, h = lane >> 5;
+  f32x16 acc = zero16();
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c) {
+    const vec16_t<T> a = load16(tile + (row0 + c32) * C::LDS_ROW + 2 * C::VEC * c + C::VEC * h);
+    acc = mfma_chunk(a, frag[c], acc);
+  }
+  return acc;
+}
+
+// Lane's register fragment of row `row` of a [S, HD] matrix (zero past the end).
+template <typename T, int HD, int NCH>
+__device__ __forceinline__ void load_fragment(vec16_t<T> (&frag)[NCH], const T* base, int row,
+                                              int S, int h) {
+  using C = Tile<T, HD>;
+  static_assert(NCH == C::NCH, "fragment must cover head_dim");
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c)
+    frag[c] = row < S ? load16(base + (size_t)row * HD + 2 * C::VEC * c + C::VEC * h)
+                      : vzero<T>();
+}
+
+// Copy rows r0..r0+nrows-1 of a [S, HD] matrix into a zero-padded LDS tile, using
+// `nthr` threads starting at thread index `t`.
+template <typename T, int HD>
+__device__ __forceinline__ void stage_rows(T* tile, const T* src, int r0, int nrows, int S,
+                                           int t, int nthr) {
+  using C = Tile<T, HD>;
+  for (int idx = t; idx < nrows * C::CPR; idx += nthr) {
+    const int r = idx / C::CPR, cc = (idx % C::CPR) * C::VEC;
+    const int gr = r0 + r;
+    vec16_t<T> x = vzero<T>();
+    if (gr < S && cc < HD) x = load16(src + (size_t)gr * HD + cc);
+    store16(tile + r * C::LDS_ROW + cc, x);
+  }
+}
+
+// Store the lane's column of a 32-row-tiled [HD] accumulator (rows d = 32*dt + 8*g + 4*h
+// + 0..3) as row `row` of an [S, HD] output, times `mul`.
+template <typename TO, int HD, int NDT>
+__device__ __forceinline__ void store_column(TO* dst, const f32x16 (&acc)[NDT], float mul,
+                                             int h) {
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * dt + 8 * g + 4 * h;
+      if (d < HD) {
+        if constexpr (std::is_same<TO, float>::value) {
+          f32x4 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = acc[dt][4 * g + j] * mul;
+          *reinterpret_cast<f32x4*>(dst + d) = o;
+        } else {
+          bf16x4 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = (bf16)(acc[dt][4 * g + j] * mul);
+          *reinterpret_cast<bf16x4*>(dst + d) = o;
+        }
+      }
+    }
+  }
+}
+
+constexpr int kWaves = 4;
+constexpr int kBlockM = 32 * kWaves;  // queries per forward / dq workgroup
+constexpr int kBlockN = 64;           // keys per LDS stage in forward / dq
+
+// --------------------------------------------------------------------------------------
+// forward: one workgroup per (batch*head, 128-query tile); 4 waves x 32 queries.
+// --------------------------------------------------------------------------------------
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ q,
+                                                       const T* __restrict__ k,
+                                                       const T* __restrict__ v,
+                                                       T* __restrict__ out,
+                                                       float* __restrict__ lse, int S, int H,
+                                                       int Hkv, float scale_log2) {
+  using C = Tile<T, HD>;
+  __shared__ __attribute__((aligned(16))) T ks[kBlockN * C::LDS_ROW];
+  __shared__ __attribute__((aligned(16))) T vs[kBlockN * C::LDS_ROW];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
+  const int bh = blockIdx.x;
+  const int qt = gridDim.y - 1 - blockIdx.y;  // heaviest query tiles first
+  const int b = bh / H, qh = bh - b * H;
+  const int kvbh = b * Hkv + qh / (H / Hkv);
+  const T* qp = q + (size_t)bh * S * HD;
+  const T* kp = k + (size_t)kvbh * S * HD;
+  const T* vp = v + (size_t)kvbh * S * HD;
+  const int q0 = qt * kBlockM;
+  const int qw0 = q0 + 32 * w;
+  const int qrow = qw0 + c32;
+
+  vec16_t<T> qf[C::NCH];
+  load_fragment<T, HD>(qf, qp, qrow, S, h);
+  f32x16 o[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) o[dt] = zero16();
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kend = min(S, q0 + kBlockM);
+  const int ntiles = (kend + kBlockN - 1) / kBlockN;
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int k0 = kt * kBlockN;
+    __syncthreads();
+    stage_rows<T, HD>(ks, kp, k0, kBlockN, S, tid, 256);
+    stage_rows<T, HD>(vs, vp, k0, kBlockN, S, tid, 256);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kBlockN / 32; ++s) {
+      const int kb = k0 + 32 * s;
+      if (kb > qw0 + 31 || kb >= S) break;  // wave-uniform: keys all in the future / past end
+      f32x16 st = contract_hd<T, HD>(ks, 32 * s, qf, lane);
+      const bool edge = (kb + 31 > qw0) || (kb + 31 >= S);
+      float sv[16];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = st[i] * scale_log2;
+        if (edge) {
+          const int key = kb + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (key > qrow || key >= S) x = -INFINITY;
+        }
+        sv[i] = x;
+        tmax = fmaxf(tmax, x);
+      }
+      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = fast_exp2(m_run - m_new);
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sv[i] = fast_exp2(sv[i] - m_new);
+        psum += sv[i];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) o[dt] *= alpha;
+      accumulate_transposed<T, HD>(o, vs, 32 * s, sv, lane);
+    }
+  }
+
+  l_run += shfl_xor(l_run, 32);
+  if (qrow < S) {
+    store_column<T, HD, C::NDT>(out + ((size_t)bh * S + qrow) * HD, o, 1.0f / l_run, h);
+    if (h == 0) lse[(size_t)bh * S + qrow] = (m_run + log2f(l_run)) * kLn2;
+  }
+}
+
+// --------------------------------------------------------------------------------------
+// backward, dq: one workgroup per (batch*head, 128-query tile); also writes
+// delta_i = dO_i . out_i for the dk/dv kernel.
+// --------------------------------------------------------------------------------------
+template <typename T, int HD, typename TG>
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ out, const T* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ delta, TG* __restrict__ dq, int S, int H, int Hkv, float scale_log2,
+    float scale) {
+  using C = Tile<T, HD>;
+  __shared__ __attribute__((aligned(16))) T ks[kBlockN * C::LDS_ROW];
+  __shared__ __attribute__((aligned(16))) T vs[kBlockN * C::LDS_ROW];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
+  const int bh = blockIdx.x;
+  const int qt = gridDim.y - 1 - blockIdx.y;
+  const int b = bh / H, qh = bh - b * H;
+  const int kvbh = b * Hkv + qh / (H / Hkv);
+  const T* kp = k + (size_t)kvbh * S * HD;
+  const T* vp = v + (size_t)kvbh * S * HD;
+  const int q0 = qt * kBlockM;
+  const int qw0 = q0 + 32 * w;
+  const int qrow = qw0 + c32;
+  const size_t head_off = (size_t)bh * S * HD;
+
+  vec16_t<T> qf[C::NCH], df[C::NCH];
+  load_fragment<T, HD>(qf, q + head_off, qrow, S, h);
+  load_fragment<T, HD>(df, dout + head_off, qrow, S, h);
+  // delta = dO . out over this lane's chunks, then across the two lane halves
+  float dsum = 0.f;
+  {
+    vec16_t<T> of[C::NCH];
+    load_fragment<T, HD>(of, out + head_off, qrow, S, h);
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c)
+#pragma unroll
+      for (int j = 0; j < C::VEC; ++j) dsum += to_f32(df[c][j]) * to_f32(of[c][j]);
+  }
+  const float D = dsum + shfl_xor(dsum, 32);
+  const float lse2 = qrow < S ? lse[(size_t)bh * S + qrow] * kLog2e : 0.f;
+  if (qrow < S && h == 0) delta[(size_t)bh * S + qrow] = D;
+
+  f32x16 acc[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) acc[dt] = zero16();
+
+  const int kend = min(S, q0 + kBlockM);
+  const int ntiles = (kend + kBlockN - 1) / kBlockN;
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int k0 = kt * kBlockN;
+    __syncthreads();
+    stage_rows<T, HD>(ks, kp, k0, kBlockN, S, tid, 256);
+    stage_rows<T, HD>(vs, vp, k0, kBlockN, S, tid, 256);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kBlockN / 32; ++s) {
+      const int kb = k0 + 32 * s;
+      if (kb > qw0 + 31 || kb >= S) break;
+      const f32x16 st = contract_hd<T, HD>(ks, 32 * s, qf, lane);   // S^T: keys x queries
+      const f32x16 dpt = contract_hd<T, HD>(vs, 32 * s, df, lane);  // dP^T
+      const bool edge = (kb + 31 > qw0) || (kb + 31 >= S);
+      float dsv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(st[i] * scale_log2 - lse2);
+        if (edge) {
+          const int key = kb + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (key > qrow || key >= S) p = 0.f;
+        }
+        dsv[i] = p * (dpt[i] - D);
+      }
+      accumulate_transposed<T, HD>(acc, ks, 32 * s, dsv, lane);  // dQ^T += K^T dS^T
+    }
+  }
+  if (qrow < S) store_column<TG, HD, C::NDT>(dq + ((size_t)bh * S + qrow) * HD, acc, scale, h);
+}
+
+// --------------------------------------------------------------------------------------
+// backward, dk/dv: one workgroup owns 32*KW keys of one KV head; QS query splits
+// (QS * KW = 4 waves) walk interleaved 32-query tiles of every query head of the group,
+// r ascending; the split partials are added in split order at the end.  Every dk/dv
+// element therefore has one owner and a fixed summation order.
+// --------------------------------------------------------------------------------------
+constexpr int kBlockMQ = 32;  // queries per LDS stage in dk/dv
+
+template <typename T, int HD, typename TG, int QS>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ delta, TG* __restrict__ dk, T* __restrict__ dv, int S, int H,
+    int Hkv, float scale_log2, float scale) {
+  using C = Tile<T, HD>;
+  constexpr int KW = kWaves / QS;
+  constexpr int BNK = 32 * KW;
+  constexpr int TILE = kBlockMQ * C::LDS_ROW;
+  // Q tiles of the QS splits, then their dO tiles (one buffer so that the split
+  // reduction at the end can reuse all of it as fp32 scratch).
+  __shared__ __attribute__((aligned(16))) T stage[2 * QS * TILE];
+  __shared__ float lse_s[QS][kBlockMQ];
+  __shared__ float del_s[QS][kBlockMQ];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
+  const int kw = w % KW, sp = w / KW;
+  const int st_tid = tid % (64 * KW);
+  const int kvbh = blockIdx.x;
+  const int b = kvbh / Hkv, kvh = kvbh - b * Hkv;
+  const int group = H / Hkv;
+  const int k0 = blockIdx.y * BNK;  // lowest key tiles (most work) dispatched first
+  const int kw0 = k0 + 32 * kw;
+  const int key = kw0 + c32;
+  T* qtile = stage + sp * TILE;
+  T* dtile = stage + (QS + sp) * TILE;
+
+  vec16_t<T> kf[C::NCH], vf[C::NCH];
+  load_fragment<T, HD>(kf, k + (size_t)kvbh * S * HD, key, S, h);
+  load_fragment<T, HD>(vf, v + (size_t)kvbh * S * HD, key, S, h);
+  f32x16 dkt[C::NDT], dvt[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) dkt[dt] = dvt[dt] = zero16();
+
+  const int qt_first = k0 / kBlockMQ;
+  const int nqt = (S + kBlockMQ - 1) / kBlockMQ;
+  const int nsteps = (nqt - qt_first + QS - 1) / QS;
+  const bool wave_live = kw0 < S;
+
+  for (int r = 0; r < group; ++r) {
+    const int bh = b * H + kvh * group + r;
+    const T* qp = q + (size_t)bh * S * HD;
+    const T* dop = dout + (size_t)bh * S * HD;
+    for (int step = 0; step < nsteps; ++step) {
+      const int qt = qt_first + step * QS + sp;
+      const int q0 = qt * kBlockMQ;
+      __syncthreads();
+      if (qt < nqt) {
+        stage_rows<T, HD>(qtile, qp, q0, kBlockMQ, S, st_tid, 64 * KW);
+        stage_rows<T, HD>(dtile, dop, q0, kBlockMQ, S, st_tid, 64 * KW);
+        for (int i = st_tid; i < kBlockMQ; i += 64 * KW) {
+          const int qi = q0 + i;
+          lse_s[sp][i] = qi < S ? lse[(size_t)bh * S + qi] * kLog2e : INFINITY;
+          del_s[sp][i] = qi < S ? delta[(size_t)bh * S + qi] : 0.f;
+        }
+      }
+      __syncthreads();
+      if (qt >= nqt || !wave_live || q0 + kBlockMQ - 1 < kw0) continue;
+
+      const f32x16 st = contract_hd<T, HD>(qtile, 0, kf, lane);   // S: queries x keys
+      const f32x16 dpt = contract_hd<T, HD>(dtile, 0, vf, lane);  // dP
+      const bool edge = q0 < kw0 + 31;
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int mi = 8 * (i >> 2) + 4 * h + (i & 3);
+        float p = fast_exp2(st[i] * scale_log2 - lse_s[sp][mi]);
+        if (edge && q0 + mi < key) p = 0.f;
+        pv[i] = p;
+        dsv[i] = p * (dpt[i] - del_s[sp][mi]);
+      }
+      accumulate_transposed<T, HD>(dvt, dtile, 0, pv, lane);   // dV^T += dO^T P
+      accumulate_transposed<T, HD>(dkt, qtile, 0, dsv, lane);  // dK^T += Q^T dS
+    }
+  }
+
+  if constexpr (QS > 1) {
+    // Fixed-order combination of the split partials through LDS, one 32-row tile of one
+    // tensor at a time: total = split0 + split1 + ... + split(QS-1).
+    static_assert((QS - 1) * KW * 64 * 16 * sizeof(float) <= 2 * QS * TILE * sizeof(T),
+                  "reduction scratch must fit in the staging tiles");
+    float* red = reinterpret_cast<float*>(stage);
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) {
+        __syncthreads();
+        if (sp > 0) {
+          float* slot = red + (((sp - 1) * KW + kw) * 64 + lane) * 16;
+          const f32x16& src = which == 0 ? dkt[dt] : dvt[dt];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) slot[i] = src[i];
+        }
+        __syncthreads();
+        if (sp == 0) {
+#pragma unroll
+          for (int s2 = 1; s2 < QS; ++s2) {
+            const float* slot = red + (((s2 - 1) * KW + kw) * 64 + lane) * 16;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              if (which == 0) dkt[dt][i] += slot[i];
+              else dvt[dt][i] += slot[i];
+            }
+          }
+        }
+      }
+    }
+  }
+  if (sp == 0 && key < S) {
+    store_column<TG, HD, C::NDT>(dk + ((size_t)kvbh * S + key) * HD, dkt, scale, h);
+    store_column<T, HD, C::NDT>(dv + ((size_t)kvbh * S + key) * HD, dvt, 1.0f, h);
+  }
+}
+
+// --------------------------------------------------------------------------------------
+// launchers
+// --------------------------------------------------------------------------------------
+static inline float scale_of(int hd) { return 1.0f / sqrtf((float)hd); }
+
+template <typename T, int HD>
+static hipError_t fwd_impl(const AttnShape& s, const void* q, const void* k, const void* v,
+                           void* out, float* lse, hipStream_t stream) {
+  const dim3 grid(s.batch * s.num_heads, (s.seq_len + kBlockM - 1) / kBlockM);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(256), 0, stream, (const T*)q,
+                     (const T*)k, (const T*)v, (T*)out, lse, s.seq_len, s.num_heads,
+                     s.num_kv_heads, scale_of(HD) * kLog2e);
+  return hipPeekAtLastError();
+}
+
+hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const void* k,
+                           const void* v, void* out, float* lse, hipStream_t stream) {
+#define XATTN_CASE(T, HD) \
+  if (s.head_dim == HD) return fwd_impl<T, HD>(s, q, k, v, out, lse, stream);
+  if (io == IO_F32) {
+    XATTN_CASE(float, 16) XATTN_CASE(float, 32) XATTN_CASE(float, 64) XATTN_CASE(float, 128)
+  } else {
+    XATTN_CASE(bf16, 16) XATTN_CASE(bf16, 32) XATTN_CASE(bf16, 64) XATTN_CASE(bf16, 128)
+  }
+#undef XATTN_CASE
+  return hipErrorInvalidValue;
+}
+
+// Query splits for the dk/dv kernel: split the query walk only when there are too few
+// key tiles to fill the machine (256 CUs).  Depends on the shape only, so results stay
+// bitwise reproducible for a given shape.
+static int dkdv_splits(const AttnShape& s) {
+  const long long bkv = (long long)s.batch * s.num_kv_heads;
+  for (int qs = 1; qs <= 4; qs *= 2) {
+    const int bnk = 32 * (kWaves / qs);
+    const long long blocks = bkv * ((s.seq_len + bnk - 1) / bnk);
+    if (blocks >= 1024) return qs;
+  }
+  return 4;
+}
+
+template <typename T, int HD, typename TG, int QS>
+static void launch_dkdv(const AttnShape& s, const void* q, const void* k, const void* v,
+                        const void* dout, const float* lse, const float* delta, void* dk,
+                        void* dv, hipStream_t stream) {
+  constexpr int BNK = 32 * (kWaves / QS);
+  const dim3 grid(s.batch * s.num_kv_heads, (s.seq_len + BNK - 1) / BNK);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD, TG, QS>), grid, dim3(256), 0, stream,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta,
+                     (TG*)dk, (T*)dv, s.seq_len, s.num_heads, s.num_kv_heads,
+                     scale_of(HD) * kLog2e, scale_of(HD));
+}
+
+template <typename T, int HD, typename TG>
+static hipError_t bwd_impl(const AttnShape& s, const void* q, const void* k, const void* v,
+                           const void* out, const float* lse, const void* dout, void* dq,
+                           void* dk, void* dv, float* delta, hipStream_t stream) {
+  const dim3 grid(s.batch * s.num_heads, (s.seq_len + kBlockM - 1) / kBlockM);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD, TG>), grid, dim3(256), 0, stream,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)out, (const T*)dout, lse,
+                     delta, (TG*)dq, s.seq_len, s.num_heads, s.num_kv_heads,
+                     scale_of(HD) * kLog2e, scale_of(HD));
+  hipError_t e = hipPeekAtLastError();
+  if (e != hipSuccess) return e;
+  switch (dkdv_splits(s)) {
+    case 1: launch_dkdv<T, HD, TG, 1>(s, q, k, v, dout, lse, delta, dk, dv, stream); break;
+    case 2: launch_dkdv<T, HD, TG, 2>(s, q, k, v, dout, lse, delta, dk, dv, stream); break;
+    default: launch_dkdv<T, HD, TG, 4>(s, q, k, v, dout, lse, delta, dk, dv, stream); break;
+  }
+  return hipPeekAtLastError();
+}
+
+hipError_t launch_attn_bwd(IoType io, const AttnShape& s, const void* q, const void* k,
+                           const void* v, const void* out, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv, float* delta,
+                           bool grads_f32, hipStream_t stream) {
+#define XATTN_CASE(T, HD, TG)                                                          \
+  if (s.head_dim == HD)                                                                \
+    return bwd_impl<T, HD, TG>(s, q, k, v, out, lse, dout, dq, dk, dv, delta, stream);
+  if (io == IO_F32) {
+    XATTN_CASE(float, 16, float) XATTN_CASE(float, 32, float) XATTN_CASE(float, 64, float)
+    XATTN_CASE(float, 128, float)
+  } else if (grads_f32) {
+    XATTN_CASE(bf16, 16, float) XATTN_CASE(bf16, 32, float) XATTN_CASE(bf16, 64, float)
+    XATTN_CASE(bf16, 128, float)
+  } else {
+    XATTN_CASE(bf16, 16, bf16) XATTN_CASE(bf16, 32, bf16) XATTN_CASE(bf16, 64, bf16)
+    XATTN_CASE(bf16, 128, bf16)
+  }
+#undef XATTN_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace xattn

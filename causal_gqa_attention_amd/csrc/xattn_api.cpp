@@ -1,0 +1,357 @@
+// C-ABI layer of libxattn: argument validation, workspace carving, dispatch.
+//
+// Error discipline: every argument is checked before anything is enqueued, so a
+// rejected call has no side effects; launch errors are read with hipPeekAtLastError
+// (the sticky error is left for the caller to see); no exception crosses the ABI and
+// nothing here exits the process.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <initializer_list>
+#include <string>
+
+#include "../../include/xattn.h"
+#include "xattn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;  // exclusive bound on any element count
+
+struct Fail {
+  xattn_status status;
+};
+
+[[noreturn]] void fail(xattn_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  throw Fail{st};
+}
+
+void check_ptr(const void* p, const char* name) {
+  if (p == nullptr) fail(XATTN_ERR_INVALID_ARG, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    fail(XATTN_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+}
+
+void check_pos(int64_t v, const char* name) {
+  if (v <= 0) fail(XATTN_ERR_INVALID_ARG, "%s must be positive (got %lld)", name, (long long)v);
+}
+
+// a * b * c * d with an overflow check against kMaxElems (all factors already > 0)
+int64_t count4(int64_t a, int64_t b, int64_t c, int64_t d, const char* what) {
+  const long double n = (long double)a * (long double)b * (long double)c * (long double)d;
+  if (n >= (long double)kMaxElems)
+    fail(XATTN_ERR_INVALID_ARG, "%s: element count %.0Lf does not fit in int32", what, n);
+  return a * b * c * d;
+}
+
+void check_head_dim(int64_t hd) {
+  if (hd <= 0 || hd % 2 != 0)
+    fail(XATTN_ERR_INVALID_ARG, "head_dim must be positive and even (got %lld)", (long long)hd);
+  if (hd != 16 && hd != 32 && hd != 64 && hd != 128)
+    fail(XATTN_ERR_UNSUPPORTED, "head_dim %lld not supported (16, 32, 64, 128)", (long long)hd);
+}
+
+xattn::IoType check_dtype(int32_t dt) {
+  if (dt != XATTN_F32 && dt != XATTN_BF16)
+    fail(XATTN_ERR_INVALID_ARG, "dtype %d is not XATTN_F32 or XATTN_BF16", (int)dt);
+  return dt == XATTN_F32 ? xattn::IO_F32 : xattn::IO_BF16;
+}
+
+size_t io_size(xattn::IoType io) { return io == xattn::IO_F32 ? 4 : 2; }
+
+struct Range {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+// Outputs must not overlap inputs or each other.
+void check_no_overlap(std::initializer_list<Range> outs, std::initializer_list<Range> ins) {
+  auto overlap = [](const Range& a, const Range& b) {
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+  };
+  for (auto o = outs.begin(); o != outs.end(); ++o) {
+    for (const Range& i : ins)
+      if (overlap(*o, i)) fail(XATTN_ERR_INVALID_ARG, "output %s overlaps input %s", o->name, i.name);
+    for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+      if (overlap(*o, *o2)) fail(XATTN_ERR_INVALID_ARG, "outputs %s and %s overlap", o->name, o2->name);
+  }
+}
+
+void hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) fail(XATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+template <typename F>
+xattn_status guarded(F&& f) {
+  try {
+    f();
+    g_last_error.clear();
+    return XATTN_OK;
+  } catch (const Fail& e) {
+    return e.status;
+  } catch (...) {
+    g_last_error = "internal error";
+    return XATTN_ERR_INVALID_ARG;
+  }
+}
+
+struct DimsChecked {
+  xattn::AttnShape s;
+  xattn::IoType io;
+  int64_t q_elems, kv_elems, rows_q;
+};
+
+DimsChecked check_dims(const xattn_dims* d) {
+  if (d == nullptr) fail(XATTN_ERR_INVALID_ARG, "dims is NULL");
+  check_pos(d->batch, "batch");
+  check_pos(d->seq_len, "seq_len");
+  check_pos(d->num_heads, "num_heads");
+  check_pos(d->num_kv_heads, "num_kv_heads");
+  check_head_dim(d->head_dim);
+  if (d->num_heads % d->num_kv_heads != 0)
+    fail(XATTN_ERR_INVALID_ARG, "num_heads (%lld) must be a multiple of num_kv_heads (%lld)",
+         (long long)d->num_heads, (long long)d->num_kv_heads);
+  DimsChecked c;
+  c.io = check_dtype(d->dtype);
+  c.q_elems = count4(d->batch, d->num_heads, d->seq_len, d->head_dim, "q");
+  c.kv_elems = count4(d->batch, d->num_kv_heads, d->seq_len, d->head_dim, "k/v");
+  c.rows_q = d->batch * d->num_heads * d->seq_len;
+  c.s = {(int)d->batch, (int)d->seq_len, (int)d->num_heads, (int)d->num_kv_heads,
+         (int)d->head_dim};
+  return c;
+}
+
+size_t bwd_workspace(const DimsChecked& c, bool with_prologue) {
+  size_t n = align256((size_t)c.rows_q * sizeof(float));  // delta
+  if (with_prologue) {
+    const int64_t rows_k = (int64_t)c.s.batch * c.s.num_kv_heads * c.s.seq_len;
+    n += align256((size_t)c.q_elems * sizeof(float));      // dq w.r.t. the rotated q
+    n += align256((size_t)c.kv_elems * sizeof(float));     // dk w.r.t. the rotated k
+    n += align256((size_t)xattn::qknorm_rope_bwd_blocks(c.rows_q) * c.s.head_dim * sizeof(float));
+    n += align256((size_t)xattn::qknorm_rope_bwd_blocks(rows_k) * c.s.head_dim * sizeof(float));
+  }
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* xattn_version(void) { return "libxattn 0.1.0 (gfx950)"; }
+
+const char* xattn_status_string(xattn_status s) {
+  switch (s) {
+    case XATTN_OK: return "XATTN_OK";
+    case XATTN_ERR_INVALID_ARG: return "XATTN_ERR_INVALID_ARG: invalid argument";
+    case XATTN_ERR_UNSUPPORTED: return "XATTN_ERR_UNSUPPORTED: unsupported head_dim";
+    case XATTN_ERR_HIP: return "XATTN_ERR_HIP: HIP runtime error";
+  }
+  return "unknown xattn_status";
+}
+
+const char* xattn_last_error(void) { return g_last_error.c_str(); }
+
+xattn_status xattn_rope_cache(float* cos_tab, float* sin_tab, int64_t seq_len,
+                              int64_t head_dim, double theta, void* stream) {
+  return guarded([&] {
+    check_ptr(cos_tab, "cos_tab");
+    check_ptr(sin_tab, "sin_tab");
+    check_pos(seq_len, "seq_len");
+    check_head_dim(head_dim);
+    if (!(theta > 0.0) || !std::isfinite(theta))
+      fail(XATTN_ERR_INVALID_ARG, "theta must be positive and finite");
+    const int64_t n = count4(seq_len, head_dim / 2, 1, 1, "rope table");
+    check_no_overlap({{cos_tab, (size_t)n * 4, "cos_tab"}, {sin_tab, (size_t)n * 4, "sin_tab"}}, {});
+    hip_check(xattn::launch_rope_cache(cos_tab, sin_tab, (int)seq_len, (int)head_dim, theta,
+                                       (hipStream_t)stream),
+              "rope_cache launch");
+  });
+}
+
+xattn_status xattn_qknorm_rope_fwd(const void* x, const float* gamma, const float* cos_tab,
+                                   const float* sin_tab, void* y, float* rstd, int64_t rows,
+                                   int64_t seq_len, int64_t head_dim, float eps,
+                                   int32_t dtype, void* stream) {
+  return guarded([&] {
+    check_ptr(x, "x");
+    check_ptr(gamma, "gamma");
+    check_ptr(cos_tab, "cos_tab");
+    check_ptr(sin_tab, "sin_tab");
+    check_ptr(y, "y");
+    check_ptr(rstd, "rstd");
+    check_pos(rows, "rows");
+    check_pos(seq_len, "seq_len");
+    check_head_dim(head_dim);
+    const xattn::IoType io = check_dtype(dtype);
+    if (!(eps >= 0.f) || !std::isfinite(eps))
+      fail(XATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    const int64_t n = count4(rows, seq_len, head_dim, 1, "x");
+    const size_t xb = (size_t)n * io_size(io);
+    const size_t tb = (size_t)seq_len * (head_dim / 2) * 4;
+    check_no_overlap({{y, xb, "y"}, {rstd, (size_t)(rows * seq_len) * 4, "rstd"}},
+                     {{x, xb, "x"}, {gamma, (size_t)head_dim * 4, "gamma"},
+                      {cos_tab, tb, "cos_tab"}, {sin_tab, tb, "sin_tab"}});
+    hip_check(xattn::launch_qknorm_rope_fwd(io, (int)head_dim, x, gamma, cos_tab, sin_tab, y,
+                                            rstd, (int)(rows * seq_len), (int)seq_len, eps,
+                                            (hipStream_t)stream),
+              "qknorm_rope_fwd launch");
+  });
+}
+
+size_t xattn_qknorm_rope_bwd_workspace_bytes(int64_t rows, int64_t seq_len, int64_t head_dim) {
+  if (rows <= 0 || seq_len <= 0 || head_dim <= 0) return 0;
+  return (size_t)xattn::qknorm_rope_bwd_blocks(rows * seq_len) * (size_t)head_dim *
+         sizeof(float);
+}
+
+xattn_status xattn_qknorm_rope_bwd(const void* dy, const void* x, const float* gamma,
+                                   const float* rstd, const float* cos_tab,
+                                   const float* sin_tab, void* dx, float* dgamma,
+                                   void* workspace, size_t workspace_bytes, int64_t rows,
+                                   int64_t seq_len, int64_t head_dim, int32_t dtype,
+                                   void* stream) {
+  return guarded([&] {
+    check_ptr(dy, "dy");
+    check_ptr(x, "x");
+    check_ptr(gamma, "gamma");
+    check_ptr(rstd, "rstd");
+    check_ptr(cos_tab, "cos_tab");
+    check_ptr(sin_tab, "sin_tab");
+    check_ptr(dx, "dx");
+    check_ptr(dgamma, "dgamma");
+    check_ptr(workspace, "workspace");
+    check_pos(rows, "rows");
+    check_pos(seq_len, "seq_len");
+    check_head_dim(head_dim);
+    const xattn::IoType io = check_dtype(dtype);
+    const int64_t n = count4(rows, seq_len, head_dim, 1, "x");
+    const size_t need = xattn_qknorm_rope_bwd_workspace_bytes(rows, seq_len, head_dim);
+    if (workspace_bytes < need)
+      fail(XATTN_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, need);
+    const size_t xb = (size_t)n * io_size(io);
+    const size_t tb = (size_t)seq_len * (head_dim / 2) * 4;
+    check_no_overlap({{dx, xb, "dx"}, {dgamma, (size_t)head_dim * 4, "dgamma"},
+                      {workspace, need, "workspace"}},
+                     {{dy, xb, "dy"}, {x, xb, "x"}, {gamma, (size_t)head_dim * 4, "gamma"},
+                      {rstd, (size_t)(rows * seq_len) * 4, "rstd"}, {cos_tab, tb, "cos_tab"},
+                      {sin_tab, tb, "sin_tab"}});
+    hip_check(xattn::launch_qknorm_rope_bwd(io, io, (int)head_dim, dy, x, gamma, rstd, cos_tab,
+                                            sin_tab, dx, dgamma, (float*)workspace,
+                                            (int)(rows * seq_len), (int)seq_len,
+                                            (hipStream_t)stream),
+              "qknorm_rope_bwd launch");
+  });
+}
+
+xattn_status xattn_fwd(const xattn_dims* dims, const void* q, const void* k, const void* v,
+                       void* out, float* lse, void* stream) {
+  return guarded([&] {
+    const DimsChecked c = check_dims(dims);
+    check_ptr(q, "q");
+    check_ptr(k, "k");
+    check_ptr(v, "v");
+    check_ptr(out, "out");
+    check_ptr(lse, "lse");
+    const size_t qb = (size_t)c.q_elems * io_size(c.io), kb = (size_t)c.kv_elems * io_size(c.io);
+    check_no_overlap({{out, qb, "out"}, {lse, (size_t)c.rows_q * 4, "lse"}},
+                     {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}});
+    hip_check(xattn::launch_attn_fwd(c.io, c.s, q, k, v, out, lse, (hipStream_t)stream),
+              "attention forward launch");
+  });
+}
+
+size_t xattn_bwd_workspace_bytes(const xattn_dims* dims, int with_prologue) {
+  size_t n = 0;
+  const xattn_status st = guarded([&] { n = bwd_workspace(check_dims(dims), with_prologue != 0); });
+  return st == XATTN_OK ? n : 0;
+}
+
+xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, const void* v,
+                       const void* out, const float* lse, const void* dout, void* dq,
+                       void* dk, void* dv, const xattn_prologue* pro, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return guarded([&] {
+    const DimsChecked c = check_dims(dims);
+    for (auto [p, name] : {std::pair<const void*, const char*>{q, "q"}, {k, "k"}, {v, "v"},
+                           {out, "out"}, {lse, "lse"}, {dout, "dout"}, {dq, "dq"}, {dk, "dk"},
+                           {dv, "dv"}, {workspace, "workspace"}})
+      check_ptr(p, name);
+    const size_t need = bwd_workspace(c, pro != nullptr);
+    if (workspace_bytes < need)
+      fail(XATTN_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, need);
+    const size_t es = io_size(c.io);
+    const size_t qb = (size_t)c.q_elems * es, kb = (size_t)c.kv_elems * es;
+    const size_t hdb = (size_t)c.s.head_dim * 4;
+    const size_t tb = (size_t)c.s.seq_len * (c.s.head_dim / 2) * 4;
+    const int64_t rows_k = (int64_t)c.s.batch * c.s.num_kv_heads * c.s.seq_len;
+    if (pro != nullptr) {
+      for (auto [p, name] :
+           {std::pair<const void*, const char*>{pro->xq, "pro->xq"}, {pro->xk, "pro->xk"},
+            {pro->gamma_q, "pro->gamma_q"}, {pro->gamma_k, "pro->gamma_k"},
+            {pro->rstd_q, "pro->rstd_q"}, {pro->rstd_k, "pro->rstd_k"},
+            {pro->cos_tab, "pro->cos_tab"}, {pro->sin_tab, "pro->sin_tab"},
+            {pro->dgamma_q, "pro->dgamma_q"}, {pro->dgamma_k, "pro->dgamma_k"}})
+        check_ptr(p, name);
+      check_no_overlap(
+          {{dq, qb, "dq"}, {dk, kb, "dk"}, {dv, kb, "dv"}, {workspace, need, "workspace"},
+           {pro->dgamma_q, hdb, "pro->dgamma_q"}, {pro->dgamma_k, hdb, "pro->dgamma_k"}},
+          {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {out, qb, "out"},
+           {lse, (size_t)c.rows_q * 4, "lse"}, {dout, qb, "dout"}, {pro->xq, qb, "pro->xq"},
+           {pro->xk, kb, "pro->xk"}, {pro->gamma_q, hdb, "pro->gamma_q"},
+           {pro->gamma_k, hdb, "pro->gamma_k"}, {pro->rstd_q, (size_t)c.rows_q * 4, "pro->rstd_q"},
+           {pro->rstd_k, (size_t)rows_k * 4, "pro->rstd_k"}, {pro->cos_tab, tb, "pro->cos_tab"},
+           {pro->sin_tab, tb, "pro->sin_tab"}});
+    } else {
+      check_no_overlap({{dq, qb, "dq"}, {dk, kb, "dk"}, {dv, kb, "dv"}, {workspace, need, "workspace"}},
+                       {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {out, qb, "out"},
+                        {lse, (size_t)c.rows_q * 4, "lse"}, {dout, qb, "dout"}});
+    }
+
+    char* ws = static_cast<char*>(workspace);
+    float* delta = reinterpret_cast<float*>(ws);
+    ws += align256((size_t)c.rows_q * sizeof(float));
+    const hipStream_t st = (hipStream_t)stream;
+    if (pro == nullptr) {
+      hip_check(xattn::launch_attn_bwd(c.io, c.s, q, k, v, out, lse, dout, dq, dk, dv, delta,
+                                       false, st),
+                "attention backward launch");
+      return;
+    }
+    float* dyq = reinterpret_cast<float*>(ws);
+    ws += align256((size_t)c.q_elems * sizeof(float));
+    float* dyk = reinterpret_cast<float*>(ws);
+    ws += align256((size_t)c.kv_elems * sizeof(float));
+    float* part_q = reinterpret_cast<float*>(ws);
+    ws += align256((size_t)xattn::qknorm_rope_bwd_blocks(c.rows_q) * c.s.head_dim * sizeof(float));
+    float* part_k = reinterpret_cast<float*>(ws);
+    hip_check(xattn::launch_attn_bwd(c.io, c.s, q, k, v, out, lse, dout, dyq, dyk, dv, delta,
+                                     true, st),
+              "attention backward launch");
+    hip_check(xattn::launch_qknorm_rope_bwd(xattn::IO_F32, c.io, c.s.head_dim, dyq, pro->xq,
+                                            pro->gamma_q, pro->rstd_q, pro->cos_tab,
+                                            pro->sin_tab, dq, pro->dgamma_q, part_q,
+                                            (int)c.rows_q, c.s.seq_len, st),
+              "prologue backward (q) launch");
+    hip_check(xattn::launch_qknorm_rope_bwd(xattn::IO_F32, c.io, c.s.head_dim, dyk, pro->xk,
+                                            pro->gamma_k, pro->rstd_k, pro->cos_tab,
+                                            pro->sin_tab, dk, pro->dgamma_k, part_k,
+                                            (int)rows_k, c.s.seq_len, st),
+              "prologue backward (k) launch");
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Internal launcher interface between the C-ABI layer (xattn_api.cpp) and the HIP
+// kernels.  All arguments have been validated by the caller: sizes are positive,
+// element counts fit in int32, pointers are non-null and 16-byte aligned.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace xattn {
+
+enum IoType { IO_F32 = 0, IO_BF16 = 1 };
+
+// ---- prologue ------------------------------------------------------------------------
+hipError_t launch_rope_cache(float* cos_tab, float* sin_tab, int seq_len, int head_dim,
+                             double theta, hipStream_t stream);
+
+hipError_t launch_qknorm_rope_fwd(IoType io, int head_dim, const void* x, const float* gamma,
+                                  const float* cos_tab, const float* sin_tab, void* y,
+                                  float* rstd, int nrows, int seq_len, float eps,
+                                  hipStream_t stream);
+
+// Number of per-block dgamma partial rows the backward writes for `nrows` rows.
+int qknorm_rope_bwd_blocks(int64_t nrows);
+
+// dy_io is the dtype of dy (may be fp32 while x / dx are bf16).
+hipError_t launch_qknorm_rope_bwd(IoType dy_io, IoType x_io, int head_dim, const void* dy,
+                                  const void* x, const float* gamma, const float* rstd,
+                                  const float* cos_tab, const float* sin_tab, void* dx,
+                                  float* dgamma, float* partials, int nrows, int seq_len,
+                                  hipStream_t stream);
+
+// ---- attention -----------------------------------------------------------------------
+struct AttnShape {
+  int batch, seq_len, num_heads, num_kv_heads, head_dim;
+};
+
+hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const void* k,
+                           const void* v, void* out, float* lse, hipStream_t stream);
+
+// dq_f32 / dk_f32: when true, dq / dk are written as fp32 (used when the prologue
+// backward follows inside xattn_bwd); otherwise in the io dtype.
+hipError_t launch_attn_bwd(IoType io, const AttnShape& s, const void* q, const void* k,
+                           const void* v, const void* out, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv, float* delta,
+                           bool grads_f32, hipStream_t stream);
+
+}  // namespace xattn

@@ -1,0 +1,164 @@
+/*
+ * libxattn: causal multi-head / grouped-query scaled-dot-product attention with a
+ * per-head QK-RMSNorm + rotate_half RoPE prologue, forward and backward, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what each call computes (page titles and sections):
+ *   [T9]   xtrain "Phase T9: Export to xserv": conventions table (RMSNorm with no mean
+ *          subtraction, per-head QK-norm with one gamma[head_dim] per tensor, rotate_half
+ *          RoPE with frequency theta^(-2i/hd) and position = token index, scale
+ *          1/sqrt(head_dim), causal mask) and Decision 1 (QK-norm after the head reshape,
+ *          before RoPE).
+ *   [MINT] Mint documentation, sections 5.3.1 (score, causal mask, stable softmax,
+ *          weighted sum), 5.4.1-5.4.4 (RoPE rotation, angle, backward = rotation by the
+ *          negative angle, positions restart at 0 per sequence, cached frequencies),
+ *          5.5.1-5.5.2 (RMSNorm forward and backward, dgamma accumulated across rows).
+ *   [T15]  xtrain "Phase T15: GQA": layouts [batch*heads, S, hd] for Q and
+ *          [batch*num_kv_heads, S, hd] for K/V; query head qh reads KV head qh/group;
+ *          num_heads % num_kv_heads == 0; the K/V gradient of a shared head is the
+ *          deterministic sum of its group's query-head gradients, with no atomics.
+ *   [T12]  xtrain "Phase T12: bf16 mixed precision", precision table: bf16 activations
+ *          with fp32 accumulation; softmax, norm and RoPE computed in fp32; fp32 master
+ *          weights (gamma) and gradients.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers to contiguous row-major tensors owned by the caller,
+ *     16-byte aligned.  Outputs are overwritten, never accumulated into, and must not
+ *     alias inputs.  The library never allocates or frees device memory; scratch comes
+ *     from a caller-provided workspace sized by the matching *_workspace_bytes query.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue work and
+ *     return; results are valid once the caller synchronises the stream.
+ *   - io dtype: XATTN_F32 (fp32 everywhere) or XATTN_BF16 (bf16 tensors, fp32
+ *     arithmetic inside, fp32 lse / rstd / gamma / dgamma).
+ *   - Errors: every argument is validated before any device work; an invalid call
+ *     returns a status and has no side effects.  Kernel-launch failures are reported
+ *     as XATTN_ERR_HIP (the HIP error is peeked, not cleared).  Faults inside kernels
+ *     surface at the caller's next synchronisation.  No call aborts the process or lets
+ *     a C++ exception escape.  xattn_last_error() gives a thread-local message.
+ *   - Inputs are assumed finite; non-finite inputs propagate, results unspecified.
+ *   - Supported head_dim: 16, 32, 64, 128.  seq_len >= 1.  Every tensor's element count
+ *     must stay below 2^31.
+ */
+#ifndef XATTN_H
+#define XATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { XATTN_F32 = 0, XATTN_BF16 = 1 } xattn_dtype;
+
+typedef enum {
+  XATTN_OK = 0,
+  XATTN_ERR_INVALID_ARG = 1,  /* null pointer, size <= 0, H % Hkv != 0, odd head_dim,
+                                 misaligned pointer, element count >= 2^31, bad dtype */
+  XATTN_ERR_UNSUPPORTED = 2,  /* head_dim not in {16, 32, 64, 128} */
+  XATTN_ERR_HIP = 3           /* a kernel launch reported a HIP error */
+} xattn_status;
+
+/* Shape of one attention call ([T15] layouts). */
+typedef struct {
+  int64_t batch;         /* B */
+  int64_t seq_len;       /* S: query and key length (square causal self-attention) */
+  int64_t num_heads;     /* H: query heads */
+  int64_t num_kv_heads;  /* Hkv: K/V heads; H % Hkv == 0, group = H / Hkv */
+  int64_t head_dim;      /* hd */
+  int32_t dtype;         /* xattn_dtype of q, k, v, out, dout, dq, dk, dv */
+} xattn_dims;
+
+/* Prologue inputs that let xattn_bwd also run the QK-norm + RoPE backward, so that
+ * dq / dk come out with respect to the raw (pre-norm) projections. */
+typedef struct {
+  const void* xq;          /* [B*H, S, hd] io dtype: raw Q before QK-norm */
+  const void* xk;          /* [B*Hkv, S, hd] io dtype: raw K before QK-norm */
+  const float* gamma_q;    /* [hd] fp32 */
+  const float* gamma_k;    /* [hd] fp32 */
+  const float* rstd_q;     /* [B*H*S] fp32, as written by xattn_qknorm_rope_fwd */
+  const float* rstd_k;     /* [B*Hkv*S] fp32 */
+  const float* cos_tab;    /* [S, hd/2] fp32, from xattn_rope_cache */
+  const float* sin_tab;    /* [S, hd/2] fp32 */
+  float* dgamma_q;         /* [hd] fp32 output (overwritten) */
+  float* dgamma_k;         /* [hd] fp32 output (overwritten) */
+} xattn_prologue;
+
+/* RoPE cos/sin table ([MINT] 5.4.2 and 5.4.4, [T9] "cos/sin cache"):
+ *   angle(t, i) = t * theta^(-2i/head_dim), t in [0, seq_len), i in [0, head_dim/2),
+ * evaluated in fp64 on the device and rounded once to fp32.
+ * cos_tab, sin_tab: [seq_len, head_dim/2] fp32 outputs. */
+xattn_status xattn_rope_cache(float* cos_tab, float* sin_tab, int64_t seq_len,
+                              int64_t head_dim, double theta, void* stream);
+
+/* Prologue forward ([T9] Decision 1, [MINT] 5.4.1 and 5.5.1), per row x in R^hd of a
+ * [rows, seq_len, hd] tensor (rows = B*H for Q or B*Hkv for K), row position t = s:
+ *   rstd = 1 / sqrt(mean(x^2) + eps);  n = gamma * x * rstd;
+ *   y[i] = n[i] cos - n[i+hd/2] sin;  y[i+hd/2] = n[i] sin + n[i+hd/2] cos.
+ * x, y: io dtype [rows, S, hd]; gamma: fp32 [hd]; cos/sin: fp32 [S, hd/2];
+ * rstd: fp32 [rows*S] output (kept for the backward). */
+xattn_status xattn_qknorm_rope_fwd(const void* x, const float* gamma, const float* cos_tab,
+                                   const float* sin_tab, void* y, float* rstd, int64_t rows,
+                                   int64_t seq_len, int64_t head_dim, float eps,
+                                   int32_t dtype, void* stream);
+
+/* Bytes of workspace xattn_qknorm_rope_bwd needs (per-block dgamma partials). */
+size_t xattn_qknorm_rope_bwd_workspace_bytes(int64_t rows, int64_t seq_len, int64_t head_dim);
+
+/* Prologue backward ([MINT] 5.4.4 and 5.5.2): dn = rotation of dy by the negative angle;
+ *   dot = sum(gamma * dn * x);  dx = gamma * dn * rstd - x * dot * rstd^3 / hd;
+ *   dgamma = sum over all rows*S rows of dn * x * rstd, reduced in a fixed order
+ *   (bitwise reproducible run to run).
+ * dy, x, dx: io dtype [rows, S, hd]; rstd: fp32 [rows*S]; dgamma: fp32 [hd] output. */
+xattn_status xattn_qknorm_rope_bwd(const void* dy, const void* x, const float* gamma,
+                                   const float* rstd, const float* cos_tab,
+                                   const float* sin_tab, void* dx, float* dgamma,
+                                   void* workspace, size_t workspace_bytes, int64_t rows,
+                                   int64_t seq_len, int64_t head_dim, int32_t dtype,
+                                   void* stream);
+
+/* Attention forward ([MINT] 5.3.1, [T9] scale and causal mask, [T15] head mapping):
+ * for batch b, query head qh (kv head kvh = qh / group), query i and key j <= i:
+ *   s_ij = q_i . k_j / sqrt(hd);  p_ij = softmax_j(s_ij) (fp32, max-subtracted);
+ *   out_i = sum_j p_ij v_j;  lse_i = ln(sum_{j<=i} exp(s_ij)).
+ * q, out: [B*H, S, hd] io dtype; k, v: [B*Hkv, S, hd] io dtype; lse: [B*H*S] fp32 output.
+ * For bf16 the probabilities are rounded to bf16 before the P.V product. */
+xattn_status xattn_fwd(const xattn_dims* dims, const void* q, const void* k, const void* v,
+                       void* out, float* lse, void* stream);
+
+/* Bytes of workspace xattn_bwd needs; with_prologue != 0 sizes it for a call with a
+ * non-NULL xattn_prologue. */
+size_t xattn_bwd_workspace_bytes(const xattn_dims* dims, int with_prologue);
+
+/* Attention backward: the chain rule of xattn_fwd.  With D_i = sum_d dout_id out_id,
+ *   dP_ij = dout_i . v_j;  dS_ij = p_ij (dP_ij - D_i);
+ *   dq_i = sum_j dS_ij k_j / sqrt(hd);
+ *   dk_j = sum_{r<group} sum_{i>=j} dS^(r)_ij q^(r)_i / sqrt(hd);
+ *   dv_j = sum_{r<group} sum_{i>=j} p^(r)_ij dout^(r)_i,
+ * where r runs over the query heads kvh*group + r sharing the KV head ([T15] Decision 2).
+ * Each dk/dv element has a single owner that sums its group in a fixed order: no
+ * atomics, bitwise reproducible run to run (dq, too).
+ * pro == NULL: dq, dk are gradients w.r.t. the q, k that xattn_fwd consumed.
+ * pro != NULL: the prologue backward runs too; dq, dk are then gradients w.r.t. the raw
+ * pro->xq, pro->xk and pro->dgamma_q / dgamma_k are written.
+ * q, out, dout, dq: [B*H, S, hd]; k, v, dk, dv: [B*Hkv, S, hd]; lse: [B*H*S] fp32 from
+ * xattn_fwd.  workspace: device memory of at least xattn_bwd_workspace_bytes bytes. */
+xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, const void* v,
+                       const void* out, const float* lse, const void* dout, void* dq,
+                       void* dk, void* dv, const xattn_prologue* pro, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* xattn_status_string(xattn_status s);
+
+/* Thread-local message describing the last failing call on this thread ("" if none). */
+const char* xattn_last_error(void);
+
+/* Library version string. */
+const char* xattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XATTN_H */

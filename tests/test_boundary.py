@@ -1,0 +1,147 @@
+"""Host-side checks of the C-ABI boundary: the library loads, exports every entry point
+include/xattn.h declares, and rejects every invalid argument with the documented status
+before touching the device.  No call here reaches a kernel launch (no GPU needed): each
+one fails validation first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_gqa_attention_amd as X
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "xattn.h")
+
+OK, INVALID, UNSUPPORTED, HIPERR = 0, 1, 2, 3
+A = 0x10000  # a 16-byte aligned fake device address; never dereferenced
+MB = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(xattn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(X.library_path()):
+        pytest.fail("libxattn.so is not built (run python -m causal_gqa_attention_amd.build)")
+    return X.load_library()
+
+
+def test_library_exports_every_declared_entry_point(lib):
+    names = declared_functions()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert "gfx950" in X.xattn_version()
+
+
+def test_status_strings(lib):
+    for s in (OK, INVALID, UNSUPPORTED, HIPERR):
+        assert lib.xattn_status_string(s).decode().startswith(
+            ["XATTN_OK", "XATTN_ERR_INVALID_ARG", "XATTN_ERR_UNSUPPORTED", "XATTN_ERR_HIP"][s])
+    assert "unknown" in lib.xattn_status_string(99).decode()
+
+
+def dims(B=2, S=64, H=8, Hkv=2, hd=64, dt=1):
+    return X.Dims(B, S, H, Hkv, hd, dt)
+
+
+def fwd(lib, d, q=A, k=A + 8 * MB, v=A + 16 * MB, out=A + 24 * MB, lse=A + 32 * MB):
+    return lib.xattn_fwd(ctypes.byref(d), q, k, v, out, lse, None)
+
+
+def last(lib):
+    return lib.xattn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(H=6, Hkv=4), INVALID, "multiple of num_kv_heads"),
+    (dict(Hkv=0), INVALID, "num_kv_heads"),
+    (dict(B=0), INVALID, "batch"),
+    (dict(S=-3), INVALID, "seq_len"),
+    (dict(hd=63), INVALID, "even"),
+    (dict(hd=48), UNSUPPORTED, "not supported"),
+    (dict(hd=256), UNSUPPORTED, "not supported"),
+    (dict(dt=7), INVALID, "dtype"),
+    (dict(B=1 << 20, S=1 << 12, H=8, Hkv=8, hd=128), INVALID, "int32"),
+])
+def test_fwd_rejects_bad_dims(lib, kw, status, msg):
+    assert fwd(lib, dims(**kw)) == status
+    assert msg in last(lib)
+
+
+def test_fwd_rejects_null_and_misaligned_pointers(lib):
+    d = dims()
+    assert fwd(lib, d, q=None) == INVALID and "q is NULL" in last(lib)
+    assert fwd(lib, d, lse=None) == INVALID and "lse is NULL" in last(lib)
+    assert fwd(lib, d, v=A + 8 * MB + 16 * MB + 2) == INVALID and "aligned" in last(lib)
+    assert lib.xattn_fwd(None, A, A, A, A, A, None) == INVALID and "dims" in last(lib)
+
+
+def test_fwd_rejects_aliasing_outputs(lib):
+    d = dims()
+    assert fwd(lib, d, out=A) == INVALID and "overlaps input q" in last(lib)
+    assert fwd(lib, d, lse=A + 24 * MB + 4096) == INVALID and "overlap" in last(lib)
+
+
+def test_prologue_fwd_validation(lib):
+    f = lib.xattn_qknorm_rope_fwd
+    base = [A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB]
+    assert f(None, *base[1:], 4, 16, 64, 1e-5, 0, None) == INVALID
+    assert f(*base, 4, 16, 64, -1.0, 0, None) == INVALID and "eps" in last(lib)
+    assert f(*base, 4, 16, 64, float("nan"), 0, None) == INVALID
+    assert f(*base, 4, 16, 60, 1e-5, 0, None) == UNSUPPORTED
+    assert f(*base, 0, 16, 64, 1e-5, 0, None) == INVALID and "rows" in last(lib)
+    # y overlapping x
+    assert f(A, base[1], base[2], base[3], A + 64, base[5], 4, 16, 64, 1e-5, 0, None) == INVALID
+
+
+def test_rope_cache_validation(lib):
+    f = lib.xattn_rope_cache
+    assert f(A, A + MB, 16, 64, 0.0, None) == INVALID and "theta" in last(lib)
+    assert f(A, A + MB, 16, 64, float("inf"), None) == INVALID
+    assert f(A, A + MB, 0, 64, 1e4, None) == INVALID
+    assert f(A, A + 8, 16, 64, 1e4, None) == INVALID  # tables overlap
+    assert f(A, None, 16, 64, 1e4, None) == INVALID
+
+
+def test_prologue_bwd_workspace_and_validation(lib):
+    ws = lib.xattn_qknorm_rope_bwd_workspace_bytes(1024, 1024, 64)
+    assert ws > 0 and ws % (64 * 4) == 0
+    assert lib.xattn_qknorm_rope_bwd_workspace_bytes(0, 1, 64) == 0
+    f = lib.xattn_qknorm_rope_bwd
+    p = [A + i * 64 * MB for i in range(9)]
+    assert f(*p, ws - 4, 1024, 1024, 64, 1, None) == INVALID and "workspace too small" in last(lib)
+    assert f(*p[:8], None, ws, 1024, 1024, 64, 1, None) == INVALID
+
+
+def test_bwd_workspace_and_validation(lib):
+    d = dims()
+    w0 = lib.xattn_bwd_workspace_bytes(ctypes.byref(d), 0)
+    w1 = lib.xattn_bwd_workspace_bytes(ctypes.byref(d), 1)
+    assert w0 >= 2 * 8 * 64 * 4 and w1 > w0
+    bad = dims(H=6, Hkv=4)
+    assert lib.xattn_bwd_workspace_bytes(ctypes.byref(bad), 0) == 0
+    p = [A + i * 16 * MB for i in range(10)]
+    f = lib.xattn_bwd
+    assert f(ctypes.byref(d), *p[:9], None, p[9], w0 - 1, None) == INVALID
+    assert "workspace too small" in last(lib)
+    assert f(ctypes.byref(d), *p[:9], None, None, w0, None) == INVALID
+    # dq aliasing dout
+    assert f(ctypes.byref(d), *p[:6], p[5], p[7], p[8], None, p[9], w0, None) == INVALID
+    # prologue with a NULL member
+    pro = X.Prologue(*[A + (20 + i) * 16 * MB for i in range(10)])
+    pro.rstd_k = None
+    assert f(ctypes.byref(d), *p[:9], ctypes.byref(pro), p[9], w1, None) == INVALID
+    assert "rstd_k" in last(lib)
+
+
+def test_python_binding_fails_loudly_without_device_tensors():
+    import torch
+    q = torch.zeros(16, 8, 64)
+    with pytest.raises(ValueError, match="device tensor"):
+        X.attn_fwd(q, q, q, 8, 2)

@@ -1,0 +1,129 @@
+"""Parity of the HIP path (through the C ABI) with the float64 CPU oracle on the same
+seeded inputs.  Bar: norm-wise max relative error <= 1e-4 for fp32 io, <= 2e-2 for bf16
+io, per output tensor.
+
+Small shapes are compared element by element over every output; the full-size
+workloads 3-5 run the whole step on the GPU and are compared on sampled heads (the
+oracle computes those heads one by one), plus the prologue over every row."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import (TOL, assert_close, attention_only, note, q_heads_of, run_step,
+                      sampled_kv_heads, seeded_attention_inputs)
+
+pytestmark = pytest.mark.gpu
+
+R = W.small_ragged
+SMALL = [
+    W.WORKLOADS[1],
+    W.WORKLOADS[2],
+    R("f32", 16, 7, 1, 2, 1, index=201),
+    R("f32", 32, 77, 2, 6, 2, index=202),
+    R("f32", 64, 130, 1, 4, 4, index=203),
+    R("f32", 128, 100, 1, 4, 2, theta=1e6, eps=1e-6, index=204),
+    R("f32", 64, 1, 2, 4, 2, index=205),
+    R("bf16", 16, 33, 1, 3, 1, index=206),
+    R("bf16", 32, 200, 2, 4, 4, index=207),
+    R("bf16", 64, 77, 2, 6, 2, index=208),
+    R("bf16", 64, 513, 1, 5, 1, index=209),
+    R("bf16", 128, 257, 1, 8, 2, theta=1e6, eps=1e-6, index=210),
+    R("bf16", 128, 1, 1, 4, 1, index=211),
+    W.WORKLOADS[4].replace(batch=2, seq_len=190, index=212),
+    W.WORKLOADS[5].replace(seq_len=300, index=213),
+]
+SMALL_IDS = [w.name if w.index < 100 else f"{w.dtype}_hd{w.head_dim}_S{w.seq_len}_"
+             f"B{w.batch}_H{w.num_heads}_kv{w.num_kv_heads}" for w in SMALL]
+
+
+def _compare_step(w, g, f, b, rows_q=None, rows_k=None, q_heads=None, kv_heads=None):
+    tol = TOL[w.dtype]
+    S = w.seq_len
+    errs = {}
+    for n in ("yq", "yk"):
+        errs[n] = assert_close(n, g[n], f[n], tol)
+    errs["rstd_q"] = assert_close("rstd_q", g["rstd_q"], f["rstd_q"].reshape(-1), tol)
+    errs["rstd_k"] = assert_close("rstd_k", g["rstd_k"], f["rstd_k"].reshape(-1), tol)
+    qh = slice(None) if q_heads is None else q_heads
+    kh = slice(None) if kv_heads is None else kv_heads
+    errs["out"] = assert_close("out", g["out"][qh], f["out"][qh], tol)
+    errs["lse"] = assert_close("lse", g["lse"].reshape(-1, S)[qh], f["lse"][qh], tol)
+    errs["dxq"] = assert_close("dxq", g["dxq"][qh], b["dxq"][qh], tol)
+    errs["dxk"] = assert_close("dxk", g["dxk"][kh], b["dxk"][kh], tol)
+    errs["dv"] = assert_close("dv", g["dv"][kh], b["dv"][kh], tol)
+    if q_heads is None:
+        errs["dgamma_q"] = assert_close("dgamma_q", g["dgamma_q"], b["dgamma_q"], tol)
+        errs["dgamma_k"] = assert_close("dgamma_k", g["dgamma_k"], b["dgamma_k"], tol)
+    print(w.name, {k: f"{v:.2e}" for k, v in errs.items()})
+
+
+@pytest.mark.parametrize("w", SMALL, ids=SMALL_IDS)
+def test_step_matches_oracle(w):
+    x = W.make_inputs(w)
+    note(f"step {w}")
+    g = run_step(w, x)
+    f = oracle.forward(x.xq, x.xk, x.v, x.gamma_q, x.gamma_k, w.num_heads, w.num_kv_heads,
+                       w.eps, w.theta)
+    b = oracle.backward(x.xq, x.xk, x.v, x.gamma_q, x.gamma_k, x.dout, w.num_heads,
+                        w.num_kv_heads, w.eps, w.theta)
+    cos, sin = oracle.rope_tables(w.seq_len, w.head_dim, w.theta)
+    np.testing.assert_allclose(g["cos"], cos, rtol=0, atol=2e-7)
+    np.testing.assert_allclose(g["sin"], sin, rtol=0, atol=2e-7)
+    _compare_step(w, g, f, b)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=SMALL_IDS)
+def test_attention_matches_oracle(w):
+    """Attention alone (q, k, v given directly): out, lse and dq, dk, dv."""
+    q, k, v, do = seeded_attention_inputs(w, 1000 + w.index)
+    note(f"attention {w}")
+    g = attention_only(w, q, k, v, do)
+    out, lse = oracle.attention_fwd(q, k, v, w.num_heads, w.num_kv_heads)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, w.num_heads, w.num_kv_heads)
+    tol = TOL[w.dtype]
+    errs = {n: assert_close(n, g[n], r, tol) for n, r in
+            (("out", out), ("dq", dq), ("dk", dk), ("dv", dv))}
+    errs["lse"] = assert_close("lse", g["lse"].reshape(lse.shape), lse, tol)
+    print(w.name, {k: f"{e:.2e}" for k, e in errs.items()})
+
+
+@pytest.mark.parametrize("idx", [3, 4, 5])
+def test_full_size_step_on_sampled_heads(idx):
+    w = W.WORKLOADS[idx]
+    x = W.make_inputs(w)
+    note(f"full-size step {w}")
+    g = run_step(w, x)
+    kvs = sampled_kv_heads(w, 1 if idx == 5 else 2)
+    qs = [h for kv in kvs for h in q_heads_of(w, kv)]
+    f = oracle.forward(x.xq, x.xk, x.v, x.gamma_q, x.gamma_k, w.num_heads, w.num_kv_heads,
+                       w.eps, w.theta, heads=qs)
+    b = oracle.backward(x.xq, x.xk, x.v, x.gamma_q, x.gamma_k, x.dout, w.num_heads,
+                        w.num_kv_heads, w.eps, w.theta, kv_heads=kvs)
+    _compare_step(w, g, f, b, q_heads=qs, kv_heads=kvs)
+    # every head (not only the sampled ones) produced finite values
+    for n in ("out", "lse", "dxq", "dxk", "dv", "dgamma_q", "dgamma_k"):
+        assert np.all(np.isfinite(g[n])), n
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_prologue_matches_oracle_every_row(idx):
+    """QK-norm + RoPE forward and backward on every row of the workload's Q and K, with
+    the seeded dout (for Q) and v (for K) standing in for the upstream gradients."""
+    import causal_gqa_attention_amd as X
+    from gpu_util import dev, host
+    w = W.WORKLOADS[idx]
+    x = W.make_inputs(w)
+    tol = TOL[w.dtype]
+    note(f"prologue {w}")
+    cos, sin = X.rope_cache(w.seq_len, w.head_dim, w.theta)
+    for name, xin, gam, dy in (("q", x.xq, x.gamma_q, x.dout), ("k", x.xk, x.gamma_k, x.v)):
+        tx, tg, tdy = dev(xin, w.dtype), dev(gam, "f32"), dev(dy, w.dtype)
+        y, rstd = X.qknorm_rope_fwd(tx, tg, cos, sin, w.eps)
+        dx, dg = X.qknorm_rope_bwd(tdy, tx, tg, rstd, cos, sin)
+        ry, rr = oracle.qknorm_rope_fwd(xin, gam, w.eps, w.theta)
+        rdx, rdg = oracle.qknorm_rope_bwd(dy, xin, gam, rr, w.theta)
+        assert_close(f"y{name}", host(y), ry, tol)
+        assert_close(f"rstd{name}", host(rstd), rr.reshape(-1), tol)
+        assert_close(f"dx{name}", host(dx), rdx, tol)
+        assert_close(f"dgamma{name}", host(dg), rdg, tol)
