@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark: causal GQA attention fwd+bwd (with the QK-norm + RoPE prologue) on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input: RoPE cache,
+QK-norm + RoPE on Q and K, attention forward, attention backward with the group sum,
+prologue backward and dgamma reductions (libxattn kernels only, preallocated buffers,
+one stream).  The workload is the long-context Qwen3-shaped GQA configuration (B=1,
+S=4096, 32 query heads, 8 KV heads, head_dim 128, bf16 in / fp32 accumulate).
+
+value = algorithmic attention FLOP per step (12 * hd per causal pair per query head:
+4 * hd forward, 8 * hd backward; recompute not counted) / measured step time, in TFLOP/s.
+The step time includes the prologue kernels, which do no counted FLOP.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
+  python bench.py --copy-calibration   # plain device copy of known size, for PMC scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal GQA attn fwd+bwd TFLOP/s (bf16) and % of MI355X MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X published dense MFMA peaks
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_bwd_dkdv_qwen3_long_gqa_bf16.json")
+ATTN_SRC = os.path.join(ROOT, "causal_gqa_attention_amd", "csrc", "attn.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=5, help="index of the workload shape")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain device copy of 1 GiB (for HBM counter scaling)")
+    return p.parse_args()
+
+
+def kernel_units(w):
+    """Algorithmic work per launch of each kernel of the step (flops for MFMA kernels,
+    HBM bytes for the memory-bound prologue), and the bound that applies."""
+    pairs = w.causal_pairs() * w.bh
+    hd = w.head_dim
+    io = 2 if w.dtype == "bf16" else 4
+    rows_q, rows_k = w.bh * w.seq_len, w.bkv * w.seq_len
+    return {
+        "attn_fwd": ("mfma", 4 * hd * pairs, "QK^T and PV: 4*hd per causal pair"),
+        "attn_bwd_dkdv": ("mfma", 6 * hd * pairs, "dP, dV, dK: 6*hd per causal pair"),
+        "attn_bwd_dq": ("mfma", 2 * hd * pairs, "dQ: 2*hd per causal pair"),
+        # prologue: per launch average over the Q launch and the K launch
+        "qknorm_rope_fwd": ("hbm", ((rows_q + rows_k) * (hd * 2 * io + 4)) / 2,
+                            "read x, write y (io dtype), write rstd"),
+        "qknorm_rope_bwd": ("hbm", ((rows_q + rows_k) * (hd * (4 + 2 * io) + 4)) / 2,
+                            "read fp32 dy, read x, write dx (io dtype), read rstd"),
+    }
+
+
+def traffic_for(kernel, w):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel source for this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(ATTN_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel") != kernel or t.get("workload") != w.name or t.get("source_sha256") != sha:
+        return None
+    scale = t["copy_scale"]
+    return (t["fetch_kib_per_dispatch"] / scale["fetch"] +
+            t["write_kib_per_dispatch"] / scale["write"]) * 1024.0
+
+
+def cpu_baseline(w, x, budget_s=10.0):
+    """The CPU oracle on a bounded sample of the workload: whole KV-head groups (a KV
+    head with its query heads: prologue + attention forward + backward), taken in order
+    until about `budget_s` seconds of CPU work or the whole workload is done."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in info}))
+    except Exception:  # threadpoolctl missing: report the affinity set
+        threads, blas = len(os.sched_getaffinity(0)), "unknown"
+    g = w.group
+    sub = w.replace(batch=1, num_heads=g, num_kv_heads=1)
+    done, dt = 0, 0.0
+    for kv in range(w.bkv):
+        b, kvh = divmod(kv, w.num_kv_heads)
+        qs = [b * w.num_heads + kvh * g + r for r in range(g)]
+        xq, xk, v, do = x.xq[qs], x.xk[[kv]], x.v[[kv]], x.dout[qs]
+        t0 = time.perf_counter()
+        oracle.forward(xq, xk, v, x.gamma_q, x.gamma_k, g, 1, w.eps, w.theta)
+        oracle.backward(xq, xk, v, x.gamma_q, x.gamma_k, do, g, 1, w.eps, w.theta)
+        dt += time.perf_counter() - t0
+        done += 1
+        if dt >= budget_s:
+            break
+    flops = sub.attn_flops()["total"] * done
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"{done} of {w.bkv} KV-head groups (each a KV head with its {g} query "
+                       f"heads, S={w.seq_len}): float64 numpy oracle, prologue + attention "
+                       f"fwd + bwd, {dt:.1f} s, {flops / 1e9:.1f} GFLOP algorithmic"),
+            "seconds": dt, "blas": blas, "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for i in range(5):
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy {i}: {n} bytes read, {n} bytes written")
+    print(json.dumps({"copy_calibration_bytes": n, "dispatches": 5}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this path shards by "
+              "KV-head groups with no exchange besides a 2*hd-float dgamma all-reduce, and "
+              "no multi-GPU figure is produced.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import causal_gqa_attention_amd as X
+    import workloads as W
+    from causal_gqa_attention_amd.step import AttentionStep
+
+    w = W.WORKLOADS[args.workload]
+    log(f"workload {w}")
+    x = W.make_inputs(w)
+    torch.cuda.set_device(0)
+    step = AttentionStep(w.batch, w.seq_len, w.num_heads, w.num_kv_heads, w.head_dim, w.dtype,
+                         w.eps, w.theta).load(x.xq, x.xk, x.v, x.dout, x.gamma_q, x.gamma_k)
+    stream = torch.cuda.current_stream()
+    flops = w.attn_flops()
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    # timed region: K steps, bracketed by a synchronisation on both sides
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step.run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    value = flops["total"] / (ms * 1e-3) / 1e12
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}), "
+        f"{value:.1f} TFLOP/s")
+
+    # per-kernel durations: the same K steps again with library HIP events around every
+    # launch (recorded on the launch stream)
+    X.xattn_profile_start()
+    tp0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.run()
+    torch.cuda.synchronize()
+    prof = X.xattn_profile_stop()
+    prof_ms = (time.perf_counter() - tp0) * 1e3 / args.steps
+    units = kernel_units(w)
+    kernels = {}
+    for name, (n, tot) in prof.items():
+        avg = tot / max(n, 1)
+        k = {"launches_per_step": n / args.steps, "avg_ms": avg,
+             "ms_per_step": tot / args.steps}
+        if name in units:
+            bound, work, _ = units[name]
+            if bound == "mfma":
+                k["tflops"] = work / (avg * 1e-3) / 1e12
+            else:
+                k["gbs"] = work / (avg * 1e-3) / 1e9
+        kernels[name] = k
+    dom = max((n for n in kernels if n in units), key=lambda n: kernels[n]["ms_per_step"])
+    bound, work, what = units[dom]
+    avg_s = kernels[dom]["avg_ms"] * 1e-3
+    if bound == "mfma":
+        achieved, peak, unit = work / avg_s / 1e12, PEAK_TFLOPS[w.dtype], "TFLOP/s"
+    else:
+        achieved, peak, unit = work / avg_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    traffic = traffic_for(dom, w)
+    roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                "frac": achieved / peak, "traffic": traffic, "kernel": dom,
+                "work_per_launch": work, "work_basis": what}
+    log(f"kernels: " + ", ".join(f"{n} {k['avg_ms']:.3f} ms x{k['launches_per_step']:.0f}"
+                                  for n, k in kernels.items()))
+    attn_ms = sum(kernels[n]["ms_per_step"] for n in ("attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv")
+                  if n in kernels)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(w, x)
+        log(f"cpu baseline {cpu['value'] * 1e3:.2f} GFLOP/s in {cpu['seconds']:.1f} s")
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len,
+                   "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "io_dtype": w.dtype, "parallelism": "none (1 GPU)"},
+        "pct_of_peak": 100.0 * value / PEAK_TFLOPS[w.dtype],
+        "attention_kernels_tflops": flops["total"] / (attn_ms * 1e-3) / 1e12 if attn_ms else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "profiled_ms_per_step": prof_ms,
+        "flop_per_step": flops["total"],
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

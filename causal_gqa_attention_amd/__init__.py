@@ -22,7 +22,8 @@ __all__ = [
     "XattnError", "library_path", "load_library",
     "xattn_rope_cache", "xattn_qknorm_rope_fwd", "xattn_qknorm_rope_bwd_workspace_bytes",
     "xattn_qknorm_rope_bwd", "xattn_fwd", "xattn_bwd_workspace_bytes", "xattn_bwd",
-    "xattn_status_string", "xattn_last_error", "xattn_version",
+    "xattn_status_string", "xattn_last_error", "xattn_version", "xattn_profile_start",
+    "xattn_profile_stop",
     "rope_cache", "qknorm_rope_fwd", "qknorm_rope_bwd", "attn_fwd", "attn_bwd",
 ]
 
@@ -38,6 +39,11 @@ class XattnError(RuntimeError):
     def __init__(self, status: int, where: str, detail: str):
         self.status = status
         super().__init__(f"{where}: status {status} ({detail})")
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double)]
 
 
 class Dims(ctypes.Structure):
@@ -80,6 +86,8 @@ def load_library() -> ctypes.CDLL:
         "xattn_bwd_workspace_bytes": (sz, [ctypes.POINTER(Dims), ctypes.c_int]),
         "xattn_bwd": (i32, [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                             ctypes.POINTER(Prologue), vp, sz, vp]),
+        "xattn_profile_start": (i32, []),
+        "xattn_profile_stop": (i32, [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]),
         "xattn_status_string": (ctypes.c_char_p, [i32]),
         "xattn_last_error": (ctypes.c_char_p, []),
         "xattn_version": (ctypes.c_char_p, []),
@@ -143,6 +151,20 @@ def xattn_status_string(status: int) -> str:
 
 def xattn_last_error() -> str:
     return load_library().xattn_last_error().decode()
+
+
+def xattn_profile_start():
+    _check(load_library().xattn_profile_start(), "xattn_profile_start")
+
+
+def xattn_profile_stop(max_entries: int = 32) -> dict:
+    """Returns {kernel name: (launches, total milliseconds)} in first-launch order."""
+    entries = (KernelTime * max_entries)()
+    n = ctypes.c_int32(0)
+    _check(load_library().xattn_profile_stop(entries, max_entries, ctypes.byref(n)),
+           "xattn_profile_stop")
+    return {entries[i].name.decode(): (int(entries[i].launches), float(entries[i].total_ms))
+            for i in range(min(n.value, max_entries))}
 
 
 def xattn_rope_cache(cos_tab, sin_tab, seq_len, head_dim, theta, stream=None):

@@ -459,6 +459,7 @@ template <typename T, int HD>
 static hipError_t fwd_impl(const AttnShape& s, const void* q, const void* k, const void* v,
                            void* out, float* lse, hipStream_t stream) {
   const dim3 grid(s.batch * s.num_heads, (s.seq_len + kBlockM - 1) / kBlockM);
+  ProfScope prof("attn_fwd", stream);
   hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(256), 0, stream, (const T*)q,
                      (const T*)k, (const T*)v, (T*)out, lse, s.seq_len, s.num_heads,
                      s.num_kv_heads, scale_of(HD) * kLog2e);
@@ -497,6 +498,7 @@ static void launch_dkdv(const AttnShape& s, const void* q, const void* k, const 
                         void* dv, hipStream_t stream) {
   constexpr int BNK = 32 * (kWaves / QS);
   const dim3 grid(s.batch * s.num_kv_heads, (s.seq_len + BNK - 1) / BNK);
+  ProfScope prof("attn_bwd_dkdv", stream);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD, TG, QS>), grid, dim3(256), 0, stream,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta,
                      (TG*)dk, (T*)dv, s.seq_len, s.num_heads, s.num_kv_heads,
@@ -508,10 +510,13 @@ static hipError_t bwd_impl(const AttnShape& s, const void* q, const void* k, con
                            const void* out, const float* lse, const void* dout, void* dq,
                            void* dk, void* dv, float* delta, hipStream_t stream) {
   const dim3 grid(s.batch * s.num_heads, (s.seq_len + kBlockM - 1) / kBlockM);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD, TG>), grid, dim3(256), 0, stream,
-                     (const T*)q, (const T*)k, (const T*)v, (const T*)out, (const T*)dout, lse,
-                     delta, (TG*)dq, s.seq_len, s.num_heads, s.num_kv_heads,
-                     scale_of(HD) * kLog2e, scale_of(HD));
+  {
+    ProfScope prof("attn_bwd_dq", stream);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD, TG>), grid, dim3(256), 0, stream,
+                       (const T*)q, (const T*)k, (const T*)v, (const T*)out, (const T*)dout,
+                       lse, delta, (TG*)dq, s.seq_len, s.num_heads, s.num_kv_heads,
+                       scale_of(HD) * kLog2e, scale_of(HD));
+  }
   hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess) return e;
   switch (dkdv_splits(s)) {

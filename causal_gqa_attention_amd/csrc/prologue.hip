@@ -36,6 +36,7 @@ __global__ void rope_cache_kernel(float* __restrict__ cos_tab, float* __restrict
 hipError_t launch_rope_cache(float* cos_tab, float* sin_tab, int seq_len, int head_dim,
                              double theta, hipStream_t stream) {
   const int n = seq_len * (head_dim / 2);
+  ProfScope prof("rope_cache", stream);
   hipLaunchKernelGGL(rope_cache_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, cos_tab,
                      sin_tab, seq_len, head_dim, theta);
   return hipPeekAtLastError();
@@ -123,6 +124,7 @@ static hipError_t fwd_dispatch(const void* x, const float* gamma, const float* c
   constexpr int LPR = (HD / 2) / V16<T>::n;
   const long long threads = (long long)nrows * LPR;
   const int blocks = (int)((threads + 255) / 256);
+  ProfScope prof("qknorm_rope_fwd", stream);
   hipLaunchKernelGGL((qknorm_rope_fwd_kernel<T, HD>), dim3(blocks), dim3(256), 0, stream,
                      (const T*)x, gamma, cos_tab, sin_tab, (T*)y, rstd, nrows, seq_len, eps);
   return hipPeekAtLastError();
@@ -260,13 +262,19 @@ static hipError_t bwd_dispatch(const void* dy, const void* x, const float* gamma
                                int seq_len, hipStream_t stream) {
   const int nb = qknorm_rope_bwd_blocks(nrows);
   const int rpb = (nrows + nb - 1) / nb;
-  hipLaunchKernelGGL((qknorm_rope_bwd_kernel<TDy, TX, HD>), dim3(nb), dim3(256), 0, stream,
-                     (const TDy*)dy, (const TX*)x, gamma, rstd, cos_tab, sin_tab, (TX*)dx,
-                     partials, nrows, seq_len, rpb);
+  {
+    ProfScope prof("qknorm_rope_bwd", stream);
+    hipLaunchKernelGGL((qknorm_rope_bwd_kernel<TDy, TX, HD>), dim3(nb), dim3(256), 0, stream,
+                       (const TDy*)dy, (const TX*)x, gamma, rstd, cos_tab, sin_tab, (TX*)dx,
+                       partials, nrows, seq_len, rpb);
+  }
   hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dgamma_reduce_kernel, dim3((HD + 3) / 4), dim3(256), 0, stream,
-                     (const float*)partials, dgamma, nb, HD);
+  {
+    ProfScope prof("dgamma_reduce", stream);
+    hipLaunchKernelGGL(dgamma_reduce_kernel, dim3((HD + 3) / 4), dim3(256), 0, stream,
+                       (const float*)partials, dgamma, nb, HD);
+  }
   return hipPeekAtLastError();
 }
 

@@ -12,6 +12,7 @@
 #include <cstring>
 #include <initializer_list>
 #include <string>
+#include <vector>
 
 #include "../../include/xattn.h"
 #include "xattn_internal.h"
@@ -164,6 +165,35 @@ const char* xattn_status_string(xattn_status s) {
 }
 
 const char* xattn_last_error(void) { return g_last_error.c_str(); }
+
+xattn_status xattn_profile_start(void) {
+  return guarded([&] { xattn::profile_start(); });
+}
+
+xattn_status xattn_profile_stop(xattn_kernel_time* entries, int32_t max_entries,
+                                int32_t* n_entries) {
+  return guarded([&] {
+    if (n_entries == nullptr) fail(XATTN_ERR_INVALID_ARG, "n_entries is NULL");
+    if (max_entries < 0 || (max_entries > 0 && entries == nullptr))
+      fail(XATTN_ERR_INVALID_ARG, "entries must hold max_entries >= 0 records");
+    struct Name {
+      char s[48];
+    };
+    std::vector<Name> names(max_entries > 0 ? max_entries : 1);
+    std::vector<long long> launches(names.size());
+    std::vector<double> ms(names.size());
+    hipError_t err = hipSuccess;
+    const int n = xattn::profile_stop(reinterpret_cast<char(*)[48]>(names.data()),
+                                      launches.data(), ms.data(), max_entries, &err);
+    for (int i = 0; i < n && i < max_entries; ++i) {
+      std::memcpy(entries[i].name, names[i].s, 48);
+      entries[i].launches = launches[i];
+      entries[i].total_ms = ms[i];
+    }
+    *n_entries = n;
+    hip_check(err, "profile event wait");
+  });
+}
 
 xattn_status xattn_rope_cache(float* cos_tab, float* sin_tab, int64_t seq_len,
                               int64_t head_dim, double theta, void* stream) {

@@ -38,11 +38,33 @@ struct AttnShape {
 hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const void* k,
                            const void* v, void* out, float* lse, hipStream_t stream);
 
-// dq_f32 / dk_f32: when true, dq / dk are written as fp32 (used when the prologue
-// backward follows inside xattn_bwd); otherwise in the io dtype.
+// grads_f32: when true, dq and dk are written as fp32 (used when the prologue backward
+// follows inside xattn_bwd); otherwise in the io dtype.  dv is always in the io dtype.
 hipError_t launch_attn_bwd(IoType io, const AttnShape& s, const void* q, const void* k,
                            const void* v, const void* out, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, float* delta,
                            bool grads_f32, hipStream_t stream);
+
+// ---- opt-in per-kernel event timing (see xattn_profile_start) ------------------------
+// Construct around each kernel launch: records a start event now and a stop event at
+// scope exit on `stream`, when timing is enabled.
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t stream);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  hipStream_t stream_;
+  const char* name_ = nullptr;
+  hipEvent_t start_ = nullptr, stop_ = nullptr;
+};
+
+void profile_start();
+// Waits for the recorded events, aggregates elapsed time per kernel name (in first-launch
+// order), disables timing.  Returns the number of distinct kernels (may exceed max_entries).
+int profile_stop(char (*names)[48], long long* launches, double* total_ms, int max_entries,
+                 hipError_t* err);
 
 }  // namespace xattn

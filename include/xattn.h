@@ -148,6 +148,24 @@ xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, con
                        void* dk, void* dv, const xattn_prologue* pro, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* ---- Instrumentation (no effect on results) ---------------------------------------------
+ * Per-kernel timing with HIP events: between xattn_profile_start and xattn_profile_stop,
+ * every kernel the library launches is bracketed by two events recorded on its launch
+ * stream (process-wide, all threads).  xattn_profile_stop waits for those events, turns
+ * timing off and writes, in first-launch order, one entry per kernel name: the number of
+ * launches and their summed elapsed milliseconds.  Up to max_entries entries are written;
+ * *n_entries receives the number of distinct kernels.  Timing adds a few microseconds per
+ * launch while on and costs nothing measurable while off. */
+typedef struct {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} xattn_kernel_time;
+
+xattn_status xattn_profile_start(void);
+xattn_status xattn_profile_stop(xattn_kernel_time* entries, int32_t max_entries,
+                                int32_t* n_entries);
+
 /* Static description of a status code. */
 const char* xattn_status_string(xattn_status s);
 

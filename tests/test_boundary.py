@@ -33,7 +33,7 @@ def lib():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
     assert "gfx950" in X.xattn_version()
@@ -138,6 +138,15 @@ def test_bwd_workspace_and_validation(lib):
     pro.rstd_k = None
     assert f(ctypes.byref(d), *p[:9], ctypes.byref(pro), p[9], w1, None) == INVALID
     assert "rstd_k" in last(lib)
+
+
+def test_profile_stop_validation_and_empty_session(lib):
+    n = ctypes.c_int32(-1)
+    assert lib.xattn_profile_stop(None, 4, ctypes.byref(n)) == INVALID
+    assert lib.xattn_profile_stop(None, 0, None) == INVALID
+    # a session with no launches reports no kernels (no device work involved)
+    assert lib.xattn_profile_start() == OK
+    assert lib.xattn_profile_stop(None, 0, ctypes.byref(n)) == OK and n.value == 0
 
 
 def test_python_binding_fails_loudly_without_device_tensors():
