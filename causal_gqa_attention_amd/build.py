@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libxattn.so")
-SOURCES = ["attn.hip", "prologue.hip", "xattn_api.cpp", "profile.cpp"]
+SOURCES = ["attn.hip", "attn_bf16.hip", "prologue.hip", "xattn_api.cpp", "profile.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -468,6 +468,8 @@ static hipError_t fwd_impl(const AttnShape& s, const void* q, const void* k, con
 
 hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const void* k,
                            const void* v, void* out, float* lse, hipStream_t stream) {
+  if (io == IO_BF16 && fast_bf16_supported(s.head_dim))
+    return launch_attn_fwd_bf16_fast(s, q, k, v, out, lse, stream);
 #define XATTN_CASE(T, HD) \
   if (s.head_dim == HD) return fwd_impl<T, HD>(s, q, k, v, out, lse, stream);
   if (io == IO_F32) {
@@ -530,7 +532,10 @@ static hipError_t bwd_impl(const AttnShape& s, const void* q, const void* k, con
 hipError_t launch_attn_bwd(IoType io, const AttnShape& s, const void* q, const void* k,
                            const void* v, const void* out, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, float* delta,
-                           bool grads_f32, hipStream_t stream) {
+                           float* lse2, bool grads_f32, hipStream_t stream) {
+  if (io == IO_BF16 && fast_bf16_supported(s.head_dim))
+    return launch_attn_bwd_bf16_fast(s, q, k, v, out, lse, dout, dq, dk, dv, delta, lse2,
+                                     grads_f32, stream);
 #define XATTN_CASE(T, HD, TG)                                                          \
   if (s.head_dim == HD)                                                                \
     return bwd_impl<T, HD, TG>(s, q, k, v, out, lse, dout, dq, dk, dv, delta, stream);

@@ -137,7 +137,7 @@ DimsChecked check_dims(const xattn_dims* d) {
 }
 
 size_t bwd_workspace(const DimsChecked& c, bool with_prologue) {
-  size_t n = align256((size_t)c.rows_q * sizeof(float));  // delta
+  size_t n = 2 * align256((size_t)c.rows_q * sizeof(float));  // delta, lse * log2(e)
   if (with_prologue) {
     const int64_t rows_k = (int64_t)c.s.batch * c.s.num_kv_heads * c.s.seq_len;
     n += align256((size_t)c.q_elems * sizeof(float));      // dq w.r.t. the rotated q
@@ -354,10 +354,12 @@ xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, con
     char* ws = static_cast<char*>(workspace);
     float* delta = reinterpret_cast<float*>(ws);
     ws += align256((size_t)c.rows_q * sizeof(float));
+    float* lse2 = reinterpret_cast<float*>(ws);
+    ws += align256((size_t)c.rows_q * sizeof(float));
     const hipStream_t st = (hipStream_t)stream;
     if (pro == nullptr) {
       hip_check(xattn::launch_attn_bwd(c.io, c.s, q, k, v, out, lse, dout, dq, dk, dv, delta,
-                                       false, st),
+                                       lse2, false, st),
                 "attention backward launch");
       return;
     }
@@ -369,7 +371,7 @@ xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, con
     ws += align256((size_t)xattn::qknorm_rope_bwd_blocks(c.rows_q) * c.s.head_dim * sizeof(float));
     float* part_k = reinterpret_cast<float*>(ws);
     hip_check(xattn::launch_attn_bwd(c.io, c.s, q, k, v, out, lse, dout, dyq, dyk, dv, delta,
-                                     true, st),
+                                     lse2, true, st),
               "attention backward launch");
     hip_check(xattn::launch_qknorm_rope_bwd(xattn::IO_F32, c.io, c.s.head_dim, dyq, pro->xq,
                                             pro->gamma_q, pro->rstd_q, pro->cos_tab,

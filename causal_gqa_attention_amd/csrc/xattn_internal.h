@@ -38,12 +38,23 @@ struct AttnShape {
 hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const void* k,
                            const void* v, void* out, float* lse, hipStream_t stream);
 
+// gfx950 fast path (bf16 io, head_dim 64 or 128), attn_bf16.hip.  The backward also
+// writes lse2 = lse * log2(e) and delta per query row (workspace) for its dk/dv kernel.
+bool fast_bf16_supported(int head_dim);
+hipError_t launch_attn_fwd_bf16_fast(const AttnShape& s, const void* q, const void* k,
+                                     const void* v, void* out, float* lse, hipStream_t stream);
+hipError_t launch_attn_bwd_bf16_fast(const AttnShape& s, const void* q, const void* k,
+                                     const void* v, const void* out, const float* lse,
+                                     const void* dout, void* dq, void* dk, void* dv,
+                                     float* delta, float* lse2, bool grads_f32,
+                                     hipStream_t stream);
+
 // grads_f32: when true, dq and dk are written as fp32 (used when the prologue backward
 // follows inside xattn_bwd); otherwise in the io dtype.  dv is always in the io dtype.
 hipError_t launch_attn_bwd(IoType io, const AttnShape& s, const void* q, const void* k,
                            const void* v, const void* out, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, float* delta,
-                           bool grads_f32, hipStream_t stream);
+                           float* lse2, bool grads_f32, hipStream_t stream);
 
 // ---- opt-in per-kernel event timing (see xattn_profile_start) ------------------------
 // Construct around each kernel launch: records a start event now and a stop event at
