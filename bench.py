@@ -31,7 +31,7 @@ METRIC = "causal GQA attn fwd+bwd TFLOP/s (bf16) and % of MI355X MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X published dense MFMA peaks
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_bwd_dkdv_qwen3_long_gqa_bf16.json")
-ATTN_SRC = os.path.join(ROOT, "causal_gqa_attention_amd", "csrc", "attn.hip")
+CSRC = os.path.join(ROOT, "causal_gqa_attention_amd", "csrc")
 
 
 def log(msg):
@@ -75,9 +75,12 @@ def traffic_for(kernel, w):
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        with open(ATTN_SRC, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-    except (OSError, ValueError):
+        h = hashlib.sha256()
+        for name in t["source_files"]:
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+        sha = h.hexdigest()
+    except (OSError, ValueError, KeyError):
         return None
     if t.get("kernel") != kernel or t.get("workload") != w.name or t.get("source_sha256") != sha:
         return None

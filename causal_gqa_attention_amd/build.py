@@ -18,6 +18,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libxattn.so")
 SOURCES = ["attn.hip", "attn_bf16.hip", "prologue.hip", "xattn_api.cpp", "profile.cpp"]
+# Per-source extra flags.  attn_bf16.hip: MFMA results go to VGPRs (the score tiles are
+# consumed by VALU right away; AGPR results would need a copy per element).
+SOURCE_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -53,7 +56,8 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        jobs.append((obj, [hipcc, *flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj]))
+        extra = SOURCE_FLAGS.get(src, [])
+        jobs.append((obj, [hipcc, *flags, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]))
     with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
         outs = list(ex.map(lambda j: _run(j[1]), jobs))
     if verbose:

@@ -5,18 +5,30 @@
 // throughput:
 //
 //   * HBM -> LDS staging with gfx950 direct-to-LDS loads (global_load_lds_dwordx4): no
-//     register round trip, issued one or two tiles ahead so loads overlap the MFMA work.
-//     A wave-level load writes 64 x 16 contiguous bytes, so tile rows are unpadded and
-//     bank conflicts are avoided by XOR-swizzling the 16-byte chunks of each row.
+//     register round trip, issued one or two stages ahead so the loads overlap the MFMA
+//     work.  A wave-level load writes 64 x 16 contiguous bytes, so tile rows are unpadded
+//     and bank conflicts are avoided by XOR-swizzling the 16-byte chunks of each row.
+//   * The swizzle depends on the row modulo 16 only and satisfies swz(r + 8) = swz(r) ^ 2,
+//     so every LDS operand address is (a lane-constant value) XOR (a compile-time constant)
+//     plus a base.  Load addresses are per-lane 32-bit offsets from a wave-uniform base,
+//     fixed for the whole kernel.
 //   * One barrier per stage: the wait for this stage's loads (vmcnt), the barrier and an
 //     LDS-only acquire fence; no release fence (it would drain the prefetches).
+//   * Causal / sequence-end masking runs only on the few stages that straddle the diagonal
+//     or the sequence end: the stage loop is split into segments that call a masked or an
+//     unmasked instantiation of the step (no per-element selects in the steady state, and
+//     no branch merge inside a loop, which would make the register allocator copy every
+//     live accumulator).
+//   * Stage buffers are picked at run time; with the swizzle above a lane's LDS address is
+//     (lane base | buffer base) ^ constant, one ALU operation per operand read.
 //   * Forward softmax rescales the output accumulator only when the running max grows by
 //     more than 2^8 (exact: numerator and denominator use the same reference max).
 //   * dk/dv: when the KV tiles are too few to fill the machine, each wave of a workgroup
 //     streams its own interleaved query tiles through private LDS buffers (no barriers in
 //     the main loop); the four partial dK/dV are added in wave order at the end.
-//   * Work is mapped to blocks so that the blocks of one KV head land on one XCD (its L2),
-//     heaviest causal tiles first.
+//   * Blocks of one KV head are mapped to one XCD (its L2), heaviest causal tiles first.
+#include <type_traits>
+
 #include "xattn_device.h"
 #include "xattn_internal.h"
 
@@ -24,22 +36,87 @@ namespace xattn {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-// XOR swizzle of the 16-byte chunks of a bf16 row of HD elements.  For HD = 128 the 16
-// rows read together by a 16-lane LDS phase get 16 distinct chunk positions, and the four
-// rows read by a transposing read phase get disjoint 64-byte windows; HD = 64 (two rows per
-// 256-byte bank window) is arranged the same way.
+// Swizzled bf16 tile rows of HD elements (ROWB bytes): physical 16-byte chunk =
+// logical chunk ^ swz(row).  For HD = 128 the 16 rows read together by one LDS phase of
+// row reads land on 16 distinct chunk positions and the four rows of one transposing
+// read phase on disjoint 64-byte windows; HD = 64 (two rows per 256-byte bank window) is
+// arranged the same way.
 template <int HD>
-struct Sw {
+struct Lay {
+  static constexpr int ROWB = 2 * HD;
   static constexpr int CPR = HD / 8;
-  __device__ static __forceinline__ int swz(int row) {
-    if constexpr (HD == 128) return 4 * (row & 3) + ((row >> 2) & 3);
-    else return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (HD == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+    else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
   }
-  __device__ static __forceinline__ int at(int row, int col) {
-    return row * HD + ((((col >> 3) ^ swz(row))) << 3) + (col & 7);
+  // Row reads: row R0 + lane%32 (R0 a multiple of 32), logical chunk 2c + lane/32 sits at
+  // byte R0*ROWB + (a_lane ^ (c << 5)).
+  __device__ static __forceinline__ uint32_t a_lane(int lane) {
+    const int r = lane & 31, h = lane >> 5;
+    return (uint32_t)(r * ROWB) | (uint32_t)((h ^ swz(r)) << 4);
+  }
+  // Transposing reads for the 8 k-slots (rows R0 + 16*c2 + 4h + {0..3} and +8 + {0..3})
+  // of column 32*dt + lane%32: the two reads sit at R0*ROWB + 16*c2*ROWB + (t_lane ^
+  // ((4*dt) << 4)) and R0*ROWB + (16*c2 + 8)*ROWB + (t_lane ^ ((4*dt ^ 2) << 4)).
+  __device__ static __forceinline__ uint32_t t_lane(int lane) {
+    const int g = lane >> 4, li = lane & 15, h = lane >> 5;
+    const int r = 4 * h + (li >> 2);
+    return (uint32_t)(r * ROWB) |
+           (uint32_t)(((2 * (g & 1) + ((li & 3) >> 1)) ^ swz(r)) << 4) |
+           (uint32_t)((li & 1) << 3);
   }
 };
+
+// Re-materialisation point for lane address bases: without it the compiler hoists every
+// (lane base ^ constant) out of the stage loop and keeps them all live in registers.
+__device__ __forceinline__ void rematerialize(uint32_t& a, uint32_t& b) {
+  asm volatile("" : "+v"(a), "+v"(b));
+}
+
+template <int HD>
+__device__ __forceinline__ bf16x8 lds_a(const char* base, uint32_t al, int c) {
+  return *reinterpret_cast<const bf16x8*>(base + (al ^ (uint32_t)(c << 5)));
+}
+
+template <int HD>
+__device__ __forceinline__ bf16x8 lds_t(const char* base, uint32_t tl, int c2, int dt) {
+  constexpr int ROWB = Lay<HD>::ROWB;
+  const char* p0 = base + 16 * c2 * ROWB + (tl ^ (uint32_t)((4 * dt) << 4));
+  const char* p1 = base + (16 * c2 + 8) * ROWB + (tl ^ (uint32_t)(((4 * dt) ^ 2) << 4));
+  const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p0));
+  const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p1));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// sum over hd of tile rows (base = row R0) with the lane's register fragment
+template <int HD>
+__device__ __forceinline__ f32x16 contract_rows(const char* base, uint32_t al,
+                                                const bf16x8 (&frag)[HD / 16]) {
+  f32x16 acc = zero16();
+#pragma unroll
+  for (int c = 0; c < HD / 16; ++c) acc = mfma_bf16(lds_a<HD>(base, al, c), frag[c], acc);
+  return acc;
+}
+
+// acc[dt] += (tile rows R0..R0+31, transposed) x (two packed 8-slot operands)
+template <int HD>
+__device__ __forceinline__ void acc_tr(f32x16 (&acc)[HD / 32], const char* base, uint32_t tl,
+                                       const bf16x8 (&pb)[2]) {
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt)
+      acc[dt] = mfma_bf16(lds_t<HD>(base, tl, c2, dt), pb[c2], acc[dt]);
+}
+
+__device__ __forceinline__ void pack16(bf16x8 (&pb)[2], const float (&v)[16]) {
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pb[c2][j] = (bf16)v[8 * c2 + j];
+}
 
 // s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt unconstrained).
 template <int N>
@@ -62,82 +139,50 @@ __device__ __forceinline__ void stage_wait_private() {
   lds_acquire();
 }
 
-// Direct HBM -> LDS copy of rows g0 .. g0+ROWS-1 of a [S, HD] bf16 matrix (rows past the
-// end re-read row S-1; callers mask them) into a swizzled tile, shared by NW waves.
+// Direct HBM -> LDS copy of ROWS rows of a [S, HD] bf16 matrix into a swizzled tile,
+// shared by NW waves.  Each lane's byte offsets within the source rows are fixed; a tile
+// that runs past the sequence end re-reads its last valid row (callers mask those rows).
 template <int HD, int ROWS, int NW>
-__device__ __forceinline__ void dma_rows(bf16* tile, const bf16* __restrict__ src, int g0,
-                                         int S, int wv, int lane) {
-  constexpr int CPR = HD / 8;
-  constexpr int PER = ROWS * CPR / (64 * NW);
-  static_assert(ROWS * CPR % (64 * NW) == 0, "tile must split into whole wave loads");
+struct Dma {
+  static constexpr int ROWB = 2 * HD;
+  static constexpr int PER = ROWS * (HD / 8) / (64 * NW);
+  static_assert(ROWS * (HD / 8) % (64 * NW) == 0, "tile must split into whole wave loads");
+  uint32_t off[PER];
+  __device__ __forceinline__ void init(int wv, int lane) {
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int p0 = (wv * PER + j) * 64;
-    const int p = p0 + lane;
-    const int row = p / CPR;
-    const int c = (p % CPR) ^ Sw<HD>::swz(row);
-    const int gr = min(g0 + row, S - 1);
-    __builtin_amdgcn_global_load_lds(src + (size_t)gr * HD + c * 8,
-                                     (lds_void_t*)(tile + p0 * 8), 16, 0, 0);
+    for (int j = 0; j < PER; ++j) {
+      const int p = (wv * PER + j) * 64 + lane;
+      const int row = p / (HD / 8);
+      const int c = (p % (HD / 8)) ^ Lay<HD>::swz(row);
+      off[j] = (uint32_t)(row * ROWB + c * 16);
+    }
   }
-}
+  // src: first row of the tile in global memory; nvalid: rows of it before the end.
+  __device__ __forceinline__ void issue(char* tile, const char* src, int wv, int nvalid) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      uint32_t o = off[j];
+      if (nvalid < ROWS) {
+        const int row = (int)(o / ROWB);
+        if (row >= nvalid) o -= (uint32_t)((row - nvalid + 1) * ROWB);
+      }
+      __builtin_amdgcn_global_load_lds(src + o, (lds_void_t*)(tile + (wv * PER + j) * 1024), 16,
+                                       0, 0);
+    }
+  }
+};
 
-// Per-query fp32 pair (lse2, delta) for 32 rows q0.. into LDS: [0,32) lse2, [32,64) delta.
-// NW waves share it: wave wv moves entries wv*64/NW .. with 4-byte loads.
+// (lse2, delta) of 32 query rows q0.. into LDS [0,32) and [32,64); NW waves share it.
 template <int NW>
-__device__ __forceinline__ void dma_rowstats(float* dst, const float* __restrict__ lse2,
-                                             const float* __restrict__ delta, int q0, int S,
-                                             int wv, int lane) {
+__device__ __forceinline__ void dma_rowstats(float* dst, const float* lse2,
+                                             const float* delta, int q0, int S, int wv,
+                                             int lane) {
   constexpr int PER = 64 / NW;
   if (lane < PER) {
     const int e = wv * PER + lane;
     const int r = min(q0 + (e & 31), S - 1);
-    const float* src = (e < 32 ? lse2 : delta) + r;
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + wv * PER), 4, 0, 0);
-  }
-}
-
-template <int HD>
-__device__ __forceinline__ bf16x8 lds_rows_a(const bf16* tile, int row0, int c, int lane) {
-  const int row = row0 + (lane & 31);
-  return *reinterpret_cast<const bf16x8*>(
-      tile + row * HD + (((2 * c + (lane >> 5)) ^ Sw<HD>::swz(row)) << 3));
-}
-
-// sum over hd of tile rows row0..row0+31 (A) with the lane's register fragment (B)
-template <int HD>
-__device__ __forceinline__ f32x16 contract_rows(const bf16* tile, int row0,
-                                                const bf16x8 (&frag)[HD / 16], int lane) {
-  f32x16 acc = zero16();
-#pragma unroll
-  for (int c = 0; c < HD / 16; ++c) acc = mfma_bf16(lds_rows_a<HD>(tile, row0, c, lane), frag[c], acc);
-  return acc;
-}
-
-// A operand contracted over the tile's row index: rows row0+16*c2+4h+{0..3, 8..11},
-// column 32*dt + (lane % 32).
-template <int HD>
-__device__ __forceinline__ bf16x8 lds_tr_a(const bf16* tile, int row0, int c2, int dt,
-                                           int lane) {
-  const int g = lane >> 4, li = lane & 15, h = lane >> 5;
-  const int row = row0 + 16 * c2 + 4 * h + (li >> 2);
-  const int col = 32 * dt + 16 * (g & 1) + 4 * (li & 3);
-  const bf16x4 lo = lds_read_tr16(tile + Sw<HD>::at(row, col));
-  const bf16x4 hi = lds_read_tr16(tile + Sw<HD>::at(row + 8, col));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-template <int HD>
-__device__ __forceinline__ void acc_tr(f32x16 (&acc)[HD / 32], const bf16* tile, int row0,
-                                       const float (&pv)[16], int lane) {
-#pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2) {
-    bf16x8 b;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = (bf16)pv[8 * c2 + j];
-#pragma unroll
-    for (int dt = 0; dt < HD / 32; ++dt)
-      acc[dt] = mfma_bf16(lds_tr_a<HD>(tile, row0, c2, dt, lane), b, acc[dt]);
+    __builtin_amdgcn_global_load_lds((e < 32 ? lse2 : delta) + r,
+                                     (lds_void_t*)(dst + wv * PER), 4, 0, 0);
   }
 }
 
@@ -200,12 +245,67 @@ __device__ __forceinline__ QMap map_qblock(int lin, int BH, int H, int Hkv, int 
   return m;
 }
 
+__device__ __forceinline__ void map_kvblock(int lin, int BKV, bool xcd, int& kvbh, int& kt) {
+  if (xcd) {
+    const int x = lin & 7, slot = lin >> 3, per = BKV / 8;
+    kt = slot / per;
+    kvbh = x + 8 * (slot % per);
+  } else {
+    kvbh = lin % BKV;
+    kt = lin / BKV;
+  }
+}
+
 constexpr int kBM = 128;  // queries per forward / dq block (4 waves x 32)
 constexpr int kBN = 64;   // keys per stage
 
 // ---------------------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------------------
+struct SoftmaxState {
+  float m, l;
+};
+
+// One 32-key sub-tile of the forward: scores st (keys x this lane's query), online softmax
+// update and O^T += V^T P^T.
+template <int HD, bool MASK>
+__device__ __forceinline__ void fwd_subtile(f32x16 (&o)[HD / 32], SoftmaxState& sm,
+                                            const f32x16& st, const char* vsub, uint32_t tl,
+                                            int kb, int qrow, int S, int h, float scale_log2) {
+  float sv[16];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float x = st[i];
+    if constexpr (MASK) {
+      const int key = kb + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (key > qrow || key >= S) x = -INFINITY;
+    }
+    sv[i] = x;
+    tmax = fmaxf(tmax, x);
+  }
+  tmax = fmaxf(tmax, shfl_xor(tmax, 32)) * scale_log2;
+  // rescale only when the reference max grows by more than 2^8
+  if (__any(tmax > sm.m + 8.f)) {
+    const float m_new = fmaxf(sm.m, tmax);
+    const float alpha = fast_exp2(sm.m - m_new);
+    sm.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt) o[dt] *= alpha;
+    sm.m = m_new;
+  }
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    sv[i] = fast_exp2(sv[i] * scale_log2 - sm.m);
+    psum += sv[i];
+  }
+  sm.l += psum;
+  bf16x8 pb[2];
+  pack16(pb, sv);
+  acc_tr<HD>(o, vsub, tl, pb);
+}
+
 template <int HD, int NBUF>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const bf16* __restrict__ q,
                                                      const bf16* __restrict__ k,
@@ -214,111 +314,117 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const bf16* __restrict__ q,
                                                      float* __restrict__ lse, int S, int H,
                                                      int Hkv, float scale_log2, int nqt,
                                                      int xcd) {
-  constexpr int TILE = kBN * HD;
-  constexpr int NL = 2 * (kBN * HD / 8) / 256;  // loads per wave per stage (K and V)
-  __shared__ __attribute__((aligned(1024))) bf16 lds[NBUF][2][TILE];
+  constexpr int ROWB = 2 * HD;
+  constexpr int TILEB = kBN * ROWB;
+  using D = Dma<HD, kBN, 4>;
+  constexpr int NL = 2 * D::PER;  // loads per wave per stage
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF * 2 * TILEB];
   const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int BH = gridDim.x / nqt;
   const QMap mp = map_qblock(blockIdx.x, BH, H, Hkv, nqt, xcd != 0);
   const int bh = mp.bh, b = bh / H, qh = bh - b * H;
   const int kvbh = b * Hkv + qh / (H / Hkv);
-  const bf16* kp = k + (size_t)kvbh * S * HD;
-  const bf16* vp = v + (size_t)kvbh * S * HD;
+  const char* kp = reinterpret_cast<const char*>(k + (size_t)kvbh * S * HD);
+  const char* vp = reinterpret_cast<const char*>(v + (size_t)kvbh * S * HD);
   const int q0 = mp.qt * kBM, qw0 = q0 + 32 * wv, qrow = qw0 + c32;
+  const uint32_t al = Lay<HD>::a_lane(lane), tl = Lay<HD>::t_lane(lane);
+  D dma;
+  dma.init(wv, lane);
 
   bf16x8 qf[HD / 16];
   load_frag<HD>(qf, q + (size_t)bh * S * HD, qrow, S, lane);
   f32x16 o[HD / 32];
 #pragma unroll
   for (int dt = 0; dt < HD / 32; ++dt) o[dt] = zero16();
-  float m_run = -INFINITY, l_run = 0.f;
+  SoftmaxState sm{-INFINITY, 0.f};
 
   const int ntiles = (min(S, q0 + kBM) + kBN - 1) / kBN;
+  auto issue = [&](int t, int buf) {
+    const int g0 = t * kBN, nv = S - g0;
+    dma.issue(lds + (2 * buf) * TILEB, kp + (size_t)g0 * ROWB, wv, nv);
+    dma.issue(lds + (2 * buf + 1) * TILEB, vp + (size_t)g0 * ROWB, wv, nv);
+  };
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t)
-    if (t < ntiles) {
-      dma_rows<HD, kBN, 4>(lds[t][0], kp, t * kBN, S, wv, lane);
-      dma_rows<HD, kBN, 4>(lds[t][1], vp, t * kBN, S, wv, lane);
-    }
-  for (int kt = 0; kt < ntiles; ++kt) {
-    if (NBUF > 2 && kt + 1 < ntiles) stage_barrier<(NBUF > 2 ? NL : 0)>();
+    if (t < ntiles) issue(t, t);
+  // Stage t: wait for its tile, prefetch stage t + NBUF - 1, then compute.  Stages below
+  // nplain lie strictly before the block's first query and inside the sequence, so no
+  // wave needs masking there; the few remaining (diagonal / ragged end) stages run the
+  // masked instantiation.
+  auto stage = [&](auto mask_tag, int t) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if (NBUF > 2 && t + 1 < ntiles) stage_barrier<(NBUF > 2 ? NL : 0)>();
     else stage_barrier<0>();
-    const int nxt = kt + NBUF - 1;
-    if (nxt < ntiles) {
-      dma_rows<HD, kBN, 4>(lds[nxt % NBUF][0], kp, nxt * kBN, S, wv, lane);
-      dma_rows<HD, kBN, 4>(lds[nxt % NBUF][1], vp, nxt * kBN, S, wv, lane);
-    }
-    const bf16* ks = lds[kt % NBUF][0];
-    const bf16* vs = lds[kt % NBUF][1];
-    const int k0 = kt * kBN;
+    if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
+    const int bb = t % NBUF;
+    const char* ks = lds + (2 * bb) * TILEB;
+    const char* vs = lds + (2 * bb + 1) * TILEB;
 #pragma unroll
     for (int s = 0; s < kBN / 32; ++s) {
-      const int kb = k0 + 32 * s;
-      if (kb > qw0 + 31 || kb >= S) break;  // wave-uniform
-      const f32x16 st = contract_rows<HD>(ks, 32 * s, qf, lane);
-      const bool edge = (kb + 31 > qw0) || (kb + 31 >= S);
-      float sv[16];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = st[i];
-        if (edge) {
-          const int key = kb + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (key > qrow || key >= S) x = -INFINITY;
-        }
-        sv[i] = x;
-        tmax = fmaxf(tmax, x);
-      }
-      tmax = fmaxf(tmax, shfl_xor(tmax, 32)) * scale_log2;
-      // rescale only when the reference max grows by more than 2^8
-      if (__any(tmax > m_run + 8.f)) {
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < HD / 32; ++dt) o[dt] *= alpha;
-        m_run = m_new;
-      }
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sv[i] = fast_exp2(sv[i] * scale_log2 - m_run);
-        psum += sv[i];
-      }
-      l_run += psum;
-      acc_tr<HD>(o, vs, 32 * s, sv, lane);
+      const int kb = t * kBN + 32 * s;
+      if (MASK && (kb > qw0 + 31 || kb >= S)) break;  // wave-uniform
+      const f32x16 st = contract_rows<HD>(ks + 32 * s * ROWB, al, qf);
+      fwd_subtile<HD, MASK>(o, sm, st, vs + 32 * s * ROWB, tl, kb, qrow, S, h, scale_log2);
     }
-  }
-  l_run += shfl_xor(l_run, 32);
+  };
+  const int nplain = min(q0 / kBN, S / kBN);
+  for (int t = 0; t < nplain; ++t) stage(std::false_type{}, t);
+  for (int t = nplain; t < ntiles; ++t) stage(std::true_type{}, t);
+  const float l = sm.l + shfl_xor(sm.l, 32);
   if (qrow < S) {
-    store_col<bf16, HD>(out + ((size_t)bh * S + qrow) * HD, o, 1.0f / l_run, h);
-    if (h == 0) lse[(size_t)bh * S + qrow] = (m_run + log2f(l_run)) * kLn2;
+    store_col<bf16, HD>(out + ((size_t)bh * S + qrow) * HD, o, 1.0f / l, h);
+    if (h == 0) lse[(size_t)bh * S + qrow] = (sm.m + log2f(l)) * kLn2;
   }
 }
 
 // ---------------------------------------------------------------------------------------
 // backward, dq (+ per-query delta = dO . out and lse2 = lse * log2 e for the dk/dv kernel)
 // ---------------------------------------------------------------------------------------
+template <int HD, bool MASK>
+__device__ __forceinline__ void dq_subtile(f32x16 (&acc)[HD / 32], const f32x16& st,
+                                           const f32x16& dpt, const char* ksub, uint32_t tl,
+                                           int kb, int qrow, int S, int h, float scale_log2,
+                                           float lse2, float D) {
+  float dsv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float p = fast_exp2(st[i] * scale_log2 - lse2);
+    if constexpr (MASK) {
+      const int key = kb + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (key > qrow || key >= S) p = 0.f;
+    }
+    dsv[i] = p * (dpt[i] - D);
+  }
+  bf16x8 db[2];
+  pack16(db, dsv);
+  acc_tr<HD>(acc, ksub, tl, db);  // dQ^T += K^T dS^T
+}
+
 template <int HD, int NBUF, typename TG>
 __global__ __launch_bounds__(256, 2) void dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ out, const bf16* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ lse2_out, float* __restrict__ delta, TG* __restrict__ dq, int S, int H,
     int Hkv, float scale_log2, float scale, int nqt, int xcd) {
-  constexpr int TILE = kBN * HD;
-  constexpr int NL = 2 * (kBN * HD / 8) / 256;
-  __shared__ __attribute__((aligned(1024))) bf16 lds[NBUF][2][TILE];
+  constexpr int ROWB = 2 * HD;
+  constexpr int TILEB = kBN * ROWB;
+  using D = Dma<HD, kBN, 4>;
+  constexpr int NL = 2 * D::PER;
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF * 2 * TILEB];
   const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int BH = gridDim.x / nqt;
   const QMap mp = map_qblock(blockIdx.x, BH, H, Hkv, nqt, xcd != 0);
   const int bh = mp.bh, b = bh / H, qh = bh - b * H;
   const int kvbh = b * Hkv + qh / (H / Hkv);
-  const bf16* kp = k + (size_t)kvbh * S * HD;
-  const bf16* vp = v + (size_t)kvbh * S * HD;
+  const char* kp = reinterpret_cast<const char*>(k + (size_t)kvbh * S * HD);
+  const char* vp = reinterpret_cast<const char*>(v + (size_t)kvbh * S * HD);
   const int q0 = mp.qt * kBM, qw0 = q0 + 32 * wv, qrow = qw0 + c32;
   const size_t hoff = (size_t)bh * S * HD;
+  uint32_t al = Lay<HD>::a_lane(lane), tl = Lay<HD>::t_lane(lane);
+  D dma;
+  dma.init(wv, lane);
 
   bf16x8 qf[HD / 16], df[HD / 16];
   load_frag<HD>(qf, q + hoff, qrow, S, lane);
@@ -332,10 +438,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) dsum += (float)df[c][j] * (float)of[c][j];
   }
-  const float D = dsum + shfl_xor(dsum, 32);
+  const float Dq = dsum + shfl_xor(dsum, 32);
   const float lse2 = qrow < S ? lse[(size_t)bh * S + qrow] * kLog2e : 0.f;
   if (qrow < S && h == 0) {
-    delta[(size_t)bh * S + qrow] = D;
+    delta[(size_t)bh * S + qrow] = Dq;
     lse2_out[(size_t)bh * S + qrow] = lse2;
   }
   f32x16 acc[HD / 32];
@@ -343,43 +449,35 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
   for (int dt = 0; dt < HD / 32; ++dt) acc[dt] = zero16();
 
   const int ntiles = (min(S, q0 + kBM) + kBN - 1) / kBN;
+  auto issue = [&](int t, int buf) {
+    const int g0 = t * kBN, nv = S - g0;
+    dma.issue(lds + (2 * buf) * TILEB, kp + (size_t)g0 * ROWB, wv, nv);
+    dma.issue(lds + (2 * buf + 1) * TILEB, vp + (size_t)g0 * ROWB, wv, nv);
+  };
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t)
-    if (t < ntiles) {
-      dma_rows<HD, kBN, 4>(lds[t][0], kp, t * kBN, S, wv, lane);
-      dma_rows<HD, kBN, 4>(lds[t][1], vp, t * kBN, S, wv, lane);
-    }
-  for (int kt = 0; kt < ntiles; ++kt) {
-    if (NBUF > 2 && kt + 1 < ntiles) stage_barrier<(NBUF > 2 ? NL : 0)>();
+    if (t < ntiles) issue(t, t);
+  auto stage = [&](auto mask_tag, int t) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if (NBUF > 2 && t + 1 < ntiles) stage_barrier<(NBUF > 2 ? NL : 0)>();
     else stage_barrier<0>();
-    const int nxt = kt + NBUF - 1;
-    if (nxt < ntiles) {
-      dma_rows<HD, kBN, 4>(lds[nxt % NBUF][0], kp, nxt * kBN, S, wv, lane);
-      dma_rows<HD, kBN, 4>(lds[nxt % NBUF][1], vp, nxt * kBN, S, wv, lane);
-    }
-    const bf16* ks = lds[kt % NBUF][0];
-    const bf16* vs = lds[kt % NBUF][1];
-    const int k0 = kt * kBN;
+    if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
+    const int bb = t % NBUF;
+    const char* ks = lds + (2 * bb) * TILEB;
+    const char* vs = lds + (2 * bb + 1) * TILEB;
 #pragma unroll
     for (int s = 0; s < kBN / 32; ++s) {
-      const int kb = k0 + 32 * s;
-      if (kb > qw0 + 31 || kb >= S) break;
-      const f32x16 st = contract_rows<HD>(ks, 32 * s, qf, lane);   // S^T
-      const f32x16 dpt = contract_rows<HD>(vs, 32 * s, df, lane);  // dP^T
-      const bool edge = (kb + 31 > qw0) || (kb + 31 >= S);
-      float dsv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(st[i] * scale_log2 - lse2);
-        if (edge) {
-          const int key = kb + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (key > qrow || key >= S) p = 0.f;
-        }
-        dsv[i] = p * (dpt[i] - D);
-      }
-      acc_tr<HD>(acc, ks, 32 * s, dsv, lane);  // dQ^T += K^T dS^T
+      const int kb = t * kBN + 32 * s;
+      if (MASK && (kb > qw0 + 31 || kb >= S)) break;
+      const f32x16 st = contract_rows<HD>(ks + 32 * s * ROWB, al, qf);   // S^T
+      const f32x16 dpt = contract_rows<HD>(vs + 32 * s * ROWB, al, df);  // dP^T
+      dq_subtile<HD, MASK>(acc, st, dpt, ks + 32 * s * ROWB, tl, kb, qrow, S, h, scale_log2,
+                           lse2, Dq);
     }
-  }
+  };
+  const int nplain = min(q0 / kBN, S / kBN);
+  for (int t = 0; t < nplain; ++t) stage(std::false_type{}, t);
+  for (int t = nplain; t < ntiles; ++t) stage(std::true_type{}, t);
   if (qrow < S) store_col<TG, HD>(dq + ((size_t)bh * S + qrow) * HD, acc, scale, h);
 }
 
@@ -389,36 +487,42 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
 constexpr int kBQ = 32;  // queries per dk/dv stage
 
 // One 32x32 (queries x keys) step of the dk/dv recurrence on a staged Q / dO tile.
-template <int HD>
+template <int HD, bool MASK>
 __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[HD / 32], f32x16 (&dvt)[HD / 32],
-                                          const bf16* qs, const bf16* dos, const float* stats,
+                                          const char* qs, const char* dos, const float* stats,
                                           const bf16x8 (&kf)[HD / 16],
-                                          const bf16x8 (&vf)[HD / 16], int q0, int key,
-                                          int kw0, int S, float scale_log2, int lane) {
-  const int h = lane >> 5;
-  const f32x16 st = contract_rows<HD>(qs, 0, kf, lane);    // S: queries x keys
-  const f32x16 dpt = contract_rows<HD>(dos, 0, vf, lane);  // dP
-  const bool edge = (q0 < kw0 + 31) || (q0 + kBQ > S);
-  float pv[16], dsv[16];
+                                          const bf16x8 (&vf)[HD / 16], uint32_t al,
+                                          uint32_t tl, int q0, int key, int S,
+                                          float scale_log2, int h) {
+  const f32x16 st = contract_rows<HD>(qs, al, kf);    // S: queries x keys
+  float pv[16];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const int m0 = 8 * g + 4 * h;
-    const f32x4 l2 = *reinterpret_cast<const f32x4*>(stats + m0);
-    const f32x4 dd = *reinterpret_cast<const f32x4*>(stats + 32 + m0);
+    const f32x4 l2 = *reinterpret_cast<const f32x4*>(stats + 8 * g + 4 * h);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int i = 4 * g + j;
-      float p = fast_exp2(st[i] * scale_log2 - l2[j]);
-      if (edge) {
-        const int qi = q0 + m0 + j;
+      float p = fast_exp2(st[4 * g + j] * scale_log2 - l2[j]);
+      if constexpr (MASK) {
+        const int qi = q0 + 8 * g + 4 * h + j;
         if (qi < key || qi >= S) p = 0.f;
       }
-      pv[i] = p;
-      dsv[i] = p * (dpt[i] - dd[j]);
+      pv[4 * g + j] = p;
     }
   }
-  acc_tr<HD>(dvt, dos, 0, pv, lane);  // dV^T += dO^T P
-  acc_tr<HD>(dkt, qs, 0, dsv, lane);  // dK^T += Q^T dS
+  bf16x8 pb[2];
+  pack16(pb, pv);
+  const f32x16 dpt = contract_rows<HD>(dos, al, vf);  // dP
+  float dsv[16];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 dd = *reinterpret_cast<const f32x4*>(stats + 32 + 8 * g + 4 * h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dsv[4 * g + j] = pv[4 * g + j] * (dpt[4 * g + j] - dd[j]);
+  }
+  bf16x8 db[2];
+  pack16(db, dsv);
+  acc_tr<HD>(dvt, dos, tl, pb);  // dV^T += dO^T P
+  acc_tr<HD>(dkt, qs, tl, db);   // dK^T += Q^T dS
 }
 
 // Shared variant: 4 waves own 128 consecutive keys of one KV head and share each staged
@@ -429,24 +533,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_shared_kernel(
     const bf16* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ delta, TG* __restrict__ dk, bf16* __restrict__ dv, int S, int H,
     int Hkv, float scale_log2, float scale, int nkt, int xcd) {
-  constexpr int TILE = kBQ * HD;
-  constexpr int NL = 2 * (kBQ * HD / 8) / 256 + 1;
-  __shared__ __attribute__((aligned(1024))) bf16 lds[NBUF][2][TILE];
+  constexpr int ROWB = 2 * HD;
+  constexpr int TILEB = kBQ * ROWB;
+  using D = Dma<HD, kBQ, 4>;
+  constexpr int NL = 2 * D::PER + 1;
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF * 2 * TILEB];
   __shared__ __attribute__((aligned(16))) float stats[NBUF][64];
   const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int BKV = gridDim.x / nkt;
   int kvbh, kt;
-  if (xcd) {
-    const int lin = blockIdx.x, x = lin & 7, slot = lin >> 3, per = BKV / 8;
-    kt = slot / per;
-    kvbh = x + 8 * (slot % per);
-  } else {
-    kvbh = blockIdx.x % BKV;
-    kt = blockIdx.x / BKV;
-  }
+  map_kvblock(blockIdx.x, gridDim.x / nkt, xcd != 0, kvbh, kt);
   const int b = kvbh / Hkv, kvh = kvbh - b * Hkv, group = H / Hkv;
   const int k0 = kt * 128, kw0 = k0 + 32 * wv, key = kw0 + c32;
+  const uint32_t al = Lay<HD>::a_lane(lane), tl = Lay<HD>::t_lane(lane);
+  D dma;
+  dma.init(wv, lane);
   bf16x8 kf[HD / 16], vf[HD / 16];
   load_frag<HD>(kf, k + (size_t)kvbh * S * HD, key, S, lane);
   load_frag<HD>(vf, v + (size_t)kvbh * S * HD, key, S, lane);
@@ -459,23 +560,39 @@ __global__ __launch_bounds__(256, 1) void dkdv_shared_kernel(
   const int nst = group * per_r;
   auto issue = [&](int t, int buf) {
     const int r = t / per_r, qt = qt_first + t % per_r;
-    const int bh = b * H + kvh * group + r;
-    dma_rows<HD, kBQ, 4>(lds[buf][0], q + (size_t)bh * S * HD, qt * kBQ, S, wv, lane);
-    dma_rows<HD, kBQ, 4>(lds[buf][1], dout + (size_t)bh * S * HD, qt * kBQ, S, wv, lane);
-    dma_rowstats<4>(stats[buf], lse2 + (size_t)bh * S, delta + (size_t)bh * S, qt * kBQ, S,
-                    wv, lane);
+    const size_t bh = (size_t)(b * H + kvh * group + r);
+    const int g0 = qt * kBQ, nv = S - g0;
+    dma.issue(lds + (2 * buf) * TILEB, reinterpret_cast<const char*>(q + (bh * S + g0) * HD),
+              wv, nv);
+    dma.issue(lds + (2 * buf + 1) * TILEB,
+              reinterpret_cast<const char*>(dout + (bh * S + g0) * HD), wv, nv);
+    dma_rowstats<4>(stats[buf], lse2 + bh * S, delta + bh * S, g0, S, wv, lane);
   };
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t)
     if (t < nst) issue(t, t);
-  for (int t = 0; t < nst; ++t) {
+  const bool live = kw0 < S;
+  auto stage = [&](auto mask_tag, int t) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     if (NBUF > 2 && t + 1 < nst) stage_barrier<(NBUF > 2 ? NL : 0)>();
     else stage_barrier<0>();
     if (t + NBUF - 1 < nst) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
+    const int bb = t % NBUF;
     const int q0 = (qt_first + t % per_r) * kBQ;
-    if (kw0 < S && q0 + kBQ - 1 >= kw0)
-      dkdv_step<HD>(dkt, dvt, lds[t % NBUF][0], lds[t % NBUF][1], stats[t % NBUF], kf, vf, q0,
-                    key, kw0, S, scale_log2, lane);
+    if (live && q0 + kBQ - 1 >= kw0)
+      dkdv_step<HD, MASK>(dkt, dvt, lds + (2 * bb) * TILEB, lds + (2 * bb + 1) * TILEB,
+                          stats[bb], kf, vf, al, tl, q0, key, S, scale_log2, h);
+  };
+  // Per query head: the first four query tiles straddle the diagonal of some wave's keys
+  // and a ragged last tile runs past the sequence end; the rest need no masking.
+  const bool ragged = (S % kBQ) != 0;
+  const int nmask_head = min(4, per_r);
+  const int plain_end = per_r - ((ragged && per_r > nmask_head) ? 1 : 0);
+  for (int r = 0; r < group; ++r) {
+    const int t0 = r * per_r;
+    for (int i = 0; i < nmask_head; ++i) stage(std::true_type{}, t0 + i);
+    for (int i = nmask_head; i < plain_end; ++i) stage(std::false_type{}, t0 + i);
+    if (plain_end < per_r) stage(std::true_type{}, t0 + per_r - 1);
   }
   if (key < S) {
     store_col<TG, HD>(dk + ((size_t)kvbh * S + key) * HD, dkt, scale, h);
@@ -492,24 +609,23 @@ __global__ __launch_bounds__(256, 1) void dkdv_private_kernel(
     const bf16* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ delta, TG* __restrict__ dk, bf16* __restrict__ dv, int S, int H,
     int Hkv, float scale_log2, float scale, int nkt, int xcd) {
-  constexpr int TILE = kBQ * HD;
-  constexpr int NL = 2 * (kBQ * HD / 8) / 64 + 1;
-  __shared__ __attribute__((aligned(1024))) bf16 lds[4][NBUF][2][TILE];
+  constexpr int ROWB = 2 * HD;
+  constexpr int TILEB = kBQ * ROWB;
+  constexpr int WAVEB = NBUF * 2 * TILEB;  // one wave's staging bytes
+  using D = Dma<HD, kBQ, 1>;
+  constexpr int NL = 2 * D::PER + 1;
+  __shared__ __attribute__((aligned(1024))) char lds[4 * WAVEB];
   __shared__ __attribute__((aligned(16))) float stats[4][NBUF][64];
   const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int BKV = gridDim.x / nkt;
   int kvbh, kt;
-  if (xcd) {
-    const int lin = blockIdx.x, x = lin & 7, slot = lin >> 3, per = BKV / 8;
-    kt = slot / per;
-    kvbh = x + 8 * (slot % per);
-  } else {
-    kvbh = blockIdx.x % BKV;
-    kt = blockIdx.x / BKV;
-  }
+  map_kvblock(blockIdx.x, gridDim.x / nkt, xcd != 0, kvbh, kt);
   const int b = kvbh / Hkv, kvh = kvbh - b * Hkv, group = H / Hkv;
   const int kw0 = kt * 32, key = kw0 + c32;
+  const uint32_t al = Lay<HD>::a_lane(lane), tl = Lay<HD>::t_lane(lane);
+  D dma;
+  dma.init(0, lane);
+  char* mine = lds + wv * WAVEB;
   bf16x8 kf[HD / 16], vf[HD / 16];
   load_frag<HD>(kf, k + (size_t)kvbh * S * HD, key, S, lane);
   load_frag<HD>(vf, v + (size_t)kvbh * S * HD, key, S, lane);
@@ -522,26 +638,43 @@ __global__ __launch_bounds__(256, 1) void dkdv_private_kernel(
   const int nst = group * per_r;
   auto issue = [&](int t, int buf) {
     const int r = t / per_r, qt = qt_first + wv + 4 * (t % per_r);
-    const int bh = b * H + kvh * group + r;
-    dma_rows<HD, kBQ, 1>(lds[wv][buf][0], q + (size_t)bh * S * HD, qt * kBQ, S, 0, lane);
-    dma_rows<HD, kBQ, 1>(lds[wv][buf][1], dout + (size_t)bh * S * HD, qt * kBQ, S, 0, lane);
-    dma_rowstats<1>(stats[wv][buf], lse2 + (size_t)bh * S, delta + (size_t)bh * S, qt * kBQ,
-                    S, 0, lane);
+    const size_t bh = (size_t)(b * H + kvh * group + r);
+    const int g0 = qt * kBQ, nv = S - g0;
+    dma.issue(mine + (2 * buf) * TILEB, reinterpret_cast<const char*>(q + (bh * S + g0) * HD), 0,
+              nv);
+    dma.issue(mine + (2 * buf + 1) * TILEB,
+              reinterpret_cast<const char*>(dout + (bh * S + g0) * HD), 0, nv);
+    dma_rowstats<1>(stats[wv][buf], lse2 + bh * S, delta + bh * S, g0, S, 0, lane);
   };
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t)
     if (t < nst) issue(t, t);
-  for (int t = 0; t < nst; ++t) {
+  auto stage = [&](auto mask_tag, int t) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     if (NBUF > 2 && t + 1 < nst) stage_wait_private<(NBUF > 2 ? NL : 0)>();
     else stage_wait_private<0>();
     if (t + NBUF - 1 < nst) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
+    const int bb = t % NBUF;
     const int q0 = (qt_first + wv + 4 * (t % per_r)) * kBQ;
-    dkdv_step<HD>(dkt, dvt, lds[wv][t % NBUF][0], lds[wv][t % NBUF][1], stats[wv][t % NBUF],
-                  kf, vf, q0, key, kw0, S, scale_log2, lane);
+    dkdv_step<HD, MASK>(dkt, dvt, mine + (2 * bb) * TILEB, mine + (2 * bb + 1) * TILEB,
+                        stats[wv][bb], kf, vf, al, tl, q0, key, S, scale_log2, h);
+  };
+  // Per query head: only wave 0's first tile meets the diagonal (its keys start at its
+  // first query), and a ragged last tile runs past the sequence end.
+  if (per_r > 0) {
+    const int first_mask = (wv == 0) ? 1 : 0;
+    const int last_qt = qt_first + wv + 4 * (per_r - 1);
+    const int last_mask = ((S % kBQ) != 0 && last_qt == nqt - 1 && per_r > first_mask) ? 1 : 0;
+    for (int r = 0; r < group; ++r) {
+      const int t0 = r * per_r;
+      if (first_mask) stage(std::true_type{}, t0);
+      for (int i = first_mask; i < per_r - last_mask; ++i) stage(std::false_type{}, t0 + i);
+      if (last_mask) stage(std::true_type{}, t0 + per_r - 1);
+    }
   }
 
   // wave-ordered combination of the four partials, one 32-row tile of one tensor at a time
-  float* red = reinterpret_cast<float*>(&lds[0][0][0][0]);
+  float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
 #pragma unroll
