@@ -100,6 +100,23 @@ __device__ __forceinline__ f32x16 contract_rows(const char* base, uint32_t al,
   return acc;
 }
 
+// sum over hd of (rows of tile A) x (rows of tile B), both from LDS; every operand read is
+// issued before the MFMA chain so the chain does not wait on LDS latency per step.
+template <int HD>
+__device__ __forceinline__ f32x16 contract_lds(const char* abase, const char* bbase,
+                                               uint32_t al) {
+  bf16x8 a[HD / 16], b[HD / 16];
+#pragma unroll
+  for (int c = 0; c < HD / 16; ++c) {
+    a[c] = lds_a<HD>(abase, al, c);
+    b[c] = lds_a<HD>(bbase, al, c);
+  }
+  f32x16 acc = zero16();
+#pragma unroll
+  for (int c = 0; c < HD / 16; ++c) acc = mfma_bf16(a[c], b[c], acc);
+  return acc;
+}
+
 // acc[dt] += (tile rows R0..R0+31, transposed) x (two packed 8-slot operands)
 template <int HD>
 __device__ __forceinline__ void acc_tr(f32x16 (&acc)[HD / 32], const char* base, uint32_t tl,
@@ -487,14 +504,18 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
 constexpr int kBQ = 32;  // queries per dk/dv stage
 
 // One 32x32 (queries x keys) step of the dk/dv recurrence on a staged Q / dO tile.
-template <int HD, bool MASK>
+// The K and V operands come either from register fragments (kvf = {kf, vf}) or, with
+// KV_LDS, from swizzled K / V tiles in LDS (kvt = {K tile, V tile}).
+template <int HD, bool MASK, bool KV_LDS>
 __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[HD / 32], f32x16 (&dvt)[HD / 32],
                                           const char* qs, const char* dos, const float* stats,
                                           const bf16x8 (&kf)[HD / 16],
-                                          const bf16x8 (&vf)[HD / 16], uint32_t al,
-                                          uint32_t tl, int q0, int key, int S,
-                                          float scale_log2, int h) {
-  const f32x16 st = contract_rows<HD>(qs, al, kf);    // S: queries x keys
+                                          const bf16x8 (&vf)[HD / 16], const char* kt_lds,
+                                          const char* vt_lds, uint32_t al, uint32_t tl, int q0,
+                                          int key, int S, float scale_log2, int h) {
+  f32x16 st;  // S: queries x keys
+  if constexpr (KV_LDS) st = contract_lds<HD>(qs, kt_lds, al);
+  else st = contract_rows<HD>(qs, al, kf);
   float pv[16];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -511,7 +532,9 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[HD / 32], f32x16 (&dvt)[
   }
   bf16x8 pb[2];
   pack16(pb, pv);
-  const f32x16 dpt = contract_rows<HD>(dos, al, vf);  // dP
+  f32x16 dpt;  // dP
+  if constexpr (KV_LDS) dpt = contract_lds<HD>(dos, vt_lds, al);
+  else dpt = contract_rows<HD>(dos, al, vf);
   float dsv[16];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -580,8 +603,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_shared_kernel(
     const int bb = t % NBUF;
     const int q0 = (qt_first + t % per_r) * kBQ;
     if (live && q0 + kBQ - 1 >= kw0)
-      dkdv_step<HD, MASK>(dkt, dvt, lds + (2 * bb) * TILEB, lds + (2 * bb + 1) * TILEB,
-                          stats[bb], kf, vf, al, tl, q0, key, S, scale_log2, h);
+      dkdv_step<HD, MASK, false>(dkt, dvt, lds + (2 * bb) * TILEB, lds + (2 * bb + 1) * TILEB,
+                                 stats[bb], kf, vf, nullptr, nullptr, al, tl, q0, key, S,
+                                 scale_log2, h);
   };
   // Per query head: the first four query tiles straddle the diagonal of some wave's keys
   // and a ragged last tile runs past the sequence end; the rest need no masking.
@@ -615,6 +639,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_private_kernel(
   using D = Dma<HD, kBQ, 1>;
   constexpr int NL = 2 * D::PER + 1;
   __shared__ __attribute__((aligned(1024))) char lds[4 * WAVEB];
+  __shared__ __attribute__((aligned(1024))) char kvt[2 * TILEB];  // the block's K, V rows
   __shared__ __attribute__((aligned(16))) float stats[4][NBUF][64];
   const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -626,9 +651,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_private_kernel(
   D dma;
   dma.init(0, lane);
   char* mine = lds + wv * WAVEB;
-  bf16x8 kf[HD / 16], vf[HD / 16];
-  load_frag<HD>(kf, k + (size_t)kvbh * S * HD, key, S, lane);
-  load_frag<HD>(vf, v + (size_t)kvbh * S * HD, key, S, lane);
+  {
+    // the four waves share the block's 32 K and V rows through LDS
+    Dma<HD, kBQ, 4> kvdma;
+    kvdma.init(wv, lane);
+    kvdma.issue(kvt, reinterpret_cast<const char*>(k + ((size_t)kvbh * S + kw0) * HD), wv,
+                S - kw0);
+    kvdma.issue(kvt + TILEB, reinterpret_cast<const char*>(v + ((size_t)kvbh * S + kw0) * HD),
+                wv, S - kw0);
+  }
+  bf16x8 kf[HD / 16], vf[HD / 16];  // unused: K and V are read from LDS
   f32x16 dkt[HD / 32], dvt[HD / 32];
 #pragma unroll
   for (int dt = 0; dt < HD / 32; ++dt) dkt[dt] = dvt[dt] = zero16();
@@ -649,6 +681,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_private_kernel(
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t)
     if (t < nst) issue(t, t);
+  wait_vm<0>();  // K / V rows (and the first stage) have landed
+  __builtin_amdgcn_s_barrier();
+  lds_acquire();
   auto stage = [&](auto mask_tag, int t) {
     constexpr bool MASK = decltype(mask_tag)::value;
     if (NBUF > 2 && t + 1 < nst) stage_wait_private<(NBUF > 2 ? NL : 0)>();
@@ -656,8 +691,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_private_kernel(
     if (t + NBUF - 1 < nst) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
     const int bb = t % NBUF;
     const int q0 = (qt_first + wv + 4 * (t % per_r)) * kBQ;
-    dkdv_step<HD, MASK>(dkt, dvt, mine + (2 * bb) * TILEB, mine + (2 * bb + 1) * TILEB,
-                        stats[wv][bb], kf, vf, al, tl, q0, key, S, scale_log2, h);
+    dkdv_step<HD, MASK, true>(dkt, dvt, mine + (2 * bb) * TILEB, mine + (2 * bb + 1) * TILEB,
+                              stats[wv][bb], kf, vf, kvt, kvt + TILEB, al, tl, q0, key, S,
+                              scale_log2, h);
   };
   // Per query head: only wave 0's first tile meets the diagonal (its keys start at its
   // first query), and a ragged last tile runs past the sequence end.
