@@ -88,6 +88,36 @@ def test_attention_matches_oracle(w):
     print(w.name, {k: f"{e:.2e}" for k, e in errs.items()})
 
 
+# Shapes whose dk/dv runs the shared-tile path (at least 1024 blocks of 128 keys).  The
+# first is small enough to compare every head; the second has 9 key tiles with a ragged
+# last one and is compared on sampled KV heads (first, last, middle) with all their
+# query heads.
+SHARED_PATH = [
+    (W.small_ragged("bf16", 128, 200, 128, 8, 4, theta=1e4, eps=1e-5, index=230), None),
+    (W.small_ragged("bf16", 64, 1100, 16, 8, 8, theta=1e6, eps=1e-6, index=231), 3),
+]
+
+
+@pytest.mark.parametrize("w,nkv", SHARED_PATH,
+                         ids=[f"hd{w.head_dim}_S{w.seq_len}_B{w.batch}_H{w.num_heads}_kv{w.num_kv_heads}"
+                              for w, _ in SHARED_PATH])
+def test_attention_shared_dkdv_path_matches_oracle(w, nkv):
+    assert w.bkv * -(-w.seq_len // 128) >= 1024
+    q, k, v, do = seeded_attention_inputs(w, 2000 + w.index)
+    note(f"attention (shared dk/dv path) {w}")
+    g = attention_only(w, q, k, v, do)
+    kvs = list(range(w.bkv)) if nkv is None else sampled_kv_heads(w, nkv)
+    qs = [h for kv in kvs for h in q_heads_of(w, kv)]
+    out, lse = oracle.attention_fwd(q, k, v, w.num_heads, w.num_kv_heads, heads=qs)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, w.num_heads, w.num_kv_heads, kv_heads=kvs)
+    tol = TOL[w.dtype]
+    lse_g = g["lse"].reshape(lse.shape)
+    errs = {n: assert_close(n, x[idx], r[idx], tol) for n, x, r, idx in
+            (("out", g["out"], out, qs), ("lse", lse_g, lse, qs), ("dq", g["dq"], dq, qs),
+             ("dk", g["dk"], dk, kvs), ("dv", g["dv"], dv, kvs))}
+    print(w.name, {k: f"{e:.2e}" for k, e in errs.items()})
+
+
 @pytest.mark.parametrize("idx", [3, 4, 5])
 def test_full_size_step_on_sampled_heads(idx):
     w = W.WORKLOADS[idx]
