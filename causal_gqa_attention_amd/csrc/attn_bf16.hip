@@ -4,14 +4,18 @@
 // xtrain "Phase T15: GQA" head mapping and deterministic group sum), restructured for
 // throughput:
 //
-//   * HBM -> LDS staging with gfx950 direct-to-LDS loads (global_load_lds_dwordx4): no
-//     register round trip, issued one or two stages ahead so the loads overlap the MFMA
-//     work.  A wave-level load writes 64 x 16 contiguous bytes, so tile rows are unpadded
-//     and bank conflicts are avoided by XOR-swizzling the 16-byte chunks of each row.
+//   * HBM -> LDS staging with direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): no
+//     register round trip, issued a stage or two ahead so the loads overlap the MFMA work.
+//     A wave-level load writes 64 x 16 contiguous bytes, so tile rows are unpadded and bank
+//     conflicts are avoided by XOR-swizzling the 16-byte chunks of each row.  Each tile gets
+//     a buffer descriptor that covers only its rows before the sequence end: the hardware
+//     range check fills the rest with zeros, so ragged tiles need no per-lane clamping.
+//   * The copies are inline assembly, invisible to the compiler's wait-count insertion
+//     (which would otherwise make every transposing LDS read wait for all loads in flight);
+//     the kernels order them against LDS reads with explicit vmcnt waits and barriers.
 //   * The swizzle depends on the row modulo 16 only and satisfies swz(r + 8) = swz(r) ^ 2,
 //     so every LDS operand address is (a lane-constant value) XOR (a compile-time constant)
-//     plus a base.  Load addresses are per-lane 32-bit offsets from a wave-uniform base,
-//     fixed for the whole kernel.
+//     plus a base.  Load addresses are per-lane 32-bit offsets, fixed for the whole kernel.
 //   * One barrier per stage: the wait for this stage's loads (vmcnt), the barrier and an
 //     LDS-only acquire fence; no release fence (it would drain the prefetches).
 //   * Causal / sequence-end masking runs only on the few stages that straddle the diagonal
@@ -19,13 +23,13 @@
 //     unmasked instantiation of the step (no per-element selects in the steady state, and
 //     no branch merge inside a loop, which would make the register allocator copy every
 //     live accumulator).
-//   * Stage buffers are picked at run time; with the swizzle above a lane's LDS address is
-//     (lane base | buffer base) ^ constant, one ALU operation per operand read.
 //   * Forward softmax rescales the output accumulator only when the running max grows by
 //     more than 2^8 (exact: numerator and denominator use the same reference max).
-//   * dk/dv: when the KV tiles are too few to fill the machine, each wave of a workgroup
-//     streams its own interleaved query tiles through private LDS buffers (no barriers in
-//     the main loop); the four partial dK/dV are added in wave order at the end.
+//   * dk/dv keep the lane's K and V rows in registers and read the step's LDS operands in
+//     groups ahead of their MFMAs.  When the KV tiles are too few to fill the machine, each
+//     wave of a workgroup streams its own interleaved query tiles through private LDS
+//     buffers (no barriers in the main loop); the four partial dK/dV are added in wave
+//     order at the end.
 //   * Blocks of one KV head are mapped to one XCD (its L2), heaviest causal tiles first.
 #include <type_traits>
 
@@ -37,6 +41,7 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 // Swizzled bf16 tile rows of HD elements (ROWB bytes): physical 16-byte chunk =
 // logical chunk ^ swz(row).  For HD = 128 the 16 rows read together by one LDS phase of
@@ -69,12 +74,6 @@ struct Lay {
   }
 };
 
-// Re-materialisation point for lane address bases: without it the compiler hoists every
-// (lane base ^ constant) out of the stage loop and keeps them all live in registers.
-__device__ __forceinline__ void rematerialize(uint32_t& a, uint32_t& b) {
-  asm volatile("" : "+v"(a), "+v"(b));
-}
-
 template <int HD>
 __device__ __forceinline__ bf16x8 lds_a(const char* base, uint32_t al, int c) {
   return *reinterpret_cast<const bf16x8*>(base + (al ^ (uint32_t)(c << 5)));
@@ -97,23 +96,6 @@ __device__ __forceinline__ f32x16 contract_rows(const char* base, uint32_t al,
   f32x16 acc = zero16();
 #pragma unroll
   for (int c = 0; c < HD / 16; ++c) acc = mfma_bf16(lds_a<HD>(base, al, c), frag[c], acc);
-  return acc;
-}
-
-// sum over hd of (rows of tile A) x (rows of tile B), both from LDS; every operand read is
-// issued before the MFMA chain so the chain does not wait on LDS latency per step.
-template <int HD>
-__device__ __forceinline__ f32x16 contract_lds(const char* abase, const char* bbase,
-                                               uint32_t al) {
-  bf16x8 a[HD / 16], b[HD / 16];
-#pragma unroll
-  for (int c = 0; c < HD / 16; ++c) {
-    a[c] = lds_a<HD>(abase, al, c);
-    b[c] = lds_a<HD>(bbase, al, c);
-  }
-  f32x16 acc = zero16();
-#pragma unroll
-  for (int c = 0; c < HD / 16; ++c) acc = mfma_bf16(a[c], b[c], acc);
   return acc;
 }
 
@@ -156,6 +138,73 @@ __device__ __forceinline__ void stage_wait_private() {
   lds_acquire();
 }
 
+// Direct global -> LDS copies (gfx950 global_load_lds): lane l's bytes land at the
+// wave-uniform LDS address dst + size * l.  They are written as inline assembly so that the
+// compiler does not see an LDS write in flight: it would otherwise make every later
+// transposing LDS read wait for all outstanding loads, prefetches included.  Callers order
+// the copies against LDS reads themselves, with vmcnt waits and barriers.  M0 (the LDS
+// destination) is saved and restored around the copy; one wait state separates its write
+// from the load that reads it.
+// PER consecutive 1 KiB wave copies into dst, dst + 1 KiB, ...: lane l of copy j reads
+// byte voff[j] of a raw buffer of nbytes bytes at gbase (buffer_load_dwordx4 ... lds).  The
+// buffer's range check turns reads at or past nbytes into zeros, so tiles that run past the
+// sequence end need no clamping.  M0 is saved once and stepped between the copies.
+template <int PER>
+__device__ __forceinline__ void dma16_rows(void* dst, const char* gbase, uint32_t nbytes,
+                                           const uint32_t (&voff)[PER]) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)(lds_void_t*)dst;
+  const uint64_t ga = (uint64_t)(uintptr_t)gbase;
+  i32x4 rsrc;  // base, stride 0, nbytes, raw 32-bit format
+  rsrc[0] = (int)(uint32_t)ga;
+  rsrc[1] = (int)((uint32_t)(ga >> 32) & 0xFFFFu);
+  rsrc[2] = (int)nbytes;
+  rsrc[3] = 0x00020000;
+  uint32_t saved;
+#define XATTN_LD(i) "buffer_load_dwordx4 %[o" #i "], %[r], 0 offen lds\n\t"
+#define XATTN_STEP "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+#define XATTN_HEAD "s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[m]\n\ts_nop 0\n\t"
+#define XATTN_TAIL "s_mov_b32 m0, %[sv]"
+  if constexpr (PER == 1) {
+    asm volatile(XATTN_HEAD XATTN_LD(0) XATTN_TAIL
+                 : [sv] "=&s"(saved) : [m] "s"(m0v), [r] "s"(rsrc), [o0] "v"(voff[0])
+                 : "memory", "scc");
+  } else if constexpr (PER == 2) {
+    asm volatile(XATTN_HEAD XATTN_LD(0) XATTN_STEP XATTN_LD(1) XATTN_TAIL
+                 : [sv] "=&s"(saved) : [m] "s"(m0v), [r] "s"(rsrc), [o0] "v"(voff[0]),
+                   [o1] "v"(voff[1])
+                 : "memory", "scc");
+  } else if constexpr (PER == 4) {
+    asm volatile(XATTN_HEAD XATTN_LD(0) XATTN_STEP XATTN_LD(1) XATTN_STEP XATTN_LD(2)
+                     XATTN_STEP XATTN_LD(3) XATTN_TAIL
+                 : [sv] "=&s"(saved) : [m] "s"(m0v), [r] "s"(rsrc), [o0] "v"(voff[0]),
+                   [o1] "v"(voff[1]), [o2] "v"(voff[2]), [o3] "v"(voff[3])
+                 : "memory", "scc");
+  } else {
+    static_assert(PER == 8, "1, 2, 4 or 8 copies");
+    asm volatile(XATTN_HEAD XATTN_LD(0) XATTN_STEP XATTN_LD(1) XATTN_STEP XATTN_LD(2)
+                     XATTN_STEP XATTN_LD(3) XATTN_STEP XATTN_LD(4) XATTN_STEP XATTN_LD(5)
+                         XATTN_STEP XATTN_LD(6) XATTN_STEP XATTN_LD(7) XATTN_TAIL
+                 : [sv] "=&s"(saved) : [m] "s"(m0v), [r] "s"(rsrc), [o0] "v"(voff[0]),
+                   [o1] "v"(voff[1]), [o2] "v"(voff[2]), [o3] "v"(voff[3]), [o4] "v"(voff[4]),
+                   [o5] "v"(voff[5]), [o6] "v"(voff[6]), [o7] "v"(voff[7])
+                 : "memory", "scc");
+  }
+#undef XATTN_LD
+#undef XATTN_STEP
+#undef XATTN_HEAD
+#undef XATTN_TAIL
+}
+__device__ __forceinline__ void dma4(void* dst, const float* gaddr) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)(lds_void_t*)dst;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "global_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0v), "v"(gaddr)
+      : "memory");
+}
+
 // Direct HBM -> LDS copy of ROWS rows of a [S, HD] bf16 matrix into a swizzled tile,
 // shared by NW waves.  Each lane's byte offsets within the source rows are fixed; a tile
 // that runs past the sequence end re-reads its last valid row (callers mask those rows).
@@ -174,18 +223,10 @@ struct Dma {
       off[j] = (uint32_t)(row * ROWB + c * 16);
     }
   }
-  // src: first row of the tile in global memory; nvalid: rows of it before the end.
+  // src: first row of the tile in global memory; nvalid: rows of it before the sequence
+  // end (rows at or past it are filled with zeros)
   __device__ __forceinline__ void issue(char* tile, const char* src, int wv, int nvalid) const {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      uint32_t o = off[j];
-      if (nvalid < ROWS) {
-        const int row = (int)(o / ROWB);
-        if (row >= nvalid) o -= (uint32_t)((row - nvalid + 1) * ROWB);
-      }
-      __builtin_amdgcn_global_load_lds(src + o, (lds_void_t*)(tile + (wv * PER + j) * 1024), 16,
-                                       0, 0);
-    }
+    dma16_rows<PER>(tile + wv * PER * 1024, src, (uint32_t)(min(nvalid, ROWS) * ROWB), off);
   }
 };
 
@@ -198,8 +239,7 @@ __device__ __forceinline__ void dma_rowstats(float* dst, const float* lse2,
   if (lane < PER) {
     const int e = wv * PER + lane;
     const int r = min(q0 + (e & 31), S - 1);
-    __builtin_amdgcn_global_load_lds((e < 32 ? lse2 : delta) + r,
-                                     (lds_void_t*)(dst + wv * PER), 4, 0, 0);
+    dma4(dst + wv * PER, (e < 32 ? lse2 : delta) + r);
   }
 }
 
@@ -502,20 +542,54 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
 // backward, dk/dv
 // ---------------------------------------------------------------------------------------
 constexpr int kBQ = 32;  // queries per dk/dv stage
+constexpr int kDkdvPF = 1;  // operand read-ahead of the dk/dv step (see dkdv_step_reg)
 
-// One 32x32 (queries x keys) step of the dk/dv recurrence on a staged Q / dO tile.
-// The K and V operands come either from register fragments (kvf = {kf, vf}) or, with
-// KV_LDS, from swizzled K / V tiles in LDS (kvt = {K tile, V tile}).
-template <int HD, bool MASK, bool KV_LDS>
-__device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[HD / 32], f32x16 (&dvt)[HD / 32],
-                                          const char* qs, const char* dos, const float* stats,
-                                          const bf16x8 (&kf)[HD / 16],
-                                          const bf16x8 (&vf)[HD / 16], const char* kt_lds,
-                                          const char* vt_lds, uint32_t al, uint32_t tl, int q0,
-                                          int key, int S, float scale_log2, int h) {
-  f32x16 st;  // S: queries x keys
-  if constexpr (KV_LDS) st = contract_lds<HD>(qs, kt_lds, al);
-  else st = contract_rows<HD>(qs, al, kf);
+// One 32x32 (queries x keys) step of the dk/dv recurrence on a staged Q / dO tile, with the
+// lane's K and V rows in registers.  LDS operand reads are issued in groups ahead
+// of the MFMAs that consume them, each group fenced off from the scheduler (which would
+// otherwise sink every read next to its MFMA and expose the LDS latency each time).
+// PF = 0: every read up front; 1: row operands up front, transposed ones after the S / dP
+// chains are issued; 2: each group one phase ahead.
+template <int HD, bool MASK, int PF>
+__device__ __forceinline__ void dkdv_step_reg(f32x16 (&dkt)[HD / 32], f32x16 (&dvt)[HD / 32],
+                                              const char* qs, const char* dos,
+                                              const float* stats, const bf16x8 (&kf)[HD / 16],
+                                              const bf16x8 (&vf)[HD / 16], uint32_t al,
+                                              uint32_t tl, int q0, int key, int S,
+                                              float scale_log2, int h) {
+  bf16x8 qa[HD / 16], da[HD / 16], ta[2][HD / 32], tq[2][HD / 32];
+  auto read_rows = [&](bf16x8 (&x)[HD / 16], const char* base) {
+#pragma unroll
+    for (int c = 0; c < HD / 16; ++c) x[c] = lds_a<HD>(base, al, c);
+  };
+  auto read_tr = [&](bf16x8 (&x)[2][HD / 32], const char* base) {
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int dt = 0; dt < HD / 32; ++dt) x[c2][dt] = lds_t<HD>(base, tl, c2, dt);
+  };
+  read_rows(qa, qs);
+  if constexpr (PF <= 1) read_rows(da, dos);
+  if constexpr (PF == 0) {
+    read_tr(ta, dos);
+    read_tr(tq, qs);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 st = zero16();  // S: queries x keys
+#pragma unroll
+  for (int c = 0; c < HD / 16; ++c) st = mfma_bf16(qa[c], kf[c], st);
+  if constexpr (PF == 2) {
+    read_rows(da, dos);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  f32x16 dpt = zero16();  // dP
+#pragma unroll
+  for (int c = 0; c < HD / 16; ++c) dpt = mfma_bf16(da[c], vf[c], dpt);
+  if constexpr (PF >= 1) {
+    read_tr(ta, dos);
+    if constexpr (PF == 1) read_tr(tq, qs);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   float pv[16];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -532,9 +606,14 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[HD / 32], f32x16 (&dvt)[
   }
   bf16x8 pb[2];
   pack16(pb, pv);
-  f32x16 dpt;  // dP
-  if constexpr (KV_LDS) dpt = contract_lds<HD>(dos, vt_lds, al);
-  else dpt = contract_rows<HD>(dos, al, vf);
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt) dvt[dt] = mfma_bf16(ta[c2][dt], pb[c2], dvt[dt]);
+  if constexpr (PF == 2) {
+    read_tr(tq, qs);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   float dsv[16];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -544,14 +623,16 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[HD / 32], f32x16 (&dvt)[
   }
   bf16x8 db[2];
   pack16(db, dsv);
-  acc_tr<HD>(dvt, dos, tl, pb);  // dV^T += dO^T P
-  acc_tr<HD>(dkt, qs, tl, db);   // dK^T += Q^T dS
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt) dkt[dt] = mfma_bf16(tq[c2][dt], db[c2], dkt[dt]);
 }
 
 // Shared variant: 4 waves own 128 consecutive keys of one KV head and share each staged
 // 32-query tile of every query head of the group.
 template <int HD, int NBUF, typename TG>
-__global__ __launch_bounds__(256, 1) void dkdv_shared_kernel(
+__global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_shared_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ delta, TG* __restrict__ dk, bf16* __restrict__ dv, int S, int H,
@@ -603,9 +684,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_shared_kernel(
     const int bb = t % NBUF;
     const int q0 = (qt_first + t % per_r) * kBQ;
     if (live && q0 + kBQ - 1 >= kw0)
-      dkdv_step<HD, MASK, false>(dkt, dvt, lds + (2 * bb) * TILEB, lds + (2 * bb + 1) * TILEB,
-                                 stats[bb], kf, vf, nullptr, nullptr, al, tl, q0, key, S,
-                                 scale_log2, h);
+      dkdv_step_reg<HD, MASK, kDkdvPF>(dkt, dvt, lds + (2 * bb) * TILEB,
+                                       lds + (2 * bb + 1) * TILEB, stats[bb], kf, vf, al, tl,
+                                       q0, key, S, scale_log2, h);
   };
   // Per query head: the first four query tiles straddle the diagonal of some wave's keys
   // and a ragged last tile runs past the sequence end; the rest need no masking.
@@ -628,7 +709,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_shared_kernel(
 // w, w+4, w+8, ... (of every query head of the group, r ascending) through its own LDS
 // buffers, so the main loop needs no barrier.  Partials are added in wave order.
 template <int HD, int NBUF, typename TG>
-__global__ __launch_bounds__(256, 1) void dkdv_private_kernel(
+__global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_private_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ delta, TG* __restrict__ dk, bf16* __restrict__ dv, int S, int H,
@@ -639,7 +720,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_private_kernel(
   using D = Dma<HD, kBQ, 1>;
   constexpr int NL = 2 * D::PER + 1;
   __shared__ __attribute__((aligned(1024))) char lds[4 * WAVEB];
-  __shared__ __attribute__((aligned(1024))) char kvt[2 * TILEB];  // the block's K, V rows
   __shared__ __attribute__((aligned(16))) float stats[4][NBUF][64];
   const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -651,16 +731,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_private_kernel(
   D dma;
   dma.init(0, lane);
   char* mine = lds + wv * WAVEB;
-  {
-    // the four waves share the block's 32 K and V rows through LDS
-    Dma<HD, kBQ, 4> kvdma;
-    kvdma.init(wv, lane);
-    kvdma.issue(kvt, reinterpret_cast<const char*>(k + ((size_t)kvbh * S + kw0) * HD), wv,
-                S - kw0);
-    kvdma.issue(kvt + TILEB, reinterpret_cast<const char*>(v + ((size_t)kvbh * S + kw0) * HD),
-                wv, S - kw0);
-  }
-  bf16x8 kf[HD / 16], vf[HD / 16];  // unused: K and V are read from LDS
+  bf16x8 kf[HD / 16], vf[HD / 16];  // K and V rows of the lane's key
+  load_frag<HD>(kf, k + (size_t)kvbh * S * HD, key, S, lane);
+  load_frag<HD>(vf, v + (size_t)kvbh * S * HD, key, S, lane);
   f32x16 dkt[HD / 32], dvt[HD / 32];
 #pragma unroll
   for (int dt = 0; dt < HD / 32; ++dt) dkt[dt] = dvt[dt] = zero16();
@@ -668,32 +741,41 @@ __global__ __launch_bounds__(256, 1) void dkdv_private_kernel(
   const int qt_first = kw0 / kBQ, nqt = (S + kBQ - 1) / kBQ;
   const int per_r = (nqt - qt_first - wv + 3) / 4;  // this wave's tiles per query head
   const int nst = group * per_r;
-  auto issue = [&](int t, int buf) {
-    const int r = t / per_r, qt = qt_first + wv + 4 * (t % per_r);
-    const size_t bh = (size_t)(b * H + kvh * group + r);
-    const int g0 = qt * kBQ, nv = S - g0;
-    dma.issue(mine + (2 * buf) * TILEB, reinterpret_cast<const char*>(q + (bh * S + g0) * HD), 0,
-              nv);
+  // tiles are issued in order: (query head r, this wave's i-th tile of it); the cursor
+  // avoids a division per stage
+  int next_r = 0, next_i = 0, issued = 0;
+  const size_t bh0 = (size_t)(b * H + kvh * group);
+  auto issue_next = [&](int buf) {
+    const size_t bh = bh0 + next_r;
+    const int g0 = (qt_first + wv + 4 * next_i) * kBQ, nv = S - g0;
+    dma.issue(mine + (2 * buf) * TILEB, reinterpret_cast<const char*>(q + (bh * S + g0) * HD),
+                  0, nv);
     dma.issue(mine + (2 * buf + 1) * TILEB,
-              reinterpret_cast<const char*>(dout + (bh * S + g0) * HD), 0, nv);
+                  reinterpret_cast<const char*>(dout + (bh * S + g0) * HD), 0, nv);
     dma_rowstats<1>(stats[wv][buf], lse2 + bh * S, delta + bh * S, g0, S, 0, lane);
+    if (++next_i == per_r) {
+      next_i = 0;
+      ++next_r;
+    }
+    ++issued;
   };
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t)
-    if (t < nst) issue(t, t);
-  wait_vm<0>();  // K / V rows (and the first stage) have landed
+    if (issued < nst) issue_next(t);
+  wait_vm<0>();  // the first stage has landed
   __builtin_amdgcn_s_barrier();
   lds_acquire();
-  auto stage = [&](auto mask_tag, int t) {
+  // stage t = (head r, tile i of this wave in it)
+  auto stage = [&](auto mask_tag, int t, int i) {
     constexpr bool MASK = decltype(mask_tag)::value;
     if (NBUF > 2 && t + 1 < nst) stage_wait_private<(NBUF > 2 ? NL : 0)>();
     else stage_wait_private<0>();
-    if (t + NBUF - 1 < nst) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
+    if (issued < nst) issue_next((t + NBUF - 1) % NBUF);
     const int bb = t % NBUF;
-    const int q0 = (qt_first + wv + 4 * (t % per_r)) * kBQ;
-    dkdv_step<HD, MASK, true>(dkt, dvt, mine + (2 * bb) * TILEB, mine + (2 * bb + 1) * TILEB,
-                              stats[wv][bb], kf, vf, kvt, kvt + TILEB, al, tl, q0, key, S,
-                              scale_log2, h);
+    const int q0 = (qt_first + wv + 4 * i) * kBQ;
+    dkdv_step_reg<HD, MASK, kDkdvPF>(dkt, dvt, mine + (2 * bb) * TILEB,
+                                     mine + (2 * bb + 1) * TILEB, stats[wv][bb], kf, vf, al, tl,
+                                     q0, key, S, scale_log2, h);
   };
   // Per query head: only wave 0's first tile meets the diagonal (its keys start at its
   // first query), and a ragged last tile runs past the sequence end.
@@ -703,9 +785,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_private_kernel(
     const int last_mask = ((S % kBQ) != 0 && last_qt == nqt - 1 && per_r > first_mask) ? 1 : 0;
     for (int r = 0; r < group; ++r) {
       const int t0 = r * per_r;
-      if (first_mask) stage(std::true_type{}, t0);
-      for (int i = first_mask; i < per_r - last_mask; ++i) stage(std::false_type{}, t0 + i);
-      if (last_mask) stage(std::true_type{}, t0 + per_r - 1);
+      if (first_mask) stage(std::true_type{}, t0, 0);
+      for (int i = first_mask; i < per_r - last_mask; ++i) stage(std::false_type{}, t0 + i, i);
+      if (last_mask) stage(std::true_type{}, t0 + per_r - 1, per_r - 1);
     }
   }
 
