@@ -21,24 +21,34 @@
 
 namespace xattn {
 
-__global__ void rope_cache_kernel(float* __restrict__ cos_tab, float* __restrict__ sin_tab,
-                                  int seq_len, int head_dim, double theta) {
+// One block covers 4 * (256 / half) consecutive positions: thread f = tid % half owns one
+// frequency, evaluates theta^(-2f/hd) once and the angle's cos and sin at 4 positions.
+__global__ __launch_bounds__(256) void rope_cache_kernel(float* __restrict__ cos_tab,
+                                                         float* __restrict__ sin_tab,
+                                                         int seq_len, int head_dim,
+                                                         double theta) {
   const int half = head_dim / 2;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= seq_len * half) return;
-  const int t = idx / half, i = idx % half;
-  const double inv_freq = pow(theta, -2.0 * (double)i / (double)head_dim);
-  const double a = (double)t * inv_freq;
-  cos_tab[idx] = (float)cos(a);
-  sin_tab[idx] = (float)sin(a);
+  const int f = threadIdx.x % half, lanes = 256 / half;
+  const double inv_freq = pow(theta, -2.0 * (double)f / (double)head_dim);
+  const int t0 = blockIdx.x * 4 * lanes + (int)threadIdx.x / half;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int t = t0 + k * lanes;
+    if (t < seq_len) {
+      double sv, cv;
+      sincos((double)t * inv_freq, &sv, &cv);
+      cos_tab[(size_t)t * half + f] = (float)cv;
+      sin_tab[(size_t)t * half + f] = (float)sv;
+    }
+  }
 }
 
 hipError_t launch_rope_cache(float* cos_tab, float* sin_tab, int seq_len, int head_dim,
                              double theta, hipStream_t stream) {
-  const int n = seq_len * (head_dim / 2);
+  const int per_block = 4 * (256 / (head_dim / 2));
   ProfScope prof("rope_cache", stream);
-  hipLaunchKernelGGL(rope_cache_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, cos_tab,
-                     sin_tab, seq_len, head_dim, theta);
+  hipLaunchKernelGGL(rope_cache_kernel, dim3((seq_len + per_block - 1) / per_block), dim3(256),
+                     0, stream, cos_tab, sin_tab, seq_len, head_dim, theta);
   return hipPeekAtLastError();
 }
 
@@ -71,62 +81,83 @@ __device__ __forceinline__ void store_from_f32(T* __restrict__ p, const float (&
 // --------------------------------------------------------------------------------------
 // forward
 // --------------------------------------------------------------------------------------
-template <typename T, int HD>
+// Rows are taken in groups of R heads at one position t (rows h*S + t, h in the group):
+// the lanes of a row group load the position's cos / sin and gamma once and issue the R
+// rows' loads together.  Row groups are numbered with t fastest, so neighbouring groups
+// read neighbouring rows.
+template <typename T, int HD, int R>
 __global__ __launch_bounds__(256) void qknorm_rope_fwd_kernel(
     const T* __restrict__ x, const float* __restrict__ gamma, const float* __restrict__ cos_tab,
-    const float* __restrict__ sin_tab, T* __restrict__ y, float* __restrict__ rstd, int nrows,
+    const float* __restrict__ sin_tab, T* __restrict__ y, float* __restrict__ rstd, int ngroups,
     int seq_len, float eps) {
   constexpr int VEC = V16<T>::n;
   constexpr int HALF = HD / 2;
   constexpr int LPR = HALF / VEC;  // lanes per row
   static_assert(LPR >= 1 && 64 % LPR == 0, "row must split over a power-of-two lane count");
   const int g = blockIdx.x * 256 + threadIdx.x;
-  const int row = g / LPR, part = g % LPR;
-  const bool valid = row < nrows;
-  const int rr = valid ? row : 0;  // rows past the end read row 0 and store nothing
+  const int rg = g / LPR, part = g % LPR;
+  const bool valid = rg < ngroups;
+  const int rgv = valid ? rg : 0;  // lanes past the end redo group 0 and store nothing
+  const int t = rgv % seq_len, h0 = (rgv / seq_len) * R;
   const int c0 = part * VEC;
 
-  float a[VEC], b[VEC];
-  load_f32<T, VEC>(x + (size_t)rr * HD + c0, a);
-  load_f32<T, VEC>(x + (size_t)rr * HD + HALF + c0, b);
-  float ss = 0.f;
+  float a[R][VEC], b[R][VEC];
 #pragma unroll
-  for (int j = 0; j < VEC; ++j) ss += a[j] * a[j] + b[j] * b[j];
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) ss += shfl_xor(ss, m);
-  const float r = 1.0f / sqrtf(ss * (1.0f / (float)HD) + eps);
-
-  const int t = rr % seq_len;
+  for (int j = 0; j < R; ++j) {
+    const size_t row = (size_t)(h0 + j) * seq_len + t;
+    load_f32<T, VEC>(x + row * HD + c0, a[j]);
+    load_f32<T, VEC>(x + row * HD + HALF + c0, b[j]);
+  }
   float cs[VEC], sn[VEC], g1[VEC], g2[VEC];
   load_f32<float, VEC>(cos_tab + (size_t)t * HALF + c0, cs);
   load_f32<float, VEC>(sin_tab + (size_t)t * HALF + c0, sn);
   load_f32<float, VEC>(gamma + c0, g1);
   load_f32<float, VEC>(gamma + HALF + c0, g2);
-  float o1[VEC], o2[VEC];
 #pragma unroll
-  for (int j = 0; j < VEC; ++j) {
-    const float n1 = a[j] * r * g1[j];
-    const float n2 = b[j] * r * g2[j];
-    o1[j] = n1 * cs[j] - n2 * sn[j];
-    o2[j] = n1 * sn[j] + n2 * cs[j];
-  }
-  if (valid) {
-    store_from_f32<T, VEC>(y + (size_t)row * HD + c0, o1);
-    store_from_f32<T, VEC>(y + (size_t)row * HD + HALF + c0, o2);
-    if (part == 0) rstd[row] = r;
+  for (int j = 0; j < R; ++j) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) ss += a[j][e] * a[j][e] + b[j][e] * b[j][e];
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) ss += shfl_xor(ss, m);
+    const float r = 1.0f / sqrtf(ss * (1.0f / (float)HD) + eps);
+    float o1[VEC], o2[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const float n1 = a[j][e] * r * g1[e];
+      const float n2 = b[j][e] * r * g2[e];
+      o1[e] = n1 * cs[e] - n2 * sn[e];
+      o2[e] = n1 * sn[e] + n2 * cs[e];
+    }
+    if (valid) {
+      const size_t row = (size_t)(h0 + j) * seq_len + t;
+      store_from_f32<T, VEC>(y + row * HD + c0, o1);
+      store_from_f32<T, VEC>(y + row * HD + HALF + c0, o2);
+      if (part == 0) rstd[row] = r;
+    }
   }
 }
+
+// heads per row group: 4 when the head count allows it
+static int fwd_group(int heads) { return heads % 4 == 0 ? 4 : (heads % 2 == 0 ? 2 : 1); }
 
 template <typename T, int HD>
 static hipError_t fwd_dispatch(const void* x, const float* gamma, const float* cos_tab,
                                const float* sin_tab, void* y, float* rstd, int nrows,
                                int seq_len, float eps, hipStream_t stream) {
   constexpr int LPR = (HD / 2) / V16<T>::n;
-  const long long threads = (long long)nrows * LPR;
+  const int heads = nrows / seq_len, R = fwd_group(heads);
+  const int ngroups = (heads / R) * seq_len;
+  const long long threads = (long long)ngroups * LPR;
   const int blocks = (int)((threads + 255) / 256);
   ProfScope prof("qknorm_rope_fwd", stream);
-  hipLaunchKernelGGL((qknorm_rope_fwd_kernel<T, HD>), dim3(blocks), dim3(256), 0, stream,
-                     (const T*)x, gamma, cos_tab, sin_tab, (T*)y, rstd, nrows, seq_len, eps);
+#define XATTN_FWD_R(RV)                                                                    \
+  hipLaunchKernelGGL((qknorm_rope_fwd_kernel<T, HD, RV>), dim3(blocks), dim3(256), 0, stream, \
+                     (const T*)x, gamma, cos_tab, sin_tab, (T*)y, rstd, ngroups, seq_len, eps)
+  if (R == 4) XATTN_FWD_R(4);
+  else if (R == 2) XATTN_FWD_R(2);
+  else XATTN_FWD_R(1);
+#undef XATTN_FWD_R
   return hipPeekAtLastError();
 }
 
@@ -152,130 +183,214 @@ hipError_t launch_qknorm_rope_fwd(IoType io, int head_dim, const void* x, const 
 // --------------------------------------------------------------------------------------
 // backward
 // --------------------------------------------------------------------------------------
-// Rows are split into fixed contiguous chunks, one per block; each block writes one
-// [HD] row of dgamma partials, summed over its rows in ascending row order.  The
-// partials are then summed over blocks in a fixed order.  Both orders depend only on
-// the shape, so dgamma is bitwise reproducible run to run.
+// Row groups (R heads at one position, as in the forward) are split into equal contiguous
+// chunks, one per block; a block's 256 / LPR group slots take the chunk's groups in turn.
+// Each lane accumulates its dgamma terms in a fixed order, the block sums its lanes in a
+// fixed order into one partial per column, stored column-major ([HD][nblocks]) so that the
+// reduction reads each column contiguously; a reduction wave then sums a column's partials
+// in a fixed order.  Every order depends only on the shape, so dgamma is bitwise
+// reproducible run to run.  One launch serves one or two tensors (Q and K).
 constexpr int kBwdMaxBlocks = 1024;
-constexpr int kBwdMinRowsPerBlock = 64;
+constexpr int kBwdRowsPerBlock = 128;
+constexpr int kBwdHeadsPerGroup = 2;  // rows handled together by a lane (1, 2 or 4)
 
 int qknorm_rope_bwd_blocks(int64_t nrows) {
-  int64_t nb = (nrows + kBwdMinRowsPerBlock - 1) / kBwdMinRowsPerBlock;
+  int64_t nb = (nrows + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock;
   if (nb > kBwdMaxBlocks) nb = kBwdMaxBlocks;
   if (nb < 1) nb = 1;
   return (int)nb;
 }
 
-template <typename TDy, typename TX, int HD>
-__global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(
-    const TDy* __restrict__ dy, const TX* __restrict__ x, const float* __restrict__ gamma,
-    const float* __restrict__ rstd, const float* __restrict__ cos_tab,
-    const float* __restrict__ sin_tab, TX* __restrict__ dx, float* __restrict__ partials,
-    int nrows, int seq_len, int rows_per_block) {
+struct BwdJob {
+  const void* dy;
+  const void* x;
+  const float* gamma;
+  const float* rstd;
+  void* dx;
+  float* partials;  // [HD][nblocks]
+  float* dgamma;
+  int ngroups, groups_per_block, nblocks, heads_per_group;
+};
+
+template <typename TDy, typename TX, int HD, int R>
+__device__ __forceinline__ void qknorm_rope_bwd_block(const BwdJob& jb, int blk,
+                                                      const float* __restrict__ cos_tab,
+                                                      const float* __restrict__ sin_tab,
+                                                      int seq_len, float (*red)[2 * V16<TX>::n]) {
   constexpr int VEC = V16<TX>::n;
   constexpr int HALF = HD / 2;
   constexpr int LPR = HALF / VEC;
-  constexpr int RPP = 256 / LPR;  // rows per pass of the block
-  __shared__ float red[256][2 * VEC];
+  constexpr int GPB = 256 / LPR;  // group slots per block
+  const TDy* __restrict__ dy = static_cast<const TDy*>(jb.dy);
+  const TX* __restrict__ x = static_cast<const TX*>(jb.x);
+  TX* __restrict__ dx = static_cast<TX*>(jb.dx);
+  const float* __restrict__ rstd = jb.rstd;
 
   const int tid = threadIdx.x;
-  const int sub = tid / LPR, part = tid % LPR;
+  const int slot = tid / LPR, part = tid % LPR;
   const int c0 = part * VEC;
-  const int r0 = blockIdx.x * rows_per_block;
-  const int r1 = min(nrows, r0 + rows_per_block);
+  const int gs = blk * jb.groups_per_block;
+  const int ge = min(jb.ngroups, gs + jb.groups_per_block);
 
   float g1[VEC], g2[VEC];
-  load_f32<float, VEC>(gamma + c0, g1);
-  load_f32<float, VEC>(gamma + HALF + c0, g2);
+  load_f32<float, VEC>(jb.gamma + c0, g1);
+  load_f32<float, VEC>(jb.gamma + HALF + c0, g2);
   float acc1[VEC], acc2[VEC];
 #pragma unroll
-  for (int j = 0; j < VEC; ++j) acc1[j] = acc2[j] = 0.f;
+  for (int e = 0; e < VEC; ++e) acc1[e] = acc2[e] = 0.f;
 
-  for (int row = r0 + sub; row < r1; row += RPP) {
-    float d1[VEC], d2[VEC], x1[VEC], x2[VEC], cs[VEC], sn[VEC];
-    load_f32<TDy, VEC>(dy + (size_t)row * HD + c0, d1);
-    load_f32<TDy, VEC>(dy + (size_t)row * HD + HALF + c0, d2);
-    load_f32<TX, VEC>(x + (size_t)row * HD + c0, x1);
-    load_f32<TX, VEC>(x + (size_t)row * HD + HALF + c0, x2);
-    const int t = row % seq_len;
+  for (int rg = gs + slot; rg < ge; rg += GPB) {
+    const int t = rg % seq_len, h0 = (rg / seq_len) * R;
+    float d1[R][VEC], d2[R][VEC], x1[R][VEC], x2[R][VEC], rr[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const size_t row = (size_t)(h0 + j) * seq_len + t;
+      load_f32<TDy, VEC>(dy + row * HD + c0, d1[j]);
+      load_f32<TDy, VEC>(dy + row * HD + HALF + c0, d2[j]);
+      load_f32<TX, VEC>(x + row * HD + c0, x1[j]);
+      load_f32<TX, VEC>(x + row * HD + HALF + c0, x2[j]);
+      rr[j] = rstd[row];
+    }
+    float cs[VEC], sn[VEC];
     load_f32<float, VEC>(cos_tab + (size_t)t * HALF + c0, cs);
     load_f32<float, VEC>(sin_tab + (size_t)t * HALF + c0, sn);
-    const float r = rstd[row];
-    float n1[VEC], n2[VEC];
-    float dot = 0.f;
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      n1[j] = d1[j] * cs[j] + d2[j] * sn[j];   // rotation by the negative angle
-      n2[j] = -d1[j] * sn[j] + d2[j] * cs[j];
-      dot += g1[j] * n1[j] * x1[j] + g2[j] * n2[j] * x2[j];
+    for (int j = 0; j < R; ++j) {
+      const float r = rr[j];
+      float n1[VEC], n2[VEC];
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        n1[e] = d1[j][e] * cs[e] + d2[j][e] * sn[e];  // rotation by the negative angle
+        n2[e] = -d1[j][e] * sn[e] + d2[j][e] * cs[e];
+        dot += g1[e] * n1[e] * x1[j][e] + g2[e] * n2[e] * x2[j][e];
+      }
+#pragma unroll
+      for (int m = 1; m < LPR; m <<= 1) dot += shfl_xor(dot, m);
+      const float coef = dot * r * r * r * (1.0f / (float)HD);
+      float o1[VEC], o2[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        o1[e] = g1[e] * n1[e] * r - x1[j][e] * coef;
+        o2[e] = g2[e] * n2[e] * r - x2[j][e] * coef;
+        acc1[e] += n1[e] * x1[j][e] * r;
+        acc2[e] += n2[e] * x2[j][e] * r;
+      }
+      const size_t row = (size_t)(h0 + j) * seq_len + t;
+      store_from_f32<TX, VEC>(dx + row * HD + c0, o1);
+      store_from_f32<TX, VEC>(dx + row * HD + HALF + c0, o2);
     }
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) dot += shfl_xor(dot, m);
-    const float coef = dot * r * r * r * (1.0f / (float)HD);
-    float o1[VEC], o2[VEC];
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      o1[j] = g1[j] * n1[j] * r - x1[j] * coef;
-      o2[j] = g2[j] * n2[j] * r - x2[j] * coef;
-      acc1[j] += n1[j] * x1[j] * r;
-      acc2[j] += n2[j] * x2[j] * r;
-    }
-    store_from_f32<TX, VEC>(dx + (size_t)row * HD + c0, o1);
-    store_from_f32<TX, VEC>(dx + (size_t)row * HD + HALF + c0, o2);
   }
 
 #pragma unroll
-  for (int j = 0; j < VEC; ++j) {
-    red[tid][j] = acc1[j];
-    red[tid][VEC + j] = acc2[j];
+  for (int e = 0; e < VEC; ++e) {
+    red[tid][e] = acc1[e];
+    red[tid][VEC + e] = acc2[e];
   }
   __syncthreads();
   if (tid < HD) {
     const int col = tid;
     const int hsel = col / HALF, cc = col % HALF;
-    const int p = cc / VEC, j = cc % VEC;
-    float s = 0.f;
-    for (int sb = 0; sb < RPP; ++sb) s += red[sb * LPR + p][hsel * VEC + j];
-    partials[(size_t)blockIdx.x * HD + col] = s;
+    const int p = cc / VEC, e = cc % VEC;
+    float sum = 0.f;
+    for (int sb = 0; sb < GPB; ++sb) sum += red[sb * LPR + p][hsel * VEC + e];
+    jb.partials[(size_t)col * jb.nblocks + blk] = sum;
   }
 }
 
-// One wave per dgamma column: lane k sums partial rows k, k+64, ... in ascending order,
-// then a fixed xor butterfly combines the 64 lane sums.
-__global__ __launch_bounds__(256) void dgamma_reduce_kernel(const float* __restrict__ partials,
-                                                            float* __restrict__ dgamma,
-                                                            int nblocks, int head_dim) {
-  const int col = blockIdx.x * 4 + threadIdx.x / 64;
+template <typename TDy, typename TX, int HD>
+__global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(BwdJob j0, BwdJob j1,
+                                                              const float* __restrict__ cos_tab,
+                                                              const float* __restrict__ sin_tab,
+                                                              int seq_len) {
+  __shared__ float red[256][2 * V16<TX>::n];
+  const bool second = (int)blockIdx.x >= j0.nblocks;
+  const BwdJob& jb = second ? j1 : j0;
+  const int blk = second ? (int)blockIdx.x - j0.nblocks : (int)blockIdx.x;
+  if (jb.heads_per_group == 4)
+    qknorm_rope_bwd_block<TDy, TX, HD, 4>(jb, blk, cos_tab, sin_tab, seq_len, red);
+  else if (jb.heads_per_group == 2)
+    qknorm_rope_bwd_block<TDy, TX, HD, 2>(jb, blk, cos_tab, sin_tab, seq_len, red);
+  else
+    qknorm_rope_bwd_block<TDy, TX, HD, 1>(jb, blk, cos_tab, sin_tab, seq_len, red);
+}
+
+// One wave per dgamma column of one or two tensors: lane k sums partials k, k + 64, ... of
+// the column (contiguous) in ascending order, then a fixed xor butterfly combines the lanes.
+__global__ __launch_bounds__(256) void dgamma_reduce_kernel(BwdJob j0, BwdJob j1, int head_dim) {
+  const int w = blockIdx.x * 4 + threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
+  const bool second = w >= head_dim;
+  const BwdJob& jb = second ? j1 : j0;
+  const int col = second ? w - head_dim : w;
   if (col >= head_dim) return;
+  const float* p = jb.partials + (size_t)col * jb.nblocks;
   float s = 0.f;
-  for (int b = lane; b < nblocks; b += 64) s += partials[(size_t)b * head_dim + col];
+  for (int b = lane; b < jb.nblocks; b += 64) s += p[b];
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) s += shfl_xor(s, m);
-  if (lane == 0) dgamma[col] = s;
+  if (lane == 0) jb.dgamma[col] = s;
+}
+
+static BwdJob make_job(const void* dy, const void* x, const float* gamma, const float* rstd,
+                       void* dx, float* dgamma, float* partials, int nrows, int seq_len) {
+  const int heads = nrows / seq_len;
+  int R = 1;
+  if (kBwdHeadsPerGroup >= 4 && heads % 4 == 0) R = 4;
+  else if (kBwdHeadsPerGroup >= 2 && heads % 2 == 0) R = 2;
+  BwdJob j;
+  j.heads_per_group = R;
+  j.dy = dy, j.x = x, j.gamma = gamma, j.rstd = rstd, j.dx = dx, j.partials = partials;
+  j.dgamma = dgamma;
+  j.nblocks = qknorm_rope_bwd_blocks(nrows);
+  j.ngroups = (nrows / seq_len / R) * seq_len;
+  j.groups_per_block = (j.ngroups + j.nblocks - 1) / j.nblocks;
+  return j;
 }
 
 template <typename TDy, typename TX, int HD>
-static hipError_t bwd_dispatch(const void* dy, const void* x, const float* gamma,
-                               const float* rstd, const float* cos_tab, const float* sin_tab,
-                               void* dx, float* dgamma, float* partials, int nrows,
-                               int seq_len, hipStream_t stream) {
-  const int nb = qknorm_rope_bwd_blocks(nrows);
-  const int rpb = (nrows + nb - 1) / nb;
+static hipError_t bwd_dispatch(const BwdJob& j0, const BwdJob& j1, const float* cos_tab,
+                               const float* sin_tab, int seq_len, hipStream_t stream) {
+  const int nb = j0.nblocks + j1.nblocks;
+  const int njobs = j1.nblocks > 0 ? 2 : 1;
   {
     ProfScope prof("qknorm_rope_bwd", stream);
     hipLaunchKernelGGL((qknorm_rope_bwd_kernel<TDy, TX, HD>), dim3(nb), dim3(256), 0, stream,
-                       (const TDy*)dy, (const TX*)x, gamma, rstd, cos_tab, sin_tab, (TX*)dx,
-                       partials, nrows, seq_len, rpb);
+                       j0, j1, cos_tab, sin_tab, seq_len);
   }
   hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess) return e;
   {
     ProfScope prof("dgamma_reduce", stream);
-    hipLaunchKernelGGL(dgamma_reduce_kernel, dim3((HD + 3) / 4), dim3(256), 0, stream,
-                       (const float*)partials, dgamma, nb, HD);
+    hipLaunchKernelGGL(dgamma_reduce_kernel, dim3((njobs * HD + 3) / 4), dim3(256), 0, stream,
+                       j0, j1, HD);
   }
   return hipPeekAtLastError();
+}
+
+template <typename TDy, typename TX>
+static hipError_t bwd_hd(int head_dim, const BwdJob& j0, const BwdJob& j1,
+                         const float* cos_tab, const float* sin_tab, int seq_len,
+                         hipStream_t stream) {
+  switch (head_dim) {
+    case 16: return bwd_dispatch<TDy, TX, 16>(j0, j1, cos_tab, sin_tab, seq_len, stream);
+    case 32: return bwd_dispatch<TDy, TX, 32>(j0, j1, cos_tab, sin_tab, seq_len, stream);
+    case 64: return bwd_dispatch<TDy, TX, 64>(j0, j1, cos_tab, sin_tab, seq_len, stream);
+    case 128: return bwd_dispatch<TDy, TX, 128>(j0, j1, cos_tab, sin_tab, seq_len, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+static hipError_t bwd_types(IoType dy_io, IoType x_io, int head_dim, const BwdJob& j0,
+                            const BwdJob& j1, const float* cos_tab, const float* sin_tab,
+                            int seq_len, hipStream_t stream) {
+  if (x_io == IO_F32 && dy_io == IO_F32)
+    return bwd_hd<float, float>(head_dim, j0, j1, cos_tab, sin_tab, seq_len, stream);
+  if (x_io == IO_BF16 && dy_io == IO_BF16)
+    return bwd_hd<bf16, bf16>(head_dim, j0, j1, cos_tab, sin_tab, seq_len, stream);
+  if (x_io == IO_BF16 && dy_io == IO_F32)
+    return bwd_hd<float, bf16>(head_dim, j0, j1, cos_tab, sin_tab, seq_len, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_qknorm_rope_bwd(IoType dy_io, IoType x_io, int head_dim, const void* dy,
@@ -283,22 +398,23 @@ hipError_t launch_qknorm_rope_bwd(IoType dy_io, IoType x_io, int head_dim, const
                                   const float* cos_tab, const float* sin_tab, void* dx,
                                   float* dgamma, float* partials, int nrows, int seq_len,
                                   hipStream_t stream) {
-#define XATTN_BWD_CASE(TDY, TX, HD)                                                        \
-  if (head_dim == HD)                                                                      \
-    return bwd_dispatch<TDY, TX, HD>(dy, x, gamma, rstd, cos_tab, sin_tab, dx, dgamma,     \
-                                     partials, nrows, seq_len, stream);
-#define XATTN_BWD_HDS(TDY, TX)                                                     \
-  XATTN_BWD_CASE(TDY, TX, 16) XATTN_BWD_CASE(TDY, TX, 32) XATTN_BWD_CASE(TDY, TX, 64) \
-  XATTN_BWD_CASE(TDY, TX, 128)
-  if (x_io == IO_F32) {
-    if (dy_io == IO_F32) { XATTN_BWD_HDS(float, float) }
-  } else {
-    if (dy_io == IO_BF16) { XATTN_BWD_HDS(bf16, bf16) }
-    if (dy_io == IO_F32) { XATTN_BWD_HDS(float, bf16) }
-  }
-#undef XATTN_BWD_HDS
-#undef XATTN_BWD_CASE
-  return hipErrorInvalidValue;
+  const BwdJob j0 = make_job(dy, x, gamma, rstd, dx, dgamma, partials, nrows, seq_len);
+  BwdJob j1{};
+  return bwd_types(dy_io, x_io, head_dim, j0, j1, cos_tab, sin_tab, seq_len, stream);
+}
+
+hipError_t launch_qknorm_rope_bwd_qk(IoType dy_io, IoType x_io, int head_dim, const void* dyq,
+                                     const void* xq, const float* gamma_q, const float* rstd_q,
+                                     void* dxq, float* dgamma_q, float* partials_q, int nrows_q,
+                                     const void* dyk, const void* xk, const float* gamma_k,
+                                     const float* rstd_k, void* dxk, float* dgamma_k,
+                                     float* partials_k, int nrows_k, const float* cos_tab,
+                                     const float* sin_tab, int seq_len, hipStream_t stream) {
+  const BwdJob jq = make_job(dyq, xq, gamma_q, rstd_q, dxq, dgamma_q, partials_q, nrows_q,
+                             seq_len);
+  const BwdJob jk = make_job(dyk, xk, gamma_k, rstd_k, dxk, dgamma_k, partials_k, nrows_k,
+                             seq_len);
+  return bwd_types(dy_io, x_io, head_dim, jq, jk, cos_tab, sin_tab, seq_len, stream);
 }
 
 }  // namespace xattn

@@ -373,16 +373,12 @@ xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, con
     hip_check(xattn::launch_attn_bwd(c.io, c.s, q, k, v, out, lse, dout, dyq, dyk, dv, delta,
                                      lse2, true, st),
               "attention backward launch");
-    hip_check(xattn::launch_qknorm_rope_bwd(xattn::IO_F32, c.io, c.s.head_dim, dyq, pro->xq,
-                                            pro->gamma_q, pro->rstd_q, pro->cos_tab,
-                                            pro->sin_tab, dq, pro->dgamma_q, part_q,
-                                            (int)c.rows_q, c.s.seq_len, st),
-              "prologue backward (q) launch");
-    hip_check(xattn::launch_qknorm_rope_bwd(xattn::IO_F32, c.io, c.s.head_dim, dyk, pro->xk,
-                                            pro->gamma_k, pro->rstd_k, pro->cos_tab,
-                                            pro->sin_tab, dk, pro->dgamma_k, part_k,
-                                            (int)rows_k, c.s.seq_len, st),
-              "prologue backward (k) launch");
+    hip_check(xattn::launch_qknorm_rope_bwd_qk(
+                  xattn::IO_F32, c.io, c.s.head_dim, dyq, pro->xq, pro->gamma_q, pro->rstd_q, dq,
+                  pro->dgamma_q, part_q, (int)c.rows_q, dyk, pro->xk, pro->gamma_k, pro->rstd_k,
+                  dk, pro->dgamma_k, part_k, (int)rows_k, pro->cos_tab, pro->sin_tab,
+                  c.s.seq_len, st),
+              "prologue backward launch");
   });
 }
 

@@ -23,12 +23,23 @@ hipError_t launch_qknorm_rope_fwd(IoType io, int head_dim, const void* x, const 
 // Number of per-block dgamma partial rows the backward writes for `nrows` rows.
 int qknorm_rope_bwd_blocks(int64_t nrows);
 
-// dy_io is the dtype of dy (may be fp32 while x / dx are bf16).
+// dy_io is the dtype of dy (may be fp32 while x / dx are bf16).  partials: workspace of
+// qknorm_rope_bwd_blocks(nrows) * head_dim floats.
 hipError_t launch_qknorm_rope_bwd(IoType dy_io, IoType x_io, int head_dim, const void* dy,
                                   const void* x, const float* gamma, const float* rstd,
                                   const float* cos_tab, const float* sin_tab, void* dx,
                                   float* dgamma, float* partials, int nrows, int seq_len,
                                   hipStream_t stream);
+
+// Q and K in one launch (and one dgamma reduction launch); same arithmetic and orders
+// as two launch_qknorm_rope_bwd calls.
+hipError_t launch_qknorm_rope_bwd_qk(IoType dy_io, IoType x_io, int head_dim, const void* dyq,
+                                     const void* xq, const float* gamma_q, const float* rstd_q,
+                                     void* dxq, float* dgamma_q, float* partials_q, int nrows_q,
+                                     const void* dyk, const void* xk, const float* gamma_k,
+                                     const float* rstd_k, void* dxk, float* dgamma_k,
+                                     float* partials_k, int nrows_k, const float* cos_tab,
+                                     const float* sin_tab, int seq_len, hipStream_t stream);
 
 // ---- attention -----------------------------------------------------------------------
 struct AttnShape {
