@@ -323,12 +323,13 @@ struct SoftmaxState {
   float m, l;
 };
 
-// One 32-key sub-tile of the forward: scores st (keys x this lane's query), online softmax
-// update and O^T += V^T P^T.
+// Online softmax of one 32-key sub-tile: scores st (keys x this lane's query) update the
+// running max / sum (rescaling the output accumulator lazily) and give the packed P^T
+// operand of the P.V product.
 template <int HD, bool MASK>
-__device__ __forceinline__ void fwd_subtile(f32x16 (&o)[HD / 32], SoftmaxState& sm,
-                                            const f32x16& st, const char* vsub, uint32_t tl,
-                                            int kb, int qrow, int S, int h, float scale_log2) {
+__device__ __forceinline__ void fwd_softmax(f32x16 (&o)[HD / 32], SoftmaxState& sm,
+                                            const f32x16& st, bf16x8 (&pb)[2], int kb,
+                                            int qrow, int S, int h, float scale_log2) {
   float sv[16];
   float tmax = -INFINITY;
 #pragma unroll
@@ -358,8 +359,16 @@ __device__ __forceinline__ void fwd_subtile(f32x16 (&o)[HD / 32], SoftmaxState& 
     psum += sv[i];
   }
   sm.l += psum;
-  bf16x8 pb[2];
   pack16(pb, sv);
+}
+
+// One 32-key sub-tile: softmax, then O^T += V^T P^T.
+template <int HD, bool MASK>
+__device__ __forceinline__ void fwd_subtile(f32x16 (&o)[HD / 32], SoftmaxState& sm,
+                                            const f32x16& st, const char* vsub, uint32_t tl,
+                                            int kb, int qrow, int S, int h, float scale_log2) {
+  bf16x8 pb[2];
+  fwd_softmax<HD, MASK>(o, sm, st, pb, kb, qrow, S, h, scale_log2);
   acc_tr<HD>(o, vsub, tl, pb);
 }
 
