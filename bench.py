@@ -64,7 +64,8 @@ def kernel_units(w):
         # prologue: per launch average over the Q launch and the K launch
         "qknorm_rope_fwd": ("hbm", ((rows_q + rows_k) * (hd * 2 * io + 4)) / 2,
                             "read x, write y (io dtype), write rstd"),
-        "qknorm_rope_bwd": ("hbm", ((rows_q + rows_k) * (hd * (4 + 2 * io) + 4)) / 2,
+        # prologue backward: one launch for Q and K together
+        "qknorm_rope_bwd": ("hbm", (rows_q + rows_k) * (hd * (4 + 2 * io) + 4),
                             "read fp32 dy, read x, write dx (io dtype), read rstd"),
     }
 
