@@ -2,9 +2,9 @@
 """Benchmark: causal GQA attention fwd+bwd (with the QK-norm + RoPE prologue) on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input: RoPE cache,
-QK-norm + RoPE on Q and K, attention forward, attention backward with the group sum,
-prologue backward and dgamma reductions (libxattn kernels only, preallocated buffers,
-one stream).  The workload is the long-context Qwen3-shaped GQA configuration (B=1,
+QK-norm + RoPE on Q and K, attention forward, attention backward with the group sum and
+the prologue backward (for bf16 io applied inside the dq and dk/dv kernels' stores), and
+the dgamma reductions (libxattn kernels only, preallocated buffers, one stream).  The workload is the long-context Qwen3-shaped GQA configuration (B=1,
 S=4096, 32 query heads, 8 KV heads, head_dim 128, bf16 in / fp32 accumulate).
 
 value = algorithmic attention FLOP per step (12 * hd per causal pair per query head:
@@ -64,7 +64,8 @@ def kernel_units(w):
         # prologue: per launch average over the Q launch and the K launch
         "qknorm_rope_fwd": ("hbm", ((rows_q + rows_k) * (hd * 2 * io + 4)) / 2,
                             "read x, write y (io dtype), write rstd"),
-        # prologue backward: one launch for Q and K together
+        # standalone prologue backward (fp32 io; bf16 io fuses it into attn_bwd_dq / dkdv):
+        # one launch for Q and K together
         "qknorm_rope_bwd": ("hbm", (rows_q + rows_k) * (hd * (4 + 2 * io) + 4),
                             "read fp32 dy, read x, write dx (io dtype), read rstd"),
     }

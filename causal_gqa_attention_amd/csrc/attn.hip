@@ -533,9 +533,9 @@ hipError_t launch_attn_bwd(IoType io, const AttnShape& s, const void* q, const v
                            const void* v, const void* out, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, float* delta,
                            float* lse2, bool grads_f32, hipStream_t stream) {
-  if (io == IO_BF16 && fast_bf16_supported(s.head_dim))
+  if (io == IO_BF16 && fast_bf16_supported(s.head_dim) && !grads_f32)
     return launch_attn_bwd_bf16_fast(s, q, k, v, out, lse, dout, dq, dk, dv, delta, lse2,
-                                     grads_f32, stream);
+                                     nullptr, stream);
 #define XATTN_CASE(T, HD, TG)                                                          \
   if (s.head_dim == HD)                                                                \
     return bwd_impl<T, HD, TG>(s, q, k, v, out, lse, dout, dq, dk, dv, delta, stream);

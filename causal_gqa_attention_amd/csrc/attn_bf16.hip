@@ -31,6 +31,10 @@
 //     buffers (no barriers in the main loop); the four partial dK/dV are added in wave
 //     order at the end.
 //   * Blocks of one KV head are mapped to one XCD (its L2), heaviest causal tiles first.
+//   * With the QK-norm + RoPE prologue, its backward runs in the dq and dk stores: the
+//     gradient tiles pass through LDS once more as fp32 rows and leave as the gradient
+//     w.r.t. the raw rows, with one dgamma partial per workgroup.
+#include <algorithm>
 #include <type_traits>
 
 #include "xattn_device.h"
@@ -279,6 +283,196 @@ __device__ __forceinline__ void store_col(TO* dst, const f32x16 (&acc)[HD / 32],
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Prologue backward fused into the dq / dk stores (Mint documentation 5.4.4 and 5.5.2; the
+// arithmetic of the standalone prologue backward).  The gradient w.r.t. the rotated,
+// normalised rows never goes to HBM: the accumulator tiles (scaled) are written to LDS as
+// fp32 rows, and each wave then walks rows in row-major order the way the standalone
+// kernel does: HD/16 lanes per row, lane part p owning columns [8p, 8p+8) and the matching
+// second-half columns (complete rotation pairs), 16-byte loads of x and stores of dx, and
+// the row sum over the HD/16 lanes.  The dgamma terms of a workgroup's rows are summed in
+// a fixed order into one partial slot per workgroup, reduced by a separate launch.
+// ---------------------------------------------------------------------------------------
+struct ProBwd {
+  const bf16* x;         // pre-norm rows, indexed like the gradient ([rows, S, HD])
+  const float* gamma;    // [HD]
+  const float* rstd;     // [rows * S], from the prologue forward
+  const float* cos_tab;  // [S, HD / 2]
+  const float* sin_tab;  // [S, HD / 2]
+  float* partials;       // [HD][nparts] column-major, one slot per workgroup
+  int nparts;
+};
+
+// LDS tile of fp32 rows of HD: row r, 16-byte chunk c at chunk position c ^ (r & 15)
+// (the rows a b128 access phase touches fall on distinct bank groups).
+template <int HD>
+__device__ __forceinline__ f32x4* epi_chunk(float* tile, int r, int c) {
+  return reinterpret_cast<f32x4*>(tile + r * HD + 4 * (c ^ (r & 15)));
+}
+
+// acc * mul (accumulator layout: row lane%32, column 32 dt + 8 g + 4 h + j) into tile rows
+// 0..31.
+template <int HD>
+__device__ __forceinline__ void acc_to_tile(float* tile, const f32x16 (&acc)[HD / 32],
+                                            float mul, int lane) {
+  const int c32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = acc[dt][4 * g + j] * mul;
+      *epi_chunk<HD>(tile, c32, 8 * dt + 2 * g + h) = o;
+    }
+}
+
+// Sums v[0..N) over the lanes that differ in lane bits M, M/2, .., MLAST by recursive
+// halving: at the step for bit m the lane keeps one half of its remaining values (the upper
+// one if its bit m is set), sends the other half to lane ^ m and adds what that lane sends.
+// Fixed order, so bitwise reproducible.
+template <int NV, int N, int M, int MLAST>
+__device__ __forceinline__ void halving_sum(float (&v)[NV], int lane) {
+  constexpr int H = N / 2;
+  const bool up = (lane & M) != 0;
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const float keep = up ? v[k + H] : v[k];
+    const float send = up ? v[k] : v[k + H];
+    v[k] = keep + shfl_xor(send, M);
+  }
+  if constexpr (M > MLAST) halving_sum<NV, H, M / 2, MLAST>(v, lane);
+}
+
+// s_waitcnt lgkmcnt(0) + workgroup barrier + LDS acquire; outstanding global stores are
+// not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  wait_vm<63>();
+  __builtin_amdgcn_s_barrier();
+  lds_acquire();
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each group of LPR (4 or 8) consecutive lanes, the same value in every lane of the
+// group: DPP xor-1 and xor-2 quad permutations, then (LPR = 8) the mirrored lane of the
+// half-row, which lies in the other quad.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_f32<0xB1>(v);  // quad_perm [1, 0, 3, 2]
+  v += dpp_f32<0x4E>(v);  // quad_perm [2, 3, 0, 1]
+  if constexpr (LPR == 8) v += dpp_f32<0x141>(v);  // row_half_mirror
+  static_assert(LPR == 4 || LPR == 8, "row group of 4 or 8 lanes");
+  return v;
+}
+
+// Prologue backward of tile rows r0 .. r0 + NROWS - 1, the gradient w.r.t. y at positions
+// t0 + r of the head whose rows start at head_row0; writes dx rows into dx_head + t * HD
+// and adds the lane's dgamma terms (its 16 columns) into dg.  Rows t >= S store and
+// contribute nothing.  Every load of the NROWS rows is issued before the arithmetic, so
+// the passes share one memory round trip.
+template <int HD, int NROWS>
+__device__ __forceinline__ void pro_rows(float* tile, int r0, bf16* __restrict__ dx_head,
+                                         const ProBwd& pb, size_t head_row0, int t0, int S,
+                                         int lane, float (&dg)[16]) {
+  constexpr int HALF = HD / 2, LPR = HD / 16, RPI = 64 / LPR, NIT = NROWS / RPI;
+  static_assert(NROWS % RPI == 0, "whole row passes");
+  const int part = lane % LPR, slot = lane / LPR;
+  const int c1 = 8 * part;
+  float g[16];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    g[e] = pb.gamma[c1 + e];
+    g[8 + e] = pb.gamma[HALF + c1 + e];
+  }
+  float rr[NIT];
+  bf16x8 x1[NIT], x2[NIT];
+  f32x4 cs[NIT][2], sn[NIT][2], d1[NIT][2], d2[NIT][2];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int r = r0 + it * RPI + slot, t = t0 + r;
+    const int tc = t < S ? t : S - 1;
+    const size_t row = head_row0 + tc;
+    rr[it] = pb.rstd[row];
+    x1[it] = *reinterpret_cast<const bf16x8*>(pb.x + row * HD + c1);
+    x2[it] = *reinterpret_cast<const bf16x8*>(pb.x + row * HD + HALF + c1);
+    const float* cr = pb.cos_tab + (size_t)tc * HALF + c1;
+    const float* sr = pb.sin_tab + (size_t)tc * HALF + c1;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      cs[it][u] = *reinterpret_cast<const f32x4*>(cr + 4 * u);
+      sn[it][u] = *reinterpret_cast<const f32x4*>(sr + 4 * u);
+      d1[it][u] = *epi_chunk<HD>(tile, r, c1 / 4 + u);
+      d2[it][u] = *epi_chunk<HD>(tile, r, (HALF + c1) / 4 + u);
+    }
+  }
+  bf16x8 o1[NIT], o2[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const bool valid = t0 + r0 + it * RPI + slot < S;
+    float n[16], xf[16];
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float a = d1[it][e / 4][e % 4], b = d2[it][e / 4][e % 4];
+      const float c = cs[it][e / 4][e % 4], sv = sn[it][e / 4][e % 4];
+      n[e] = a * c + b * sv;  // rotation by the negative angle
+      n[8 + e] = b * c - a * sv;
+      xf[e] = (float)x1[it][e];
+      xf[8 + e] = (float)x2[it][e];
+      dot += g[e] * n[e] * xf[e] + g[8 + e] * n[8 + e] * xf[8 + e];
+    }
+    dot = group_sum<LPR>(dot);
+    const float r = rr[it];
+    const float coef = dot * r * r * r * (1.0f / (float)HD);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o1[it][e] = (bf16)(g[e] * n[e] * r - xf[e] * coef);
+      o2[it][e] = (bf16)(g[8 + e] * n[8 + e] * r - xf[8 + e] * coef);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dg[e] += valid ? n[e] * xf[e] * r : 0.f;
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int t = t0 + r0 + it * RPI + slot;
+    if (t < S) {
+      *reinterpret_cast<bf16x8*>(dx_head + (size_t)t * HD + c1) = o1[it];
+      *reinterpret_cast<bf16x8*>(dx_head + (size_t)t * HD + HALF + c1) = o2[it];
+    }
+  }
+}
+
+// Workgroup dgamma partial from the four waves' dg: each wave sums its lanes' terms per
+// column (halving over the row-slot lane bits) into red_w (HD floats of LDS only this wave
+// uses until the barrier; wave w's at red0 + w * red_stride), then threads 0..HD-1 add the
+// four waves in wave order into partial slot `slot`.  Every thread of the workgroup calls.
+template <int HD>
+__device__ __forceinline__ void pro_partial(float (&dg)[16], float* red0, int red_stride,
+                                            const ProBwd& pb, int slot, int wv, int lane,
+                                            int tid) {
+  constexpr int HALF = HD / 2, LPR = HD / 16, PER = LPR / 4;  // columns per lane after sum
+  halving_sum<16, 16, 32, LPR>(dg, lane);
+  float* red = red0 + wv * red_stride;
+  const int part = lane % LPR, slot_bits = lane / LPR;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int k = PER * slot_bits + e;  // index into the lane's 16 columns
+    const int col = (k < 8 ? 0 : HALF - 8) + 8 * part + k;
+    red[col] = dg[e];
+  }
+  lds_barrier();
+  if (tid < HD) {
+    const float s = ((red0[tid] + red0[red_stride + tid]) + red0[2 * red_stride + tid]) +
+                    red0[3 * red_stride + tid];
+    pb.partials[(size_t)tid * pb.nparts + slot] = s;
+  }
+}
+
 // Block -> (query head, query tile) with the query tiles walked heaviest first and, when
 // the KV rows split evenly over the 8 XCDs, the query heads of KV row kv placed on XCD
 // kv % 8 (blocks are dispatched to XCDs round robin).
@@ -467,12 +661,12 @@ __device__ __forceinline__ void dq_subtile(f32x16 (&acc)[HD / 32], const f32x16&
   acc_tr<HD>(acc, ksub, tl, db);  // dQ^T += K^T dS^T
 }
 
-template <int HD, int NBUF, typename TG>
+template <int HD, int NBUF, bool PRO>
 __global__ __launch_bounds__(256, 2) void dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ out, const bf16* __restrict__ dout, const float* __restrict__ lse,
-    float* __restrict__ lse2_out, float* __restrict__ delta, TG* __restrict__ dq, int S, int H,
-    int Hkv, float scale_log2, float scale, int nqt, int xcd) {
+    float* __restrict__ lse2_out, float* __restrict__ delta, bf16* __restrict__ dq, int S, int H,
+    int Hkv, float scale_log2, float scale, int nqt, int xcd, ProBwd pro) {
   constexpr int ROWB = 2 * HD;
   constexpr int TILEB = kBN * ROWB;
   using D = Dma<HD, kBN, 4>;
@@ -544,7 +738,19 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
   const int nplain = min(q0 / kBN, S / kBN);
   for (int t = 0; t < nplain; ++t) stage(std::false_type{}, t);
   for (int t = nplain; t < ntiles; ++t) stage(std::true_type{}, t);
-  if (qrow < S) store_col<TG, HD>(dq + ((size_t)bh * S + qrow) * HD, acc, scale, h);
+  if constexpr (PRO) {
+    static_assert(sizeof(lds) >= 4 * 32 * HD * sizeof(float), "epilogue tiles fit");
+    lds_barrier();  // every wave is done with the staged tiles
+    float* tile = reinterpret_cast<float*>(lds) + wv * 32 * HD;
+    acc_to_tile<HD>(tile, acc, scale, lane);
+    float dg[16] = {};
+    pro_rows<HD, 32>(tile, 0, dq + hoff, pro, (size_t)bh * S, qw0, S, lane, dg);
+    asm volatile("" ::: "memory");
+    pro_partial<HD>(dg, reinterpret_cast<float*>(lds), 32 * HD, pro, bh * nqt + mp.qt, wv, lane,
+                    tid);
+  } else if (qrow < S) {
+    store_col<bf16, HD>(dq + ((size_t)bh * S + qrow) * HD, acc, scale, h);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -640,17 +846,18 @@ __device__ __forceinline__ void dkdv_step_reg(f32x16 (&dkt)[HD / 32], f32x16 (&d
 
 // Shared variant: 4 waves own 128 consecutive keys of one KV head and share each staged
 // 32-query tile of every query head of the group.
-template <int HD, int NBUF, typename TG>
+template <int HD, int NBUF, bool PRO>
 __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_shared_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse2,
-    const float* __restrict__ delta, TG* __restrict__ dk, bf16* __restrict__ dv, int S, int H,
-    int Hkv, float scale_log2, float scale, int nkt, int xcd) {
+    const float* __restrict__ delta, bf16* __restrict__ dk, bf16* __restrict__ dv, int S, int H,
+    int Hkv, float scale_log2, float scale, int nkt, int xcd, ProBwd pro) {
   constexpr int ROWB = 2 * HD;
   constexpr int TILEB = kBQ * ROWB;
   using D = Dma<HD, kBQ, 4>;
   constexpr int NL = 2 * D::PER + 1;
-  __shared__ __attribute__((aligned(1024))) char lds[NBUF * 2 * TILEB];
+  constexpr int EPIB = PRO ? 4 * 32 * HD * (int)sizeof(float) : 0;  // epilogue tiles
+  __shared__ __attribute__((aligned(1024))) char lds[std::max(NBUF * 2 * TILEB, EPIB)];
   __shared__ __attribute__((aligned(16))) float stats[NBUF][64];
   const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -708,21 +915,33 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_shared_kernel(
     for (int i = nmask_head; i < plain_end; ++i) stage(std::false_type{}, t0 + i);
     if (plain_end < per_r) stage(std::true_type{}, t0 + per_r - 1);
   }
-  if (key < S) {
-    store_col<TG, HD>(dk + ((size_t)kvbh * S + key) * HD, dkt, scale, h);
-    store_col<bf16, HD>(dv + ((size_t)kvbh * S + key) * HD, dvt, 1.0f, h);
+  if (key < S) store_col<bf16, HD>(dv + ((size_t)kvbh * S + key) * HD, dvt, 1.0f, h);
+  if constexpr (PRO) {
+    lds_barrier();  // every wave is done with the staged tiles
+    float* tile = reinterpret_cast<float*>(lds) + wv * 32 * HD;
+    float dg[16] = {};
+    if (kw0 < S) {
+      acc_to_tile<HD>(tile, dkt, scale, lane);
+      pro_rows<HD, 32>(tile, 0, dk + (size_t)kvbh * S * HD, pro, (size_t)kvbh * S, kw0, S,
+                       lane, dg);
+    }
+    asm volatile("" ::: "memory");
+    pro_partial<HD>(dg, reinterpret_cast<float*>(lds), 32 * HD, pro, kvbh * nkt + kt, wv, lane,
+                    tid);
+  } else if (key < S) {
+    store_col<bf16, HD>(dk + ((size_t)kvbh * S + key) * HD, dkt, scale, h);
   }
 }
 
 // Private variant: 4 waves own the same 32 keys of one KV head; wave w walks query tiles
 // w, w+4, w+8, ... (of every query head of the group, r ascending) through its own LDS
 // buffers, so the main loop needs no barrier.  Partials are added in wave order.
-template <int HD, int NBUF, typename TG>
+template <int HD, int NBUF, bool PRO>
 __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_private_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse2,
-    const float* __restrict__ delta, TG* __restrict__ dk, bf16* __restrict__ dv, int S, int H,
-    int Hkv, float scale_log2, float scale, int nkt, int xcd) {
+    const float* __restrict__ delta, bf16* __restrict__ dk, bf16* __restrict__ dv, int S, int H,
+    int Hkv, float scale_log2, float scale, int nkt, int xcd, ProBwd pro) {
   constexpr int ROWB = 2 * HD;
   constexpr int TILEB = kBQ * ROWB;
   constexpr int WAVEB = NBUF * 2 * TILEB;  // one wave's staging bytes
@@ -827,8 +1046,28 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_private_kernel(
       }
     }
   }
-  if (wv == 0 && key < S) {
-    store_col<TG, HD>(dk + ((size_t)kvbh * S + key) * HD, dkt, scale, h);
+  if constexpr (PRO) {
+    // wave 0 holds the sums; the prologue backward of the 32 rows is shared by the waves
+    constexpr int TILE_AT = 16384, RED_AT = 32768;  // clear of the combination slots
+    static_assert(sizeof(lds) >= RED_AT + 4 * HD * sizeof(float), "epilogue fits");
+    float* tile = reinterpret_cast<float*>(lds + TILE_AT);
+    if (wv == 0) {
+      acc_to_tile<HD>(tile, dkt, scale, lane);
+      if (key < S) store_col<bf16, HD>(dv + ((size_t)kvbh * S + key) * HD, dvt, 1.0f, h);
+    }
+    lds_barrier();
+    constexpr int RPW = 64 / (HD / 16);  // rows per wave: one row-major pass
+    float dg[16] = {};
+    if (wv * RPW < 32)
+      pro_rows<HD, RPW>(tile, wv * RPW, dk + (size_t)kvbh * S * HD, pro, (size_t)kvbh * S,
+                        kw0, S, lane, dg);
+    pro_partial<HD>(dg, reinterpret_cast<float*>(lds + RED_AT), HD, pro, kvbh * nkt + kt, wv,
+                    lane, tid);
+    return;
+  }
+  if (wv != 0) return;
+  if (key < S) {
+    store_col<bf16, HD>(dk + ((size_t)kvbh * S + key) * HD, dkt, scale, h);
     store_col<bf16, HD>(dv + ((size_t)kvbh * S + key) * HD, dvt, 1.0f, h);
   }
 }
@@ -852,10 +1091,15 @@ hipError_t fwd_launch(const AttnShape& s, const void* q, const void* k, const vo
   return hipPeekAtLastError();
 }
 
-template <int HD, typename TG>
+// dk/dv kernel choice: the shared-tile kernel when its 128-key workgroups fill the
+// machine, else the private one (32 keys per workgroup).
+bool dkdv_shared(int BKV, int S) { return (long long)BKV * ((S + 127) / 128) >= 1024; }
+
+template <int HD, bool PRO>
 hipError_t bwd_launch(const AttnShape& s, const void* q, const void* k, const void* v,
                       const void* out, const float* lse, const void* dout, void* dq, void* dk,
-                      void* dv, float* delta, float* lse2, hipStream_t stream) {
+                      void* dv, float* delta, float* lse2, const ProBwd& pq, const ProBwd& pk,
+                      hipStream_t stream) {
   const int S = s.seq_len;
   const int nqt = (S + kBM - 1) / kBM;
   const int BH = s.batch * s.num_heads;
@@ -864,29 +1108,38 @@ hipError_t bwd_launch(const AttnShape& s, const void* q, const void* k, const vo
   const float scale = 1.0f / sqrtf((float)HD), sl2 = kLog2e * scale;
   {
     ProfScope prof("attn_bwd_dq", stream);
-    hipLaunchKernelGGL((dq_kernel<HD, kDqBuf, TG>), dim3(BH * nqt), dim3(256), 0, stream,
+    hipLaunchKernelGGL((dq_kernel<HD, kDqBuf, PRO>), dim3(BH * nqt), dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)out,
-                       (const bf16*)dout, lse, lse2, delta, (TG*)dq, S, s.num_heads,
-                       s.num_kv_heads, sl2, scale, nqt, xcd);
+                       (const bf16*)dout, lse, lse2, delta, (bf16*)dq, S, s.num_heads,
+                       s.num_kv_heads, sl2, scale, nqt, xcd, pq);
   }
   hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess) return e;
-  const long long shared_blocks = (long long)BKV * ((S + 127) / 128);
   ProfScope prof("attn_bwd_dkdv", stream);
-  if (shared_blocks >= 1024) {
+  if (dkdv_shared(BKV, S)) {
     const int nkt = (S + 127) / 128;
-    hipLaunchKernelGGL((dkdv_shared_kernel<HD, kDkdvSharedBuf, TG>), dim3(BKV * nkt), dim3(256),
-                       0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
-                       (const bf16*)dout, (const float*)lse2, (const float*)delta, (TG*)dk,
-                       (bf16*)dv, S, s.num_heads, s.num_kv_heads, sl2, scale, nkt, xcd);
+    hipLaunchKernelGGL((dkdv_shared_kernel<HD, kDkdvSharedBuf, PRO>), dim3(BKV * nkt),
+                       dim3(256), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
+                       (const bf16*)dout, (const float*)lse2, (const float*)delta, (bf16*)dk,
+                       (bf16*)dv, S, s.num_heads, s.num_kv_heads, sl2, scale, nkt, xcd, pk);
   } else {
     const int nkt = (S + 31) / 32;
-    hipLaunchKernelGGL((dkdv_private_kernel<HD, kDkdvPrivateBuf, TG>), dim3(BKV * nkt),
+    hipLaunchKernelGGL((dkdv_private_kernel<HD, kDkdvPrivateBuf, PRO>), dim3(BKV * nkt),
                        dim3(256), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
-                       (const bf16*)dout, (const float*)lse2, (const float*)delta, (TG*)dk,
-                       (bf16*)dv, S, s.num_heads, s.num_kv_heads, sl2, scale, nkt, xcd);
+                       (const bf16*)dout, (const float*)lse2, (const float*)delta, (bf16*)dk,
+                       (bf16*)dv, S, s.num_heads, s.num_kv_heads, sl2, scale, nkt, xcd, pk);
   }
   return hipPeekAtLastError();
+}
+
+ProBwd make_pro(const void* x, const float* gamma, const float* rstd, const float* cos_tab,
+                const float* sin_tab, float* partials, int nparts) {
+  ProBwd p;
+  p.x = static_cast<const bf16*>(x);
+  p.gamma = gamma, p.rstd = rstd, p.cos_tab = cos_tab, p.sin_tab = sin_tab;
+  p.partials = partials;
+  p.nparts = nparts;
+  return p;
 }
 
 }  // namespace
@@ -900,23 +1153,40 @@ hipError_t launch_attn_fwd_bf16_fast(const AttnShape& s, const void* q, const vo
   return hipErrorInvalidValue;
 }
 
+// dgamma partial slots: one per dq workgroup (128 queries), one per dk/dv workgroup
+// (128 or 32 keys; the workspace is sized for 32).
+int fused_pro_parts_q(int64_t q_heads, int seq_len) {
+  return (int)(q_heads * ((seq_len + kBM - 1) / kBM));
+}
+int fused_pro_parts_k(int64_t kv_heads, int seq_len) {
+  return (int)(kv_heads * ((seq_len + 31) / 32));
+}
+
 hipError_t launch_attn_bwd_bf16_fast(const AttnShape& s, const void* q, const void* k,
                                      const void* v, const void* out, const float* lse,
                                      const void* dout, void* dq, void* dk, void* dv,
-                                     float* delta, float* lse2, bool grads_f32,
+                                     float* delta, float* lse2, const ProFuse* pro,
                                      hipStream_t stream) {
-#define XATTN_CASE(HD, TG)                                                                \
-  return bwd_launch<HD, TG>(s, q, k, v, out, lse, dout, dq, dk, dv, delta, lse2, stream);
-  if (s.head_dim == 128) {
-    if (grads_f32) { XATTN_CASE(128, float) }
-    XATTN_CASE(128, bf16)
+  ProBwd pq{}, pk{};
+  if (pro != nullptr) {
+    const int BKV = s.batch * s.num_kv_heads, S = s.seq_len;
+    pq = make_pro(pro->xq, pro->gamma_q, pro->rstd_q, pro->cos_tab, pro->sin_tab,
+                  pro->partials_q, fused_pro_parts_q(s.batch * s.num_heads, S));
+    pk = make_pro(pro->xk, pro->gamma_k, pro->rstd_k, pro->cos_tab, pro->sin_tab,
+                  pro->partials_k, BKV * (dkdv_shared(BKV, S) ? (S + 127) / 128 : (S + 31) / 32));
   }
-  if (s.head_dim == 64) {
-    if (grads_f32) { XATTN_CASE(64, float) }
-    XATTN_CASE(64, bf16)
+#define XATTN_CASE(HD, PRO)                                                                \
+  e = bwd_launch<HD, PRO>(s, q, k, v, out, lse, dout, dq, dk, dv, delta, lse2, pq, pk, stream);
+  hipError_t e = hipErrorInvalidValue;
+  if (s.head_dim == 128) {
+    if (pro != nullptr) { XATTN_CASE(128, true) } else { XATTN_CASE(128, false) }
+  } else if (s.head_dim == 64) {
+    if (pro != nullptr) { XATTN_CASE(64, true) } else { XATTN_CASE(64, false) }
   }
 #undef XATTN_CASE
-  return hipErrorInvalidValue;
+  if (e != hipSuccess || pro == nullptr) return e;
+  return launch_dgamma_reduce_qk(s.head_dim, pq.partials, pq.nparts, pro->dgamma_q,
+                                 pk.partials, pk.nparts, pro->dgamma_k, stream);
 }
 
 }  // namespace xattn

@@ -417,4 +417,38 @@ hipError_t launch_qknorm_rope_bwd_qk(IoType dy_io, IoType x_io, int head_dim, co
   return bwd_types(dy_io, x_io, head_dim, jq, jk, cos_tab, sin_tab, seq_len, stream);
 }
 
+// One block per dgamma column of one or two tensors, for many partials per column:
+// thread t sums partials t, t + 256, ... in ascending order, a fixed xor butterfly
+// combines each wave and thread 0 adds the four wave sums in wave order.
+__global__ __launch_bounds__(256) void dgamma_reduce_wide_kernel(const float* __restrict__ pq,
+                                                                 int nq, float* __restrict__ gq,
+                                                                 const float* __restrict__ pk,
+                                                                 int nk, float* __restrict__ gk,
+                                                                 int head_dim) {
+  __shared__ float wsum[4];
+  const bool second = (int)blockIdx.x >= head_dim;
+  const int col = second ? blockIdx.x - head_dim : blockIdx.x;
+  const int n = second ? nk : nq;
+  const float* p = (second ? pk : pq) + (size_t)col * n;
+  const int tid = threadIdx.x;
+  float s = 0.f;
+#pragma unroll 8
+  for (int b = tid; b < n; b += 256) s += p[b];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) s += shfl_xor(s, m);
+  if ((tid & 63) == 0) wsum[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) (second ? gk : gq)[col] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+}
+
+hipError_t launch_dgamma_reduce_qk(int head_dim, const float* partials_q, int nparts_q,
+                                   float* dgamma_q, const float* partials_k, int nparts_k,
+                                   float* dgamma_k, hipStream_t stream) {
+  const int njobs = nparts_k > 0 ? 2 : 1;
+  ProfScope prof("dgamma_reduce", stream);
+  hipLaunchKernelGGL(dgamma_reduce_wide_kernel, dim3(njobs * head_dim), dim3(256), 0, stream,
+                     partials_q, nparts_q, dgamma_q, partials_k, nparts_k, dgamma_k, head_dim);
+  return hipPeekAtLastError();
+}
+
 }  // namespace xattn

@@ -136,9 +136,20 @@ DimsChecked check_dims(const xattn_dims* d) {
   return c;
 }
 
+// The bf16 fast path applies the prologue backward inside its dq / dk stores.
+bool fused_prologue_bwd(const DimsChecked& c) {
+  return c.io == xattn::IO_BF16 && xattn::fast_bf16_supported(c.s.head_dim);
+}
+
 size_t bwd_workspace(const DimsChecked& c, bool with_prologue) {
   size_t n = 2 * align256((size_t)c.rows_q * sizeof(float));  // delta, lse * log2(e)
-  if (with_prologue) {
+  if (with_prologue && fused_prologue_bwd(c)) {
+    const int64_t hq = (int64_t)c.s.batch * c.s.num_heads;
+    const int64_t hk = (int64_t)c.s.batch * c.s.num_kv_heads;
+    const size_t col = (size_t)c.s.head_dim * sizeof(float);  // dgamma partials per slot
+    n += align256((size_t)xattn::fused_pro_parts_q(hq, c.s.seq_len) * col);
+    n += align256((size_t)xattn::fused_pro_parts_k(hk, c.s.seq_len) * col);
+  } else if (with_prologue) {
     const int64_t rows_k = (int64_t)c.s.batch * c.s.num_kv_heads * c.s.seq_len;
     n += align256((size_t)c.q_elems * sizeof(float));      // dq w.r.t. the rotated q
     n += align256((size_t)c.kv_elems * sizeof(float));     // dk w.r.t. the rotated k
@@ -360,6 +371,22 @@ xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, con
     if (pro == nullptr) {
       hip_check(xattn::launch_attn_bwd(c.io, c.s, q, k, v, out, lse, dout, dq, dk, dv, delta,
                                        lse2, false, st),
+                "attention backward launch");
+      return;
+    }
+    if (fused_prologue_bwd(c)) {
+      xattn::ProFuse pf;
+      pf.xq = pro->xq, pf.xk = pro->xk, pf.gamma_q = pro->gamma_q, pf.gamma_k = pro->gamma_k;
+      pf.rstd_q = pro->rstd_q, pf.rstd_k = pro->rstd_k;
+      pf.cos_tab = pro->cos_tab, pf.sin_tab = pro->sin_tab;
+      pf.dgamma_q = pro->dgamma_q, pf.dgamma_k = pro->dgamma_k;
+      const int64_t hq = (int64_t)c.s.batch * c.s.num_heads;
+      pf.partials_q = reinterpret_cast<float*>(ws);
+      ws += align256((size_t)xattn::fused_pro_parts_q(hq, c.s.seq_len) * c.s.head_dim *
+                     sizeof(float));
+      pf.partials_k = reinterpret_cast<float*>(ws);
+      hip_check(xattn::launch_attn_bwd_bf16_fast(c.s, q, k, v, out, lse, dout, dq, dk, dv,
+                                                 delta, lse2, &pf, st),
                 "attention backward launch");
       return;
     }

@@ -41,6 +41,12 @@ hipError_t launch_qknorm_rope_bwd_qk(IoType dy_io, IoType x_io, int head_dim, co
                                      float* partials_k, int nrows_k, const float* cos_tab,
                                      const float* sin_tab, int seq_len, hipStream_t stream);
 
+// dgamma of one or two tensors from per-slot partials ([head_dim][nparts], column-major),
+// summed in a fixed order.  nparts_k == 0 reduces the first tensor only.
+hipError_t launch_dgamma_reduce_qk(int head_dim, const float* partials_q, int nparts_q,
+                                   float* dgamma_q, const float* partials_k, int nparts_k,
+                                   float* dgamma_k, hipStream_t stream);
+
 // ---- attention -----------------------------------------------------------------------
 struct AttnShape {
   int batch, seq_len, num_heads, num_kv_heads, head_dim;
@@ -54,10 +60,23 @@ hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const v
 bool fast_bf16_supported(int head_dim);
 hipError_t launch_attn_fwd_bf16_fast(const AttnShape& s, const void* q, const void* k,
                                      const void* v, void* out, float* lse, hipStream_t stream);
+//
+// With `pro` non-null the prologue backward is applied in the dq and dk stores: dq, dk
+// receive the gradients w.r.t. the raw xq, xk (io dtype) and dgamma_q, dgamma_k are
+// written from partials_q / partials_k (workspace of fused_pro_parts_q(B*H, S) and
+// fused_pro_parts_k(B*Hkv, S) slots of head_dim floats each).
+struct ProFuse {
+  const void* xq;
+  const void* xk;
+  const float *gamma_q, *gamma_k, *rstd_q, *rstd_k, *cos_tab, *sin_tab;
+  float *partials_q, *partials_k, *dgamma_q, *dgamma_k;
+};
+int fused_pro_parts_q(int64_t q_heads, int seq_len);
+int fused_pro_parts_k(int64_t kv_heads, int seq_len);
 hipError_t launch_attn_bwd_bf16_fast(const AttnShape& s, const void* q, const void* k,
                                      const void* v, const void* out, const float* lse,
                                      const void* dout, void* dq, void* dk, void* dv,
-                                     float* delta, float* lse2, bool grads_f32,
+                                     float* delta, float* lse2, const ProFuse* pro,
                                      hipStream_t stream);
 
 // grads_f32: when true, dq and dk are written as fp32 (used when the prologue backward

@@ -140,7 +140,10 @@ size_t xattn_bwd_workspace_bytes(const xattn_dims* dims, int with_prologue);
  * atomics, bitwise reproducible run to run (dq, too).
  * pro == NULL: dq, dk are gradients w.r.t. the q, k that xattn_fwd consumed.
  * pro != NULL: the prologue backward runs too; dq, dk are then gradients w.r.t. the raw
- * pro->xq, pro->xk and pro->dgamma_q / dgamma_k are written.
+ * pro->xq, pro->xk and pro->dgamma_q / dgamma_k are written (the arithmetic of
+ * xattn_qknorm_rope_bwd; dgamma summed in a fixed order, bitwise reproducible).  For bf16
+ * io at hd 64 / 128 it is applied inside the dq and dk stores (the gradients w.r.t. the
+ * rotated q, k never reach memory); otherwise as a separate pass over fp32 gradients.
  * q, out, dout, dq: [B*H, S, hd]; k, v, dk, dv: [B*Hkv, S, hd]; lse: [B*H*S] fp32 from
  * xattn_fwd.  workspace: device memory of at least xattn_bwd_workspace_bytes bytes. */
 xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, const void* v,

@@ -118,6 +118,28 @@ def test_attention_shared_dkdv_path_matches_oracle(w, nkv):
     print(w.name, {k: f"{e:.2e}" for k, e in errs.items()})
 
 
+SHARED_PATH_STEP = [
+    SHARED_PATH[0][0],
+    W.small_ragged("bf16", 64, 100, 256, 8, 4, theta=1e4, eps=1e-6, index=232),
+]
+
+
+@pytest.mark.parametrize("w", SHARED_PATH_STEP,
+                         ids=[f"hd{w.head_dim}_S{w.seq_len}_B{w.batch}" for w in SHARED_PATH_STEP])
+def test_step_shared_dkdv_path_matches_oracle(w):
+    """Whole step (prologue backward fused into the dk stores of the shared-tile dk/dv
+    kernel), every head and dgamma compared."""
+    assert w.bkv * -(-w.seq_len // 128) >= 1024
+    x = W.make_inputs(w)
+    note(f"step (shared dk/dv path) {w}")
+    g = run_step(w, x)
+    f = oracle.forward(x.xq, x.xk, x.v, x.gamma_q, x.gamma_k, w.num_heads, w.num_kv_heads,
+                       w.eps, w.theta)
+    b = oracle.backward(x.xq, x.xk, x.v, x.gamma_q, x.gamma_k, x.dout, w.num_heads,
+                        w.num_kv_heads, w.eps, w.theta)
+    _compare_step(w, g, f, b)
+
+
 @pytest.mark.parametrize("idx", [3, 4, 5])
 def test_full_size_step_on_sampled_heads(idx):
     w = W.WORKLOADS[idx]
