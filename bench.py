@@ -2,10 +2,12 @@
 """Benchmark: causal GQA attention fwd+bwd (with the QK-norm + RoPE prologue) on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input: RoPE cache,
-QK-norm + RoPE on Q and K, attention forward, attention backward with the group sum and
-the prologue backward (for bf16 io applied inside the dq and dk/dv kernels' stores), and
-the dgamma reductions (libxattn kernels only, preallocated buffers, one stream).  The workload is the long-context Qwen3-shaped GQA configuration (B=1,
-S=4096, 32 query heads, 8 KV heads, head_dim 128, bf16 in / fp32 accumulate).
+QK-norm + RoPE on K, attention forward (for bf16 io with QK-norm + RoPE of Q inside it),
+attention backward with the group sum and the prologue backward (for bf16 io applied inside
+the dq and dk/dv kernels' stores), and the dgamma reductions (libxattn kernels only,
+preallocated buffers, one stream).  The workload is the long-context Qwen3-shaped GQA
+configuration (B=1, S=4096, 32 query heads, 8 KV heads, head_dim 128, bf16 in / fp32
+accumulate).
 
 value = algorithmic attention FLOP per step (12 * hd per causal pair per query head:
 4 * hd forward, 8 * hd backward; recompute not counted) / measured step time, in TFLOP/s.
@@ -57,13 +59,15 @@ def kernel_units(w):
     hd = w.head_dim
     io = 2 if w.dtype == "bf16" else 4
     rows_q, rows_k = w.bh * w.seq_len, w.bkv * w.seq_len
+    fused_q = w.dtype == "bf16" and hd in (64, 128)
     return {
         "attn_fwd": ("mfma", 4 * hd * pairs, "QK^T and PV: 4*hd per causal pair"),
         "attn_bwd_dkdv": ("mfma", 6 * hd * pairs, "dP, dV, dK: 6*hd per causal pair"),
         "attn_bwd_dq": ("mfma", 2 * hd * pairs, "dQ: 2*hd per causal pair"),
-        # prologue: per launch average over the Q launch and the K launch
-        "qknorm_rope_fwd": ("hbm", ((rows_q + rows_k) * (hd * 2 * io + 4)) / 2,
-                            "read x, write y (io dtype), write rstd"),
+        # prologue forward: K alone when the Q side runs inside attn_fwd (bf16, hd 64/128),
+        # else the per-launch average over the Q launch and the K launch
+        "qknorm_rope_fwd": ("hbm", (rows_k if fused_q else (rows_q + rows_k) / 2)
+                            * (hd * 2 * io + 4), "read x, write y (io dtype), write rstd"),
         # standalone prologue backward (fp32 io; bf16 io fuses it into attn_bwd_dq / dkdv):
         # one launch for Q and K together
         "qknorm_rope_bwd": ("hbm", (rows_q + rows_k) * (hd * (4 + 2 * io) + 4),

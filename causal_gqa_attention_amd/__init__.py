@@ -21,10 +21,12 @@ import torch
 __all__ = [
     "XattnError", "library_path", "load_library",
     "xattn_rope_cache", "xattn_qknorm_rope_fwd", "xattn_qknorm_rope_bwd_workspace_bytes",
-    "xattn_qknorm_rope_bwd", "xattn_fwd", "xattn_bwd_workspace_bytes", "xattn_bwd",
+    "xattn_qknorm_rope_bwd", "xattn_fwd", "xattn_fwd_qnorm", "xattn_bwd_workspace_bytes",
+    "xattn_bwd",
     "xattn_status_string", "xattn_last_error", "xattn_version", "xattn_profile_start",
     "xattn_profile_stop",
-    "rope_cache", "qknorm_rope_fwd", "qknorm_rope_bwd", "attn_fwd", "attn_bwd",
+    "rope_cache", "qknorm_rope_fwd", "qknorm_rope_bwd", "attn_fwd", "attn_fwd_qnorm",
+    "attn_bwd",
 ]
 
 XATTN_F32 = 0
@@ -60,6 +62,12 @@ class Prologue(ctypes.Structure):
                 ("dgamma_q", ctypes.c_void_p), ("dgamma_k", ctypes.c_void_p)]
 
 
+class FwdPrologue(ctypes.Structure):
+    _fields_ = [("xq", ctypes.c_void_p), ("gamma_q", ctypes.c_void_p),
+                ("cos_tab", ctypes.c_void_p), ("sin_tab", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("yq", ctypes.c_void_p), ("rstd_q", ctypes.c_void_p)]
+
+
 def library_path() -> str:
     return os.path.join(_HERE, "libxattn.so")
 
@@ -83,6 +91,8 @@ def load_library() -> ctypes.CDLL:
         "xattn_qknorm_rope_bwd": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64,
                                         i32, vp]),
         "xattn_fwd": (i32, [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp]),
+        "xattn_fwd_qnorm": (i32, [ctypes.POINTER(Dims), ctypes.POINTER(FwdPrologue), vp, vp, vp,
+                                  vp, vp]),
         "xattn_bwd_workspace_bytes": (sz, [ctypes.POINTER(Dims), ctypes.c_int]),
         "xattn_bwd": (i32, [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                             ctypes.POINTER(Prologue), vp, sz, vp]),
@@ -211,6 +221,18 @@ def xattn_fwd(dims: Dims, q, k, v, out, lse, stream=None):
         "xattn_fwd")
 
 
+def xattn_fwd_qnorm(dims: Dims, xq, gamma_q, cos_tab, sin_tab, eps, yq, rstd_q, k, v, out,
+                    lse, stream=None):
+    pro = FwdPrologue(_ptr(xq, "xq"), _ptr(gamma_q, "gamma_q", torch.float32),
+                      _ptr(cos_tab, "cos_tab", torch.float32),
+                      _ptr(sin_tab, "sin_tab", torch.float32), float(eps),
+                      _ptr(yq, "yq", xq.dtype), _ptr(rstd_q, "rstd_q", torch.float32))
+    _check(load_library().xattn_fwd_qnorm(
+        ctypes.byref(dims), ctypes.byref(pro), _ptr(k, "k", xq.dtype), _ptr(v, "v", xq.dtype),
+        _ptr(out, "out", xq.dtype), _ptr(lse, "lse", torch.float32), _stream(stream)),
+        "xattn_fwd_qnorm")
+
+
 def xattn_bwd_workspace_bytes(dims: Dims, with_prologue: bool) -> int:
     return int(load_library().xattn_bwd_workspace_bytes(ctypes.byref(dims), int(with_prologue)))
 
@@ -279,6 +301,17 @@ def attn_fwd(q, k, v, num_heads, num_kv_heads, stream=None):
     lse = torch.empty(q.shape[0] * q.shape[1], dtype=torch.float32, device=q.device)
     xattn_fwd(dims, q, k, v, out, lse, stream)
     return out, lse
+
+
+def attn_fwd_qnorm(xq, gamma_q, cos_tab, sin_tab, eps, k, v, num_heads, num_kv_heads,
+                   stream=None):
+    """Forward with the Q-side QK-norm + RoPE fused; returns (out, lse, yq, rstd_q)."""
+    dims = make_dims(xq, num_heads, num_kv_heads)
+    out, yq = torch.empty_like(xq), torch.empty_like(xq)
+    lse = torch.empty(xq.shape[0] * xq.shape[1], dtype=torch.float32, device=xq.device)
+    rstd_q = torch.empty_like(lse)
+    xattn_fwd_qnorm(dims, xq, gamma_q, cos_tab, sin_tab, eps, yq, rstd_q, k, v, out, lse, stream)
+    return out, lse, yq, rstd_q
 
 
 def attn_bwd(q, k, v, out, lse, dout, num_heads, num_kv_heads, prologue=None, stream=None,

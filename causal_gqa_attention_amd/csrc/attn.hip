@@ -469,7 +469,7 @@ static hipError_t fwd_impl(const AttnShape& s, const void* q, const void* k, con
 hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const void* k,
                            const void* v, void* out, float* lse, hipStream_t stream) {
   if (io == IO_BF16 && fast_bf16_supported(s.head_dim))
-    return launch_attn_fwd_bf16_fast(s, q, k, v, out, lse, stream);
+    return launch_attn_fwd_bf16_fast(s, q, k, v, out, lse, nullptr, stream);
 #define XATTN_CASE(T, HD) \
   if (s.head_dim == HD) return fwd_impl<T, HD>(s, q, k, v, out, lse, stream);
   if (io == IO_F32) {

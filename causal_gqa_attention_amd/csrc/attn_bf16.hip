@@ -566,14 +566,86 @@ __device__ __forceinline__ void fwd_subtile(f32x16 (&o)[HD / 32], SoftmaxState& 
   acc_tr<HD>(o, vsub, tl, pb);
 }
 
-template <int HD, int NBUF>
+// QK-norm + RoPE forward on the forward's resident Q rows (Mint documentation 5.4.1,
+// 5.4.4 and 5.5.1; the arithmetic of the standalone prologue forward).  The lane's fragment
+// (load_frag layout: chunk c holds columns 16 c + 8 h .. + 7) keeps both members of every
+// rotation pair (chunks c and c + HD/32) and half of the row, so the mean square needs one
+// exchange between the lane's halves.
+struct ProFwd {
+  const bf16* x;         // raw rows [rows, S, HD]
+  const float* gamma;    // [HD]
+  const float* cos_tab;  // [S, HD / 2]
+  const float* sin_tab;  // [S, HD / 2]
+  bf16* y;               // rotated rows [rows, S, HD] (output)
+  float* rstd;           // [rows * S] (output)
+  float eps;
+};
+
+// Loads the raw row at position t of the head whose rows start at row0 into the lane's
+// fragment and replaces it with y = rotate(gamma * x * rstd) rounded to bf16; y and rstd are
+// also stored when t < S (the fragment is zero past the sequence end).  Every load (x, cos,
+// sin, gamma) is issued before the first use, so they share one memory round trip.
+template <int HD>
+__device__ __forceinline__ void qknorm_rope_frag(bf16x8 (&frag)[HD / 16], const ProFwd& pf,
+                                                 size_t row0, int t, int S, int lane) {
+  constexpr int NC = HD / 16, HC = NC / 2, HALF = HD / 2;
+  const int h = lane >> 5;
+  const bool valid = t < S;
+  const int tc = valid ? t : S - 1;
+  const bf16* xr = pf.x + (row0 + tc) * HD + 8 * h;
+  const float* cr = pf.cos_tab + (size_t)tc * HALF;
+  const float* sr = pf.sin_tab + (size_t)tc * HALF;
+  f32x4 cs[HC][2], sn[HC][2], g1[HC][2], g2[HC][2];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) frag[c] = *reinterpret_cast<const bf16x8*>(xr + 16 * c);
+#pragma unroll
+  for (int c = 0; c < HC; ++c)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int f = 16 * c + 8 * h + 4 * u;
+      cs[c][u] = *reinterpret_cast<const f32x4*>(cr + f);
+      sn[c][u] = *reinterpret_cast<const f32x4*>(sr + f);
+      g1[c][u] = *reinterpret_cast<const f32x4*>(pf.gamma + f);
+      g2[c][u] = *reinterpret_cast<const f32x4*>(pf.gamma + HALF + f);
+    }
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float xv = (float)frag[c][j];
+      ss += xv * xv;
+    }
+  ss += shfl_xor(ss, 32);
+  const float r = 1.0f / sqrtf(ss * (1.0f / (float)HD) + pf.eps);
+#pragma unroll
+  for (int c = 0; c < HC; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int u = j / 4, e = j % 4;
+      const float n1 = (float)frag[c][j] * r * g1[c][u][e];
+      const float n2 = (float)frag[c + HC][j] * r * g2[c][u][e];
+      const float y1 = n1 * cs[c][u][e] - n2 * sn[c][u][e];
+      const float y2 = n1 * sn[c][u][e] + n2 * cs[c][u][e];
+      frag[c][j] = (bf16)(valid ? y1 : 0.f);
+      frag[c + HC][j] = (bf16)(valid ? y2 : 0.f);
+    }
+  if (valid) {
+    bf16* yr = pf.y + (row0 + t) * HD + 8 * h;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) *reinterpret_cast<bf16x8*>(yr + 16 * c) = frag[c];
+    if (h == 0) pf.rstd[row0 + t] = r;
+  }
+}
+
+template <int HD, int NBUF, bool PROQ>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const bf16* __restrict__ q,
                                                      const bf16* __restrict__ k,
                                                      const bf16* __restrict__ v,
                                                      bf16* __restrict__ out,
                                                      float* __restrict__ lse, int S, int H,
                                                      int Hkv, float scale_log2, int nqt,
-                                                     int xcd) {
+                                                     int xcd, ProFwd pro) {
   constexpr int ROWB = 2 * HD;
   constexpr int TILEB = kBN * ROWB;
   using D = Dma<HD, kBN, 4>;
@@ -592,22 +664,29 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const bf16* __restrict__ q,
   D dma;
   dma.init(wv, lane);
 
-  bf16x8 qf[HD / 16];
-  load_frag<HD>(qf, q + (size_t)bh * S * HD, qrow, S, lane);
-  f32x16 o[HD / 32];
-#pragma unroll
-  for (int dt = 0; dt < HD / 32; ++dt) o[dt] = zero16();
-  SoftmaxState sm{-INFINITY, 0.f};
-
   const int ntiles = (min(S, q0 + kBM) + kBN - 1) / kBN;
   auto issue = [&](int t, int buf) {
     const int g0 = t * kBN, nv = S - g0;
     dma.issue(lds + (2 * buf) * TILEB, kp + (size_t)g0 * ROWB, wv, nv);
     dma.issue(lds + (2 * buf + 1) * TILEB, vp + (size_t)g0 * ROWB, wv, nv);
   };
+  bf16x8 qf[HD / 16];
+  if constexpr (PROQ) {
+    // the first tiles' copies are in flight while the Q rows are normalised and rotated
 #pragma unroll
-  for (int t = 0; t < NBUF - 1; ++t)
-    if (t < ntiles) issue(t, t);
+    for (int t = 0; t < NBUF - 1; ++t)
+      if (t < ntiles) issue(t, t);
+    qknorm_rope_frag<HD>(qf, pro, (size_t)bh * S, qrow, S, lane);
+  } else {
+    load_frag<HD>(qf, q + (size_t)bh * S * HD, qrow, S, lane);
+#pragma unroll
+    for (int t = 0; t < NBUF - 1; ++t)
+      if (t < ntiles) issue(t, t);
+  }
+  f32x16 o[HD / 32];
+#pragma unroll
+  for (int dt = 0; dt < HD / 32; ++dt) o[dt] = zero16();
+  SoftmaxState sm{-INFINITY, 0.f};
   // Stage t: wait for its tile, prefetch stage t + NBUF - 1, then compute.  Stages below
   // nplain lie strictly before the block's first query and inside the sequence, so no
   // wave needs masking there; the few remaining (diagonal / ragged end) stages run the
@@ -1077,17 +1156,17 @@ constexpr int kDqBuf = 2;
 constexpr int kDkdvSharedBuf = 3;
 constexpr int kDkdvPrivateBuf = 2;
 
-template <int HD>
+template <int HD, bool PROQ>
 hipError_t fwd_launch(const AttnShape& s, const void* q, const void* k, const void* v, void* out,
-                      float* lse, hipStream_t stream) {
+                      float* lse, const ProFwd& pro, hipStream_t stream) {
   const int nqt = (s.seq_len + kBM - 1) / kBM;
   const int BH = s.batch * s.num_heads;
   const int BKV = s.batch * s.num_kv_heads;
   const int xcd = (BKV % 8 == 0) ? 1 : 0;
   ProfScope prof("attn_fwd", stream);
-  hipLaunchKernelGGL((fwd_kernel<HD, kFwdBuf>), dim3(BH * nqt), dim3(256), 0, stream,
+  hipLaunchKernelGGL((fwd_kernel<HD, kFwdBuf, PROQ>), dim3(BH * nqt), dim3(256), 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)out, lse, s.seq_len,
-                     s.num_heads, s.num_kv_heads, kLog2e / sqrtf((float)HD), nqt, xcd);
+                     s.num_heads, s.num_kv_heads, kLog2e / sqrtf((float)HD), nqt, xcd, pro);
   return hipPeekAtLastError();
 }
 
@@ -1147,9 +1226,22 @@ ProBwd make_pro(const void* x, const float* gamma, const float* rstd, const floa
 bool fast_bf16_supported(int head_dim) { return head_dim == 64 || head_dim == 128; }
 
 hipError_t launch_attn_fwd_bf16_fast(const AttnShape& s, const void* q, const void* k,
-                                     const void* v, void* out, float* lse, hipStream_t stream) {
-  if (s.head_dim == 128) return fwd_launch<128>(s, q, k, v, out, lse, stream);
-  if (s.head_dim == 64) return fwd_launch<64>(s, q, k, v, out, lse, stream);
+                                     const void* v, void* out, float* lse,
+                                     const QProFuse* pro, hipStream_t stream) {
+  ProFwd pf{};
+  if (pro != nullptr) {
+    pf.x = static_cast<const bf16*>(pro->xq);
+    pf.gamma = pro->gamma_q, pf.cos_tab = pro->cos_tab, pf.sin_tab = pro->sin_tab;
+    pf.y = static_cast<bf16*>(pro->yq);
+    pf.rstd = pro->rstd_q;
+    pf.eps = pro->eps;
+  }
+  if (s.head_dim == 128)
+    return pro != nullptr ? fwd_launch<128, true>(s, q, k, v, out, lse, pf, stream)
+                          : fwd_launch<128, false>(s, q, k, v, out, lse, pf, stream);
+  if (s.head_dim == 64)
+    return pro != nullptr ? fwd_launch<64, true>(s, q, k, v, out, lse, pf, stream)
+                          : fwd_launch<64, false>(s, q, k, v, out, lse, pf, stream);
   return hipErrorInvalidValue;
 }
 

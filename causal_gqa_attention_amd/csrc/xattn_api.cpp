@@ -315,6 +315,46 @@ xattn_status xattn_fwd(const xattn_dims* dims, const void* q, const void* k, con
   });
 }
 
+xattn_status xattn_fwd_qnorm(const xattn_dims* dims, const xattn_fwd_prologue* pro,
+                             const void* k, const void* v, void* out, float* lse,
+                             void* stream) {
+  return guarded([&] {
+    const DimsChecked c = check_dims(dims);
+    if (pro == nullptr) fail(XATTN_ERR_INVALID_ARG, "pro is NULL");
+    for (auto [p, name] : {std::pair<const void*, const char*>{pro->xq, "pro->xq"},
+                           {pro->gamma_q, "pro->gamma_q"}, {pro->cos_tab, "pro->cos_tab"},
+                           {pro->sin_tab, "pro->sin_tab"}, {pro->yq, "pro->yq"},
+                           {pro->rstd_q, "pro->rstd_q"}, {k, "k"}, {v, "v"}, {out, "out"},
+                           {lse, "lse"}})
+      check_ptr(p, name);
+    if (!(pro->eps >= 0.f) || !std::isfinite(pro->eps))
+      fail(XATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    const size_t qb = (size_t)c.q_elems * io_size(c.io), kb = (size_t)c.kv_elems * io_size(c.io);
+    const size_t rb = (size_t)c.rows_q * 4, hdb = (size_t)c.s.head_dim * 4;
+    const size_t tb = (size_t)c.s.seq_len * (c.s.head_dim / 2) * 4;
+    check_no_overlap({{pro->yq, qb, "pro->yq"}, {pro->rstd_q, rb, "pro->rstd_q"}, {out, qb, "out"},
+                      {lse, rb, "lse"}},
+                     {{pro->xq, qb, "pro->xq"}, {pro->gamma_q, hdb, "pro->gamma_q"},
+                      {pro->cos_tab, tb, "pro->cos_tab"}, {pro->sin_tab, tb, "pro->sin_tab"},
+                      {k, kb, "k"}, {v, kb, "v"}});
+    const hipStream_t st = (hipStream_t)stream;
+    if (c.io == xattn::IO_BF16 && xattn::fast_bf16_supported(c.s.head_dim)) {
+      xattn::QProFuse pf;
+      pf.xq = pro->xq, pf.gamma_q = pro->gamma_q, pf.cos_tab = pro->cos_tab;
+      pf.sin_tab = pro->sin_tab, pf.yq = pro->yq, pf.rstd_q = pro->rstd_q, pf.eps = pro->eps;
+      hip_check(xattn::launch_attn_fwd_bf16_fast(c.s, nullptr, k, v, out, lse, &pf, st),
+                "attention forward launch");
+      return;
+    }
+    hip_check(xattn::launch_qknorm_rope_fwd(c.io, c.s.head_dim, pro->xq, pro->gamma_q,
+                                            pro->cos_tab, pro->sin_tab, pro->yq, pro->rstd_q,
+                                            (int)c.rows_q, c.s.seq_len, pro->eps, st),
+              "prologue forward launch");
+    hip_check(xattn::launch_attn_fwd(c.io, c.s, pro->yq, k, v, out, lse, st),
+              "attention forward launch");
+  });
+}
+
 size_t xattn_bwd_workspace_bytes(const xattn_dims* dims, int with_prologue) {
   size_t n = 0;
   const xattn_status st = guarded([&] { n = bwd_workspace(check_dims(dims), with_prologue != 0); });

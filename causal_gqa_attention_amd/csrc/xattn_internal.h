@@ -58,8 +58,19 @@ hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const v
 // gfx950 fast path (bf16 io, head_dim 64 or 128), attn_bf16.hip.  The backward also
 // writes lse2 = lse * log2(e) and delta per query row (workspace) for its dk/dv kernel.
 bool fast_bf16_supported(int head_dim);
+// With `pro` non-null the forward reads the raw pro->xq instead of q and applies the
+// QK-norm + RoPE forward to its resident Q rows itself, writing the rotated rows to
+// pro->yq and their rstd to pro->rstd_q (what xattn_bwd takes as q and rstd_q).
+struct QProFuse {
+  const void* xq;
+  const float *gamma_q, *cos_tab, *sin_tab;
+  void* yq;
+  float* rstd_q;
+  float eps;
+};
 hipError_t launch_attn_fwd_bf16_fast(const AttnShape& s, const void* q, const void* k,
-                                     const void* v, void* out, float* lse, hipStream_t stream);
+                                     const void* v, void* out, float* lse,
+                                     const QProFuse* pro, hipStream_t stream);
 //
 // With `pro` non-null the prologue backward is applied in the dq and dk stores: dq, dk
 // receive the gradients w.r.t. the raw xq, xk (io dtype) and dgamma_q, dgamma_k are

@@ -1,8 +1,8 @@
 """One step of the hot path over preallocated device buffers.
 
-A step is the whole path once: RoPE cos/sin cache, QK-norm + RoPE on Q and on K,
-attention forward (out, lse), then the backward (delta, dq, dk/dv with the group sum,
-prologue backward for Q and K, dgamma reductions).  Buffers are allocated once at
+A step is the whole path once: RoPE cos/sin cache, QK-norm + RoPE on K, attention forward
+(out, lse) with QK-norm + RoPE of Q fused into it, then the backward (delta, dq, dk/dv with
+the group sum, prologue backward for Q and K, dgamma reductions).  Buffers are allocated once at
 construction with torch (plumbing only); every step runs only libxattn kernels, on one
 stream, with no allocation.
 """
@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (Dims, make_dims, xattn_bwd, xattn_bwd_workspace_bytes, xattn_fwd,
+from . import (Dims, make_dims, xattn_bwd, xattn_bwd_workspace_bytes, xattn_fwd_qnorm,
                xattn_qknorm_rope_fwd, xattn_rope_cache)
 
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -57,11 +57,10 @@ class AttentionStep:
     def forward(self, stream=None):
         S, hd = self.S, self.hd
         xattn_rope_cache(self.cos, self.sin, S, hd, self.theta, stream)
-        xattn_qknorm_rope_fwd(self.xq, self.gamma_q, self.cos, self.sin, self.yq, self.rstd_q,
-                              self.B * self.H, S, hd, self.eps, stream)
         xattn_qknorm_rope_fwd(self.xk, self.gamma_k, self.cos, self.sin, self.yk, self.rstd_k,
                               self.B * self.Hkv, S, hd, self.eps, stream)
-        xattn_fwd(self.dims, self.yq, self.yk, self.v, self.out, self.lse, stream)
+        xattn_fwd_qnorm(self.dims, self.xq, self.gamma_q, self.cos, self.sin, self.eps, self.yq,
+                        self.rstd_q, self.yk, self.v, self.out, self.lse, stream)
 
     def backward(self, stream=None):
         xattn_bwd(self.dims, self.yq, self.yk, self.v, self.out, self.lse, self.dout, self.dxq,

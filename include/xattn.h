@@ -126,6 +126,29 @@ xattn_status xattn_qknorm_rope_bwd(const void* dy, const void* x, const float* g
 xattn_status xattn_fwd(const xattn_dims* dims, const void* q, const void* k, const void* v,
                        void* out, float* lse, void* stream);
 
+/* Q side of the prologue, for xattn_fwd_qnorm. */
+typedef struct {
+  const void* xq;          /* [B*H, S, hd] io dtype: raw Q before QK-norm */
+  const float* gamma_q;    /* [hd] fp32 */
+  const float* cos_tab;    /* [S, hd/2] fp32, from xattn_rope_cache */
+  const float* sin_tab;    /* [S, hd/2] fp32 */
+  float eps;               /* finite, >= 0 */
+  void* yq;                /* [B*H, S, hd] io dtype output: normalised, rotated Q */
+  float* rstd_q;           /* [B*H*S] fp32 output */
+} xattn_fwd_prologue;
+
+/* Attention forward with the Q side of the prologue fused ([T9] Decision 1, [MINT] 5.4.1,
+ * 5.4.4, 5.5.1 and 5.3.1): the same results as xattn_qknorm_rope_fwd(pro->xq) into
+ * pro->yq / pro->rstd_q followed by xattn_fwd(pro->yq, k, v).  For bf16 io at hd 64 / 128
+ * it is one pass: the attention reads the raw Q rows it keeps resident and normalises and
+ * rotates them itself (yq and rstd_q are still written, as xattn_bwd needs them);
+ * otherwise the two calls run in sequence.  k must already be normalised and rotated
+ * (xattn_qknorm_rope_fwd): every query tile reads every K tile before it, so K is
+ * prepared once.  out, lse as in xattn_fwd. */
+xattn_status xattn_fwd_qnorm(const xattn_dims* dims, const xattn_fwd_prologue* pro,
+                             const void* k, const void* v, void* out, float* lse,
+                             void* stream);
+
 /* Bytes of workspace xattn_bwd needs; with_prologue != 0 sizes it for a call with a
  * non-NULL xattn_prologue. */
 size_t xattn_bwd_workspace_bytes(const xattn_dims* dims, int with_prologue);

@@ -33,7 +33,7 @@ def lib():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert "gfx950" in X.xattn_version()
@@ -98,6 +98,26 @@ def test_prologue_fwd_validation(lib):
     assert f(*base, 0, 16, 64, 1e-5, 0, None) == INVALID and "rows" in last(lib)
     # y overlapping x
     assert f(A, base[1], base[2], base[3], A + 64, base[5], 4, 16, 64, 1e-5, 0, None) == INVALID
+
+
+def fwd_qnorm(lib, d, pro, k=A + 40 * MB, v=A + 48 * MB, out=A + 56 * MB, lse=A + 64 * MB):
+    return lib.xattn_fwd_qnorm(ctypes.byref(d), ctypes.byref(pro) if pro is not None else None,
+                               k, v, out, lse, None)
+
+
+def test_fwd_qnorm_validation(lib):
+    d = dims()  # bf16, B=2, S=64, H=8, hd=64: every tensor is well under 8 MiB
+    good = dict(xq=A, gamma_q=A + 8 * MB, cos_tab=A + 9 * MB, sin_tab=A + 10 * MB, eps=1e-5,
+                yq=A + 16 * MB, rstd_q=A + 24 * MB)
+    pro = lambda **kw: X.FwdPrologue(**{**good, **kw})
+    assert fwd_qnorm(lib, d, None) == INVALID and "pro is NULL" in last(lib)
+    assert fwd_qnorm(lib, d, pro(xq=None)) == INVALID and "pro->xq is NULL" in last(lib)
+    assert fwd_qnorm(lib, d, pro(eps=-1.0)) == INVALID and "eps" in last(lib)
+    assert fwd_qnorm(lib, d, pro(eps=float("nan"))) == INVALID and "eps" in last(lib)
+    assert fwd_qnorm(lib, d, pro(yq=A + 64)) == INVALID and "overlaps input pro->xq" in last(lib)
+    assert fwd_qnorm(lib, d, pro(rstd_q=A + 56 * MB)) == INVALID and "overlap" in last(lib)
+    assert fwd_qnorm(lib, d, pro(), k=A + 8 * MB + 2) == INVALID and "aligned" in last(lib)
+    assert fwd_qnorm(lib, dims(hd=48), pro()) == UNSUPPORTED
 
 
 def test_rope_cache_validation(lib):

@@ -192,3 +192,35 @@ def test_fused_prologue_backward_equals_separate_calls_f32():
     torch.cuda.synchronize()
     for a, b in ((dxq, dxq2), (dxk, dxk2), (dv, dv2), (dgq, dgq2), (dgk, dgk2)):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("wi,dtype", [(5, "bf16"), (4, "bf16"), (2, "f32")])
+def test_forward_with_fused_q_prologue_matches_separate_calls(wi, dtype):
+    """xattn_fwd_qnorm: out and lse are bitwise those of xattn_fwd on the yq it wrote, and
+    yq / rstd_q match xattn_qknorm_rope_fwd (bitwise for fp32, where the two calls run in
+    sequence; for bf16 the in-kernel mean square sums in another order, so rstd may differ
+    in the last bits and yq by one rounding)."""
+    w = W.WORKLOADS[wi]
+    if wi == 5:
+        w = w.replace(seq_len=1000)
+    if wi == 4:
+        w = w.replace(batch=2, seq_len=300)
+    x = W.make_inputs(w)
+    note(f"fused Q prologue forward {w}")
+    cos, sin = X.rope_cache(w.seq_len, w.head_dim, w.theta)
+    txq, txk, tv = (dev(a, dtype) for a in (x.xq, x.xk, x.v))
+    gq, gk = dev(x.gamma_q, "f32"), dev(x.gamma_k, "f32")
+    yk, _ = X.qknorm_rope_fwd(txk, gk, cos, sin, w.eps)
+    out, lse, yq, rq = X.attn_fwd_qnorm(txq, gq, cos, sin, w.eps, yk, tv, w.num_heads,
+                                        w.num_kv_heads)
+    out2, lse2 = X.attn_fwd(yq, yk, tv, w.num_heads, w.num_kv_heads)
+    yq2, rq2 = X.qknorm_rope_fwd(txq, gq, cos, sin, w.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    if dtype == "f32":
+        assert torch.equal(yq, yq2) and torch.equal(rq, rq2)
+    else:
+        np.testing.assert_allclose(host(rq), host(rq2), rtol=2e-6, atol=0)
+        d = (yq.float() - yq2.float()).abs()
+        ulp = yq2.float().abs().clamp_min(2.0 ** -126) * 2.0 ** -7
+        assert bool((d <= ulp).all()), float((d / ulp).max())
