@@ -27,6 +27,9 @@ Sources (titles of the pages and the section each function follows):
     sum over r < group of the gradients of query heads kvh*group + r.
   * "Phase T12: bf16 mixed precision", precision table: softmax, RoPE and norm in
     fp32 on the device; the oracle uses float64 throughout.
+  * Mint documentation, section 10.3 (KV cache): a new token computes its own
+    Q/K/V, appends K/V to the cache, and its query attends to every cached key;
+    the result equals full-sequence attention (decode()).
 
 Readings where the pages leave a step open (listed with the design notes):
   * masking: the pages use an additive -1e9 / -1e38 or a causal flag; all three
@@ -229,3 +232,36 @@ def backward(xq, xk, v, gamma_q, gamma_k, dout, num_heads, num_kv_heads, eps, th
     dxq, dgq = qknorm_rope_bwd(dyq, xq, gamma_q, f["rstd_q"], theta, pos_offset)
     dxk, dgk = qknorm_rope_bwd(dyk, xk, gamma_k, f["rstd_k"], theta, pos_offset)
     return dict(dyq=dyq, dyk=dyk, dxq=dxq, dxk=dxk, dv=dv, dgamma_q=dgq, dgamma_k=dgk)
+
+
+# --------------------------------------------------------------------------
+# KV-cache decode (Mint documentation 10.3)
+# --------------------------------------------------------------------------
+def decode(xq, xk, v, gamma_q, gamma_k, k_cache, v_cache, cache_len: int, num_heads: int,
+           num_kv_heads: int, eps: float, theta: float):
+    """One cached decode step.  The Sq new tokens of each sequence sit at positions
+    cache_len .. cache_len + Sq - 1: their q, k get QK-norm + RoPE at those absolute
+    positions, k and v are appended after the first cache_len rows of the caches, and
+    new token i attends to the cached keys j <= cache_len + i of its KV head.
+    xq: [B*H, Sq, hd]; xk, v: [B*Hkv, Sq, hd] (raw); k_cache, v_cache: [B*Hkv, >= cache_len,
+    hd] (rotated keys and values of the earlier tokens; rows past cache_len are ignored).
+    Returns (out [B*H, Sq, hd], lse [B*H, Sq], k_cache', v_cache' [B*Hkv, cache_len+Sq, hd])."""
+    _check_heads(num_heads, num_kv_heads)
+    yq, _ = qknorm_rope_fwd(xq, gamma_q, eps, theta, pos_offset=cache_len)
+    yk, _ = qknorm_rope_fwd(xk, gamma_k, eps, theta, pos_offset=cache_len)
+    kc = np.concatenate([_f64(k_cache)[:, :cache_len], yk], axis=1)
+    vc = np.concatenate([_f64(v_cache)[:, :cache_len], _f64(v)], axis=1)
+    BH, Sq, hd = yq.shape
+    scale = 1.0 / np.sqrt(hd)
+    out = np.zeros((BH, Sq, hd))
+    lse = np.zeros((BH, Sq))
+    for bh in range(BH):
+        kv = _kv_index(bh, num_heads, num_kv_heads)
+        for i in range(Sq):
+            t = cache_len + i
+            s = (kc[kv, :t + 1] @ yq[bh, i]) * scale  # every cached key at or before t
+            m = s.max()
+            e = np.exp(s - m)
+            out[bh, i] = (e / e.sum()) @ vc[kv, :t + 1]
+            lse[bh, i] = m + np.log(e.sum())
+    return out, lse, kc, vc

@@ -519,3 +519,72 @@ def test_planted_transposed_dk_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(O, "attention_bwd", bad)
     with pytest.raises(AssertionError):
         _fd_check(TINY_GQA, _inputs(TINY_GQA))
+
+
+# --------------------------------------------------------------------------
+# KV-cache decode (Mint documentation 10.3: cached decoding equals full-sequence
+# attention; the pages' own check is token-by-token cached inference against one
+# full-sequence pass)
+# --------------------------------------------------------------------------
+def _decode_all(x, w, q_len):
+    """Run O.decode over the whole sequence in steps of q_len new tokens from an empty
+    cache; returns the stacked (out, lse) and the final caches."""
+    S = w.seq_len
+    kc = np.zeros((w.bkv, 0, w.head_dim))
+    vc = np.zeros((w.bkv, 0, w.head_dim))
+    outs, lses = [], []
+    for t in range(0, S, q_len):
+        n = min(q_len, S - t)
+        o, l, kc, vc = O.decode(x.xq[:, t:t + n], x.xk[:, t:t + n], x.v[:, t:t + n],
+                                x.gamma_q, x.gamma_k, kc, vc, t, w.num_heads,
+                                w.num_kv_heads, w.eps, w.theta)
+        outs.append(o)
+        lses.append(l)
+    return np.concatenate(outs, axis=1), np.concatenate(lses, axis=1), kc, vc
+
+
+@pytest.mark.parametrize("q_len", [1, 3])
+def test_cached_decode_equals_full_sequence(q_len):
+    w = W.small_ragged("f32", 32, 17, 2, 6, 2, theta=1e4, eps=1e-5, index=301)
+    x = W.make_inputs(w)
+    f = O.forward(x.xq, x.xk, x.v, x.gamma_q, x.gamma_k, w.num_heads, w.num_kv_heads, w.eps,
+                  w.theta)
+    out, lse, kc, vc = _decode_all(x, w, q_len)
+    np.testing.assert_allclose(out, f["out"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, f["lse"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(kc, f["yk"], rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(vc, x.v.astype(np.float64))
+
+
+def test_decode_step_matches_library_sdpa_on_the_cache():
+    """One new token at position t: softmax(q k^T / sqrt(hd)) v over cache rows 0..t, by
+    torch's float64 scaled_dot_product_attention (no mask: every cached key is visible)."""
+    w = W.small_ragged("f32", 16, 9, 1, 4, 2, index=302)
+    x = W.make_inputs(w)
+    t = 8
+    yk, _ = O.qknorm_rope_fwd(x.xk[:, :t], x.gamma_k, w.eps, w.theta)
+    out, lse, kc, vc = O.decode(x.xq[:, t:], x.xk[:, t:], x.v[:, t:], x.gamma_q, x.gamma_k, yk,
+                                x.v[:, :t], t, w.num_heads, w.num_kv_heads, w.eps, w.theta)
+    yq, _ = O.qknorm_rope_fwd(x.xq[:, t:], x.gamma_q, w.eps, w.theta, pos_offset=t)
+    group = w.num_heads // w.num_kv_heads
+    q = torch.from_numpy(yq)                                   # [H, 1, hd]
+    k = torch.from_numpy(kc).repeat_interleave(group, dim=0)   # [H, t+1, hd]
+    v = torch.from_numpy(vc).repeat_interleave(group, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v).numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    s = (q @ k.transpose(1, 2)).numpy()[:, 0] / math.sqrt(w.head_dim)
+    np.testing.assert_allclose(lse[:, 0], scipy.special.logsumexp(s, axis=1), rtol=0, atol=1e-12)
+
+
+def test_planted_decode_position_mistake_is_caught(monkeypatch):
+    """New tokens rotated as if they sat at position 0 (the absolute position dropped):
+    cached decoding no longer equals the full sequence."""
+    w = W.small_ragged("f32", 16, 6, 1, 2, 1, index=303)
+    x = W.make_inputs(w)
+    f = O.forward(x.xq, x.xk, x.v, x.gamma_q, x.gamma_k, w.num_heads, w.num_kv_heads, w.eps,
+                  w.theta)
+    real = O.qknorm_rope_fwd
+    monkeypatch.setattr(O, "qknorm_rope_fwd",
+                        lambda xx, g, eps, theta, pos_offset=0: real(xx, g, eps, theta, 0))
+    out, _, _, _ = _decode_all(x, w, 1)
+    assert np.abs(out - f["out"]).max() > 1e-3
