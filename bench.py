@@ -49,6 +49,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of 1 GiB (for HBM counter scaling)")
+    p.add_argument("--decode", action="store_true",
+                   help="measure the KV-cache decode step instead (xattn_decode)")
+    p.add_argument("--decode-batch", type=int, default=8)
+    p.add_argument("--decode-cache", type=int, default=4096,
+                   help="cache capacity; the step decodes one token at position capacity-1")
     return p.parse_args()
 
 
@@ -143,6 +148,140 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "dispatches": 5}))
 
 
+DECODE_METRIC = "KV-cache decode step: cache bytes streamed per second (HBM GB/s)"
+
+
+def decode_ranges(bkv, rows):
+    """Key ranges per KV head of the library's decode plan: ranges of at least 64 keys, at
+    most ceil(2048 / bkv) of them, equal length."""
+    cap_splits = 1 if bkv >= 2048 else -(-2048 // bkv)
+    n = max(1, min(-(-rows // 64), cap_splits))
+    ks = -(-rows // n)
+    return -(-rows // ks)
+
+
+def decode_bench(args):
+    """One decode step = xattn_decode of one new token per sequence against a full cache
+    (Qwen3-shaped heads: 32 query heads, 8 KV heads, head_dim 128, bf16, theta 1e6), the
+    cache and the new token's inputs seeded and synthetic, resident in HBM.  value = the
+    step's algorithmic HBM bytes (K and V cache rows read, new rows written, q / k / v read,
+    out written) / step time."""
+    import numpy as np
+    import torch
+
+    import causal_gqa_attention_amd as X
+    import workloads as W
+
+    base = W.WORKLOADS[5]
+    B, cap, q_len = args.decode_batch, args.decode_cache, 1
+    H, Hkv, hd = base.num_heads, base.num_kv_heads, base.head_dim
+    pos = cap - q_len
+    name = f"qwen3_decode_b{B}_cache{cap}_bf16"
+    log(f"decode workload {name}: B={B} H={H} Hkv={Hkv} hd={hd} cache_len={pos} q_len={q_len}")
+    rng = np.random.default_rng(55)
+    f32 = np.float32
+    kc_h = W.bf16_round(rng.standard_normal((B * Hkv, cap, hd), dtype=f32))
+    vc_h = W.bf16_round(rng.standard_normal((B * Hkv, cap, hd), dtype=f32))
+    xq_h = W.bf16_round(rng.standard_normal((B * H, q_len, hd), dtype=f32))
+    xk_h = W.bf16_round(rng.standard_normal((B * Hkv, q_len, hd), dtype=f32))
+    v_h = W.bf16_round(rng.standard_normal((B * Hkv, q_len, hd), dtype=f32))
+    g_h = (1.0 + 0.1 * rng.standard_normal((2, hd), dtype=f32)).astype(f32)
+    torch.cuda.set_device(0)
+    d = lambda a, dt=torch.bfloat16: torch.from_numpy(a).to("cuda").to(dt)
+    kc, vc, xq, xk, v = d(kc_h), d(vc_h), d(xq_h), d(xk_h), d(v_h)
+    gq, gk = d(g_h[0], torch.float32), d(g_h[1], torch.float32)
+    cos, sin = X.rope_cache(cap, hd, base.theta)
+    dims = X.make_decode_dims(xq, kc, H, Hkv, pos)
+    ws = torch.empty(X.xattn_decode_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(xq)
+    lse = torch.empty(B * H * q_len, dtype=torch.float32, device="cuda")
+
+    def step():
+        X.xattn_decode(dims, xq, xk, v, gq, gk, cos, sin, base.eps, kc, vc, out, lse, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    Lk = pos + q_len
+    cache_read = 2 * B * Hkv * Lk * hd * 2          # every visible K and V row, bf16
+    small = (B * H + 2 * B * Hkv) * q_len * hd * 2 + 2 * B * Hkv * q_len * hd * 2 \
+        + B * H * q_len * (hd * 2 + 4)              # new q/k/v in, new rows, out + lse
+    total = cache_read + small
+    value = total / (ms * 1e-3) / 1e9
+    log(f"timed {args.steps} decode steps: {ms * 1e3:.1f} us/step, {value:.0f} GB/s, "
+        f"{B * q_len / (ms * 1e-3):.0f} tokens/s")
+
+    X.xattn_profile_start()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = X.xattn_profile_stop()
+    kernels = {n: {"launches_per_step": c / args.steps, "avg_ms": t / max(c, 1),
+                   "ms_per_step": t / args.steps} for n, (c, t) in prof.items()}
+    log("kernels: " + ", ".join(f"{n} {k['avg_ms'] * 1e3:.1f} us" for n, k in kernels.items()))
+    # dominant kernel: the split attention; its algorithmic bytes are the cache rows it
+    # streams plus the rotated queries it reads and the partials it writes
+    ranges = decode_ranges(B * Hkv, Lk)
+    split_bytes = (cache_read + B * H * q_len * hd * 2
+                   + B * Hkv * ranges * (H // Hkv) * q_len * (hd + 2) * 4)
+    k = kernels["decode_split"]
+    achieved = split_bytes / (k["avg_ms"] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "decode_split",
+                "work_per_launch": split_bytes,
+                "work_basis": "K and V cache rows read (bf16) + rotated q read + fp32 range "
+                              "partials written"}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("timing the CPU oracle on a bounded sample ...")
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            threads = len(os.sched_getaffinity(0))
+        g = H // Hkv
+        done, dt = 0, 0.0
+        for kv in range(B * Hkv):
+            b, kvh = divmod(kv, Hkv)
+            qs = [b * H + kvh * g + r for r in range(g)]
+            t0 = time.perf_counter()
+            oracle.decode(xq_h[qs], xk_h[[kv]], v_h[[kv]], g_h[0], g_h[1], kc_h[[kv]],
+                          vc_h[[kv]], pos, g, 1, base.eps, base.theta)
+            dt += time.perf_counter() - t0
+            done += 1
+            if dt >= 10.0:
+                break
+        per_group = total / (B * Hkv)
+        cpu = {"value": done * per_group / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+               "kind": "oracle",
+               "sample": f"{done} of {B * Hkv} KV-head groups (a KV head's {Lk} cached rows "
+                         f"with its {g} query heads): float64 numpy oracle.decode, {dt:.1f} s"}
+    line = {
+        "metric": DECODE_METRIC, "value": value, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": B, "cache_len": pos, "q_len": q_len,
+                   "num_heads": H, "num_kv_heads": Hkv, "head_dim": hd, "io_dtype": "bf16",
+                   "parallelism": "none (1 GPU)"},
+        "tokens_per_s": B * q_len / (ms * 1e-3),
+        "pct_of_hbm_peak": 100.0 * value / PEAK_HBM_GBS,
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+        "bytes_per_step": total,
+    }
+    print(json.dumps(line))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -152,6 +291,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.decode:
+        decode_bench(args)
         return
 
     import numpy as np

@@ -23,10 +23,11 @@ __all__ = [
     "xattn_rope_cache", "xattn_qknorm_rope_fwd", "xattn_qknorm_rope_bwd_workspace_bytes",
     "xattn_qknorm_rope_bwd", "xattn_fwd", "xattn_fwd_qnorm", "xattn_bwd_workspace_bytes",
     "xattn_bwd",
+    "xattn_decode_workspace_bytes", "xattn_decode",
     "xattn_status_string", "xattn_last_error", "xattn_version", "xattn_profile_start",
     "xattn_profile_stop",
     "rope_cache", "qknorm_rope_fwd", "qknorm_rope_bwd", "attn_fwd", "attn_fwd_qnorm",
-    "attn_bwd",
+    "attn_bwd", "decode",
 ]
 
 XATTN_F32 = 0
@@ -68,6 +69,11 @@ class FwdPrologue(ctypes.Structure):
                 ("eps", ctypes.c_float), ("yq", ctypes.c_void_p), ("rstd_q", ctypes.c_void_p)]
 
 
+class DecodeDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("batch", "num_heads", "num_kv_heads", "head_dim",
+                                              "dtype", "q_len", "cache_len", "capacity")]
+
+
 def library_path() -> str:
     return os.path.join(_HERE, "libxattn.so")
 
@@ -96,6 +102,9 @@ def load_library() -> ctypes.CDLL:
         "xattn_bwd_workspace_bytes": (sz, [ctypes.POINTER(Dims), ctypes.c_int]),
         "xattn_bwd": (i32, [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                             ctypes.POINTER(Prologue), vp, sz, vp]),
+        "xattn_decode_workspace_bytes": (sz, [ctypes.POINTER(DecodeDims)]),
+        "xattn_decode": (i32, [ctypes.POINTER(DecodeDims), vp, vp, vp, vp, vp, vp, vp,
+                               ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]),
         "xattn_profile_start": (i32, []),
         "xattn_profile_stop": (i32, [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]),
         "xattn_status_string": (ctypes.c_char_p, [i32]),
@@ -262,6 +271,30 @@ def xattn_bwd(dims: Dims, q, k, v, out, lse, dout, dq, dk, dv, prologue, workspa
         _stream(stream)), "xattn_bwd")
 
 
+def make_decode_dims(xq, k_cache, num_heads, num_kv_heads, cache_len) -> DecodeDims:
+    bh, sq, hd = xq.shape
+    if bh % num_heads:
+        raise ValueError("xq.shape[0] must be batch * num_heads")
+    return DecodeDims(bh // num_heads, num_heads, num_kv_heads, hd, _io(xq, "xq"), sq,
+                      int(cache_len), k_cache.shape[1])
+
+
+def xattn_decode_workspace_bytes(dims: DecodeDims) -> int:
+    return int(load_library().xattn_decode_workspace_bytes(ctypes.byref(dims)))
+
+
+def xattn_decode(dims: DecodeDims, xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, eps,
+                 k_cache, v_cache, out, lse, workspace, stream=None):
+    _check(load_library().xattn_decode(
+        ctypes.byref(dims), _ptr(xq, "xq"), _ptr(xk, "xk", xq.dtype), _ptr(v, "v", xq.dtype),
+        _ptr(gamma_q, "gamma_q", torch.float32), _ptr(gamma_k, "gamma_k", torch.float32),
+        _ptr(cos_tab, "cos_tab", torch.float32), _ptr(sin_tab, "sin_tab", torch.float32),
+        float(eps), _ptr(k_cache, "k_cache", xq.dtype), _ptr(v_cache, "v_cache", xq.dtype),
+        _ptr(out, "out", xq.dtype), _ptr(lse, "lse", torch.float32),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "xattn_decode")
+
+
 # ----------------------------------------------------------------------------------------
 # allocating helpers
 # ----------------------------------------------------------------------------------------
@@ -332,3 +365,17 @@ def attn_bwd(q, k, v, out, lse, dout, num_heads, num_kv_heads, prologue=None, st
     if pro is None:
         return dq, dk, dv
     return dq, dk, dv, pro["dgamma_q"], pro["dgamma_k"]
+
+
+def decode(xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, eps, k_cache, v_cache, cache_len,
+           num_heads, num_kv_heads, stream=None, workspace=None):
+    """One KV-cache decode step: appends the new tokens' rotated keys and values to the
+    caches (rows cache_len ..) and returns (out, lse) of the new queries."""
+    dims = make_decode_dims(xq, k_cache, num_heads, num_kv_heads, cache_len)
+    out = torch.empty_like(xq)
+    lse = torch.empty(xq.shape[0] * xq.shape[1], dtype=torch.float32, device=xq.device)
+    if workspace is None:
+        workspace = _workspace(xattn_decode_workspace_bytes(dims), xq.device)
+    xattn_decode(dims, xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, eps, k_cache, v_cache, out,
+                 lse, workspace, stream)
+    return out, lse

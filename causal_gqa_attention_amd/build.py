@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libxattn.so")
-SOURCES = ["attn.hip", "attn_bf16.hip", "prologue.hip", "xattn_api.cpp", "profile.cpp"]
+SOURCES = ["attn.hip", "attn_bf16.hip", "prologue.hip", "decode.hip", "xattn_api.cpp",
+           "profile.cpp"]
 # Per-source extra flags.  attn_bf16.hip: MFMA results go to VGPRs (the score tiles are
 # consumed by VALU right away; AGPR results would need a copy per element).
 SOURCE_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}

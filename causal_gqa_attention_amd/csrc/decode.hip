@@ -1,0 +1,448 @@
+// KV-cache decode attention: a few new tokens per sequence attend to every cached key.
+//
+// What is computed (Mint documentation 10.3 "KV cache": each new token computes its own
+// Q/K/V, its K/V are appended to the layer's cache in place, and its query attends to all
+// cached keys, which are causal by construction; the result equals full-sequence attention.
+// Mint 14.2 item 5: per-head extract / RoPE / append / attention launches dominate a GPU
+// decode step, so they are merged):
+//   for new token i in [0, Sq) of sequence b at absolute position t = pos + i:
+//     q, k = QK-norm + RoPE at position t (the prologue forward of the training path),
+//     k and v are written to cache row t of their KV head,
+//     out = softmax_j(q . k_j / sqrt(hd)) v_j over cache rows j <= t, lse = ln sum exp.
+//
+// Layout on MI355X.  Decode reads the whole cache once and holds only (group x Sq) query
+// rows per KV head, so it is bound by HBM bandwidth, not by arithmetic: a KV head's cache
+// is split into key ranges, one wave per (KV head, range); a wave streams its range with
+// 16-byte loads (a key row spread over HD*size/16 lanes, several keys per wave load, four
+// loads in flight per lane), keeps every query row of the group in registers, and runs an
+// online softmax per lane group with one rescale per four keys.  The lane groups of a wave
+// are merged by a fixed xor butterfly, the ranges in range order by a third launch, so the
+// result is bitwise reproducible.  Three launches: prologue + append, split attention,
+// combine.
+#include <math.h>
+
+#include "xattn_device.h"
+#include "xattn_internal.h"
+
+namespace xattn {
+namespace {
+
+struct DecodeArgs {
+  const void* xq;        // [B*H, Sq, HD] raw new queries
+  const void* xk;        // [B*Hkv, Sq, HD] raw new keys
+  const void* v;         // [B*Hkv, Sq, HD] new values
+  const float* gamma_q;  // [HD]
+  const float* gamma_k;  // [HD]
+  const float* cos_tab;  // [cap, HD/2]
+  const float* sin_tab;  // [cap, HD/2]
+  void* k_cache;         // [B*Hkv, cap, HD]
+  void* v_cache;         // [B*Hkv, cap, HD]
+  void* out;             // [B*H, Sq, HD]
+  float* lse;            // [B*H*Sq]
+  void* yq;              // workspace [B*H, Sq, HD] io dtype: normalised, rotated queries
+  float* part_o;         // workspace [B*Hkv][nsplit][R][HD]
+  float* part_ml;        // workspace [B*Hkv][nsplit][R][2]: running max (log2 units), sum
+  int B, H, Hkv, Sq, pos, cap, nsplit, ks;  // ks: keys per range
+  float eps, scale_log2;
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of N consecutive lanes (N a power of two up to 64), the same
+// bits in every lane of the group: DPP quad permutations, the half-row and row mirrors
+// (each pairs a lane with one in the other half of its 8- or 16-lane group), then xor
+// exchanges across rows.
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  if constexpr (N >= 2) v += dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  if constexpr (N >= 4) v += dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  if constexpr (N >= 8) v += dpp<0x141>(v);  // row_half_mirror
+  if constexpr (N >= 16) v += dpp<0x140>(v); // row_mirror
+  if constexpr (N >= 32) v += shfl_xor(v, 16);
+  if constexpr (N >= 64) v += shfl_xor(v, 32);
+  return v;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void load_vec(const T* p, float (&out)[N]) {
+  constexpr int per = V16<T>::n;
+#pragma unroll
+  for (int k = 0; k < N / per; ++k) {
+    const vec16_t<T> w = load16(p + k * per);
+#pragma unroll
+    for (int j = 0; j < per; ++j) out[k * per + j] = to_f32(w[j]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// 1. prologue + append.  Rows [0, B*H*Sq) are the new queries (normalised and rotated into
+// the yq workspace), rows [B*H*Sq, B*H*Sq + B*Hkv*Sq) the new keys (normalised and rotated
+// into cache row pos + i; the same lanes copy the value row into the V cache).  LPR lanes
+// per row, each owning VEC columns of the first half and the matching second-half columns;
+// the arithmetic is that of the prologue forward.
+// ---------------------------------------------------------------------------------------
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void decode_prologue_kernel(DecodeArgs a) {
+  constexpr int VEC = V16<T>::n, HALF = HD / 2;
+  constexpr int W = HALF < VEC ? HALF : VEC;  // columns of each half per lane
+  constexpr int LPR = HALF / W;
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  const int row = g / LPR, part = g % LPR;
+  const int nq = a.B * a.H * a.Sq, nk = a.B * a.Hkv * a.Sq;
+  const bool valid = row < nq + nk;
+  const bool isq = row < nq;
+  const int rr = !valid ? 0 : (isq ? row : row - nq);  // row within its tensor
+  const int head = rr / a.Sq, t = a.pos + rr % a.Sq;
+  const T* x = static_cast<const T*>(isq ? a.xq : a.xk) + (size_t)rr * HD;
+  const float* gamma = isq ? a.gamma_q : a.gamma_k;
+  const int c0 = part * W;
+  float x1[W], x2[W], cs[W], sn[W], g1[W], g2[W];
+  if constexpr (W == VEC) {
+    load_vec<T, W>(x + c0, x1);
+    load_vec<T, W>(x + HALF + c0, x2);
+  } else {
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      x1[e] = to_f32(x[c0 + e]);
+      x2[e] = to_f32(x[HALF + c0 + e]);
+    }
+  }
+  if constexpr (W % 4 == 0) {
+    load_vec<float, W>(a.cos_tab + (size_t)t * HALF + c0, cs);
+    load_vec<float, W>(a.sin_tab + (size_t)t * HALF + c0, sn);
+    load_vec<float, W>(gamma + c0, g1);
+    load_vec<float, W>(gamma + HALF + c0, g2);
+  } else {
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      cs[e] = a.cos_tab[(size_t)t * HALF + c0 + e];
+      sn[e] = a.sin_tab[(size_t)t * HALF + c0 + e];
+      g1[e] = gamma[c0 + e];
+      g2[e] = gamma[HALF + c0 + e];
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < W; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) ss += shfl_xor(ss, m);
+  const float r = 1.0f / sqrtf(ss * (1.0f / (float)HD) + a.eps);
+  if (!valid) return;
+  T* dst = isq ? static_cast<T*>(a.yq) + (size_t)rr * HD
+               : static_cast<T*>(a.k_cache) + ((size_t)head * a.cap + t) * HD;
+#pragma unroll
+  for (int e = 0; e < W; ++e) {
+    const float n1 = x1[e] * r * g1[e];
+    const float n2 = x2[e] * r * g2[e];
+    dst[c0 + e] = from_f32<T>(n1 * cs[e] - n2 * sn[e]);
+    dst[HALF + c0 + e] = from_f32<T>(n1 * sn[e] + n2 * cs[e]);
+  }
+  if (!isq) {
+    const T* vs = static_cast<const T*>(a.v) + (size_t)rr * HD;
+    T* vd = static_cast<T*>(a.v_cache) + ((size_t)head * a.cap + t) * HD;
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      vd[c0 + e] = vs[c0 + e];
+      vd[HALF + c0 + e] = vs[HALF + c0 + e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// 2. split attention.  Wave w = (KV row bkv, range sp) handles cache rows [sp*ks,
+// min(Lk, sp*ks + ks)), Lk = pos + Sq.  Query row r = g*Sq + i (g < group, i < Sq) is query
+// head kvh*group + g at position pos + i and sees cache rows j <= pos + i.  Lane l owns the
+// VEC columns part = l % LPK of the key rows j0 + l / LPK (KPW keys per wave load); each lane
+// group keeps its own (max, sum, accumulator) per query row, merged at the end.
+// ---------------------------------------------------------------------------------------
+constexpr int kDecodeUnroll = 4;  // wave loads of K and of V in flight per lane
+
+template <typename T, int HD, int RM>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+  constexpr int VEC = V16<T>::n, LPK = HD / VEC, KPW = 64 / LPK, UN = kDecodeUnroll;
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= a.B * a.Hkv * a.nsplit) return;  // whole waves; the kernel has no barrier
+  const int bkv = w / a.nsplit, sp = w - bkv * a.nsplit;
+  const int b = bkv / a.Hkv, kvh = bkv - b * a.Hkv, group = a.H / a.Hkv;
+  const int R = group * a.Sq, Lk = a.pos + a.Sq;
+  const int k0 = sp * a.ks, k1 = min(Lk, k0 + a.ks);
+  const int part = lane % LPK, kg = lane / LPK;
+
+  float q[RM][VEC];
+  int lim[RM];  // last visible cache row of each query row (-1: padding row)
+#pragma unroll
+  for (int r = 0; r < RM; ++r) {
+    lim[r] = -1;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) q[r][e] = 0.f;
+    if (r < R) {
+      const int g = r / a.Sq, i = r - g * a.Sq;
+      const T* yr = static_cast<const T*>(a.yq) +
+                    ((size_t)(b * a.H + kvh * group + g) * a.Sq + i) * HD + part * VEC;
+      load_vec<T, VEC>(yr, q[r]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) q[r][e] *= a.scale_log2;
+      lim[r] = a.pos + i;
+    }
+  }
+  float m[RM], l[RM], o[RM][VEC];
+#pragma unroll
+  for (int r = 0; r < RM; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[r][e] = 0.f;
+  }
+  const T* kc = static_cast<const T*>(a.k_cache) + (size_t)bkv * a.cap * HD + part * VEC;
+  const T* vc = static_cast<const T*>(a.v_cache) + (size_t)bkv * a.cap * HD + part * VEC;
+
+  // the lane's 16 bytes of UN key / value rows; the next group's loads are issued before
+  // the current group's arithmetic
+  vec16_t<T> kv[UN], vv[UN], kn[UN], vn[UN];
+  auto load_group = [&](int j0, vec16_t<T> (&kk)[UN], vec16_t<T> (&vk)[UN]) {
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int j = j0 + u * KPW + kg;
+      const size_t jr = (size_t)(j < k1 ? j : k0) * HD;  // past the range: a row of it
+      kk[u] = load16(kc + jr);
+      vk[u] = load16(vc + jr);
+    }
+  };
+  load_group(k0, kv, vv);
+  for (int j0 = k0; j0 < k1; j0 += KPW * UN) {
+    if (j0 + KPW * UN < k1) load_group(j0 + KPW * UN, kn, vn);  // wave-uniform
+    int jj[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int j = j0 + u * KPW + kg;
+      jj[u] = j < k1 ? j : 0x7fffffff;  // past the range: never visible
+    }
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      if (r < R) {  // wave-uniform
+      float s[UN];
+      float smax = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) d += q[r][e] * to_f32(kv[u][e]);
+        d = lane_group_sum<LPK>(d);
+        s[u] = jj[u] <= lim[r] ? d : -INFINITY;
+        smax = fmaxf(smax, s[u]);
+      }
+      const float mn = fmaxf(m[r], smax);
+      // reference point: mn, or 0 while this lane group has seen no visible key (then
+      // every term below is exp2(-inf) = 0 and the state stays empty)
+      const float mref = mn == -INFINITY ? 0.f : mn;
+      const float alpha = exp2f(m[r] - mref);  // 0 when m was -inf
+      l[r] *= alpha;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[r][e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const float p = exp2f(s[u] - mref);  // 0 for masked keys
+        l[r] += p;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[r][e] += p * to_f32(vv[u][e]);
+      }
+      m[r] = mn;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      kv[u] = kn[u];
+      vv[u] = vn[u];
+    }
+  }
+
+  // merge the lane groups (same columns, other keys): fixed xor butterfly
+#pragma unroll
+  for (int msk = LPK; msk < 64; msk <<= 1) {
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      if (r >= R) continue;  // wave-uniform
+      const float mp = shfl_xor(m[r], msk), lp = shfl_xor(l[r], msk);
+      const float mn = fmaxf(m[r], mp);
+      const float a1 = m[r] == -INFINITY ? 0.f : exp2f(m[r] - mn);
+      const float a2 = mp == -INFINITY ? 0.f : exp2f(mp - mn);
+      l[r] = l[r] * a1 + lp * a2;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float op = shfl_xor(o[r][e], msk);
+        o[r][e] = o[r][e] * a1 + op * a2;
+      }
+      m[r] = mn;
+    }
+  }
+  if (kg != 0) return;
+  const size_t base = ((size_t)bkv * a.nsplit + sp) * R;
+  {
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      if (r >= R) continue;  // wave-uniform
+      float* po = a.part_o + (base + r) * HD + part * VEC;
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4) {
+        f32x4 w4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w4[j] = o[r][e + j];
+        *reinterpret_cast<f32x4*>(po + e) = w4;
+      }
+      if (part == 0) {
+        a.part_ml[(base + r) * 2] = m[r];
+        a.part_ml[(base + r) * 2 + 1] = l[r];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// 3. combine.  One wave per output row (b, query head, i): the common maximum over the
+// ranges (lane s reading ranges s, s + 64, ...; an exact max, so any order), then the
+// ranges' sums and partial accumulators added in range order.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int PER = (HD + 63) / 64;
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= a.B * a.H * a.Sq) return;
+  const int i = w % a.Sq, bh = w / a.Sq, b = bh / a.H, qh = bh - b * a.H;
+  const int group = a.H / a.Hkv, kvh = qh / group, g = qh - kvh * group;
+  const int R = group * a.Sq, r = g * a.Sq + i;
+  const size_t base = (size_t)(b * a.Hkv + kvh) * a.nsplit * R + r;  // + range * R
+  float M = -INFINITY;
+  for (int c = 0; c < a.nsplit; c += 64)
+    if (c + lane < a.nsplit) M = fmaxf(M, a.part_ml[(base + (size_t)(c + lane) * R) * 2]);
+  M = wave_max(M);
+  float L = 0.f, acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+#pragma unroll 8
+  for (int sp = 0; sp < a.nsplit; ++sp) {
+    const size_t idx = base + (size_t)sp * R;
+    const float ms = a.part_ml[idx * 2];
+    const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    L += a.part_ml[idx * 2 + 1] * f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int d = lane + 64 * k;
+      if (d < HD) acc[k] += a.part_o[idx * HD + d] * f;
+    }
+  }
+  T* dst = static_cast<T*>(a.out) + (size_t)w * HD;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int d = lane + 64 * k;
+    if (d < HD) dst[d] = from_f32<T>(acc[k] / L);
+  }
+  if (lane == 0) a.lse[w] = (M + log2f(L)) * kLn2;
+}
+
+// Query rows per KV head (group * Sq) a split-kernel instantiation holds in registers.
+template <typename T>
+constexpr int decode_rows_max() { return 64 / V16<T>::n; }
+
+// The smallest instantiation whose register rows cover the R query rows.
+template <typename T, int HD, int RMV>
+hipError_t split_launch(int R, dim3 grid, const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (RMV > decode_rows_max<T>()) {
+    return hipErrorInvalidValue;
+  } else {
+    if (R > RMV) return split_launch<T, HD, 2 * RMV>(R, grid, a, stream);
+    hipLaunchKernelGGL((decode_split_kernel<T, HD, RMV>), grid, dim3(256), 0, stream, a);
+    return hipSuccess;
+  }
+}
+
+template <typename T, int HD>
+hipError_t decode_launch(const DecodeArgs& a, hipStream_t stream) {
+  const int nrows = (a.B * a.H + a.B * a.Hkv) * a.Sq;
+  constexpr int LPR = (HD / 2) / V16<T>::n > 0 ? (HD / 2) / V16<T>::n : 1;
+  {
+    ProfScope prof("decode_prologue", stream);
+    const long long threads = (long long)nrows * LPR;
+    hipLaunchKernelGGL((decode_prologue_kernel<T, HD>), dim3((int)((threads + 255) / 256)),
+                       dim3(256), 0, stream, a);
+  }
+  hipError_t e = hipPeekAtLastError();
+  if (e != hipSuccess) return e;
+  const int R = (a.H / a.Hkv) * a.Sq;
+  const int waves = a.B * a.Hkv * a.nsplit;
+  {
+    ProfScope prof("decode_split", stream);
+    e = split_launch<T, HD, 1>(R, dim3((waves + 3) / 4), a, stream);
+    if (e != hipSuccess) return e;
+  }
+  e = hipPeekAtLastError();
+  if (e != hipSuccess) return e;
+  ProfScope prof("decode_combine", stream);
+  const int outs = a.B * a.H * a.Sq;
+  hipLaunchKernelGGL((decode_combine_kernel<T, HD>), dim3((outs + 3) / 4), dim3(256), 0, stream,
+                     a);
+  return hipPeekAtLastError();
+}
+
+}  // namespace
+
+int decode_rows_limit(IoType io) {
+  return io == IO_F32 ? decode_rows_max<float>() : decode_rows_max<bf16>();
+}
+
+// Key ranges: at least 64 keys each, and no more than needed for about 2048 waves (eight
+// per CU).  Both bounds grow with the cache rows, so decode_max_splits(capacity) bounds
+// every call with that capacity.
+int decode_max_splits(int batch, int num_kv_heads, int cache_rows) {
+  const int bkv = batch * num_kv_heads;
+  const int cap_splits = bkv >= 2048 ? 1 : (2048 + bkv - 1) / bkv;
+  int n = (cache_rows + 63) / 64;
+  if (n > cap_splits) n = cap_splits;
+  return n < 1 ? 1 : n;
+}
+
+DecodePlan decode_plan(const DecodeShape& d, int cache_rows) {
+  DecodePlan p;
+  const int n = decode_max_splits(d.batch, d.num_kv_heads, cache_rows);
+  p.ks = (cache_rows + n - 1) / n;
+  p.nsplit = (cache_rows + p.ks - 1) / p.ks;
+  return p;
+}
+
+hipError_t launch_decode(IoType io, const DecodeShape& d, const DecodeBufs& bufs,
+                         hipStream_t stream) {
+  DecodeArgs a;
+  a.xq = bufs.xq, a.xk = bufs.xk, a.v = bufs.v;
+  a.gamma_q = bufs.gamma_q, a.gamma_k = bufs.gamma_k;
+  a.cos_tab = bufs.cos_tab, a.sin_tab = bufs.sin_tab;
+  a.k_cache = bufs.k_cache, a.v_cache = bufs.v_cache, a.out = bufs.out, a.lse = bufs.lse;
+  a.yq = bufs.yq, a.part_o = bufs.part_o, a.part_ml = bufs.part_ml;
+  a.B = d.batch, a.H = d.num_heads, a.Hkv = d.num_kv_heads, a.Sq = d.q_len;
+  a.pos = d.cache_len, a.cap = d.capacity;
+  const DecodePlan p = decode_plan(d, d.cache_len + d.q_len);
+  a.nsplit = p.nsplit, a.ks = p.ks;
+  a.eps = d.eps;
+  a.scale_log2 = kLog2e / sqrtf((float)d.head_dim);
+#define XATTN_CASE(T, HD) \
+  if (d.head_dim == HD) return decode_launch<T, HD>(a, stream);
+  if (io == IO_F32) {
+    XATTN_CASE(float, 16) XATTN_CASE(float, 32) XATTN_CASE(float, 64) XATTN_CASE(float, 128)
+  } else {
+    XATTN_CASE(bf16, 16) XATTN_CASE(bf16, 32) XATTN_CASE(bf16, 64) XATTN_CASE(bf16, 128)
+  }
+#undef XATTN_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace xattn

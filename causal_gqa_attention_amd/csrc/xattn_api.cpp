@@ -159,6 +159,61 @@ size_t bwd_workspace(const DimsChecked& c, bool with_prologue) {
   return n;
 }
 
+struct DecodeChecked {
+  xattn::DecodeShape d;
+  xattn::IoType io;
+  int64_t q_elems, kv_new_elems, cache_elems, rows_q;
+};
+
+DecodeChecked check_decode_dims(const xattn_decode_dims* d, float eps) {
+  if (d == nullptr) fail(XATTN_ERR_INVALID_ARG, "dims is NULL");
+  check_pos(d->batch, "batch");
+  check_pos(d->num_heads, "num_heads");
+  check_pos(d->num_kv_heads, "num_kv_heads");
+  check_head_dim(d->head_dim);
+  if (d->num_heads % d->num_kv_heads != 0)
+    fail(XATTN_ERR_INVALID_ARG, "num_heads (%d) must be a multiple of num_kv_heads (%d)",
+         d->num_heads, d->num_kv_heads);
+  check_pos(d->q_len, "q_len");
+  if (d->cache_len < 0) fail(XATTN_ERR_INVALID_ARG, "cache_len must be >= 0");
+  check_pos(d->capacity, "capacity");
+  if ((int64_t)d->cache_len + d->q_len > d->capacity)
+    fail(XATTN_ERR_INVALID_ARG, "cache_len + q_len (%lld) exceeds capacity (%d)",
+         (long long)d->cache_len + d->q_len, d->capacity);
+  DecodeChecked c;
+  c.io = check_dtype(d->dtype);
+  if (!(eps >= 0.f) || !std::isfinite(eps))
+    fail(XATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const int64_t rows = (int64_t)(d->num_heads / d->num_kv_heads) * d->q_len;
+  if (rows > xattn::decode_rows_limit(c.io))
+    fail(XATTN_ERR_UNSUPPORTED, "(num_heads / num_kv_heads) * q_len = %lld exceeds %d",
+         (long long)rows, xattn::decode_rows_limit(c.io));
+  c.q_elems = count4(d->batch, d->num_heads, d->q_len, d->head_dim, "xq");
+  c.kv_new_elems = count4(d->batch, d->num_kv_heads, d->q_len, d->head_dim, "xk");
+  c.cache_elems = count4(d->batch, d->num_kv_heads, d->capacity, d->head_dim, "k_cache");
+  c.rows_q = (int64_t)d->batch * d->num_heads * d->q_len;
+  c.d = {d->batch, d->num_heads, d->num_kv_heads, d->head_dim, d->q_len, d->cache_len,
+         d->capacity, eps};
+  return c;
+}
+
+// yq, then the range partials of the output and of (max, sum), each 256-byte aligned
+struct DecodeWorkspace {
+  size_t yq, part_o, part_ml, total;
+};
+DecodeWorkspace decode_workspace(const DecodeChecked& c) {
+  const xattn::DecodeShape& d = c.d;
+  const size_t ranges = (size_t)d.batch * d.num_kv_heads *
+                        xattn::decode_max_splits(d.batch, d.num_kv_heads, d.capacity) *
+                        (size_t)(d.num_heads / d.num_kv_heads) * d.q_len;
+  DecodeWorkspace w;
+  w.yq = 0;
+  w.part_o = align256((size_t)c.q_elems * io_size(c.io));
+  w.part_ml = w.part_o + align256(ranges * d.head_dim * sizeof(float));
+  w.total = w.part_ml + align256(ranges * 2 * sizeof(float));
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -352,6 +407,48 @@ xattn_status xattn_fwd_qnorm(const xattn_dims* dims, const xattn_fwd_prologue* p
               "prologue forward launch");
     hip_check(xattn::launch_attn_fwd(c.io, c.s, pro->yq, k, v, out, lse, st),
               "attention forward launch");
+  });
+}
+
+size_t xattn_decode_workspace_bytes(const xattn_decode_dims* dims) {
+  size_t n = 0;
+  const xattn_status st = guarded([&] { n = decode_workspace(check_decode_dims(dims, 0.f)).total; });
+  return st == XATTN_OK ? n : 0;
+}
+
+xattn_status xattn_decode(const xattn_decode_dims* dims, const void* xq, const void* xk,
+                          const void* v, const float* gamma_q, const float* gamma_k,
+                          const float* cos_tab, const float* sin_tab, float eps, void* k_cache,
+                          void* v_cache, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return guarded([&] {
+    const DecodeChecked c = check_decode_dims(dims, eps);
+    for (auto [p, name] : {std::pair<const void*, const char*>{xq, "xq"}, {xk, "xk"}, {v, "v"},
+                           {gamma_q, "gamma_q"}, {gamma_k, "gamma_k"}, {cos_tab, "cos_tab"},
+                           {sin_tab, "sin_tab"}, {k_cache, "k_cache"}, {v_cache, "v_cache"},
+                           {out, "out"}, {lse, "lse"}, {workspace, "workspace"}})
+      check_ptr(p, name);
+    const DecodeWorkspace w = decode_workspace(c);
+    if (workspace_bytes < w.total)
+      fail(XATTN_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, w.total);
+    const size_t es = io_size(c.io);
+    const size_t qb = (size_t)c.q_elems * es, nb = (size_t)c.kv_new_elems * es;
+    const size_t cb = (size_t)c.cache_elems * es, hdb = (size_t)c.d.head_dim * 4;
+    const size_t tb = (size_t)c.d.capacity * (c.d.head_dim / 2) * 4;
+    check_no_overlap({{k_cache, cb, "k_cache"}, {v_cache, cb, "v_cache"}, {out, qb, "out"},
+                      {lse, (size_t)c.rows_q * 4, "lse"}, {workspace, w.total, "workspace"}},
+                     {{xq, qb, "xq"}, {xk, nb, "xk"}, {v, nb, "v"}, {gamma_q, hdb, "gamma_q"},
+                      {gamma_k, hdb, "gamma_k"}, {cos_tab, tb, "cos_tab"},
+                      {sin_tab, tb, "sin_tab"}});
+    char* ws = static_cast<char*>(workspace);
+    xattn::DecodeBufs b;
+    b.xq = xq, b.xk = xk, b.v = v, b.gamma_q = gamma_q, b.gamma_k = gamma_k;
+    b.cos_tab = cos_tab, b.sin_tab = sin_tab, b.k_cache = k_cache, b.v_cache = v_cache;
+    b.out = out, b.lse = lse;
+    b.yq = ws + w.yq;
+    b.part_o = reinterpret_cast<float*>(ws + w.part_o);
+    b.part_ml = reinterpret_cast<float*>(ws + w.part_ml);
+    hip_check(xattn::launch_decode(c.io, c.d, b, (hipStream_t)stream), "decode launch");
   });
 }
 

@@ -97,6 +97,30 @@ hipError_t launch_attn_bwd(IoType io, const AttnShape& s, const void* q, const v
                            const void* dout, void* dq, void* dk, void* dv, float* delta,
                            float* lse2, bool grads_f32, hipStream_t stream);
 
+// ---- KV-cache decode (decode.hip) ---------------------------------------------------
+struct DecodeShape {
+  int batch, num_heads, num_kv_heads, head_dim, q_len, cache_len, capacity;
+  float eps;
+};
+struct DecodeBufs {
+  const void *xq, *xk, *v;
+  const float *gamma_q, *gamma_k, *cos_tab, *sin_tab;
+  void *k_cache, *v_cache, *out;
+  float* lse;
+  void* yq;        // workspace: new queries after the prologue, io dtype [B*H, Sq, hd]
+  float* part_o;   // workspace: [B*Hkv][splits][group*Sq][hd]
+  float* part_ml;  // workspace: [B*Hkv][splits][group*Sq][2]
+};
+struct DecodePlan {
+  int nsplit, ks;  // key ranges per KV head and keys per range
+};
+// Largest group * q_len the split kernel holds in registers for this io dtype.
+int decode_rows_limit(IoType io);
+int decode_max_splits(int batch, int num_kv_heads, int cache_rows);
+DecodePlan decode_plan(const DecodeShape& d, int cache_rows);
+hipError_t launch_decode(IoType io, const DecodeShape& d, const DecodeBufs& bufs,
+                         hipStream_t stream);
+
 // ---- opt-in per-kernel event timing (see xattn_profile_start) ------------------------
 // Construct around each kernel launch: records a start event now and a stop event at
 // scope exit on `stream`, when timing is enabled.

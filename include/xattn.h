@@ -17,6 +17,9 @@
  *          [batch*num_kv_heads, S, hd] for K/V; query head qh reads KV head qh/group;
  *          num_heads % num_kv_heads == 0; the K/V gradient of a shared head is the
  *          deterministic sum of its group's query-head gradients, with no atomics.
+ *   [MINT] (continued) 10.3 (KV cache: append in place, attention of the new token over
+ *          every cached key, equal to full-sequence attention), 14.2 item 5 (fused
+ *          single-token GPU decode).
  *   [T12]  xtrain "Phase T12: bf16 mixed precision", precision table: bf16 activations
  *          with fp32 accumulation; softmax, norm and RoPE computed in fp32; fp32 master
  *          weights (gamma) and gradients.
@@ -173,6 +176,46 @@ xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, con
                        const void* out, const float* lse, const void* dout, void* dq,
                        void* dk, void* dv, const xattn_prologue* pro, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* ---- KV-cache decode ---------------------------------------------------------------------
+ * Shape of a decode call: each of `batch` sequences has cache_len tokens cached and adds
+ * q_len new ones at positions cache_len .. cache_len + q_len - 1. */
+typedef struct {
+  int32_t batch;
+  int32_t num_heads;     /* query heads H */
+  int32_t num_kv_heads;  /* Hkv; H % Hkv == 0 */
+  int32_t head_dim;      /* 16, 32, 64 or 128 */
+  int32_t dtype;         /* xattn_dtype of xq, xk, v, the caches and out */
+  int32_t q_len;         /* new tokens per sequence, >= 1 */
+  int32_t cache_len;     /* tokens already in the cache per sequence, >= 0 */
+  int32_t capacity;      /* cache rows per (sequence, KV head); cache_len + q_len <= capacity */
+} xattn_decode_dims;
+
+/* Bytes of workspace xattn_decode needs.  It depends on capacity, not on cache_len, so one
+ * workspace serves every step of a cache; 0 for invalid dims. */
+size_t xattn_decode_workspace_bytes(const xattn_decode_dims* dims);
+
+/* KV-cache decode step ([MINT] 10.3 "KV cache": the new tokens' K/V are appended to the
+ * cache in place and their queries attend to every cached key; equal to full-sequence
+ * attention; [MINT] 14.2 item 5: RoPE, append and attention fused instead of per-head
+ * launches).  For new token i of sequence b at position t = cache_len + i:
+ *   q_t, k_t = QK-norm + RoPE of xq, xk at position t (as xattn_qknorm_rope_fwd);
+ *   k_cache, v_cache row t of KV head (b, kvh) <- k_t, v;
+ *   out_t = sum_{j <= t} softmax_j(q_t . k_j / sqrt(hd)) v_j over that KV head's cache rows,
+ *   lse_t = ln sum_{j <= t} exp(q_t . k_j / sqrt(hd)),
+ * for every query head qh of the group kvh = qh / (H / Hkv).
+ * xq: [B*H, q_len, hd]; xk, v: [B*Hkv, q_len, hd] (raw, io dtype); gamma_q, gamma_k: [hd];
+ * cos_tab, sin_tab: [capacity, hd/2] from xattn_rope_cache(capacity); k_cache, v_cache:
+ * [B*Hkv, capacity, hd] io dtype, rows [0, cache_len) hold the previous tokens' rotated keys
+ * and values (read), rows [cache_len, cache_len + q_len) are written, the rest untouched;
+ * out: [B*H, q_len, hd]; lse: [B*H*q_len] fp32.  (H / Hkv) * q_len must not exceed 16 for
+ * fp32 io, 8 for bf16 (XATTN_ERR_UNSUPPORTED otherwise).  The key ranges are summed in a
+ * fixed order: bitwise reproducible run to run. */
+xattn_status xattn_decode(const xattn_decode_dims* dims, const void* xq, const void* xk,
+                          const void* v, const float* gamma_q, const float* gamma_k,
+                          const float* cos_tab, const float* sin_tab, float eps, void* k_cache,
+                          void* v_cache, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* ---- Instrumentation (no effect on results) ---------------------------------------------
  * Per-kernel timing with HIP events: between xattn_profile_start and xattn_profile_stop,

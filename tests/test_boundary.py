@@ -33,7 +33,7 @@ def lib():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
     assert "gfx950" in X.xattn_version()
@@ -118,6 +118,60 @@ def test_fwd_qnorm_validation(lib):
     assert fwd_qnorm(lib, d, pro(rstd_q=A + 56 * MB)) == INVALID and "overlap" in last(lib)
     assert fwd_qnorm(lib, d, pro(), k=A + 8 * MB + 2) == INVALID and "aligned" in last(lib)
     assert fwd_qnorm(lib, dims(hd=48), pro()) == UNSUPPORTED
+
+
+def ddims(B=2, H=8, Hkv=2, hd=64, dt=1, q_len=1, cache_len=10, cap=64):
+    return X.DecodeDims(B, H, Hkv, hd, dt, q_len, cache_len, cap)
+
+
+def decode_call(lib, d, eps=1e-5, ws_bytes=None, **kw):
+    # every tensor of ddims() is well under 1 MiB; 1 MiB apart each
+    names = ["xq", "xk", "v", "gamma_q", "gamma_k", "cos_tab", "sin_tab", "k_cache", "v_cache",
+             "out", "lse", "workspace"]
+    p = {n: A + i * MB for i, n in enumerate(names)}
+    p.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.xattn_decode_workspace_bytes(ctypes.byref(d))
+    return lib.xattn_decode(ctypes.byref(d), p["xq"], p["xk"], p["v"], p["gamma_q"],
+                            p["gamma_k"], p["cos_tab"], p["sin_tab"], eps, p["k_cache"],
+                            p["v_cache"], p["out"], p["lse"], p["workspace"], ws_bytes, None)
+
+
+def test_decode_workspace_query(lib):
+    w = [lib.xattn_decode_workspace_bytes(ctypes.byref(ddims(cache_len=c))) for c in (0, 10, 63)]
+    assert w[0] > 0 and w[0] == w[1] == w[2]  # sized by capacity, not by cache_len
+    assert lib.xattn_decode_workspace_bytes(ctypes.byref(ddims(cache_len=64))) == 0
+    assert lib.xattn_decode_workspace_bytes(None) == 0
+
+
+def test_decode_validation(lib):
+    assert decode_call(lib, ddims(cache_len=64), ws_bytes=1 << 20) == INVALID
+    assert "exceeds capacity" in last(lib)
+    assert decode_call(lib, ddims(cache_len=-1), ws_bytes=1 << 20) == INVALID
+    assert "cache_len" in last(lib)
+    assert decode_call(lib, ddims(q_len=0), ws_bytes=1 << 20) == INVALID and "q_len" in last(lib)
+    assert decode_call(lib, ddims(H=6, Hkv=4), ws_bytes=1 << 20) == INVALID
+    # bf16: group * q_len = 4 * 3 = 12 > 8 rows held per KV head
+    assert decode_call(lib, ddims(q_len=3), ws_bytes=1 << 20) == UNSUPPORTED
+    assert "exceeds 8" in last(lib)
+    assert decode_call(lib, ddims(hd=48), ws_bytes=1 << 20) == UNSUPPORTED
+    assert decode_call(lib, ddims(), eps=-1.0) == INVALID and "eps" in last(lib)
+    assert decode_call(lib, ddims(), xq=None) == INVALID and "xq is NULL" in last(lib)
+    assert decode_call(lib, ddims(), lse=A + 10 * MB + 4) == INVALID and "aligned" in last(lib)
+    d = ddims()
+    ws = lib.xattn_decode_workspace_bytes(ctypes.byref(d))
+    assert decode_call(lib, d, ws_bytes=ws - 1) == INVALID and "workspace too small" in last(lib)
+    assert decode_call(lib, d, out=A) == INVALID and "overlaps input xq" in last(lib)
+    assert decode_call(lib, d, v_cache=A + 7 * MB + 256) == INVALID and "overlap" in last(lib)
+
+
+def test_decode_fp32_allows_sixteen_rows(lib):
+    # fp32: group * q_len up to 16 passes the row check and fails only on the fake pointers'
+    # workspace size (given too small on purpose), before any launch
+    d = ddims(dt=0, q_len=4)
+    assert decode_call(lib, d, ws_bytes=16) == INVALID and "workspace too small" in last(lib)
+    d = ddims(dt=0, q_len=5)
+    assert decode_call(lib, d, ws_bytes=16) == UNSUPPORTED and "exceeds 16" in last(lib)
 
 
 def test_rope_cache_validation(lib):
