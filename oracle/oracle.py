@@ -30,6 +30,10 @@ Sources (titles of the pages and the section each function follows):
   * Mint documentation, section 10.3 (KV cache): a new token computes its own
     Q/K/V, appends K/V to the cache, and its query attends to every cached key;
     the result equals full-sequence attention (decode()).
+  * Mint documentation, section 8.2 (block-causal mask of a flattened batch:
+    no attention across sample blocks, causal inside a block; RoPE positions
+    numbered inside each sample): `segments` below, documents packed along the
+    sequence axis, each a block of the mask with its own positions from 0.
 
 Readings where the pages leave a step open (listed with the design notes):
   * masking: the pages use an additive -1e9 / -1e38 or a causal flag; all three
@@ -66,6 +70,32 @@ def rope_tables(seq_len: int, head_dim: int, theta: float, pos_offset: int = 0):
     t = np.arange(seq_len, dtype=np.float64) + pos_offset
     angle = t[:, None] * inv_freq[None, :]
     return np.cos(angle), np.sin(angle)
+
+
+def rope_tables_at(positions, head_dim: int, theta: float):
+    """cos/sin of the rotation angle p * theta^(-2i/hd) for explicit per-row positions p
+    (the position of each token inside its own sample).  Returns two [len, hd/2] arrays."""
+    if head_dim % 2:
+        raise ValueError("head_dim must be even")
+    half = head_dim // 2
+    i = np.arange(half, dtype=np.float64)
+    inv_freq = np.power(np.float64(theta), -2.0 * i / head_dim)
+    angle = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return np.cos(angle), np.sin(angle)
+
+
+def segment_arrays(lengths):
+    """Documents of the given lengths packed one after another along the sequence axis.
+    Returns int64 arrays over the packed rows: lo (first row of the row's document), hi
+    (its last row) and positions (row - lo: numbering restarts in every document)."""
+    lengths = [int(n) for n in lengths]
+    if any(n <= 0 for n in lengths):
+        raise ValueError("document lengths must be positive")
+    lo = np.concatenate([np.full(n, start) for n, start in
+                         zip(lengths, np.cumsum([0] + lengths[:-1]))]).astype(np.int64)
+    hi = np.concatenate([np.full(n, start + n - 1) for n, start in
+                         zip(lengths, np.cumsum([0] + lengths[:-1]))]).astype(np.int64)
+    return lo, hi, np.arange(len(lo), dtype=np.int64) - lo
 
 
 def rope_apply(n, cos, sin):
@@ -113,22 +143,28 @@ def qk_rmsnorm_bwd(dn, x, gamma, rstd):
     return dx, dgamma
 
 
-def qknorm_rope_fwd(x, gamma, eps: float, theta: float, pos_offset: int = 0):
-    """Prologue forward on a [rows, S, hd] tensor: y = RoPE(QKnorm(x)).
-    Returns (y, rstd[rows, S])."""
+def _tables(S, hd, theta, pos_offset, positions):
+    if positions is not None:
+        return rope_tables_at(positions, hd, theta)
+    return rope_tables(S, hd, theta, pos_offset)
+
+
+def qknorm_rope_fwd(x, gamma, eps: float, theta: float, pos_offset: int = 0, positions=None):
+    """Prologue forward on a [rows, S, hd] tensor: y = RoPE(QKnorm(x)); row s at position
+    pos_offset + s, or positions[s] when given.  Returns (y, rstd[rows, S])."""
     x = _f64(x)
     _, S, hd = x.shape
-    cos, sin = rope_tables(S, hd, theta, pos_offset)
+    cos, sin = _tables(S, hd, theta, pos_offset, positions)
     n, rstd = qk_rmsnorm(x, gamma, eps)
     return rope_apply(n, cos, sin), rstd
 
 
-def qknorm_rope_bwd(dy, x, gamma, rstd, theta: float, pos_offset: int = 0):
+def qknorm_rope_bwd(dy, x, gamma, rstd, theta: float, pos_offset: int = 0, positions=None):
     """Prologue backward: dn = RoPE^-1(dy), then the RMSNorm backward.
     Returns (dx, dgamma)."""
     x = _f64(x)
     _, S, hd = x.shape
-    cos, sin = rope_tables(S, hd, theta, pos_offset)
+    cos, sin = _tables(S, hd, theta, pos_offset, positions)
     dn = rope_apply_inverse(dy, cos, sin)
     return qk_rmsnorm_bwd(dn, x, gamma, rstd)
 
@@ -142,12 +178,15 @@ def _kv_index(bh: int, num_heads: int, num_kv_heads: int) -> int:
     return b * num_kv_heads + qh // group
 
 
-def _probs(qrow, krows, scale):
-    """Scores s_ij = q_i.k_j * scale for j <= i, the rest excluded; returns
-    (P, lse) with P the causal softmax (float64)."""
+def _probs(qrow, krows, scale, seg_lo=None):
+    """Scores s_ij = q_i.k_j * scale for j <= i (and j >= seg_lo[i], the first row of
+    row i's document, when given), the rest excluded; returns (P, lse) with P the causal
+    softmax (float64)."""
     S = qrow.shape[0]
     s = (qrow @ krows.T) * scale
     keep = np.tril(np.ones((S, S), dtype=bool))
+    if seg_lo is not None:
+        keep &= np.arange(S)[None, :] >= np.asarray(seg_lo)[:, None]
     s = np.where(keep, s, -np.inf)
     m = np.max(s, axis=1, keepdims=True)
     e = np.where(keep, np.exp(s - m), 0.0)
@@ -160,10 +199,11 @@ def _check_heads(num_heads, num_kv_heads):
         raise ValueError("num_heads must be a multiple of num_kv_heads")
 
 
-def attention_fwd(q, k, v, num_heads: int, num_kv_heads: int, heads=None):
+def attention_fwd(q, k, v, num_heads: int, num_kv_heads: int, heads=None, seg_lo=None):
     """q: [B*H, S, hd]; k, v: [B*Hkv, S, hd].  Returns (out [B*H,S,hd], lse [B*H,S]).
     `heads` optionally restricts the computation to a list of B*H row indices
-    (the others stay zero)."""
+    (the others stay zero).  seg_lo: optional [S] first row of each row's document
+    (block-causal mask, the same packing for every batch row)."""
     _check_heads(num_heads, num_kv_heads)
     q, k, v = _f64(q), _f64(k), _f64(v)
     BH, S, hd = q.shape
@@ -172,12 +212,13 @@ def attention_fwd(q, k, v, num_heads: int, num_kv_heads: int, heads=None):
     lse = np.zeros((BH, S))
     for bh in (range(BH) if heads is None else heads):
         kv = _kv_index(bh, num_heads, num_kv_heads)
-        p, lse[bh] = _probs(q[bh], k[kv], scale)
+        p, lse[bh] = _probs(q[bh], k[kv], scale, seg_lo)
         out[bh] = p @ v[kv]
     return out, lse
 
 
-def attention_bwd(q, k, v, dout, num_heads: int, num_kv_heads: int, kv_heads=None):
+def attention_bwd(q, k, v, dout, num_heads: int, num_kv_heads: int, kv_heads=None,
+                  seg_lo=None):
     """Chain rule of attention_fwd.  Returns (dq, dk, dv) w.r.t. the q, k, v that
     attention_fwd consumed.  For each KV head the gradients of its `group` query
     heads are summed in ascending r.  `kv_heads` optionally restricts the work to a
@@ -197,7 +238,7 @@ def attention_bwd(q, k, v, dout, num_heads: int, num_kv_heads: int, kv_heads=Non
         dv_sum = np.zeros((S, hd))
         for r in range(group):
             bh = b * num_heads + kvh * group + r
-            p, _ = _probs(q[bh], k[kv], scale)
+            p, _ = _probs(q[bh], k[kv], scale, seg_lo)
             dp = dout[bh] @ v[kv].T                        # dP_ij = dO_i . v_j
             D = np.sum(p * dp, axis=1, keepdims=True)      # D_i = sum_j p_ij dP_ij
             ds = p * (dp - D)                              # dS_ij = p_ij (dP_ij - D_i)
@@ -213,24 +254,32 @@ def attention_bwd(q, k, v, dout, num_heads: int, num_kv_heads: int, kv_heads=Non
 # Whole path: prologue on Q and K, then attention
 # --------------------------------------------------------------------------
 def forward(xq, xk, v, gamma_q, gamma_k, num_heads, num_kv_heads, eps, theta,
-            heads=None, pos_offset: int = 0):
-    """Returns a dict with yq, rstd_q, yk, rstd_k, out, lse."""
-    yq, rq = qknorm_rope_fwd(xq, gamma_q, eps, theta, pos_offset)
-    yk, rk = qknorm_rope_fwd(xk, gamma_k, eps, theta, pos_offset)
-    out, lse = attention_fwd(yq, yk, v, num_heads, num_kv_heads, heads)
+            heads=None, pos_offset: int = 0, segments=None):
+    """Returns a dict with yq, rstd_q, yk, rstd_k, out, lse.  segments: optional list of
+    document lengths packed along the sequence axis (block-causal mask, positions
+    restarting in every document)."""
+    lo, pos = None, None
+    if segments is not None:
+        lo, _, pos = segment_arrays(segments)
+    yq, rq = qknorm_rope_fwd(xq, gamma_q, eps, theta, pos_offset, pos)
+    yk, rk = qknorm_rope_fwd(xk, gamma_k, eps, theta, pos_offset, pos)
+    out, lse = attention_fwd(yq, yk, v, num_heads, num_kv_heads, heads, lo)
     return dict(yq=yq, rstd_q=rq, yk=yk, rstd_k=rk, out=out, lse=lse)
 
 
 def backward(xq, xk, v, gamma_q, gamma_k, dout, num_heads, num_kv_heads, eps, theta,
-             kv_heads=None, pos_offset: int = 0):
+             kv_heads=None, pos_offset: int = 0, segments=None):
     """Gradients of sum(dout * out) w.r.t. the raw inputs.  Returns a dict with
     dyq, dyk (w.r.t. the post-RoPE q, k), dxq, dxk, dv, dgamma_q, dgamma_k."""
+    lo, pos = None, None
+    if segments is not None:
+        lo, _, pos = segment_arrays(segments)
     f = forward(xq, xk, v, gamma_q, gamma_k, num_heads, num_kv_heads, eps, theta,
-                heads=[], pos_offset=pos_offset)
+                heads=[], pos_offset=pos_offset, segments=segments)
     dyq, dyk, dv = attention_bwd(f["yq"], f["yk"], v, dout, num_heads, num_kv_heads,
-                                 kv_heads)
-    dxq, dgq = qknorm_rope_bwd(dyq, xq, gamma_q, f["rstd_q"], theta, pos_offset)
-    dxk, dgk = qknorm_rope_bwd(dyk, xk, gamma_k, f["rstd_k"], theta, pos_offset)
+                                 kv_heads, lo)
+    dxq, dgq = qknorm_rope_bwd(dyq, xq, gamma_q, f["rstd_q"], theta, pos_offset, pos)
+    dxk, dgk = qknorm_rope_bwd(dyk, xk, gamma_k, f["rstd_k"], theta, pos_offset, pos)
     return dict(dyq=dyq, dyk=dyk, dxq=dxq, dxk=dxk, dv=dv, dgamma_q=dgq, dgamma_k=dgk)
 
 

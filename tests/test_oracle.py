@@ -427,14 +427,15 @@ def test_qknorm_unit_gamma_is_not_identity_and_has_unit_rms():
 # ---------------------------------------------------------------------------
 # gradients: central finite differences in float64 (the pages' L = sum(W * out) harness)
 # ---------------------------------------------------------------------------
-def _fd_check(w, x, h=1e-6, tol=1e-6):
+def _fd_check(w, x, h=1e-6, tol=1e-6, segments=None):
     def loss(xq, xk, v, gq, gk):
         out = oracle.forward(xq, xk, v, gq, gk, w.num_heads, w.num_kv_heads, w.eps,
-                             w.theta)["out"]
+                             w.theta, segments=segments)["out"]
         return float(np.sum(out * x.dout))
 
     base = [np.asarray(a, np.float64).copy() for a in (x.xq, x.xk, x.v, x.gamma_q, x.gamma_k)]
-    g = oracle.backward(*base, x.dout, w.num_heads, w.num_kv_heads, w.eps, w.theta)
+    g = oracle.backward(*base, x.dout, w.num_heads, w.num_kv_heads, w.eps, w.theta,
+                        segments=segments)
     names = ["dxq", "dxk", "dv", "dgamma_q", "dgamma_k"]
     for idx, name in enumerate(names):
         arr = base[idx]
@@ -513,8 +514,8 @@ def test_planted_missing_eps_is_caught(monkeypatch):
 def test_planted_transposed_dk_mistake_is_caught(monkeypatch):
     real_bwd = O.attention_bwd
 
-    def bad(q, k, v, dout, H, Hkv, kv_heads=None):
-        dq, dk, dv = real_bwd(q, k, v, dout, H, Hkv, kv_heads)
+    def bad(q, k, v, dout, H, Hkv, kv_heads=None, seg_lo=None):
+        dq, dk, dv = real_bwd(q, k, v, dout, H, Hkv, kv_heads, seg_lo)
         return dq, dk[:, ::-1].copy(), dv
     monkeypatch.setattr(O, "attention_bwd", bad)
     with pytest.raises(AssertionError):
@@ -588,3 +589,95 @@ def test_planted_decode_position_mistake_is_caught(monkeypatch):
                         lambda xx, g, eps, theta, pos_offset=0: real(xx, g, eps, theta, 0))
     out, _, _, _ = _decode_all(x, w, 1)
     assert np.abs(out - f["out"]).max() > 1e-3
+
+
+# --------------------------------------------------------------------------
+# Block-causal mask over packed documents (Mint documentation 8.2: a flattened batch
+# is masked block by block, no attention across samples, causal inside; RoPE positions
+# counted inside each sample)
+# --------------------------------------------------------------------------
+def _pack(a, B, heads):
+    """[B*heads, S, hd] -> [heads, B*S, hd]: the batch's samples one after another."""
+    _, S, hd = a.shape
+    return np.ascontiguousarray(a.reshape(B, heads, S, hd).transpose(1, 0, 2, 3)
+                                .reshape(heads, B * S, hd))
+
+
+def _unpack(a, B, heads):
+    """Inverse of _pack for [heads, B*S, ...] arrays."""
+    S = a.shape[1] // B
+    rest = a.shape[2:]
+    return np.ascontiguousarray(a.reshape((heads, B, S) + rest).transpose((1, 0, 2) + tuple(
+        range(3, 3 + len(rest)))).reshape((B * heads, S) + rest))
+
+
+def test_segment_arrays():
+    lo, hi, pos = O.segment_arrays([3, 1, 2])
+    np.testing.assert_array_equal(lo, [0, 0, 0, 3, 4, 4])
+    np.testing.assert_array_equal(hi, [2, 2, 2, 3, 5, 5])
+    np.testing.assert_array_equal(pos, [0, 1, 2, 0, 0, 1])
+    with pytest.raises(ValueError):
+        O.segment_arrays([2, 0])
+
+
+def test_block_causal_flattened_batch_equals_batched():
+    """The pages' case: a batch of B samples of length S flattened to one row of B*S with
+    blocks of S gives, sample by sample, exactly the batched causal attention (forward,
+    backward, prologue with positions restarting per sample)."""
+    w = W.small_ragged("f32", 16, 7, 3, 4, 2, index=310)
+    x = _inputs(w)
+    B, H, Hkv = w.batch, w.num_heads, w.num_kv_heads
+    f = _fwd(w, x)
+    g = _bwd(w, x)
+    fx = oracle.forward(_pack(x.xq, B, H), _pack(x.xk, B, Hkv), _pack(x.v, B, Hkv), x.gamma_q,
+                        x.gamma_k, H, Hkv, w.eps, w.theta, segments=[w.seq_len] * B)
+    gx = oracle.backward(_pack(x.xq, B, H), _pack(x.xk, B, Hkv), _pack(x.v, B, Hkv), x.gamma_q,
+                         x.gamma_k, _pack(x.dout, B, H), H, Hkv, w.eps, w.theta,
+                         segments=[w.seq_len] * B)
+    for name, heads in (("out", H), ("lse", H), ("yq", H), ("yk", Hkv)):
+        np.testing.assert_allclose(_unpack(fx[name], B, heads), f[name], rtol=0, atol=1e-12)
+    for name, heads in (("dxq", H), ("dxk", Hkv), ("dv", Hkv)):
+        np.testing.assert_allclose(_unpack(gx[name], B, heads), g[name], rtol=0, atol=1e-12)
+    for name in ("dgamma_q", "dgamma_k"):
+        np.testing.assert_allclose(gx[name], g[name], rtol=1e-12, atol=1e-12)
+
+
+def test_single_segment_is_plain_causal():
+    w = W.small_ragged("f32", 32, 11, 1, 4, 1, index=311)
+    x = _inputs(w)
+    a, b = _fwd(w, x), _fwd(w, x, segments=[w.seq_len])
+    for n in ("out", "lse", "yq", "yk"):
+        np.testing.assert_array_equal(a[n], b[n])
+
+
+def test_segmented_attention_scalar_definition():
+    """Row i of a document starting at lo_i: softmax over keys lo_i <= j <= i only, written
+    out with scalar loops."""
+    rng = np.random.default_rng(312)
+    S, hd, segs = 9, 4, [2, 4, 1, 2]
+    q, k, v = (rng.standard_normal((1, S, hd)) for _ in range(3))
+    lo, _, _ = O.segment_arrays(segs)
+    out, lse = O.attention_fwd(q, k, v, 1, 1, seg_lo=lo)
+    for i in range(S):
+        keys = range(int(lo[i]), i + 1)
+        s = [sum(q[0, i, d] * k[0, j, d] for d in range(hd)) / math.sqrt(hd) for j in keys]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        z = sum(e)
+        for d in range(hd):
+            ref = sum(e[n] * v[0, j, d] for n, j in enumerate(keys)) / z
+            assert abs(out[0, i, d] - ref) < 1e-12
+        assert abs(lse[0, i] - (m + math.log(z))) < 1e-12
+
+
+def test_segmented_finite_difference_gradcheck():
+    _fd_check(TINY_GQA, _inputs(TINY_GQA), segments=[3, 1, 4])
+
+
+def test_planted_missing_segment_mask_is_caught(monkeypatch):
+    """A mask that forgets the document boundary (plain causal) breaks the flattened-batch
+    equality."""
+    real = O._probs
+    monkeypatch.setattr(O, "_probs", lambda q, k, scale, seg_lo=None: real(q, k, scale))
+    with pytest.raises(AssertionError):
+        test_block_causal_flattened_batch_equals_batched()
