@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of 1 GiB (for HBM counter scaling)")
+    p.add_argument("--docs", type=str, default=None,
+                   help="comma-separated document lengths packed along the sequence "
+                        "(block-causal mask); must sum to the workload's seq_len")
     p.add_argument("--decode", action="store_true",
                    help="measure the KV-cache decode step instead (xattn_decode)")
     p.add_argument("--decode-batch", type=int, default=8)
@@ -57,10 +60,18 @@ def parse():
     return p.parse_args()
 
 
-def kernel_units(w):
+def doc_pairs(w, docs):
+    """Visible (query, key) pairs per query head: S(S+1)/2 for plain causal attention, the
+    sum of L(L+1)/2 over the documents with the block-causal mask."""
+    if not docs:
+        return w.causal_pairs()
+    return sum(n * (n + 1) // 2 for n in docs)
+
+
+def kernel_units(w, docs=None):
     """Algorithmic work per launch of each kernel of the step (flops for MFMA kernels,
     HBM bytes for the memory-bound prologue), and the bound that applies."""
-    pairs = w.causal_pairs() * w.bh
+    pairs = doc_pairs(w, docs) * w.bh
     hd = w.head_dim
     io = 2 if w.dtype == "bf16" else 4
     rows_q, rows_k = w.bh * w.seq_len, w.bkv * w.seq_len
@@ -80,7 +91,7 @@ def kernel_units(w):
     }
 
 
-def traffic_for(kernel, w):
+def traffic_for(kernel, name):
     """HBM bytes per launch from the committed counter summary, if it was taken on the
     current kernel source for this workload; else None."""
     try:
@@ -93,14 +104,14 @@ def traffic_for(kernel, w):
         sha = h.hexdigest()
     except (OSError, ValueError, KeyError):
         return None
-    if t.get("kernel") != kernel or t.get("workload") != w.name or t.get("source_sha256") != sha:
+    if t.get("kernel") != kernel or t.get("workload") != name or t.get("source_sha256") != sha:
         return None
     scale = t["copy_scale"]
     return (t["fetch_kib_per_dispatch"] / scale["fetch"] +
             t["write_kib_per_dispatch"] / scale["write"]) * 1024.0
 
 
-def cpu_baseline(w, x, budget_s=10.0):
+def cpu_baseline(w, x, budget_s=10.0, docs=None):
     """The CPU oracle on a bounded sample of the workload: whole KV-head groups (a KV
     head with its query heads: prologue + attention forward + backward), taken in order
     until about `budget_s` seconds of CPU work or the whole workload is done."""
@@ -120,13 +131,14 @@ def cpu_baseline(w, x, budget_s=10.0):
         qs = [b * w.num_heads + kvh * g + r for r in range(g)]
         xq, xk, v, do = x.xq[qs], x.xk[[kv]], x.v[[kv]], x.dout[qs]
         t0 = time.perf_counter()
-        oracle.forward(xq, xk, v, x.gamma_q, x.gamma_k, g, 1, w.eps, w.theta)
-        oracle.backward(xq, xk, v, x.gamma_q, x.gamma_k, do, g, 1, w.eps, w.theta)
+        oracle.forward(xq, xk, v, x.gamma_q, x.gamma_k, g, 1, w.eps, w.theta, segments=docs)
+        oracle.backward(xq, xk, v, x.gamma_q, x.gamma_k, do, g, 1, w.eps, w.theta,
+                        segments=docs)
         dt += time.perf_counter() - t0
         done += 1
         if dt >= budget_s:
             break
-    flops = sub.attn_flops()["total"] * done
+    flops = 12 * w.head_dim * doc_pairs(w, docs) * sub.bh * done
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": (f"{done} of {w.bkv} KV-head groups (each a KV head with its {g} query "
@@ -304,13 +316,21 @@ def main():
     from causal_gqa_attention_amd.step import AttentionStep
 
     w = W.WORKLOADS[args.workload]
-    log(f"workload {w}")
+    docs = [int(n) for n in args.docs.split(",")] if args.docs else None
+    if docs and sum(docs) != w.seq_len:
+        print(f"--docs must sum to seq_len {w.seq_len}", file=sys.stderr)
+        sys.exit(2)
+    wname = w.name if not docs else f"{w.name}_docs{len(docs)}"
+    log(f"workload {w}" + (f", documents {docs}" if docs else ""))
     x = W.make_inputs(w)
     torch.cuda.set_device(0)
     step = AttentionStep(w.batch, w.seq_len, w.num_heads, w.num_kv_heads, w.head_dim, w.dtype,
-                         w.eps, w.theta).load(x.xq, x.xk, x.v, x.dout, x.gamma_q, x.gamma_k)
+                         w.eps, w.theta, doc_lengths=docs).load(x.xq, x.xk, x.v, x.dout,
+                                                                x.gamma_q, x.gamma_k)
     stream = torch.cuda.current_stream()
-    flops = w.attn_flops()
+    units_per_head = doc_pairs(w, docs) * w.bh
+    flops = {"fwd": 4 * w.head_dim * units_per_head, "bwd": 8 * w.head_dim * units_per_head,
+             "total": 12 * w.head_dim * units_per_head}
 
     for _ in range(args.warmup):
         step.run()
@@ -341,7 +361,7 @@ def main():
     torch.cuda.synchronize()
     prof = X.xattn_profile_stop()
     prof_ms = (time.perf_counter() - tp0) * 1e3 / args.steps
-    units = kernel_units(w)
+    units = kernel_units(w, docs)
     kernels = {}
     for name, (n, tot) in prof.items():
         avg = tot / max(n, 1)
@@ -361,7 +381,7 @@ def main():
         achieved, peak, unit = work / avg_s / 1e12, PEAK_TFLOPS[w.dtype], "TFLOP/s"
     else:
         achieved, peak, unit = work / avg_s / 1e9, PEAK_HBM_GBS, "GB/s"
-    traffic = traffic_for(dom, w)
+    traffic = traffic_for(dom, wname)
     roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                 "frac": achieved / peak, "traffic": traffic, "kernel": dom,
                 "work_per_launch": work, "work_basis": what}
@@ -373,7 +393,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        cpu = cpu_baseline(w, x)
+        cpu = cpu_baseline(w, x, docs=docs)
         log(f"cpu baseline {cpu['value'] * 1e3:.2f} GFLOP/s in {cpu['seconds']:.1f} s")
 
     line = {
@@ -381,9 +401,10 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len,
+        "config": {"workload": wname, "batch": w.batch, "seq_len": w.seq_len,
                    "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
-                   "head_dim": w.head_dim, "io_dtype": w.dtype, "parallelism": "none (1 GPU)"},
+                   "head_dim": w.head_dim, "io_dtype": w.dtype, "parallelism": "none (1 GPU)",
+                   **({"documents": docs} if docs else {})},
         "pct_of_peak": 100.0 * value / PEAK_TFLOPS[w.dtype],
         "attention_kernels_tflops": flops["total"] / (attn_ms * 1e-3) / 1e12 if attn_ms else None,
         "roofline": roofline,

@@ -23,11 +23,11 @@ __all__ = [
     "xattn_rope_cache", "xattn_qknorm_rope_fwd", "xattn_qknorm_rope_bwd_workspace_bytes",
     "xattn_qknorm_rope_bwd", "xattn_fwd", "xattn_fwd_qnorm", "xattn_bwd_workspace_bytes",
     "xattn_bwd",
-    "xattn_decode_workspace_bytes", "xattn_decode",
+    "xattn_decode_workspace_bytes", "xattn_decode", "xattn_segments", "xattn_rope_cache_at",
     "xattn_status_string", "xattn_last_error", "xattn_version", "xattn_profile_start",
     "xattn_profile_stop",
     "rope_cache", "qknorm_rope_fwd", "qknorm_rope_bwd", "attn_fwd", "attn_fwd_qnorm",
-    "attn_bwd", "decode",
+    "attn_bwd", "decode", "segments", "rope_cache_at",
 ]
 
 XATTN_F32 = 0
@@ -52,7 +52,8 @@ class KernelTime(ctypes.Structure):
 class Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64),
                 ("num_heads", ctypes.c_int64), ("num_kv_heads", ctypes.c_int64),
-                ("head_dim", ctypes.c_int64), ("dtype", ctypes.c_int32)]
+                ("head_dim", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("seg_lo", ctypes.c_void_p), ("seg_hi", ctypes.c_void_p)]
 
 
 class Prologue(ctypes.Structure):
@@ -91,6 +92,8 @@ def load_library() -> ctypes.CDLL:
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     sigs = {
         "xattn_rope_cache": (i32, [vp, vp, i64, i64, ctypes.c_double, vp]),
+        "xattn_rope_cache_at": (i32, [vp, vp, vp, i64, i64, ctypes.c_double, vp]),
+        "xattn_segments": (i32, [vp, i32, i64, vp, vp, vp, vp]),
         "xattn_qknorm_rope_fwd": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_float,
                                         i32, vp]),
         "xattn_qknorm_rope_bwd_workspace_bytes": (sz, [i64, i64, i64]),
@@ -216,11 +219,30 @@ def xattn_qknorm_rope_bwd(dy, x, gamma, rstd, cos_tab, sin_tab, dx, dgamma, work
         _stream(stream)), "xattn_qknorm_rope_bwd")
 
 
-def make_dims(q, num_heads, num_kv_heads) -> Dims:
+def make_dims(q, num_heads, num_kv_heads, segments=None) -> Dims:
+    """segments: None, or (seg_lo, seg_hi) int32 device tensors [S] (see xattn_segments)."""
     bh, S, hd = q.shape
     if bh % num_heads:
         raise ValueError("q.shape[0] must be batch * num_heads")
-    return Dims(bh // num_heads, S, num_heads, num_kv_heads, hd, _io(q, "q"))
+    lo = hi = None
+    if segments is not None:
+        lo = _ptr(segments[0], "seg_lo", torch.int32)
+        hi = _ptr(segments[1], "seg_hi", torch.int32)
+    return Dims(bh // num_heads, S, num_heads, num_kv_heads, hd, _io(q, "q"), lo, hi)
+
+
+def xattn_segments(cu_seqlens, ndocs, seq_len, seg_lo, seg_hi, positions=None, stream=None):
+    _check(load_library().xattn_segments(
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32), int(ndocs), int(seq_len),
+        _ptr(seg_lo, "seg_lo", torch.int32), _ptr(seg_hi, "seg_hi", torch.int32),
+        _ptr(positions, "positions", torch.int32), _stream(stream)), "xattn_segments")
+
+
+def xattn_rope_cache_at(cos_tab, sin_tab, positions, rows, head_dim, theta, stream=None):
+    _check(load_library().xattn_rope_cache_at(
+        _ptr(cos_tab, "cos_tab", torch.float32), _ptr(sin_tab, "sin_tab", torch.float32),
+        _ptr(positions, "positions", torch.int32), rows, head_dim, theta, _stream(stream)),
+        "xattn_rope_cache_at")
 
 
 def xattn_fwd(dims: Dims, q, k, v, out, lse, stream=None):
@@ -328,8 +350,29 @@ def qknorm_rope_bwd(dy, x, gamma, rstd, cos_tab, sin_tab, stream=None, workspace
     return dx, dgamma
 
 
-def attn_fwd(q, k, v, num_heads, num_kv_heads, stream=None):
-    dims = make_dims(q, num_heads, num_kv_heads)
+def segments(doc_lengths, device="cuda", stream=None):
+    """Packed documents of the given lengths: (seg_lo, seg_hi, positions) int32 device
+    tensors over the packed rows, built by xattn_segments from the document offsets."""
+    offs = [0]
+    for n in doc_lengths:
+        offs.append(offs[-1] + int(n))
+    cu = torch.tensor(offs, dtype=torch.int32, device=device)
+    S = offs[-1]
+    lo, hi, pos = (torch.empty(S, dtype=torch.int32, device=device) for _ in range(3))
+    xattn_segments(cu, len(offs) - 1, S, lo, hi, pos, stream)
+    return lo, hi, pos
+
+
+def rope_cache_at(positions, head_dim, theta, stream=None):
+    rows = positions.numel()
+    cos_tab = torch.empty(rows, head_dim // 2, dtype=torch.float32, device=positions.device)
+    sin_tab = torch.empty_like(cos_tab)
+    xattn_rope_cache_at(cos_tab, sin_tab, positions, rows, head_dim, theta, stream)
+    return cos_tab, sin_tab
+
+
+def attn_fwd(q, k, v, num_heads, num_kv_heads, stream=None, segments=None):
+    dims = make_dims(q, num_heads, num_kv_heads, segments)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[0] * q.shape[1], dtype=torch.float32, device=q.device)
     xattn_fwd(dims, q, k, v, out, lse, stream)
@@ -337,9 +380,9 @@ def attn_fwd(q, k, v, num_heads, num_kv_heads, stream=None):
 
 
 def attn_fwd_qnorm(xq, gamma_q, cos_tab, sin_tab, eps, k, v, num_heads, num_kv_heads,
-                   stream=None):
+                   stream=None, segments=None):
     """Forward with the Q-side QK-norm + RoPE fused; returns (out, lse, yq, rstd_q)."""
-    dims = make_dims(xq, num_heads, num_kv_heads)
+    dims = make_dims(xq, num_heads, num_kv_heads, segments)
     out, yq = torch.empty_like(xq), torch.empty_like(xq)
     lse = torch.empty(xq.shape[0] * xq.shape[1], dtype=torch.float32, device=xq.device)
     rstd_q = torch.empty_like(lse)
@@ -348,10 +391,10 @@ def attn_fwd_qnorm(xq, gamma_q, cos_tab, sin_tab, eps, k, v, num_heads, num_kv_h
 
 
 def attn_bwd(q, k, v, out, lse, dout, num_heads, num_kv_heads, prologue=None, stream=None,
-             workspace=None):
+             workspace=None, segments=None):
     """Returns (dq, dk, dv); with a prologue dict (see xattn_bwd, without the dgamma
     entries) returns (dxq, dxk, dv, dgamma_q, dgamma_k)."""
-    dims = make_dims(q, num_heads, num_kv_heads)
+    dims = make_dims(q, num_heads, num_kv_heads, segments)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     pro = None
     if prologue is not None:

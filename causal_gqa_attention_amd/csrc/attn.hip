@@ -164,6 +164,16 @@ __device__ __forceinline__ void store_column(TO* dst, const f32x16 (&acc)[NDT], 
   }
 }
 
+// Packed documents (block-causal mask): first / last row of row i's document, clamped into
+// the sequence (so a bad array gives wrong values but no access outside the tensors);
+// without documents 0 and S - 1.
+__device__ __forceinline__ int doc_lo(const int* seg_lo, int i, int S) {
+  return seg_lo == nullptr ? 0 : min(max(seg_lo[min(i, S - 1)], 0), S - 1);
+}
+__device__ __forceinline__ int doc_hi(const int* seg_hi, int i, int S) {
+  return seg_hi == nullptr ? S - 1 : min(max(seg_hi[min(i, S - 1)], 0), S - 1);
+}
+
 constexpr int kWaves = 4;
 constexpr int kBlockM = 32 * kWaves;  // queries per forward / dq workgroup
 constexpr int kBlockN = 64;           // keys per LDS stage in forward / dq
@@ -177,7 +187,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ q,
                                                        const T* __restrict__ v,
                                                        T* __restrict__ out,
                                                        float* __restrict__ lse, int S, int H,
-                                                       int Hkv, float scale_log2) {
+                                                       int Hkv, float scale_log2,
+                                                       const int* __restrict__ seg_lo) {
   using C = Tile<T, HD>;
   __shared__ __attribute__((aligned(16))) T ks[kBlockN * C::LDS_ROW];
   __shared__ __attribute__((aligned(16))) T vs[kBlockN * C::LDS_ROW];
@@ -199,10 +210,13 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ q,
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt) o[dt] = zero16();
   float m_run = -INFINITY, l_run = 0.f;
+  // row i sees keys doc_lo(i) <= j <= i
+  const bool docs = seg_lo != nullptr;
+  const int lo_row = doc_lo(seg_lo, qrow, S), lo_wave = doc_lo(seg_lo, qw0, S);
 
   const int kend = min(S, q0 + kBlockM);
   const int ntiles = (kend + kBlockN - 1) / kBlockN;
-  for (int kt = 0; kt < ntiles; ++kt) {
+  for (int kt = doc_lo(seg_lo, q0, S) / kBlockN; kt < ntiles; ++kt) {
     const int k0 = kt * kBlockN;
     __syncthreads();
     stage_rows<T, HD>(ks, kp, k0, kBlockN, S, tid, 256);
@@ -212,8 +226,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ q,
     for (int s = 0; s < kBlockN / 32; ++s) {
       const int kb = k0 + 32 * s;
       if (kb > qw0 + 31 || kb >= S) break;  // wave-uniform: keys all in the future / past end
+      if (kb + 31 < lo_wave) continue;      // wave-uniform: before every row's document
       f32x16 st = contract_hd<T, HD>(ks, 32 * s, qf, lane);
-      const bool edge = (kb + 31 > qw0) || (kb + 31 >= S);
+      const bool edge = (kb + 31 > qw0) || (kb + 31 >= S) || docs;
       float sv[16];
       float tmax = -INFINITY;
 #pragma unroll
@@ -221,18 +236,20 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ q,
         float x = st[i] * scale_log2;
         if (edge) {
           const int key = kb + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (key > qrow || key >= S) x = -INFINITY;
+          if (key > qrow || key >= S || key < lo_row) x = -INFINITY;
         }
         sv[i] = x;
         tmax = fmaxf(tmax, x);
       }
       tmax = fmaxf(tmax, shfl_xor(tmax, 32));
       const float m_new = fmaxf(m_run, tmax);
-      const float alpha = fast_exp2(m_run - m_new);
+      // a row that has seen no visible key yet (possible with documents) stays empty
+      const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_ref);
       float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        sv[i] = fast_exp2(sv[i] - m_new);
+        sv[i] = fast_exp2(sv[i] - m_ref);
         psum += sv[i];
       }
       l_run = l_run * alpha + psum;
@@ -259,7 +276,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ out, const T* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ delta, TG* __restrict__ dq, int S, int H, int Hkv, float scale_log2,
-    float scale) {
+    float scale, const int* __restrict__ seg_lo) {
   using C = Tile<T, HD>;
   __shared__ __attribute__((aligned(16))) T ks[kBlockN * C::LDS_ROW];
   __shared__ __attribute__((aligned(16))) T vs[kBlockN * C::LDS_ROW];
@@ -296,9 +313,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt) acc[dt] = zero16();
 
+  const bool docs = seg_lo != nullptr;
+  const int lo_row = doc_lo(seg_lo, qrow, S), lo_wave = doc_lo(seg_lo, qw0, S);
   const int kend = min(S, q0 + kBlockM);
   const int ntiles = (kend + kBlockN - 1) / kBlockN;
-  for (int kt = 0; kt < ntiles; ++kt) {
+  for (int kt = doc_lo(seg_lo, q0, S) / kBlockN; kt < ntiles; ++kt) {
     const int k0 = kt * kBlockN;
     __syncthreads();
     stage_rows<T, HD>(ks, kp, k0, kBlockN, S, tid, 256);
@@ -308,16 +327,17 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     for (int s = 0; s < kBlockN / 32; ++s) {
       const int kb = k0 + 32 * s;
       if (kb > qw0 + 31 || kb >= S) break;
+      if (kb + 31 < lo_wave) continue;
       const f32x16 st = contract_hd<T, HD>(ks, 32 * s, qf, lane);   // S^T: keys x queries
       const f32x16 dpt = contract_hd<T, HD>(vs, 32 * s, df, lane);  // dP^T
-      const bool edge = (kb + 31 > qw0) || (kb + 31 >= S);
+      const bool edge = (kb + 31 > qw0) || (kb + 31 >= S) || docs;
       float dsv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float p = fast_exp2(st[i] * scale_log2 - lse2);
         if (edge) {
           const int key = kb + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (key > qrow || key >= S) p = 0.f;
+          if (key > qrow || key >= S || key < lo_row) p = 0.f;
         }
         dsv[i] = p * (dpt[i] - D);
       }
@@ -340,7 +360,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, TG* __restrict__ dk, T* __restrict__ dv, int S, int H,
-    int Hkv, float scale_log2, float scale) {
+    int Hkv, float scale_log2, float scale, const int* __restrict__ seg_hi) {
   using C = Tile<T, HD>;
   constexpr int KW = kWaves / QS;
   constexpr int BNK = 32 * KW;
@@ -370,9 +390,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt) dkt[dt] = dvt[dt] = zero16();
 
+  // key j is seen by queries j <= i <= doc_hi(j); query tiles end at the workgroup's last
+  // key's last query
+  const bool docs = seg_hi != nullptr;
+  const int hi_key = doc_hi(seg_hi, key, S);
   const int qt_first = k0 / kBlockMQ;
-  const int nqt = (S + kBlockMQ - 1) / kBlockMQ;
-  const int nsteps = (nqt - qt_first + QS - 1) / QS;
+  const int nqt = min((S + kBlockMQ - 1) / kBlockMQ,
+                      doc_hi(seg_hi, k0 + BNK - 1, S) / kBlockMQ + 1);
+  const int nsteps = max(0, (nqt - qt_first + QS - 1) / QS);
   const bool wave_live = kw0 < S;
 
   for (int r = 0; r < group; ++r) {
@@ -397,13 +422,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 
       const f32x16 st = contract_hd<T, HD>(qtile, 0, kf, lane);   // S: queries x keys
       const f32x16 dpt = contract_hd<T, HD>(dtile, 0, vf, lane);  // dP
-      const bool edge = q0 < kw0 + 31;
+      const bool edge = q0 < kw0 + 31 || docs;
       float pv[16], dsv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int mi = 8 * (i >> 2) + 4 * h + (i & 3);
         float p = fast_exp2(st[i] * scale_log2 - lse_s[sp][mi]);
-        if (edge && q0 + mi < key) p = 0.f;
+        if (edge && (q0 + mi < key || q0 + mi > hi_key)) p = 0.f;
         pv[i] = p;
         dsv[i] = p * (dpt[i] - del_s[sp][mi]);
       }
@@ -462,7 +487,7 @@ static hipError_t fwd_impl(const AttnShape& s, const void* q, const void* k, con
   ProfScope prof("attn_fwd", stream);
   hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(256), 0, stream, (const T*)q,
                      (const T*)k, (const T*)v, (T*)out, lse, s.seq_len, s.num_heads,
-                     s.num_kv_heads, scale_of(HD) * kLog2e);
+                     s.num_kv_heads, scale_of(HD) * kLog2e, s.seg_lo);
   return hipPeekAtLastError();
 }
 
@@ -504,7 +529,7 @@ static void launch_dkdv(const AttnShape& s, const void* q, const void* k, const 
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD, TG, QS>), grid, dim3(256), 0, stream,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta,
                      (TG*)dk, (T*)dv, s.seq_len, s.num_heads, s.num_kv_heads,
-                     scale_of(HD) * kLog2e, scale_of(HD));
+                     scale_of(HD) * kLog2e, scale_of(HD), s.seg_hi);
 }
 
 template <typename T, int HD, typename TG>
@@ -517,7 +542,7 @@ static hipError_t bwd_impl(const AttnShape& s, const void* q, const void* k, con
     hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD, TG>), grid, dim3(256), 0, stream,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)out, (const T*)dout,
                        lse, delta, (TG*)dq, s.seq_len, s.num_heads, s.num_kv_heads,
-                       scale_of(HD) * kLog2e, scale_of(HD));
+                       scale_of(HD) * kLog2e, scale_of(HD), s.seg_lo);
   }
   hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess) return e;

@@ -520,10 +520,14 @@ struct SoftmaxState {
 // Online softmax of one 32-key sub-tile: scores st (keys x this lane's query) update the
 // running max / sum (rescaling the output accumulator lazily) and give the packed P^T
 // operand of the P.V product.
+// Masked sub-tiles also exclude keys before lo (the first row of the lane's document);
+// a row can then meet a sub-tile with no visible key before its first one, so the masked
+// instantiation keeps a row with no visible key yet (max -inf) empty instead of forming
+// -inf - -inf.
 template <int HD, bool MASK>
 __device__ __forceinline__ void fwd_softmax(f32x16 (&o)[HD / 32], SoftmaxState& sm,
                                             const f32x16& st, bf16x8 (&pb)[2], int kb,
-                                            int qrow, int S, int h, float scale_log2) {
+                                            int qrow, int lo, int S, int h, float scale_log2) {
   float sv[16];
   float tmax = -INFINITY;
 #pragma unroll
@@ -531,7 +535,7 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&o)[HD / 32], SoftmaxState& 
     float x = st[i];
     if constexpr (MASK) {
       const int key = kb + 8 * (i >> 2) + 4 * h + (i & 3);
-      if (key > qrow || key >= S) x = -INFINITY;
+      if (key > qrow || key >= S || key < lo) x = -INFINITY;
     }
     sv[i] = x;
     tmax = fmaxf(tmax, x);
@@ -540,16 +544,17 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&o)[HD / 32], SoftmaxState& 
   // rescale only when the reference max grows by more than 2^8
   if (__any(tmax > sm.m + 8.f)) {
     const float m_new = fmaxf(sm.m, tmax);
-    const float alpha = fast_exp2(sm.m - m_new);
+    const float alpha = (MASK && m_new == -INFINITY) ? 1.f : fast_exp2(sm.m - m_new);
     sm.l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < HD / 32; ++dt) o[dt] *= alpha;
     sm.m = m_new;
   }
+  const float mref = (MASK && sm.m == -INFINITY) ? 0.f : sm.m;
   float psum = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    sv[i] = fast_exp2(sv[i] * scale_log2 - sm.m);
+    sv[i] = fast_exp2(sv[i] * scale_log2 - mref);
     psum += sv[i];
   }
   sm.l += psum;
@@ -560,10 +565,46 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&o)[HD / 32], SoftmaxState& 
 template <int HD, bool MASK>
 __device__ __forceinline__ void fwd_subtile(f32x16 (&o)[HD / 32], SoftmaxState& sm,
                                             const f32x16& st, const char* vsub, uint32_t tl,
-                                            int kb, int qrow, int S, int h, float scale_log2) {
+                                            int kb, int qrow, int lo, int S, int h,
+                                            float scale_log2) {
   bf16x8 pb[2];
-  fwd_softmax<HD, MASK>(o, sm, st, pb, kb, qrow, S, h, scale_log2);
+  fwd_softmax<HD, MASK>(o, sm, st, pb, kb, qrow, lo, S, h, scale_log2);
   acc_tr<HD>(o, vsub, tl, pb);
+}
+
+// Document bounds of a query-major workgroup (Mint documentation 8.2, block-causal mask
+// of packed documents: row i sees keys seg_lo[i] <= j <= i).  seg_lo is non-decreasing;
+// without documents every bound is 0.  Values are clamped into the sequence, so a bad
+// array gives wrong results but no access outside the tensors.
+struct QDoc {
+  int lo_row;   // first key of the lane's row
+  int lo_wave;  // first key of the wave's first row (the wave's smallest)
+  int t_first;  // first key stage any row of the workgroup sees
+  int t_plain;  // first stage whose keys every row of the workgroup sees (below the diagonal)
+};
+__device__ __forceinline__ QDoc q_doc(const int* __restrict__ seg_lo, int q0, int qw0,
+                                      int qrow, int S) {
+  QDoc d{0, 0, 0, 0};
+  if (seg_lo != nullptr) {
+    auto at = [&](int i) { return min(max(seg_lo[min(i, S - 1)], 0), S - 1); };
+    d.lo_row = at(qrow);
+    d.lo_wave = __builtin_amdgcn_readfirstlane(at(qw0));
+    d.t_first = __builtin_amdgcn_readfirstlane(at(q0)) / kBN;
+    d.t_plain = (__builtin_amdgcn_readfirstlane(at(q0 + kBM - 1)) + kBN - 1) / kBN;
+  }
+  return d;
+}
+
+// Stage loop of a query-major workgroup over key stages [t_first, ntiles): stages that every
+// row sees in full run `plain`, the rest (document starts, the diagonal, the ragged end)
+// `masked`.
+template <typename F>
+__device__ __forceinline__ void q_stage_loop(const QDoc& doc, int nplain, int ntiles, F&& stage) {
+  const int a = min(doc.t_plain, ntiles);
+  for (int t = doc.t_first; t < a; ++t) stage(std::true_type{}, t);
+  for (int t = max(doc.t_plain, doc.t_first); t < nplain; ++t) stage(std::false_type{}, t);
+  for (int t = max(max(nplain, doc.t_plain), doc.t_first); t < ntiles; ++t)
+    stage(std::true_type{}, t);
 }
 
 // QK-norm + RoPE forward on the forward's resident Q rows (Mint documentation 5.4.1,
@@ -645,7 +686,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const bf16* __restrict__ q,
                                                      bf16* __restrict__ out,
                                                      float* __restrict__ lse, int S, int H,
                                                      int Hkv, float scale_log2, int nqt,
-                                                     int xcd, ProFwd pro) {
+                                                     int xcd, ProFwd pro,
+                                                     const int* __restrict__ seg_lo) {
   constexpr int ROWB = 2 * HD;
   constexpr int TILEB = kBN * ROWB;
   using D = Dma<HD, kBN, 4>;
@@ -664,6 +706,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const bf16* __restrict__ q,
   D dma;
   dma.init(wv, lane);
 
+  const QDoc doc = q_doc(seg_lo, q0, qw0, qrow, S);
+  const int t0 = doc.t_first;  // stages run from t0; buffers are numbered from it
   const int ntiles = (min(S, q0 + kBM) + kBN - 1) / kBN;
   auto issue = [&](int t, int buf) {
     const int g0 = t * kBN, nv = S - g0;
@@ -674,42 +718,42 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const bf16* __restrict__ q,
   if constexpr (PROQ) {
     // the first tiles' copies are in flight while the Q rows are normalised and rotated
 #pragma unroll
-    for (int t = 0; t < NBUF - 1; ++t)
-      if (t < ntiles) issue(t, t);
+    for (int u = 0; u < NBUF - 1; ++u)
+      if (t0 + u < ntiles) issue(t0 + u, u);
     qknorm_rope_frag<HD>(qf, pro, (size_t)bh * S, qrow, S, lane);
   } else {
     load_frag<HD>(qf, q + (size_t)bh * S * HD, qrow, S, lane);
 #pragma unroll
-    for (int t = 0; t < NBUF - 1; ++t)
-      if (t < ntiles) issue(t, t);
+    for (int u = 0; u < NBUF - 1; ++u)
+      if (t0 + u < ntiles) issue(t0 + u, u);
   }
   f32x16 o[HD / 32];
 #pragma unroll
   for (int dt = 0; dt < HD / 32; ++dt) o[dt] = zero16();
   SoftmaxState sm{-INFINITY, 0.f};
   // Stage t: wait for its tile, prefetch stage t + NBUF - 1, then compute.  Stages below
-  // nplain lie strictly before the block's first query and inside the sequence, so no
-  // wave needs masking there; the few remaining (diagonal / ragged end) stages run the
-  // masked instantiation.
+  // nplain lie strictly before the block's first query and inside the sequence, and (with
+  // documents) at or after every row's document start, so no wave needs masking there; the
+  // few remaining stages run the masked instantiation.
   auto stage = [&](auto mask_tag, int t) {
     constexpr bool MASK = decltype(mask_tag)::value;
     if (NBUF > 2 && t + 1 < ntiles) stage_barrier<(NBUF > 2 ? NL : 0)>();
     else stage_barrier<0>();
-    if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
-    const int bb = t % NBUF;
+    if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1, (t - t0 + NBUF - 1) % NBUF);
+    const int bb = (t - t0) % NBUF;
     const char* ks = lds + (2 * bb) * TILEB;
     const char* vs = lds + (2 * bb + 1) * TILEB;
 #pragma unroll
     for (int s = 0; s < kBN / 32; ++s) {
       const int kb = t * kBN + 32 * s;
       if (MASK && (kb > qw0 + 31 || kb >= S)) break;  // wave-uniform
+      if (MASK && kb + 31 < doc.lo_wave) continue;     // before every row's document
       const f32x16 st = contract_rows<HD>(ks + 32 * s * ROWB, al, qf);
-      fwd_subtile<HD, MASK>(o, sm, st, vs + 32 * s * ROWB, tl, kb, qrow, S, h, scale_log2);
+      fwd_subtile<HD, MASK>(o, sm, st, vs + 32 * s * ROWB, tl, kb, qrow, doc.lo_row, S, h,
+                            scale_log2);
     }
   };
-  const int nplain = min(q0 / kBN, S / kBN);
-  for (int t = 0; t < nplain; ++t) stage(std::false_type{}, t);
-  for (int t = nplain; t < ntiles; ++t) stage(std::true_type{}, t);
+  q_stage_loop(doc, min(q0 / kBN, S / kBN), ntiles, stage);
   const float l = sm.l + shfl_xor(sm.l, 32);
   if (qrow < S) {
     store_col<bf16, HD>(out + ((size_t)bh * S + qrow) * HD, o, 1.0f / l, h);
@@ -723,15 +767,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const bf16* __restrict__ q,
 template <int HD, bool MASK>
 __device__ __forceinline__ void dq_subtile(f32x16 (&acc)[HD / 32], const f32x16& st,
                                            const f32x16& dpt, const char* ksub, uint32_t tl,
-                                           int kb, int qrow, int S, int h, float scale_log2,
-                                           float lse2, float D) {
+                                           int kb, int qrow, int lo, int S, int h,
+                                           float scale_log2, float lse2, float D) {
   float dsv[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     float p = fast_exp2(st[i] * scale_log2 - lse2);
     if constexpr (MASK) {
       const int key = kb + 8 * (i >> 2) + 4 * h + (i & 3);
-      if (key > qrow || key >= S) p = 0.f;
+      if (key > qrow || key >= S || key < lo) p = 0.f;
     }
     dsv[i] = p * (dpt[i] - D);
   }
@@ -745,7 +789,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ out, const bf16* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ lse2_out, float* __restrict__ delta, bf16* __restrict__ dq, int S, int H,
-    int Hkv, float scale_log2, float scale, int nqt, int xcd, ProBwd pro) {
+    int Hkv, float scale_log2, float scale, int nqt, int xcd, ProBwd pro,
+    const int* __restrict__ seg_lo) {
   constexpr int ROWB = 2 * HD;
   constexpr int TILEB = kBN * ROWB;
   using D = Dma<HD, kBN, 4>;
@@ -787,6 +832,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
 #pragma unroll
   for (int dt = 0; dt < HD / 32; ++dt) acc[dt] = zero16();
 
+  const QDoc doc = q_doc(seg_lo, q0, qw0, qrow, S);
+  const int t0 = doc.t_first;  // stages run from t0; buffers are numbered from it
   const int ntiles = (min(S, q0 + kBM) + kBN - 1) / kBN;
   auto issue = [&](int t, int buf) {
     const int g0 = t * kBN, nv = S - g0;
@@ -794,29 +841,28 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
     dma.issue(lds + (2 * buf + 1) * TILEB, vp + (size_t)g0 * ROWB, wv, nv);
   };
 #pragma unroll
-  for (int t = 0; t < NBUF - 1; ++t)
-    if (t < ntiles) issue(t, t);
+  for (int u = 0; u < NBUF - 1; ++u)
+    if (t0 + u < ntiles) issue(t0 + u, u);
   auto stage = [&](auto mask_tag, int t) {
     constexpr bool MASK = decltype(mask_tag)::value;
     if (NBUF > 2 && t + 1 < ntiles) stage_barrier<(NBUF > 2 ? NL : 0)>();
     else stage_barrier<0>();
-    if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
-    const int bb = t % NBUF;
+    if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1, (t - t0 + NBUF - 1) % NBUF);
+    const int bb = (t - t0) % NBUF;
     const char* ks = lds + (2 * bb) * TILEB;
     const char* vs = lds + (2 * bb + 1) * TILEB;
 #pragma unroll
     for (int s = 0; s < kBN / 32; ++s) {
       const int kb = t * kBN + 32 * s;
       if (MASK && (kb > qw0 + 31 || kb >= S)) break;
+      if (MASK && kb + 31 < doc.lo_wave) continue;  // before every row's document
       const f32x16 st = contract_rows<HD>(ks + 32 * s * ROWB, al, qf);   // S^T
       const f32x16 dpt = contract_rows<HD>(vs + 32 * s * ROWB, al, df);  // dP^T
-      dq_subtile<HD, MASK>(acc, st, dpt, ks + 32 * s * ROWB, tl, kb, qrow, S, h, scale_log2,
-                           lse2, Dq);
+      dq_subtile<HD, MASK>(acc, st, dpt, ks + 32 * s * ROWB, tl, kb, qrow, doc.lo_row, S, h,
+                           scale_log2, lse2, Dq);
     }
   };
-  const int nplain = min(q0 / kBN, S / kBN);
-  for (int t = 0; t < nplain; ++t) stage(std::false_type{}, t);
-  for (int t = nplain; t < ntiles; ++t) stage(std::true_type{}, t);
+  q_stage_loop(doc, min(q0 / kBN, S / kBN), ntiles, stage);
   if constexpr (PRO) {
     static_assert(sizeof(lds) >= 4 * 32 * HD * sizeof(float), "epilogue tiles fit");
     lds_barrier();  // every wave is done with the staged tiles
@@ -849,7 +895,7 @@ __device__ __forceinline__ void dkdv_step_reg(f32x16 (&dkt)[HD / 32], f32x16 (&d
                                               const char* qs, const char* dos,
                                               const float* stats, const bf16x8 (&kf)[HD / 16],
                                               const bf16x8 (&vf)[HD / 16], uint32_t al,
-                                              uint32_t tl, int q0, int key, int S,
+                                              uint32_t tl, int q0, int key, int khi, int S,
                                               float scale_log2, int h) {
   bf16x8 qa[HD / 16], da[HD / 16], ta[2][HD / 32], tq[2][HD / 32];
   auto read_rows = [&](bf16x8 (&x)[HD / 16], const char* base) {
@@ -893,7 +939,7 @@ __device__ __forceinline__ void dkdv_step_reg(f32x16 (&dkt)[HD / 32], f32x16 (&d
       float p = fast_exp2(st[4 * g + j] * scale_log2 - l2[j]);
       if constexpr (MASK) {
         const int qi = q0 + 8 * g + 4 * h + j;
-        if (qi < key || qi >= S) p = 0.f;
+        if (qi < key || qi >= S || qi > khi) p = 0.f;
       }
       pv[4 * g + j] = p;
     }
@@ -925,12 +971,33 @@ __device__ __forceinline__ void dkdv_step_reg(f32x16 (&dkt)[HD / 32], f32x16 (&d
 
 // Shared variant: 4 waves own 128 consecutive keys of one KV head and share each staged
 // 32-query tile of every query head of the group.
+// Document bounds of a key-major workgroup (block-causal mask of packed documents: key j
+// is seen by queries j <= i <= seg_hi[j]).  seg_hi is non-decreasing; without documents
+// every bound is S - 1.  Clamped into the sequence like QDoc.
+struct KDoc {
+  int hi_key;    // last query of the lane's key
+  int hi_first;  // last query of the workgroup's (or wave's) first key: the smallest
+  int hi_last;   // last query of its last key: the largest
+};
+__device__ __forceinline__ KDoc k_doc(const int* __restrict__ seg_hi, int k_first, int k_last,
+                                      int key, int S) {
+  KDoc d{S - 1, S - 1, S - 1};
+  if (seg_hi != nullptr) {
+    auto at = [&](int i) { return min(max(seg_hi[min(i, S - 1)], 0), S - 1); };
+    d.hi_key = at(key);
+    d.hi_first = __builtin_amdgcn_readfirstlane(at(k_first));
+    d.hi_last = __builtin_amdgcn_readfirstlane(at(k_last));
+  }
+  return d;
+}
+
 template <int HD, int NBUF, bool PRO>
 __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_shared_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ delta, bf16* __restrict__ dk, bf16* __restrict__ dv, int S, int H,
-    int Hkv, float scale_log2, float scale, int nkt, int xcd, ProBwd pro) {
+    int Hkv, float scale_log2, float scale, int nkt, int xcd, ProBwd pro,
+    const int* __restrict__ seg_hi) {
   constexpr int ROWB = 2 * HD;
   constexpr int TILEB = kBQ * ROWB;
   using D = Dma<HD, kBQ, 4>;
@@ -954,8 +1021,12 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_shared_kernel(
 #pragma unroll
   for (int dt = 0; dt < HD / 32; ++dt) dkt[dt] = dvt[dt] = zero16();
 
+  const KDoc doc = k_doc(seg_hi, k0, k0 + 127, key, S);
+  const int hi_wave = __builtin_amdgcn_readfirstlane(
+      seg_hi != nullptr ? min(max(seg_hi[min(kw0 + 31, S - 1)], 0), S - 1) : S - 1);
   const int qt_first = k0 / kBQ, nqt = (S + kBQ - 1) / kBQ;
-  const int per_r = nqt - qt_first;
+  // query tiles up to the last query of the workgroup's last key
+  const int per_r = max(0, min(nqt, doc.hi_last / kBQ + 1) - qt_first);
   const int nst = group * per_r;
   auto issue = [&](int t, int buf) {
     const int r = t / per_r, qt = qt_first + t % per_r;
@@ -978,21 +1049,21 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_shared_kernel(
     if (t + NBUF - 1 < nst) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
     const int bb = t % NBUF;
     const int q0 = (qt_first + t % per_r) * kBQ;
-    if (live && q0 + kBQ - 1 >= kw0)
+    if (live && q0 + kBQ - 1 >= kw0 && q0 <= hi_wave)
       dkdv_step_reg<HD, MASK, kDkdvPF>(dkt, dvt, lds + (2 * bb) * TILEB,
                                        lds + (2 * bb + 1) * TILEB, stats[bb], kf, vf, al, tl,
-                                       q0, key, S, scale_log2, h);
+                                       q0, key, doc.hi_key, S, scale_log2, h);
   };
-  // Per query head: the first four query tiles straddle the diagonal of some wave's keys
-  // and a ragged last tile runs past the sequence end; the rest need no masking.
-  const bool ragged = (S % kBQ) != 0;
+  // Per query head: the first four query tiles straddle the diagonal of some wave's keys;
+  // tiles reaching past the first key's last query (a document end, or the ragged end of
+  // the sequence) need masking too; the rest need none.
   const int nmask_head = min(4, per_r);
-  const int plain_end = per_r - ((ragged && per_r > nmask_head) ? 1 : 0);
+  const int plain_end = max(nmask_head, min(per_r, (doc.hi_first + 1) / kBQ - qt_first));
   for (int r = 0; r < group; ++r) {
     const int t0 = r * per_r;
     for (int i = 0; i < nmask_head; ++i) stage(std::true_type{}, t0 + i);
     for (int i = nmask_head; i < plain_end; ++i) stage(std::false_type{}, t0 + i);
-    if (plain_end < per_r) stage(std::true_type{}, t0 + per_r - 1);
+    for (int i = plain_end; i < per_r; ++i) stage(std::true_type{}, t0 + i);
   }
   if (key < S) store_col<bf16, HD>(dv + ((size_t)kvbh * S + key) * HD, dvt, 1.0f, h);
   if constexpr (PRO) {
@@ -1020,7 +1091,8 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_private_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ delta, bf16* __restrict__ dk, bf16* __restrict__ dv, int S, int H,
-    int Hkv, float scale_log2, float scale, int nkt, int xcd, ProBwd pro) {
+    int Hkv, float scale_log2, float scale, int nkt, int xcd, ProBwd pro,
+    const int* __restrict__ seg_hi) {
   constexpr int ROWB = 2 * HD;
   constexpr int TILEB = kBQ * ROWB;
   constexpr int WAVEB = NBUF * 2 * TILEB;  // one wave's staging bytes
@@ -1045,8 +1117,11 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_private_kernel(
 #pragma unroll
   for (int dt = 0; dt < HD / 32; ++dt) dkt[dt] = dvt[dt] = zero16();
 
-  const int qt_first = kw0 / kBQ, nqt = (S + kBQ - 1) / kBQ;
-  const int per_r = (nqt - qt_first - wv + 3) / 4;  // this wave's tiles per query head
+  const KDoc doc = k_doc(seg_hi, kw0, kw0 + 31, key, S);
+  const int qt_first = kw0 / kBQ;
+  // query tiles up to the last query of the workgroup's last key
+  const int qt_end = min((S + kBQ - 1) / kBQ, doc.hi_last / kBQ + 1);
+  const int per_r = max(0, (qt_end - qt_first - wv + 3) / 4);  // this wave's tiles per head
   const int nst = group * per_r;
   // tiles are issued in order: (query head r, this wave's i-th tile of it); the cursor
   // avoids a division per stage
@@ -1082,19 +1157,20 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_private_kernel(
     const int q0 = (qt_first + wv + 4 * i) * kBQ;
     dkdv_step_reg<HD, MASK, kDkdvPF>(dkt, dvt, mine + (2 * bb) * TILEB,
                                      mine + (2 * bb + 1) * TILEB, stats[wv][bb], kf, vf, al, tl,
-                                     q0, key, S, scale_log2, h);
+                                     q0, key, doc.hi_key, S, scale_log2, h);
   };
   // Per query head: only wave 0's first tile meets the diagonal (its keys start at its
-  // first query), and a ragged last tile runs past the sequence end.
+  // first query); tiles reaching past the first key's last query (a document end, or the
+  // ragged end of the sequence) need masking too: a suffix of the wave's tiles.
   if (per_r > 0) {
     const int first_mask = (wv == 0) ? 1 : 0;
-    const int last_qt = qt_first + wv + 4 * (per_r - 1);
-    const int last_mask = ((S % kBQ) != 0 && last_qt == nqt - 1 && per_r > first_mask) ? 1 : 0;
+    const int qt_plain_end = (doc.hi_first + 1) / kBQ;  // tiles below it end by hi_first
+    const int i_mask = max(first_mask, min(per_r, (qt_plain_end - qt_first - wv + 3) / 4));
     for (int r = 0; r < group; ++r) {
       const int t0 = r * per_r;
       if (first_mask) stage(std::true_type{}, t0, 0);
-      for (int i = first_mask; i < per_r - last_mask; ++i) stage(std::false_type{}, t0 + i, i);
-      if (last_mask) stage(std::true_type{}, t0 + per_r - 1, per_r - 1);
+      for (int i = first_mask; i < i_mask; ++i) stage(std::false_type{}, t0 + i, i);
+      for (int i = i_mask; i < per_r; ++i) stage(std::true_type{}, t0 + i, i);
     }
   }
 
@@ -1166,7 +1242,8 @@ hipError_t fwd_launch(const AttnShape& s, const void* q, const void* k, const vo
   ProfScope prof("attn_fwd", stream);
   hipLaunchKernelGGL((fwd_kernel<HD, kFwdBuf, PROQ>), dim3(BH * nqt), dim3(256), 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)out, lse, s.seq_len,
-                     s.num_heads, s.num_kv_heads, kLog2e / sqrtf((float)HD), nqt, xcd, pro);
+                     s.num_heads, s.num_kv_heads, kLog2e / sqrtf((float)HD), nqt, xcd, pro,
+                     s.seg_lo);
   return hipPeekAtLastError();
 }
 
@@ -1190,7 +1267,7 @@ hipError_t bwd_launch(const AttnShape& s, const void* q, const void* k, const vo
     hipLaunchKernelGGL((dq_kernel<HD, kDqBuf, PRO>), dim3(BH * nqt), dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)out,
                        (const bf16*)dout, lse, lse2, delta, (bf16*)dq, S, s.num_heads,
-                       s.num_kv_heads, sl2, scale, nqt, xcd, pq);
+                       s.num_kv_heads, sl2, scale, nqt, xcd, pq, s.seg_lo);
   }
   hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess) return e;
@@ -1200,13 +1277,15 @@ hipError_t bwd_launch(const AttnShape& s, const void* q, const void* k, const vo
     hipLaunchKernelGGL((dkdv_shared_kernel<HD, kDkdvSharedBuf, PRO>), dim3(BKV * nkt),
                        dim3(256), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
                        (const bf16*)dout, (const float*)lse2, (const float*)delta, (bf16*)dk,
-                       (bf16*)dv, S, s.num_heads, s.num_kv_heads, sl2, scale, nkt, xcd, pk);
+                       (bf16*)dv, S, s.num_heads, s.num_kv_heads, sl2, scale, nkt, xcd, pk,
+                       s.seg_hi);
   } else {
     const int nkt = (S + 31) / 32;
     hipLaunchKernelGGL((dkdv_private_kernel<HD, kDkdvPrivateBuf, PRO>), dim3(BKV * nkt),
                        dim3(256), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
                        (const bf16*)dout, (const float*)lse2, (const float*)delta, (bf16*)dk,
-                       (bf16*)dv, S, s.num_heads, s.num_kv_heads, sl2, scale, nkt, xcd, pk);
+                       (bf16*)dv, S, s.num_heads, s.num_kv_heads, sl2, scale, nkt, xcd, pk,
+                       s.seg_hi);
   }
   return hipPeekAtLastError();
 }

@@ -52,6 +52,69 @@ hipError_t launch_rope_cache(float* cos_tab, float* sin_tab, int seq_len, int he
   return hipPeekAtLastError();
 }
 
+// The same table for explicit per-row positions (tokens of packed documents, whose
+// positions restart in every document): thread f of a row group owns one frequency.
+__global__ __launch_bounds__(256) void rope_cache_at_kernel(float* __restrict__ cos_tab,
+                                                            float* __restrict__ sin_tab,
+                                                            const int* __restrict__ positions,
+                                                            int rows, int head_dim,
+                                                            double theta) {
+  const int half = head_dim / 2;
+  const int f = threadIdx.x % half, lanes = 256 / half;
+  const double inv_freq = pow(theta, -2.0 * (double)f / (double)head_dim);
+  const int r0 = blockIdx.x * 4 * lanes + (int)threadIdx.x / half;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = r0 + k * lanes;
+    if (r < rows) {
+      double sv, cv;
+      sincos((double)positions[r] * inv_freq, &sv, &cv);
+      cos_tab[(size_t)r * half + f] = (float)cv;
+      sin_tab[(size_t)r * half + f] = (float)sv;
+    }
+  }
+}
+
+hipError_t launch_rope_cache_at(float* cos_tab, float* sin_tab, const int* positions, int rows,
+                                int head_dim, double theta, hipStream_t stream) {
+  const int per_block = 4 * (256 / (head_dim / 2));
+  ProfScope prof("rope_cache", stream);
+  hipLaunchKernelGGL(rope_cache_at_kernel, dim3((rows + per_block - 1) / per_block), dim3(256),
+                     0, stream, cos_tab, sin_tab, positions, rows, head_dim, theta);
+  return hipPeekAtLastError();
+}
+
+// Row r of a sequence of packed documents (offsets cu_seqlens[0] = 0 < ... <
+// cu_seqlens[ndocs] = seq_len): its document d is the last one with cu_seqlens[d] <= r
+// (binary search); seg_lo = cu_seqlens[d], seg_hi = cu_seqlens[d + 1] - 1, position =
+// r - seg_lo.  Results are clamped into [0, seq_len) whatever the offsets hold.
+__global__ __launch_bounds__(256) void segments_kernel(const int* __restrict__ cu, int ndocs,
+                                                       int seq_len, int* __restrict__ seg_lo,
+                                                       int* __restrict__ seg_hi,
+                                                       int* __restrict__ positions) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= seq_len) return;
+  int lo = 0, hi = ndocs - 1;  // invariant: cu[lo] <= r (cu[0] = 0), answer in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (cu[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  const int a = min(max(cu[lo], 0), r);
+  const int b = min(max(cu[lo + 1] - 1, r), seq_len - 1);
+  seg_lo[r] = a;
+  seg_hi[r] = b;
+  if (positions != nullptr) positions[r] = r - a;
+}
+
+hipError_t launch_segments(const int* cu_seqlens, int ndocs, int seq_len, int* seg_lo,
+                           int* seg_hi, int* positions, hipStream_t stream) {
+  ProfScope prof("segments", stream);
+  hipLaunchKernelGGL(segments_kernel, dim3((seq_len + 255) / 256), dim3(256), 0, stream,
+                     cu_seqlens, ndocs, seq_len, seg_lo, seg_hi, positions);
+  return hipPeekAtLastError();
+}
+
 // Load N contiguous elements (N * sizeof(T) a multiple of 16 bytes) as floats.
 template <typename T, int N>
 __device__ __forceinline__ void load_f32(const T* __restrict__ p, float (&out)[N]) {

@@ -133,7 +133,23 @@ DimsChecked check_dims(const xattn_dims* d) {
   c.rows_q = d->batch * d->num_heads * d->seq_len;
   c.s = {(int)d->batch, (int)d->seq_len, (int)d->num_heads, (int)d->num_kv_heads,
          (int)d->head_dim};
+  if ((d->seg_lo == nullptr) != (d->seg_hi == nullptr))
+    fail(XATTN_ERR_INVALID_ARG, "seg_lo and seg_hi must both be set or both be NULL");
+  if (d->seg_lo != nullptr) {
+    check_ptr(d->seg_lo, "seg_lo");
+    check_ptr(d->seg_hi, "seg_hi");
+    c.s.seg_lo = d->seg_lo;
+    c.s.seg_hi = d->seg_hi;
+  }
   return c;
+}
+
+// Ranges of the document arrays, for the overlap checks (empty without documents).
+Range seg_lo_range(const DimsChecked& c) {
+  return {c.s.seg_lo, c.s.seg_lo ? (size_t)c.s.seq_len * 4 : 0, "seg_lo"};
+}
+Range seg_hi_range(const DimsChecked& c) {
+  return {c.s.seg_hi, c.s.seg_hi ? (size_t)c.s.seq_len * 4 : 0, "seg_hi"};
 }
 
 // The bf16 fast path applies the prologue backward inside its dq / dk stores.
@@ -278,6 +294,46 @@ xattn_status xattn_rope_cache(float* cos_tab, float* sin_tab, int64_t seq_len,
   });
 }
 
+xattn_status xattn_segments(const int32_t* cu_seqlens, int32_t ndocs, int64_t seq_len,
+                            int32_t* seg_lo, int32_t* seg_hi, int32_t* positions, void* stream) {
+  return guarded([&] {
+    check_ptr(cu_seqlens, "cu_seqlens");
+    check_ptr(seg_lo, "seg_lo");
+    check_ptr(seg_hi, "seg_hi");
+    if (positions != nullptr) check_ptr(positions, "positions");
+    check_pos(ndocs, "ndocs");
+    check_pos(seq_len, "seq_len");
+    if (seq_len >= ((int64_t)1 << 31)) fail(XATTN_ERR_INVALID_ARG, "seq_len must stay below 2^31");
+    if (ndocs > seq_len) fail(XATTN_ERR_INVALID_ARG, "ndocs (%d) exceeds seq_len", ndocs);
+    const size_t rb = (size_t)seq_len * 4;
+    check_no_overlap({{seg_lo, rb, "seg_lo"}, {seg_hi, rb, "seg_hi"},
+                      {positions, positions ? rb : 0, "positions"}},
+                     {{cu_seqlens, (size_t)(ndocs + 1) * 4, "cu_seqlens"}});
+    hip_check(xattn::launch_segments(cu_seqlens, ndocs, (int)seq_len, seg_lo, seg_hi, positions,
+                                     (hipStream_t)stream),
+              "segments launch");
+  });
+}
+
+xattn_status xattn_rope_cache_at(float* cos_tab, float* sin_tab, const int32_t* positions,
+                                 int64_t rows, int64_t head_dim, double theta, void* stream) {
+  return guarded([&] {
+    check_ptr(cos_tab, "cos_tab");
+    check_ptr(sin_tab, "sin_tab");
+    check_ptr(positions, "positions");
+    check_pos(rows, "rows");
+    check_head_dim(head_dim);
+    if (!(theta > 0.0) || !std::isfinite(theta))
+      fail(XATTN_ERR_INVALID_ARG, "theta must be positive and finite");
+    const int64_t n = count4(rows, head_dim / 2, 1, 1, "rope table");
+    check_no_overlap({{cos_tab, (size_t)n * 4, "cos_tab"}, {sin_tab, (size_t)n * 4, "sin_tab"}},
+                     {{positions, (size_t)rows * 4, "positions"}});
+    hip_check(xattn::launch_rope_cache_at(cos_tab, sin_tab, positions, (int)rows, (int)head_dim,
+                                          theta, (hipStream_t)stream),
+              "rope_cache_at launch");
+  });
+}
+
 xattn_status xattn_qknorm_rope_fwd(const void* x, const float* gamma, const float* cos_tab,
                                    const float* sin_tab, void* y, float* rstd, int64_t rows,
                                    int64_t seq_len, int64_t head_dim, float eps,
@@ -364,7 +420,8 @@ xattn_status xattn_fwd(const xattn_dims* dims, const void* q, const void* k, con
     check_ptr(lse, "lse");
     const size_t qb = (size_t)c.q_elems * io_size(c.io), kb = (size_t)c.kv_elems * io_size(c.io);
     check_no_overlap({{out, qb, "out"}, {lse, (size_t)c.rows_q * 4, "lse"}},
-                     {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}});
+                     {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, seg_lo_range(c),
+                      seg_hi_range(c)});
     hip_check(xattn::launch_attn_fwd(c.io, c.s, q, k, v, out, lse, (hipStream_t)stream),
               "attention forward launch");
   });
@@ -391,7 +448,7 @@ xattn_status xattn_fwd_qnorm(const xattn_dims* dims, const xattn_fwd_prologue* p
                       {lse, rb, "lse"}},
                      {{pro->xq, qb, "pro->xq"}, {pro->gamma_q, hdb, "pro->gamma_q"},
                       {pro->cos_tab, tb, "pro->cos_tab"}, {pro->sin_tab, tb, "pro->sin_tab"},
-                      {k, kb, "k"}, {v, kb, "v"}});
+                      {k, kb, "k"}, {v, kb, "v"}, seg_lo_range(c), seg_hi_range(c)});
     const hipStream_t st = (hipStream_t)stream;
     if (c.io == xattn::IO_BF16 && xattn::fast_bf16_supported(c.s.head_dim)) {
       xattn::QProFuse pf;
@@ -492,11 +549,12 @@ xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, con
            {pro->xk, kb, "pro->xk"}, {pro->gamma_q, hdb, "pro->gamma_q"},
            {pro->gamma_k, hdb, "pro->gamma_k"}, {pro->rstd_q, (size_t)c.rows_q * 4, "pro->rstd_q"},
            {pro->rstd_k, (size_t)rows_k * 4, "pro->rstd_k"}, {pro->cos_tab, tb, "pro->cos_tab"},
-           {pro->sin_tab, tb, "pro->sin_tab"}});
+           {pro->sin_tab, tb, "pro->sin_tab"}, seg_lo_range(c), seg_hi_range(c)});
     } else {
       check_no_overlap({{dq, qb, "dq"}, {dk, kb, "dk"}, {dv, kb, "dv"}, {workspace, need, "workspace"}},
                        {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {out, qb, "out"},
-                        {lse, (size_t)c.rows_q * 4, "lse"}, {dout, qb, "dout"}});
+                        {lse, (size_t)c.rows_q * 4, "lse"}, {dout, qb, "dout"},
+                        seg_lo_range(c), seg_hi_range(c)});
     }
 
     char* ws = static_cast<char*>(workspace);

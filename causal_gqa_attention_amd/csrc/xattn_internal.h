@@ -14,6 +14,12 @@ enum IoType { IO_F32 = 0, IO_BF16 = 1 };
 // ---- prologue ------------------------------------------------------------------------
 hipError_t launch_rope_cache(float* cos_tab, float* sin_tab, int seq_len, int head_dim,
                              double theta, hipStream_t stream);
+// Table rows at explicit positions: row r holds the angles of position positions[r].
+hipError_t launch_rope_cache_at(float* cos_tab, float* sin_tab, const int* positions, int rows,
+                                int head_dim, double theta, hipStream_t stream);
+// Per-row document bounds and positions from cu_seqlens ([ndocs + 1] document offsets).
+hipError_t launch_segments(const int* cu_seqlens, int ndocs, int seq_len, int* seg_lo,
+                           int* seg_hi, int* positions, hipStream_t stream);
 
 hipError_t launch_qknorm_rope_fwd(IoType io, int head_dim, const void* x, const float* gamma,
                                   const float* cos_tab, const float* sin_tab, void* y,
@@ -50,6 +56,10 @@ hipError_t launch_dgamma_reduce_qk(int head_dim, const float* partials_q, int np
 // ---- attention -----------------------------------------------------------------------
 struct AttnShape {
   int batch, seq_len, num_heads, num_kv_heads, head_dim;
+  // block-causal mask of packed documents: [seq_len] first / last row of each row's
+  // document (both null: plain causal attention)
+  const int* seg_lo = nullptr;
+  const int* seg_hi = nullptr;
 };
 
 hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const void* k,

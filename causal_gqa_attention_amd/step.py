@@ -10,15 +10,19 @@ from __future__ import annotations
 
 import torch
 
-from . import (Dims, make_dims, xattn_bwd, xattn_bwd_workspace_bytes, xattn_fwd_qnorm,
-               xattn_qknorm_rope_fwd, xattn_rope_cache)
+from . import (Dims, make_dims, segments, xattn_bwd, xattn_bwd_workspace_bytes,
+               xattn_fwd_qnorm, xattn_qknorm_rope_fwd, xattn_rope_cache, xattn_rope_cache_at)
 
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
 class AttentionStep:
+    """doc_lengths: optional document lengths packed along the sequence axis (summing to
+    seq_len, the same packing for every batch row): block-causal mask and RoPE positions
+    restarting in every document."""
+
     def __init__(self, batch, seq_len, num_heads, num_kv_heads, head_dim, dtype, eps, theta,
-                 device="cuda"):
+                 device="cuda", doc_lengths=None):
         self.B, self.S, self.H, self.Hkv, self.hd = batch, seq_len, num_heads, num_kv_heads, head_dim
         self.eps, self.theta = float(eps), float(theta)
         self.dtype = _TORCH_DTYPE[dtype] if isinstance(dtype, str) else dtype
@@ -39,7 +43,13 @@ class AttentionStep:
         # backward products (w.r.t. the raw inputs)
         self.dxq, self.dxk, self.dv = e(qshape), e(kshape), e(kshape)
         self.dgamma_q, self.dgamma_k = e(head_dim, f32), e(head_dim, f32)
-        self.dims: Dims = make_dims(self.yq, num_heads, num_kv_heads)
+        self.seg = None
+        if doc_lengths is not None:
+            if sum(int(n) for n in doc_lengths) != seq_len:
+                raise ValueError("doc_lengths must sum to seq_len")
+            self.seg = segments(doc_lengths, dev)  # (seg_lo, seg_hi, positions)
+        self.dims: Dims = make_dims(self.yq, num_heads, num_kv_heads,
+                                    None if self.seg is None else self.seg[:2])
         self.workspace = torch.empty(max(16, xattn_bwd_workspace_bytes(self.dims, True)),
                                      dtype=torch.uint8, device=dev)
         self.prologue = dict(xq=self.xq, xk=self.xk, gamma_q=self.gamma_q, gamma_k=self.gamma_k,
@@ -56,7 +66,10 @@ class AttentionStep:
 
     def forward(self, stream=None):
         S, hd = self.S, self.hd
-        xattn_rope_cache(self.cos, self.sin, S, hd, self.theta, stream)
+        if self.seg is None:
+            xattn_rope_cache(self.cos, self.sin, S, hd, self.theta, stream)
+        else:
+            xattn_rope_cache_at(self.cos, self.sin, self.seg[2], S, hd, self.theta, stream)
         xattn_qknorm_rope_fwd(self.xk, self.gamma_k, self.cos, self.sin, self.yk, self.rstd_k,
                               self.B * self.Hkv, S, hd, self.eps, stream)
         xattn_fwd_qnorm(self.dims, self.xq, self.gamma_q, self.cos, self.sin, self.eps, self.yq,

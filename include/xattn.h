@@ -19,7 +19,8 @@
  *          deterministic sum of its group's query-head gradients, with no atomics.
  *   [MINT] (continued) 10.3 (KV cache: append in place, attention of the new token over
  *          every cached key, equal to full-sequence attention), 14.2 item 5 (fused
- *          single-token GPU decode).
+ *          single-token GPU decode), 8.2 (block-causal mask of a flattened batch: no
+ *          attention across samples, causal inside a sample).
  *   [T12]  xtrain "Phase T12: bf16 mixed precision", precision table: bf16 activations
  *          with fp32 accumulation; softmax, norm and RoPE computed in fp32; fp32 master
  *          weights (gamma) and gradients.
@@ -70,6 +71,15 @@ typedef struct {
   int64_t num_kv_heads;  /* Hkv: K/V heads; H % Hkv == 0, group = H / Hkv */
   int64_t head_dim;      /* hd */
   int32_t dtype;         /* xattn_dtype of q, k, v, out, dout, dq, dk, dv */
+  /* Packed documents ([MINT] 8.2, block-causal mask): NULL and NULL for plain causal
+   * attention over each batch row; otherwise device int32 arrays [seq_len] giving, for
+   * every row, the first (seg_lo) and last (seg_hi) row of the document it belongs to,
+   * the same packing for every batch row.  Row i then attends to keys
+   * seg_lo[i] <= j <= i only.  Documents are contiguous (both arrays non-decreasing,
+   * seg_lo[i] <= i <= seg_hi[i]); xattn_segments builds them from document offsets.
+   * Other contents give unspecified values but no access outside the tensors. */
+  const int32_t* seg_lo;
+  const int32_t* seg_hi;
 } xattn_dims;
 
 /* Prologue inputs that let xattn_bwd also run the QK-norm + RoPE backward, so that
@@ -93,6 +103,22 @@ typedef struct {
  * cos_tab, sin_tab: [seq_len, head_dim/2] fp32 outputs. */
 xattn_status xattn_rope_cache(float* cos_tab, float* sin_tab, int64_t seq_len,
                               int64_t head_dim, double theta, void* stream);
+
+/* Packed documents ([MINT] 8.2; 5.4.4: positions restart in every sequence): from the
+ * document offsets cu_seqlens[0] = 0 < cu_seqlens[1] < ... < cu_seqlens[ndocs] = seq_len
+ * (device int32 [ndocs + 1]) writes, for every row r in [0, seq_len), seg_lo[r] and
+ * seg_hi[r] (first and last row of r's document, as xattn_dims takes them) and, when
+ * positions is not NULL, positions[r] = r - seg_lo[r] (its position in its document, for
+ * xattn_rope_cache_at).  Outputs: device int32 [seq_len]. */
+xattn_status xattn_segments(const int32_t* cu_seqlens, int32_t ndocs, int64_t seq_len,
+                            int32_t* seg_lo, int32_t* seg_hi, int32_t* positions, void* stream);
+
+/* RoPE table at explicit positions: row r of cos_tab / sin_tab ([rows, head_dim/2] fp32)
+ * holds the angles of position positions[r] (device int32 [rows]), evaluated like
+ * xattn_rope_cache.  With packed documents, positions from xattn_segments give the
+ * per-row table the prologue calls take (row t of the table for row t of the sequence). */
+xattn_status xattn_rope_cache_at(float* cos_tab, float* sin_tab, const int32_t* positions,
+                                 int64_t rows, int64_t head_dim, double theta, void* stream);
 
 /* Prologue forward ([T9] Decision 1, [MINT] 5.4.1 and 5.5.1), per row x in R^hd of a
  * [rows, seq_len, hd] tensor (rows = B*H for Q or B*Hkv for K), row position t = s:

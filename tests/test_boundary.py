@@ -33,7 +33,7 @@ def lib():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
     assert "gfx950" in X.xattn_version()
@@ -172,6 +172,30 @@ def test_decode_fp32_allows_sixteen_rows(lib):
     assert decode_call(lib, d, ws_bytes=16) == INVALID and "workspace too small" in last(lib)
     d = ddims(dt=0, q_len=5)
     assert decode_call(lib, d, ws_bytes=16) == UNSUPPORTED and "exceeds 16" in last(lib)
+
+
+def test_document_arrays_validation(lib):
+    d = dims()
+    d.seg_lo = A + 40 * MB
+    assert fwd(lib, d) == INVALID and "both be set" in last(lib)
+    d.seg_hi = A + 40 * MB + 4  # misaligned
+    assert fwd(lib, d) == INVALID and "aligned" in last(lib)
+    d.seg_hi = A + 48 * MB
+    assert fwd(lib, d, out=A + 40 * MB) == INVALID and "overlaps input seg_lo" in last(lib)
+
+
+def test_segments_and_rope_table_at_validation(lib):
+    f = lib.xattn_segments
+    assert f(None, 2, 16, A, A + MB, A + 2 * MB, None) == INVALID and "cu_seqlens" in last(lib)
+    assert f(A, 0, 16, A + MB, A + 2 * MB, None, None) == INVALID and "ndocs" in last(lib)
+    assert f(A, 17, 16, A + MB, A + 2 * MB, None, None) == INVALID and "exceeds" in last(lib)
+    assert f(A, 2, 16, A + MB, A + MB + 32, None, None) == INVALID and "overlap" in last(lib)
+    assert f(A, 2, 16, A, A + MB, None, None) == INVALID and "overlaps input" in last(lib)
+    g = lib.xattn_rope_cache_at
+    assert g(A, A + MB, None, 16, 64, 1e4, None) == INVALID and "positions" in last(lib)
+    assert g(A, A + MB, A + 2 * MB, 16, 64, -1.0, None) == INVALID and "theta" in last(lib)
+    assert g(A, A + MB, A + 2 * MB, 16, 48, 1e4, None) == UNSUPPORTED
+    assert g(A, A + MB, A, 16, 64, 1e4, None) == INVALID and "overlaps input" in last(lib)
 
 
 def test_rope_cache_validation(lib):
