@@ -30,6 +30,11 @@ Sources (titles of the pages and the section each function follows):
   * Mint documentation, section 10.3 (KV cache): a new token computes its own
     Q/K/V, appends K/V to the cache, and its query attends to every cached key;
     the result equals full-sequence attention (decode()).
+  * Mint documentation, sections 5.3.1-5.3.2 (Q = X Wq + bq, K, V alike; output
+    Concat(heads) Wo + bo, weights [d_in, d_out] applied as x @ W), "Phase T5: Tiny
+    Transformer" layout pipeline (projection, reshape [seq, nh, hd], transpose to
+    [nh, seq, hd] per head; merge back to [seq, nh*hd] before Wo) and "Phase T12"
+    (linear GEMMs bf16 in / fp32 accumulate, gradients fp32): the projections below.
   * Mint documentation, section 8.2 (block-causal mask of a flattened batch:
     no attention across sample blocks, causal inside a block; RoPE positions
     numbered inside each sample): `segments` below, documents packed along the
@@ -314,3 +319,59 @@ def decode(xq, xk, v, gamma_q, gamma_k, k_cache, v_cache, cache_len: int, num_he
             out[bh, i] = (e / e.sum()) @ vc[kv, :t + 1]
             lse[bh, i] = m + np.log(e.sum())
     return out, lse, kc, vc
+
+
+# --------------------------------------------------------------------------
+# Projections around attention (Mint documentation 5.3.1-5.3.2; Phase T5 layout pipeline)
+# --------------------------------------------------------------------------
+def split_heads(m, batch: int, seq_len: int, heads: int, head_dim: int):
+    """[B*S, heads*hd] (token rows, head-major columns) -> [B*heads, S, hd]: the reshape to
+    [seq, nh, hd] and the transpose that makes each head's [seq, hd] block contiguous."""
+    m = _f64(m)
+    return np.ascontiguousarray(m.reshape(batch, seq_len, heads, head_dim)
+                                .transpose(0, 2, 1, 3).reshape(batch * heads, seq_len, head_dim))
+
+
+def merge_heads(t, batch: int, seq_len: int, heads: int, head_dim: int):
+    """Inverse of split_heads: [B*heads, S, hd] -> [B*S, heads*hd]."""
+    t = _f64(t)
+    return np.ascontiguousarray(t.reshape(batch, heads, seq_len, head_dim)
+                                .transpose(0, 2, 1, 3).reshape(batch * seq_len, heads * head_dim))
+
+
+def _affine(x, w, b):
+    y = _f64(x) @ _f64(w)
+    return y if b is None else y + _f64(b)[None, :]
+
+
+def qkv_proj(x, wq, wk, wv, bq, bk, bv, batch, seq_len, num_heads, num_kv_heads, head_dim):
+    """x: [B*S, d] token rows; wq: [d, H*hd], wk, wv: [d, Hkv*hd]; biases None or [out].
+    Returns (xq [B*H, S, hd], xk, v [B*Hkv, S, hd]): q = x Wq + bq split into heads, etc."""
+    return (split_heads(_affine(x, wq, bq), batch, seq_len, num_heads, head_dim),
+            split_heads(_affine(x, wk, bk), batch, seq_len, num_kv_heads, head_dim),
+            split_heads(_affine(x, wv, bv), batch, seq_len, num_kv_heads, head_dim))
+
+
+def out_proj(out, wo, bo, batch, seq_len, num_heads, head_dim):
+    """out: [B*H, S, hd]; wo: [H*hd, d]; bo None or [d].  y = merge_heads(out) Wo + bo,
+    [B*S, d]."""
+    return _affine(merge_heads(out, batch, seq_len, num_heads, head_dim), wo, bo)
+
+
+def out_proj_bwd(out, wo, dy, batch, seq_len, num_heads, head_dim):
+    """Chain rule of out_proj.  Returns (dout [B*H, S, hd], dwo [H*hd, d], dbo [d])."""
+    dy = _f64(dy)
+    om = merge_heads(out, batch, seq_len, num_heads, head_dim)
+    dout = split_heads(dy @ _f64(wo).T, batch, seq_len, num_heads, head_dim)
+    return dout, om.T @ dy, dy.sum(axis=0)
+
+
+def qkv_proj_bwd(x, wq, wk, wv, dxq, dxk, dv, batch, seq_len, num_heads, num_kv_heads,
+                 head_dim):
+    """Chain rule of qkv_proj.  Returns dx [B*S, d] and (dwq, dwk, dwv), (dbq, dbk, dbv)."""
+    x = _f64(x)
+    dq = merge_heads(dxq, batch, seq_len, num_heads, head_dim)
+    dk = merge_heads(dxk, batch, seq_len, num_kv_heads, head_dim)
+    dvm = merge_heads(dv, batch, seq_len, num_kv_heads, head_dim)
+    dx = dq @ _f64(wq).T + dk @ _f64(wk).T + dvm @ _f64(wv).T
+    return dx, (x.T @ dq, x.T @ dk, x.T @ dvm), (dq.sum(axis=0), dk.sum(axis=0), dvm.sum(axis=0))

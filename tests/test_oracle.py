@@ -681,3 +681,95 @@ def test_planted_missing_segment_mask_is_caught(monkeypatch):
     monkeypatch.setattr(O, "_probs", lambda q, k, scale, seg_lo=None: real(q, k, scale))
     with pytest.raises(AssertionError):
         test_block_causal_flattened_batch_equals_batched()
+
+
+# --------------------------------------------------------------------------
+# Projections (Mint documentation 5.3.1-5.3.2; Phase T5 layout pipeline)
+# --------------------------------------------------------------------------
+def _proj_inputs(seed, B=2, S=3, H=4, Hkv=2, hd=4, d=6, bias=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B * S, d))
+    wq = rng.standard_normal((d, H * hd))
+    wk = rng.standard_normal((d, Hkv * hd))
+    wv = rng.standard_normal((d, Hkv * hd))
+    wo = rng.standard_normal((H * hd, d))
+    bs = [rng.standard_normal(n) if bias else None for n in (H * hd, Hkv * hd, Hkv * hd, d)]
+    return x, wq, wk, wv, wo, bs
+
+
+def test_projection_scalar_definition_and_head_layout():
+    """q_t = x_t Wq + bq (row vector times matrix), then head h of token (b, s) is columns
+    h*hd .. h*hd + hd - 1 of that row, at [b*H + h, s]; written out with scalar loops."""
+    B, S, H, Hkv, hd, d = 2, 3, 4, 2, 4, 6
+    x, wq, wk, wv, wo, (bq, bk, bv, bo) = _proj_inputs(320)
+    xq, xk, v = O.qkv_proj(x, wq, wk, wv, bq, bk, bv, B, S, H, Hkv, hd)
+    for b in range(B):
+        for s in range(S):
+            for h in range(H):
+                for e in range(hd):
+                    c = h * hd + e
+                    ref = sum(x[b * S + s, i] * wq[i, c] for i in range(d)) + bq[c]
+                    assert abs(xq[b * H + h, s, e] - ref) < 1e-12
+            for h in range(Hkv):
+                for e in range(hd):
+                    c = h * hd + e
+                    ref = sum(x[b * S + s, i] * wv[i, c] for i in range(d)) + bv[c]
+                    assert abs(v[b * Hkv + h, s, e] - ref) < 1e-12
+    out = np.random.default_rng(321).standard_normal((B * H, S, hd))
+    y = O.out_proj(out, wo, bo, B, S, H, hd)
+    for b in range(B):
+        for s in range(S):
+            for j in range(d):
+                ref = sum(out[b * H + h, s, e] * wo[h * hd + e, j]
+                          for h in range(H) for e in range(hd)) + bo[j]
+                assert abs(y[b * S + s, j] - ref) < 1e-12
+    np.testing.assert_array_equal(O.merge_heads(O.split_heads(x @ wq, B, S, H, hd), B, S, H, hd),
+                                  x @ wq)
+
+
+def test_projection_backward_finite_differences():
+    B, S, H, Hkv, hd, d = 1, 3, 2, 1, 4, 5
+    x, wq, wk, wv, wo, (bq, bk, bv, bo) = _proj_inputs(322, B, S, H, Hkv, hd, d)
+    rng = np.random.default_rng(323)
+    gq = rng.standard_normal((B * H, S, hd))
+    gk = rng.standard_normal((B * Hkv, S, hd))
+    gv = rng.standard_normal((B * Hkv, S, hd))
+    dy = rng.standard_normal((B * S, d))
+    out = rng.standard_normal((B * H, S, hd))
+
+    def loss_in(x_, wq_, wk_, wv_, bq_, bk_, bv_):
+        q, k, v = O.qkv_proj(x_, wq_, wk_, wv_, bq_, bk_, bv_, B, S, H, Hkv, hd)
+        return float(np.sum(q * gq) + np.sum(k * gk) + np.sum(v * gv))
+
+    def loss_out(out_, wo_, bo_):
+        return float(np.sum(O.out_proj(out_, wo_, bo_, B, S, H, hd) * dy))
+
+    dx, (dwq, dwk, dwv), (dbq, dbk, dbv) = O.qkv_proj_bwd(x, wq, wk, wv, gq, gk, gv, B, S, H,
+                                                          Hkv, hd)
+    dout, dwo, dbo = O.out_proj_bwd(out, wo, dy, B, S, H, hd)
+
+    def fd(f, args, i):
+        a = args[i]
+        g = np.zeros(a.size)
+        for e in range(a.size):
+            old = a.flat[e]
+            a.flat[e] = old + 1e-6
+            up = f(*args)
+            a.flat[e] = old - 1e-6
+            dn = f(*args)
+            a.flat[e] = old
+            g[e] = (up - dn) / 2e-6
+        return g.reshape(a.shape)
+
+    ins = [x, wq, wk, wv, bq, bk, bv]
+    for i, ref in enumerate([dx, dwq, dwk, dwv, dbq, dbk, dbv]):
+        np.testing.assert_allclose(fd(loss_in, ins, i), ref, rtol=1e-6, atol=1e-6)
+    outs = [out, wo, bo]
+    for i, ref in enumerate([dout, dwo, dbo]):
+        np.testing.assert_allclose(fd(loss_out, outs, i), ref, rtol=1e-6, atol=1e-6)
+
+
+def test_projection_without_bias_is_plain_product():
+    x, wq, wk, wv, wo, _ = _proj_inputs(324, bias=False)
+    q, _, _ = O.qkv_proj(x, wq, wk, wv, None, None, None, 2, 3, 4, 2, 4)
+    np.testing.assert_array_equal(O.merge_heads(q, 2, 3, 4, 4), x @ wq)
