@@ -52,6 +52,10 @@ def parse():
     p.add_argument("--docs", type=str, default=None,
                    help="comma-separated document lengths packed along the sequence "
                         "(block-causal mask); must sum to the workload's seq_len")
+    p.add_argument("--proj", action="store_true",
+                   help="measure the projections around attention instead (QKV and output "
+                        "GEMMs, forward and backward)")
+    p.add_argument("--model-dim", type=int, default=4096)
     p.add_argument("--decode", action="store_true",
                    help="measure the KV-cache decode step instead (xattn_decode)")
     p.add_argument("--decode-batch", type=int, default=8)
@@ -158,6 +162,111 @@ def copy_calibration():
         torch.cuda.synchronize()
         log(f"copy {i}: {n} bytes read, {n} bytes written")
     print(json.dumps({"copy_calibration_bytes": n, "dispatches": 5}))
+
+
+PROJ_METRIC = "attention-block projections fwd+bwd TFLOP/s (bf16 GEMMs, fp32 accumulate)"
+
+
+def proj_bench(args):
+    """One projection step = the QKV projection and the output projection, forward and
+    backward (weight and bias gradients included), on the workload's heads with model
+    dimension --model-dim; inputs seeded, synthetic, resident in HBM."""
+    import numpy as np
+    import torch
+
+    import causal_gqa_attention_amd as X
+    import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    B, S, H, Hkv, hd, d = w.batch, w.seq_len, w.num_heads, w.num_kv_heads, w.head_dim, args.model_dim
+    M, nq, nk = B * S, H * hd, Hkv * hd
+    name = f"{w.name}_proj_d{d}"
+    log(f"projection workload {name}: tokens {M}, d={d}, q {nq}, k/v {nk}, {w.dtype}")
+    torch.cuda.set_device(0)
+    g = torch.Generator(device="cpu").manual_seed(77)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    rnd = lambda *shape, scale=1.0: (torch.randn(*shape, generator=g) * scale).to(dt).to("cuda")
+    x = rnd(M, d)
+    wq, wk, wv = rnd(d, nq, scale=d ** -0.5), rnd(d, nk, scale=d ** -0.5), rnd(d, nk, scale=d ** -0.5)
+    wo = rnd(nq, d, scale=nq ** -0.5)
+    bias = [(0.1 * torch.randn(n, generator=g)).to("cuda") for n in (nq, nk, nk, d)]
+    pr = X.Projection(B, S, H, Hkv, hd, wq, wk, wv, wo, *bias)
+    out, dy = rnd(B * H, S, hd), rnd(M, d)
+    gq, gk, gv = rnd(B * H, S, hd), rnd(B * Hkv, S, hd), rnd(B * Hkv, S, hd)
+
+    def step():
+        pr.qkv_fwd(x)
+        pr.out_fwd(out)
+        pr.out_bwd(out, dy)
+        pr.qkv_bwd(x, gq, gk, gv)
+
+    flops = 2 * M * d * (nq + 2 * nk) + 2 * M * nq * d      # forward: QKV, output
+    flops += 2 * (2 * M * d * nq)                             # output backward: dO, dWo
+    flops += 2 * (2 * M * d * (nq + 2 * nk))                  # QKV backward: dx, dW
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"timed {args.steps} projection steps: {ms:.3f} ms/step, {value:.1f} TFLOP/s")
+    X.xattn_profile_start()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = X.xattn_profile_stop()
+    kernels = {n: {"launches_per_step": c / args.steps, "avg_ms": t / max(c, 1),
+                   "ms_per_step": t / args.steps} for n, (c, t) in prof.items()}
+    log("kernels: " + ", ".join(f"{n} {k['avg_ms'] * 1e3:.1f} us x{k['launches_per_step']:.0f}"
+                                for n, k in kernels.items()))
+    k = kernels["proj_gemm"]
+    achieved = flops / (k["ms_per_step"] * 1e-3) / 1e12  # all GEMM flops over all GEMM time
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS[w.dtype],
+                "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS[w.dtype], "traffic": None,
+                "kernel": "proj_gemm (hipBLASLt)", "work_per_launch": flops / k["launches_per_step"],
+                "work_basis": "2*M*N*K of the step's 10 GEMMs, averaged per launch"}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        import os as _os
+        log("timing the CPU oracle on a bounded sample ...")
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            threads = len(_os.sched_getaffinity(0))
+        rows = min(S, 256)  # the first `rows` tokens of batch row 0, every head
+        xs = x[:rows].float().cpu().numpy()
+        wn = [t.float().cpu().numpy() for t in (wq, wk, wv, wo)]
+        bn = [t.cpu().numpy() for t in bias]
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 10.0:
+            q_, k_, v_ = oracle.qkv_proj(xs, *wn[:3], *bn[:3], 1, rows, H, Hkv, hd)
+            oracle.out_proj(q_, wn[3], bn[3], 1, rows, H, hd)
+            oracle.out_proj_bwd(q_, wn[3], xs, 1, rows, H, hd)
+            oracle.qkv_proj_bwd(xs, *wn[:3], q_, k_, v_, 1, rows, H, Hkv, hd)
+            reps += 1
+        dtc = time.perf_counter() - t0
+        cpu = {"value": flops * rows / M * reps / dtc / 1e12, "unit": "TFLOP/s",
+               "cores": int(threads), "kind": "oracle",
+               "sample": f"{reps} x the step on the first {rows} of {M} token rows: float64 "
+                         f"numpy oracle projections fwd + bwd, {dtc:.1f} s"}
+    print(json.dumps({
+        "metric": PROJ_METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": name, "tokens": M, "model_dim": d, "num_heads": H,
+                   "num_kv_heads": Hkv, "head_dim": hd, "io_dtype": w.dtype,
+                   "parallelism": "none (1 GPU)"},
+        "pct_of_peak": 100.0 * value / PEAK_TFLOPS[w.dtype], "roofline": roofline,
+        "cpu_baseline": cpu, "kernels": kernels, "flop_per_step": flops}))
 
 
 DECODE_METRIC = "KV-cache decode step: cache bytes streamed per second (HBM GB/s)"
@@ -306,6 +415,9 @@ def main():
         return
     if args.decode:
         decode_bench(args)
+        return
+    if args.proj:
+        proj_bench(args)
         return
 
     import numpy as np

@@ -24,10 +24,12 @@ __all__ = [
     "xattn_qknorm_rope_bwd", "xattn_fwd", "xattn_fwd_qnorm", "xattn_bwd_workspace_bytes",
     "xattn_bwd",
     "xattn_decode_workspace_bytes", "xattn_decode", "xattn_segments", "xattn_rope_cache_at",
+    "xattn_proj_workspace_bytes", "xattn_qkv_proj_fwd", "xattn_out_proj_fwd",
+    "xattn_out_proj_bwd", "xattn_qkv_proj_bwd",
     "xattn_status_string", "xattn_last_error", "xattn_version", "xattn_profile_start",
     "xattn_profile_stop",
     "rope_cache", "qknorm_rope_fwd", "qknorm_rope_bwd", "attn_fwd", "attn_fwd_qnorm",
-    "attn_bwd", "decode", "segments", "rope_cache_at",
+    "attn_bwd", "decode", "segments", "rope_cache_at", "Projection",
 ]
 
 XATTN_F32 = 0
@@ -70,6 +72,11 @@ class FwdPrologue(ctypes.Structure):
                 ("eps", ctypes.c_float), ("yq", ctypes.c_void_p), ("rstd_q", ctypes.c_void_p)]
 
 
+class Proj(ctypes.Structure):
+    _fields_ = [("model_dim", ctypes.c_int64)] + [
+        (n, ctypes.c_void_p) for n in ("wq", "wk", "wv", "wo", "bq", "bk", "bv", "bo")]
+
+
 class DecodeDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("batch", "num_heads", "num_kv_heads", "head_dim",
                                               "dtype", "q_len", "cache_len", "capacity")]
@@ -105,6 +112,15 @@ def load_library() -> ctypes.CDLL:
         "xattn_bwd_workspace_bytes": (sz, [ctypes.POINTER(Dims), ctypes.c_int]),
         "xattn_bwd": (i32, [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                             ctypes.POINTER(Prologue), vp, sz, vp]),
+        "xattn_proj_workspace_bytes": (sz, [ctypes.POINTER(Dims), i64]),
+        "xattn_qkv_proj_fwd": (i32, [ctypes.POINTER(Dims), ctypes.POINTER(Proj), vp, vp, vp,
+                                     vp, vp, sz, vp]),
+        "xattn_out_proj_fwd": (i32, [ctypes.POINTER(Dims), ctypes.POINTER(Proj), vp, vp, vp,
+                                     sz, vp]),
+        "xattn_out_proj_bwd": (i32, [ctypes.POINTER(Dims), ctypes.POINTER(Proj), vp, vp, vp,
+                                     vp, vp, vp, sz, vp]),
+        "xattn_qkv_proj_bwd": (i32, [ctypes.POINTER(Dims), ctypes.POINTER(Proj), vp, vp, vp,
+                                     vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "xattn_decode_workspace_bytes": (sz, [ctypes.POINTER(DecodeDims)]),
         "xattn_decode": (i32, [ctypes.POINTER(DecodeDims), vp, vp, vp, vp, vp, vp, vp,
                                ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]),
@@ -422,3 +438,69 @@ def decode(xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, eps, k_cache, v_cache,
     xattn_decode(dims, xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, eps, k_cache, v_cache, out,
                  lse, workspace, stream)
     return out, lse
+
+
+class Projection:
+    """The projections around attention for one shape: weights [d_in, d_out] (io dtype),
+    optional fp32 biases; one preallocated workspace.  q/k/v/out tensors use the attention
+    layouts ([B*H, S, hd], [B*Hkv, S, hd]); x, y are token rows [B*S, d]."""
+
+    def __init__(self, batch, seq_len, num_heads, num_kv_heads, head_dim, wq, wk, wv, wo,
+                 bq=None, bk=None, bv=None, bo=None):
+        self.B, self.S, self.H, self.Hkv, self.hd = batch, seq_len, num_heads, num_kv_heads, head_dim
+        self.d = wq.shape[0]
+        self.dt = wq.dtype
+        self.dims = Dims(batch, seq_len, num_heads, num_kv_heads, head_dim, _io(wq, "wq"))
+        self._keep = (wq, wk, wv, wo, bq, bk, bv, bo)
+        f32 = torch.float32
+        self.p = Proj(self.d, _ptr(wq, "wq"), _ptr(wk, "wk", self.dt), _ptr(wv, "wv", self.dt),
+                      _ptr(wo, "wo", self.dt), _ptr(bq, "bq", f32), _ptr(bk, "bk", f32),
+                      _ptr(bv, "bv", f32), _ptr(bo, "bo", f32))
+        n = int(load_library().xattn_proj_workspace_bytes(ctypes.byref(self.dims), self.d))
+        if n == 0:
+            raise XattnError(1, "xattn_proj_workspace_bytes", xattn_last_error())
+        self.ws = _workspace(n, wq.device)
+
+    def _e(self, *shape, dtype=None):
+        return torch.empty(shape, dtype=dtype or self.dt, device=self.ws.device)
+
+    def qkv_fwd(self, x, stream=None):
+        BH, BKV = self.B * self.H, self.B * self.Hkv
+        xq, xk, v = self._e(BH, self.S, self.hd), self._e(BKV, self.S, self.hd), \
+            self._e(BKV, self.S, self.hd)
+        _check(load_library().xattn_qkv_proj_fwd(
+            ctypes.byref(self.dims), ctypes.byref(self.p), _ptr(x, "x", self.dt),
+            _ptr(xq, "xq"), _ptr(xk, "xk"), _ptr(v, "v"), _ptr(self.ws, "ws"),
+            self.ws.numel(), _stream(stream)), "xattn_qkv_proj_fwd")
+        return xq, xk, v
+
+    def out_fwd(self, out, stream=None):
+        y = self._e(self.B * self.S, self.d)
+        _check(load_library().xattn_out_proj_fwd(
+            ctypes.byref(self.dims), ctypes.byref(self.p), _ptr(out, "out", self.dt),
+            _ptr(y, "y"), _ptr(self.ws, "ws"), self.ws.numel(), _stream(stream)),
+            "xattn_out_proj_fwd")
+        return y
+
+    def out_bwd(self, out, dy, with_bias=True, stream=None):
+        dout = self._e(self.B * self.H, self.S, self.hd)
+        dwo = self._e(self.H * self.hd, self.d, dtype=torch.float32)
+        dbo = self._e(self.d, dtype=torch.float32) if with_bias else None
+        _check(load_library().xattn_out_proj_bwd(
+            ctypes.byref(self.dims), ctypes.byref(self.p), _ptr(out, "out", self.dt),
+            _ptr(dy, "dy", self.dt), _ptr(dout, "dout"), _ptr(dwo, "dwo"), _ptr(dbo, "dbo"),
+            _ptr(self.ws, "ws"), self.ws.numel(), _stream(stream)), "xattn_out_proj_bwd")
+        return dout, dwo, dbo
+
+    def qkv_bwd(self, x, dxq, dxk, dv, with_bias=True, stream=None):
+        nq, nk = self.H * self.hd, self.Hkv * self.hd
+        dx = self._e(self.B * self.S, self.d)
+        f32 = torch.float32
+        dw = [self._e(self.d, n, dtype=f32) for n in (nq, nk, nk)]
+        db = [self._e(n, dtype=f32) if with_bias else None for n in (nq, nk, nk)]
+        _check(load_library().xattn_qkv_proj_bwd(
+            ctypes.byref(self.dims), ctypes.byref(self.p), _ptr(x, "x", self.dt),
+            _ptr(dxq, "dxq", self.dt), _ptr(dxk, "dxk", self.dt), _ptr(dv, "dv", self.dt),
+            _ptr(dx, "dx"), *[_ptr(t, "dw") for t in dw], *[_ptr(t, "db") for t in db],
+            _ptr(self.ws, "ws"), self.ws.numel(), _stream(stream)), "xattn_qkv_proj_bwd")
+        return dx, dw, db

@@ -17,8 +17,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libxattn.so")
-SOURCES = ["attn.hip", "attn_bf16.hip", "prologue.hip", "decode.hip", "xattn_api.cpp",
-           "profile.cpp"]
+SOURCES = ["attn.hip", "attn_bf16.hip", "prologue.hip", "decode.hip", "proj.hip",
+           "proj_gemm.cpp", "xattn_api.cpp", "profile.cpp"]
+# The projection GEMMs call hipBLASLt (a library of the ROCm install, found there at run time).
+LINK_LIBS = ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lhipblaslt"]
 # Per-source extra flags.  attn_bf16.hip: MFMA results go to VGPRs (the score tiles are
 # consumed by VALU right away; AGPR results would need a copy per element).
 SOURCE_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
@@ -66,7 +68,8 @@ def build(verbose: bool = False, extra_flags=None) -> str:
             if o.strip():
                 print(o)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[j[0] for j in jobs]])
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[j[0] for j in jobs],
+          *LINK_LIBS])
     os.replace(tmp, LIB)
     return LIB
 

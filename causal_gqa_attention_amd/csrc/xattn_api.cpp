@@ -6,6 +6,7 @@
 // nothing here exits the process.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -173,6 +174,73 @@ size_t bwd_workspace(const DimsChecked& c, bool with_prologue) {
     n += align256((size_t)xattn::qknorm_rope_bwd_blocks(rows_k) * c.s.head_dim * sizeof(float));
   }
   return n;
+}
+
+// ---- projections ------------------------------------------------------------------------
+struct ProjChecked {
+  DimsChecked c;
+  int M, d, nq, nk;  // token rows, model dim, Q and K/V feature widths
+  size_t io;
+};
+
+ProjChecked check_proj(const xattn_dims* dims, int64_t model_dim) {
+  ProjChecked p;
+  p.c = check_dims(dims);
+  check_pos(model_dim, "model_dim");
+  if (model_dim % 8 != 0) fail(XATTN_ERR_INVALID_ARG, "model_dim must be a multiple of 8");
+  const int64_t M = (int64_t)p.c.s.batch * p.c.s.seq_len;
+  const int64_t nq = (int64_t)p.c.s.num_heads * p.c.s.head_dim;
+  const int64_t nk = (int64_t)p.c.s.num_kv_heads * p.c.s.head_dim;
+  count4(M, model_dim, 1, 1, "token rows x model_dim");
+  count4(model_dim, nq, 1, 1, "weights");
+  p.M = (int)M, p.d = (int)model_dim, p.nq = (int)nq, p.nk = (int)nk;
+  p.io = io_size(p.c.io);
+  return p;
+}
+
+// Workspace regions of the projection calls (each call uses a prefix of its own plan;
+// the GEMM library's scratch follows at `gemm`).
+size_t proj_scratch_bytes(const ProjChecked& p) {
+  const size_t M = p.M, f32 = 4, parts = (size_t)xattn::colsum_parts(p.M) * 4;
+  const size_t qkv_fwd = align256(M * p.nq * f32) + 2 * align256(M * p.nk * f32);
+  const size_t out_fwd = align256(M * p.nq * p.io) + align256(M * p.d * f32);
+  const size_t out_bwd = align256(M * p.nq * f32) + align256(M * p.nq * p.io) +
+                         align256(parts * p.d);
+  const size_t qkv_bwd = align256(M * p.nq * p.io) + 2 * align256(M * p.nk * p.io) +
+                         align256(M * p.d * f32) + align256(parts * p.nq) +
+                         2 * align256(parts * p.nk);
+  return std::max(std::max(qkv_fwd, out_fwd), std::max(out_bwd, qkv_bwd));
+}
+
+size_t proj_workspace(const ProjChecked& p) {
+  return proj_scratch_bytes(p) + xattn::kGemmWorkspace;
+}
+
+// Sequential carving of a workspace into 256-byte aligned regions.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t bytes) {
+    T* r = reinterpret_cast<T*>(base + off);
+    off += align256(bytes);
+    return r;
+  }
+};
+
+void gemm_or_fail(const ProjChecked& p, bool ta, bool tb, int M, int N, int K, const void* A,
+                  int lda, const void* B, int ldb, float beta, float* C, int ldc, void* ws,
+                  hipStream_t st) {
+  char err[160] = {0};
+  if (!xattn::gemm_rm(p.c.io, ta, tb, M, N, K, A, lda, B, ldb, beta, C, ldc,
+                      static_cast<char*>(ws) + proj_scratch_bytes(p), xattn::kGemmWorkspace, st,
+                      &err))
+    fail(XATTN_ERR_HIP, "%s", err);
+}
+
+void check_ws(void* ws, size_t have, size_t need) {
+  check_ptr(ws, "workspace");
+  if (have < need) fail(XATTN_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", have, need);
 }
 
 struct DecodeChecked {
@@ -464,6 +532,185 @@ xattn_status xattn_fwd_qnorm(const xattn_dims* dims, const xattn_fwd_prologue* p
               "prologue forward launch");
     hip_check(xattn::launch_attn_fwd(c.io, c.s, pro->yq, k, v, out, lse, st),
               "attention forward launch");
+  });
+}
+
+size_t xattn_proj_workspace_bytes(const xattn_dims* dims, int64_t model_dim) {
+  size_t n = 0;
+  const xattn_status st = guarded([&] { n = proj_workspace(check_proj(dims, model_dim)); });
+  return st == XATTN_OK ? n : 0;
+}
+
+xattn_status xattn_qkv_proj_fwd(const xattn_dims* dims, const xattn_proj* pr, const void* x,
+                                void* xq, void* xk, void* v, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return guarded([&] {
+    if (pr == nullptr) fail(XATTN_ERR_INVALID_ARG, "p is NULL");
+    const ProjChecked p = check_proj(dims, pr->model_dim);
+    for (auto [q, name] : {std::pair<const void*, const char*>{x, "x"}, {pr->wq, "p->wq"},
+                           {pr->wk, "p->wk"}, {pr->wv, "p->wv"}, {xq, "xq"}, {xk, "xk"},
+                           {v, "v"}})
+      check_ptr(q, name);
+    for (auto [q, name] : {std::pair<const void*, const char*>{pr->bq, "p->bq"},
+                           {pr->bk, "p->bk"}, {pr->bv, "p->bv"}})
+      if (q != nullptr) check_ptr(q, name);
+    check_ws(workspace, workspace_bytes, proj_workspace(p));
+    const size_t M = p.M;
+    check_no_overlap({{xq, M * p.nq * p.io, "xq"}, {xk, M * p.nk * p.io, "xk"},
+                      {v, M * p.nk * p.io, "v"}, {workspace, proj_workspace(p), "workspace"}},
+                     {{x, M * p.d * p.io, "x"}, {pr->wq, (size_t)p.d * p.nq * p.io, "p->wq"},
+                      {pr->wk, (size_t)p.d * p.nk * p.io, "p->wk"},
+                      {pr->wv, (size_t)p.d * p.nk * p.io, "p->wv"},
+                      {pr->bq, pr->bq ? (size_t)p.nq * 4 : 0, "p->bq"},
+                      {pr->bk, pr->bk ? (size_t)p.nk * 4 : 0, "p->bk"},
+                      {pr->bv, pr->bv ? (size_t)p.nk * 4 : 0, "p->bv"}});
+    const hipStream_t st = (hipStream_t)stream;
+    Carver w{static_cast<char*>(workspace)};
+    float* cq = w.take<float>(M * p.nq * 4);
+    float* ck = w.take<float>(M * p.nk * 4);
+    float* cv = w.take<float>(M * p.nk * 4);
+    gemm_or_fail(p, false, false, p.M, p.nq, p.d, x, p.d, pr->wq, p.nq, 0.f, cq, p.nq,
+                 workspace, st);
+    gemm_or_fail(p, false, false, p.M, p.nk, p.d, x, p.d, pr->wk, p.nk, 0.f, ck, p.nk,
+                 workspace, st);
+    gemm_or_fail(p, false, false, p.M, p.nk, p.d, x, p.d, pr->wv, p.nk, 0.f, cv, p.nk,
+                 workspace, st);
+    xattn::SplitJobs jobs{{{cq, pr->bq, xq, p.M, p.nq}, {ck, pr->bk, xk, p.M, p.nk},
+                           {cv, pr->bv, v, p.M, p.nk}}, 3};
+    hip_check(xattn::launch_split_heads(p.c.io, jobs, p.c.s.seq_len, p.c.s.head_dim, st),
+              "split_heads launch");
+  });
+}
+
+xattn_status xattn_out_proj_fwd(const xattn_dims* dims, const xattn_proj* pr, const void* out,
+                                void* y, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return guarded([&] {
+    if (pr == nullptr) fail(XATTN_ERR_INVALID_ARG, "p is NULL");
+    const ProjChecked p = check_proj(dims, pr->model_dim);
+    check_ptr(out, "out");
+    check_ptr(pr->wo, "p->wo");
+    check_ptr(y, "y");
+    if (pr->bo != nullptr) check_ptr(pr->bo, "p->bo");
+    check_ws(workspace, workspace_bytes, proj_workspace(p));
+    const size_t M = p.M;
+    check_no_overlap({{y, M * p.d * p.io, "y"}, {workspace, proj_workspace(p), "workspace"}},
+                     {{out, M * p.nq * p.io, "out"},
+                      {pr->wo, (size_t)p.nq * p.d * p.io, "p->wo"},
+                      {pr->bo, pr->bo ? (size_t)p.d * 4 : 0, "p->bo"}});
+    const hipStream_t st = (hipStream_t)stream;
+    Carver w{static_cast<char*>(workspace)};
+    void* om = w.take<char>(M * p.nq * p.io);
+    float* cy = w.take<float>(M * p.d * 4);
+    xattn::MergeJobs mj{{{out, om, p.M, p.nq}}, 1};
+    hip_check(xattn::launch_merge_heads(p.c.io, mj, p.c.s.seq_len, p.c.s.head_dim, st),
+              "merge_heads launch");
+    gemm_or_fail(p, false, false, p.M, p.d, p.nq, om, p.nq, pr->wo, p.d, 0.f, cy, p.d,
+                 workspace, st);
+    hip_check(xattn::launch_round_bias(p.c.io, cy, pr->bo, y, M, p.d, st), "round launch");
+  });
+}
+
+xattn_status xattn_out_proj_bwd(const xattn_dims* dims, const xattn_proj* pr, const void* out,
+                                const void* dy, void* dout, float* dwo, float* dbo,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return guarded([&] {
+    if (pr == nullptr) fail(XATTN_ERR_INVALID_ARG, "p is NULL");
+    const ProjChecked p = check_proj(dims, pr->model_dim);
+    for (auto [q, name] : {std::pair<const void*, const char*>{out, "out"}, {dy, "dy"},
+                           {pr->wo, "p->wo"}, {dout, "dout"}, {dwo, "dwo"}})
+      check_ptr(q, name);
+    if (dbo != nullptr) check_ptr(dbo, "dbo");
+    check_ws(workspace, workspace_bytes, proj_workspace(p));
+    const size_t M = p.M;
+    check_no_overlap({{dout, M * p.nq * p.io, "dout"}, {dwo, (size_t)p.nq * p.d * 4, "dwo"},
+                      {dbo, dbo ? (size_t)p.d * 4 : 0, "dbo"},
+                      {workspace, proj_workspace(p), "workspace"}},
+                     {{out, M * p.nq * p.io, "out"}, {dy, M * p.d * p.io, "dy"},
+                      {pr->wo, (size_t)p.nq * p.d * p.io, "p->wo"}});
+    const hipStream_t st = (hipStream_t)stream;
+    Carver w{static_cast<char*>(workspace)};
+    float* dom = w.take<float>(M * p.nq * 4);
+    void* om = w.take<char>(M * p.nq * p.io);
+    float* part = w.take<float>((size_t)xattn::colsum_parts(p.M) * p.d * 4);
+    // dout = split(dy Wo^T): Wo stored [nq, d] = [N, K]
+    gemm_or_fail(p, false, true, p.M, p.nq, p.d, dy, p.d, pr->wo, p.d, 0.f, dom, p.nq,
+                 workspace, st);
+    xattn::SplitJobs sj{{{dom, nullptr, dout, p.M, p.nq}}, 1};
+    hip_check(xattn::launch_split_heads(p.c.io, sj, p.c.s.seq_len, p.c.s.head_dim, st),
+              "split_heads launch");
+    // dwo = merge(out)^T dy: A stored [M, nq] = [K, M'], B stored [M, d] = [K, N]
+    xattn::MergeJobs mj{{{out, om, p.M, p.nq}}, 1};
+    hip_check(xattn::launch_merge_heads(p.c.io, mj, p.c.s.seq_len, p.c.s.head_dim, st),
+              "merge_heads launch");
+    gemm_or_fail(p, true, false, p.nq, p.d, p.M, om, p.nq, dy, p.d, 0.f, dwo, p.d, workspace,
+                 st);
+    if (dbo != nullptr) {
+      xattn::ColsumJobs cj{{{dy, part, dbo, p.M, p.d}}, 1};
+      hip_check(xattn::launch_colsum(p.c.io, cj, st), "bias gradient launch");
+    }
+  });
+}
+
+xattn_status xattn_qkv_proj_bwd(const xattn_dims* dims, const xattn_proj* pr, const void* x,
+                                const void* dxq, const void* dxk, const void* dv, void* dx,
+                                float* dwq, float* dwk, float* dwv, float* dbq, float* dbk,
+                                float* dbv, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return guarded([&] {
+    if (pr == nullptr) fail(XATTN_ERR_INVALID_ARG, "p is NULL");
+    const ProjChecked p = check_proj(dims, pr->model_dim);
+    for (auto [q, name] : {std::pair<const void*, const char*>{x, "x"}, {dxq, "dxq"},
+                           {dxk, "dxk"}, {dv, "dv"}, {pr->wq, "p->wq"}, {pr->wk, "p->wk"},
+                           {pr->wv, "p->wv"}, {dx, "dx"}, {dwq, "dwq"}, {dwk, "dwk"},
+                           {dwv, "dwv"}})
+      check_ptr(q, name);
+    for (auto [q, name] : {std::pair<const void*, const char*>{dbq, "dbq"}, {dbk, "dbk"},
+                           {dbv, "dbv"}})
+      if (q != nullptr) check_ptr(q, name);
+    check_ws(workspace, workspace_bytes, proj_workspace(p));
+    const size_t M = p.M;
+    check_no_overlap(
+        {{dx, M * p.d * p.io, "dx"}, {dwq, (size_t)p.d * p.nq * 4, "dwq"},
+         {dwk, (size_t)p.d * p.nk * 4, "dwk"}, {dwv, (size_t)p.d * p.nk * 4, "dwv"},
+         {dbq, dbq ? (size_t)p.nq * 4 : 0, "dbq"}, {dbk, dbk ? (size_t)p.nk * 4 : 0, "dbk"},
+         {dbv, dbv ? (size_t)p.nk * 4 : 0, "dbv"}, {workspace, proj_workspace(p), "workspace"}},
+        {{x, M * p.d * p.io, "x"}, {dxq, M * p.nq * p.io, "dxq"}, {dxk, M * p.nk * p.io, "dxk"},
+         {dv, M * p.nk * p.io, "dv"}, {pr->wq, (size_t)p.d * p.nq * p.io, "p->wq"},
+         {pr->wk, (size_t)p.d * p.nk * p.io, "p->wk"},
+         {pr->wv, (size_t)p.d * p.nk * p.io, "p->wv"}});
+    const hipStream_t st = (hipStream_t)stream;
+    Carver w{static_cast<char*>(workspace)};
+    void* gq = w.take<char>(M * p.nq * p.io);
+    void* gk = w.take<char>(M * p.nk * p.io);
+    void* gv = w.take<char>(M * p.nk * p.io);
+    float* cdx = w.take<float>(M * p.d * 4);
+    float* pq = w.take<float>((size_t)xattn::colsum_parts(p.M) * p.nq * 4);
+    float* pk = w.take<float>((size_t)xattn::colsum_parts(p.M) * p.nk * 4);
+    float* pv = w.take<float>((size_t)xattn::colsum_parts(p.M) * p.nk * 4);
+    xattn::MergeJobs mj{{{dxq, gq, p.M, p.nq}, {dxk, gk, p.M, p.nk}, {dv, gv, p.M, p.nk}}, 3};
+    hip_check(xattn::launch_merge_heads(p.c.io, mj, p.c.s.seq_len, p.c.s.head_dim, st),
+              "merge_heads launch");
+    // dx = gq Wq^T + gk Wk^T + gv Wv^T (W stored [d, n] = [N, K]), summed in fp32
+    gemm_or_fail(p, false, true, p.M, p.d, p.nq, gq, p.nq, pr->wq, p.nq, 0.f, cdx, p.d,
+                 workspace, st);
+    gemm_or_fail(p, false, true, p.M, p.d, p.nk, gk, p.nk, pr->wk, p.nk, 1.f, cdx, p.d,
+                 workspace, st);
+    gemm_or_fail(p, false, true, p.M, p.d, p.nk, gv, p.nk, pr->wv, p.nk, 1.f, cdx, p.d,
+                 workspace, st);
+    hip_check(xattn::launch_round_bias(p.c.io, cdx, nullptr, dx, M, p.d, st), "round launch");
+    // dW = x^T g: A stored [M, d] = [K, M'], B stored [M, n] = [K, N]
+    gemm_or_fail(p, true, false, p.d, p.nq, p.M, x, p.d, gq, p.nq, 0.f, dwq, p.nq, workspace,
+                 st);
+    gemm_or_fail(p, true, false, p.d, p.nk, p.M, x, p.d, gk, p.nk, 0.f, dwk, p.nk, workspace,
+                 st);
+    gemm_or_fail(p, true, false, p.d, p.nk, p.M, x, p.d, gv, p.nk, 0.f, dwv, p.nk, workspace,
+                 st);
+    xattn::ColsumJobs cj{};
+    if (dbq != nullptr) cj.job[cj.n++] = {gq, pq, dbq, p.M, p.nq};
+    if (dbk != nullptr) cj.job[cj.n++] = {gk, pk, dbk, p.M, p.nk};
+    if (dbv != nullptr) cj.job[cj.n++] = {gv, pv, dbv, p.M, p.nk};
+    if (cj.n > 0) hip_check(xattn::launch_colsum(p.c.io, cj, st), "bias gradient launch");
   });
 }
 

@@ -131,6 +131,58 @@ DecodePlan decode_plan(const DecodeShape& d, int cache_rows);
 hipError_t launch_decode(IoType io, const DecodeShape& d, const DecodeBufs& bufs,
                          hipStream_t stream);
 
+// ---- projections (proj.hip, proj.cpp) -------------------------------------------------
+// Head split of fp32 token rows [rows, cols] (+ bias) into a head-major io-dtype tensor.
+struct SplitJob {
+  const float* src;
+  const float* bias;  // [cols] or null
+  void* dst;
+  int rows, cols;
+};
+struct SplitJobs {
+  SplitJob job[3];
+  int n;
+};
+// Head merge of a head-major io-dtype tensor into token rows [rows, cols].
+struct MergeJob {
+  const void* src;
+  void* dst;
+  int rows, cols;
+};
+struct MergeJobs {
+  MergeJob job[3];
+  int n;
+};
+// Column sums of an io-dtype [rows, cols] matrix (bias gradients), in a fixed order.
+constexpr int kColsumRows = 128;  // rows per partial sum
+inline int colsum_parts(int rows) { return (rows + kColsumRows - 1) / kColsumRows; }
+struct ColsumJob {
+  const void* src;
+  float* partial;  // [colsum_parts(rows)][cols] scratch
+  float* out;      // [cols]
+  int rows, cols;
+};
+struct ColsumJobs {
+  ColsumJob job[3];
+  int n;
+};
+hipError_t launch_split_heads(IoType io, const SplitJobs& jobs, int S, int hd,
+                              hipStream_t stream);
+hipError_t launch_merge_heads(IoType io, const MergeJobs& jobs, int S, int hd,
+                              hipStream_t stream);
+hipError_t launch_round_bias(IoType io, const float* src, const float* bias, void* dst,
+                             size_t rows, int cols, hipStream_t stream);
+hipError_t launch_colsum(IoType io, const ColsumJobs& jobs, hipStream_t stream);
+
+// Row-major C[M, N] (fp32) = op(A) op(B) + beta * C, op(A) [M, K], op(B) [K, N]; A stored
+// [M, K] (lda) or, with ta, [K, M]; B stored [K, N] (ldb) or, with tb, [N, K].  A and B in
+// the io dtype; fp32 accumulate.  A library GEMM (hipBLASLt); `ws` is its workspace.
+// Returns false (and a message in *err) when no algorithm supports the call.
+constexpr size_t kGemmWorkspace = (size_t)64 << 20;
+bool gemm_rm(IoType io, bool ta, bool tb, int M, int N, int K, const void* A, int lda,
+             const void* B, int ldb, float beta, float* C, int ldc, void* ws, size_t ws_bytes,
+             hipStream_t stream, char (*err)[160]);
+
 // ---- opt-in per-kernel event timing (see xattn_profile_start) ------------------------
 // Construct around each kernel launch: records a start event now and a stop event at
 // scope exit on `stream`, when timing is enabled.

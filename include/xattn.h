@@ -203,6 +203,59 @@ xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, con
                        void* dk, void* dv, const xattn_prologue* pro, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* ---- Projections around attention --------------------------------------------------------
+ * [MINT] 5.3.1-5.3.2: Q = X Wq + bq, K = X Wk + bk, V = X Wv + bv, output
+ * Concat(heads) Wo + bo, with weights [d_in, d_out] applied as x @ W; [T5] layout pipeline:
+ * the projections' token rows are split into heads ([B*H, S, hd], [B*Hkv, S, hd], what the
+ * prologue and attention take) and the attention output is merged back into token rows
+ * before Wo; [T12]: GEMMs take the io dtype with fp32 accumulation, the weight and bias
+ * gradients are fp32.  Token rows: x, y, dx [B*S, d], row b*S + s.  The GEMMs are library
+ * calls (hipBLASLt); splits, merges, bias and rounding run in the library's own kernels.
+ * Requires d % 8 == 0.  The segment fields of dims are ignored. */
+typedef struct {
+  int64_t model_dim;  /* d */
+  const void* wq;     /* [d, H*hd] io dtype */
+  const void* wk;     /* [d, Hkv*hd] io dtype */
+  const void* wv;     /* [d, Hkv*hd] io dtype */
+  const void* wo;     /* [H*hd, d] io dtype */
+  const float* bq;    /* NULL (no bias) or fp32 [H*hd] */
+  const float* bk;    /* NULL or fp32 [Hkv*hd] */
+  const float* bv;    /* NULL or fp32 [Hkv*hd] */
+  const float* bo;    /* NULL or fp32 [d] */
+} xattn_proj;
+
+/* Bytes of workspace each projection call below needs (one size serves all four). */
+size_t xattn_proj_workspace_bytes(const xattn_dims* dims, int64_t model_dim);
+
+/* xq, xk, v (head layouts, io dtype) = split_heads(x Wq + bq), ... (only wq, wk, wv and
+ * their biases are read). */
+xattn_status xattn_qkv_proj_fwd(const xattn_dims* dims, const xattn_proj* p, const void* x,
+                                void* xq, void* xk, void* v, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* y [B*S, d] = merge_heads(out) Wo + bo; out: [B*H, S, hd]. */
+xattn_status xattn_out_proj_fwd(const xattn_dims* dims, const xattn_proj* p, const void* out,
+                                void* y, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Chain rule of xattn_out_proj_fwd for the upstream gradient dy [B*S, d]:
+ *   dout = split_heads(dy Wo^T) [B*H, S, hd] (io dtype); dwo = merge_heads(out)^T dy
+ *   [H*hd, d] fp32; dbo = column sums of dy [d] fp32 (NULL: not computed). */
+xattn_status xattn_out_proj_bwd(const xattn_dims* dims, const xattn_proj* p, const void* out,
+                                const void* dy, void* dout, float* dwo, float* dbo,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Chain rule of xattn_qkv_proj_fwd for the gradients dxq, dxk, dv (head layouts):
+ *   dx = merge(dxq) Wq^T + merge(dxk) Wk^T + merge(dv) Wv^T [B*S, d] (io dtype, summed in
+ *   fp32 before one rounding); dwq = x^T merge(dxq) [d, H*hd] fp32, dwk, dwv likewise;
+ *   dbq, dbk, dbv = column sums of the merged gradients (fp32, each NULL: not computed).
+ *   Column sums are taken in a fixed order (bitwise reproducible). */
+xattn_status xattn_qkv_proj_bwd(const xattn_dims* dims, const xattn_proj* p, const void* x,
+                                const void* dxq, const void* dxk, const void* dv, void* dx,
+                                float* dwq, float* dwk, float* dwv, float* dbq, float* dbk,
+                                float* dbv, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* ---- KV-cache decode ---------------------------------------------------------------------
  * Shape of a decode call: each of `batch` sequences has cache_len tokens cached and adds
  * q_len new ones at positions cache_len .. cache_len + q_len - 1. */

@@ -33,7 +33,7 @@ def lib():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(lib, n), n
     assert "gfx950" in X.xattn_version()
@@ -196,6 +196,30 @@ def test_segments_and_rope_table_at_validation(lib):
     assert g(A, A + MB, A + 2 * MB, 16, 64, -1.0, None) == INVALID and "theta" in last(lib)
     assert g(A, A + MB, A + 2 * MB, 16, 48, 1e4, None) == UNSUPPORTED
     assert g(A, A + MB, A, 16, 64, 1e4, None) == INVALID and "overlaps input" in last(lib)
+
+
+def test_projection_validation(lib):
+    d = dims()  # B=2, S=64, H=8, Hkv=2, hd=64, bf16
+    ws = lib.xattn_proj_workspace_bytes(ctypes.byref(d), 128)
+    assert ws > 0
+    assert lib.xattn_proj_workspace_bytes(ctypes.byref(d), 100) == 0  # d % 8 != 0
+    assert "multiple of 8" in last(lib)
+    p = X.Proj(128, A, A + MB, A + 2 * MB, A + 3 * MB, None, None, None, None)
+    f = lib.xattn_qkv_proj_fwd
+    io = [A + 4 * MB, A + 8 * MB, A + 12 * MB, A + 16 * MB]  # x, xq, xk, v
+    assert f(ctypes.byref(d), None, *io, A + 32 * MB, ws, None) == INVALID and "p is NULL" in last(lib)
+    assert f(ctypes.byref(d), ctypes.byref(p), *io, A + 32 * MB, ws - 1, None) == INVALID
+    assert "workspace too small" in last(lib)
+    assert f(ctypes.byref(d), ctypes.byref(p), None, *io[1:], A + 32 * MB, ws, None) == INVALID
+    assert f(ctypes.byref(d), ctypes.byref(p), io[0], A, io[2], io[3], A + 32 * MB, ws,
+             None) == INVALID and "overlaps input" in last(lib)
+    p.bq = A + 3 * MB + 2
+    assert f(ctypes.byref(d), ctypes.byref(p), *io, A + 32 * MB, ws, None) == INVALID
+    assert "aligned" in last(lib)
+    g = lib.xattn_out_proj_bwd
+    p.bq = None
+    assert g(ctypes.byref(d), ctypes.byref(p), A + 4 * MB, A + 8 * MB, A + 12 * MB, None, None,
+             A + 32 * MB, ws, None) == INVALID and "dwo is NULL" in last(lib)
 
 
 def test_rope_cache_validation(lib):
