@@ -156,12 +156,13 @@ __device__ __forceinline__ void stage_wait_private() {
 template <int PER>
 __device__ __forceinline__ void dma16_rows(void* dst, const char* gbase, uint32_t nbytes,
                                            const uint32_t (&voff)[PER]) {
-  const uint32_t m0v = (uint32_t)(uintptr_t)(lds_void_t*)dst;
+  // every operand is wave-uniform; readfirstlane keeps them in scalar registers
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)dst);
   const uint64_t ga = (uint64_t)(uintptr_t)gbase;
   i32x4 rsrc;  // base, stride 0, nbytes, raw 32-bit format
-  rsrc[0] = (int)(uint32_t)ga;
-  rsrc[1] = (int)((uint32_t)(ga >> 32) & 0xFFFFu);
-  rsrc[2] = (int)nbytes;
+  rsrc[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)ga);
+  rsrc[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(ga >> 32) & 0xFFFFu));
+  rsrc[2] = __builtin_amdgcn_readfirstlane((int)nbytes);
   rsrc[3] = 0x00020000;
   uint32_t saved;
 #define XATTN_LD(i) "buffer_load_dwordx4 %[o" #i "], %[r], 0 offen lds\n\t"
@@ -1227,6 +1228,246 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_private_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// dk/dv, software-pipelined variant (head_dim 128, one wave per SIMD).  A workgroup owns
+// 64 keys of one KV head: wave w holds keys k0 + 32 (w & 1) .. + 31 in registers and walks
+// the query tiles of stream w >> 1 (tiles k0/32 + s, + s + 2, ..., every query head of the
+// group in turn); the two waves of a stream share each staged tile, so four tiles per
+// stream stay resident.  Iteration t issues the S and dP products of tile t + 1 while the
+// vector unit forms P and dS of tile t, then the dV and dK products of tile t: the matrix
+// pipe always has independent work queued while the softmax arithmetic runs.  The two
+// streams' partial dK / dV of the same keys are added in stream order at the end.
+// ---------------------------------------------------------------------------------------
+constexpr int kPipeBuf = 4;  // staged tiles per stream
+
+template <int HD>
+__device__ __forceinline__ void rows_of(bf16x8 (&x)[HD / 16], const char* base, uint32_t al) {
+#pragma unroll
+  for (int c = 0; c < HD / 16; ++c) x[c] = lds_a<HD>(base, al, c);
+}
+template <int HD>
+__device__ __forceinline__ void tr_of(bf16x8 (&x)[2][HD / 32], const char* base, uint32_t tl) {
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt) x[c2][dt] = lds_t<HD>(base, tl, c2, dt);
+}
+
+template <int HD, bool PRO>
+__global__ __launch_bounds__(256, 1) void dkdv_pipe_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse2,
+    const float* __restrict__ delta, bf16* __restrict__ dk, bf16* __restrict__ dv, int S, int H,
+    int Hkv, float scale_log2, float scale, int nkt, int xcd, ProBwd pro,
+    const int* __restrict__ seg_hi) {
+  constexpr int NB = kPipeBuf;
+  constexpr int ROWB = 2 * HD;
+  constexpr int TILEB = kBQ * ROWB;
+  constexpr int STREAMB = NB * 2 * TILEB;  // one stream's staging bytes
+  using D = Dma<HD, kBQ, 2>;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STREAMB];
+  __shared__ __attribute__((aligned(16))) float stats[2][NB][64];
+  const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = wv & 1, st = wv >> 1;  // key half, query stream
+  int kvbh, kt;
+  map_kvblock(blockIdx.x, gridDim.x / nkt, xcd != 0, kvbh, kt);
+  const int b = kvbh / Hkv, kvh = kvbh - b * Hkv, group = H / Hkv;
+  const int k0 = kt * 64, kw0 = k0 + 32 * kb, key = kw0 + c32;
+  const uint32_t al = Lay<HD>::a_lane(lane), tl = Lay<HD>::t_lane(lane);
+  D dma;
+  dma.init(kb, lane);
+  char* mine = lds + st * STREAMB;
+  float(*sst)[64] = stats[st];
+  bf16x8 kf[HD / 16], vf[HD / 16];  // K and V rows of the lane's key
+  load_frag<HD>(kf, k + (size_t)kvbh * S * HD, key, S, lane);
+  load_frag<HD>(vf, v + (size_t)kvbh * S * HD, key, S, lane);
+  f32x16 dkt[HD / 32], dvt[HD / 32];
+#pragma unroll
+  for (int dt = 0; dt < HD / 32; ++dt) dkt[dt] = dvt[dt] = zero16();
+
+  const KDoc doc = k_doc(seg_hi, k0, min(k0 + 63, S - 1), key, S);
+  const int qt_first = k0 / kBQ;
+  // query tiles up to the last query of the workgroup's last key, split over the streams;
+  // both streams run the same count (a stream's extra tile is past every visible query)
+  const int qt_end = min((S + kBQ - 1) / kBQ, doc.hi_last / kBQ + 1);
+  const int per_r = max(0, (qt_end - qt_first + 1) / 2);
+  const int nst = group * per_r;
+  int next_r = 0, next_i = 0, issued = 0;
+  const size_t bh0 = (size_t)(b * H + kvh * group);
+  // Issues the next tile of the stream.  Past the last tile it issues an empty copy (no
+  // bytes read; the free buffer it lands in is never read again), so the loop body needs
+  // no branch.
+  auto issue_next = [&]() {
+    const int buf = issued % NB;
+    const bool real = issued < nst;
+    const size_t bh = bh0 + (real ? next_r : 0);
+    // a stream's extra tile may start past the sequence: nothing is read for it either
+    const int g0 = (qt_first + st + 2 * next_i) * kBQ, nv = real ? max(S - g0, 0) : 0;
+    dma.issue(mine + (2 * buf) * TILEB, reinterpret_cast<const char*>(q + (bh * S + g0) * HD),
+              kb, nv);
+    dma.issue(mine + (2 * buf + 1) * TILEB,
+              reinterpret_cast<const char*>(dout + (bh * S + g0) * HD), kb, nv);
+    dma_rowstats<2>(sst[buf], lse2 + bh * S, delta + bh * S, g0, S, kb, lane);
+    if (++next_i == per_r) {
+      next_i = 0;
+      ++next_r;
+    }
+    ++issued;
+  };
+
+  constexpr int NL = 2 * D::PER + 1;  // loads per wave per tile
+  // prologue: tiles 0..3 in flight; S and dP of tile 0; row operands of tile 1
+  bf16x8 qa[HD / 16], da[HD / 16];
+  f32x16 s_cur = zero16(), p_cur = zero16();
+  if (nst > 0) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) issue_next();
+    wait_vm<2 * NL>();  // tiles 0 and 1
+    __builtin_amdgcn_s_barrier();
+    lds_acquire();
+    rows_of<HD>(qa, mine, al);
+    rows_of<HD>(da, mine + TILEB, al);
+#pragma unroll
+    for (int c = 0; c < HD / 16; ++c) {
+      s_cur = mfma_bf16(qa[c], kf[c], s_cur);
+      p_cur = mfma_bf16(da[c], vf[c], p_cur);
+    }
+    rows_of<HD>(qa, mine + 2 * TILEB, al);
+    rows_of<HD>(da, mine + 3 * TILEB, al);
+  }
+
+  // Iteration t: P / dS of tile t under the S / dP products of tile t + 1, then tile t's
+  // dV / dK products.  Tile t's buffer is free after the barrier (its last reads, the
+  // transposed operands, are complete by then) and receives tile t + 4.
+  auto iter = [&](auto mask_tag, int t, int i) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const char* cur = mine + (2 * (t % NB)) * TILEB;
+    const float* stt = sst[t % NB];
+    const int q0 = (qt_first + st + 2 * i) * kBQ;
+    f32x4 l2[4], dd[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      l2[g] = *reinterpret_cast<const f32x4*>(stt + 8 * g + 4 * h);
+      dd[g] = *reinterpret_cast<const f32x4*>(stt + 32 + 8 * g + 4 * h);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s_nxt = zero16(), p_nxt = zero16();
+#pragma unroll
+    for (int c = 0; c < HD / 16; ++c) {
+      s_nxt = mfma_bf16(qa[c], kf[c], s_nxt);
+      p_nxt = mfma_bf16(da[c], vf[c], p_nxt);
+    }
+    float pv[16], dsv[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float p = fast_exp2(s_cur[4 * g + j] * scale_log2 - l2[g][j]);
+        if constexpr (MASK) {
+          const int qi = q0 + 8 * g + 4 * h + j;
+          if (qi < key || qi >= S || qi > doc.hi_key) p = 0.f;
+        }
+        pv[4 * g + j] = p;
+        dsv[4 * g + j] = p * (p_cur[4 * g + j] - dd[g][j]);
+      }
+    bf16x8 pb[2], db[2];
+    pack16(pb, pv);
+    pack16(db, dsv);
+    bf16x8 ta[2][HD / 32], tq[2][HD / 32];  // transposed operands of tile t
+    tr_of<HD>(ta, cur + TILEB, tl);
+    tr_of<HD>(tq, cur, tl);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA,
+      __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);  // VALU / transcendental,
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+    }
+    // P and dS are formed here, under the matrix products, not after the barrier
+    asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(db[0]), "v"(db[1]));
+    __builtin_amdgcn_sched_barrier(0);
+    // tile t + 2 has landed for every wave (t + 3 may still be in flight)
+    wait_vm<NL>();
+    __builtin_amdgcn_s_barrier();
+    lds_acquire();
+    issue_next();  // tile t + 4 into tile t's buffer
+    const char* nx2 = mine + (2 * ((t + 2) % NB)) * TILEB;
+    rows_of<HD>(qa, nx2, al);
+    rows_of<HD>(da, nx2 + TILEB, al);
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int dt = 0; dt < HD / 32; ++dt) {
+        dvt[dt] = mfma_bf16(ta[c2][dt], pb[c2], dvt[dt]);
+        dkt[dt] = mfma_bf16(tq[c2][dt], db[c2], dkt[dt]);
+      }
+    s_cur = s_nxt;
+    p_cur = p_nxt;
+  };
+  // Per query head: tile 0 of each stream meets the diagonal of one of the key halves;
+  // tiles reaching past the first key's last query (a document end, the ragged end of the
+  // sequence, a stream's extra tile) need masking too: a suffix of the stream's tiles.
+  if (per_r > 0) {
+    const int qt_plain_end = (doc.hi_first + 1) / kBQ;  // tiles below it end by hi_first
+    const int i_mask = max(1, min(per_r, (qt_plain_end - qt_first - st + 1) / 2));
+    for (int r = 0; r < group; ++r) {
+      const int t0 = r * per_r;
+      iter(std::true_type{}, t0, 0);
+      for (int i = 1; i < i_mask; ++i) iter(std::false_type{}, t0 + i, i);
+      for (int i = i_mask; i < per_r; ++i) iter(std::true_type{}, t0 + i, i);
+    }
+  }
+  wait_vm<0>();
+
+  // stream-ordered combination of the two partials of each key half
+  float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt) {
+      __syncthreads();
+      if (st == 1) {
+        float* slot = red + (kb * 64 + lane) * 16;
+        const f32x16& src = which == 0 ? dkt[dt] : dvt[dt];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) slot[e] = src[e];
+      }
+      __syncthreads();
+      if (st == 0) {
+        const float* slot = red + (kb * 64 + lane) * 16;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (which == 0) dkt[dt][e] += slot[e];
+          else dvt[dt][e] += slot[e];
+        }
+      }
+    }
+  }
+  if constexpr (PRO) {
+    // stream 0 holds the sums; the prologue backward of the 64 rows is shared by the waves
+    constexpr int TILE_AT = 16384, RED_AT = TILE_AT + 64 * HD * 4;
+    static_assert(sizeof(lds) >= RED_AT + 4 * HD * sizeof(float), "epilogue fits");
+    float* tile = reinterpret_cast<float*>(lds + TILE_AT);
+    if (st == 0) {
+      acc_to_tile<HD>(tile + kb * 32 * HD, dkt, scale, lane);
+      if (key < S) store_col<bf16, HD>(dv + ((size_t)kvbh * S + key) * HD, dvt, 1.0f, h);
+    }
+    lds_barrier();
+    constexpr int RPW = 64 / (HD / 16);  // rows per wave pass
+    float dg[16] = {};
+    pro_rows<HD, 2 * RPW>(tile, wv * 2 * RPW, dk + (size_t)kvbh * S * HD, pro, (size_t)kvbh * S,
+                          k0, S, lane, dg);
+    pro_partial<HD>(dg, reinterpret_cast<float*>(lds + RED_AT), HD, pro, kvbh * nkt + kt, wv,
+                    lane, tid);
+    return;
+  }
+  if (st != 0) return;
+  if (key < S) {
+    store_col<bf16, HD>(dk + ((size_t)kvbh * S + key) * HD, dkt, scale, h);
+    store_col<bf16, HD>(dv + ((size_t)kvbh * S + key) * HD, dvt, 1.0f, h);
+  }
+}
+
 constexpr int kFwdBuf = 2;
 constexpr int kDqBuf = 2;
 constexpr int kDkdvSharedBuf = 3;
@@ -1248,8 +1489,14 @@ hipError_t fwd_launch(const AttnShape& s, const void* q, const void* k, const vo
 }
 
 // dk/dv kernel choice: the shared-tile kernel when its 128-key workgroups fill the
-// machine, else the private one (32 keys per workgroup).
+// machine; else, at head_dim 128, the pipelined one (64 keys per workgroup), else the
+// private one (32 keys per workgroup).
 bool dkdv_shared(int BKV, int S) { return (long long)BKV * ((S + 127) / 128) >= 1024; }
+constexpr bool kDkdvPipe = true;
+int dkdv_keys_per_block(int BKV, int S, int HD) {
+  if (dkdv_shared(BKV, S)) return 128;
+  return (kDkdvPipe && HD == 128) ? 64 : 32;
+}
 
 template <int HD, bool PRO>
 hipError_t bwd_launch(const AttnShape& s, const void* q, const void* k, const void* v,
@@ -1279,6 +1526,12 @@ hipError_t bwd_launch(const AttnShape& s, const void* q, const void* k, const vo
                        (const bf16*)dout, (const float*)lse2, (const float*)delta, (bf16*)dk,
                        (bf16*)dv, S, s.num_heads, s.num_kv_heads, sl2, scale, nkt, xcd, pk,
                        s.seg_hi);
+  } else if (dkdv_keys_per_block(BKV, S, HD) == 64) {
+    const int nkt = (S + 63) / 64;
+    hipLaunchKernelGGL((dkdv_pipe_kernel<HD, PRO>), dim3(BKV * nkt), dim3(256), 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
+                       (const float*)lse2, (const float*)delta, (bf16*)dk, (bf16*)dv, S,
+                       s.num_heads, s.num_kv_heads, sl2, scale, nkt, xcd, pk, s.seg_hi);
   } else {
     const int nkt = (S + 31) / 32;
     hipLaunchKernelGGL((dkdv_private_kernel<HD, kDkdvPrivateBuf, PRO>), dim3(BKV * nkt),
@@ -1344,7 +1597,8 @@ hipError_t launch_attn_bwd_bf16_fast(const AttnShape& s, const void* q, const vo
     pq = make_pro(pro->xq, pro->gamma_q, pro->rstd_q, pro->cos_tab, pro->sin_tab,
                   pro->partials_q, fused_pro_parts_q(s.batch * s.num_heads, S));
     pk = make_pro(pro->xk, pro->gamma_k, pro->rstd_k, pro->cos_tab, pro->sin_tab,
-                  pro->partials_k, BKV * (dkdv_shared(BKV, S) ? (S + 127) / 128 : (S + 31) / 32));
+                  pro->partials_k, BKV * ((S + dkdv_keys_per_block(BKV, S, s.head_dim) - 1) /
+                                          dkdv_keys_per_block(BKV, S, s.head_dim)));
   }
 #define XATTN_CASE(HD, PRO)                                                                \
   e = bwd_launch<HD, PRO>(s, q, k, v, out, lse, dout, dq, dk, dv, delta, lse2, pq, pk, stream);
