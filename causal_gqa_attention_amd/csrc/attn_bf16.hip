@@ -121,6 +121,27 @@ __device__ __forceinline__ void pack16(bf16x8 (&pb)[2], const float (&v)[16]) {
     for (int j = 0; j < 8; ++j) pb[c2][j] = (bf16)v[8 * c2 + j];
 }
 
+// Max / sum of a value over lanes l and l ^ 32, the same in both lanes: one
+// v_permlane32_swap (lanes 32..63 of the first operand trade places with lanes 0..31 of the
+// second) instead of an LDS permute, so no LDS round trip and no lgkmcnt wait.  The sum adds
+// the lower lane's value first in both halves.
+__device__ __forceinline__ void swap_halves(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  lo = __builtin_bit_cast(float, (unsigned)r[0]);  // lane l: value of lane l & 31
+  hi = __builtin_bit_cast(float, (unsigned)r[1]);  // lane l: value of lane l | 32
+}
+__device__ __forceinline__ float halves_max(float v) {
+  float lo, hi;
+  swap_halves(v, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  float lo, hi;
+  swap_halves(v, lo, hi);
+  return lo + hi;
+}
+
 // s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt unconstrained).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -541,7 +562,7 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&o)[HD / 32], SoftmaxState& 
     sv[i] = x;
     tmax = fmaxf(tmax, x);
   }
-  tmax = fmaxf(tmax, shfl_xor(tmax, 32)) * scale_log2;
+  tmax = halves_max(tmax) * scale_log2;
   // rescale only when the reference max grows by more than 2^8
   if (__any(tmax > sm.m + 8.f)) {
     const float m_new = fmaxf(sm.m, tmax);
@@ -552,13 +573,15 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&o)[HD / 32], SoftmaxState& 
     sm.m = m_new;
   }
   const float mref = (MASK && sm.m == -INFINITY) ? 0.f : sm.m;
-  float psum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    sv[i] = fast_exp2(sv[i] * scale_log2 - mref);
-    psum += sv[i];
-  }
-  sm.l += psum;
+  for (int i = 0; i < 16; ++i) sv[i] = fast_exp2(sv[i] * scale_log2 - mref);
+  // pairwise sum (a short dependency chain)
+  float ps[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ps[i] = sv[2 * i] + sv[2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ps[i] += ps[i + 4];
+  sm.l += (ps[0] + ps[2]) + (ps[1] + ps[3]);
   pack16(pb, sv);
 }
 
@@ -658,7 +681,7 @@ __device__ __forceinline__ void qknorm_rope_frag(bf16x8 (&frag)[HD / 16], const 
       const float xv = (float)frag[c][j];
       ss += xv * xv;
     }
-  ss += shfl_xor(ss, 32);
+  ss = halves_sum(ss);
   const float r = 1.0f / sqrtf(ss * (1.0f / (float)HD) + pf.eps);
 #pragma unroll
   for (int c = 0; c < HC; ++c)
@@ -755,7 +778,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const bf16* __restrict__ q,
     }
   };
   q_stage_loop(doc, min(q0 / kBN, S / kBN), ntiles, stage);
-  const float l = sm.l + shfl_xor(sm.l, 32);
+  const float l = halves_sum(sm.l);
   if (qrow < S) {
     store_col<bf16, HD>(out + ((size_t)bh * S + qrow) * HD, o, 1.0f / l, h);
     if (h == 0) lse[(size_t)bh * S + qrow] = (sm.m + log2f(l)) * kLn2;
@@ -823,7 +846,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) dsum += (float)df[c][j] * (float)of[c][j];
   }
-  const float Dq = dsum + shfl_xor(dsum, 32);
+  const float Dq = halves_sum(dsum);
   const float lse2 = qrow < S ? lse[(size_t)bh * S + qrow] * kLog2e : 0.f;
   if (qrow < S && h == 0) {
     delta[(size_t)bh * S + qrow] = Dq;
