@@ -13,8 +13,13 @@ value = algorithmic attention FLOP per step (12 * hd per causal pair per query h
 4 * hd forward, 8 * hd backward; recompute not counted) / measured step time, in TFLOP/s.
 The step time includes the prologue kernels, which do no counted FLOP.
 
+Before the W untimed warmup steps the step runs for --settle-ms (default 200 ms) of wall
+time: from idle the GPU runs at a low clock and needs tens of milliseconds of continuous
+load to reach its sustained clock (measured on workload 5: 0.99 ms for the first 20 steps,
+0.66 ms from about the 60th on).  The timed region is then K whole steps as usual.
+
 Prints ONE JSON line on stdout; progress goes to stderr.
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms 200] [--workload 5]
   python bench.py --copy-calibration   # plain device copy of known size, for PMC scaling
 """
 from __future__ import annotations
@@ -45,6 +50,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--settle-ms", type=float, default=200.0,
+                   help="before the warmup steps, run the step until the GPU has been busy "
+                        "this long (it leaves its idle clock state only after tens of ms "
+                        "of load); 0 disables")
     p.add_argument("--workload", type=int, default=5, help="index of the workload shape")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
@@ -62,6 +71,22 @@ def parse():
     p.add_argument("--decode-cache", type=int, default=4096,
                    help="cache capacity; the step decodes one token at position capacity-1")
     return p.parse_args()
+
+
+def settle(step, min_ms):
+    """Run `step` (synchronised each time) until min_ms of wall time have passed.  From
+    idle the GPU starts at a low clock and reaches its sustained clock only after tens of
+    milliseconds of continuous load; a training or serving loop runs in that sustained
+    state, so the timed steps should too.  Untimed, like the warmup steps."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while n == 0 or (time.perf_counter() - t0) * 1e3 < min_ms:
+        step()
+        torch.cuda.synchronize()
+        n += 1
+    ms = (time.perf_counter() - t0) * 1e3
+    log(f"settle: {n} steps in {ms:.0f} ms")
+    return {"ms": round(ms, 1), "steps": n}
 
 
 def doc_pairs(w, docs):
@@ -102,8 +127,8 @@ def traffic_for(kernel, name):
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         h = hashlib.sha256()
-        for name in t["source_files"]:
-            with open(os.path.join(CSRC, name), "rb") as f:
+        for src in t["source_files"]:
+            with open(os.path.join(CSRC, src), "rb") as f:
                 h.update(f.read())
         sha = h.hexdigest()
     except (OSError, ValueError, KeyError):
@@ -203,6 +228,7 @@ def proj_bench(args):
     flops = 2 * M * d * (nq + 2 * nk) + 2 * M * nq * d      # forward: QKV, output
     flops += 2 * (2 * M * d * nq)                             # output backward: dO, dWo
     flops += 2 * (2 * M * d * (nq + 2 * nk))                  # QKV backward: dx, dW
+    settled = settle(step, args.settle_ms) if args.settle_ms > 0 else None
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -260,7 +286,8 @@ def proj_bench(args):
                          f"numpy oracle projections fwd + bwd, {dtc:.1f} s"}
     print(json.dumps({
         "metric": PROJ_METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup, "settle": settled, "ms_per_step": ms,
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": name, "tokens": M, "model_dim": d, "num_heads": H,
                    "num_kv_heads": Hkv, "head_dim": hd, "io_dtype": w.dtype,
@@ -320,6 +347,7 @@ def decode_bench(args):
     def step():
         X.xattn_decode(dims, xq, xk, v, gq, gk, cos, sin, base.eps, kc, vc, out, lse, ws)
 
+    settled = settle(step, args.settle_ms) if args.settle_ms > 0 else None
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -389,7 +417,7 @@ def decode_bench(args):
                          f"with its {g} query heads): float64 numpy oracle.decode, {dt:.1f} s"}
     line = {
         "metric": DECODE_METRIC, "value": value, "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "steps": args.steps, "warmup": args.warmup, "settle": settled, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": name, "batch": B, "cache_len": pos, "q_len": q_len,
@@ -444,6 +472,7 @@ def main():
     flops = {"fwd": 4 * w.head_dim * units_per_head, "bwd": 8 * w.head_dim * units_per_head,
              "total": 12 * w.head_dim * units_per_head}
 
+    settled = settle(step.run, args.settle_ms) if args.settle_ms > 0 else None
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -510,7 +539,7 @@ def main():
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "steps": args.steps, "warmup": args.warmup, "settle": settled, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": wname, "batch": w.batch, "seq_len": w.seq_len,

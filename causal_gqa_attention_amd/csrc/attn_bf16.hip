@@ -103,6 +103,21 @@ __device__ __forceinline__ f32x16 contract_rows(const char* base, uint32_t al,
   return acc;
 }
 
+// The lane's row operands (rows R0 + lane%32, all hd) and transposed operands (the 8 k-slots
+// of every 32-column block) of a 32-row tile, read into registers ahead of their MFMAs.
+template <int HD>
+__device__ __forceinline__ void rows_of(bf16x8 (&x)[HD / 16], const char* base, uint32_t al) {
+#pragma unroll
+  for (int c = 0; c < HD / 16; ++c) x[c] = lds_a<HD>(base, al, c);
+}
+template <int HD>
+__device__ __forceinline__ void tr_of(bf16x8 (&x)[2][HD / 32], const char* base, uint32_t tl) {
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt) x[c2][dt] = lds_t<HD>(base, tl, c2, dt);
+}
+
 // acc[dt] += (tile rows R0..R0+31, transposed) x (two packed 8-slot operands)
 template <int HD>
 __device__ __forceinline__ void acc_tr(f32x16 (&acc)[HD / 32], const char* base, uint32_t tl,
@@ -1262,19 +1277,6 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_private_kernel(
 // streams' partial dK / dV of the same keys are added in stream order at the end.
 // ---------------------------------------------------------------------------------------
 constexpr int kPipeBuf = 4;  // staged tiles per stream
-
-template <int HD>
-__device__ __forceinline__ void rows_of(bf16x8 (&x)[HD / 16], const char* base, uint32_t al) {
-#pragma unroll
-  for (int c = 0; c < HD / 16; ++c) x[c] = lds_a<HD>(base, al, c);
-}
-template <int HD>
-__device__ __forceinline__ void tr_of(bf16x8 (&x)[2][HD / 32], const char* base, uint32_t tl) {
-#pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-    for (int dt = 0; dt < HD / 32; ++dt) x[c2][dt] = lds_t<HD>(base, tl, c2, dt);
-}
 
 template <int HD, bool PRO>
 __global__ __launch_bounds__(256, 1) void dkdv_pipe_kernel(

@@ -32,6 +32,10 @@ SMALL = [
     R("bf16", 128, 1, 1, 4, 1, index=211),
     W.WORKLOADS[4].replace(batch=2, seq_len=190, index=212),
     W.WORKLOADS[5].replace(seq_len=300, index=213),
+    # hd 128 shapes for the pipelined dk/dv kernel: MHA over two batch rows with a ragged
+    # 64-key block; group 8 with the sequence exactly one 64-key block
+    R("bf16", 128, 161, 2, 2, 2, theta=1e6, eps=1e-6, index=214),
+    R("bf16", 128, 64, 1, 16, 2, index=215),
 ]
 SMALL_IDS = [w.name if w.index < 100 else f"{w.dtype}_hd{w.head_dim}_S{w.seq_len}_"
              f"B{w.batch}_H{w.num_heads}_kv{w.num_kv_heads}" for w in SMALL]
