@@ -16,9 +16,12 @@
 // 16-byte loads (a key row spread over HD*size/16 lanes, several keys per wave load, four
 // loads in flight per lane), keeps every query row of the group in registers, and runs an
 // online softmax per lane group with one rescale per four keys.  The lane groups of a wave
-// are merged by a fixed xor butterfly, the ranges in range order by a third launch, so the
-// result is bitwise reproducible.  Three launches: prologue + append, split attention,
-// combine.
+// are merged by a fixed xor butterfly, the ranges in range order by a second launch, so the
+// result is bitwise reproducible.  The prologue forward runs inside the split launch: each
+// wave normalises and rotates its group's query rows in the lane layout of its loads, and
+// the wave whose range holds a new token's row writes that token's rotated key and its
+// value into the caches before streaming the range (its own loads then read them back).
+// Two launches: split attention (with prologue and append), combine.
 #include <math.h>
 
 #include "xattn_device.h"
@@ -39,7 +42,6 @@ struct DecodeArgs {
   void* v_cache;         // [B*Hkv, cap, HD]
   void* out;             // [B*H, Sq, HD]
   float* lse;            // [B*H*Sq]
-  void* yq;              // workspace [B*H, Sq, HD] io dtype: normalised, rotated queries
   float* part_o;         // workspace [B*Hkv][nsplit][R][HD]
   float* part_ml;        // workspace [B*Hkv][nsplit][R][2]: running max (log2 units), sum
   int B, H, Hkv, Sq, pos, cap, nsplit, ks;  // ks: keys per range
@@ -79,76 +81,43 @@ __device__ __forceinline__ void load_vec(const T* p, float (&out)[N]) {
 }
 
 // ---------------------------------------------------------------------------------------
-// 1. prologue + append.  Rows [0, B*H*Sq) are the new queries (normalised and rotated into
-// the yq workspace), rows [B*H*Sq, B*H*Sq + B*Hkv*Sq) the new keys (normalised and rotated
-// into cache row pos + i; the same lanes copy the value row into the V cache).  LPR lanes
-// per row, each owning VEC columns of the first half and the matching second-half columns;
-// the arithmetic is that of the prologue forward.
+// 1. prologue forward in the split kernel's lane layout.  A row of HD columns is spread over
+// LPK lanes, lane part p holding columns [p*VEC, p*VEC + VEC); the partner of column c
+// (c < HD/2) in its rotation pair is c + HD/2, held by part p + LPK/2.  Returns the lane's
+// VEC columns of y = rotate_t(gamma * x * rsqrt(mean x^2 + eps)) rounded to the io dtype
+// (the prologue forward's arithmetic: normalise, scale by gamma, rotate by the angles of
+// position t).
 // ---------------------------------------------------------------------------------------
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void decode_prologue_kernel(DecodeArgs a) {
-  constexpr int VEC = V16<T>::n, HALF = HD / 2;
-  constexpr int W = HALF < VEC ? HALF : VEC;  // columns of each half per lane
-  constexpr int LPR = HALF / W;
-  const int g = blockIdx.x * 256 + threadIdx.x;
-  const int row = g / LPR, part = g % LPR;
-  const int nq = a.B * a.H * a.Sq, nk = a.B * a.Hkv * a.Sq;
-  const bool valid = row < nq + nk;
-  const bool isq = row < nq;
-  const int rr = !valid ? 0 : (isq ? row : row - nq);  // row within its tensor
-  const int head = rr / a.Sq, t = a.pos + rr % a.Sq;
-  const T* x = static_cast<const T*>(isq ? a.xq : a.xk) + (size_t)rr * HD;
-  const float* gamma = isq ? a.gamma_q : a.gamma_k;
-  const int c0 = part * W;
-  float x1[W], x2[W], cs[W], sn[W], g1[W], g2[W];
-  if constexpr (W == VEC) {
-    load_vec<T, W>(x + c0, x1);
-    load_vec<T, W>(x + HALF + c0, x2);
-  } else {
+__device__ __forceinline__ void prologue_lanes(const T* __restrict__ xrow,
+                                               const float* __restrict__ gamma,
+                                               const float* __restrict__ cos_tab,
+                                               const float* __restrict__ sin_tab, int t,
+                                               float eps, int part, float (&y)[V16<T>::n]) {
+  constexpr int VEC = V16<T>::n, LPK = HD / VEC, HALF = HD / 2, PH = LPK / 2;
+  static_assert(HALF % VEC == 0, "each half spans whole lane parts");
+  float x[VEC], g[VEC], cs[VEC], sn[VEC];
+  load_vec<T, VEC>(xrow + part * VEC, x);
+  const int cp = (part % PH) * VEC;  // column of the pair's first-half member
 #pragma unroll
-    for (int e = 0; e < W; ++e) {
-      x1[e] = to_f32(x[c0 + e]);
-      x2[e] = to_f32(x[HALF + c0 + e]);
-    }
-  }
-  if constexpr (W % 4 == 0) {
-    load_vec<float, W>(a.cos_tab + (size_t)t * HALF + c0, cs);
-    load_vec<float, W>(a.sin_tab + (size_t)t * HALF + c0, sn);
-    load_vec<float, W>(gamma + c0, g1);
-    load_vec<float, W>(gamma + HALF + c0, g2);
-  } else {
-#pragma unroll
-    for (int e = 0; e < W; ++e) {
-      cs[e] = a.cos_tab[(size_t)t * HALF + c0 + e];
-      sn[e] = a.sin_tab[(size_t)t * HALF + c0 + e];
-      g1[e] = gamma[c0 + e];
-      g2[e] = gamma[HALF + c0 + e];
-    }
+  for (int e = 0; e < VEC; ++e) {
+    g[e] = gamma[part * VEC + e];
+    cs[e] = cos_tab[(size_t)t * HALF + cp + e];
+    sn[e] = sin_tab[(size_t)t * HALF + cp + e];
   }
   float ss = 0.f;
 #pragma unroll
-  for (int e = 0; e < W; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
+  for (int e = 0; e < VEC; ++e) ss += x[e] * x[e];
+  ss = lane_group_sum<LPK>(ss);
+  const float r = 1.0f / sqrtf(ss * (1.0f / (float)HD) + eps);
+  const bool first = part < PH;
 #pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) ss += shfl_xor(ss, m);
-  const float r = 1.0f / sqrtf(ss * (1.0f / (float)HD) + a.eps);
-  if (!valid) return;
-  T* dst = isq ? static_cast<T*>(a.yq) + (size_t)rr * HD
-               : static_cast<T*>(a.k_cache) + ((size_t)head * a.cap + t) * HD;
-#pragma unroll
-  for (int e = 0; e < W; ++e) {
-    const float n1 = x1[e] * r * g1[e];
-    const float n2 = x2[e] * r * g2[e];
-    dst[c0 + e] = from_f32<T>(n1 * cs[e] - n2 * sn[e]);
-    dst[HALF + c0 + e] = from_f32<T>(n1 * sn[e] + n2 * cs[e]);
-  }
-  if (!isq) {
-    const T* vs = static_cast<const T*>(a.v) + (size_t)rr * HD;
-    T* vd = static_cast<T*>(a.v_cache) + ((size_t)head * a.cap + t) * HD;
-#pragma unroll
-    for (int e = 0; e < W; ++e) {
-      vd[c0 + e] = vs[c0 + e];
-      vd[HALF + c0 + e] = vs[HALF + c0 + e];
-    }
+  for (int e = 0; e < VEC; ++e) {
+    const float n = x[e] * r * g[e];
+    const float m = shfl_xor(n, PH);  // the pair's other member
+    const float n1 = first ? n : m, n2 = first ? m : n;
+    const float v = first ? n1 * cs[e] - n2 * sn[e] : n1 * sn[e] + n2 * cs[e];
+    y[e] = to_f32(from_f32<T>(v));
   }
 }
 
@@ -180,15 +149,38 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     lim[r] = -1;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) q[r][e] = 0.f;
-    if (r < R) {
+    if (r < R) {  // wave-uniform
       const int g = r / a.Sq, i = r - g * a.Sq;
-      const T* yr = static_cast<const T*>(a.yq) +
-                    ((size_t)(b * a.H + kvh * group + g) * a.Sq + i) * HD + part * VEC;
-      load_vec<T, VEC>(yr, q[r]);
+      const T* xr = static_cast<const T*>(a.xq) +
+                    ((size_t)(b * a.H + kvh * group + g) * a.Sq + i) * HD;
+      prologue_lanes<T, HD>(xr, a.gamma_q, a.cos_tab, a.sin_tab, a.pos + i, a.eps, part, q[r]);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) q[r][e] *= a.scale_log2;
       lim[r] = a.pos + i;
     }
+  }
+  // Append: the new tokens' rows of this range (cache rows pos .. pos + Sq - 1 that fall in
+  // [k0, k1)) get the rotated key and the value, KPW rows per pass; then the stores are
+  // made visible to this wave's own loads below.
+  const int n0 = max(k0, a.pos);
+  if (n0 < k1) {  // wave-uniform
+    for (int j0 = n0; j0 < k1; j0 += KPW) {
+      const int j = j0 + kg;
+      const int i = (j < k1 ? j : n0) - a.pos;  // token (clamped for idle lanes)
+      const size_t src = ((size_t)bkv * a.Sq + i) * HD;
+      float yk[VEC];
+      prologue_lanes<T, HD>(static_cast<const T*>(a.xk) + src, a.gamma_k, a.cos_tab,
+                            a.sin_tab, a.pos + i, a.eps, part, yk);
+      if (j < k1) {
+        const size_t dst = ((size_t)bkv * a.cap + j) * HD + part * VEC;
+        T* kd = static_cast<T*>(a.k_cache) + dst;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) kd[e] = from_f32<T>(yk[e]);
+        store16(static_cast<T*>(a.v_cache) + dst,
+                load16(static_cast<const T*>(a.v) + src + part * VEC));
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   }
   float m[RM], l[RM], o[RM][VEC];
 #pragma unroll
@@ -369,16 +361,7 @@ hipError_t split_launch(int R, dim3 grid, const DecodeArgs& a, hipStream_t strea
 
 template <typename T, int HD>
 hipError_t decode_launch(const DecodeArgs& a, hipStream_t stream) {
-  const int nrows = (a.B * a.H + a.B * a.Hkv) * a.Sq;
-  constexpr int LPR = (HD / 2) / V16<T>::n > 0 ? (HD / 2) / V16<T>::n : 1;
-  {
-    ProfScope prof("decode_prologue", stream);
-    const long long threads = (long long)nrows * LPR;
-    hipLaunchKernelGGL((decode_prologue_kernel<T, HD>), dim3((int)((threads + 255) / 256)),
-                       dim3(256), 0, stream, a);
-  }
-  hipError_t e = hipPeekAtLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
   const int R = (a.H / a.Hkv) * a.Sq;
   const int waves = a.B * a.Hkv * a.nsplit;
   {
@@ -427,7 +410,7 @@ hipError_t launch_decode(IoType io, const DecodeShape& d, const DecodeBufs& bufs
   a.gamma_q = bufs.gamma_q, a.gamma_k = bufs.gamma_k;
   a.cos_tab = bufs.cos_tab, a.sin_tab = bufs.sin_tab;
   a.k_cache = bufs.k_cache, a.v_cache = bufs.v_cache, a.out = bufs.out, a.lse = bufs.lse;
-  a.yq = bufs.yq, a.part_o = bufs.part_o, a.part_ml = bufs.part_ml;
+  a.part_o = bufs.part_o, a.part_ml = bufs.part_ml;
   a.B = d.batch, a.H = d.num_heads, a.Hkv = d.num_kv_heads, a.Sq = d.q_len;
   a.pos = d.cache_len, a.cap = d.capacity;
   const DecodePlan p = decode_plan(d, d.cache_len + d.q_len);

@@ -281,9 +281,9 @@ DecodeChecked check_decode_dims(const xattn_decode_dims* d, float eps) {
   return c;
 }
 
-// yq, then the range partials of the output and of (max, sum), each 256-byte aligned
+// the range partials of the output and of (max, sum), each 256-byte aligned
 struct DecodeWorkspace {
-  size_t yq, part_o, part_ml, total;
+  size_t part_o, part_ml, total;
 };
 DecodeWorkspace decode_workspace(const DecodeChecked& c) {
   const xattn::DecodeShape& d = c.d;
@@ -291,8 +291,7 @@ DecodeWorkspace decode_workspace(const DecodeChecked& c) {
                         xattn::decode_max_splits(d.batch, d.num_kv_heads, d.capacity) *
                         (size_t)(d.num_heads / d.num_kv_heads) * d.q_len;
   DecodeWorkspace w;
-  w.yq = 0;
-  w.part_o = align256((size_t)c.q_elems * io_size(c.io));
+  w.part_o = 0;
   w.part_ml = w.part_o + align256(ranges * d.head_dim * sizeof(float));
   w.total = w.part_ml + align256(ranges * 2 * sizeof(float));
   return w;
@@ -749,7 +748,6 @@ xattn_status xattn_decode(const xattn_decode_dims* dims, const void* xq, const v
     b.xq = xq, b.xk = xk, b.v = v, b.gamma_q = gamma_q, b.gamma_k = gamma_k;
     b.cos_tab = cos_tab, b.sin_tab = sin_tab, b.k_cache = k_cache, b.v_cache = v_cache;
     b.out = out, b.lse = lse;
-    b.yq = ws + w.yq;
     b.part_o = reinterpret_cast<float*>(ws + w.part_o);
     b.part_ml = reinterpret_cast<float*>(ws + w.part_ml);
     hip_check(xattn::launch_decode(c.io, c.d, b, (hipStream_t)stream), "decode launch");

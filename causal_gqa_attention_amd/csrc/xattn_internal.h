@@ -117,7 +117,6 @@ struct DecodeBufs {
   const float *gamma_q, *gamma_k, *cos_tab, *sin_tab;
   void *k_cache, *v_cache, *out;
   float* lse;
-  void* yq;        // workspace: new queries after the prologue, io dtype [B*H, Sq, hd]
   float* part_o;   // workspace: [B*Hkv][splits][group*Sq][hd]
   float* part_ml;  // workspace: [B*Hkv][splits][group*Sq][2]
 };
