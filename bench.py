@@ -21,6 +21,8 @@ load to reach its sustained clock (measured on workload 5: 0.99 ms for the first
 Prints ONE JSON line on stdout; progress goes to stderr.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms 200] [--workload 5]
   python bench.py --copy-calibration   # plain device copy of known size, for PMC scaling
+  python bench.py --traffic-summary FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+      # writes the dk/dv traffic summary from four `rocprofv3 --pmc` output folders
 """
 from __future__ import annotations
 
@@ -58,6 +60,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of 1 GiB (for HBM counter scaling)")
+    p.add_argument("--traffic-summary", nargs=4, default=None,
+                   metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                   help="write the HBM traffic summary of the dk/dv kernel from the counter "
+                        "CSVs of four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the "
+                        "bench, then of --copy-calibration); no GPU use")
     p.add_argument("--docs", type=str, default=None,
                    help="comma-separated document lengths packed along the sequence "
                         "(block-causal mask); must sum to the workload's seq_len")
@@ -187,6 +194,68 @@ def copy_calibration():
         torch.cuda.synchronize()
         log(f"copy {i}: {n} bytes read, {n} bytes written")
     print(json.dumps({"copy_calibration_bytes": n, "dispatches": 5}))
+
+
+def pmc_per_dispatch(folder, counter, name_part):
+    """Average of `counter` per dispatch over the dispatches whose kernel name contains
+    `name_part`, from the counter-collection CSVs rocprofv3 wrote under `folder`."""
+    import csv
+    import glob
+    per = {}
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                if name_part.lower() not in row.get("Kernel_Name", "").lower():
+                    continue
+                key = (fn, row.get("Dispatch_Id"))
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for kernels matching '{name_part}' under {folder}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def traffic_summary(dirs, workload_name):
+    """Write the committed traffic summary of the dk/dv kernel: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) and the same counters per KiB of a plain 1 GiB device copy, with the
+    hash of the kernel sources they were taken on (the bench reports `traffic` only while
+    that hash still matches)."""
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
+    fetch, n_f = pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "dkdv")
+    write, n_w = pmc_per_dispatch(write_dir, "WRITE_SIZE", "dkdv")
+    cfetch, _ = pmc_per_dispatch(cfetch_dir, "FETCH_SIZE", "copy")
+    cwrite, _ = pmc_per_dispatch(cwrite_dir, "WRITE_SIZE", "copy")
+    kib = (1 << 30) / 1024.0
+    files = ["attn.hip", "attn_bf16.hip", "xattn_device.h"]
+    h = hashlib.sha256()
+    for src in files:
+        with open(os.path.join(CSRC, src), "rb") as f:
+            h.update(f.read())
+    scale = {"fetch": cfetch / kib, "write": cwrite / kib,
+             "note": "FETCH_SIZE / WRITE_SIZE (KiB) of one 1 GiB device copy divided by "
+                     "1 GiB in KiB"}
+    pre = "cd /tmp && export TMPDIR=/tmp && "
+    bench_cmd = "-- python3 $REPO/bench.py --steps 3 --warmup 1 --settle-ms 0 --no-cpu-baseline"
+    t = {"kernel": "attn_bwd_dkdv", "workload": workload_name,
+         "source_sha256": h.hexdigest(), "source_files": files,
+         "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+         "dispatches": min(n_f, n_w), "copy_scale": scale,
+         "commands": [
+             pre + f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex dkdv "
+             f"-d $REPO/{fetch_dir} -o dkdv -f csv " + bench_cmd,
+             pre + f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --kernel-include-regex dkdv "
+             f"-d $REPO/{write_dir} -o dkdv -f csv " + bench_cmd,
+             pre + f"timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE -d $REPO/{cfetch_dir} -o copy "
+             "-f csv -- python3 $REPO/bench.py --copy-calibration",
+             pre + f"timeout -s KILL 90 rocprofv3 --pmc WRITE_SIZE -d $REPO/{cwrite_dir} -o copy "
+             "-f csv -- python3 $REPO/bench.py --copy-calibration",
+             f"python3 bench.py --traffic-summary {fetch_dir} {write_dir} {cfetch_dir} {cwrite_dir}"],
+         "hbm_bytes_per_dispatch": (fetch / scale["fetch"] + write / scale["write"]) * 1024.0}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+    log(f"wrote {TRAFFIC_FILE}: {t['hbm_bytes_per_dispatch'] / 1e6:.1f} MB per dispatch")
 
 
 PROJ_METRIC = "attention-block projections fwd+bwd TFLOP/s (bf16 GEMMs, fp32 accumulate)"
@@ -440,6 +509,10 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.traffic_summary:
+        import workloads as W
+        traffic_summary(args.traffic_summary, W.WORKLOADS[args.workload].name)
         return
     if args.decode:
         decode_bench(args)
