@@ -484,11 +484,11 @@ __device__ __forceinline__ void pro_rows(float* tile, int r0, bf16* __restrict__
   }
 }
 
-// Workgroup dgamma partial from the four waves' dg: each wave sums its lanes' terms per
+// Workgroup dgamma partial from the NW waves' dg: each wave sums its lanes' terms per
 // column (halving over the row-slot lane bits) into red_w (HD floats of LDS only this wave
 // uses until the barrier; wave w's at red0 + w * red_stride), then threads 0..HD-1 add the
-// four waves in wave order into partial slot `slot`.  Every thread of the workgroup calls.
-template <int HD>
+// NW waves in wave order into partial slot `slot`.  Every thread of the workgroup calls.
+template <int HD, int NW = 4>
 __device__ __forceinline__ void pro_partial(float (&dg)[16], float* red0, int red_stride,
                                             const ProBwd& pb, int slot, int wv, int lane,
                                             int tid) {
@@ -504,8 +504,9 @@ __device__ __forceinline__ void pro_partial(float (&dg)[16], float* red0, int re
   }
   lds_barrier();
   if (tid < HD) {
-    const float s = ((red0[tid] + red0[red_stride + tid]) + red0[2 * red_stride + tid]) +
-                    red0[3 * red_stride + tid];
+    float s = red0[tid];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) s += red0[w * red_stride + tid];
     pb.partials[(size_t)tid * pb.nparts + slot] = s;
   }
 }
@@ -544,7 +545,11 @@ __device__ __forceinline__ void map_kvblock(int lin, int BKV, bool xcd, int& kvb
   }
 }
 
-constexpr int kBM = 128;  // queries per forward / dq block (4 waves x 32)
+// Forward / dq workgroup: kQW waves of 32 queries.  Eight waves (256 queries) halve the
+// K/V tile copies per query against four (each staged tile feeds twice the queries) at the
+// same occupancy (two waves per SIMD, one workgroup per CU).
+constexpr int kQW = 8;
+constexpr int kBM = 32 * kQW;  // queries per forward / dq block
 constexpr int kBN = 64;   // keys per stage
 
 // ---------------------------------------------------------------------------------------
@@ -719,7 +724,7 @@ __device__ __forceinline__ void qknorm_rope_frag(bf16x8 (&frag)[HD / 16], const 
 }
 
 template <int HD, int NBUF, bool PROQ>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(const bf16* __restrict__ q,
+__global__ __launch_bounds__(64 * kQW, 1) void fwd_kernel(const bf16* __restrict__ q,
                                                      const bf16* __restrict__ k,
                                                      const bf16* __restrict__ v,
                                                      bf16* __restrict__ out,
@@ -729,7 +734,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const bf16* __restrict__ q,
                                                      const int* __restrict__ seg_lo) {
   constexpr int ROWB = 2 * HD;
   constexpr int TILEB = kBN * ROWB;
-  using D = Dma<HD, kBN, 4>;
+  using D = Dma<HD, kBN, kQW>;
   constexpr int NL = 2 * D::PER;  // loads per wave per stage
   __shared__ __attribute__((aligned(1024))) char lds[NBUF * 2 * TILEB];
   const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
@@ -824,7 +829,7 @@ __device__ __forceinline__ void dq_subtile(f32x16 (&acc)[HD / 32], const f32x16&
 }
 
 template <int HD, int NBUF, bool PRO>
-__global__ __launch_bounds__(256, 2) void dq_kernel(
+__global__ __launch_bounds__(64 * kQW, 1) void dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ out, const bf16* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ lse2_out, float* __restrict__ delta, bf16* __restrict__ dq, int S, int H,
@@ -832,9 +837,11 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
     const int* __restrict__ seg_lo) {
   constexpr int ROWB = 2 * HD;
   constexpr int TILEB = kBN * ROWB;
-  using D = Dma<HD, kBN, 4>;
+  using D = Dma<HD, kBN, kQW>;
   constexpr int NL = 2 * D::PER;
-  __shared__ __attribute__((aligned(1024))) char lds[NBUF * 2 * TILEB];
+  // staged K/V tiles; with the prologue also each wave's fp32 dq tile in the epilogue
+  constexpr int EPIB = PRO ? kQW * 32 * HD * (int)sizeof(float) : 0;
+  __shared__ __attribute__((aligned(1024))) char lds[std::max(NBUF * 2 * TILEB, EPIB)];
   const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int BH = gridDim.x / nqt;
@@ -903,15 +910,15 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
   };
   q_stage_loop(doc, min(q0 / kBN, S / kBN), ntiles, stage);
   if constexpr (PRO) {
-    static_assert(sizeof(lds) >= 4 * 32 * HD * sizeof(float), "epilogue tiles fit");
+    static_assert(sizeof(lds) >= kQW * 32 * HD * sizeof(float), "epilogue tiles fit");
     lds_barrier();  // every wave is done with the staged tiles
     float* tile = reinterpret_cast<float*>(lds) + wv * 32 * HD;
     acc_to_tile<HD>(tile, acc, scale, lane);
     float dg[16] = {};
     pro_rows<HD, 32>(tile, 0, dq + hoff, pro, (size_t)bh * S, qw0, S, lane, dg);
     asm volatile("" ::: "memory");
-    pro_partial<HD>(dg, reinterpret_cast<float*>(lds), 32 * HD, pro, bh * nqt + mp.qt, wv, lane,
-                    tid);
+    pro_partial<HD, kQW>(dg, reinterpret_cast<float*>(lds), 32 * HD, pro, bh * nqt + mp.qt, wv,
+                         lane, tid);
   } else if (qrow < S) {
     store_col<bf16, HD>(dq + ((size_t)bh * S + qrow) * HD, acc, scale, h);
   }
@@ -1506,7 +1513,7 @@ hipError_t fwd_launch(const AttnShape& s, const void* q, const void* k, const vo
   const int BKV = s.batch * s.num_kv_heads;
   const int xcd = (BKV % 8 == 0) ? 1 : 0;
   ProfScope prof("attn_fwd", stream);
-  hipLaunchKernelGGL((fwd_kernel<HD, kFwdBuf, PROQ>), dim3(BH * nqt), dim3(256), 0, stream,
+  hipLaunchKernelGGL((fwd_kernel<HD, kFwdBuf, PROQ>), dim3(BH * nqt), dim3(64 * kQW), 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)out, lse, s.seq_len,
                      s.num_heads, s.num_kv_heads, kLog2e / sqrtf((float)HD), nqt, xcd, pro,
                      s.seg_lo);
@@ -1536,7 +1543,7 @@ hipError_t bwd_launch(const AttnShape& s, const void* q, const void* k, const vo
   const float scale = 1.0f / sqrtf((float)HD), sl2 = kLog2e * scale;
   {
     ProfScope prof("attn_bwd_dq", stream);
-    hipLaunchKernelGGL((dq_kernel<HD, kDqBuf, PRO>), dim3(BH * nqt), dim3(256), 0, stream,
+    hipLaunchKernelGGL((dq_kernel<HD, kDqBuf, PRO>), dim3(BH * nqt), dim3(64 * kQW), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)out,
                        (const bf16*)dout, lse, lse2, delta, (bf16*)dq, S, s.num_heads,
                        s.num_kv_heads, sl2, scale, nqt, xcd, pq, s.seg_lo);
@@ -1602,7 +1609,7 @@ hipError_t launch_attn_fwd_bf16_fast(const AttnShape& s, const void* q, const vo
   return hipErrorInvalidValue;
 }
 
-// dgamma partial slots: one per dq workgroup (128 queries), one per dk/dv workgroup
+// dgamma partial slots: one per dq workgroup (kBM queries), one per dk/dv workgroup
 // (128 or 32 keys; the workspace is sized for 32).
 int fused_pro_parts_q(int64_t q_heads, int seq_len) {
   return (int)(q_heads * ((seq_len + kBM - 1) / kBM));
