@@ -550,7 +550,7 @@ __device__ __forceinline__ void map_kvblock(int lin, int BKV, bool xcd, int& kvb
 // same occupancy (two waves per SIMD, one workgroup per CU).
 constexpr int kQW = 8;
 constexpr int kBM = 32 * kQW;  // queries per forward / dq block
-constexpr int kBN = 64;   // keys per stage
+constexpr int kBN = 128;  // keys per stage
 
 // ---------------------------------------------------------------------------------------
 // forward
