@@ -20,7 +20,8 @@ import torch
 
 __all__ = [
     "XattnError", "library_path", "load_library",
-    "xattn_rope_cache", "xattn_qknorm_rope_fwd", "xattn_qknorm_rope_bwd_workspace_bytes",
+    "xattn_rope_cache", "xattn_qknorm_rope_fwd", "xattn_qknorm_rope_fwd_table",
+    "xattn_qknorm_rope_bwd_workspace_bytes",
     "xattn_qknorm_rope_bwd", "xattn_fwd", "xattn_fwd_qnorm", "xattn_bwd_workspace_bytes",
     "xattn_bwd",
     "xattn_decode_workspace_bytes", "xattn_decode", "xattn_segments", "xattn_rope_cache_at",
@@ -28,7 +29,7 @@ __all__ = [
     "xattn_out_proj_bwd", "xattn_qkv_proj_bwd",
     "xattn_status_string", "xattn_last_error", "xattn_version", "xattn_profile_start",
     "xattn_profile_stop",
-    "rope_cache", "qknorm_rope_fwd", "qknorm_rope_bwd", "attn_fwd", "attn_fwd_qnorm",
+    "rope_cache", "qknorm_rope_fwd", "qknorm_rope_fwd_table", "qknorm_rope_bwd", "attn_fwd", "attn_fwd_qnorm",
     "attn_bwd", "decode", "segments", "rope_cache_at", "Projection",
 ]
 
@@ -103,6 +104,8 @@ def load_library() -> ctypes.CDLL:
         "xattn_segments": (i32, [vp, i32, i64, vp, vp, vp, vp]),
         "xattn_qknorm_rope_fwd": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_float,
                                         i32, vp]),
+        "xattn_qknorm_rope_fwd_table": (i32, [vp, vp, vp, ctypes.c_double, vp, vp, vp, vp, i64,
+                                              i64, i64, ctypes.c_float, i32, vp]),
         "xattn_qknorm_rope_bwd_workspace_bytes": (sz, [i64, i64, i64]),
         "xattn_qknorm_rope_bwd": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64,
                                         i32, vp]),
@@ -218,6 +221,16 @@ def xattn_qknorm_rope_fwd(x, gamma, cos_tab, sin_tab, y, rstd, rows, seq_len, he
         _ptr(sin_tab, "sin_tab", torch.float32), _ptr(y, "y", x.dtype),
         _ptr(rstd, "rstd", torch.float32), rows, seq_len, head_dim, float(eps), _io(x, "x"),
         _stream(stream)), "xattn_qknorm_rope_fwd")
+
+
+def xattn_qknorm_rope_fwd_table(x, gamma, positions, theta, cos_tab, sin_tab, y, rstd, rows,
+                                seq_len, head_dim, eps, stream=None):
+    _check(load_library().xattn_qknorm_rope_fwd_table(
+        _ptr(x, "x"), _ptr(gamma, "gamma", torch.float32),
+        None if positions is None else _ptr(positions, "positions", torch.int32), float(theta),
+        _ptr(cos_tab, "cos_tab", torch.float32), _ptr(sin_tab, "sin_tab", torch.float32),
+        _ptr(y, "y", x.dtype), _ptr(rstd, "rstd", torch.float32), rows, seq_len, head_dim,
+        float(eps), _io(x, "x"), _stream(stream)), "xattn_qknorm_rope_fwd_table")
 
 
 def xattn_qknorm_rope_bwd_workspace_bytes(rows, seq_len, head_dim) -> int:
@@ -353,6 +366,19 @@ def qknorm_rope_fwd(x, gamma, cos_tab, sin_tab, eps, stream=None):
     rstd = torch.empty(rows * S, dtype=torch.float32, device=x.device)
     xattn_qknorm_rope_fwd(x, gamma, cos_tab, sin_tab, y, rstd, rows, S, hd, eps, stream)
     return y, rstd
+
+
+def qknorm_rope_fwd_table(x, gamma, theta, eps, positions=None, stream=None):
+    """QK-norm + RoPE of x with the RoPE table built in the same launch: (y, rstd, cos_tab,
+    sin_tab); positions (int32 [S]) restart the angles per row as rope_cache_at does."""
+    rows, S, hd = x.shape
+    y = torch.empty_like(x)
+    rstd = torch.empty(rows * S, dtype=torch.float32, device=x.device)
+    cos_tab = torch.empty(S, hd // 2, dtype=torch.float32, device=x.device)
+    sin_tab = torch.empty_like(cos_tab)
+    xattn_qknorm_rope_fwd_table(x, gamma, positions, theta, cos_tab, sin_tab, y, rstd, rows, S,
+                                hd, eps, stream)
+    return y, rstd, cos_tab, sin_tab
 
 
 def qknorm_rope_bwd(dy, x, gamma, rstd, cos_tab, sin_tab, stream=None, workspace=None):

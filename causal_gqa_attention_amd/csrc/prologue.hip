@@ -16,6 +16,8 @@
 // so each lane moves whole 16-byte vectors; LPR lanes share a row (the first-half chunk
 // and the matching second-half chunk, so each lane owns complete rotation pairs) and the
 // row reduction is a short xor-shuffle within those lanes.
+#include <algorithm>
+
 #include "xattn_device.h"
 #include "xattn_internal.h"
 
@@ -144,6 +146,34 @@ __device__ __forceinline__ void store_from_f32(T* __restrict__ p, const float (&
 // --------------------------------------------------------------------------------------
 // forward
 // --------------------------------------------------------------------------------------
+// The arithmetic of one row for the lane owning columns [c0, c0 + VEC) and the matching
+// second-half columns (a: first-half values, b: second-half values): the row's mean square
+// over its LPR lanes, rstd, then y = rotate(gamma * x * rstd).  Shared by both forward
+// kernels, so they give bitwise the same rows: every product and sum is rounded on its own
+// (no multiply-add contraction, whose choice could differ with the inlining context).
+template <int HD, int VEC>
+__device__ __forceinline__ float qknorm_rope_row(const float (&a)[VEC], const float (&b)[VEC],
+                                                 const float (&g1)[VEC], const float (&g2)[VEC],
+                                                 const float (&cs)[VEC], const float (&sn)[VEC],
+                                                 float eps, float (&o1)[VEC], float (&o2)[VEC]) {
+#pragma clang fp contract(off)
+  constexpr int LPR = (HD / 2) / VEC;
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) ss += a[e] * a[e] + b[e] * b[e];
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) ss += shfl_xor(ss, m);
+  const float r = 1.0f / sqrtf(ss * (1.0f / (float)HD) + eps);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    const float n1 = a[e] * r * g1[e];
+    const float n2 = b[e] * r * g2[e];
+    o1[e] = n1 * cs[e] - n2 * sn[e];
+    o2[e] = n1 * sn[e] + n2 * cs[e];
+  }
+  return r;
+}
+
 // Rows are taken in groups of R heads at one position t (rows h*S + t, h in the group):
 // the lanes of a row group load the position's cos / sin and gamma once and issue the R
 // rows' loads together.  Row groups are numbered with t fastest, so neighbouring groups
@@ -178,20 +208,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_fwd_kernel(
   load_f32<float, VEC>(gamma + HALF + c0, g2);
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) ss += a[j][e] * a[j][e] + b[j][e] * b[j][e];
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) ss += shfl_xor(ss, m);
-    const float r = 1.0f / sqrtf(ss * (1.0f / (float)HD) + eps);
     float o1[VEC], o2[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const float n1 = a[j][e] * r * g1[e];
-      const float n2 = b[j][e] * r * g2[e];
-      o1[e] = n1 * cs[e] - n2 * sn[e];
-      o2[e] = n1 * sn[e] + n2 * cs[e];
-    }
+    const float r = qknorm_rope_row<HD, VEC>(a[j], b[j], g1, g2, cs, sn, eps, o1, o2);
     if (valid) {
       const size_t row = (size_t)(h0 + j) * seq_len + t;
       store_from_f32<T, VEC>(y + row * HD + c0, o1);
@@ -232,6 +250,117 @@ hipError_t launch_qknorm_rope_fwd(IoType io, int head_dim, const void* x, const 
   if (head_dim == HD)                                                                    \
     return fwd_dispatch<T, HD>(x, gamma, cos_tab, sin_tab, y, rstd, nrows, seq_len, eps, \
                                stream);
+  if (io == IO_F32) {
+    XATTN_FWD_CASE(float, 16) XATTN_FWD_CASE(float, 32) XATTN_FWD_CASE(float, 64)
+    XATTN_FWD_CASE(float, 128)
+  } else {
+    XATTN_FWD_CASE(bf16, 16) XATTN_FWD_CASE(bf16, 32) XATTN_FWD_CASE(bf16, 64)
+    XATTN_FWD_CASE(bf16, 128)
+  }
+#undef XATTN_FWD_CASE
+  return hipErrorInvalidValue;
+}
+
+// Prologue forward with the RoPE table built in the same launch.  Block b owns positions
+// [b*P, b*P + P) of every row (P * HD/2 <= 256 table entries, one per thread, evaluated as
+// the table kernels do: one pow and one sincos in fp64, rounded once to fp32), writes them
+// to the table and to LDS, and then normalises and rotates the rows at its positions in
+// passes of 256 / LPR rows.  The first pass's loads are issued before the fp64 work, which
+// runs under them.  Every row and table entry is bitwise what xattn_rope_cache(_at) followed
+// by xattn_qknorm_rope_fwd give.
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void qknorm_rope_fwd_table_kernel(
+    const T* __restrict__ x, const float* __restrict__ gamma, const int* __restrict__ positions,
+    double theta, float* __restrict__ cos_tab, float* __restrict__ sin_tab, T* __restrict__ y,
+    float* __restrict__ rstd, int heads, int seq_len, int P, float eps) {
+  constexpr int VEC = V16<T>::n;
+  constexpr int HALF = HD / 2;
+  constexpr int LPR = HALF / VEC;
+  constexpr int NG = 256 / LPR;  // rows per pass
+  __shared__ float tcs[256], tsn[256];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * P;
+  const int np = min(P, seq_len - t0);  // positions of this block
+  const int nrows = heads * np;         // rows, position fastest: (h, t0 + i) at h * np + i
+  const int g = tid / LPR, part = tid % LPR, c0 = part * VEC;
+  float g1[VEC], g2[VEC];
+  load_f32<float, VEC>(gamma + c0, g1);
+  load_f32<float, VEC>(gamma + HALF + c0, g2);
+  auto row_of = [&](int ri) {
+    const int h = ri / np, i = ri - h * np;
+    return (size_t)h * seq_len + t0 + i;
+  };
+  // first pass's loads
+  float a[VEC], b[VEC];
+  {
+    const size_t row = row_of(g < nrows ? g : 0);
+    load_f32<T, VEC>(x + row * HD + c0, a);
+    load_f32<T, VEC>(x + row * HD + HALF + c0, b);
+  }
+  // table entries of the block's positions: thread tid -> (position tid / HALF, frequency
+  // tid % HALF)
+  if (tid < np * HALF) {
+    const int p = tid / HALF, f = tid % HALF, t = t0 + p;
+    const double inv_freq = pow(theta, -2.0 * (double)f / (double)HD);
+    const int pos = positions != nullptr ? positions[t] : t;
+    double sv, cv;
+    sincos((double)pos * inv_freq, &sv, &cv);
+    tcs[tid] = (float)cv;
+    tsn[tid] = (float)sv;
+    cos_tab[(size_t)t * HALF + f] = (float)cv;
+    sin_tab[(size_t)t * HALF + f] = (float)sv;
+  }
+  __syncthreads();
+  for (int r0 = 0; r0 < nrows; r0 += NG) {
+    const int ri = r0 + g;
+    if (r0 > 0) {
+      const size_t row = row_of(ri < nrows ? ri : 0);
+      load_f32<T, VEC>(x + row * HD + c0, a);
+      load_f32<T, VEC>(x + row * HD + HALF + c0, b);
+    }
+    const int i = (ri < nrows ? ri : 0) % np;  // position within the block
+    float cs[VEC], sn[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      cs[e] = tcs[i * HALF + c0 + e];
+      sn[e] = tsn[i * HALF + c0 + e];
+    }
+    float o1[VEC], o2[VEC];
+    const float r = qknorm_rope_row<HD, VEC>(a, b, g1, g2, cs, sn, eps, o1, o2);
+    if (ri < nrows) {
+      const size_t row = row_of(ri);
+      store_from_f32<T, VEC>(y + row * HD + c0, o1);
+      store_from_f32<T, VEC>(y + row * HD + HALF + c0, o2);
+      if (part == 0) rstd[row] = r;
+    }
+  }
+}
+
+template <typename T, int HD>
+static hipError_t fwd_table_dispatch(const void* x, const float* gamma, const int* positions,
+                                     double theta, float* cos_tab, float* sin_tab, void* y,
+                                     float* rstd, int heads, int seq_len, float eps,
+                                     hipStream_t stream) {
+  constexpr int HALF = HD / 2;
+  constexpr int NG = 256 / (HALF / V16<T>::n);
+  // positions per block: enough for one pass of rows, at most one table entry per thread
+  const int P = std::max(1, std::min(256 / HALF, NG / heads));
+  const int blocks = (seq_len + P - 1) / P;
+  ProfScope prof("qknorm_rope_fwd", stream);
+  hipLaunchKernelGGL((qknorm_rope_fwd_table_kernel<T, HD>), dim3(blocks), dim3(256), 0, stream,
+                     (const T*)x, gamma, positions, theta, cos_tab, sin_tab, (T*)y, rstd, heads,
+                     seq_len, P, eps);
+  return hipPeekAtLastError();
+}
+
+hipError_t launch_qknorm_rope_fwd_table(IoType io, int head_dim, const void* x,
+                                        const float* gamma, const int* positions, double theta,
+                                        float* cos_tab, float* sin_tab, void* y, float* rstd,
+                                        int heads, int seq_len, float eps, hipStream_t stream) {
+#define XATTN_FWD_CASE(T, HD)                                                                \
+  if (head_dim == HD)                                                                        \
+    return fwd_table_dispatch<T, HD>(x, gamma, positions, theta, cos_tab, sin_tab, y, rstd, \
+                                     heads, seq_len, eps, stream);
   if (io == IO_F32) {
     XATTN_FWD_CASE(float, 16) XATTN_FWD_CASE(float, 32) XATTN_FWD_CASE(float, 64)
     XATTN_FWD_CASE(float, 128)

@@ -431,6 +431,42 @@ xattn_status xattn_qknorm_rope_fwd(const void* x, const float* gamma, const floa
   });
 }
 
+xattn_status xattn_qknorm_rope_fwd_table(const void* x, const float* gamma,
+                                         const int32_t* positions, double theta,
+                                         float* cos_tab, float* sin_tab, void* y, float* rstd,
+                                         int64_t rows, int64_t seq_len, int64_t head_dim,
+                                         float eps, int32_t dtype, void* stream) {
+  return guarded([&] {
+    check_ptr(x, "x");
+    check_ptr(gamma, "gamma");
+    if (positions != nullptr) check_ptr(positions, "positions");
+    check_ptr(cos_tab, "cos_tab");
+    check_ptr(sin_tab, "sin_tab");
+    check_ptr(y, "y");
+    check_ptr(rstd, "rstd");
+    check_pos(rows, "rows");
+    check_pos(seq_len, "seq_len");
+    check_head_dim(head_dim);
+    const xattn::IoType io = check_dtype(dtype);
+    if (!(eps >= 0.f) || !std::isfinite(eps))
+      fail(XATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (!(theta > 0.0) || !std::isfinite(theta))
+      fail(XATTN_ERR_INVALID_ARG, "theta must be positive and finite");
+    const int64_t n = count4(rows, seq_len, head_dim, 1, "x");
+    count4(seq_len, head_dim / 2, 1, 1, "rope table");
+    const size_t xb = (size_t)n * io_size(io);
+    const size_t tb = (size_t)seq_len * (head_dim / 2) * 4;
+    check_no_overlap({{y, xb, "y"}, {rstd, (size_t)(rows * seq_len) * 4, "rstd"},
+                      {cos_tab, tb, "cos_tab"}, {sin_tab, tb, "sin_tab"}},
+                     {{x, xb, "x"}, {gamma, (size_t)head_dim * 4, "gamma"},
+                      {positions, positions ? (size_t)seq_len * 4 : 0, "positions"}});
+    hip_check(xattn::launch_qknorm_rope_fwd_table(io, (int)head_dim, x, gamma, positions, theta,
+                                                  cos_tab, sin_tab, y, rstd, (int)rows,
+                                                  (int)seq_len, eps, (hipStream_t)stream),
+              "qknorm_rope_fwd_table launch");
+  });
+}
+
 size_t xattn_qknorm_rope_bwd_workspace_bytes(int64_t rows, int64_t seq_len, int64_t head_dim) {
   if (rows <= 0 || seq_len <= 0 || head_dim <= 0) return 0;
   return (size_t)xattn::qknorm_rope_bwd_blocks(rows * seq_len) * (size_t)head_dim *

@@ -25,6 +25,13 @@ hipError_t launch_qknorm_rope_fwd(IoType io, int head_dim, const void* x, const 
                                   const float* cos_tab, const float* sin_tab, void* y,
                                   float* rstd, int nrows, int seq_len, float eps,
                                   hipStream_t stream);
+// The same rows with the RoPE table built in the launch (written to cos_tab / sin_tab as
+// launch_rope_cache, or launch_rope_cache_at when positions is not null); heads = rows of
+// the [heads, seq_len, head_dim] tensor.
+hipError_t launch_qknorm_rope_fwd_table(IoType io, int head_dim, const void* x,
+                                        const float* gamma, const int* positions, double theta,
+                                        float* cos_tab, float* sin_tab, void* y, float* rstd,
+                                        int heads, int seq_len, float eps, hipStream_t stream);
 
 // Number of per-block dgamma partial rows the backward writes for `nrows` rows.
 int qknorm_rope_bwd_blocks(int64_t nrows);

@@ -1,7 +1,7 @@
 """One step of the hot path over preallocated device buffers.
 
-A step is the whole path once: RoPE cos/sin cache, QK-norm + RoPE on K, attention forward
-(out, lse) with QK-norm + RoPE of Q fused into it, then the backward (delta, dq, dk/dv with
+A step is the whole path once: RoPE cos/sin cache and QK-norm + RoPE on K (one launch),
+attention forward (out, lse) with QK-norm + RoPE of Q fused into it, then the backward (delta, dq, dk/dv with
 the group sum, prologue backward for Q and K, dgamma reductions).  Buffers are allocated once at
 construction with torch (plumbing only); every step runs only libxattn kernels, on one
 stream, with no allocation.
@@ -11,7 +11,7 @@ from __future__ import annotations
 import torch
 
 from . import (Dims, make_dims, segments, xattn_bwd, xattn_bwd_workspace_bytes,
-               xattn_fwd_qnorm, xattn_qknorm_rope_fwd, xattn_rope_cache, xattn_rope_cache_at)
+               xattn_fwd_qnorm, xattn_qknorm_rope_fwd_table)
 
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -66,12 +66,12 @@ class AttentionStep:
 
     def forward(self, stream=None):
         S, hd = self.S, self.hd
-        if self.seg is None:
-            xattn_rope_cache(self.cos, self.sin, S, hd, self.theta, stream)
-        else:
-            xattn_rope_cache_at(self.cos, self.sin, self.seg[2], S, hd, self.theta, stream)
-        xattn_qknorm_rope_fwd(self.xk, self.gamma_k, self.cos, self.sin, self.yk, self.rstd_k,
-                              self.B * self.Hkv, S, hd, self.eps, stream)
+        # RoPE table (positions restart per document when there are documents) and the K
+        # prologue in one launch
+        xattn_qknorm_rope_fwd_table(self.xk, self.gamma_k,
+                                    None if self.seg is None else self.seg[2], self.theta,
+                                    self.cos, self.sin, self.yk, self.rstd_k, self.B * self.Hkv,
+                                    S, hd, self.eps, stream)
         xattn_fwd_qnorm(self.dims, self.xq, self.gamma_q, self.cos, self.sin, self.eps, self.yq,
                         self.rstd_q, self.yk, self.v, self.out, self.lse, stream)
 

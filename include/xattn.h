@@ -131,6 +131,20 @@ xattn_status xattn_qknorm_rope_fwd(const void* x, const float* gamma, const floa
                                    int64_t seq_len, int64_t head_dim, float eps,
                                    int32_t dtype, void* stream);
 
+/* Prologue forward with the RoPE table built in the same launch ([T9] "cos/sin cache",
+ * [MINT] 5.4.2, 5.4.4, 5.4.1 and 5.5.1): writes cos_tab / sin_tab ([seq_len, hd/2] fp32)
+ * exactly as xattn_rope_cache(seq_len, hd, theta) does (positions == NULL) or as
+ * xattn_rope_cache_at(positions, seq_len rows) does (positions: device int32 [seq_len]), and
+ * y, rstd exactly as xattn_qknorm_rope_fwd with that table: bitwise the results of the two
+ * calls, in one launch (the table's fp64 evaluation runs under the rows' loads).  Arguments
+ * as in those two calls; the table is an output here and must not overlap x, gamma, y,
+ * rstd or positions. */
+xattn_status xattn_qknorm_rope_fwd_table(const void* x, const float* gamma,
+                                         const int32_t* positions, double theta,
+                                         float* cos_tab, float* sin_tab, void* y, float* rstd,
+                                         int64_t rows, int64_t seq_len, int64_t head_dim,
+                                         float eps, int32_t dtype, void* stream);
+
 /* Bytes of workspace xattn_qknorm_rope_bwd needs (per-block dgamma partials). */
 size_t xattn_qknorm_rope_bwd_workspace_bytes(int64_t rows, int64_t seq_len, int64_t head_dim);
 

@@ -33,7 +33,7 @@ def lib():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(lib, n), n
     assert "gfx950" in X.xattn_version()
@@ -229,6 +229,24 @@ def test_rope_cache_validation(lib):
     assert f(A, A + MB, 0, 64, 1e4, None) == INVALID
     assert f(A, A + 8, 16, 64, 1e4, None) == INVALID  # tables overlap
     assert f(A, None, 16, 64, 1e4, None) == INVALID
+
+
+def test_prologue_fwd_table_validation(lib):
+    f = lib.xattn_qknorm_rope_fwd_table
+    # x, gamma, positions, theta, cos, sin, y, rstd, rows, S, hd, eps, dtype, stream
+    x, g, cs, sn, y, r = A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB
+    assert f(None, g, None, 1e4, cs, sn, y, r, 4, 16, 64, 1e-5, 0, None) == INVALID
+    assert f(x, g, None, 0.0, cs, sn, y, r, 4, 16, 64, 1e-5, 0, None) == INVALID
+    assert "theta" in last(lib)
+    assert f(x, g, None, 1e4, cs, sn, y, r, 4, 16, 64, -1.0, 0, None) == INVALID
+    assert "eps" in last(lib)
+    assert f(x, g, None, 1e4, cs, sn, y, r, 4, 16, 48, 1e-5, 0, None) == UNSUPPORTED
+    assert f(x, g, None, 1e4, cs, sn, y, r, 4, 0, 64, 1e-5, 0, None) == INVALID
+    assert f(x, g, A + 6 * MB + 2, 1e4, cs, sn, y, r, 4, 16, 64, 1e-5, 0, None) == INVALID
+    # the table is an output: it may not overlap x, another output or the positions
+    assert f(x, g, None, 1e4, x + 64, sn, y, r, 4, 16, 64, 1e-5, 0, None) == INVALID
+    assert f(x, g, None, 1e4, cs, cs + 8, y, r, 4, 16, 64, 1e-5, 0, None) == INVALID
+    assert f(x, g, sn, 1e4, cs, sn, y, r, 4, 16, 64, 1e-5, 0, None) == INVALID
 
 
 def test_prologue_bwd_workspace_and_validation(lib):

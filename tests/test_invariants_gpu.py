@@ -224,3 +224,27 @@ def test_forward_with_fused_q_prologue_matches_separate_calls(wi, dtype):
         d = (yq.float() - yq2.float()).abs()
         ulp = yq2.float().abs().clamp_min(2.0 ** -126) * 2.0 ** -7
         assert bool((d <= ulp).all()), float((d / ulp).max())
+
+
+@pytest.mark.parametrize("dtype,hd,S,rows,docs", [
+    ("f32", 16, 7, 3, None),        # one block, ragged position block
+    ("f32", 128, 100, 8, None),
+    ("bf16", 64, 77, 12, [30, 47]),  # positions restart per document
+    ("bf16", 128, 300, 8, None),     # workload 5's K shape per position block
+    ("bf16", 128, 33, 70, None),     # more rows than one pass: one position per block
+    ("bf16", 32, 513, 5, [1, 500, 12])])
+def test_prologue_with_table_equals_separate_calls(dtype, hd, S, rows, docs):
+    """xattn_qknorm_rope_fwd_table: the table, y and rstd are bitwise those of
+    xattn_rope_cache (or xattn_rope_cache_at) followed by xattn_qknorm_rope_fwd."""
+    note(f"prologue with table {dtype} hd={hd} S={S} rows={rows} docs={docs}")
+    rng = np.random.default_rng(hd * 1000 + S)
+    x = dev(rng.standard_normal((rows, S, hd), dtype=np.float32), dtype)
+    g = dev(1.0 + 0.1 * rng.standard_normal(hd).astype(np.float32), "f32")
+    theta, eps = 1e4 if hd < 128 else 1e6, 1e-6
+    pos = None if docs is None else X.segments(docs)[2]
+    cos, sin = X.rope_cache(S, hd, theta) if pos is None else X.rope_cache_at(pos, hd, theta)
+    y, r = X.qknorm_rope_fwd(x, g, cos, sin, eps)
+    y2, r2, cos2, sin2 = X.qknorm_rope_fwd_table(x, g, theta, eps, positions=pos)
+    torch.cuda.synchronize()
+    for a, b in ((cos, cos2), (sin, sin2), (y, y2), (r, r2)):
+        assert torch.equal(a, b)
