@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark: causal GQA attention fwd+bwd (with the QK-norm + RoPE prologue) on one MI355X.
 
-A step is one pass of the whole hot path over one batch of synthetic input: RoPE cache,
-QK-norm + RoPE on K, attention forward (for bf16 io with QK-norm + RoPE of Q inside it),
+A step is one pass of the whole hot path over one batch of synthetic input: RoPE cache and
+QK-norm + RoPE on K (one launch), attention forward (for bf16 io with QK-norm + RoPE of Q inside it),
 attention backward with the group sum and the prologue backward (for bf16 io applied inside
 the dq and dk/dv kernels' stores), and the dgamma reductions (libxattn kernels only,
 preallocated buffers, one stream).  The workload is the long-context Qwen3-shaped GQA

@@ -261,42 +261,36 @@ hipError_t launch_qknorm_rope_fwd(IoType io, int head_dim, const void* x, const 
   return hipErrorInvalidValue;
 }
 
-// Prologue forward with the RoPE table built in the same launch.  Block b owns positions
-// [b*P, b*P + P) of every row (P * HD/2 <= 256 table entries, one per thread, evaluated as
-// the table kernels do: one pow and one sincos in fp64, rounded once to fp32), writes them
-// to the table and to LDS, and then normalises and rotates the rows at its positions in
-// passes of 256 / LPR rows.  The first pass's loads are issued before the fp64 work, which
-// runs under them.  Every row and table entry is bitwise what xattn_rope_cache(_at) followed
-// by xattn_qknorm_rope_fwd give.
+// Prologue forward with the RoPE table built in the same launch.  Block (bx, by) owns
+// positions [bx*P, bx*P + P) of head rows [by*HB, by*HB + HB): at most 256 / LPR rows, one
+// pass, its loads issued first.  Under them it evaluates the table entries of its positions
+// (P * HD/2 <= 256, one per thread, as the table kernels do: one pow and one sincos in fp64,
+// rounded once to fp32) into LDS; blocks with by == 0 also write them to the table.  Then it
+// normalises and rotates its rows.  Every row and table entry is bitwise what
+// xattn_rope_cache(_at) followed by xattn_qknorm_rope_fwd give.
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void qknorm_rope_fwd_table_kernel(
     const T* __restrict__ x, const float* __restrict__ gamma, const int* __restrict__ positions,
     double theta, float* __restrict__ cos_tab, float* __restrict__ sin_tab, T* __restrict__ y,
-    float* __restrict__ rstd, int heads, int seq_len, int P, float eps) {
+    float* __restrict__ rstd, int heads, int seq_len, int P, int HB, float eps) {
   constexpr int VEC = V16<T>::n;
   constexpr int HALF = HD / 2;
   constexpr int LPR = HALF / VEC;
-  constexpr int NG = 256 / LPR;  // rows per pass
   __shared__ float tcs[256], tsn[256];
   const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * P;
+  const int t0 = blockIdx.x * P, h0 = blockIdx.y * HB;
   const int np = min(P, seq_len - t0);  // positions of this block
-  const int nrows = heads * np;         // rows, position fastest: (h, t0 + i) at h * np + i
+  const int nh = min(HB, heads - h0);   // head rows of this block
+  const int nrows = nh * np;            // (h0 + k / np, t0 + k % np) for k < nrows
   const int g = tid / LPR, part = tid % LPR, c0 = part * VEC;
-  float g1[VEC], g2[VEC];
+  const int k = g < nrows ? g : 0;      // lanes past the rows redo row 0 and store nothing
+  const int i = k % np;
+  const size_t row = (size_t)(h0 + k / np) * seq_len + t0 + i;
+  float a[VEC], b[VEC], g1[VEC], g2[VEC];
+  load_f32<T, VEC>(x + row * HD + c0, a);
+  load_f32<T, VEC>(x + row * HD + HALF + c0, b);
   load_f32<float, VEC>(gamma + c0, g1);
   load_f32<float, VEC>(gamma + HALF + c0, g2);
-  auto row_of = [&](int ri) {
-    const int h = ri / np, i = ri - h * np;
-    return (size_t)h * seq_len + t0 + i;
-  };
-  // first pass's loads
-  float a[VEC], b[VEC];
-  {
-    const size_t row = row_of(g < nrows ? g : 0);
-    load_f32<T, VEC>(x + row * HD + c0, a);
-    load_f32<T, VEC>(x + row * HD + HALF + c0, b);
-  }
   // table entries of the block's positions: thread tid -> (position tid / HALF, frequency
   // tid % HALF)
   if (tid < np * HALF) {
@@ -307,32 +301,24 @@ __global__ __launch_bounds__(256) void qknorm_rope_fwd_table_kernel(
     sincos((double)pos * inv_freq, &sv, &cv);
     tcs[tid] = (float)cv;
     tsn[tid] = (float)sv;
-    cos_tab[(size_t)t * HALF + f] = (float)cv;
-    sin_tab[(size_t)t * HALF + f] = (float)sv;
+    if (blockIdx.y == 0) {
+      cos_tab[(size_t)t * HALF + f] = (float)cv;
+      sin_tab[(size_t)t * HALF + f] = (float)sv;
+    }
   }
   __syncthreads();
-  for (int r0 = 0; r0 < nrows; r0 += NG) {
-    const int ri = r0 + g;
-    if (r0 > 0) {
-      const size_t row = row_of(ri < nrows ? ri : 0);
-      load_f32<T, VEC>(x + row * HD + c0, a);
-      load_f32<T, VEC>(x + row * HD + HALF + c0, b);
-    }
-    const int i = (ri < nrows ? ri : 0) % np;  // position within the block
-    float cs[VEC], sn[VEC];
+  float cs[VEC], sn[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      cs[e] = tcs[i * HALF + c0 + e];
-      sn[e] = tsn[i * HALF + c0 + e];
-    }
-    float o1[VEC], o2[VEC];
-    const float r = qknorm_rope_row<HD, VEC>(a, b, g1, g2, cs, sn, eps, o1, o2);
-    if (ri < nrows) {
-      const size_t row = row_of(ri);
-      store_from_f32<T, VEC>(y + row * HD + c0, o1);
-      store_from_f32<T, VEC>(y + row * HD + HALF + c0, o2);
-      if (part == 0) rstd[row] = r;
-    }
+  for (int e = 0; e < VEC; ++e) {
+    cs[e] = tcs[i * HALF + c0 + e];
+    sn[e] = tsn[i * HALF + c0 + e];
+  }
+  float o1[VEC], o2[VEC];
+  const float r = qknorm_rope_row<HD, VEC>(a, b, g1, g2, cs, sn, eps, o1, o2);
+  if (g < nrows) {
+    store_from_f32<T, VEC>(y + row * HD + c0, o1);
+    store_from_f32<T, VEC>(y + row * HD + HALF + c0, o2);
+    if (part == 0) rstd[row] = r;
   }
 }
 
@@ -342,14 +328,16 @@ static hipError_t fwd_table_dispatch(const void* x, const float* gamma, const in
                                      float* rstd, int heads, int seq_len, float eps,
                                      hipStream_t stream) {
   constexpr int HALF = HD / 2;
-  constexpr int NG = 256 / (HALF / V16<T>::n);
-  // positions per block: enough for one pass of rows, at most one table entry per thread
+  constexpr int NG = 256 / (HALF / V16<T>::n);  // rows per block
+  // positions per block: as many as leave one row group per head row (at most one table
+  // entry per thread); head rows per block: the rest of the block
   const int P = std::max(1, std::min(256 / HALF, NG / heads));
-  const int blocks = (seq_len + P - 1) / P;
+  const int HB = std::max(1, NG / P);
+  const dim3 grid((seq_len + P - 1) / P, (heads + HB - 1) / HB);
   ProfScope prof("qknorm_rope_fwd", stream);
-  hipLaunchKernelGGL((qknorm_rope_fwd_table_kernel<T, HD>), dim3(blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL((qknorm_rope_fwd_table_kernel<T, HD>), grid, dim3(256), 0, stream,
                      (const T*)x, gamma, positions, theta, cos_tab, sin_tab, (T*)y, rstd, heads,
-                     seq_len, P, eps);
+                     seq_len, P, HB, eps);
   return hipPeekAtLastError();
 }
 
