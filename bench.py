@@ -127,6 +127,16 @@ def kernel_units(w, docs=None):
     }
 
 
+def executed_work(w, docs=None):
+    """Flops of the products each MFMA kernel executes, recomputation included: not the
+    metric, but the matrix units' own rate, reported next to the algorithmic one."""
+    pairs = doc_pairs(w, docs) * w.bh
+    hd = w.head_dim
+    return {"attn_fwd": (4 * hd * pairs, "QK^T, PV"),
+            "attn_bwd_dkdv": (8 * hd * pairs, "S recompute, dP, dV, dK"),
+            "attn_bwd_dq": (6 * hd * pairs, "S and dP recompute, dQ")}
+
+
 def traffic_for(kernel, name):
     """HBM bytes per launch from the committed counter summary, if it was taken on the
     current kernel source for this workload; else None."""
@@ -581,6 +591,7 @@ def main():
     prof = X.xattn_profile_stop()
     prof_ms = (time.perf_counter() - tp0) * 1e3 / args.steps
     units = kernel_units(w, docs)
+    executed = executed_work(w, docs)
     kernels = {}
     for name, (n, tot) in prof.items():
         avg = tot / max(n, 1)
@@ -590,6 +601,9 @@ def main():
             bound, work, _ = units[name]
             if bound == "mfma":
                 k["tflops"] = work / (avg * 1e-3) / 1e12
+                ex, basis = executed[name]
+                k["executed_tflops"] = ex / (avg * 1e-3) / 1e12
+                k["executed_basis"] = basis
             else:
                 k["gbs"] = work / (avg * 1e-3) / 1e9
         kernels[name] = k

@@ -78,3 +78,15 @@ def test_gpus_above_one_exits_with_a_message(bench, monkeypatch, capsys):
         bench.main()
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_executed_work_counts_the_recomputation(bench):
+    import workloads as W
+    w = W.WORKLOADS[5]
+    alg, ex = bench.kernel_units(w), bench.executed_work(w)
+    assert ex["attn_fwd"][0] == alg["attn_fwd"][1]
+    assert ex["attn_bwd_dq"][0] == 3 * alg["attn_bwd_dq"][1]
+    assert 3 * ex["attn_bwd_dkdv"][0] == 4 * alg["attn_bwd_dkdv"][1]
+    # the step's headline counts 12 * hd per causal pair: forward + dk/dv + dq algorithmic
+    total = sum(alg[k][1] for k in ("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq"))
+    assert total == 12 * w.head_dim * w.causal_pairs() * w.bh
