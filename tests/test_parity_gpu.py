@@ -183,3 +183,21 @@ def test_prologue_matches_oracle_every_row(idx):
         assert_close(f"rstd{name}", host(rstd), rr.reshape(-1), tol)
         assert_close(f"dx{name}", host(dx), rdx, tol)
         assert_close(f"dgamma{name}", host(dg), rdg, tol)
+
+
+@pytest.mark.parametrize("wi,kw", [(5, dict(seq_len=300)), (4, dict(batch=2, seq_len=190)),
+                                   (3, dict(batch=1, seq_len=257))])
+def test_bf16_kernels_agree_with_the_fp32_kernels(wi, kw):
+    """Cross-path gate (the pages' flash == composed check, here between two independent
+    kernel sets): the bf16 kernels (bf16 io, fused prologue) and the generic fp32 kernels,
+    run on the same bf16-valued inputs, agree within the bf16 band on every output."""
+    w = W.WORKLOADS[wi].replace(**kw)
+    x = W.make_inputs(w)  # bf16-valued inputs
+    note(f"cross-path bf16 vs f32 {w}")
+    gb = run_step(w, x)
+    gf = run_step(w.replace(dtype="f32"), x)
+    S = w.seq_len
+    for n in ("yq", "yk", "rstd_q", "rstd_k", "out", "dxq", "dxk", "dv", "dgamma_q",
+              "dgamma_k", "cos", "sin"):
+        assert_close(n, gb[n], gf[n], TOL["bf16"])
+    assert_close("lse", gb["lse"].reshape(-1, S), gf["lse"].reshape(-1, S), TOL["bf16"])
