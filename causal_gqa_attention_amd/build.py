@@ -2,7 +2,7 @@
 
 Usage: python -m causal_gqa_attention_amd.build   (or build() from Python).
 Objects go to _build/ at the repository root; the shared library is written next to
-this file so the binding (and a GPU machine receiving the tree) finds it.
+this file, where the binding loads it (a copy of the tree carries it along).
 """
 from __future__ import annotations
 
