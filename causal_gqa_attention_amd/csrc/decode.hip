@@ -24,6 +24,8 @@
 // Two launches: split attention (with prologue and append), combine.
 #include <math.h>
 
+#include <type_traits>
+
 #include "xattn_device.h"
 #include "xattn_internal.h"
 
@@ -54,6 +56,35 @@ __device__ __forceinline__ float dpp(float v) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
+// The value of lane l ^ M (M a power of two up to 32) without an LDS round trip: DPP within
+// a 16-lane row (quad permutations; quad reversal then the half-row mirror for 4; a rotation
+// by 8), v_permlane16_swap / v_permlane32_swap across rows.
+template <int M>
+__device__ __forceinline__ float xor_lanes(float v) {
+  if constexpr (M == 1) {
+    return dpp<0xB1>(v);  // quad_perm [1, 0, 3, 2]
+  } else if constexpr (M == 2) {
+    return dpp<0x4E>(v);  // quad_perm [2, 3, 0, 1]
+  } else if constexpr (M == 4) {
+    return dpp<0x141>(dpp<0x1B>(v));  // quad_perm [3, 2, 1, 0], then row_half_mirror
+  } else if constexpr (M == 8) {
+    return dpp<0x128>(v);  // row_ror:8
+  } else {
+    static_assert(M == 16 || M == 32, "xor of a power of two up to 32");
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const int lane = __lane_id();
+    if constexpr (M == 16) {
+      // result 0: lane l holds lane (l & ~16); result 1: lane (l | 16)
+      const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      return __builtin_bit_cast(float, (unsigned)((lane & 16) ? r[0] : r[1]));
+    } else {
+      // result 0: lane l holds lane (l & 31); result 1: lane (l | 32)
+      const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      return __builtin_bit_cast(float, (unsigned)((lane & 32) ? r[0] : r[1]));
+    }
+  }
+}
+
 // Sum over each aligned group of N consecutive lanes (N a power of two up to 64), the same
 // bits in every lane of the group: DPP quad permutations, the half-row and row mirrors
 // (each pairs a lane with one in the other half of its 8- or 16-lane group), then xor
@@ -64,8 +95,8 @@ __device__ __forceinline__ float lane_group_sum(float v) {
   if constexpr (N >= 4) v += dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
   if constexpr (N >= 8) v += dpp<0x141>(v);  // row_half_mirror
   if constexpr (N >= 16) v += dpp<0x140>(v); // row_mirror
-  if constexpr (N >= 32) v += shfl_xor(v, 16);
-  if constexpr (N >= 64) v += shfl_xor(v, 32);
+  if constexpr (N >= 32) v += xor_lanes<16>(v);
+  if constexpr (N >= 64) v += xor_lanes<32>(v);
   return v;
 }
 
@@ -114,7 +145,7 @@ __device__ __forceinline__ void prologue_lanes(const T* __restrict__ xrow,
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     const float n = x[e] * r * g[e];
-    const float m = shfl_xor(n, PH);  // the pair's other member
+    const float m = xor_lanes<PH>(n);  // the pair's other member
     const float n1 = first ? n : m, n2 = first ? m : n;
     const float v = first ? n1 * cs[e] - n2 * sn[e] : n1 * sn[e] + n2 * cs[e];
     y[e] = to_f32(from_f32<T>(v));
@@ -141,6 +172,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int R = group * a.Sq, Lk = a.pos + a.Sq;
   const int k0 = sp * a.ks, k1 = min(Lk, k0 + a.ks);
   const int part = lane % LPK, kg = lane / LPK;
+  // a wave whose range holds no new token issues its first loads now, under the prologue
+  const int n0 = max(k0, a.pos);
+  const bool appends = n0 < k1;  // wave-uniform
+  const T* kc = static_cast<const T*>(a.k_cache) + (size_t)bkv * a.cap * HD + part * VEC;
+  const T* vc = static_cast<const T*>(a.v_cache) + (size_t)bkv * a.cap * HD + part * VEC;
+
+  // the lane's 16 bytes of UN key / value rows; the next group's loads are issued before
+  // the current group's arithmetic
+  vec16_t<T> kv[UN], vv[UN], kn[UN], vn[UN];
+  auto load_group = [&](int j0, vec16_t<T> (&kk)[UN], vec16_t<T> (&vk)[UN]) {
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int j = j0 + u * KPW + kg;
+      const size_t jr = (size_t)(j < k1 ? j : k0) * HD;  // past the range: a row of it
+      kk[u] = load16(kc + jr);
+      vk[u] = load16(vc + jr);
+    }
+  };
+  if (!appends) load_group(k0, kv, vv);
 
   float q[RM][VEC];
   int lim[RM];  // last visible cache row of each query row (-1: padding row)
@@ -162,8 +212,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   // Append: the new tokens' rows of this range (cache rows pos .. pos + Sq - 1 that fall in
   // [k0, k1)) get the rotated key and the value, KPW rows per pass; then the stores are
   // made visible to this wave's own loads below.
-  const int n0 = max(k0, a.pos);
-  if (n0 < k1) {  // wave-uniform
+  if (appends) {
     for (int j0 = n0; j0 < k1; j0 += KPW) {
       const int j = j0 + kg;
       const int i = (j < k1 ? j : n0) - a.pos;  // token (clamped for idle lanes)
@@ -181,6 +230,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    load_group(k0, kv, vv);
   }
   float m[RM], l[RM], o[RM][VEC];
 #pragma unroll
@@ -190,22 +240,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) o[r][e] = 0.f;
   }
-  const T* kc = static_cast<const T*>(a.k_cache) + (size_t)bkv * a.cap * HD + part * VEC;
-  const T* vc = static_cast<const T*>(a.v_cache) + (size_t)bkv * a.cap * HD + part * VEC;
-
-  // the lane's 16 bytes of UN key / value rows; the next group's loads are issued before
-  // the current group's arithmetic
-  vec16_t<T> kv[UN], vv[UN], kn[UN], vn[UN];
-  auto load_group = [&](int j0, vec16_t<T> (&kk)[UN], vec16_t<T> (&vk)[UN]) {
-#pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const int j = j0 + u * KPW + kg;
-      const size_t jr = (size_t)(j < k1 ? j : k0) * HD;  // past the range: a row of it
-      kk[u] = load16(kc + jr);
-      vk[u] = load16(vc + jr);
-    }
-  };
-  load_group(k0, kv, vv);
   for (int j0 = k0; j0 < k1; j0 += KPW * UN) {
     if (j0 + KPW * UN < k1) load_group(j0 + KPW * UN, kn, vn);  // wave-uniform
     int jj[UN];
@@ -232,13 +266,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       // reference point: mn, or 0 while this lane group has seen no visible key (then
       // every term below is exp2(-inf) = 0 and the state stays empty)
       const float mref = mn == -INFINITY ? 0.f : mn;
-      const float alpha = exp2f(m[r] - mref);  // 0 when m was -inf
+      const float alpha = fast_exp2(m[r] - mref);  // 0 when m was -inf
       l[r] *= alpha;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) o[r][e] *= alpha;
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
-        const float p = exp2f(s[u] - mref);  // 0 for masked keys
+        const float p = fast_exp2(s[u] - mref);  // 0 for masked keys
         l[r] += p;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) o[r][e] += p * to_f32(vv[u][e]);
@@ -254,24 +288,32 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   }
 
   // merge the lane groups (same columns, other keys): fixed xor butterfly
+  auto merge = [&](auto mask_tag) {
+    constexpr int MSK = decltype(mask_tag)::value;
+    if constexpr (MSK >= LPK && MSK < 64) {
 #pragma unroll
-  for (int msk = LPK; msk < 64; msk <<= 1) {
+      for (int r = 0; r < RM; ++r) {
+        if (r >= R) continue;  // wave-uniform
+        const float mp = xor_lanes<MSK>(m[r]), lp = xor_lanes<MSK>(l[r]);
+        const float mn = fmaxf(m[r], mp);
+        const float a1 = m[r] == -INFINITY ? 0.f : fast_exp2(m[r] - mn);
+        const float a2 = mp == -INFINITY ? 0.f : fast_exp2(mp - mn);
+        l[r] = l[r] * a1 + lp * a2;
 #pragma unroll
-    for (int r = 0; r < RM; ++r) {
-      if (r >= R) continue;  // wave-uniform
-      const float mp = shfl_xor(m[r], msk), lp = shfl_xor(l[r], msk);
-      const float mn = fmaxf(m[r], mp);
-      const float a1 = m[r] == -INFINITY ? 0.f : exp2f(m[r] - mn);
-      const float a2 = mp == -INFINITY ? 0.f : exp2f(mp - mn);
-      l[r] = l[r] * a1 + lp * a2;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float op = shfl_xor(o[r][e], msk);
-        o[r][e] = o[r][e] * a1 + op * a2;
+        for (int e = 0; e < VEC; ++e) {
+          const float op = xor_lanes<MSK>(o[r][e]);
+          o[r][e] = o[r][e] * a1 + op * a2;
+        }
+        m[r] = mn;
       }
-      m[r] = mn;
     }
-  }
+  };
+  merge(std::integral_constant<int, 1>{});
+  merge(std::integral_constant<int, 2>{});
+  merge(std::integral_constant<int, 4>{});
+  merge(std::integral_constant<int, 8>{});
+  merge(std::integral_constant<int, 16>{});
+  merge(std::integral_constant<int, 32>{});
   if (kg != 0) return;
   const size_t base = ((size_t)bkv * a.nsplit + sp) * R;
   {
@@ -300,8 +342,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 // ranges' sums and partial accumulators added in range order.
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  v = fmaxf(v, xor_lanes<32>(v));
+  v = fmaxf(v, xor_lanes<16>(v));
+  v = fmaxf(v, xor_lanes<8>(v));
+  v = fmaxf(v, xor_lanes<4>(v));
+  v = fmaxf(v, xor_lanes<2>(v));
+  v = fmaxf(v, xor_lanes<1>(v));
   return v;
 }
 
@@ -326,7 +372,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   for (int sp = 0; sp < a.nsplit; ++sp) {
     const size_t idx = base + (size_t)sp * R;
     const float ms = a.part_ml[idx * 2];
-    const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
     L += a.part_ml[idx * 2 + 1] * f;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
