@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ q,
         sv[i] = x;
         tmax = fmaxf(tmax, x);
       }
-      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+      tmax = fmaxf(tmax, xor_lanes<32>(tmax));
       const float m_new = fmaxf(m_run, tmax);
       // a row that has seen no visible key yet (possible with documents) stays empty
       const float m_ref = m_new == -INFINITY ? 0.f : m_new;
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ q,
     }
   }
 
-  l_run += shfl_xor(l_run, 32);
+  l_run += xor_lanes<32>(l_run);
   if (qrow < S) {
     store_column<T, HD, C::NDT>(out + ((size_t)bh * S + qrow) * HD, o, 1.0f / l_run, h);
     if (h == 0) lse[(size_t)bh * S + qrow] = (m_run + log2f(l_run)) * kLn2;
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int j = 0; j < C::VEC; ++j) dsum += to_f32(df[c][j]) * to_f32(of[c][j]);
   }
-  const float D = dsum + shfl_xor(dsum, 32);
+  const float D = dsum + xor_lanes<32>(dsum);
   const float lse2 = qrow < S ? lse[(size_t)bh * S + qrow] * kLog2e : 0.f;
   if (qrow < S && h == 0) delta[(size_t)bh * S + qrow] = D;
 

@@ -376,7 +376,7 @@ __device__ __forceinline__ void halving_sum(float (&v)[NV], int lane) {
   for (int k = 0; k < H; ++k) {
     const float keep = up ? v[k + H] : v[k];
     const float send = up ? v[k] : v[k + H];
-    v[k] = keep + shfl_xor(send, M);
+    v[k] = keep + xor_lanes<M>(send);
   }
   if constexpr (M > MLAST) halving_sum<NV, H, M / 2, MLAST>(v, lane);
 }

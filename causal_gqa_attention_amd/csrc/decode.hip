@@ -50,51 +50,16 @@ struct DecodeArgs {
   float eps, scale_log2;
 };
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
-// The value of lane l ^ M (M a power of two up to 32) without an LDS round trip: DPP within
-// a 16-lane row (quad permutations; quad reversal then the half-row mirror for 4; a rotation
-// by 8), v_permlane16_swap / v_permlane32_swap across rows.
-template <int M>
-__device__ __forceinline__ float xor_lanes(float v) {
-  if constexpr (M == 1) {
-    return dpp<0xB1>(v);  // quad_perm [1, 0, 3, 2]
-  } else if constexpr (M == 2) {
-    return dpp<0x4E>(v);  // quad_perm [2, 3, 0, 1]
-  } else if constexpr (M == 4) {
-    return dpp<0x141>(dpp<0x1B>(v));  // quad_perm [3, 2, 1, 0], then row_half_mirror
-  } else if constexpr (M == 8) {
-    return dpp<0x128>(v);  // row_ror:8
-  } else {
-    static_assert(M == 16 || M == 32, "xor of a power of two up to 32");
-    const unsigned u = __builtin_bit_cast(unsigned, v);
-    const int lane = __lane_id();
-    if constexpr (M == 16) {
-      // result 0: lane l holds lane (l & ~16); result 1: lane (l | 16)
-      const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-      return __builtin_bit_cast(float, (unsigned)((lane & 16) ? r[0] : r[1]));
-    } else {
-      // result 0: lane l holds lane (l & 31); result 1: lane (l | 32)
-      const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-      return __builtin_bit_cast(float, (unsigned)((lane & 32) ? r[0] : r[1]));
-    }
-  }
-}
-
 // Sum over each aligned group of N consecutive lanes (N a power of two up to 64), the same
 // bits in every lane of the group: DPP quad permutations, the half-row and row mirrors
 // (each pairs a lane with one in the other half of its 8- or 16-lane group), then xor
 // exchanges across rows.
 template <int N>
 __device__ __forceinline__ float lane_group_sum(float v) {
-  if constexpr (N >= 2) v += dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-  if constexpr (N >= 4) v += dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-  if constexpr (N >= 8) v += dpp<0x141>(v);  // row_half_mirror
-  if constexpr (N >= 16) v += dpp<0x140>(v); // row_mirror
+  if constexpr (N >= 2) v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  if constexpr (N >= 4) v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  if constexpr (N >= 8) v += dpp_mov<0x141>(v);  // row_half_mirror
+  if constexpr (N >= 16) v += dpp_mov<0x140>(v); // row_mirror
   if constexpr (N >= 32) v += xor_lanes<16>(v);
   if constexpr (N >= 64) v += xor_lanes<32>(v);
   return v;

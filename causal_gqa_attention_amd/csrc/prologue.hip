@@ -161,8 +161,7 @@ __device__ __forceinline__ float qknorm_rope_row(const float (&a)[VEC], const fl
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) ss += a[e] * a[e] + b[e] * b[e];
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) ss += shfl_xor(ss, m);
+  ss = xor_sum_up<LPR>(ss);
   const float r = 1.0f / sqrtf(ss * (1.0f / (float)HD) + eps);
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
@@ -445,8 +444,7 @@ __device__ __forceinline__ void qknorm_rope_bwd_block(const BwdJob& jb, int blk,
         n2[e] = -d1[j][e] * sn[e] + d2[j][e] * cs[e];
         dot += g1[e] * n1[e] * x1[j][e] + g2[e] * n2[e] * x2[j][e];
       }
-#pragma unroll
-      for (int m = 1; m < LPR; m <<= 1) dot += shfl_xor(dot, m);
+      dot = xor_sum_up<LPR>(dot);
       const float coef = dot * r * r * r * (1.0f / (float)HD);
       float o1[VEC], o2[VEC];
 #pragma unroll
@@ -507,8 +505,7 @@ __global__ __launch_bounds__(256) void dgamma_reduce_kernel(BwdJob j0, BwdJob j1
   const float* p = jb.partials + (size_t)col * jb.nblocks;
   float s = 0.f;
   for (int b = lane; b < jb.nblocks; b += 64) s += p[b];
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) s += shfl_xor(s, m);
+  s = xor_sum_down<64>(s);
   if (lane == 0) jb.dgamma[col] = s;
 }
 
@@ -614,8 +611,7 @@ __global__ __launch_bounds__(256) void dgamma_reduce_wide_kernel(const float* __
   float s = 0.f;
 #pragma unroll 8
   for (int b = tid; b < n; b += 256) s += p[b];
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) s += shfl_xor(s, m);
+  s = xor_sum_down<64>(s);
   if ((tid & 63) == 0) wsum[tid >> 6] = s;
   __syncthreads();
   if (tid == 0) (second ? gk : gq)[col] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];

@@ -90,4 +90,54 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// v moved across lanes by the DPP control CTRL (lanes outside the pattern read 0).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// The value of lane l ^ M (M a power of two up to 32) without an LDS round trip: DPP within
+// a 16-lane row (quad permutations; quad reversal then the half-row mirror for 4; a rotation
+// by 8), v_permlane16_swap / v_permlane32_swap across rows.
+template <int M>
+__device__ __forceinline__ float xor_lanes(float v) {
+  if constexpr (M == 1) {
+    return dpp_mov<0xB1>(v);  // quad_perm [1, 0, 3, 2]
+  } else if constexpr (M == 2) {
+    return dpp_mov<0x4E>(v);  // quad_perm [2, 3, 0, 1]
+  } else if constexpr (M == 4) {
+    return dpp_mov<0x141>(dpp_mov<0x1B>(v));  // quad_perm [3, 2, 1, 0], then row_half_mirror
+  } else if constexpr (M == 8) {
+    return dpp_mov<0x128>(v);  // row_ror:8
+  } else {
+    static_assert(M == 16 || M == 32, "xor of a power of two up to 32");
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const int lane = __lane_id();
+    if constexpr (M == 16) {
+      // result 0: lane l holds lane (l & ~16); result 1: lane (l | 16)
+      const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      return __builtin_bit_cast(float, (unsigned)((lane & 16) ? r[0] : r[1]));
+    } else {
+      // result 0: lane l holds lane (l & 31); result 1: lane (l | 32)
+      const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      return __builtin_bit_cast(float, (unsigned)((lane & 32) ? r[0] : r[1]));
+    }
+  }
+}
+
+// Sum over groups of N consecutive lanes (N a power of two up to 64) by xor exchanges of
+// increasing distance: 1, 2, ..., N/2 (the same order as a shuffle loop over those masks).
+template <int N, int M = 1>
+__device__ __forceinline__ float xor_sum_up(float v) {
+  if constexpr (M < N) return xor_sum_up<N, 2 * M>(v + xor_lanes<M>(v));
+  else return v;
+}
+// The same with decreasing distances N/2, ..., 1.
+template <int N>
+__device__ __forceinline__ float xor_sum_down(float v) {
+  if constexpr (N > 1) return xor_sum_down<N / 2>(v + xor_lanes<N / 2>(v));
+  else return v;
+}
+
 }  // namespace xattn
