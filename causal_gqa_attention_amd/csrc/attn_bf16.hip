@@ -45,6 +45,16 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef __attribute__((address_space(3))) const bf16x8 lds_cbf16x8_t;
+typedef __attribute__((address_space(3))) const char lds_cchar_t;
+using lptr = lds_cchar_t*;  // LDS operand tiles are read through LDS-typed pointers
+
+// LDS address of a generic pointer into LDS: its low 32 bits.  Taken once per buffer, so
+// the offsets added after it fold into the LDS instructions, and without the null test
+// that an address-space cast of a generic pointer carries.
+__device__ __forceinline__ lptr to_lds(const char* p) {
+  return (lptr)(uintptr_t)(uint32_t)(uintptr_t)p;
+}
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 // Swizzled bf16 tile rows of HD elements (ROWB bytes): physical 16-byte chunk =
@@ -79,15 +89,15 @@ struct Lay {
 };
 
 template <int HD>
-__device__ __forceinline__ bf16x8 lds_a(const char* base, uint32_t al, int c) {
-  return *reinterpret_cast<const bf16x8*>(base + (al ^ (uint32_t)(c << 5)));
+__device__ __forceinline__ bf16x8 lds_a(lptr base, uint32_t al, int c) {
+  return *(lds_cbf16x8_t*)(base + (al ^ (uint32_t)(c << 5)));
 }
 
 template <int HD>
-__device__ __forceinline__ bf16x8 lds_t(const char* base, uint32_t tl, int c2, int dt) {
+__device__ __forceinline__ bf16x8 lds_t(lptr base, uint32_t tl, int c2, int dt) {
   constexpr int ROWB = Lay<HD>::ROWB;
-  const char* p0 = base + 16 * c2 * ROWB + (tl ^ (uint32_t)((4 * dt) << 4));
-  const char* p1 = base + (16 * c2 + 8) * ROWB + (tl ^ (uint32_t)(((4 * dt) ^ 2) << 4));
+  lptr p0 = base + 16 * c2 * ROWB + (tl ^ (uint32_t)((4 * dt) << 4));
+  lptr p1 = base + (16 * c2 + 8) * ROWB + (tl ^ (uint32_t)(((4 * dt) ^ 2) << 4));
   const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p0));
   const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p1));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -95,7 +105,7 @@ __device__ __forceinline__ bf16x8 lds_t(const char* base, uint32_t tl, int c2, i
 
 // sum over hd of tile rows (base = row R0) with the lane's register fragment
 template <int HD>
-__device__ __forceinline__ f32x16 contract_rows(const char* base, uint32_t al,
+__device__ __forceinline__ f32x16 contract_rows(lptr base, uint32_t al,
                                                 const bf16x8 (&frag)[HD / 16]) {
   f32x16 acc = zero16();
 #pragma unroll
@@ -106,12 +116,12 @@ __device__ __forceinline__ f32x16 contract_rows(const char* base, uint32_t al,
 // The lane's row operands (rows R0 + lane%32, all hd) and transposed operands (the 8 k-slots
 // of every 32-column block) of a 32-row tile, read into registers ahead of their MFMAs.
 template <int HD>
-__device__ __forceinline__ void rows_of(bf16x8 (&x)[HD / 16], const char* base, uint32_t al) {
+__device__ __forceinline__ void rows_of(bf16x8 (&x)[HD / 16], lptr base, uint32_t al) {
 #pragma unroll
   for (int c = 0; c < HD / 16; ++c) x[c] = lds_a<HD>(base, al, c);
 }
 template <int HD>
-__device__ __forceinline__ void tr_of(bf16x8 (&x)[2][HD / 32], const char* base, uint32_t tl) {
+__device__ __forceinline__ void tr_of(bf16x8 (&x)[2][HD / 32], lptr base, uint32_t tl) {
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
@@ -120,7 +130,7 @@ __device__ __forceinline__ void tr_of(bf16x8 (&x)[2][HD / 32], const char* base,
 
 // acc[dt] += (tile rows R0..R0+31, transposed) x (two packed 8-slot operands)
 template <int HD>
-__device__ __forceinline__ void acc_tr(f32x16 (&acc)[HD / 32], const char* base, uint32_t tl,
+__device__ __forceinline__ void acc_tr(f32x16 (&acc)[HD / 32], lptr base, uint32_t tl,
                                        const bf16x8 (&pb)[2]) {
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2)
@@ -193,7 +203,7 @@ template <int PER>
 __device__ __forceinline__ void dma16_rows(void* dst, const char* gbase, uint32_t nbytes,
                                            const uint32_t (&voff)[PER]) {
   // every operand is wave-uniform; readfirstlane keeps them in scalar registers
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)dst);
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
   const uint64_t ga = (uint64_t)(uintptr_t)gbase;
   i32x4 rsrc;  // base, stride 0, nbytes, raw 32-bit format
   rsrc[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)ga);
@@ -236,7 +246,7 @@ __device__ __forceinline__ void dma16_rows(void* dst, const char* gbase, uint32_
 #undef XATTN_TAIL
 }
 __device__ __forceinline__ void dma4(void* dst, const float* gaddr) {
-  const uint32_t m0v = (uint32_t)(uintptr_t)(lds_void_t*)dst;
+  const uint32_t m0v = (uint32_t)(uintptr_t)dst;
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
@@ -559,6 +569,43 @@ struct SoftmaxState {
   float m, l;
 };
 
+// Index range test on a 32x32 score tile: accumulator i of a lane sits at tile index
+// base + c(i), c(i) = 8 (i / 4) + i % 4, where base is the tile origin plus 4 for the upper
+// half-wave.  keep(i) is lo <= base + c(i) <= hi, evaluated as the one unsigned compare
+// c(i) - a <= span with a = lo - base, span = hi - lo; an empty range takes a = 64, which
+// every c(i) < 32 wraps below.
+struct TileRange {
+  uint32_t a, span;
+  __device__ __forceinline__ TileRange(int base, int lo, int hi) {
+    const int a0 = lo - base, b0 = hi - base;
+    a = b0 >= a0 ? (uint32_t)a0 : 64u;
+    span = b0 >= a0 ? (uint32_t)(b0 - a0) : 0u;
+  }
+  __device__ __forceinline__ bool keep(int i) const {
+    return (uint32_t)(8 * (i >> 2) + (i & 3)) - a <= span;
+  }
+};
+
+// Stage kinds of the stage loops: plain (every score visible), diag (no documents, inside the
+// sequence: only the causal diagonal sub-tile of a wave is masked, in place on the scores)
+// and masked (document bounds, the ragged sequence end: every element is tested).
+using PlainStage = std::integral_constant<int, 0>;
+using MaskedStage = std::integral_constant<int, 1>;
+using DiagStage = std::integral_constant<int, 2>;
+
+// Causal mask of a 32x32 score tile on the diagonal (tile rows and lane columns start at
+// the same index): with keys on the rows (query-major kernels) row r is hidden from lane
+// column c when r > c; with queries on the rows (key-major kernels) when r < c.
+template <bool KEYS_ON_ROWS>
+__device__ __forceinline__ void diag_mask(f32x16& st, int lane) {
+  const int c = lane & 31, h4 = 4 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 8 * (i >> 2) + h4 + (i & 3);
+    if (KEYS_ON_ROWS ? r > c : r < c) st[i] = -INFINITY;
+  }
+}
+
 // Online softmax of one 32-key sub-tile: scores st (keys x this lane's query) update the
 // running max / sum (rescaling the output accumulator lazily) and give the packed P^T
 // operand of the P.V product.
@@ -572,13 +619,12 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&o)[HD / 32], SoftmaxState& 
                                             int qrow, int lo, int S, int h, float scale_log2) {
   float sv[16];
   float tmax = -INFINITY;
+  // keys lo .. min(qrow, S - 1) are visible
+  const TileRange rg(kb + 4 * h, lo, min(qrow, S - 1));
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     float x = st[i];
-    if constexpr (MASK) {
-      const int key = kb + 8 * (i >> 2) + 4 * h + (i & 3);
-      if (key > qrow || key >= S || key < lo) x = -INFINITY;
-    }
+    if (MASK && !rg.keep(i)) x = -INFINITY;
     sv[i] = x;
     tmax = fmaxf(tmax, x);
   }
@@ -608,7 +654,7 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&o)[HD / 32], SoftmaxState& 
 // One 32-key sub-tile: softmax, then O^T += V^T P^T.
 template <int HD, bool MASK>
 __device__ __forceinline__ void fwd_subtile(f32x16 (&o)[HD / 32], SoftmaxState& sm,
-                                            const f32x16& st, const char* vsub, uint32_t tl,
+                                            const f32x16& st, lptr vsub, uint32_t tl,
                                             int kb, int qrow, int lo, int S, int h,
                                             float scale_log2) {
   bf16x8 pb[2];
@@ -641,14 +687,18 @@ __device__ __forceinline__ QDoc q_doc(const int* __restrict__ seg_lo, int q0, in
 
 // Stage loop of a query-major workgroup over key stages [t_first, ntiles): stages that every
 // row sees in full run `plain`, the rest (document starts, the diagonal, the ragged end)
-// `masked`.
+// `masked`, except that without documents the diagonal stages that end inside the sequence
+// run `diag`.
 template <typename F>
-__device__ __forceinline__ void q_stage_loop(const QDoc& doc, int nplain, int ntiles, F&& stage) {
+__device__ __forceinline__ void q_stage_loop(const QDoc& doc, bool docs, int nplain, int ntiles,
+                                             int S, F&& stage) {
   const int a = min(doc.t_plain, ntiles);
-  for (int t = doc.t_first; t < a; ++t) stage(std::true_type{}, t);
-  for (int t = max(doc.t_plain, doc.t_first); t < nplain; ++t) stage(std::false_type{}, t);
-  for (int t = max(max(nplain, doc.t_plain), doc.t_first); t < ntiles; ++t)
-    stage(std::true_type{}, t);
+  for (int t = doc.t_first; t < a; ++t) stage(MaskedStage{}, t);
+  for (int t = max(doc.t_plain, doc.t_first); t < nplain; ++t) stage(PlainStage{}, t);
+  const int t3 = max(max(nplain, doc.t_plain), doc.t_first);
+  const int d_end = docs ? t3 : max(t3, min(ntiles, S / kBN));
+  for (int t = t3; t < d_end; ++t) stage(DiagStage{}, t);
+  for (int t = d_end; t < ntiles; ++t) stage(MaskedStage{}, t);
 }
 
 // QK-norm + RoPE forward on the forward's resident Q rows (Mint documentation 5.4.1,
@@ -779,25 +829,27 @@ __global__ __launch_bounds__(64 * kQW, 1) void fwd_kernel(const bf16* __restrict
   // nplain lie strictly before the block's first query and inside the sequence, and (with
   // documents) at or after every row's document start, so no wave needs masking there; the
   // few remaining stages run the masked instantiation.
-  auto stage = [&](auto mask_tag, int t) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  auto stage = [&](auto kind, int t) {
+    constexpr int KIND = decltype(kind)::value;
+    constexpr bool MASK = KIND == MaskedStage::value, DIAG = KIND == DiagStage::value;
     if (NBUF > 2 && t + 1 < ntiles) stage_barrier<(NBUF > 2 ? NL : 0)>();
     else stage_barrier<0>();
     if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1, (t - t0 + NBUF - 1) % NBUF);
     const int bb = (t - t0) % NBUF;
-    const char* ks = lds + (2 * bb) * TILEB;
-    const char* vs = lds + (2 * bb + 1) * TILEB;
+    const lptr ks = to_lds(lds) + (2 * bb) * TILEB;
+    const lptr vs = ks + TILEB;
 #pragma unroll
     for (int s = 0; s < kBN / 32; ++s) {
       const int kb = t * kBN + 32 * s;
-      if (MASK && (kb > qw0 + 31 || kb >= S)) break;  // wave-uniform
-      if (MASK && kb + 31 < doc.lo_wave) continue;     // before every row's document
-      const f32x16 st = contract_rows<HD>(ks + 32 * s * ROWB, al, qf);
+      if ((MASK || DIAG) && (kb > qw0 + 31 || kb >= S)) break;  // wave-uniform
+      if (MASK && kb + 31 < doc.lo_wave) continue;              // before every row's document
+      f32x16 st = contract_rows<HD>(ks + 32 * s * ROWB, al, qf);
+      if (DIAG && kb == qw0) diag_mask<true>(st, lane);
       fwd_subtile<HD, MASK>(o, sm, st, vs + 32 * s * ROWB, tl, kb, qrow, doc.lo_row, S, h,
                             scale_log2);
     }
   };
-  q_stage_loop(doc, min(q0 / kBN, S / kBN), ntiles, stage);
+  q_stage_loop(doc, seg_lo != nullptr, min(q0 / kBN, S / kBN), ntiles, S, stage);
   const float l = halves_sum(sm.l);
   if (qrow < S) {
     store_col<bf16, HD>(out + ((size_t)bh * S + qrow) * HD, o, 1.0f / l, h);
@@ -810,17 +862,15 @@ __global__ __launch_bounds__(64 * kQW, 1) void fwd_kernel(const bf16* __restrict
 // ---------------------------------------------------------------------------------------
 template <int HD, bool MASK>
 __device__ __forceinline__ void dq_subtile(f32x16 (&acc)[HD / 32], const f32x16& st,
-                                           const f32x16& dpt, const char* ksub, uint32_t tl,
+                                           const f32x16& dpt, lptr ksub, uint32_t tl,
                                            int kb, int qrow, int lo, int S, int h,
                                            float scale_log2, float lse2, float D) {
   float dsv[16];
+  const TileRange rg(kb + 4 * h, lo, min(qrow, S - 1));  // visible keys
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     float p = fast_exp2(st[i] * scale_log2 - lse2);
-    if constexpr (MASK) {
-      const int key = kb + 8 * (i >> 2) + 4 * h + (i & 3);
-      if (key > qrow || key >= S || key < lo) p = 0.f;
-    }
+    if (MASK && !rg.keep(i)) p = 0.f;
     dsv[i] = p * (dpt[i] - D);
   }
   bf16x8 db[2];
@@ -856,6 +906,18 @@ __global__ __launch_bounds__(64 * kQW, 1) void dq_kernel(
   D dma;
   dma.init(wv, lane);
 
+  const QDoc doc = q_doc(seg_lo, q0, qw0, qrow, S);
+  const int t0 = doc.t_first;  // stages run from t0; buffers are numbered from it
+  const int ntiles = (min(S, q0 + kBM) + kBN - 1) / kBN;
+  auto issue = [&](int t, int buf) {
+    const int g0 = t * kBN, nv = S - g0;
+    dma.issue(lds + (2 * buf) * TILEB, kp + (size_t)g0 * ROWB, wv, nv);
+    dma.issue(lds + (2 * buf + 1) * TILEB, vp + (size_t)g0 * ROWB, wv, nv);
+  };
+  // the first tiles' copies are in flight while the row operands load and delta is formed
+#pragma unroll
+  for (int u = 0; u < NBUF - 1; ++u)
+    if (t0 + u < ntiles) issue(t0 + u, u);
   bf16x8 qf[HD / 16], df[HD / 16];
   load_frag<HD>(qf, q + hoff, qrow, S, lane);
   load_frag<HD>(df, dout + hoff, qrow, S, lane);
@@ -878,37 +940,28 @@ __global__ __launch_bounds__(64 * kQW, 1) void dq_kernel(
 #pragma unroll
   for (int dt = 0; dt < HD / 32; ++dt) acc[dt] = zero16();
 
-  const QDoc doc = q_doc(seg_lo, q0, qw0, qrow, S);
-  const int t0 = doc.t_first;  // stages run from t0; buffers are numbered from it
-  const int ntiles = (min(S, q0 + kBM) + kBN - 1) / kBN;
-  auto issue = [&](int t, int buf) {
-    const int g0 = t * kBN, nv = S - g0;
-    dma.issue(lds + (2 * buf) * TILEB, kp + (size_t)g0 * ROWB, wv, nv);
-    dma.issue(lds + (2 * buf + 1) * TILEB, vp + (size_t)g0 * ROWB, wv, nv);
-  };
-#pragma unroll
-  for (int u = 0; u < NBUF - 1; ++u)
-    if (t0 + u < ntiles) issue(t0 + u, u);
-  auto stage = [&](auto mask_tag, int t) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  auto stage = [&](auto kind, int t) {
+    constexpr int KIND = decltype(kind)::value;
+    constexpr bool MASK = KIND == MaskedStage::value, DIAG = KIND == DiagStage::value;
     if (NBUF > 2 && t + 1 < ntiles) stage_barrier<(NBUF > 2 ? NL : 0)>();
     else stage_barrier<0>();
     if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1, (t - t0 + NBUF - 1) % NBUF);
     const int bb = (t - t0) % NBUF;
-    const char* ks = lds + (2 * bb) * TILEB;
-    const char* vs = lds + (2 * bb + 1) * TILEB;
+    const lptr ks = to_lds(lds) + (2 * bb) * TILEB;
+    const lptr vs = ks + TILEB;
 #pragma unroll
     for (int s = 0; s < kBN / 32; ++s) {
       const int kb = t * kBN + 32 * s;
-      if (MASK && (kb > qw0 + 31 || kb >= S)) break;
+      if ((MASK || DIAG) && (kb > qw0 + 31 || kb >= S)) break;
       if (MASK && kb + 31 < doc.lo_wave) continue;  // before every row's document
-      const f32x16 st = contract_rows<HD>(ks + 32 * s * ROWB, al, qf);   // S^T
+      f32x16 st = contract_rows<HD>(ks + 32 * s * ROWB, al, qf);  // S^T
       const f32x16 dpt = contract_rows<HD>(vs + 32 * s * ROWB, al, df);  // dP^T
+      if (DIAG && kb == qw0) diag_mask<true>(st, lane);
       dq_subtile<HD, MASK>(acc, st, dpt, ks + 32 * s * ROWB, tl, kb, qrow, doc.lo_row, S, h,
                            scale_log2, lse2, Dq);
     }
   };
-  q_stage_loop(doc, min(q0 / kBN, S / kBN), ntiles, stage);
+  q_stage_loop(doc, seg_lo != nullptr, min(q0 / kBN, S / kBN), ntiles, S, stage);
   if constexpr (PRO) {
     static_assert(sizeof(lds) >= kQW * 32 * HD * sizeof(float), "epilogue tiles fit");
     lds_barrier();  // every wave is done with the staged tiles
@@ -938,17 +991,17 @@ constexpr int kDkdvPF = 1;  // operand read-ahead of the dk/dv step (see dkdv_st
 // chains are issued; 2: each group one phase ahead.
 template <int HD, bool MASK, int PF>
 __device__ __forceinline__ void dkdv_step_reg(f32x16 (&dkt)[HD / 32], f32x16 (&dvt)[HD / 32],
-                                              const char* qs, const char* dos,
+                                              lptr qs, lptr dos,
                                               const float* stats, const bf16x8 (&kf)[HD / 16],
                                               const bf16x8 (&vf)[HD / 16], uint32_t al,
                                               uint32_t tl, int q0, int key, int khi, int S,
-                                              float scale_log2, int h) {
+                                              float scale_log2, int h, bool diag = false) {
   bf16x8 qa[HD / 16], da[HD / 16], ta[2][HD / 32], tq[2][HD / 32];
-  auto read_rows = [&](bf16x8 (&x)[HD / 16], const char* base) {
+  auto read_rows = [&](bf16x8 (&x)[HD / 16], lptr base) {
 #pragma unroll
     for (int c = 0; c < HD / 16; ++c) x[c] = lds_a<HD>(base, al, c);
   };
-  auto read_tr = [&](bf16x8 (&x)[2][HD / 32], const char* base) {
+  auto read_tr = [&](bf16x8 (&x)[2][HD / 32], lptr base) {
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
@@ -976,17 +1029,17 @@ __device__ __forceinline__ void dkdv_step_reg(f32x16 (&dkt)[HD / 32], f32x16 (&d
     if constexpr (PF == 1) read_tr(tq, qs);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // the query tile starts at the wave's first key (wave-uniform): the causal diagonal
+  if (diag) diag_mask<false>(st, (int)(threadIdx.x & 63));
   float pv[16];
+  const TileRange rg(q0 + 4 * h, key, min(khi, S - 1));  // queries that see the key
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const f32x4 l2 = *reinterpret_cast<const f32x4*>(stats + 8 * g + 4 * h);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float p = fast_exp2(st[4 * g + j] * scale_log2 - l2[j]);
-      if constexpr (MASK) {
-        const int qi = q0 + 8 * g + 4 * h + j;
-        if (qi < key || qi >= S || qi > khi) p = 0.f;
-      }
+      if (MASK && !rg.keep(4 * g + j)) p = 0.f;
       pv[4 * g + j] = p;
     }
   }
@@ -1088,28 +1141,34 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_shared_kernel(
   for (int t = 0; t < NBUF - 1; ++t)
     if (t < nst) issue(t, t);
   const bool live = kw0 < S;
-  auto stage = [&](auto mask_tag, int t) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  auto stage = [&](auto kind, int t) {
+    constexpr int KIND = decltype(kind)::value;
+    constexpr bool MASK = KIND == MaskedStage::value, DIAG = KIND == DiagStage::value;
     if (NBUF > 2 && t + 1 < nst) stage_barrier<(NBUF > 2 ? NL : 0)>();
     else stage_barrier<0>();
     if (t + NBUF - 1 < nst) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
     const int bb = t % NBUF;
     const int q0 = (qt_first + t % per_r) * kBQ;
-    if (live && q0 + kBQ - 1 >= kw0 && q0 <= hi_wave)
-      dkdv_step_reg<HD, MASK, kDkdvPF>(dkt, dvt, lds + (2 * bb) * TILEB,
-                                       lds + (2 * bb + 1) * TILEB, stats[bb], kf, vf, al, tl,
-                                       q0, key, doc.hi_key, S, scale_log2, h);
+    if (live && q0 + kBQ - 1 >= kw0 && q0 <= hi_wave) {
+      dkdv_step_reg<HD, MASK, kDkdvPF>(dkt, dvt, to_lds(lds) + (2 * bb) * TILEB,
+                                       to_lds(lds) + (2 * bb + 1) * TILEB, stats[bb], kf, vf, al,
+                                       tl, q0, key, doc.hi_key, S, scale_log2, h,
+                                       DIAG && q0 == kw0);
+    }
   };
-  // Per query head: the first four query tiles straddle the diagonal of some wave's keys;
-  // tiles reaching past the first key's last query (a document end, or the ragged end of
-  // the sequence) need masking too; the rest need none.
+  // Per query head: the first four query tiles straddle the diagonal of some wave's keys
+  // (without documents and inside the sequence, only each wave's diagonal tile is masked:
+  // diag stages); tiles reaching past the first key's last query (a document end, or the
+  // ragged end of the sequence) need masking too; the rest need none.
   const int nmask_head = min(4, per_r);
+  const int ndiag_head = seg_hi != nullptr ? 0 : min(nmask_head, (S - k0) / kBQ);
   const int plain_end = max(nmask_head, min(per_r, (doc.hi_first + 1) / kBQ - qt_first));
   for (int r = 0; r < group; ++r) {
     const int t0 = r * per_r;
-    for (int i = 0; i < nmask_head; ++i) stage(std::true_type{}, t0 + i);
-    for (int i = nmask_head; i < plain_end; ++i) stage(std::false_type{}, t0 + i);
-    for (int i = plain_end; i < per_r; ++i) stage(std::true_type{}, t0 + i);
+    for (int i = 0; i < ndiag_head; ++i) stage(DiagStage{}, t0 + i);
+    for (int i = ndiag_head; i < nmask_head; ++i) stage(MaskedStage{}, t0 + i);
+    for (int i = nmask_head; i < plain_end; ++i) stage(PlainStage{}, t0 + i);
+    for (int i = plain_end; i < per_r; ++i) stage(MaskedStage{}, t0 + i);
   }
   if (key < S) store_col<bf16, HD>(dv + ((size_t)kvbh * S + key) * HD, dvt, 1.0f, h);
   if constexpr (PRO) {
@@ -1156,6 +1215,7 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_private_kernel(
   D dma;
   dma.init(0, lane);
   char* mine = lds + wv * WAVEB;
+  const lptr lmine = to_lds(mine);
   bf16x8 kf[HD / 16], vf[HD / 16];  // K and V rows of the lane's key
   load_frag<HD>(kf, k + (size_t)kvbh * S * HD, key, S, lane);
   load_frag<HD>(vf, v + (size_t)kvbh * S * HD, key, S, lane);
@@ -1201,8 +1261,8 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_private_kernel(
     if (issued < nst) issue_next((t + NBUF - 1) % NBUF);
     const int bb = t % NBUF;
     const int q0 = (qt_first + wv + 4 * i) * kBQ;
-    dkdv_step_reg<HD, MASK, kDkdvPF>(dkt, dvt, mine + (2 * bb) * TILEB,
-                                     mine + (2 * bb + 1) * TILEB, stats[wv][bb], kf, vf, al, tl,
+    dkdv_step_reg<HD, MASK, kDkdvPF>(dkt, dvt, lmine + (2 * bb) * TILEB,
+                                     lmine + (2 * bb + 1) * TILEB, stats[wv][bb], kf, vf, al, tl,
                                      q0, key, doc.hi_key, S, scale_log2, h);
   };
   // Per query head: only wave 0's first tile meets the diagonal (its keys start at its
@@ -1310,6 +1370,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_kernel(
   D dma;
   dma.init(kb, lane);
   char* mine = lds + st * STREAMB;
+  const lptr lmine = to_lds(mine);
   float(*sst)[64] = stats[st];
   bf16x8 kf[HD / 16], vf[HD / 16];  // K and V rows of the lane's key
   load_frag<HD>(kf, k + (size_t)kvbh * S * HD, key, S, lane);
@@ -1358,15 +1419,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_kernel(
     wait_vm<2 * NL>();  // tiles 0 and 1
     __builtin_amdgcn_s_barrier();
     lds_acquire();
-    rows_of<HD>(qa, mine, al);
-    rows_of<HD>(da, mine + TILEB, al);
+    rows_of<HD>(qa, lmine, al);
+    rows_of<HD>(da, lmine + TILEB, al);
 #pragma unroll
     for (int c = 0; c < HD / 16; ++c) {
       s_cur = mfma_bf16(qa[c], kf[c], s_cur);
       p_cur = mfma_bf16(da[c], vf[c], p_cur);
     }
-    rows_of<HD>(qa, mine + 2 * TILEB, al);
-    rows_of<HD>(da, mine + 3 * TILEB, al);
+    rows_of<HD>(qa, lmine + 2 * TILEB, al);
+    rows_of<HD>(da, lmine + 3 * TILEB, al);
   }
 
   // Iteration t: P / dS of tile t under the S / dP products of tile t + 1, then tile t's
@@ -1374,7 +1435,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_kernel(
   // transposed operands, are complete by then) and receives tile t + 4.
   auto iter = [&](auto mask_tag, int t, int i) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const char* cur = mine + (2 * (t % NB)) * TILEB;
+    const lptr cur = lmine + (2 * (t % NB)) * TILEB;
     const float* stt = sst[t % NB];
     const int q0 = (qt_first + st + 2 * i) * kBQ;
     f32x4 l2[4], dd[4];
@@ -1391,15 +1452,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_kernel(
       p_nxt = mfma_bf16(da[c], vf[c], p_nxt);
     }
     float pv[16], dsv[16];
+    const TileRange rg(q0 + 4 * h, key, min(doc.hi_key, S - 1));  // queries that see the key
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float p = fast_exp2(s_cur[4 * g + j] * scale_log2 - l2[g][j]);
-        if constexpr (MASK) {
-          const int qi = q0 + 8 * g + 4 * h + j;
-          if (qi < key || qi >= S || qi > doc.hi_key) p = 0.f;
-        }
+        if (MASK && !rg.keep(4 * g + j)) p = 0.f;
         pv[4 * g + j] = p;
         dsv[4 * g + j] = p * (p_cur[4 * g + j] - dd[g][j]);
       }
@@ -1423,7 +1482,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_kernel(
     __builtin_amdgcn_s_barrier();
     lds_acquire();
     issue_next();  // tile t + 4 into tile t's buffer
-    const char* nx2 = mine + (2 * ((t + 2) % NB)) * TILEB;
+    const lptr nx2 = lmine + (2 * ((t + 2) % NB)) * TILEB;
     rows_of<HD>(qa, nx2, al);
     rows_of<HD>(da, nx2 + TILEB, al);
 #pragma unroll
