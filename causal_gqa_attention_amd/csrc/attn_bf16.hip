@@ -246,7 +246,7 @@ __device__ __forceinline__ void dma16_rows(void* dst, const char* gbase, uint32_
 #undef XATTN_TAIL
 }
 __device__ __forceinline__ void dma4(void* dst, const float* gaddr) {
-  const uint32_t m0v = (uint32_t)(uintptr_t)dst;
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);  // uniform
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
@@ -1127,28 +1127,37 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_shared_kernel(
   // query tiles up to the last query of the workgroup's last key
   const int per_r = max(0, min(nqt, doc.hi_last / kBQ + 1) - qt_first);
   const int nst = group * per_r;
-  auto issue = [&](int t, int buf) {
-    const int r = t / per_r, qt = qt_first + t % per_r;
-    const size_t bh = (size_t)(b * H + kvh * group + r);
-    const int g0 = qt * kBQ, nv = S - g0;
+  // tiles are issued in stage order (query head r, tile i of it); the cursor avoids a
+  // division per stage
+  int next_r = 0, next_i = 0;
+  auto issue_next = [&](int buf) {
+    const size_t bh = (size_t)(b * H + kvh * group + next_r);
+    const int g0 = (qt_first + next_i) * kBQ, nv = S - g0;
     dma.issue(lds + (2 * buf) * TILEB, reinterpret_cast<const char*>(q + (bh * S + g0) * HD),
               wv, nv);
     dma.issue(lds + (2 * buf + 1) * TILEB,
               reinterpret_cast<const char*>(dout + (bh * S + g0) * HD), wv, nv);
     dma_rowstats<4>(stats[buf], lse2 + bh * S, delta + bh * S, g0, S, wv, lane);
+    if (++next_i == per_r) {
+      next_i = 0;
+      ++next_r;
+    }
   };
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t)
-    if (t < nst) issue(t, t);
+    if (t < nst) issue_next(t);
   const bool live = kw0 < S;
-  auto stage = [&](auto kind, int t) {
-    constexpr int KIND = decltype(kind)::value;
+  // Stage t = (query head, tile i of it) in buffer t % NBUF; BUF >= 0 gives that buffer as a
+  // constant (the plain stages are unrolled by NBUF), so every LDS address of the stage is a
+  // lane constant plus an immediate offset.
+  auto stage = [&](auto kind, int t, int i, auto buf) {
+    constexpr int KIND = decltype(kind)::value, BUF = decltype(buf)::value;
     constexpr bool MASK = KIND == MaskedStage::value, DIAG = KIND == DiagStage::value;
     if (NBUF > 2 && t + 1 < nst) stage_barrier<(NBUF > 2 ? NL : 0)>();
     else stage_barrier<0>();
-    if (t + NBUF - 1 < nst) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);
-    const int bb = t % NBUF;
-    const int q0 = (qt_first + t % per_r) * kBQ;
+    const int bb = BUF >= 0 ? BUF : t % NBUF;
+    if (t + NBUF - 1 < nst) issue_next(BUF >= 0 ? (BUF + NBUF - 1) % NBUF : (t + NBUF - 1) % NBUF);
+    const int q0 = (qt_first + i) * kBQ;
     if (live && q0 + kBQ - 1 >= kw0 && q0 <= hi_wave) {
       dkdv_step_reg<HD, MASK, kDkdvPF>(dkt, dvt, to_lds(lds) + (2 * bb) * TILEB,
                                        to_lds(lds) + (2 * bb + 1) * TILEB, stats[bb], kf, vf, al,
@@ -1163,12 +1172,24 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_shared_kernel(
   const int nmask_head = min(4, per_r);
   const int ndiag_head = seg_hi != nullptr ? 0 : min(nmask_head, (S - k0) / kBQ);
   const int plain_end = max(nmask_head, min(per_r, (doc.hi_first + 1) / kBQ - qt_first));
+  static_assert(NBUF == 3, "the plain stages are unrolled by three");
+  using Any = std::integral_constant<int, -1>;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
   for (int r = 0; r < group; ++r) {
     const int t0 = r * per_r;
-    for (int i = 0; i < ndiag_head; ++i) stage(DiagStage{}, t0 + i);
-    for (int i = ndiag_head; i < nmask_head; ++i) stage(MaskedStage{}, t0 + i);
-    for (int i = nmask_head; i < plain_end; ++i) stage(PlainStage{}, t0 + i);
-    for (int i = plain_end; i < per_r; ++i) stage(MaskedStage{}, t0 + i);
+    for (int i = 0; i < ndiag_head; ++i) stage(DiagStage{}, t0 + i, i, Any{});
+    for (int i = ndiag_head; i < nmask_head; ++i) stage(MaskedStage{}, t0 + i, i, Any{});
+    int i = nmask_head;
+    for (; i < plain_end && (t0 + i) % NBUF != 0; ++i) stage(PlainStage{}, t0 + i, i, Any{});
+    for (; i + NBUF <= plain_end; i += NBUF) {
+      stage(PlainStage{}, t0 + i, i, B0{});
+      stage(PlainStage{}, t0 + i + 1, i + 1, B1{});
+      stage(PlainStage{}, t0 + i + 2, i + 2, B2{});
+    }
+    for (; i < plain_end; ++i) stage(PlainStage{}, t0 + i, i, Any{});
+    for (i = plain_end; i < per_r; ++i) stage(MaskedStage{}, t0 + i, i, Any{});
   }
   if (key < S) store_col<bf16, HD>(dv + ((size_t)kvbh * S + key) * HD, dvt, 1.0f, h);
   if constexpr (PRO) {
