@@ -879,7 +879,7 @@ __device__ __forceinline__ void dq_subtile(f32x16 (&acc)[HD / 32], const f32x16&
 }
 
 template <int HD, int NBUF, bool PRO>
-__global__ __launch_bounds__(64 * kQW, 1) void dq_kernel(
+__global__ __launch_bounds__(64 * kQW, HD == 64 ? 4 : 1) void dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ out, const bf16* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ lse2_out, float* __restrict__ delta, bf16* __restrict__ dq, int S, int H,
