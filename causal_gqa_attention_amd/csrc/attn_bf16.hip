@@ -187,6 +187,21 @@ __device__ __forceinline__ void stage_wait_private() {
   wait_vm<N>();
   lds_acquire();
 }
+// vmcnt wait that leaves the copies of `after` (0..MAXA) later tiles in flight, NL loads each
+template <int MAXA, int NL>
+__device__ __forceinline__ void wait_tiles_after(int after) {
+  if constexpr (MAXA <= 0) {
+    wait_vm<0>();
+  } else {
+    if (after >= MAXA) wait_vm<MAXA * NL>();
+    else wait_tiles_after<MAXA - 1, NL>(after);
+  }
+}
+// f(integral_constant<int, k>) for k = 0 .. N-1, in order
+template <typename F, int... K>
+__device__ __forceinline__ void for_each_buf(F&& f, std::integer_sequence<int, K...>) {
+  (f(std::integral_constant<int, K>{}), ...);
+}
 
 // Direct global -> LDS copies (gfx950 global_load_lds): lane l's bytes land at the
 // wave-uniform LDS address dst + size * l.  They are written as inline assembly so that the
@@ -1153,8 +1168,10 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_shared_kernel(
   auto stage = [&](auto kind, int t, int i, auto buf) {
     constexpr int KIND = decltype(kind)::value, BUF = decltype(buf)::value;
     constexpr bool MASK = KIND == MaskedStage::value, DIAG = KIND == DiagStage::value;
-    if (NBUF > 2 && t + 1 < nst) stage_barrier<(NBUF > 2 ? NL : 0)>();
-    else stage_barrier<0>();
+    // tile t has landed once at most the copies of the tiles after it are in flight
+    wait_tiles_after<NBUF - 2, NL>(min(NBUF - 2, nst - 1 - t));
+    __builtin_amdgcn_s_barrier();
+    lds_acquire();
     const int bb = BUF >= 0 ? BUF : t % NBUF;
     if (t + NBUF - 1 < nst) issue_next(BUF >= 0 ? (BUF + NBUF - 1) % NBUF : (t + NBUF - 1) % NBUF);
     const int q0 = (qt_first + i) * kBQ;
@@ -1172,22 +1189,18 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_shared_kernel(
   const int nmask_head = min(4, per_r);
   const int ndiag_head = seg_hi != nullptr ? 0 : min(nmask_head, (S - k0) / kBQ);
   const int plain_end = max(nmask_head, min(per_r, (doc.hi_first + 1) / kBQ - qt_first));
-  static_assert(NBUF == 3, "the plain stages are unrolled by three");
   using Any = std::integral_constant<int, -1>;
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  using B2 = std::integral_constant<int, 2>;
   for (int r = 0; r < group; ++r) {
     const int t0 = r * per_r;
     for (int i = 0; i < ndiag_head; ++i) stage(DiagStage{}, t0 + i, i, Any{});
     for (int i = ndiag_head; i < nmask_head; ++i) stage(MaskedStage{}, t0 + i, i, Any{});
     int i = nmask_head;
     for (; i < plain_end && (t0 + i) % NBUF != 0; ++i) stage(PlainStage{}, t0 + i, i, Any{});
-    for (; i + NBUF <= plain_end; i += NBUF) {
-      stage(PlainStage{}, t0 + i, i, B0{});
-      stage(PlainStage{}, t0 + i + 1, i + 1, B1{});
-      stage(PlainStage{}, t0 + i + 2, i + 2, B2{});
-    }
+    for (; i + NBUF <= plain_end; i += NBUF)
+      for_each_buf([&](auto buf) {
+        constexpr int k = decltype(buf)::value;
+        stage(PlainStage{}, t0 + i + k, i + k, buf);
+      }, std::make_integer_sequence<int, NBUF>{});
     for (; i < plain_end; ++i) stage(PlainStage{}, t0 + i, i, Any{});
     for (i = plain_end; i < per_r; ++i) stage(MaskedStage{}, t0 + i, i, Any{});
   }
