@@ -93,3 +93,25 @@ def test_document_masking_is_bitwise_reproducible():
     a, b = _step(w, x, docs), _step(w, x, docs)
     for n in ("out", "lse", "dxq", "dxk", "dv", "dgamma_q", "dgamma_k"):
         np.testing.assert_array_equal(a[n], b[n])
+
+
+# One document spanning the whole sequence sees exactly the plain causal mask, but runs the
+# document code: every stage that holds the diagonal or the ragged end goes through the
+# per-element range test, where without documents the diagonal stages only mask each wave's
+# diagonal sub-tile in place.  The two must give the same bits.
+WHOLE = [
+    R("bf16", 128, 300, 1, 8, 2, theta=1e6, eps=1e-6, index=509),  # pipelined dk/dv, hd 128
+    R("bf16", 128, 200, 128, 8, 4, index=510),                     # shared dk/dv, hd 128
+    R("bf16", 64, 330, 96, 6, 6, index=511),                       # shared dk/dv, hd 64
+    R("bf16", 64, 1000, 4, 12, 4, index=512),                      # private dk/dv, hd 64
+]
+
+
+@pytest.mark.parametrize("w", WHOLE, ids=[f"hd{w.head_dim}_S{w.seq_len}_B{w.batch}"
+                                          for w in WHOLE])
+def test_one_whole_document_equals_no_documents(w):
+    x = W.make_inputs(w)
+    note(f"whole-sequence document against none {w}")
+    a, b = _step(w, x, [w.seq_len]), _step(w, x, None)
+    for n in ("yq", "yk", "out", "lse", "dxq", "dxk", "dv", "dgamma_q", "dgamma_k"):
+        np.testing.assert_array_equal(a[n], b[n], err_msg=n)
