@@ -1,9 +1,10 @@
 """Python binding of libxattn: causal GQA attention with a QK-norm + RoPE prologue on
 MI355X (gfx950).
 
-This module only marshals arguments: it checks tensor placement, dtype and shape,
-allocates outputs and workspaces with torch (device memory and streams are all torch is
-used for) and calls the C ABI declared in include/xattn.h.  Every computation runs in
+This module only marshals arguments: it checks every tensor's element count against the
+call's dimensions (the C ABI receives raw pointers and cannot), then its dtype, placement
+and contiguity, allocates outputs and workspaces with torch (device memory and streams are
+all torch is used for) and calls the C ABI declared in include/xattn.h.  Every computation runs in
 the HIP kernels of libxattn.so; there is no fallback path.  If the library has not been
 built, every call raises.
 
@@ -144,21 +145,49 @@ def load_library() -> ctypes.CDLL:
 # ----------------------------------------------------------------------------------------
 # marshalling helpers
 # ----------------------------------------------------------------------------------------
-def _ptr(t, name, dtype=None):
-    if t is None:
-        return None
+def _ptrs(*specs):
+    """Device pointers of tensors given as (tensor, name, dtype, numel) specs, None entries
+    passing through as NULL.  Every tensor is checked for its element count (numel, when
+    not None: a shorter tensor would let the kernels read or write past it) and its dtype
+    before any is checked for placement and contiguity, so a size mismatch is reported as
+    such wherever the tensors live."""
+    for t, name, dtype, numel in specs:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if numel is not None and t.numel() != int(numel):
+            raise ValueError(f"{name} must hold {int(numel)} elements for these dimensions, "
+                             f"got {t.numel()} (shape {tuple(t.shape)})")
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    for t, name, _, _ in specs:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    return [None if t is None else t.data_ptr() for t, _, _, _ in specs]
+
+
+def _bytes(t, name):
+    """Size in bytes of a workspace tensor (the C side checks it against its query)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if dtype is not None and t.dtype != dtype:
-        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
-    return t.data_ptr()
+    return t.numel() * t.element_size()
+
+
+def _sizes(dims):
+    """Element counts of an attention call: (q / out / dout, k / v, lse / rstd_q rows,
+    rstd_k rows, one rope table)."""
+    B, S, H, Hkv, hd = dims.batch, dims.seq_len, dims.num_heads, dims.num_kv_heads, dims.head_dim
+    return B * H * S * hd, B * Hkv * S * hd, B * H * S, B * Hkv * S, S * (hd // 2)
 
 
 def _io(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype not in _DTYPES:
         raise ValueError(f"{name} must be float32 or bfloat16, got {t.dtype}")
     return _DTYPES[t.dtype]
@@ -177,6 +206,10 @@ def _check(status, where):
         lib = load_library()
         detail = lib.xattn_last_error().decode() or lib.xattn_status_string(status).decode()
         raise XattnError(status, where, detail)
+
+
+F32 = torch.float32
+I32 = torch.int32
 
 
 # ----------------------------------------------------------------------------------------
@@ -209,28 +242,37 @@ def xattn_profile_stop(max_entries: int = 32) -> dict:
 
 
 def xattn_rope_cache(cos_tab, sin_tab, seq_len, head_dim, theta, stream=None):
-    _check(load_library().xattn_rope_cache(
-        _ptr(cos_tab, "cos_tab", torch.float32), _ptr(sin_tab, "sin_tab", torch.float32),
-        seq_len, head_dim, float(theta), _stream(stream)), "xattn_rope_cache")
+    nt = int(seq_len) * (int(head_dim) // 2)
+    pc, ps = _ptrs((cos_tab, "cos_tab", F32, nt), (sin_tab, "sin_tab", F32, nt))
+    _check(load_library().xattn_rope_cache(pc, ps, seq_len, head_dim, float(theta),
+                                           _stream(stream)), "xattn_rope_cache")
+
+
+def _prologue_sizes(rows, seq_len, head_dim):
+    return int(rows) * seq_len * head_dim, int(rows) * seq_len, seq_len * (head_dim // 2)
 
 
 def xattn_qknorm_rope_fwd(x, gamma, cos_tab, sin_tab, y, rstd, rows, seq_len, head_dim, eps,
                           stream=None):
-    _check(load_library().xattn_qknorm_rope_fwd(
-        _ptr(x, "x"), _ptr(gamma, "gamma", torch.float32), _ptr(cos_tab, "cos_tab", torch.float32),
-        _ptr(sin_tab, "sin_tab", torch.float32), _ptr(y, "y", x.dtype),
-        _ptr(rstd, "rstd", torch.float32), rows, seq_len, head_dim, float(eps), _io(x, "x"),
-        _stream(stream)), "xattn_qknorm_rope_fwd")
+    n, nr, nt = _prologue_sizes(rows, seq_len, head_dim)
+    io = _io(x, "x")
+    p = _ptrs((x, "x", None, n), (gamma, "gamma", F32, head_dim), (cos_tab, "cos_tab", F32, nt),
+              (sin_tab, "sin_tab", F32, nt), (y, "y", x.dtype, n), (rstd, "rstd", F32, nr))
+    _check(load_library().xattn_qknorm_rope_fwd(*p, rows, seq_len, head_dim, float(eps), io,
+                                                _stream(stream)), "xattn_qknorm_rope_fwd")
 
 
 def xattn_qknorm_rope_fwd_table(x, gamma, positions, theta, cos_tab, sin_tab, y, rstd, rows,
                                 seq_len, head_dim, eps, stream=None):
+    n, nr, nt = _prologue_sizes(rows, seq_len, head_dim)
+    io = _io(x, "x")
+    px, pg, ppos, pc, ps, py, pr = _ptrs(
+        (x, "x", None, n), (gamma, "gamma", F32, head_dim), (positions, "positions", I32, seq_len),
+        (cos_tab, "cos_tab", F32, nt), (sin_tab, "sin_tab", F32, nt), (y, "y", x.dtype, n),
+        (rstd, "rstd", F32, nr))
     _check(load_library().xattn_qknorm_rope_fwd_table(
-        _ptr(x, "x"), _ptr(gamma, "gamma", torch.float32),
-        None if positions is None else _ptr(positions, "positions", torch.int32), float(theta),
-        _ptr(cos_tab, "cos_tab", torch.float32), _ptr(sin_tab, "sin_tab", torch.float32),
-        _ptr(y, "y", x.dtype), _ptr(rstd, "rstd", torch.float32), rows, seq_len, head_dim,
-        float(eps), _io(x, "x"), _stream(stream)), "xattn_qknorm_rope_fwd_table")
+        px, pg, ppos, float(theta), pc, ps, py, pr, rows, seq_len, head_dim, float(eps), io,
+        _stream(stream)), "xattn_qknorm_rope_fwd_table")
 
 
 def xattn_qknorm_rope_bwd_workspace_bytes(rows, seq_len, head_dim) -> int:
@@ -239,58 +281,66 @@ def xattn_qknorm_rope_bwd_workspace_bytes(rows, seq_len, head_dim) -> int:
 
 def xattn_qknorm_rope_bwd(dy, x, gamma, rstd, cos_tab, sin_tab, dx, dgamma, workspace, rows,
                           seq_len, head_dim, stream=None):
+    n, nr, nt = _prologue_sizes(rows, seq_len, head_dim)
+    io = _io(x, "x")
+    p = _ptrs((dy, "dy", x.dtype, n), (x, "x", None, n), (gamma, "gamma", F32, head_dim),
+              (rstd, "rstd", F32, nr), (cos_tab, "cos_tab", F32, nt),
+              (sin_tab, "sin_tab", F32, nt), (dx, "dx", x.dtype, n),
+              (dgamma, "dgamma", F32, head_dim), (workspace, "workspace", None, None))
     _check(load_library().xattn_qknorm_rope_bwd(
-        _ptr(dy, "dy", x.dtype), _ptr(x, "x"), _ptr(gamma, "gamma", torch.float32),
-        _ptr(rstd, "rstd", torch.float32), _ptr(cos_tab, "cos_tab", torch.float32),
-        _ptr(sin_tab, "sin_tab", torch.float32), _ptr(dx, "dx", x.dtype),
-        _ptr(dgamma, "dgamma", torch.float32), _ptr(workspace, "workspace"),
-        workspace.numel() * workspace.element_size(), rows, seq_len, head_dim, _io(x, "x"),
-        _stream(stream)), "xattn_qknorm_rope_bwd")
+        *p, _bytes(workspace, "workspace"), rows, seq_len, head_dim, io, _stream(stream)),
+        "xattn_qknorm_rope_bwd")
 
 
 def make_dims(q, num_heads, num_kv_heads, segments=None) -> Dims:
-    """segments: None, or (seg_lo, seg_hi) int32 device tensors [S] (see xattn_segments)."""
+    """q: [B*H, S, hd]; segments: None, or (seg_lo, seg_hi) int32 device tensors [S] (see
+    xattn_segments)."""
     bh, S, hd = q.shape
     if bh % num_heads:
         raise ValueError("q.shape[0] must be batch * num_heads")
     lo = hi = None
     if segments is not None:
-        lo = _ptr(segments[0], "seg_lo", torch.int32)
-        hi = _ptr(segments[1], "seg_hi", torch.int32)
+        lo, hi = _ptrs((segments[0], "seg_lo", I32, S), (segments[1], "seg_hi", I32, S))
     return Dims(bh // num_heads, S, num_heads, num_kv_heads, hd, _io(q, "q"), lo, hi)
 
 
 def xattn_segments(cu_seqlens, ndocs, seq_len, seg_lo, seg_hi, positions=None, stream=None):
-    _check(load_library().xattn_segments(
-        _ptr(cu_seqlens, "cu_seqlens", torch.int32), int(ndocs), int(seq_len),
-        _ptr(seg_lo, "seg_lo", torch.int32), _ptr(seg_hi, "seg_hi", torch.int32),
-        _ptr(positions, "positions", torch.int32), _stream(stream)), "xattn_segments")
+    S = int(seq_len)
+    p = _ptrs((cu_seqlens, "cu_seqlens", I32, int(ndocs) + 1), (seg_lo, "seg_lo", I32, S),
+              (seg_hi, "seg_hi", I32, S), (positions, "positions", I32, S))
+    _check(load_library().xattn_segments(p[0], int(ndocs), S, *p[1:], _stream(stream)),
+           "xattn_segments")
 
 
 def xattn_rope_cache_at(cos_tab, sin_tab, positions, rows, head_dim, theta, stream=None):
-    _check(load_library().xattn_rope_cache_at(
-        _ptr(cos_tab, "cos_tab", torch.float32), _ptr(sin_tab, "sin_tab", torch.float32),
-        _ptr(positions, "positions", torch.int32), rows, head_dim, theta, _stream(stream)),
-        "xattn_rope_cache_at")
+    nt = int(rows) * (int(head_dim) // 2)
+    p = _ptrs((cos_tab, "cos_tab", F32, nt), (sin_tab, "sin_tab", F32, nt),
+              (positions, "positions", I32, rows))
+    _check(load_library().xattn_rope_cache_at(*p, rows, head_dim, theta, _stream(stream)),
+           "xattn_rope_cache_at")
 
 
 def xattn_fwd(dims: Dims, q, k, v, out, lse, stream=None):
-    _check(load_library().xattn_fwd(
-        ctypes.byref(dims), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype),
-        _ptr(out, "out", q.dtype), _ptr(lse, "lse", torch.float32), _stream(stream)),
-        "xattn_fwd")
+    nq, nk, nr, _, _ = _sizes(dims)
+    _io(q, "q")
+    p = _ptrs((q, "q", None, nq), (k, "k", q.dtype, nk), (v, "v", q.dtype, nk),
+              (out, "out", q.dtype, nq), (lse, "lse", F32, nr))
+    _check(load_library().xattn_fwd(ctypes.byref(dims), *p, _stream(stream)), "xattn_fwd")
 
 
 def xattn_fwd_qnorm(dims: Dims, xq, gamma_q, cos_tab, sin_tab, eps, yq, rstd_q, k, v, out,
                     lse, stream=None):
-    pro = FwdPrologue(_ptr(xq, "xq"), _ptr(gamma_q, "gamma_q", torch.float32),
-                      _ptr(cos_tab, "cos_tab", torch.float32),
-                      _ptr(sin_tab, "sin_tab", torch.float32), float(eps),
-                      _ptr(yq, "yq", xq.dtype), _ptr(rstd_q, "rstd_q", torch.float32))
-    _check(load_library().xattn_fwd_qnorm(
-        ctypes.byref(dims), ctypes.byref(pro), _ptr(k, "k", xq.dtype), _ptr(v, "v", xq.dtype),
-        _ptr(out, "out", xq.dtype), _ptr(lse, "lse", torch.float32), _stream(stream)),
-        "xattn_fwd_qnorm")
+    nq, nk, nr, _, nt = _sizes(dims)
+    hd = dims.head_dim
+    _io(xq, "xq")
+    pxq, pg, pc, ps, pyq, pr, pk, pv, po, pl = _ptrs(
+        (xq, "xq", None, nq), (gamma_q, "gamma_q", F32, hd), (cos_tab, "cos_tab", F32, nt),
+        (sin_tab, "sin_tab", F32, nt), (yq, "yq", xq.dtype, nq), (rstd_q, "rstd_q", F32, nr),
+        (k, "k", xq.dtype, nk), (v, "v", xq.dtype, nk), (out, "out", xq.dtype, nq),
+        (lse, "lse", F32, nr))
+    pro = FwdPrologue(pxq, pg, pc, ps, float(eps), pyq, pr)
+    _check(load_library().xattn_fwd_qnorm(ctypes.byref(dims), ctypes.byref(pro), pk, pv, po, pl,
+                                          _stream(stream)), "xattn_fwd_qnorm")
 
 
 def xattn_bwd_workspace_bytes(dims: Dims, with_prologue: bool) -> int:
@@ -301,33 +351,38 @@ def xattn_bwd(dims: Dims, q, k, v, out, lse, dout, dq, dk, dv, prologue, workspa
               stream=None):
     """prologue: None or a dict with xq, xk, gamma_q, gamma_k, rstd_q, rstd_k, cos_tab,
     sin_tab, dgamma_q, dgamma_k tensors."""
-    pro = None
+    nq, nk, nr, nrk, nt = _sizes(dims)
+    hd = dims.head_dim
+    _io(q, "q")
+    specs = [(q, "q", None, nq), (k, "k", q.dtype, nk), (v, "v", q.dtype, nk),
+             (out, "out", q.dtype, nq), (lse, "lse", F32, nr), (dout, "dout", q.dtype, nq),
+             (dq, "dq", q.dtype, nq), (dk, "dk", q.dtype, nk), (dv, "dv", q.dtype, nk),
+             (workspace, "workspace", None, None)]
     if prologue is not None:
-        p = prologue
-        pro = Prologue(_ptr(p["xq"], "xq", q.dtype), _ptr(p["xk"], "xk", q.dtype),
-                       _ptr(p["gamma_q"], "gamma_q", torch.float32),
-                       _ptr(p["gamma_k"], "gamma_k", torch.float32),
-                       _ptr(p["rstd_q"], "rstd_q", torch.float32),
-                       _ptr(p["rstd_k"], "rstd_k", torch.float32),
-                       _ptr(p["cos_tab"], "cos_tab", torch.float32),
-                       _ptr(p["sin_tab"], "sin_tab", torch.float32),
-                       _ptr(p["dgamma_q"], "dgamma_q", torch.float32),
-                       _ptr(p["dgamma_k"], "dgamma_k", torch.float32))
+        pr = prologue
+        specs += [(pr["xq"], "xq", q.dtype, nq), (pr["xk"], "xk", q.dtype, nk),
+                  (pr["gamma_q"], "gamma_q", F32, hd), (pr["gamma_k"], "gamma_k", F32, hd),
+                  (pr["rstd_q"], "rstd_q", F32, nr), (pr["rstd_k"], "rstd_k", F32, nrk),
+                  (pr["cos_tab"], "cos_tab", F32, nt), (pr["sin_tab"], "sin_tab", F32, nt),
+                  (pr["dgamma_q"], "dgamma_q", F32, hd), (pr["dgamma_k"], "dgamma_k", F32, hd)]
+    p = _ptrs(*specs)
+    pro = Prologue(*p[10:]) if prologue is not None else None
     _check(load_library().xattn_bwd(
-        ctypes.byref(dims), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype),
-        _ptr(out, "out", q.dtype), _ptr(lse, "lse", torch.float32),
-        _ptr(dout, "dout", q.dtype), _ptr(dq, "dq", q.dtype), _ptr(dk, "dk", q.dtype),
-        _ptr(dv, "dv", q.dtype), ctypes.byref(pro) if pro is not None else None,
-        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-        _stream(stream)), "xattn_bwd")
+        ctypes.byref(dims), *p[:9], ctypes.byref(pro) if pro is not None else None, p[9],
+        _bytes(workspace, "workspace"), _stream(stream)), "xattn_bwd")
 
 
 def make_decode_dims(xq, k_cache, num_heads, num_kv_heads, cache_len) -> DecodeDims:
+    """xq: [B*H, q_len, hd]; k_cache: [B*Hkv, capacity, hd]."""
     bh, sq, hd = xq.shape
     if bh % num_heads:
         raise ValueError("xq.shape[0] must be batch * num_heads")
-    return DecodeDims(bh // num_heads, num_heads, num_kv_heads, hd, _io(xq, "xq"), sq,
-                      int(cache_len), k_cache.shape[1])
+    B = bh // num_heads
+    if k_cache.dim() != 3 or k_cache.shape[0] != B * num_kv_heads or k_cache.shape[2] != hd:
+        raise ValueError(f"k_cache must be [batch * num_kv_heads, capacity, head_dim] = "
+                         f"[{B * num_kv_heads}, capacity, {hd}], got {tuple(k_cache.shape)}")
+    return DecodeDims(B, num_heads, num_kv_heads, hd, _io(xq, "xq"), sq, int(cache_len),
+                      k_cache.shape[1])
 
 
 def xattn_decode_workspace_bytes(dims: DecodeDims) -> int:
@@ -336,13 +391,21 @@ def xattn_decode_workspace_bytes(dims: DecodeDims) -> int:
 
 def xattn_decode(dims: DecodeDims, xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, eps,
                  k_cache, v_cache, out, lse, workspace, stream=None):
+    d = dims
+    hd = d.head_dim
+    nq = d.batch * d.num_heads * d.q_len * hd
+    nk = d.batch * d.num_kv_heads * d.q_len * hd
+    nc = d.batch * d.num_kv_heads * d.capacity * hd
+    nt = d.capacity * (hd // 2)
+    _io(xq, "xq")
+    p = _ptrs((xq, "xq", None, nq), (xk, "xk", xq.dtype, nk), (v, "v", xq.dtype, nk),
+              (gamma_q, "gamma_q", F32, hd), (gamma_k, "gamma_k", F32, hd),
+              (cos_tab, "cos_tab", F32, nt), (sin_tab, "sin_tab", F32, nt),
+              (k_cache, "k_cache", xq.dtype, nc), (v_cache, "v_cache", xq.dtype, nc),
+              (out, "out", xq.dtype, nq), (lse, "lse", F32, d.batch * d.num_heads * d.q_len),
+              (workspace, "workspace", None, None))
     _check(load_library().xattn_decode(
-        ctypes.byref(dims), _ptr(xq, "xq"), _ptr(xk, "xk", xq.dtype), _ptr(v, "v", xq.dtype),
-        _ptr(gamma_q, "gamma_q", torch.float32), _ptr(gamma_k, "gamma_k", torch.float32),
-        _ptr(cos_tab, "cos_tab", torch.float32), _ptr(sin_tab, "sin_tab", torch.float32),
-        float(eps), _ptr(k_cache, "k_cache", xq.dtype), _ptr(v_cache, "v_cache", xq.dtype),
-        _ptr(out, "out", xq.dtype), _ptr(lse, "lse", torch.float32),
-        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        ctypes.byref(dims), *p[:7], float(eps), *p[7:], _bytes(workspace, "workspace"),
         _stream(stream)), "xattn_decode")
 
 
@@ -474,15 +537,19 @@ class Projection:
     def __init__(self, batch, seq_len, num_heads, num_kv_heads, head_dim, wq, wk, wv, wo,
                  bq=None, bk=None, bv=None, bo=None):
         self.B, self.S, self.H, self.Hkv, self.hd = batch, seq_len, num_heads, num_kv_heads, head_dim
-        self.d = wq.shape[0]
+        if not isinstance(wq, torch.Tensor) or wq.dim() != 2:
+            raise ValueError("wq must be a [model_dim, num_heads * head_dim] tensor")
+        self.d = d = wq.shape[0]
         self.dt = wq.dtype
+        self.nq, self.nk = nq, nk = num_heads * head_dim, num_kv_heads * head_dim
+        self.M = batch * seq_len
         self.dims = Dims(batch, seq_len, num_heads, num_kv_heads, head_dim, _io(wq, "wq"))
         self._keep = (wq, wk, wv, wo, bq, bk, bv, bo)
-        f32 = torch.float32
-        self.p = Proj(self.d, _ptr(wq, "wq"), _ptr(wk, "wk", self.dt), _ptr(wv, "wv", self.dt),
-                      _ptr(wo, "wo", self.dt), _ptr(bq, "bq", f32), _ptr(bk, "bk", f32),
-                      _ptr(bv, "bv", f32), _ptr(bo, "bo", f32))
-        n = int(load_library().xattn_proj_workspace_bytes(ctypes.byref(self.dims), self.d))
+        self.p = Proj(d, *_ptrs((wq, "wq", None, d * nq), (wk, "wk", self.dt, d * nk),
+                                (wv, "wv", self.dt, d * nk), (wo, "wo", self.dt, nq * d),
+                                (bq, "bq", F32, nq), (bk, "bk", F32, nk), (bv, "bv", F32, nk),
+                                (bo, "bo", F32, d)))
+        n = int(load_library().xattn_proj_workspace_bytes(ctypes.byref(self.dims), d))
         if n == 0:
             raise XattnError(1, "xattn_proj_workspace_bytes", xattn_last_error())
         self.ws = _workspace(n, wq.device)
@@ -490,43 +557,48 @@ class Projection:
     def _e(self, *shape, dtype=None):
         return torch.empty(shape, dtype=dtype or self.dt, device=self.ws.device)
 
+    def _call(self, fn, specs, where, stream):
+        p = _ptrs(*specs, (self.ws, "ws", None, None))
+        _check(getattr(load_library(), fn)(ctypes.byref(self.dims), ctypes.byref(self.p), *p,
+                                           _bytes(self.ws, "ws"), _stream(stream)), where)
+
     def qkv_fwd(self, x, stream=None):
-        BH, BKV = self.B * self.H, self.B * self.Hkv
-        xq, xk, v = self._e(BH, self.S, self.hd), self._e(BKV, self.S, self.hd), \
-            self._e(BKV, self.S, self.hd)
-        _check(load_library().xattn_qkv_proj_fwd(
-            ctypes.byref(self.dims), ctypes.byref(self.p), _ptr(x, "x", self.dt),
-            _ptr(xq, "xq"), _ptr(xk, "xk"), _ptr(v, "v"), _ptr(self.ws, "ws"),
-            self.ws.numel(), _stream(stream)), "xattn_qkv_proj_fwd")
+        M, nq, nk, dt = self.M, self.nq, self.nk, self.dt
+        xq, xk, v = self._e(self.B * self.H, self.S, self.hd), \
+            self._e(self.B * self.Hkv, self.S, self.hd), self._e(self.B * self.Hkv, self.S, self.hd)
+        self._call("xattn_qkv_proj_fwd", [(x, "x", dt, M * self.d), (xq, "xq", dt, M * nq),
+                                          (xk, "xk", dt, M * nk), (v, "v", dt, M * nk)],
+                   "xattn_qkv_proj_fwd", stream)
         return xq, xk, v
 
     def out_fwd(self, out, stream=None):
-        y = self._e(self.B * self.S, self.d)
-        _check(load_library().xattn_out_proj_fwd(
-            ctypes.byref(self.dims), ctypes.byref(self.p), _ptr(out, "out", self.dt),
-            _ptr(y, "y"), _ptr(self.ws, "ws"), self.ws.numel(), _stream(stream)),
-            "xattn_out_proj_fwd")
+        y = self._e(self.M, self.d)
+        self._call("xattn_out_proj_fwd", [(out, "out", self.dt, self.M * self.nq),
+                                          (y, "y", self.dt, self.M * self.d)],
+                   "xattn_out_proj_fwd", stream)
         return y
 
     def out_bwd(self, out, dy, with_bias=True, stream=None):
+        M, nq, d, dt = self.M, self.nq, self.d, self.dt
         dout = self._e(self.B * self.H, self.S, self.hd)
-        dwo = self._e(self.H * self.hd, self.d, dtype=torch.float32)
-        dbo = self._e(self.d, dtype=torch.float32) if with_bias else None
-        _check(load_library().xattn_out_proj_bwd(
-            ctypes.byref(self.dims), ctypes.byref(self.p), _ptr(out, "out", self.dt),
-            _ptr(dy, "dy", self.dt), _ptr(dout, "dout"), _ptr(dwo, "dwo"), _ptr(dbo, "dbo"),
-            _ptr(self.ws, "ws"), self.ws.numel(), _stream(stream)), "xattn_out_proj_bwd")
+        dwo = self._e(nq, d, dtype=F32)
+        dbo = self._e(d, dtype=F32) if with_bias else None
+        self._call("xattn_out_proj_bwd", [(out, "out", dt, M * nq), (dy, "dy", dt, M * d),
+                                          (dout, "dout", dt, M * nq), (dwo, "dwo", F32, nq * d),
+                                          (dbo, "dbo", F32, d)],
+                   "xattn_out_proj_bwd", stream)
         return dout, dwo, dbo
 
     def qkv_bwd(self, x, dxq, dxk, dv, with_bias=True, stream=None):
-        nq, nk = self.H * self.hd, self.Hkv * self.hd
-        dx = self._e(self.B * self.S, self.d)
-        f32 = torch.float32
-        dw = [self._e(self.d, n, dtype=f32) for n in (nq, nk, nk)]
-        db = [self._e(n, dtype=f32) if with_bias else None for n in (nq, nk, nk)]
-        _check(load_library().xattn_qkv_proj_bwd(
-            ctypes.byref(self.dims), ctypes.byref(self.p), _ptr(x, "x", self.dt),
-            _ptr(dxq, "dxq", self.dt), _ptr(dxk, "dxk", self.dt), _ptr(dv, "dv", self.dt),
-            _ptr(dx, "dx"), *[_ptr(t, "dw") for t in dw], *[_ptr(t, "db") for t in db],
-            _ptr(self.ws, "ws"), self.ws.numel(), _stream(stream)), "xattn_qkv_proj_bwd")
+        M, nq, nk, d, dt = self.M, self.nq, self.nk, self.d, self.dt
+        dx = self._e(M, d)
+        dw = [self._e(d, n, dtype=F32) for n in (nq, nk, nk)]
+        db = [self._e(n, dtype=F32) if with_bias else None for n in (nq, nk, nk)]
+        self._call("xattn_qkv_proj_bwd",
+                   [(x, "x", dt, M * d), (dxq, "dxq", dt, M * nq), (dxk, "dxk", dt, M * nk),
+                    (dv, "dv", dt, M * nk), (dx, "dx", dt, M * d),
+                    (dw[0], "dwq", F32, d * nq), (dw[1], "dwk", F32, d * nk),
+                    (dw[2], "dwv", F32, d * nk), (db[0], "dbq", F32, nq),
+                    (db[1], "dbk", F32, nk), (db[2], "dbv", F32, nk)],
+                   "xattn_qkv_proj_bwd", stream)
         return dx, dw, db

@@ -1444,13 +1444,19 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_kernel(
   };
 
   constexpr int NL = 2 * D::PER + 1;  // loads per wave per tile
-  // prologue: tiles 0..3 in flight; S and dP of tile 0; row operands of tile 1
+  // The copy waits count tiles in flight: the prologue issues NB tiles and needs tiles 0
+  // and 1 (NB - 2 may stay in flight); iteration t has issued tiles up to t + NB - 1 and
+  // needs tile t + 2 (NB - 3 may stay in flight).  The loop reads tile t + 2 while tiles
+  // t + 1 and t are still referenced, so at least three buffers are needed.
+  static_assert(NB >= 3, "the pipelined dk/dv loop needs at least three staged tiles");
+  constexpr int kWaitPrologue = (NB - 2) * NL, kWaitIter = (NB - 3) * NL;
+  // prologue: tiles 0..NB-1 in flight; S and dP of tile 0; row operands of tile 1
   bf16x8 qa[HD / 16], da[HD / 16];
   f32x16 s_cur = zero16(), p_cur = zero16();
   if (nst > 0) {
 #pragma unroll
     for (int u = 0; u < NB; ++u) issue_next();
-    wait_vm<2 * NL>();  // tiles 0 and 1
+    wait_vm<kWaitPrologue>();  // tiles 0 and 1
     __builtin_amdgcn_s_barrier();
     lds_acquire();
     rows_of<HD>(qa, lmine, al);
@@ -1466,7 +1472,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_kernel(
 
   // Iteration t: P / dS of tile t under the S / dP products of tile t + 1, then tile t's
   // dV / dK products.  Tile t's buffer is free after the barrier (its last reads, the
-  // transposed operands, are complete by then) and receives tile t + 4.
+  // transposed operands, are complete by then) and receives tile t + NB.
   auto iter = [&](auto mask_tag, int t, int i) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const lptr cur = lmine + (2 * (t % NB)) * TILEB;
@@ -1511,11 +1517,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_kernel(
     // P and dS are formed here, under the matrix products, not after the barrier
     asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(db[0]), "v"(db[1]));
     __builtin_amdgcn_sched_barrier(0);
-    // tile t + 2 has landed for every wave (t + 3 may still be in flight)
-    wait_vm<NL>();
+    // tile t + 2 has landed for every wave (later tiles may still be in flight)
+    wait_vm<kWaitIter>();
     __builtin_amdgcn_s_barrier();
     lds_acquire();
-    issue_next();  // tile t + 4 into tile t's buffer
+    issue_next();  // tile t + NB into tile t's buffer
     const lptr nx2 = lmine + (2 * ((t + 2) % NB)) * TILEB;
     rows_of<HD>(qa, nx2, al);
     rows_of<HD>(da, nx2 + TILEB, al);

@@ -307,7 +307,7 @@ const char* xattn_status_string(xattn_status s) {
   switch (s) {
     case XATTN_OK: return "XATTN_OK";
     case XATTN_ERR_INVALID_ARG: return "XATTN_ERR_INVALID_ARG: invalid argument";
-    case XATTN_ERR_UNSUPPORTED: return "XATTN_ERR_UNSUPPORTED: unsupported head_dim";
+    case XATTN_ERR_UNSUPPORTED: return "XATTN_ERR_UNSUPPORTED: shape not supported";
     case XATTN_ERR_HIP: return "XATTN_ERR_HIP: HIP runtime error";
   }
   return "unknown xattn_status";

@@ -59,7 +59,8 @@ typedef enum {
   XATTN_OK = 0,
   XATTN_ERR_INVALID_ARG = 1,  /* null pointer, size <= 0, H % Hkv != 0, odd head_dim,
                                  misaligned pointer, element count >= 2^31, bad dtype */
-  XATTN_ERR_UNSUPPORTED = 2,  /* head_dim not in {16, 32, 64, 128} */
+  XATTN_ERR_UNSUPPORTED = 2,  /* a valid shape this build does not run: head_dim not in
+                                 {16, 32, 64, 128}, or a decode call beyond its row limit */
   XATTN_ERR_HIP = 3           /* a kernel launch reported a HIP error */
 } xattn_status;
 

@@ -291,6 +291,101 @@ def test_profile_stop_validation_and_empty_session(lib):
 
 def test_python_binding_fails_loudly_without_device_tensors():
     import torch
-    q = torch.zeros(16, 8, 64)
+    q, k = torch.zeros(16, 8, 64), torch.zeros(4, 8, 64)
     with pytest.raises(ValueError, match="device tensor"):
-        X.attn_fwd(q, q, q, 8, 2)
+        X.attn_fwd(q, k, k, 8, 2)
+
+
+# The binding checks every tensor's element count against the call's dimensions before it
+# looks at placement: the C ABI receives raw pointers, so a short tensor would otherwise
+# reach the kernels.  CPU tensors of the right sizes get as far as the placement check.
+def _cpu(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def test_binding_checks_attention_tensor_sizes():
+    import torch
+    B, S, H, Hkv, hd = 2, 8, 4, 2, 64
+    q, k = _cpu(B * H, S, hd), _cpu(B * Hkv, S, hd)
+    lse = _cpu(B * H * S, dtype=torch.float32)
+    d = X.make_dims(q, H, Hkv)
+    with pytest.raises(ValueError, match="device tensor"):
+        X.xattn_fwd(d, q, k, k, q.clone(), lse)
+    short_k = _cpu(B * Hkv, S - 1, hd)
+    with pytest.raises(ValueError, match="k must hold 2048 elements"):
+        X.xattn_fwd(d, q, short_k, k, q.clone(), lse)
+    with pytest.raises(ValueError, match="lse must hold 64 elements"):
+        X.xattn_fwd(d, q, k, k, q.clone(), lse[:-1])
+    with pytest.raises(ValueError, match="out must hold"):
+        X.xattn_fwd(d, q, k, k, k.clone(), lse)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="dv must hold"):
+        X.xattn_bwd(d, q, k, k, q, lse, q, q.clone(), k.clone(), q.clone(), None, ws)
+    f32 = torch.float32
+    pro = dict(xq=q, xk=k, gamma_q=_cpu(hd, dtype=f32), gamma_k=_cpu(hd, dtype=f32),
+               rstd_q=_cpu(B * H * S, dtype=f32), rstd_k=_cpu(B * Hkv * S, dtype=f32),
+               cos_tab=_cpu(S, hd // 2, dtype=f32), sin_tab=_cpu(S - 1, hd // 2, dtype=f32),
+               dgamma_q=_cpu(hd, dtype=f32), dgamma_k=_cpu(hd, dtype=f32))
+    with pytest.raises(ValueError, match="sin_tab must hold 256 elements"):
+        X.xattn_bwd(d, q, k, k, q, lse, q, q.clone(), k.clone(), k.clone(), pro, ws)
+    pro["sin_tab"] = pro["cos_tab"].clone()
+    pro["rstd_k"] = _cpu(B * H * S, dtype=f32)  # sized like rstd_q: wrong
+    with pytest.raises(ValueError, match="rstd_k must hold 32 elements"):
+        X.xattn_bwd(d, q, k, k, q, lse, q, q.clone(), k.clone(), k.clone(), pro, ws)
+    with pytest.raises(ValueError, match="rstd_q must hold"):
+        X.xattn_fwd_qnorm(d, q, pro["gamma_q"], pro["cos_tab"], pro["sin_tab"], 1e-5, q.clone(),
+                          lse[:8], k, k, q.clone(), lse)
+    seg = _cpu(S - 2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="seg_lo must hold 8 elements"):
+        X.make_dims(q, H, Hkv, (seg, seg))
+
+
+def test_binding_checks_prologue_and_table_sizes():
+    import torch
+    f32 = torch.float32
+    rows, S, hd = 3, 10, 32
+    x, g = _cpu(rows, S, hd), _cpu(hd, dtype=f32)
+    cs, rs = _cpu(S, hd // 2, dtype=f32), _cpu(rows * S, dtype=f32)
+    with pytest.raises(ValueError, match="cos_tab must hold 160 elements"):
+        X.xattn_qknorm_rope_fwd(x, g, cs[:-1], cs, x.clone(), rs, rows, S, hd, 1e-5)
+    with pytest.raises(ValueError, match="gamma must hold 32 elements"):
+        X.xattn_qknorm_rope_fwd(x, g[:16], cs, cs, x.clone(), rs, rows, S, hd, 1e-5)
+    with pytest.raises(ValueError, match="y must hold"):
+        X.xattn_qknorm_rope_fwd(x, g, cs, cs, x[:2].clone(), rs, rows, S, hd, 1e-5)
+    with pytest.raises(ValueError, match="positions must hold 10 elements"):
+        X.xattn_qknorm_rope_fwd_table(x, g, _cpu(S + 1, dtype=torch.int32), 1e4, cs, cs,
+                                      x.clone(), rs, rows, S, hd, 1e-5)
+    with pytest.raises(ValueError, match="rstd must hold 30 elements"):
+        X.xattn_qknorm_rope_bwd(x, x, g, rs[:-1], cs, cs, x.clone(), g.clone(),
+                                torch.zeros(16, dtype=torch.uint8), rows, S, hd)
+    with pytest.raises(ValueError, match="sin_tab must hold 64 elements"):
+        X.xattn_rope_cache(_cpu(4, 16, dtype=f32), _cpu(3, 16, dtype=f32), 4, 32, 1e4)
+    with pytest.raises(ValueError, match="positions must hold 5 elements"):
+        X.xattn_rope_cache_at(_cpu(5, 16, dtype=f32), _cpu(5, 16, dtype=f32),
+                              _cpu(4, dtype=torch.int32), 5, 32, 1e4)
+    with pytest.raises(ValueError, match="cu_seqlens must hold 3 elements"):
+        X.xattn_segments(_cpu(4, dtype=torch.int32), 2, 9, *(_cpu(9, dtype=torch.int32)
+                                                              for _ in range(3)))
+
+
+def test_binding_checks_decode_sizes():
+    import torch
+    f32 = torch.float32
+    B, H, Hkv, hd, q_len, cap = 2, 8, 2, 128, 1, 40
+    xq, xk = _cpu(B * H, q_len, hd), _cpu(B * Hkv, q_len, hd)
+    kc = _cpu(B * Hkv, cap, hd)
+    g, tab = _cpu(hd, dtype=f32), _cpu(cap, hd // 2, dtype=f32)
+    with pytest.raises(ValueError, match="k_cache must be"):
+        X.make_decode_dims(xq, _cpu(B * Hkv + 1, cap, hd), H, Hkv, 10)
+    d = X.make_decode_dims(xq, kc, H, Hkv, 10)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    lse = _cpu(B * H * q_len, dtype=f32)
+    with pytest.raises(ValueError, match="cos_tab must hold 2560 elements"):
+        X.xattn_decode(d, xq, xk, xk, g, g, tab[:-1], tab, 1e-6, kc, kc.clone(), xq.clone(),
+                       lse, ws)
+    with pytest.raises(ValueError, match="v_cache must hold"):
+        X.xattn_decode(d, xq, xk, xk, g, g, tab, tab, 1e-6, kc, kc[:, :-1].clone(), xq.clone(),
+                       lse, ws)
+    with pytest.raises(ValueError, match="device tensor"):
+        X.xattn_decode(d, xq, xk, xk, g, g, tab, tab, 1e-6, kc, kc.clone(), xq.clone(), lse, ws)

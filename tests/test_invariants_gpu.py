@@ -74,14 +74,20 @@ def test_causal_no_peeking_bitwise(dtype, hd):
     np.testing.assert_array_equal(c[4][:, t + 1:], a[4][:, t + 1:])
 
 
-@pytest.mark.parametrize("idx", [2, 4, 5])
-def test_backward_is_bitwise_reproducible(idx):
-    """dq, dk, dv and dgamma are bitwise identical over repeated runs (no atomics;
-    fixed reduction orders)."""
+# (workload, replaced fields): workloads 3 and 4 at full size run the shared-tile dk/dv
+# kernel, workload 4 at batch 4 the private one, workload 5 the pipelined one, workload 2
+# the generic fp32 kernels.
+DETERMINISM = [(2, {}), (3, {}), (4, {}), (4, dict(batch=4)), (5, {})]
+
+
+@pytest.mark.parametrize("idx,kw", DETERMINISM,
+                         ids=[f"w{i}" + ("_" + "_".join(f"{k}{v}" for k, v in kw.items())
+                                         if kw else "") for i, kw in DETERMINISM])
+def test_backward_is_bitwise_reproducible(idx, kw):
+    """out, lse, dq, dk, dv and dgamma are bitwise identical over repeated runs (no
+    atomics; fixed reduction orders)."""
     from causal_gqa_attention_amd.step import AttentionStep
-    w = W.WORKLOADS[idx]
-    if idx == 4:
-        w = w.replace(batch=4)
+    w = W.WORKLOADS[idx].replace(**kw)
     x = W.make_inputs(w)
     note(f"determinism {w}")
     step = AttentionStep(w.batch, w.seq_len, w.num_heads, w.num_kv_heads, w.head_dim, w.dtype,
