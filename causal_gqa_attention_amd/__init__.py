@@ -145,18 +145,26 @@ def load_library() -> ctypes.CDLL:
 # ----------------------------------------------------------------------------------------
 # marshalling helpers
 # ----------------------------------------------------------------------------------------
+class AtLeast(int):
+    """An element count that a tensor may exceed (a RoPE table with more rows than the call
+    reads)."""
+
+
 def _ptrs(*specs):
     """Device pointers of tensors given as (tensor, name, dtype, numel) specs, None entries
     passing through as NULL.  Every tensor is checked for its element count (numel, when
-    not None: a shorter tensor would let the kernels read or write past it) and its dtype
-    before any is checked for placement and contiguity, so a size mismatch is reported as
-    such wherever the tensors live."""
+    not None: exactly, or at least for an AtLeast count; a shorter tensor would let the
+    kernels read or write past it) and its dtype before any is checked for placement and
+    contiguity, so a size mismatch is reported as such wherever the tensors live."""
     for t, name, dtype, numel in specs:
         if t is None:
             continue
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
-        if numel is not None and t.numel() != int(numel):
+        if isinstance(numel, AtLeast) and t.numel() < numel:
+            raise ValueError(f"{name} must hold at least {int(numel)} elements for these "
+                             f"dimensions, got {t.numel()} (shape {tuple(t.shape)})")
+        if numel is not None and not isinstance(numel, AtLeast) and t.numel() != int(numel):
             raise ValueError(f"{name} must hold {int(numel)} elements for these dimensions, "
                              f"got {t.numel()} (shape {tuple(t.shape)})")
         if dtype is not None and t.dtype != dtype:
@@ -243,7 +251,8 @@ def xattn_profile_stop(max_entries: int = 32) -> dict:
 
 def xattn_rope_cache(cos_tab, sin_tab, seq_len, head_dim, theta, stream=None):
     nt = int(seq_len) * (int(head_dim) // 2)
-    pc, ps = _ptrs((cos_tab, "cos_tab", F32, nt), (sin_tab, "sin_tab", F32, nt))
+    pc, ps = _ptrs((cos_tab, "cos_tab", F32, AtLeast(nt)),
+                   (sin_tab, "sin_tab", F32, AtLeast(nt)))
     _check(load_library().xattn_rope_cache(pc, ps, seq_len, head_dim, float(theta),
                                            _stream(stream)), "xattn_rope_cache")
 
@@ -256,8 +265,9 @@ def xattn_qknorm_rope_fwd(x, gamma, cos_tab, sin_tab, y, rstd, rows, seq_len, he
                           stream=None):
     n, nr, nt = _prologue_sizes(rows, seq_len, head_dim)
     io = _io(x, "x")
-    p = _ptrs((x, "x", None, n), (gamma, "gamma", F32, head_dim), (cos_tab, "cos_tab", F32, nt),
-              (sin_tab, "sin_tab", F32, nt), (y, "y", x.dtype, n), (rstd, "rstd", F32, nr))
+    p = _ptrs((x, "x", None, n), (gamma, "gamma", F32, head_dim),
+              (cos_tab, "cos_tab", F32, AtLeast(nt)), (sin_tab, "sin_tab", F32, AtLeast(nt)),
+              (y, "y", x.dtype, n), (rstd, "rstd", F32, nr))
     _check(load_library().xattn_qknorm_rope_fwd(*p, rows, seq_len, head_dim, float(eps), io,
                                                 _stream(stream)), "xattn_qknorm_rope_fwd")
 
@@ -268,7 +278,8 @@ def xattn_qknorm_rope_fwd_table(x, gamma, positions, theta, cos_tab, sin_tab, y,
     io = _io(x, "x")
     px, pg, ppos, pc, ps, py, pr = _ptrs(
         (x, "x", None, n), (gamma, "gamma", F32, head_dim), (positions, "positions", I32, seq_len),
-        (cos_tab, "cos_tab", F32, nt), (sin_tab, "sin_tab", F32, nt), (y, "y", x.dtype, n),
+        (cos_tab, "cos_tab", F32, AtLeast(nt)), (sin_tab, "sin_tab", F32, AtLeast(nt)),
+        (y, "y", x.dtype, n),
         (rstd, "rstd", F32, nr))
     _check(load_library().xattn_qknorm_rope_fwd_table(
         px, pg, ppos, float(theta), pc, ps, py, pr, rows, seq_len, head_dim, float(eps), io,
@@ -284,8 +295,8 @@ def xattn_qknorm_rope_bwd(dy, x, gamma, rstd, cos_tab, sin_tab, dx, dgamma, work
     n, nr, nt = _prologue_sizes(rows, seq_len, head_dim)
     io = _io(x, "x")
     p = _ptrs((dy, "dy", x.dtype, n), (x, "x", None, n), (gamma, "gamma", F32, head_dim),
-              (rstd, "rstd", F32, nr), (cos_tab, "cos_tab", F32, nt),
-              (sin_tab, "sin_tab", F32, nt), (dx, "dx", x.dtype, n),
+              (rstd, "rstd", F32, nr), (cos_tab, "cos_tab", F32, AtLeast(nt)),
+              (sin_tab, "sin_tab", F32, AtLeast(nt)), (dx, "dx", x.dtype, n),
               (dgamma, "dgamma", F32, head_dim), (workspace, "workspace", None, None))
     _check(load_library().xattn_qknorm_rope_bwd(
         *p, _bytes(workspace, "workspace"), rows, seq_len, head_dim, io, _stream(stream)),
@@ -314,7 +325,7 @@ def xattn_segments(cu_seqlens, ndocs, seq_len, seg_lo, seg_hi, positions=None, s
 
 def xattn_rope_cache_at(cos_tab, sin_tab, positions, rows, head_dim, theta, stream=None):
     nt = int(rows) * (int(head_dim) // 2)
-    p = _ptrs((cos_tab, "cos_tab", F32, nt), (sin_tab, "sin_tab", F32, nt),
+    p = _ptrs((cos_tab, "cos_tab", F32, AtLeast(nt)), (sin_tab, "sin_tab", F32, AtLeast(nt)),
               (positions, "positions", I32, rows))
     _check(load_library().xattn_rope_cache_at(*p, rows, head_dim, theta, _stream(stream)),
            "xattn_rope_cache_at")
@@ -334,8 +345,9 @@ def xattn_fwd_qnorm(dims: Dims, xq, gamma_q, cos_tab, sin_tab, eps, yq, rstd_q, 
     hd = dims.head_dim
     _io(xq, "xq")
     pxq, pg, pc, ps, pyq, pr, pk, pv, po, pl = _ptrs(
-        (xq, "xq", None, nq), (gamma_q, "gamma_q", F32, hd), (cos_tab, "cos_tab", F32, nt),
-        (sin_tab, "sin_tab", F32, nt), (yq, "yq", xq.dtype, nq), (rstd_q, "rstd_q", F32, nr),
+        (xq, "xq", None, nq), (gamma_q, "gamma_q", F32, hd),
+        (cos_tab, "cos_tab", F32, AtLeast(nt)), (sin_tab, "sin_tab", F32, AtLeast(nt)),
+        (yq, "yq", xq.dtype, nq), (rstd_q, "rstd_q", F32, nr),
         (k, "k", xq.dtype, nk), (v, "v", xq.dtype, nk), (out, "out", xq.dtype, nq),
         (lse, "lse", F32, nr))
     pro = FwdPrologue(pxq, pg, pc, ps, float(eps), pyq, pr)
@@ -363,7 +375,8 @@ def xattn_bwd(dims: Dims, q, k, v, out, lse, dout, dq, dk, dv, prologue, workspa
         specs += [(pr["xq"], "xq", q.dtype, nq), (pr["xk"], "xk", q.dtype, nk),
                   (pr["gamma_q"], "gamma_q", F32, hd), (pr["gamma_k"], "gamma_k", F32, hd),
                   (pr["rstd_q"], "rstd_q", F32, nr), (pr["rstd_k"], "rstd_k", F32, nrk),
-                  (pr["cos_tab"], "cos_tab", F32, nt), (pr["sin_tab"], "sin_tab", F32, nt),
+                  (pr["cos_tab"], "cos_tab", F32, AtLeast(nt)),
+                  (pr["sin_tab"], "sin_tab", F32, AtLeast(nt)),
                   (pr["dgamma_q"], "dgamma_q", F32, hd), (pr["dgamma_k"], "dgamma_k", F32, hd)]
     p = _ptrs(*specs)
     pro = Prologue(*p[10:]) if prologue is not None else None
@@ -400,7 +413,7 @@ def xattn_decode(dims: DecodeDims, xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab
     _io(xq, "xq")
     p = _ptrs((xq, "xq", None, nq), (xk, "xk", xq.dtype, nk), (v, "v", xq.dtype, nk),
               (gamma_q, "gamma_q", F32, hd), (gamma_k, "gamma_k", F32, hd),
-              (cos_tab, "cos_tab", F32, nt), (sin_tab, "sin_tab", F32, nt),
+              (cos_tab, "cos_tab", F32, AtLeast(nt)), (sin_tab, "sin_tab", F32, AtLeast(nt)),
               (k_cache, "k_cache", xq.dtype, nc), (v_cache, "v_cache", xq.dtype, nc),
               (out, "out", xq.dtype, nq), (lse, "lse", F32, d.batch * d.num_heads * d.q_len),
               (workspace, "workspace", None, None))

@@ -17,10 +17,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libxattn.so")
-SOURCES = ["attn.hip", "attn_bf16.hip", "prologue.hip", "decode.hip", "proj.hip",
-           "proj_gemm.cpp", "xattn_api.cpp", "profile.cpp"]
-# The projection GEMMs call hipBLASLt (a library of the ROCm install, found there at run time).
-LINK_LIBS = ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lhipblaslt"]
+SOURCES = ["attn.hip", "attn_bf16.hip", "prologue.hip", "decode.hip", "proj.hip", "gemm.hip",
+           "xattn_api.cpp", "profile.cpp"]
+LINK_LIBS: list = []
 # Per-source extra flags.  attn_bf16.hip: MFMA results go to VGPRs (the score tiles are
 # consumed by VALU right away; AGPR results would need a copy per element).
 SOURCE_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}

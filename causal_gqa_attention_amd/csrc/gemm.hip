@@ -1,0 +1,410 @@
+// Dense GEMMs of the projections around attention (Mint documentation 5.3.1-5.3.2:
+// Q = X Wq + bq, K = X Wk + bk, V = X Wv + bv, output Concat(heads) Wo + bo, weights
+// [d_in, d_out] applied as x @ W; "Phase T12: bf16 mixed precision", precision table: the
+// linear GEMMs take bf16 in and accumulate in fp32, weight gradients are fp32).
+//
+// Row-major operands, three forms: NN (C = A B, A [m, k], B [k, n]), NT (C = A B^T, B
+// stored [n, k]) and TN (C = A^T B, A stored [k, m]).  A job may sum up to three K
+// segments (own A and B each) in one fp32 accumulator before its single rounding, and one
+// launch runs up to three jobs.  Outputs: io-dtype token rows (+ bias), io-dtype head
+// layout ([B*heads, S, hd], + bias: the head split of the projections), or fp32 rows.
+// fp32 outputs may split K over several workgroups; the partial products then land in a
+// workspace and a second kernel adds them in split order, so every result has a fixed
+// summation order (bitwise reproducible run to run).
+//
+// bf16 kernel (gfx950):
+//   * 128 x 128 output tile per 256-thread workgroup, four waves of 64 x 64 (2 x 2
+//     v_mfma_f32_32x32x16_bf16 blocks), K in steps of 64, two workgroups per CU.
+//   * Both operand tiles go HBM -> LDS with direct-to-LDS buffer loads (no register round
+//     trip), one K step ahead of the MFMAs.  A chunk that lies outside its matrix gets a
+//     byte offset past the buffer's range, which the hardware turns into zeros, so ragged
+//     m, n and k need no other handling.
+//   * K-contiguous tiles ([128][64]: rows of 128 bytes) are read with ds_read_b128; the
+//     16-byte chunks of row r are XOR-swizzled by (r >> 1) & 7 so that the 16 rows one
+//     read phase touches sit on 16 distinct bank groups.  M/N-contiguous tiles ([64][128]:
+//     rows of 256 bytes) are read with the transposing ds_read_b64_tr_b16 (two reads give
+//     a lane its 8 k-slots of one column); their chunks are swizzled by 4 * (r & 3), which
+//     spreads the four rows of a read phase over the four quarters of the bank window.
+//   * The MFMA takes the B fragment as its A operand, so each accumulator holds a block of
+//     C^T: a lane owns one output row and runs of four adjacent columns, which the
+//     epilogue stores as 8- or 16-byte vectors (with the bias add and the rounding).
+#include <algorithm>
+
+#include "lds_copy.h"
+#include "xattn_device.h"
+#include "xattn_internal.h"
+
+namespace xattn {
+namespace {
+
+constexpr int kTM = 128, kTN = 128, kTK = 64;
+constexpr int kOpBytes = kTM * kTK * 2;  // one staged operand tile: 16 KiB
+constexpr int kGemmBuf = 2;              // staged K steps
+constexpr uint32_t kOutside = 0x80000000u;  // a byte offset past every operand buffer
+
+// Jobs as the kernels see them: the host-side description plus the tile bookkeeping.
+struct KJob {
+  GemmJob j;
+  int tiles_n, tiles, splits, steps_per_split, block_begin;
+};
+struct KArgs {
+  KJob job[kGemmMaxJobs];
+  int njobs, S, hd;
+};
+
+__device__ __forceinline__ int find_job(const KArgs& g, int& bid) {
+  int j = 0;
+#pragma unroll
+  for (int q = 1; q < kGemmMaxJobs; ++q)
+    if (q < g.njobs && bid >= g.job[q].block_begin) j = q;
+  bid -= g.job[j].block_begin;
+  return j;
+}
+
+// Per-lane chunk offsets of one wave's four 1 KiB copies of a staged operand tile.
+// K-contiguous tile: copy c (0..15 over the workgroup) holds rows 8c .. 8c+7, lane l the
+// physical chunk l & 7 of row 8c + l / 8, i.e. the logical chunk (l & 7) ^ swizzle.
+// M/N-contiguous tile: copy c holds k-rows 4c .. 4c+3, lane l the physical chunk l & 15 of
+// row 4c + l / 16.
+template <bool KC>
+__device__ __forceinline__ void tile_offsets(uint32_t (&off)[4], const GemmMat& a, int rows,
+                                             int kdim, int r0, int k0, int wv, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = 4 * wv + i;
+    if constexpr (KC) {
+      const int row = 8 * c + (lane >> 3);
+      const int lc = (lane & 7) ^ (4 * (c & 1) + (lane >> 4));
+      const int rg = r0 + row, kg = k0 + 8 * lc;
+      off[i] = (rg < rows && kg < kdim) ? (uint32_t)(((size_t)rg * a.ld + kg) * 2) : kOutside;
+    } else {
+      const int kr = 4 * c + (lane >> 4);
+      const int lc = (lane & 15) ^ (4 * ((lane >> 4) & 3));
+      const int kg = k0 + kr, rg = r0 + 8 * lc;
+      off[i] = (kg < kdim && rg < rows) ? (uint32_t)(((size_t)kg * a.ld + rg) * 2) : kOutside;
+    }
+  }
+}
+
+// Fragment of 32 rows (K-contiguous tile) starting at tile row R0: logical chunk 2c + h of
+// row R0 + lane % 32 sits at R0 * 128 + (a_lane ^ (c << 5)).
+__device__ __forceinline__ uint32_t kc_lane(int lane) {
+  const int r = lane & 31, h = lane >> 5;
+  return (uint32_t)(r * 128) | (uint32_t)((h ^ ((r >> 1) & 7)) << 4);
+}
+// Transposing reads (M/N-contiguous tile) of the 8 k-slots 16c + 8h + {0..7} of column
+// C0 + lane % 32: rows 16c + 8h + {0..3} at 16c*256 + (t_lane ^ ((C0 / 8) << 4)), rows
+// + 4 at 1 KiB further.
+__device__ __forceinline__ uint32_t mn_lane(int lane) {
+  const int g = lane >> 4, li = lane & 15, h = lane >> 5;
+  const int low = 2 * (g & 1) + ((li & 3) >> 1);
+  return (uint32_t)((8 * h + (li >> 2)) * 256) | (uint32_t)((low ^ (4 * (li >> 2))) << 4) |
+         (uint32_t)((li & 1) << 3);
+}
+
+template <bool KC>
+__device__ __forceinline__ bf16x8 frag(lptr tile, uint32_t ln, int blk32, int c) {
+  if constexpr (KC) {
+    return *(lds_cbf16x8_t*)(tile + blk32 * 32 * 128 + (ln ^ (uint32_t)(c << 5)));
+  } else {
+    lptr p0 = tile + c * 16 * 256 + (ln ^ (uint32_t)((blk32 * 4) << 4));
+    const bf16x4 lo = __builtin_bit_cast(
+        bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p0));
+    const bf16x4 hi = __builtin_bit_cast(
+        bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0 + 4 * 256)));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+template <int FORM, int OUT>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(KArgs g) {
+  constexpr bool AK = FORM != GEMM_TN;  // A K-contiguous
+  constexpr bool BK = FORM == GEMM_NT;  // B K-contiguous
+  __shared__ __attribute__((aligned(1024))) char lds[kGemmBuf * 2 * kOpBytes];
+  int bid = blockIdx.x;
+  const KJob& kj = g.job[find_job(g, bid)];
+  const GemmJob& jb = kj.j;
+  const int split = bid / kj.tiles, t = bid - split * kj.tiles;
+  const int tm = t / kj.tiles_n, tn = t - tm * kj.tiles_n;
+  const int m0 = tm * kTM, n0 = tn * kTN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wv >> 1, wn = wv & 1;
+
+  // the K steps of this workgroup over the segments (a split job has one segment)
+  int steps = 0;
+  for (int s = 0; s < jb.nseg; ++s) steps += (jb.seg[s].k + kTK - 1) / kTK;
+  int st_begin = 0, st_end = steps;
+  if (kj.splits > 1) {
+    st_begin = split * kj.steps_per_split;
+    st_end = min(steps, st_begin + kj.steps_per_split);
+  }
+  int iseg = 0, ik0 = st_begin * kTK;  // issue cursor
+  auto issue = [&](int buf) {
+    while (ik0 >= jb.seg[iseg].k) {  // uniform: the cursor moves to the next segment
+      ik0 = 0;
+      ++iseg;
+    }
+    const GemmSeg& sg = jb.seg[iseg];
+    char* dst = lds + buf * 2 * kOpBytes + wv * 4 * 1024;
+    uint32_t off[4];
+    tile_offsets<AK>(off, sg.a, jb.m, sg.k, m0, ik0, wv, lane);
+    dma16_rows<4>(dst, static_cast<const char*>(sg.a.p), sg.a.bytes, off);
+    tile_offsets<BK>(off, sg.b, jb.n, sg.k, n0, ik0, wv, lane);
+    dma16_rows<4>(dst + kOpBytes, static_cast<const char*>(sg.b.p), sg.b.bytes, off);
+    ik0 += kTK;
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = zero16();
+  const uint32_t la = AK ? kc_lane(lane) : mn_lane(lane);
+  const uint32_t lb = BK ? kc_lane(lane) : mn_lane(lane);
+  const lptr lbase = to_lds(lds);
+  const int nst = st_end - st_begin;
+  if (nst > 0) issue(0);
+  for (int s = 0; s < nst; ++s) {
+    wait_vm<0>();  // step s has landed (this wave's copies)
+    __builtin_amdgcn_s_barrier();  // ... and every wave's; step s - 1's reads are done
+    lds_acquire();
+    if (s + 1 < nst) issue((s + 1) % kGemmBuf);
+    const lptr ta = lbase + (s % kGemmBuf) * 2 * kOpBytes;
+    const lptr tb = ta + kOpBytes;
+    bf16x8 fa[2][4], fb[2][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        fa[i][c] = frag<AK>(ta, la, 2 * wm + i, c);
+        fb[i][c] = frag<BK>(tb, lb, 2 * wn + i, c);
+      }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(fb[j][c], fa[i][c], acc[i][j]);
+  }
+
+  // epilogue: lane row m0 + 64 wm + 32 i + lane % 32, columns n0 + 64 wn + 32 j + 8 q +
+  // 4 h + {0..3} in acc[i][j][4q .. 4q+3]
+  const int h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = m0 + 64 * wm + 32 * i + (lane & 31);
+    if (row >= jb.m) continue;
+    int b = 0, sq = row;
+    if constexpr (OUT == GEMM_OUT_IO_HEADS) {
+      b = row / g.S;
+      sq = row - b * g.S;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + 64 * wn + 32 * j + 8 * q + 4 * h;
+        if (col >= jb.n) continue;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+        if constexpr (OUT == GEMM_OUT_F32) {
+          float* dst = kj.splits > 1 ? jb.part + (size_t)split * jb.m * jb.ldc : (float*)jb.c;
+          *reinterpret_cast<f32x4*>(dst + (size_t)row * jb.ldc + col) = v;
+        } else {
+          if (jb.bias != nullptr) {
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(jb.bias + col);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += bv[e];
+          }
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+          size_t at;
+          if constexpr (OUT == GEMM_OUT_IO_HEADS) {
+            const int hh = col / g.hd, e0 = col - hh * g.hd;
+            at = (((size_t)b * jb.c_heads + hh) * g.S + sq) * g.hd + e0;
+          } else {
+            at = (size_t)row * jb.ldc + col;
+          }
+          *reinterpret_cast<bf16x4*>(static_cast<bf16*>(jb.c) + at) = o;
+        }
+      }
+  }
+}
+
+// fp32 io: a plain LDS-tiled kernel (64 x 64 tile, 4 x 4 outputs per lane, K steps of 16)
+// with the same forms, jobs, segments and outputs; fp32 FMAs in a fixed k order.
+template <int FORM, int OUT>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs g) {
+  constexpr int T = 64, KS = 16;
+  __shared__ float sa[KS][T + 4], sb[KS][T + 4];
+  int bid = blockIdx.x;
+  const KJob& kj = g.job[find_job(g, bid)];
+  const GemmJob& jb = kj.j;
+  const int split = bid / kj.tiles, t = bid - split * kj.tiles;
+  const int tm = t / kj.tiles_n, tn = t - tm * kj.tiles_n;
+  const int m0 = tm * T, n0 = tn * T;
+  const int tid = threadIdx.x, tr = tid / 16, tc = tid % 16;
+  float acc[4][4] = {};
+  int steps = 0;
+  for (int s = 0; s < jb.nseg; ++s) steps += (jb.seg[s].k + KS - 1) / KS;
+  int st_begin = 0, st_end = steps;
+  if (kj.splits > 1) {
+    st_begin = split * kj.steps_per_split;
+    st_end = min(steps, st_begin + kj.steps_per_split);
+  }
+  int seg = 0, k0 = st_begin * KS;
+  for (int s = st_begin; s < st_end; ++s) {
+    while (k0 >= jb.seg[seg].k) {
+      k0 = 0;
+      ++seg;
+    }
+    const GemmSeg& sg = jb.seg[seg];
+    const float* A = static_cast<const float*>(sg.a.p);
+    const float* B = static_cast<const float*>(sg.b.p);
+    // 1024 elements per operand tile, 4 per lane
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int x = tid + 256 * e, kk = x / T, mn = x % T;
+      const int kg = k0 + kk, mg = m0 + mn, ng = n0 + mn;
+      float av = 0.f, bv = 0.f;
+      if (kg < sg.k && mg < jb.m)
+        av = FORM != GEMM_TN ? A[(size_t)mg * sg.a.ld + kg] : A[(size_t)kg * sg.a.ld + mg];
+      if (kg < sg.k && ng < jb.n)
+        bv = FORM == GEMM_NT ? B[(size_t)ng * sg.b.ld + kg] : B[(size_t)kg * sg.b.ld + ng];
+      sa[kk][mn] = av;
+      sb[kk][mn] = bv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(sa[kk][tr * 4 + i], sb[kk][tc * 4 + j], acc[i][j]);
+    __syncthreads();
+    k0 += KS;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + tr * 4 + i;
+    if (row >= jb.m) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + tc * 4 + j;
+      if (col >= jb.n) continue;
+      float v = acc[i][j];
+      if constexpr (OUT == GEMM_OUT_F32) {
+        float* dst = kj.splits > 1 ? jb.part + (size_t)split * jb.m * jb.ldc : (float*)jb.c;
+        dst[(size_t)row * jb.ldc + col] = v;
+      } else {
+        if (jb.bias != nullptr) v += jb.bias[col];
+        size_t at;
+        if constexpr (OUT == GEMM_OUT_IO_HEADS) {
+          const int b = row / g.S, sq = row - b * g.S, hh = col / g.hd, e0 = col - hh * g.hd;
+          at = (((size_t)b * jb.c_heads + hh) * g.S + sq) * g.hd + e0;
+        } else {
+          at = (size_t)row * jb.ldc + col;
+        }
+        static_cast<float*>(jb.c)[at] = v;
+      }
+    }
+  }
+}
+
+// c[i] = sum over splits s (ascending) of part[s][i], [m, n] fp32 (ldc == n).
+__global__ __launch_bounds__(256) void splitk_sum_kernel(KArgs g) {
+  const KJob& kj = g.job[blockIdx.y];
+  const GemmJob& jb = kj.j;
+  if (kj.splits <= 1) return;
+  const size_t n4 = (size_t)jb.m * jb.ldc / 4;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4* p = reinterpret_cast<const f32x4*>(jb.part) + i;
+  f32x4 s = p[0];
+  for (int q = 1; q < kj.splits; ++q) {
+    const f32x4 v = p[q * n4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] += v[e];
+  }
+  reinterpret_cast<f32x4*>(jb.c)[i] = s;
+}
+
+template <int FORM>
+hipError_t launch_form(IoType io, int out, const KArgs& a, int blocks, dim3 block,
+                       hipStream_t stream) {
+#define XATTN_GEMM(K, O) hipLaunchKernelGGL((K<FORM, O>), dim3(blocks), block, 0, stream, a)
+  if (io == IO_BF16) {
+    if (out == GEMM_OUT_IO_ROWS) XATTN_GEMM(gemm_bf16_kernel, GEMM_OUT_IO_ROWS);
+    else if (out == GEMM_OUT_IO_HEADS) XATTN_GEMM(gemm_bf16_kernel, GEMM_OUT_IO_HEADS);
+    else XATTN_GEMM(gemm_bf16_kernel, GEMM_OUT_F32);
+  } else {
+    if (out == GEMM_OUT_IO_ROWS) XATTN_GEMM(gemm_f32_kernel, GEMM_OUT_IO_ROWS);
+    else if (out == GEMM_OUT_IO_HEADS) XATTN_GEMM(gemm_f32_kernel, GEMM_OUT_IO_HEADS);
+    else XATTN_GEMM(gemm_f32_kernel, GEMM_OUT_F32);
+  }
+#undef XATTN_GEMM
+  return hipPeekAtLastError();
+}
+
+// Tile bookkeeping shared by the launcher and the workspace query.
+int plan_jobs(IoType io, const GemmJob* jobs, int njobs, KArgs* out) {
+  const int tile = io == IO_BF16 ? kTM : 64, kstep = io == IO_BF16 ? kTK : 16;
+  int blocks = 0;
+  for (int q = 0; q < njobs; ++q) {
+    KJob& k = out->job[q];
+    k.j = jobs[q];
+    k.tiles_n = (k.j.n + tile - 1) / tile;
+    k.tiles = ((k.j.m + tile - 1) / tile) * k.tiles_n;
+    int steps = 0;
+    for (int s = 0; s < k.j.nseg; ++s) steps += (k.j.seg[s].k + kstep - 1) / kstep;
+    // fp32 outputs with few tiles split K (at least 8 steps per split) to fill the chip
+    k.splits = 1;
+    if (k.j.part != nullptr && k.j.nseg == 1 && k.tiles < 512)
+      k.splits = std::max(1, std::min(steps / 8, (512 + k.tiles - 1) / k.tiles));
+    k.steps_per_split = (steps + k.splits - 1) / k.splits;
+    k.splits = (steps + k.steps_per_split - 1) / k.steps_per_split;  // no empty split
+    k.block_begin = blocks;
+    blocks += k.tiles * k.splits;
+  }
+  out->njobs = njobs;
+  return blocks;
+}
+
+}  // namespace
+
+size_t gemm_partial_floats(IoType io, const GemmJob& job) {
+  KArgs a{};
+  GemmJob j = job;
+  j.part = reinterpret_cast<float*>(16);  // any non-null: split allowed
+  plan_jobs(io, &j, 1, &a);
+  return a.job[0].splits > 1 ? (size_t)a.job[0].splits * j.m * j.n : 0;
+}
+
+hipError_t launch_gemm(IoType io, int form, int out, const GemmJob* jobs, int njobs, int S,
+                       int hd, hipStream_t stream) {
+  if (njobs < 1 || njobs > kGemmMaxJobs) return hipErrorInvalidValue;
+  KArgs a{};
+  a.S = S;
+  a.hd = hd;
+  const int blocks = plan_jobs(io, jobs, njobs, &a);
+  hipError_t e;
+  ProfScope prof(io == IO_BF16 ? "proj_gemm" : "proj_gemm_f32", stream);
+  const dim3 block(256);
+  if (form == GEMM_NN) e = launch_form<GEMM_NN>(io, out, a, blocks, block, stream);
+  else if (form == GEMM_NT) e = launch_form<GEMM_NT>(io, out, a, blocks, block, stream);
+  else e = launch_form<GEMM_TN>(io, out, a, blocks, block, stream);
+  if (e != hipSuccess) return e;
+  bool split = false;
+  size_t most = 0;
+  for (int q = 0; q < njobs; ++q) {
+    split = split || a.job[q].splits > 1;
+    most = std::max(most, (size_t)jobs[q].m * jobs[q].n / 4);
+  }
+  if (!split) return hipSuccess;
+  ProfScope prof2("proj_gemm_splitk_sum", stream);
+  hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)((most + 255) / 256), njobs), dim3(256),
+                     0, stream, a);
+  return hipPeekAtLastError();
+}
+
+}  // namespace xattn

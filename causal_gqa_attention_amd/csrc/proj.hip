@@ -3,9 +3,9 @@
 // pipeline: the projection's [tokens, heads*hd] rows are reshaped to [tokens, heads, hd] and
 // transposed so that each head's [seq, hd] block is contiguous, and merged back before Wo).
 //
-// The GEMMs themselves are library calls (hipBLASLt, bf16 or fp32 in, fp32 accumulate and
-// out); these kernels are HBM-bound passes: each lane moves 16-byte vectors, and the bias
-// add and the one rounding to the io dtype happen in the same pass as the re-layout.
+// The GEMMs (gemm.hip) split their outputs into heads themselves; what remains here are
+// HBM-bound passes: the head merge of an attention-layout tensor into token rows (each lane
+// moves 16-byte vectors) and the bias gradients as fixed-order column sums.
 #include "xattn_device.h"
 #include "xattn_internal.h"
 
@@ -18,27 +18,6 @@ __device__ __forceinline__ size_t head_index(size_t m, int c, int S, int heads, 
   const size_t b = m / S, s = m - b * S;
   const int h = c / hd, e = c - h * hd;
   return ((b * heads + h) * S + s) * hd + e;
-}
-
-// Split: dst (head-major, io dtype) = src (fp32 token rows) + bias; up to three tensors in
-// one launch.  4 columns per lane (hd is a multiple of 4, so they stay in one head).
-template <typename TO>
-__global__ __launch_bounds__(256) void split_heads_kernel(SplitJobs jobs, int S, int hd) {
-  size_t g = (size_t)blockIdx.x * 256 + threadIdx.x;
-  for (int j = 0; j < jobs.n; ++j) {
-    const SplitJob& jb = jobs.job[j];
-    const size_t nvec = (size_t)jb.rows * jb.cols / 4;
-    if (g < nvec) {
-      const size_t m = g / (jb.cols / 4);
-      const int c = (int)(g - m * (jb.cols / 4)) * 4;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(jb.src + m * jb.cols + c);
-      TO* d = static_cast<TO*>(jb.dst) + head_index(m, c, S, jb.cols / hd, hd);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) d[e] = from_f32<TO>(v[e] + (jb.bias ? jb.bias[c + e] : 0.f));
-      return;
-    }
-    g -= nvec;
-  }
 }
 
 // Merge: dst (token rows, io dtype) = src (head-major, io dtype); up to three tensors.
@@ -58,20 +37,6 @@ __global__ __launch_bounds__(256) void merge_heads_kernel(MergeJobs jobs, int S,
     }
     g -= nvec;
   }
-}
-
-// dst (io dtype) = src (fp32) + bias per column, [rows, cols] both.
-template <typename TO>
-__global__ __launch_bounds__(256) void round_bias_kernel(const float* __restrict__ src,
-                                                         const float* __restrict__ bias,
-                                                         TO* __restrict__ dst, size_t rows,
-                                                         int cols) {
-  const size_t g = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= rows * cols / 4) return;
-  const int c = (int)(g % (cols / 4)) * 4;
-  const f32x4 v = *reinterpret_cast<const f32x4*>(src + g * 4);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) dst[g * 4 + e] = from_f32<TO>(v[e] + (bias ? bias[c + e] : 0.f));
 }
 
 // Column sums of [rows, cols] in a fixed order: partial[p][c] sums rows p*chunk ..
@@ -101,19 +66,6 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(ColsumJobs jobs, int 
 
 }  // namespace
 
-hipError_t launch_split_heads(IoType io, const SplitJobs& jobs, int S, int hd,
-                              hipStream_t stream) {
-  size_t total = 0;
-  for (int j = 0; j < jobs.n; ++j) total += (size_t)jobs.job[j].rows * jobs.job[j].cols / 4;
-  ProfScope prof("split_heads", stream);
-  const dim3 grid((unsigned)((total + 255) / 256));
-  if (io == IO_F32)
-    hipLaunchKernelGGL(split_heads_kernel<float>, grid, dim3(256), 0, stream, jobs, S, hd);
-  else
-    hipLaunchKernelGGL(split_heads_kernel<bf16>, grid, dim3(256), 0, stream, jobs, S, hd);
-  return hipPeekAtLastError();
-}
-
 hipError_t launch_merge_heads(IoType io, const MergeJobs& jobs, int S, int hd,
                               hipStream_t stream) {
   const int vec = io == IO_F32 ? 4 : 8;
@@ -125,19 +77,6 @@ hipError_t launch_merge_heads(IoType io, const MergeJobs& jobs, int S, int hd,
     hipLaunchKernelGGL(merge_heads_kernel<float>, grid, dim3(256), 0, stream, jobs, S, hd);
   else
     hipLaunchKernelGGL(merge_heads_kernel<bf16>, grid, dim3(256), 0, stream, jobs, S, hd);
-  return hipPeekAtLastError();
-}
-
-hipError_t launch_round_bias(IoType io, const float* src, const float* bias, void* dst,
-                             size_t rows, int cols, hipStream_t stream) {
-  const dim3 grid((unsigned)((rows * cols / 4 + 255) / 256));
-  ProfScope prof("round_bias", stream);
-  if (io == IO_F32)
-    hipLaunchKernelGGL(round_bias_kernel<float>, grid, dim3(256), 0, stream, src, bias,
-                       (float*)dst, rows, cols);
-  else
-    hipLaunchKernelGGL(round_bias_kernel<bf16>, grid, dim3(256), 0, stream, src, bias,
-                       (bf16*)dst, rows, cols);
   return hipPeekAtLastError();
 }
 

@@ -193,28 +193,61 @@ ProjChecked check_proj(const xattn_dims* dims, int64_t model_dim) {
   const int64_t nk = (int64_t)p.c.s.num_kv_heads * p.c.s.head_dim;
   count4(M, model_dim, 1, 1, "token rows x model_dim");
   count4(model_dim, nq, 1, 1, "weights");
+  count4(M, nq, 1, 1, "merged heads");
+  // every GEMM operand buffer stays below 2^31 bytes (the kernels' byte offsets are 32-bit)
+  const int64_t es = (int64_t)io_size(p.c.io);
+  for (int64_t n : {M * model_dim, model_dim * nq, M * nq})
+    if (n * es >= kMaxElems)
+      fail(XATTN_ERR_INVALID_ARG, "projection operand of %lld bytes exceeds 2^31 bytes",
+           (long long)(n * es));
   p.M = (int)M, p.d = (int)model_dim, p.nq = (int)nq, p.nk = (int)nk;
   p.io = io_size(p.c.io);
   return p;
 }
 
-// Workspace regions of the projection calls (each call uses a prefix of its own plan;
-// the GEMM library's scratch follows at `gemm`).
-size_t proj_scratch_bytes(const ProjChecked& p) {
-  const size_t M = p.M, f32 = 4, parts = (size_t)xattn::colsum_parts(p.M) * 4;
-  const size_t qkv_fwd = align256(M * p.nq * f32) + 2 * align256(M * p.nk * f32);
-  const size_t out_fwd = align256(M * p.nq * p.io) + align256(M * p.d * f32);
-  const size_t out_bwd = align256(M * p.nq * f32) + align256(M * p.nq * p.io) +
-                         align256(parts * p.d);
-  const size_t qkv_bwd = align256(M * p.nq * p.io) + 2 * align256(M * p.nk * p.io) +
-                         align256(M * p.d * f32) + align256(parts * p.nq) +
-                         2 * align256(parts * p.nk);
-  return std::max(std::max(qkv_fwd, out_fwd), std::max(out_bwd, qkv_bwd));
+// The projection GEMMs' jobs (gemm.hip).  Operands are row-major; `w` below is the io
+// dtype's size.  Token rows: x, y, dx [M, d]; merged heads [M, n].
+xattn::GemmMat mat(const void* p, int rows, int ld, size_t w) {
+  return {p, ld, (uint32_t)((size_t)rows * ld * w)};
+}
+xattn::GemmJob job1(xattn::GemmMat a, xattn::GemmMat b, int k, int m, int n, void* c, int ldc,
+                    int c_heads, const float* bias, float* part) {
+  xattn::GemmJob j{};
+  j.seg[0] = {a, b, k};
+  j.nseg = 1;
+  j.m = m, j.n = n, j.c = c, j.ldc = ldc, j.c_heads = c_heads, j.bias = bias, j.part = part;
+  return j;
+}
+// dW = x^T g: A = x stored [M, d], B = g stored [M, n]
+xattn::GemmJob dw_job(const ProjChecked& p, const void* x, const void* g, int n, float* dw,
+                      float* part) {
+  return job1(mat(x, p.M, p.d, p.io), mat(g, p.M, n, p.io), p.M, p.d, n, dw, n, 0, nullptr,
+              part);
+}
+// dWo = merge(out)^T dy: A = merged out [M, nq], B = dy [M, d]
+xattn::GemmJob dwo_job(const ProjChecked& p, const void* om, const void* dy, float* dwo,
+                       float* part) {
+  return job1(mat(om, p.M, p.nq, p.io), mat(dy, p.M, p.d, p.io), p.M, p.nq, p.d, dwo, p.d, 0,
+              nullptr, part);
 }
 
-size_t proj_workspace(const ProjChecked& p) {
-  return proj_scratch_bytes(p) + xattn::kGemmWorkspace;
+// Workspace regions of the projection calls (each call uses a prefix of its own plan).
+size_t proj_scratch_bytes(const ProjChecked& p) {
+  const size_t M = p.M, f32 = 4, parts = (size_t)xattn::colsum_parts(p.M) * 4;
+  const auto split = [&](const xattn::GemmJob& j) {
+    return align256(xattn::gemm_partial_floats(p.c.io, j) * f32);
+  };
+  const size_t out_fwd = align256(M * p.nq * p.io);
+  const size_t out_bwd = align256(M * p.nq * p.io) + align256(parts * p.d) +
+                         split(dwo_job(p, nullptr, nullptr, nullptr, nullptr));
+  const size_t qkv_bwd = align256(M * p.nq * p.io) + 2 * align256(M * p.nk * p.io) +
+                         align256(parts * p.nq) + 2 * align256(parts * p.nk) +
+                         split(dw_job(p, nullptr, nullptr, p.nq, nullptr, nullptr)) +
+                         2 * split(dw_job(p, nullptr, nullptr, p.nk, nullptr, nullptr));
+  return std::max(std::max(out_fwd, out_bwd), std::max(qkv_bwd, (size_t)256));
 }
+
+size_t proj_workspace(const ProjChecked& p) { return proj_scratch_bytes(p); }
 
 // Sequential carving of a workspace into 256-byte aligned regions.
 struct Carver {
@@ -227,16 +260,6 @@ struct Carver {
     return r;
   }
 };
-
-void gemm_or_fail(const ProjChecked& p, bool ta, bool tb, int M, int N, int K, const void* A,
-                  int lda, const void* B, int ldb, float beta, float* C, int ldc, void* ws,
-                  hipStream_t st) {
-  char err[160] = {0};
-  if (!xattn::gemm_rm(p.c.io, ta, tb, M, N, K, A, lda, B, ldb, beta, C, ldc,
-                      static_cast<char*>(ws) + proj_scratch_bytes(p), xattn::kGemmWorkspace, st,
-                      &err))
-    fail(XATTN_ERR_HIP, "%s", err);
-}
 
 void check_ws(void* ws, size_t have, size_t need) {
   check_ptr(ws, "workspace");
@@ -599,21 +622,18 @@ xattn_status xattn_qkv_proj_fwd(const xattn_dims* dims, const xattn_proj* pr, co
                       {pr->bq, pr->bq ? (size_t)p.nq * 4 : 0, "p->bq"},
                       {pr->bk, pr->bk ? (size_t)p.nk * 4 : 0, "p->bk"},
                       {pr->bv, pr->bv ? (size_t)p.nk * 4 : 0, "p->bv"}});
-    const hipStream_t st = (hipStream_t)stream;
-    Carver w{static_cast<char*>(workspace)};
-    float* cq = w.take<float>(M * p.nq * 4);
-    float* ck = w.take<float>(M * p.nk * 4);
-    float* cv = w.take<float>(M * p.nk * 4);
-    gemm_or_fail(p, false, false, p.M, p.nq, p.d, x, p.d, pr->wq, p.nq, 0.f, cq, p.nq,
-                 workspace, st);
-    gemm_or_fail(p, false, false, p.M, p.nk, p.d, x, p.d, pr->wk, p.nk, 0.f, ck, p.nk,
-                 workspace, st);
-    gemm_or_fail(p, false, false, p.M, p.nk, p.d, x, p.d, pr->wv, p.nk, 0.f, cv, p.nk,
-                 workspace, st);
-    xattn::SplitJobs jobs{{{cq, pr->bq, xq, p.M, p.nq}, {ck, pr->bk, xk, p.M, p.nk},
-                           {cv, pr->bv, v, p.M, p.nk}}, 3};
-    hip_check(xattn::launch_split_heads(p.c.io, jobs, p.c.s.seq_len, p.c.s.head_dim, st),
-              "split_heads launch");
+    // one launch: x Wq, x Wk, x Wv, each split into heads with its bias
+    const xattn::GemmMat xm = mat(x, p.M, p.d, p.io);
+    const xattn::GemmJob jobs[3] = {
+        job1(xm, mat(pr->wq, p.d, p.nq, p.io), p.d, p.M, p.nq, xq, 0, p.c.s.num_heads, pr->bq,
+             nullptr),
+        job1(xm, mat(pr->wk, p.d, p.nk, p.io), p.d, p.M, p.nk, xk, 0, p.c.s.num_kv_heads,
+             pr->bk, nullptr),
+        job1(xm, mat(pr->wv, p.d, p.nk, p.io), p.d, p.M, p.nk, v, 0, p.c.s.num_kv_heads,
+             pr->bv, nullptr)};
+    hip_check(xattn::launch_gemm(p.c.io, xattn::GEMM_NN, xattn::GEMM_OUT_IO_HEADS, jobs, 3,
+                                 p.c.s.seq_len, p.c.s.head_dim, (hipStream_t)stream),
+              "projection GEMM launch");
   });
 }
 
@@ -636,13 +656,14 @@ xattn_status xattn_out_proj_fwd(const xattn_dims* dims, const xattn_proj* pr, co
     const hipStream_t st = (hipStream_t)stream;
     Carver w{static_cast<char*>(workspace)};
     void* om = w.take<char>(M * p.nq * p.io);
-    float* cy = w.take<float>(M * p.d * 4);
     xattn::MergeJobs mj{{{out, om, p.M, p.nq}}, 1};
     hip_check(xattn::launch_merge_heads(p.c.io, mj, p.c.s.seq_len, p.c.s.head_dim, st),
               "merge_heads launch");
-    gemm_or_fail(p, false, false, p.M, p.d, p.nq, om, p.nq, pr->wo, p.d, 0.f, cy, p.d,
-                 workspace, st);
-    hip_check(xattn::launch_round_bias(p.c.io, cy, pr->bo, y, M, p.d, st), "round launch");
+    const xattn::GemmJob j = job1(mat(om, p.M, p.nq, p.io), mat(pr->wo, p.nq, p.d, p.io), p.nq,
+                                  p.M, p.d, y, p.d, 0, pr->bo, nullptr);
+    hip_check(xattn::launch_gemm(p.c.io, xattn::GEMM_NN, xattn::GEMM_OUT_IO_ROWS, &j, 1,
+                                 p.c.s.seq_len, p.c.s.head_dim, st),
+              "projection GEMM launch");
   });
 }
 
@@ -665,21 +686,23 @@ xattn_status xattn_out_proj_bwd(const xattn_dims* dims, const xattn_proj* pr, co
                       {pr->wo, (size_t)p.nq * p.d * p.io, "p->wo"}});
     const hipStream_t st = (hipStream_t)stream;
     Carver w{static_cast<char*>(workspace)};
-    float* dom = w.take<float>(M * p.nq * 4);
     void* om = w.take<char>(M * p.nq * p.io);
     float* part = w.take<float>((size_t)xattn::colsum_parts(p.M) * p.d * 4);
-    // dout = split(dy Wo^T): Wo stored [nq, d] = [N, K]
-    gemm_or_fail(p, false, true, p.M, p.nq, p.d, dy, p.d, pr->wo, p.d, 0.f, dom, p.nq,
-                 workspace, st);
-    xattn::SplitJobs sj{{{dom, nullptr, dout, p.M, p.nq}}, 1};
-    hip_check(xattn::launch_split_heads(p.c.io, sj, p.c.s.seq_len, p.c.s.head_dim, st),
-              "split_heads launch");
-    // dwo = merge(out)^T dy: A stored [M, nq] = [K, M'], B stored [M, d] = [K, N]
+    xattn::GemmJob jw = dwo_job(p, om, dy, dwo, nullptr);
+    jw.part = w.take<float>(xattn::gemm_partial_floats(p.c.io, jw) * 4);
+    // dout = split(dy Wo^T): Wo stored [nq, d] is B^T
+    const xattn::GemmJob jd = job1(mat(dy, p.M, p.d, p.io), mat(pr->wo, p.nq, p.d, p.io), p.d,
+                                   p.M, p.nq, dout, 0, p.c.s.num_heads, nullptr, nullptr);
+    hip_check(xattn::launch_gemm(p.c.io, xattn::GEMM_NT, xattn::GEMM_OUT_IO_HEADS, &jd, 1,
+                                 p.c.s.seq_len, p.c.s.head_dim, st),
+              "projection GEMM launch");
+    // dwo = merge(out)^T dy
     xattn::MergeJobs mj{{{out, om, p.M, p.nq}}, 1};
     hip_check(xattn::launch_merge_heads(p.c.io, mj, p.c.s.seq_len, p.c.s.head_dim, st),
               "merge_heads launch");
-    gemm_or_fail(p, true, false, p.nq, p.d, p.M, om, p.nq, dy, p.d, 0.f, dwo, p.d, workspace,
-                 st);
+    hip_check(xattn::launch_gemm(p.c.io, xattn::GEMM_TN, xattn::GEMM_OUT_F32, &jw, 1,
+                                 p.c.s.seq_len, p.c.s.head_dim, st),
+              "projection GEMM launch");
     if (dbo != nullptr) {
       xattn::ColsumJobs cj{{{dy, part, dbo, p.M, p.d}}, 1};
       hip_check(xattn::launch_colsum(p.c.io, cj, st), "bias gradient launch");
@@ -719,28 +742,31 @@ xattn_status xattn_qkv_proj_bwd(const xattn_dims* dims, const xattn_proj* pr, co
     void* gq = w.take<char>(M * p.nq * p.io);
     void* gk = w.take<char>(M * p.nk * p.io);
     void* gv = w.take<char>(M * p.nk * p.io);
-    float* cdx = w.take<float>(M * p.d * 4);
     float* pq = w.take<float>((size_t)xattn::colsum_parts(p.M) * p.nq * 4);
     float* pk = w.take<float>((size_t)xattn::colsum_parts(p.M) * p.nk * 4);
     float* pv = w.take<float>((size_t)xattn::colsum_parts(p.M) * p.nk * 4);
+    xattn::GemmJob jw[3] = {dw_job(p, x, gq, p.nq, dwq, nullptr),
+                            dw_job(p, x, gk, p.nk, dwk, nullptr),
+                            dw_job(p, x, gv, p.nk, dwv, nullptr)};
+    for (xattn::GemmJob& j : jw) j.part = w.take<float>(xattn::gemm_partial_floats(p.c.io, j) * 4);
     xattn::MergeJobs mj{{{dxq, gq, p.M, p.nq}, {dxk, gk, p.M, p.nk}, {dv, gv, p.M, p.nk}}, 3};
     hip_check(xattn::launch_merge_heads(p.c.io, mj, p.c.s.seq_len, p.c.s.head_dim, st),
               "merge_heads launch");
-    // dx = gq Wq^T + gk Wk^T + gv Wv^T (W stored [d, n] = [N, K]), summed in fp32
-    gemm_or_fail(p, false, true, p.M, p.d, p.nq, gq, p.nq, pr->wq, p.nq, 0.f, cdx, p.d,
-                 workspace, st);
-    gemm_or_fail(p, false, true, p.M, p.d, p.nk, gk, p.nk, pr->wk, p.nk, 1.f, cdx, p.d,
-                 workspace, st);
-    gemm_or_fail(p, false, true, p.M, p.d, p.nk, gv, p.nk, pr->wv, p.nk, 1.f, cdx, p.d,
-                 workspace, st);
-    hip_check(xattn::launch_round_bias(p.c.io, cdx, nullptr, dx, M, p.d, st), "round launch");
-    // dW = x^T g: A stored [M, d] = [K, M'], B stored [M, n] = [K, N]
-    gemm_or_fail(p, true, false, p.d, p.nq, p.M, x, p.d, gq, p.nq, 0.f, dwq, p.nq, workspace,
-                 st);
-    gemm_or_fail(p, true, false, p.d, p.nk, p.M, x, p.d, gk, p.nk, 0.f, dwk, p.nk, workspace,
-                 st);
-    gemm_or_fail(p, true, false, p.d, p.nk, p.M, x, p.d, gv, p.nk, 0.f, dwv, p.nk, workspace,
-                 st);
+    // dx = gq Wq^T + gk Wk^T + gv Wv^T: one job, three K segments summed in fp32 (W stored
+    // [d, n] is B^T)
+    xattn::GemmJob jx{};
+    jx.seg[0] = {mat(gq, p.M, p.nq, p.io), mat(pr->wq, p.d, p.nq, p.io), p.nq};
+    jx.seg[1] = {mat(gk, p.M, p.nk, p.io), mat(pr->wk, p.d, p.nk, p.io), p.nk};
+    jx.seg[2] = {mat(gv, p.M, p.nk, p.io), mat(pr->wv, p.d, p.nk, p.io), p.nk};
+    jx.nseg = 3;
+    jx.m = p.M, jx.n = p.d, jx.c = dx, jx.ldc = p.d;
+    hip_check(xattn::launch_gemm(p.c.io, xattn::GEMM_NT, xattn::GEMM_OUT_IO_ROWS, &jx, 1,
+                                 p.c.s.seq_len, p.c.s.head_dim, st),
+              "projection GEMM launch");
+    // dW = x^T g for the three projections in one launch
+    hip_check(xattn::launch_gemm(p.c.io, xattn::GEMM_TN, xattn::GEMM_OUT_F32, jw, 3,
+                                 p.c.s.seq_len, p.c.s.head_dim, st),
+              "projection GEMM launch");
     xattn::ColsumJobs cj{};
     if (dbq != nullptr) cj.job[cj.n++] = {gq, pq, dbq, p.M, p.nq};
     if (dbk != nullptr) cj.job[cj.n++] = {gk, pk, dbk, p.M, p.nk};

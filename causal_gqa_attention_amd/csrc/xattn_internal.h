@@ -137,18 +137,7 @@ DecodePlan decode_plan(const DecodeShape& d, int cache_rows);
 hipError_t launch_decode(IoType io, const DecodeShape& d, const DecodeBufs& bufs,
                          hipStream_t stream);
 
-// ---- projections (proj.hip, proj.cpp) -------------------------------------------------
-// Head split of fp32 token rows [rows, cols] (+ bias) into a head-major io-dtype tensor.
-struct SplitJob {
-  const float* src;
-  const float* bias;  // [cols] or null
-  void* dst;
-  int rows, cols;
-};
-struct SplitJobs {
-  SplitJob job[3];
-  int n;
-};
+// ---- projections (proj.hip: layouts and bias sums; gemm.hip: the GEMMs) ----------------
 // Head merge of a head-major io-dtype tensor into token rows [rows, cols].
 struct MergeJob {
   const void* src;
@@ -172,22 +161,44 @@ struct ColsumJobs {
   ColsumJob job[3];
   int n;
 };
-hipError_t launch_split_heads(IoType io, const SplitJobs& jobs, int S, int hd,
-                              hipStream_t stream);
 hipError_t launch_merge_heads(IoType io, const MergeJobs& jobs, int S, int hd,
                               hipStream_t stream);
-hipError_t launch_round_bias(IoType io, const float* src, const float* bias, void* dst,
-                             size_t rows, int cols, hipStream_t stream);
 hipError_t launch_colsum(IoType io, const ColsumJobs& jobs, hipStream_t stream);
 
-// Row-major C[M, N] (fp32) = op(A) op(B) + beta * C, op(A) [M, K], op(B) [K, N]; A stored
-// [M, K] (lda) or, with ta, [K, M]; B stored [K, N] (ldb) or, with tb, [N, K].  A and B in
-// the io dtype; fp32 accumulate.  A library GEMM (hipBLASLt); `ws` is its workspace.
-// Returns false (and a message in *err) when no algorithm supports the call.
-constexpr size_t kGemmWorkspace = (size_t)64 << 20;
-bool gemm_rm(IoType io, bool ta, bool tb, int M, int N, int K, const void* A, int lda,
-             const void* B, int ldb, float beta, float* C, int ldc, void* ws, size_t ws_bytes,
-             hipStream_t stream, char (*err)[160]);
+// Row-major GEMMs in the io dtype with fp32 accumulation (gemm.hip).  Forms: GEMM_NN
+// C = A B (A [m, k], B [k, n]); GEMM_NT C = A B^T (B stored [n, k]); GEMM_TN C = A^T B (A
+// stored [k, m]).  A job sums its K segments (each with its own A, B and k) in one fp32
+// accumulator.  Outputs: GEMM_OUT_IO_ROWS (io dtype [m, ldc] + bias), GEMM_OUT_IO_HEADS
+// (io dtype, row r = b*S + s and column c = h*hd + e stored at [(b*c_heads + h)*S + s][e]
+// + bias), GEMM_OUT_F32 (fp32 [m, ldc], ldc == n; with `part` set, K may be split over
+// workgroups whose partial products, gemm_partial_floats floats of workspace, are added in
+// split order).  Every operand buffer must stay below 2^31 bytes; the callers guarantee
+// it and that n, every k and every ld are multiples of 8.
+enum { GEMM_NN = 0, GEMM_NT = 1, GEMM_TN = 2 };
+enum { GEMM_OUT_IO_ROWS = 0, GEMM_OUT_IO_HEADS = 1, GEMM_OUT_F32 = 2 };
+constexpr int kGemmMaxJobs = 3, kGemmMaxSegs = 3;
+struct GemmMat {
+  const void* p;
+  int ld;          // elements per stored row
+  uint32_t bytes;  // size of the stored matrix
+};
+struct GemmSeg {
+  GemmMat a, b;
+  int k;
+};
+struct GemmJob {
+  GemmSeg seg[kGemmMaxSegs];
+  int nseg;
+  int m, n;
+  void* c;
+  int ldc;
+  int c_heads;
+  const float* bias;  // [n] or null (io outputs)
+  float* part;        // split-K workspace (fp32 outputs) or null
+};
+size_t gemm_partial_floats(IoType io, const GemmJob& job);
+hipError_t launch_gemm(IoType io, int form, int out, const GemmJob* jobs, int njobs, int S,
+                       int hd, hipStream_t stream);
 
 // ---- opt-in per-kernel event timing (see xattn_profile_start) ------------------------
 // Construct around each kernel launch: records a start event now and a stop event at

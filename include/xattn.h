@@ -224,9 +224,11 @@ xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, con
  * the projections' token rows are split into heads ([B*H, S, hd], [B*Hkv, S, hd], what the
  * prologue and attention take) and the attention output is merged back into token rows
  * before Wo; [T12]: GEMMs take the io dtype with fp32 accumulation, the weight and bias
- * gradients are fp32.  Token rows: x, y, dx [B*S, d], row b*S + s.  The GEMMs are library
- * calls (hipBLASLt); splits, merges, bias and rounding run in the library's own kernels.
- * Requires d % 8 == 0.  The segment fields of dims are ignored. */
+ * gradients are fp32.  Token rows: x, y, dx [B*S, d], row b*S + s.  The GEMMs are the
+ * library's own kernels (bf16: MFMA), with the head split, bias and rounding in their
+ * epilogues; weight gradients are summed in a fixed order (bitwise reproducible).
+ * Requires d % 8 == 0 and every operand below 2^31 bytes.  The segment fields of dims are
+ * ignored. */
 typedef struct {
   int64_t model_dim;  /* d */
   const void* wq;     /* [d, H*hd] io dtype */

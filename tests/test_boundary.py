@@ -327,7 +327,7 @@ def test_binding_checks_attention_tensor_sizes():
                rstd_q=_cpu(B * H * S, dtype=f32), rstd_k=_cpu(B * Hkv * S, dtype=f32),
                cos_tab=_cpu(S, hd // 2, dtype=f32), sin_tab=_cpu(S - 1, hd // 2, dtype=f32),
                dgamma_q=_cpu(hd, dtype=f32), dgamma_k=_cpu(hd, dtype=f32))
-    with pytest.raises(ValueError, match="sin_tab must hold 256 elements"):
+    with pytest.raises(ValueError, match="sin_tab must hold at least 256 elements"):
         X.xattn_bwd(d, q, k, k, q, lse, q, q.clone(), k.clone(), k.clone(), pro, ws)
     pro["sin_tab"] = pro["cos_tab"].clone()
     pro["rstd_k"] = _cpu(B * H * S, dtype=f32)  # sized like rstd_q: wrong
@@ -347,7 +347,7 @@ def test_binding_checks_prologue_and_table_sizes():
     rows, S, hd = 3, 10, 32
     x, g = _cpu(rows, S, hd), _cpu(hd, dtype=f32)
     cs, rs = _cpu(S, hd // 2, dtype=f32), _cpu(rows * S, dtype=f32)
-    with pytest.raises(ValueError, match="cos_tab must hold 160 elements"):
+    with pytest.raises(ValueError, match="cos_tab must hold at least 160 elements"):
         X.xattn_qknorm_rope_fwd(x, g, cs[:-1], cs, x.clone(), rs, rows, S, hd, 1e-5)
     with pytest.raises(ValueError, match="gamma must hold 32 elements"):
         X.xattn_qknorm_rope_fwd(x, g[:16], cs, cs, x.clone(), rs, rows, S, hd, 1e-5)
@@ -359,7 +359,7 @@ def test_binding_checks_prologue_and_table_sizes():
     with pytest.raises(ValueError, match="rstd must hold 30 elements"):
         X.xattn_qknorm_rope_bwd(x, x, g, rs[:-1], cs, cs, x.clone(), g.clone(),
                                 torch.zeros(16, dtype=torch.uint8), rows, S, hd)
-    with pytest.raises(ValueError, match="sin_tab must hold 64 elements"):
+    with pytest.raises(ValueError, match="sin_tab must hold at least 64 elements"):
         X.xattn_rope_cache(_cpu(4, 16, dtype=f32), _cpu(3, 16, dtype=f32), 4, 32, 1e4)
     with pytest.raises(ValueError, match="positions must hold 5 elements"):
         X.xattn_rope_cache_at(_cpu(5, 16, dtype=f32), _cpu(5, 16, dtype=f32),
@@ -381,7 +381,7 @@ def test_binding_checks_decode_sizes():
     d = X.make_decode_dims(xq, kc, H, Hkv, 10)
     ws = torch.zeros(16, dtype=torch.uint8)
     lse = _cpu(B * H * q_len, dtype=f32)
-    with pytest.raises(ValueError, match="cos_tab must hold 2560 elements"):
+    with pytest.raises(ValueError, match="cos_tab must hold at least 2560 elements"):
         X.xattn_decode(d, xq, xk, xk, g, g, tab[:-1], tab, 1e-6, kc, kc.clone(), xq.clone(),
                        lse, ws)
     with pytest.raises(ValueError, match="v_cache must hold"):

@@ -20,7 +20,11 @@ SHAPES = [
     ("bf16", 2, 37, 4, 2, 64, 96, True),
     ("bf16", 1, 300, 8, 2, 128, 256, False),
     ("f32", 1, 16, 2, 2, 16, 32, True),
-    ("bf16", 32, 1024, 12, 4, 64, 768, True),   # dim768 GQA shape
+    ("bf16", 32, 1024, 12, 4, 64, 768, True),   # dim768 GQA shape (split-K weight grads)
+    ("bf16", 1, 4096, 32, 8, 128, 4096, True),  # Qwen3-shaped heads, d = 4096
+    ("bf16", 3, 50, 6, 2, 32, 200, True),       # ragged rows, columns and K in every GEMM
+    ("bf16", 2, 33, 4, 4, 16, 40, False),       # hd 16: 4-column output runs inside a head
+    ("f32", 3, 50, 6, 2, 32, 200, False),
 ]
 IDS = [f"{s[0]}_B{s[1]}_S{s[2]}_H{s[3]}_kv{s[4]}_hd{s[5]}_d{s[6]}_{'bias' if s[7] else 'nobias'}"
        for s in SHAPES]
@@ -78,6 +82,32 @@ def test_projections_forward_and_backward_match_oracle(shape):
         for n, g, ref in zip(("dbq", "dbk", "dbv"), dbs, rdbs):
             errs[n] = assert_close(n, host(g), ref, tol)
     print(shape, {k: f"{e:.2e}" for k, e in errs.items()})
+
+
+@pytest.mark.parametrize("shape", [("bf16", 32, 1024, 12, 4, 64, 768, True),
+                                   ("bf16", 1, 1024, 32, 8, 128, 4096, True)],
+                         ids=["dim768_split_k", "qwen3_d4096"])
+def test_projection_gradients_are_bitwise_reproducible(shape):
+    """dx, the weight gradients (split over K and summed in split order where the output has
+    few tiles) and the bias gradients are bitwise identical over repeated runs."""
+    dt, B, S, H, Hkv, hd, d, bias = shape
+    x, ws, wo, bs = _inputs(dt, B, S, H, Hkv, hd, d, bias, 650)
+    note(f"projection determinism {shape}")
+    pr = _proj(dt, B, S, H, Hkv, hd, ws, wo, bs)
+    rng = np.random.default_rng(651)
+    g = [dev(W.bf16_round(rng.standard_normal((B * n, S, hd), dtype=np.float32)), dt)
+         for n in (H, Hkv, Hkv)]
+    out, dy = g[0], dev(W.bf16_round(rng.standard_normal((B * S, d), dtype=np.float32)), dt)
+    tx = dev(x, dt)
+    runs = []
+    for _ in range(3):
+        dx, dws, dbs = pr.qkv_bwd(tx, *g)
+        dout, dwo, dbo = pr.out_bwd(out, dy)
+        torch.cuda.synchronize()
+        runs.append([t.clone() for t in (dx, *dws, *dbs, dout, dwo, dbo)])
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
