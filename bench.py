@@ -21,8 +21,9 @@ load to reach its sustained clock (measured on workload 5: 0.99 ms for the first
 Prints ONE JSON line on stdout; progress goes to stderr.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms 200] [--workload 5]
   python bench.py --copy-calibration   # plain device copy of known size, for PMC scaling
-  python bench.py --traffic-summary FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
-      # writes the dk/dv traffic summary from four `rocprofv3 --pmc` output folders
+  python bench.py --workload K --counter-summary SQ_DIR FETCH_DIR WRITE_DIR COPY_FETCH_DIR \
+      COPY_WRITE_DIR   # writes profiles/counters_<workload>.json/.md from five
+                       # `rocprofv3 --pmc` output folders (no GPU use)
 """
 from __future__ import annotations
 
@@ -39,8 +40,20 @@ sys.path.insert(0, ROOT)
 METRIC = "causal GQA attn fwd+bwd TFLOP/s (bf16) and % of MI355X MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X published dense MFMA peaks
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_bwd_dkdv_qwen3_long_gqa_bf16.json")
 CSRC = os.path.join(ROOT, "causal_gqa_attention_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+# sources whose text decides the attention kernels' code: counter summaries taken on other
+# text are stale and not reported
+KERNEL_SOURCES = ["attn.hip", "attn_bf16.hip", "prologue.hip", "lds_copy.h", "xattn_device.h"]
+# counters of one rocprofv3 --pmc pass (8 SQ counters and one GRBM counter fit one pass)
+SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA",
+               "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_VALU",
+               "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"]
+# library kernel name (the xattn_profile names) <- substring of the compiled kernel's name
+KERNEL_MATCH = [("attn_bwd_dkdv", "dkdv"), ("attn_bwd_dq", "dq_kernel"),
+                ("qknorm_rope_fwd", "qknorm_rope_fwd"), ("dgamma_reduce", "dgamma_reduce"),
+                ("attn_fwd", "fwd_kernel")]
+SIMDS, XCDS = 1024, 8  # MI355X: 256 CUs x 4 SIMDs, 8 XCDs
 
 
 def log(msg):
@@ -60,11 +73,13 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of 1 GiB (for HBM counter scaling)")
-    p.add_argument("--traffic-summary", nargs=4, default=None,
-                   metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                   help="write the HBM traffic summary of the dk/dv kernel from the counter "
-                        "CSVs of four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the "
-                        "bench, then of --copy-calibration); no GPU use")
+    p.add_argument("--counter-summary", nargs=5, default=None,
+                   metavar=("SQ_DIR", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                            "COPY_WRITE_DIR"),
+                   help="write the per-kernel counter summary of the workload from the CSVs "
+                        "of five rocprofv3 --pmc runs (the SQ pass, FETCH_SIZE and WRITE_SIZE "
+                        "of the bench, then FETCH_SIZE and WRITE_SIZE of --copy-calibration); "
+                        "no GPU use")
     p.add_argument("--docs", type=str, default=None,
                    help="comma-separated document lengths packed along the sequence "
                         "(block-causal mask); must sum to the workload's seq_len")
@@ -78,6 +93,29 @@ def parse():
     p.add_argument("--decode-cache", type=int, default=4096,
                    help="cache capacity; the step decodes one token at position capacity-1")
     return p.parse_args()
+
+
+# dense MFMA flop per clock per CU (gfx950, 4 SIMDs): bf16 32x32x16 in 32 clocks, fp32
+# 32x32x2 in 64 clocks (the published 2.5 PFLOP/s and 157.3 TFLOP/s at 2.4 GHz)
+MFMA_FLOP_PER_CLK_CU = {"bf16": 4 * 32 * 32 * 16 * 2 // 32, "f32": 4 * 32 * 32 * 2 * 2 // 64}
+
+
+def device_peak(dtype):
+    """The MFMA peak re-derived on this device: CU count (device properties) x dense MFMA
+    flop per clock per CU x the device's peak clock (hipDeviceAttributeClockRate)."""
+    import ctypes
+
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    khz = ctypes.c_int(0)
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, 0) != 0:  # 5: ClockRate (kHz)
+            return None
+    except OSError:
+        return None
+    tflops = cus * MFMA_FLOP_PER_CLK_CU[dtype] * khz.value * 1e3 / 1e12
+    return {"cus": cus, "clock_mhz": khz.value / 1e3, "tflops": tflops}
 
 
 def settle(step, min_ms):
@@ -137,24 +175,30 @@ def executed_work(w, docs=None):
             "attn_bwd_dq": (6 * hd * pairs, "S and dP recompute, dQ")}
 
 
-def traffic_for(kernel, name):
-    """HBM bytes per launch from the committed counter summary, if it was taken on the
-    current kernel source for this workload; else None."""
+def sources_sha():
+    h = hashlib.sha256()
+    for src in KERNEL_SOURCES:
+        with open(os.path.join(CSRC, src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counters_file(name):
+    return os.path.join(PROFILES, f"counters_{name}.json")
+
+
+def counters_for(kernel, name):
+    """The committed counter summary of `kernel` on workload `name` (HBM bytes per launch,
+    MFMA busy fraction, counter-derived TFLOP/s, ...), if it was taken on the current
+    kernel sources; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(counters_file(name)) as f:
             t = json.load(f)
-        h = hashlib.sha256()
-        for src in t["source_files"]:
-            with open(os.path.join(CSRC, src), "rb") as f:
-                h.update(f.read())
-        sha = h.hexdigest()
-    except (OSError, ValueError, KeyError):
+    except (OSError, ValueError):
         return None
-    if t.get("kernel") != kernel or t.get("workload") != name or t.get("source_sha256") != sha:
+    if t.get("source_sha256") != sources_sha():
         return None
-    scale = t["copy_scale"]
-    return (t["fetch_kib_per_dispatch"] / scale["fetch"] +
-            t["write_kib_per_dispatch"] / scale["write"]) * 1024.0
+    return t["kernels"].get(kernel)
 
 
 def cpu_baseline(w, x, budget_s=10.0, docs=None, min_s=2.0):
@@ -172,7 +216,7 @@ def cpu_baseline(w, x, budget_s=10.0, docs=None, min_s=2.0):
         threads, blas = len(os.sched_getaffinity(0)), "unknown"
     g = w.group
     sub = w.replace(batch=1, num_heads=g, num_kv_heads=1)
-    done, dt = 0, 0.0
+    done, dt_f, dt_b = 0, 0.0, 0.0
     while True:
         kv = done % w.bkv
         b, kvh = divmod(kv, w.num_kv_heads)
@@ -180,13 +224,17 @@ def cpu_baseline(w, x, budget_s=10.0, docs=None, min_s=2.0):
         xq, xk, v, do = x.xq[qs], x.xk[[kv]], x.v[[kv]], x.dout[qs]
         t0 = time.perf_counter()
         oracle.forward(xq, xk, v, x.gamma_q, x.gamma_k, g, 1, w.eps, w.theta, segments=docs)
+        t1 = time.perf_counter()
         oracle.backward(xq, xk, v, x.gamma_q, x.gamma_k, do, g, 1, w.eps, w.theta,
                         segments=docs)
-        dt += time.perf_counter() - t0
+        dt_f += t1 - t0
+        dt_b += time.perf_counter() - t1
         done += 1
+        dt = dt_f + dt_b
         if dt >= budget_s or (done >= w.bkv and dt >= min_s):
             break
-    flops = 12 * w.head_dim * doc_pairs(w, docs) * sub.bh * done
+    unit = w.head_dim * doc_pairs(w, docs) * sub.bh * done
+    flops = 12 * unit
     what = (f"{done} of {w.bkv} KV-head groups" if done <= w.bkv else
             f"{done} KV-head groups ({done / w.bkv:.1f} passes over the workload's {w.bkv})")
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
@@ -194,7 +242,9 @@ def cpu_baseline(w, x, budget_s=10.0, docs=None, min_s=2.0):
             "sample": (f"{what} (each a KV head with its {g} query heads, S={w.seq_len}): "
                        f"float64 numpy oracle, prologue + attention fwd + bwd, {dt:.1f} s, "
                        f"{flops / 1e9:.1f} GFLOP algorithmic"),
-            "seconds": dt, "blas": blas, "affinity_cpus": len(os.sched_getaffinity(0))}
+            "seconds": dt, "fwd_seconds": dt_f, "bwd_seconds": dt_b,
+            "fwd_value": 4 * unit / dt_f / 1e12, "bwd_value": 8 * unit / dt_b / 1e12,
+            "blas": blas, "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
 def copy_calibration():
@@ -210,66 +260,129 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "dispatches": 5}))
 
 
-def pmc_per_dispatch(folder, counter, name_part):
-    """Average of `counter` per dispatch over the dispatches whose kernel name contains
-    `name_part`, from the counter-collection CSVs rocprofv3 wrote under `folder`."""
+def pmc_rows(folder):
+    """Per-dispatch counter values from the counter-collection CSVs rocprofv3 wrote under
+    `folder`: {(file, dispatch): {"kernel": name, "ns": duration, counter: value}}."""
     import csv
     import glob
-    per = {}
-    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
-    for fn in files:
+    out = {}
+    for fn in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
         with open(fn, newline="") as f:
             for row in csv.DictReader(f):
-                if row.get("Counter_Name") != counter:
-                    continue
-                if name_part.lower() not in row.get("Kernel_Name", "").lower():
-                    continue
-                key = (fn, row.get("Dispatch_Id"))
-                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
-    if not per:
-        raise SystemExit(f"no {counter} rows for kernels matching '{name_part}' under {folder}")
-    return sum(per.values()) / len(per), len(per)
+                d = out.setdefault((fn, row["Dispatch_Id"]), {
+                    "kernel": row["Kernel_Name"],
+                    "ns": int(row["End_Timestamp"]) - int(row["Start_Timestamp"])})
+                d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    return out
 
 
-def traffic_summary(dirs, workload_name):
-    """Write the committed traffic summary of the dk/dv kernel: FETCH_SIZE and WRITE_SIZE
-    (KiB per dispatch) and the same counters per KiB of a plain 1 GiB device copy, with the
-    hash of the kernel sources they were taken on (the bench reports `traffic` only while
-    that hash still matches)."""
-    fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
-    fetch, n_f = pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "dkdv")
-    write, n_w = pmc_per_dispatch(write_dir, "WRITE_SIZE", "dkdv")
-    cfetch, _ = pmc_per_dispatch(cfetch_dir, "FETCH_SIZE", "copy")
-    cwrite, _ = pmc_per_dispatch(cwrite_dir, "WRITE_SIZE", "copy")
+def library_kernel(compiled_name):
+    low = compiled_name.lower()
+    for name, part in KERNEL_MATCH:
+        if part in low:
+            return name
+    return "copy" if "copy" in low else None
+
+
+def pmc_means(folder):
+    """Mean of every counter (and of the duration) per dispatch, per library kernel."""
+    acc = {}
+    for d in pmc_rows(folder).values():
+        k = library_kernel(d["kernel"])
+        if k is None:
+            continue
+        a = acc.setdefault(k, {"dispatches": 0})
+        a["dispatches"] += 1
+        for c, v in d.items():
+            if c != "kernel":
+                a[c] = a.get(c, 0.0) + v
+    return {k: {c: (v / a["dispatches"] if c != "dispatches" else v) for c, v in a.items()}
+            for k, a in acc.items()}
+
+
+def counter_summary(dirs, w):
+    """Write profiles/counters_<workload>.json and .md: per library kernel of the step, the
+    SQ counters of one pass (MFMA busy cycles and bf16 MFMA ops, LDS instructions and bank
+    conflicts, GRBM active cycles) and the HBM bytes of a FETCH_SIZE and a WRITE_SIZE pass,
+    each scaled by what the same counter reads for a plain 1 GiB device copy; tagged with the
+    hash of the kernel sources they were taken on."""
+    sq_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
+    sq, fe, wr = pmc_means(sq_dir), pmc_means(fetch_dir), pmc_means(write_dir)
     kib = (1 << 30) / 1024.0
-    files = ["attn.hip", "attn_bf16.hip", "xattn_device.h"]
-    h = hashlib.sha256()
-    for src in files:
-        with open(os.path.join(CSRC, src), "rb") as f:
-            h.update(f.read())
-    scale = {"fetch": cfetch / kib, "write": cwrite / kib,
-             "note": "FETCH_SIZE / WRITE_SIZE (KiB) of one 1 GiB device copy divided by "
-                     "1 GiB in KiB"}
+    scale = {"fetch": pmc_means(cfetch_dir)["copy"]["FETCH_SIZE"] / kib,
+             "write": pmc_means(cwrite_dir)["copy"]["WRITE_SIZE"] / kib}
+    units = kernel_units(w)
+    kernels = {}
+    for k, c in sq.items():
+        if k == "copy":
+            continue
+        e = {"dispatches": int(c["dispatches"]), "pmc_pass_us": c["ns"] / 1e3}
+        grbm = c["GRBM_GUI_ACTIVE"] / XCDS          # active cycles of one XCD
+        e["grbm_clock_ghz"] = grbm / c["ns"]
+        e["mfma_busy"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (grbm * SIMDS)
+        e["mfma_tflops_counter"] = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / (c["ns"] * 1e-9) / 1e12
+        e["mfma_insts"] = c["SQ_INSTS_MFMA"]
+        e["lds_insts"] = c["SQ_INSTS_LDS"]
+        e["lds_insts_per_mfma"] = c["SQ_INSTS_LDS"] / c["SQ_INSTS_MFMA"] if c["SQ_INSTS_MFMA"] else None
+        e["valu_insts_per_mfma"] = c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"] if c["SQ_INSTS_MFMA"] else None
+        e["lds_bank_conflict_rate"] = (c["SQ_LDS_BANK_CONFLICT"] /
+                                       max(c["SQ_LDS_IDX_ACTIVE"] - c["SQ_LDS_BANK_CONFLICT"], 1.0))
+        if k in fe and k in wr:
+            e["hbm_fetch_bytes"] = fe[k]["FETCH_SIZE"] / scale["fetch"] * 1024.0
+            e["hbm_write_bytes"] = wr[k]["WRITE_SIZE"] / scale["write"] * 1024.0
+            e["hbm_bytes"] = e["hbm_fetch_bytes"] + e["hbm_write_bytes"]
+            e["hbm_gbs_counter"] = e["hbm_bytes"] / (fe[k]["ns"] * 1e-9) / 1e9
+        if k in units:
+            e["bound"], e["algorithmic_work"], e["work_basis"] = units[k]
+        kernels[k] = e
     pre = "cd /tmp && export TMPDIR=/tmp && "
-    bench_cmd = "-- python3 $REPO/bench.py --steps 3 --warmup 1 --settle-ms 0 --no-cpu-baseline"
-    t = {"kernel": "attn_bwd_dkdv", "workload": workload_name,
-         "source_sha256": h.hexdigest(), "source_files": files,
-         "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
-         "dispatches": min(n_f, n_w), "copy_scale": scale,
+    run = f"-- python3 $REPO/bench.py --workload {w.index} --steps 3 --warmup 1 --settle-ms 0 --no-cpu-baseline"
+    copy = "-- python3 $REPO/bench.py --copy-calibration"
+    t = {"workload": w.name, "source_sha256": sources_sha(), "source_files": KERNEL_SOURCES,
+         "copy_scale": scale, "kernels": kernels,
+         "notes": {"mfma_busy": "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE of one XCD x 1024 "
+                                "SIMDs): the MFMA-busy fraction of the active cycles, i.e. the "
+                                "fraction of the MFMA peak at the measured clock",
+                   "grbm_clock_ghz": "GRBM_GUI_ACTIVE of one XCD / dispatch duration",
+                   "mfma_tflops_counter": "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / dispatch "
+                                          "duration (executed MFMA work, recompute included)",
+                   "hbm_bytes": "FETCH_SIZE / copy_scale.fetch + WRITE_SIZE / copy_scale.write, "
+                                "KiB -> bytes, per dispatch",
+                   "pmc_pass_us": "dispatch duration inside the counter pass (counter "
+                                  "collection serialises kernels; the kernel-trace stats give "
+                                  "the timing)"},
          "commands": [
-             pre + f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex dkdv "
-             f"-d $REPO/{fetch_dir} -o dkdv -f csv " + bench_cmd,
-             pre + f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --kernel-include-regex dkdv "
-             f"-d $REPO/{write_dir} -o dkdv -f csv " + bench_cmd,
-             pre + f"timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE -d $REPO/{cfetch_dir} -o copy "
-             "-f csv -- python3 $REPO/bench.py --copy-calibration",
-             pre + f"timeout -s KILL 90 rocprofv3 --pmc WRITE_SIZE -d $REPO/{cwrite_dir} -o copy "
-             "-f csv -- python3 $REPO/bench.py --copy-calibration",
-             f"python3 bench.py --traffic-summary {fetch_dir} {write_dir} {cfetch_dir} {cwrite_dir}"],
-         "hbm_bytes_per_dispatch": (fetch / scale["fetch"] + write / scale["write"]) * 1024.0}
-    with open(TRAFFIC_FILE, "w") as f:
+             pre + f"timeout -s KILL 120 rocprofv3 --pmc {' '.join(SQ_COUNTERS)} -d $REPO/{sq_dir} -o pmc -f csv " + run,
+             pre + f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d $REPO/{fetch_dir} -o pmc -f csv " + run,
+             pre + f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d $REPO/{write_dir} -o pmc -f csv " + run,
+             pre + f"timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE -d $REPO/{cfetch_dir} -o copy -f csv " + copy,
+             pre + f"timeout -s KILL 90 rocprofv3 --pmc WRITE_SIZE -d $REPO/{cwrite_dir} -o copy -f csv " + copy,
+             f"python3 bench.py --workload {w.index} --counter-summary {' '.join(dirs)}"]}
+    with open(counters_file(w.name), "w") as f:
         json.dump(t, f, indent=1)
-    log(f"wrote {TRAFFIC_FILE}: {t['hbm_bytes_per_dispatch'] / 1e6:.1f} MB per dispatch")
+    lines = [f"# Counters: {w.name}", "",
+             f"Per dispatch, means over the dispatches of `bench.py --workload {w.index}` under "
+             "rocprofv3 (three steps). Commands:", ""]
+    lines += [f"    {c}" for c in t["commands"]]
+    lines += ["", "| kernel | dispatches | MFMA busy | counter TFLOP/s | GRBM GHz | LDS inst / MFMA "
+              "| VALU inst / MFMA | LDS bank conflict | HBM MB (fetch + write) | HBM GB/s |",
+              "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    f2 = lambda v, fmt: "—" if v is None else format(v, fmt)
+    for k, e in kernels.items():
+        hb = e.get("hbm_bytes")
+        lines.append(
+            f"| {k} | {e['dispatches']} | {100 * e['mfma_busy']:.1f} % | "
+            f"{e['mfma_tflops_counter']:.0f} | {e['grbm_clock_ghz']:.2f} | "
+            f"{f2(e['lds_insts_per_mfma'], '.2f')} | {f2(e['valu_insts_per_mfma'], '.2f')} | "
+            f"{100 * e['lds_bank_conflict_rate']:.2f} % | "
+            f"{'—' if hb is None else format(hb / 1e6, '.1f')} | "
+            f"{'—' if hb is None else format(e['hbm_gbs_counter'], '.0f')} |")
+    lines += ["", "Copy calibration (counter KiB per KiB copied): "
+              f"FETCH_SIZE {scale['fetch']:.3f}, WRITE_SIZE {scale['write']:.3f}.",
+              f"Kernel sources hash: `{t['source_sha256'][:16]}`."]
+    with open(counters_file(w.name)[:-5] + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"wrote {counters_file(w.name)} and .md")
 
 
 PROJ_METRIC = "attention-block projections fwd+bwd TFLOP/s (bf16 GEMMs, fp32 accumulate)"
@@ -338,7 +451,7 @@ def proj_bench(args):
     achieved = flops / (k["ms_per_step"] * 1e-3) / 1e12  # all GEMM flops over all GEMM time
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS[w.dtype],
                 "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS[w.dtype], "traffic": None,
-                "kernel": "proj_gemm (hipBLASLt)", "work_per_launch": flops / k["launches_per_step"],
+                "kernel": "proj_gemm (gemm_bf16_kernel)", "work_per_launch": flops / k["launches_per_step"],
                 "work_basis": "2*M*N*K of the step's 10 GEMMs, averaged per launch"}
     cpu = None
     if not args.no_cpu_baseline:
@@ -529,9 +642,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    if args.traffic_summary:
+    if args.counter_summary:
         import workloads as W
-        traffic_summary(args.traffic_summary, W.WORKLOADS[args.workload].name)
+        counter_summary(args.counter_summary, W.WORKLOADS[args.workload])
         return
     if args.decode:
         decode_bench(args)
@@ -570,20 +683,24 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    # timed region: K steps, bracketed by a synchronisation on both sides
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region: K steps, bracketed by a synchronisation on both sides; an event between
+    # consecutive steps (recording one does not wait) gives each step's own time
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step.run()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    ms_median = per_step[len(per_step) // 2] if len(per_step) % 2 else \
+        0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
     value = flops["total"] / (ms * 1e-3) / 1e12
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}), "
-        f"{value:.1f} TFLOP/s")
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step (median {ms_median:.3f}, min "
+        f"{per_step[0]:.3f}; wall {wall * 1e3 / args.steps:.3f}), {value:.1f} TFLOP/s")
 
     # per-kernel durations: the same K steps again with library HIP events around every
     # launch (recorded on the launch stream)
@@ -618,10 +735,20 @@ def main():
         achieved, peak, unit = work / avg_s / 1e12, PEAK_TFLOPS[w.dtype], "TFLOP/s"
     else:
         achieved, peak, unit = work / avg_s / 1e9, PEAK_HBM_GBS, "GB/s"
-    traffic = traffic_for(dom, wname)
+    cnt = counters_for(dom, wname)
+    traffic = cnt.get("hbm_bytes") if cnt else None
     roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                 "frac": achieved / peak, "traffic": traffic, "kernel": dom,
                 "work_per_launch": work, "work_basis": what}
+    peak_dev = device_peak(w.dtype) if bound == "mfma" else None
+    if peak_dev:
+        roofline["peak_rederived"] = peak_dev
+        roofline["frac_rederived"] = achieved / peak_dev["tflops"]
+    if cnt and bound == "mfma":
+        # the same kernel's counters (committed summary, current sources): MFMA-busy fraction
+        # of the active cycles = fraction of the MFMA peak at the measured clock
+        roofline["frac_measured_clock"] = cnt["mfma_busy"]
+        roofline["measured_clock_ghz"] = cnt["grbm_clock_ghz"]
     log(f"kernels: " + ", ".join(f"{n} {k['avg_ms']:.3f} ms x{k['launches_per_step']:.0f}"
                                   for n, k in kernels.items()))
     attn_ms = sum(kernels[n]["ms_per_step"] for n in ("attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv")
@@ -636,6 +763,8 @@ def main():
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "settle": settled, "ms_per_step": ms,
+        "ms_per_step_median": ms_median, "ms_per_step_min": per_step[0],
+        "tflops_at_median": flops["total"] / (ms_median * 1e-3) / 1e12,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": wname, "batch": w.batch, "seq_len": w.seq_len,

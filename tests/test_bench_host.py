@@ -1,6 +1,7 @@
-"""Host logic of bench.py (no GPU): the rocprofv3 counter-CSV reader, the HBM traffic
-summary written from it, and the guard that reports traffic only for the kernel source
-the counters were taken on."""
+"""Host logic of bench.py (no GPU): the rocprofv3 counter-CSV reader, the per-kernel counter
+summary written from it (HBM bytes scaled by a plain copy, MFMA busy fraction, counter
+TFLOP/s), and the guard that reports counters only for the kernel sources they were taken
+on."""
 import csv
 import importlib.util
 import json
@@ -20,56 +21,77 @@ def bench():
 
 
 def write_csv(folder, rows):
-    """rows: (dispatch id, kernel name, counter, value) in rocprofv3's counter CSV layout,
-    one row per dimension instance as the tool writes them."""
+    """rows: (dispatch id, kernel name, counter, value[, duration ns]) in rocprofv3's counter
+    CSV layout, one row per dimension instance as the tool writes them."""
     os.makedirs(os.path.join(folder, "host"), exist_ok=True)
     path = os.path.join(folder, "host", "1234_counter_collection.csv")
     with open(path, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
-                                          "Counter_Value"])
+                                          "Counter_Value", "Start_Timestamp", "End_Timestamp"])
         w.writeheader()
-        for d, k, c, v in rows:
+        for r in rows:
+            d, k, c, v = r[:4]
+            ns = r[4] if len(r) > 4 else 1000
             w.writerow({"Dispatch_Id": d, "Kernel_Name": k, "Counter_Name": c,
-                        "Counter_Value": v})
+                        "Counter_Value": v, "Start_Timestamp": 5000, "End_Timestamp": 5000 + ns})
 
 
-def test_pmc_per_dispatch_sums_instances_and_averages_dispatches(bench, tmp_path):
+def test_pmc_means_sum_instances_and_average_dispatches(bench, tmp_path):
     d = str(tmp_path / "f")
-    write_csv(d, [(1, "dkdv_pipe_kernel<128>", "FETCH_SIZE", 100.0),
-                  (1, "dkdv_pipe_kernel<128>", "FETCH_SIZE", 50.0),   # second XCC instance
-                  (2, "dkdv_pipe_kernel<128>", "FETCH_SIZE", 170.0),
-                  (3, "dq_kernel<128>", "FETCH_SIZE", 1e9),            # other kernel
-                  (2, "dkdv_pipe_kernel<128>", "WRITE_SIZE", 5.0)])    # other counter
-    avg, n = bench.pmc_per_dispatch(d, "FETCH_SIZE", "dkdv")
-    assert n == 2 and avg == pytest.approx(160.0)
-    with pytest.raises(SystemExit):
-        bench.pmc_per_dispatch(d, "FETCH_SIZE", "no_such_kernel")
+    write_csv(d, [(1, "void x::dkdv_pipe_kernel<128>", "FETCH_SIZE", 100.0),
+                  (1, "void x::dkdv_pipe_kernel<128>", "FETCH_SIZE", 50.0),  # 2nd instance
+                  (2, "void x::dkdv_pipe_kernel<128>", "FETCH_SIZE", 170.0),
+                  (3, "void x::dq_kernel<128>", "FETCH_SIZE", 1e9),
+                  (4, "void x::fwd_kernel<64, true>", "FETCH_SIZE", 8.0),
+                  (5, "void x::qknorm_rope_fwd_table_kernel<1>", "FETCH_SIZE", 4.0),
+                  (6, "some_other_kernel", "FETCH_SIZE", 1.0)])
+    m = bench.pmc_means(d)
+    assert m["attn_bwd_dkdv"]["dispatches"] == 2
+    assert m["attn_bwd_dkdv"]["FETCH_SIZE"] == pytest.approx(160.0)
+    assert m["attn_bwd_dq"]["FETCH_SIZE"] == 1e9
+    assert m["attn_fwd"]["FETCH_SIZE"] == 8.0 and m["qknorm_rope_fwd"]["FETCH_SIZE"] == 4.0
+    assert set(m) == {"attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd", "qknorm_rope_fwd"}
 
 
-def test_traffic_summary_scales_by_the_copy_and_guards_the_source(bench, tmp_path,
+def test_counter_summary_scales_by_the_copy_and_guards_the_source(bench, tmp_path,
                                                                  monkeypatch):
+    import workloads as W
+    w = W.WORKLOADS[5]
     kib = float(1 << 20)  # 1 GiB in KiB
-    dirs = [str(tmp_path / n) for n in ("f", "w", "cf", "cw")]
-    write_csv(dirs[0], [(1, "dkdv", "FETCH_SIZE", 1000.0)])
-    write_csv(dirs[1], [(1, "dkdv", "WRITE_SIZE", 300.0)])
+    dirs = [str(tmp_path / n) for n in ("sq", "f", "w", "cf", "cw")]
+    k = "void x::dkdv_pipe_kernel<128, true>"
+    ns = 300_000
+    # one XCD active for 600k cycles in 300 us (2 GHz); MFMAs busy 40 % of 1024 SIMDs
+    sq = {"GRBM_GUI_ACTIVE": 8 * 600_000, "SQ_VALU_MFMA_BUSY_CYCLES": 0.4 * 600_000 * 1024,
+          "SQ_INSTS_VALU_MFMA_MOPS_BF16": 2e8, "SQ_INSTS_MFMA": 1e6, "SQ_INSTS_LDS": 2e6,
+          "SQ_LDS_BANK_CONFLICT": 10.0, "SQ_LDS_IDX_ACTIVE": 1010.0, "SQ_INSTS_VALU": 5e6,
+          "SQ_BUSY_CU_CYCLES": 1.0}
+    write_csv(dirs[0], [(1, k, c, v, ns) for c, v in sq.items()])
+    write_csv(dirs[1], [(1, k, "FETCH_SIZE", 1000.0, ns)])
+    write_csv(dirs[2], [(1, k, "WRITE_SIZE", 300.0, ns)])
     # the plain 1 GiB copy reads half its bytes in FETCH_SIZE KiB, all in WRITE_SIZE
-    write_csv(dirs[2], [(7, "__amd_rocclr_copyBuffer", "FETCH_SIZE", kib / 2)])
-    write_csv(dirs[3], [(7, "__amd_rocclr_copyBuffer", "WRITE_SIZE", kib)])
-    out = str(tmp_path / "traffic.json")
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", out)
-    bench.traffic_summary(dirs, "some_workload")
-    t = json.load(open(out))
+    write_csv(dirs[3], [(7, "__amd_rocclr_copyBuffer", "FETCH_SIZE", kib / 2)])
+    write_csv(dirs[4], [(7, "__amd_rocclr_copyBuffer", "WRITE_SIZE", kib)])
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    bench.counter_summary(dirs, w)
+    t = json.load(open(bench.counters_file(w.name)))
+    assert os.path.exists(bench.counters_file(w.name)[:-5] + ".md")
+    e = t["kernels"]["attn_bwd_dkdv"]
     assert t["copy_scale"]["fetch"] == pytest.approx(0.5)
     assert t["copy_scale"]["write"] == pytest.approx(1.0)
-    assert t["hbm_bytes_per_dispatch"] == pytest.approx((1000.0 / 0.5 + 300.0) * 1024.0)
+    assert e["hbm_bytes"] == pytest.approx((1000.0 / 0.5 + 300.0) * 1024.0)
+    assert e["mfma_busy"] == pytest.approx(0.4)
+    assert e["grbm_clock_ghz"] == pytest.approx(2.0)
+    assert e["mfma_tflops_counter"] == pytest.approx(2e8 * 512 / 300e-6 / 1e12)
+    assert e["lds_insts_per_mfma"] == pytest.approx(2.0)
+    assert e["lds_bank_conflict_rate"] == pytest.approx(0.01)
     # reported for the same kernel, workload and sources only
-    assert bench.traffic_for("attn_bwd_dkdv", "some_workload") == \
-        pytest.approx(t["hbm_bytes_per_dispatch"])
-    assert bench.traffic_for("attn_bwd_dkdv", "other_workload") is None
-    assert bench.traffic_for("attn_fwd", "some_workload") is None
+    assert bench.counters_for("attn_bwd_dkdv", w.name)["hbm_bytes"] == pytest.approx(e["hbm_bytes"])
+    assert bench.counters_for("attn_bwd_dkdv", "other_workload") is None
+    assert bench.counters_for("attn_fwd", w.name) is None
     t["source_sha256"] = "0" * 64
-    json.dump(t, open(out, "w"))
-    assert bench.traffic_for("attn_bwd_dkdv", "some_workload") is None
+    json.dump(t, open(bench.counters_file(w.name), "w"))
+    assert bench.counters_for("attn_bwd_dkdv", w.name) is None
 
 
 def test_gpus_above_one_exits_with_a_message(bench, monkeypatch, capsys):
