@@ -24,7 +24,7 @@ __all__ = [
     "xattn_rope_cache", "xattn_qknorm_rope_fwd", "xattn_qknorm_rope_fwd_table",
     "xattn_qknorm_rope_bwd_workspace_bytes",
     "xattn_qknorm_rope_bwd", "xattn_fwd", "xattn_fwd_qnorm", "xattn_bwd_workspace_bytes",
-    "xattn_bwd",
+    "xattn_bwd", "xattn_bwd_noalloc",
     "xattn_decode_workspace_bytes", "xattn_decode", "xattn_segments", "xattn_rope_cache_at",
     "xattn_proj_workspace_bytes", "xattn_qkv_proj_fwd", "xattn_out_proj_fwd",
     "xattn_out_proj_bwd", "xattn_qkv_proj_bwd",
@@ -116,6 +116,8 @@ def load_library() -> ctypes.CDLL:
         "xattn_bwd_workspace_bytes": (sz, [ctypes.POINTER(Dims), ctypes.c_int]),
         "xattn_bwd": (i32, [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                             ctypes.POINTER(Prologue), vp, sz, vp]),
+        "xattn_bwd_noalloc": (i32, [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    ctypes.POINTER(Prologue), vp]),
         "xattn_proj_workspace_bytes": (sz, [ctypes.POINTER(Dims), i64]),
         "xattn_qkv_proj_fwd": (i32, [ctypes.POINTER(Dims), ctypes.POINTER(Proj), vp, vp, vp,
                                      vp, vp, sz, vp]),
@@ -383,6 +385,30 @@ def xattn_bwd(dims: Dims, q, k, v, out, lse, dout, dq, dk, dv, prologue, workspa
     _check(load_library().xattn_bwd(
         ctypes.byref(dims), *p[:9], ctypes.byref(pro) if pro is not None else None, p[9],
         _bytes(workspace, "workspace"), _stream(stream)), "xattn_bwd")
+
+
+def xattn_bwd_noalloc(dims: Dims, q, k, v, out, lse, dout, dq, dk, dv, prologue, stream=None):
+    """xattn_bwd with the library's static scratch in place of a workspace (no allocation;
+    calls that overlap on one GPU race on that scratch)."""
+    nq, nk, nr, nrk, nt = _sizes(dims)
+    hd = dims.head_dim
+    _io(q, "q")
+    specs = [(q, "q", None, nq), (k, "k", q.dtype, nk), (v, "v", q.dtype, nk),
+             (out, "out", q.dtype, nq), (lse, "lse", F32, nr), (dout, "dout", q.dtype, nq),
+             (dq, "dq", q.dtype, nq), (dk, "dk", q.dtype, nk), (dv, "dv", q.dtype, nk)]
+    if prologue is not None:
+        pr = prologue
+        specs += [(pr["xq"], "xq", q.dtype, nq), (pr["xk"], "xk", q.dtype, nk),
+                  (pr["gamma_q"], "gamma_q", F32, hd), (pr["gamma_k"], "gamma_k", F32, hd),
+                  (pr["rstd_q"], "rstd_q", F32, nr), (pr["rstd_k"], "rstd_k", F32, nrk),
+                  (pr["cos_tab"], "cos_tab", F32, AtLeast(nt)),
+                  (pr["sin_tab"], "sin_tab", F32, AtLeast(nt)),
+                  (pr["dgamma_q"], "dgamma_q", F32, hd), (pr["dgamma_k"], "dgamma_k", F32, hd)]
+    p = _ptrs(*specs)
+    pro = Prologue(*p[9:]) if prologue is not None else None
+    _check(load_library().xattn_bwd_noalloc(
+        ctypes.byref(dims), *p[:9], ctypes.byref(pro) if pro is not None else None,
+        _stream(stream)), "xattn_bwd_noalloc")
 
 
 def make_decode_dims(xq, k_cache, num_heads, num_kv_heads, cache_len) -> DecodeDims:

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libxattn.so")
 SOURCES = ["attn.hip", "attn_bf16.hip", "prologue.hip", "decode.hip", "proj.hip", "gemm.hip",
-           "xattn_api.cpp", "profile.cpp"]
+           "xattn_api.cpp", "profile.cpp", "noalloc.hip"]
 LINK_LIBS: list = []
 # Per-source extra flags.  attn_bf16.hip: MFMA results go to VGPRs (the score tiles are
 # consumed by VALU right away; AGPR results would need a copy per element).

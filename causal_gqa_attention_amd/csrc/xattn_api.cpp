@@ -322,6 +322,8 @@ DecodeWorkspace decode_workspace(const DecodeChecked& c) {
 
 }  // namespace
 
+void xattn::set_last_error(const char* msg) { g_last_error = msg; }
+
 extern "C" {
 
 const char* xattn_version(void) { return "libxattn 0.1.0 (gfx950)"; }

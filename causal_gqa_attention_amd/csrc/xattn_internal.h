@@ -11,6 +11,9 @@ namespace xattn {
 
 enum IoType { IO_F32 = 0, IO_BF16 = 1 };
 
+// Sets the calling thread's message returned by xattn_last_error().
+void set_last_error(const char* msg);
+
 // ---- prologue ------------------------------------------------------------------------
 hipError_t launch_rope_cache(float* cos_tab, float* sin_tab, int seq_len, int head_dim,
                              double theta, hipStream_t stream);

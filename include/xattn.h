@@ -218,6 +218,23 @@ xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, con
                        void* dk, void* dv, const xattn_prologue* pro, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* Attention backward with no allocation and no workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments and results as xattn_bwd (bitwise: the same kernels),
+ * but the scratch is a static device array of XATTN_BWD_NOALLOC_SCRATCH_BYTES that each GPU
+ * holds until the process ends; its address is looked up on the first call with that GPU
+ * current.  A shape whose xattn_bwd_workspace_bytes exceeds that size is rejected with
+ * XATTN_ERR_UNSUPPORTED: 16 MiB holds, with the prologue, about 900 thousand query rows
+ * (B*H*S) of bf16 MHA at head_dim 64 (6.4 MiB for B=32, S=1024, 12 heads) and about 60
+ * thousand of fp32.  Every call on one GPU shares its array, and the array keeps the
+ * last call's contents (nothing in it needs to start at zero): calls that overlap on one
+ * GPU (different streams or threads) race and must be serialised by the caller. */
+#define XATTN_BWD_NOALLOC_SCRATCH_BYTES (16u << 20)
+xattn_status xattn_bwd_noalloc(const xattn_dims* dims, const void* q, const void* k,
+                               const void* v, const void* out, const float* lse,
+                               const void* dout, void* dq, void* dk, void* dv,
+                               const xattn_prologue* pro, void* stream);
+
 /* ---- Projections around attention --------------------------------------------------------
  * [MINT] 5.3.1-5.3.2: Q = X Wq + bq, K = X Wk + bk, V = X Wv + bv, output
  * Concat(heads) Wo + bo, with weights [d_in, d_out] applied as x @ W; [T5] layout pipeline:

@@ -33,7 +33,7 @@ def lib():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(lib, n), n
     assert "gfx950" in X.xattn_version()
@@ -389,3 +389,16 @@ def test_binding_checks_decode_sizes():
                        lse, ws)
     with pytest.raises(ValueError, match="device tensor"):
         X.xattn_decode(d, xq, xk, xk, g, g, tab, tab, 1e-6, kc, kc.clone(), xq.clone(), lse, ws)
+
+
+def test_bwd_noalloc_validation(lib):
+    """Shapes beyond the static scratch and invalid dims are rejected before any device
+    call."""
+    big = dims(B=4, S=16384, H=64, Hkv=8, hd=128)
+    assert lib.xattn_bwd_workspace_bytes(ctypes.byref(big), 0) > (16 << 20)
+    p = [A + i * 16 * MB for i in range(9)]
+    assert lib.xattn_bwd_noalloc(ctypes.byref(big), *p, None, None) == UNSUPPORTED
+    assert "static scratch" in last(lib)
+    assert lib.xattn_bwd_noalloc(ctypes.byref(dims(H=6, Hkv=4)), *p, None, None) == INVALID
+    assert "multiple of num_kv_heads" in last(lib)
+    assert lib.xattn_bwd_noalloc(None, *p, None, None) == INVALID
