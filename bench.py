@@ -73,6 +73,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of 1 GiB (for HBM counter scaling)")
+    p.add_argument("--stats-summary", nargs=3, default=None,
+                   metavar=("OUT_NAME", "DIR", "BENCH_ARGS"),
+                   help="write profiles/OUT_NAME.md from the kernel statistics CSV of a "
+                        "`rocprofv3 --kernel-trace --stats -f csv -d DIR -o kt -- python3 "
+                        "bench.py BENCH_ARGS` run; no GPU use")
     p.add_argument("--counter-summary", nargs=5, default=None,
                    metavar=("SQ_DIR", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                             "COPY_WRITE_DIR"),
@@ -298,6 +303,41 @@ def pmc_means(folder):
                 a[c] = a.get(c, 0.0) + v
     return {k: {c: (v / a["dispatches"] if c != "dispatches" else v) for c, v in a.items()}
             for k, a in acc.items()}
+
+
+def stats_summary(out_name, folder, bench_args):
+    """profiles/<out_name>.md: the kernel statistics rocprofv3 wrote (calls, total, average,
+    min and max duration per kernel) as a table, with the command that made them."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {folder}")
+    with open(files[0], newline="") as f:
+        rows = list(csv.DictReader(f))
+
+    def col(row, *keys):
+        for k in row:
+            if any(k.lower() == key.lower() for key in keys):
+                return row[k]
+        raise KeyError(keys)
+
+    cmd = (f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
+           f"-d $REPO/{folder} -o kt -- python3 $REPO/bench.py {bench_args}")
+    lines = [f"# Kernel statistics: `bench.py {bench_args}`", "",
+             "Command (one MI355X; `REPO` = the repository root; raw output stays in "
+             "gpurun_out/):", "", f"    {cmd}", "",
+             "| kernel | calls | total us | avg us | min us | max us | % |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        us = lambda *k: float(col(r, *k)) / 1e3
+        lines.append(f"| `{col(r, 'Name', 'KERNEL_NAME')}` | {col(r, 'Calls')} | "
+                     f"{us('TotalDurationNs'):.1f} | {us('AverageNs'):.1f} | "
+                     f"{us('MinNs'):.1f} | {us('MaxNs'):.1f} | "
+                     f"{float(col(r, 'Percentage')):.1f} |")
+    with open(os.path.join(PROFILES, out_name + ".md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"wrote profiles/{out_name}.md")
 
 
 def counter_summary(dirs, w):
@@ -641,6 +681,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.stats_summary:
+        stats_summary(*args.stats_summary)
         return
     if args.counter_summary:
         import workloads as W
