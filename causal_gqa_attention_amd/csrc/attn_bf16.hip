@@ -90,14 +90,36 @@ __device__ __forceinline__ bf16x8 lds_t(lptr base, uint32_t tl, int c2, int dt) 
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// sum over hd of tile rows (base = row R0) with the lane's register fragment
+// init + sum over hd of tile rows (base = row R0) with the lane's register fragment.  The
+// softmax offsets (a running max, lse, D) enter as the accumulator's initial value, so the
+// score tiles leave the matrix unit already shifted and no vector op per score is spent on
+// them.
 template <int HD>
 __device__ __forceinline__ f32x16 contract_rows(lptr base, uint32_t al,
-                                                const bf16x8 (&frag)[HD / 16]) {
-  f32x16 acc = zero16();
+                                                const bf16x8 (&frag)[HD / 16],
+                                                const f32x16& init) {
+  f32x16 acc = init;
 #pragma unroll
   for (int c = 0; c < HD / 16; ++c) acc = mfma_bf16(lds_a<HD>(base, al, c), frag[c], acc);
   return acc;
+}
+
+__device__ __forceinline__ f32x16 splat16(float v) {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = v;
+  return z;
+}
+
+// The register-resident side of the score product (Q in the forward and dq, K in dk/dv) is
+// held pre-multiplied by log2(e)/sqrt(hd), rounded to bf16 once more: the score tiles then
+// come out in the exponent's units (base 2) and need no scaling before exp2.
+template <int HD>
+__device__ __forceinline__ void scale_frag(bf16x8 (&frag)[HD / 16], float c) {
+#pragma unroll
+  for (int k = 0; k < HD / 16; ++k)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) frag[k][j] = (bf16)((float)frag[k][j] * c);
 }
 
 // The lane's row operands (rows R0 + lane%32, all hd) and transposed operands (the 8 k-slots
@@ -217,7 +239,8 @@ struct Dma {
   }
 };
 
-// (lse2, delta) of 32 query rows q0.. into LDS [0,32) and [32,64); NW waves share it.
+// Row statistics of 32 query rows q0.. into LDS: -lse*log2(e) at [0,32), -D at [32,64) (as
+// the dq kernel stores them); NW waves share the copy.
 template <int NW>
 __device__ __forceinline__ void dma_rowstats(float* dst, const float* lse2,
                                              const float* delta, int q0, int S, int wv,
@@ -501,10 +524,6 @@ constexpr int kBN = 128;  // keys per stage
 // ---------------------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------------------
-struct SoftmaxState {
-  float m, l;
-};
-
 // Index range test on a 32x32 score tile: accumulator i of a lane sits at tile index
 // base + c(i), c(i) = 8 (i / 4) + i % 4, where base is the tile origin plus 4 for the upper
 // half-wave.  keep(i) is lo <= base + c(i) <= hi, evaluated as the one unsigned compare
@@ -542,17 +561,24 @@ __device__ __forceinline__ void diag_mask(f32x16& st, int lane) {
   }
 }
 
-// Online softmax of one 32-key sub-tile: scores st (keys x this lane's query) update the
-// running max / sum (rescaling the output accumulator lazily) and give the packed P^T
-// operand of the P.V product.
-// Masked sub-tiles also exclude keys before lo (the first row of the lane's document);
-// a row can then meet a sub-tile with no visible key before its first one, so the masked
-// instantiation keeps a row with no visible key yet (max -inf) empty instead of forming
-// -inf - -inf.
+// Online softmax of one 32-key sub-tile.  st holds the scores in base-2 units minus the
+// lane's reference mref (the matrix unit started from -mref, held in nref); mref is the
+// running max m, or 0 before the row has met a visible key (m = -inf).  The reference is
+// raised only when a tile's max exceeds it by more than 2^8 (exact: numerator and
+// denominator share the reference): then the output accumulator and the sum are rescaled,
+// the tile's scores are shifted to the new reference and nref is rebuilt.  Gives the packed
+// P^T operand of the P.V product.
+// Masked sub-tiles also exclude keys before lo (the first row of the lane's document); a
+// row can then meet a sub-tile with no visible key before its first one, so the masked
+// instantiation keeps such a row empty (reference 0, max -inf).
+struct SoftmaxState {
+  float m, l, mref;
+};
+
 template <int HD, bool MASK>
 __device__ __forceinline__ void fwd_softmax(f32x16 (&o)[HD / 32], SoftmaxState& sm,
-                                            const f32x16& st, bf16x8 (&pb)[2], int kb,
-                                            int qrow, int lo, int S, int h, float scale_log2) {
+                                            f32x16& nref, const f32x16& st, bf16x8 (&pb)[2],
+                                            int kb, int qrow, int lo, int S, int h) {
   float sv[16];
   float tmax = -INFINITY;
   // keys lo .. min(qrow, S - 1) are visible
@@ -564,8 +590,7 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&o)[HD / 32], SoftmaxState& 
     sv[i] = x;
     tmax = fmaxf(tmax, x);
   }
-  tmax = halves_max(tmax) * scale_log2;
-  // rescale only when the reference max grows by more than 2^8
+  tmax = halves_max(tmax) + sm.mref;  // the tile's max in base-2 units
   if (__any(tmax > sm.m + 8.f)) {
     const float m_new = fmaxf(sm.m, tmax);
     const float alpha = (MASK && m_new == -INFINITY) ? 1.f : fast_exp2(sm.m - m_new);
@@ -573,10 +598,15 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&o)[HD / 32], SoftmaxState& 
 #pragma unroll
     for (int dt = 0; dt < HD / 32; ++dt) o[dt] *= alpha;
     sm.m = m_new;
-  }
-  const float mref = (MASK && sm.m == -INFINITY) ? 0.f : sm.m;
+    const float mref = (MASK && m_new == -INFINITY) ? 0.f : m_new;
+    const float shift = mref - sm.mref;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) sv[i] = fast_exp2(sv[i] * scale_log2 - mref);
+    for (int i = 0; i < 16; ++i) sv[i] -= shift;
+    sm.mref = mref;
+    nref = splat16(-mref);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sv[i] = fast_exp2(sv[i]);
   // pairwise sum (a short dependency chain)
   float ps[8];
 #pragma unroll
@@ -590,11 +620,11 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&o)[HD / 32], SoftmaxState& 
 // One 32-key sub-tile: softmax, then O^T += V^T P^T.
 template <int HD, bool MASK>
 __device__ __forceinline__ void fwd_subtile(f32x16 (&o)[HD / 32], SoftmaxState& sm,
-                                            const f32x16& st, lptr vsub, uint32_t tl,
-                                            int kb, int qrow, int lo, int S, int h,
-                                            float scale_log2) {
+                                            f32x16& nref, const f32x16& st, lptr vsub,
+                                            uint32_t tl, int kb, int qrow, int lo, int S,
+                                            int h) {
   bf16x8 pb[2];
-  fwd_softmax<HD, MASK>(o, sm, st, pb, kb, qrow, lo, S, h, scale_log2);
+  fwd_softmax<HD, MASK>(o, sm, nref, st, pb, kb, qrow, lo, S, h);
   acc_tr<HD>(o, vsub, tl, pb);
 }
 
@@ -757,10 +787,12 @@ __global__ __launch_bounds__(64 * kQW, 1) void fwd_kernel(const bf16* __restrict
     for (int u = 0; u < NBUF - 1; ++u)
       if (t0 + u < ntiles) issue(t0 + u, u);
   }
+  scale_frag<HD>(qf, scale_log2);
   f32x16 o[HD / 32];
 #pragma unroll
   for (int dt = 0; dt < HD / 32; ++dt) o[dt] = zero16();
-  SoftmaxState sm{-INFINITY, 0.f};
+  SoftmaxState sm{-INFINITY, 0.f, 0.f};
+  f32x16 nref = zero16();  // -mref in every accumulator slot
   // Stage t: wait for its tile, prefetch stage t + NBUF - 1, then compute.  Stages below
   // nplain lie strictly before the block's first query and inside the sequence, and (with
   // documents) at or after every row's document start, so no wave needs masking there; the
@@ -779,10 +811,10 @@ __global__ __launch_bounds__(64 * kQW, 1) void fwd_kernel(const bf16* __restrict
       const int kb = t * kBN + 32 * s;
       if ((MASK || DIAG) && (kb > qw0 + 31 || kb >= S)) break;  // wave-uniform
       if (MASK && kb + 31 < doc.lo_wave) continue;              // before every row's document
-      f32x16 st = contract_rows<HD>(ks + 32 * s * ROWB, al, qf);
+      f32x16 st = contract_rows<HD>(ks + 32 * s * ROWB, al, qf, nref);
       if (DIAG && kb == qw0) diag_mask<true>(st, lane);
-      fwd_subtile<HD, MASK>(o, sm, st, vs + 32 * s * ROWB, tl, kb, qrow, doc.lo_row, S, h,
-                            scale_log2);
+      fwd_subtile<HD, MASK>(o, sm, nref, st, vs + 32 * s * ROWB, tl, kb, qrow, doc.lo_row, S,
+                            h);
     }
   };
   q_stage_loop(doc, seg_lo != nullptr, min(q0 / kBN, S / kBN), ntiles, S, stage);
@@ -794,20 +826,27 @@ __global__ __launch_bounds__(64 * kQW, 1) void fwd_kernel(const bf16* __restrict
 }
 
 // ---------------------------------------------------------------------------------------
-// backward, dq (+ per-query delta = dO . out and lse2 = lse * log2 e for the dk/dv kernel)
+// backward, dq (+ per-query -D = -dO . out and -lse * log2(e) for the dk/dv kernel)
 // ---------------------------------------------------------------------------------------
+// At hd 128, st = S - lse (base-2 units) and dpt = dP - D come out of the matrix unit (the
+// offsets are the accumulators' initial values, two 16-register tuples): P = exp2(st),
+// dS = P * dpt.  At hd 64 the kernel runs four waves per SIMD and has no registers for the
+// tuples: the offsets lse2 and D are subtracted here.
+constexpr bool dq_offset_tuples(int hd) { return hd == 128; }
+
 template <int HD, bool MASK>
 __device__ __forceinline__ void dq_subtile(f32x16 (&acc)[HD / 32], const f32x16& st,
                                            const f32x16& dpt, lptr ksub, uint32_t tl,
-                                           int kb, int qrow, int lo, int S, int h,
-                                           float scale_log2, float lse2, float D) {
+                                           int kb, int qrow, int lo, int S, int h, float lse2,
+                                           float D) {
+  constexpr bool TUP = dq_offset_tuples(HD);
   float dsv[16];
   const TileRange rg(kb + 4 * h, lo, min(qrow, S - 1));  // visible keys
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    float p = fast_exp2(st[i] * scale_log2 - lse2);
+    float p = fast_exp2(TUP ? st[i] : st[i] - lse2);
     if (MASK && !rg.keep(i)) p = 0.f;
-    dsv[i] = p * (dpt[i] - D);
+    dsv[i] = p * (TUP ? dpt[i] : dpt[i] - D);
   }
   bf16x8 db[2];
   pack16(db, dsv);
@@ -868,10 +907,14 @@ __global__ __launch_bounds__(64 * kQW, HD == 64 ? 4 : 1) void dq_kernel(
   }
   const float Dq = halves_sum(dsum);
   const float lse2 = qrow < S ? lse[(size_t)bh * S + qrow] * kLog2e : 0.f;
+  // the dk/dv kernel takes -D and -lse*log2(e) as accumulator initial values
   if (qrow < S && h == 0) {
-    delta[(size_t)bh * S + qrow] = Dq;
-    lse2_out[(size_t)bh * S + qrow] = lse2;
+    delta[(size_t)bh * S + qrow] = -Dq;
+    lse2_out[(size_t)bh * S + qrow] = -lse2;
   }
+  scale_frag<HD>(qf, scale_log2);
+  constexpr bool TUP = dq_offset_tuples(HD);
+  const f32x16 nl2 = TUP ? splat16(-lse2) : zero16(), nd = TUP ? splat16(-Dq) : zero16();
   f32x16 acc[HD / 32];
 #pragma unroll
   for (int dt = 0; dt < HD / 32; ++dt) acc[dt] = zero16();
@@ -890,11 +933,11 @@ __global__ __launch_bounds__(64 * kQW, HD == 64 ? 4 : 1) void dq_kernel(
       const int kb = t * kBN + 32 * s;
       if ((MASK || DIAG) && (kb > qw0 + 31 || kb >= S)) break;
       if (MASK && kb + 31 < doc.lo_wave) continue;  // before every row's document
-      f32x16 st = contract_rows<HD>(ks + 32 * s * ROWB, al, qf);  // S^T
-      const f32x16 dpt = contract_rows<HD>(vs + 32 * s * ROWB, al, df);  // dP^T
+      f32x16 st = contract_rows<HD>(ks + 32 * s * ROWB, al, qf, nl2);  // S^T (- lse)
+      const f32x16 dpt = contract_rows<HD>(vs + 32 * s * ROWB, al, df, nd);  // dP^T (- D)
       if (DIAG && kb == qw0) diag_mask<true>(st, lane);
       dq_subtile<HD, MASK>(acc, st, dpt, ks + 32 * s * ROWB, tl, kb, qrow, doc.lo_row, S, h,
-                           scale_log2, lse2, Dq);
+                           lse2, Dq);
     }
   };
   q_stage_loop(doc, seg_lo != nullptr, min(q0 / kBN, S / kBN), ntiles, S, stage);
@@ -943,6 +986,19 @@ __device__ __forceinline__ void dkdv_step_reg(f32x16 (&dkt)[HD / 32], f32x16 (&d
 #pragma unroll
       for (int dt = 0; dt < HD / 32; ++dt) x[c2][dt] = lds_t<HD>(base, tl, c2, dt);
   };
+  // -lse (base 2) and -D of the tile's queries, in accumulator layout: the initial values of
+  // the S and dP products
+  f32x16 st, dpt;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 l2 = *reinterpret_cast<const f32x4*>(stats + 8 * g + 4 * h);
+    const f32x4 dd = *reinterpret_cast<const f32x4*>(stats + 32 + 8 * g + 4 * h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      st[4 * g + j] = l2[j];
+      dpt[4 * g + j] = dd[j];
+    }
+  }
   read_rows(qa, qs);
   if constexpr (PF <= 1) read_rows(da, dos);
   if constexpr (PF == 0) {
@@ -950,14 +1006,14 @@ __device__ __forceinline__ void dkdv_step_reg(f32x16 (&dkt)[HD / 32], f32x16 (&d
     read_tr(tq, qs);
   }
   __builtin_amdgcn_sched_barrier(0);
-  f32x16 st = zero16();  // S: queries x keys
+  // S - lse: queries x keys (the K rows are pre-scaled to base-2 units)
 #pragma unroll
   for (int c = 0; c < HD / 16; ++c) st = mfma_bf16(qa[c], kf[c], st);
   if constexpr (PF == 2) {
     read_rows(da, dos);
     __builtin_amdgcn_sched_barrier(0);
   }
-  f32x16 dpt = zero16();  // dP
+  // dP - D
 #pragma unroll
   for (int c = 0; c < HD / 16; ++c) dpt = mfma_bf16(da[c], vf[c], dpt);
   if constexpr (PF >= 1) {
@@ -970,14 +1026,10 @@ __device__ __forceinline__ void dkdv_step_reg(f32x16 (&dkt)[HD / 32], f32x16 (&d
   float pv[16];
   const TileRange rg(q0 + 4 * h, key, min(khi, S - 1));  // queries that see the key
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const f32x4 l2 = *reinterpret_cast<const f32x4*>(stats + 8 * g + 4 * h);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float p = fast_exp2(st[4 * g + j] * scale_log2 - l2[j]);
-      if (MASK && !rg.keep(4 * g + j)) p = 0.f;
-      pv[4 * g + j] = p;
-    }
+  for (int i = 0; i < 16; ++i) {
+    float p = fast_exp2(st[i]);
+    if (MASK && !rg.keep(i)) p = 0.f;
+    pv[i] = p;
   }
   bf16x8 pb[2];
   pack16(pb, pv);
@@ -991,11 +1043,7 @@ __device__ __forceinline__ void dkdv_step_reg(f32x16 (&dkt)[HD / 32], f32x16 (&d
   }
   float dsv[16];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const f32x4 dd = *reinterpret_cast<const f32x4*>(stats + 32 + 8 * g + 4 * h);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dsv[4 * g + j] = pv[4 * g + j] * (dpt[4 * g + j] - dd[j]);
-  }
+  for (int i = 0; i < 16; ++i) dsv[i] = pv[i] * dpt[i];
   bf16x8 db[2];
   pack16(db, dsv);
 #pragma unroll
@@ -1052,6 +1100,7 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_shared_kernel(
   bf16x8 kf[HD / 16], vf[HD / 16];
   load_frag<HD>(kf, k + (size_t)kvbh * S * HD, key, S, lane);
   load_frag<HD>(vf, v + (size_t)kvbh * S * HD, key, S, lane);
+  scale_frag<HD>(kf, scale_log2);
   f32x16 dkt[HD / 32], dvt[HD / 32];
 #pragma unroll
   for (int dt = 0; dt < HD / 32; ++dt) dkt[dt] = dvt[dt] = zero16();
@@ -1174,6 +1223,7 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_private_kernel(
   bf16x8 kf[HD / 16], vf[HD / 16];  // K and V rows of the lane's key
   load_frag<HD>(kf, k + (size_t)kvbh * S * HD, key, S, lane);
   load_frag<HD>(vf, v + (size_t)kvbh * S * HD, key, S, lane);
+  scale_frag<HD>(kf, scale_log2);
   f32x16 dkt[HD / 32], dvt[HD / 32];
 #pragma unroll
   for (int dt = 0; dt < HD / 32; ++dt) dkt[dt] = dvt[dt] = zero16();
@@ -1399,6 +1449,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_kernel(
     const lptr cur = lmine + (2 * (t % NB)) * TILEB;
     const float* stt = sst[t % NB];
     const int q0 = (qt_first + st + 2 * i) * kBQ;
+    // -lse (base 2) and -D of tile t's queries; in this kernel the offsets are applied by
+    // the vector unit (the pipelined schedule measured slower with them as the products'
+    // initial values)
     f32x4 l2[4], dd[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -1418,10 +1471,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_kernel(
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float p = fast_exp2(s_cur[4 * g + j] * scale_log2 - l2[g][j]);
+        float p = fast_exp2(s_cur[4 * g + j] * scale_log2 + l2[g][j]);
         if (MASK && !rg.keep(4 * g + j)) p = 0.f;
         pv[4 * g + j] = p;
-        dsv[4 * g + j] = p * (p_cur[4 * g + j] - dd[g][j]);
+        dsv[4 * g + j] = p * (p_cur[4 * g + j] + dd[g][j]);
       }
     bf16x8 pb[2], db[2];
     pack16(pb, pv);

@@ -76,7 +76,7 @@ hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const v
                            const void* v, void* out, float* lse, hipStream_t stream);
 
 // gfx950 fast path (bf16 io, head_dim 64 or 128), attn_bf16.hip.  The backward also
-// writes lse2 = lse * log2(e) and delta per query row (workspace) for its dk/dv kernel.
+// writes -lse * log2(e) and -D (D = dO . out) per query row (workspace) for its dk/dv kernel.
 bool fast_bf16_supported(int head_dim);
 // With `pro` non-null the forward reads the raw pro->xq instead of q and applies the
 // QK-norm + RoPE forward to its resident Q rows itself, writing the rotated rows to
