@@ -328,8 +328,10 @@ extern "C" {
 
 const char* xattn_version(void) { return "libxattn 0.1.0 (gfx950)"; }
 
-const char* xattn_status_string(xattn_status s) {
-  switch (s) {
+const char* xattn_status_string(int32_t status) {
+  // an integer, not the enum type: C callers may pass any value, and loading an
+  // out-of-range value as the enum would be undefined
+  switch (status) {
     case XATTN_OK: return "XATTN_OK";
     case XATTN_ERR_INVALID_ARG: return "XATTN_ERR_INVALID_ARG: invalid argument";
     case XATTN_ERR_UNSUPPORTED: return "XATTN_ERR_UNSUPPORTED: shape not supported";

@@ -348,8 +348,9 @@ xattn_status xattn_profile_start(void);
 xattn_status xattn_profile_stop(xattn_kernel_time* entries, int32_t max_entries,
                                 int32_t* n_entries);
 
-/* Static description of a status code. */
-const char* xattn_status_string(xattn_status s);
+/* Static description of a status code; any integer is accepted (values that are not an
+ * xattn_status give "unknown xattn_status"). */
+const char* xattn_status_string(int32_t status);
 
 /* Thread-local message describing the last failing call on this thread ("" if none). */
 const char* xattn_last_error(void);
