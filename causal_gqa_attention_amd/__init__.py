@@ -25,7 +25,7 @@ __all__ = [
     "xattn_qknorm_rope_bwd_workspace_bytes",
     "xattn_qknorm_rope_bwd", "xattn_fwd", "xattn_fwd_qnorm", "xattn_bwd_workspace_bytes",
     "xattn_bwd", "xattn_bwd_noalloc",
-    "xattn_decode_workspace_bytes", "xattn_decode", "xattn_segments", "xattn_rope_cache_at",
+    "xattn_decode_workspace_bytes", "xattn_decode", "xattn_decode_varlen", "xattn_segments", "xattn_rope_cache_at",
     "xattn_proj_workspace_bytes", "xattn_qkv_proj_fwd", "xattn_out_proj_fwd",
     "xattn_out_proj_bwd", "xattn_qkv_proj_bwd",
     "xattn_status_string", "xattn_last_error", "xattn_version", "xattn_profile_start",
@@ -130,6 +130,8 @@ def load_library() -> ctypes.CDLL:
         "xattn_decode_workspace_bytes": (sz, [ctypes.POINTER(DecodeDims)]),
         "xattn_decode": (i32, [ctypes.POINTER(DecodeDims), vp, vp, vp, vp, vp, vp, vp,
                                ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]),
+        "xattn_decode_varlen": (i32, [ctypes.POINTER(DecodeDims), vp, vp, vp, vp, vp, vp, vp,
+                                      vp, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]),
         "xattn_profile_start": (i32, []),
         "xattn_profile_stop": (i32, [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]),
         "xattn_status_string": (ctypes.c_char_p, [i32]),
@@ -428,24 +430,43 @@ def xattn_decode_workspace_bytes(dims: DecodeDims) -> int:
     return int(load_library().xattn_decode_workspace_bytes(ctypes.byref(dims)))
 
 
-def xattn_decode(dims: DecodeDims, xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, eps,
-                 k_cache, v_cache, out, lse, workspace, stream=None):
-    d = dims
+def _decode_ptrs(d, xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, k_cache, v_cache, out, lse,
+                 workspace, cache_lens=None):
     hd = d.head_dim
     nq = d.batch * d.num_heads * d.q_len * hd
     nk = d.batch * d.num_kv_heads * d.q_len * hd
     nc = d.batch * d.num_kv_heads * d.capacity * hd
     nt = d.capacity * (hd // 2)
     _io(xq, "xq")
-    p = _ptrs((xq, "xq", None, nq), (xk, "xk", xq.dtype, nk), (v, "v", xq.dtype, nk),
-              (gamma_q, "gamma_q", F32, hd), (gamma_k, "gamma_k", F32, hd),
-              (cos_tab, "cos_tab", F32, AtLeast(nt)), (sin_tab, "sin_tab", F32, AtLeast(nt)),
-              (k_cache, "k_cache", xq.dtype, nc), (v_cache, "v_cache", xq.dtype, nc),
-              (out, "out", xq.dtype, nq), (lse, "lse", F32, d.batch * d.num_heads * d.q_len),
-              (workspace, "workspace", None, None))
+    return _ptrs((xq, "xq", None, nq), (xk, "xk", xq.dtype, nk), (v, "v", xq.dtype, nk),
+                 (gamma_q, "gamma_q", F32, hd), (gamma_k, "gamma_k", F32, hd),
+                 (cos_tab, "cos_tab", F32, AtLeast(nt)), (sin_tab, "sin_tab", F32, AtLeast(nt)),
+                 (k_cache, "k_cache", xq.dtype, nc), (v_cache, "v_cache", xq.dtype, nc),
+                 (out, "out", xq.dtype, nq), (lse, "lse", F32, d.batch * d.num_heads * d.q_len),
+                 (workspace, "workspace", None, None),
+                 (cache_lens, "cache_lens", I32, d.batch))
+
+
+def xattn_decode(dims: DecodeDims, xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, eps,
+                 k_cache, v_cache, out, lse, workspace, stream=None):
+    p = _decode_ptrs(dims, xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, k_cache, v_cache, out,
+                     lse, workspace)
     _check(load_library().xattn_decode(
-        ctypes.byref(dims), *p[:7], float(eps), *p[7:], _bytes(workspace, "workspace"),
+        ctypes.byref(dims), *p[:7], float(eps), *p[7:12], _bytes(workspace, "workspace"),
         _stream(stream)), "xattn_decode")
+
+
+def xattn_decode_varlen(dims: DecodeDims, cache_lens, xq, xk, v, gamma_q, gamma_k, cos_tab,
+                        sin_tab, eps, k_cache, v_cache, out, lse, workspace, stream=None):
+    """cache_lens: int32 device tensor [batch], each sequence's cached rows (dims.cache_len
+    must be their maximum)."""
+    if cache_lens is None:
+        raise ValueError("cache_lens must be an int32 device tensor")
+    p = _decode_ptrs(dims, xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, k_cache, v_cache, out,
+                     lse, workspace, cache_lens)
+    _check(load_library().xattn_decode_varlen(
+        ctypes.byref(dims), p[12], *p[:7], float(eps), *p[7:12],
+        _bytes(workspace, "workspace"), _stream(stream)), "xattn_decode_varlen")
 
 
 # ----------------------------------------------------------------------------------------
@@ -557,14 +578,21 @@ def attn_bwd(q, k, v, out, lse, dout, num_heads, num_kv_heads, prologue=None, st
 def decode(xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, eps, k_cache, v_cache, cache_len,
            num_heads, num_kv_heads, stream=None, workspace=None):
     """One KV-cache decode step: appends the new tokens' rotated keys and values to the
-    caches (rows cache_len ..) and returns (out, lse) of the new queries."""
-    dims = make_decode_dims(xq, k_cache, num_heads, num_kv_heads, cache_len)
+    caches (rows cache_len ..) and returns (out, lse) of the new queries.  cache_len: an int
+    (every sequence), or an int32 device tensor [batch] of per-sequence lengths."""
+    per_seq = isinstance(cache_len, torch.Tensor)
+    dims = make_decode_dims(xq, k_cache, num_heads, num_kv_heads,
+                            int(cache_len.max().item()) if per_seq else cache_len)
     out = torch.empty_like(xq)
     lse = torch.empty(xq.shape[0] * xq.shape[1], dtype=torch.float32, device=xq.device)
     if workspace is None:
         workspace = _workspace(xattn_decode_workspace_bytes(dims), xq.device)
-    xattn_decode(dims, xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, eps, k_cache, v_cache, out,
-                 lse, workspace, stream)
+    if per_seq:
+        xattn_decode_varlen(dims, cache_len, xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, eps,
+                            k_cache, v_cache, out, lse, workspace, stream)
+    else:
+        xattn_decode(dims, xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, eps, k_cache, v_cache,
+                     out, lse, workspace, stream)
     return out, lse
 
 

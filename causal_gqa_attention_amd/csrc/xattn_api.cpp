@@ -291,10 +291,6 @@ DecodeChecked check_decode_dims(const xattn_decode_dims* d, float eps) {
   c.io = check_dtype(d->dtype);
   if (!(eps >= 0.f) || !std::isfinite(eps))
     fail(XATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
-  const int64_t rows = (int64_t)(d->num_heads / d->num_kv_heads) * d->q_len;
-  if (rows > xattn::decode_rows_limit(c.io))
-    fail(XATTN_ERR_UNSUPPORTED, "(num_heads / num_kv_heads) * q_len = %lld exceeds %d",
-         (long long)rows, xattn::decode_rows_limit(c.io));
   c.q_elems = count4(d->batch, d->num_heads, d->q_len, d->head_dim, "xq");
   c.kv_new_elems = count4(d->batch, d->num_kv_heads, d->q_len, d->head_dim, "xk");
   c.cache_elems = count4(d->batch, d->num_kv_heads, d->capacity, d->head_dim, "k_cache");
@@ -323,6 +319,48 @@ DecodeWorkspace decode_workspace(const DecodeChecked& c) {
 }  // namespace
 
 void xattn::set_last_error(const char* msg) { g_last_error = msg; }
+
+namespace {
+
+xattn_status decode_impl(const xattn_decode_dims* dims, const int32_t* cache_lens,
+                         const void* xq, const void* xk, const void* v, const float* gamma_q,
+                         const float* gamma_k, const float* cos_tab, const float* sin_tab,
+                         float eps, void* k_cache, void* v_cache, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return guarded([&] {
+    const DecodeChecked c = check_decode_dims(dims, eps);
+    for (auto [p, name] : {std::pair<const void*, const char*>{xq, "xq"}, {xk, "xk"}, {v, "v"},
+                           {gamma_q, "gamma_q"}, {gamma_k, "gamma_k"}, {cos_tab, "cos_tab"},
+                           {sin_tab, "sin_tab"}, {k_cache, "k_cache"}, {v_cache, "v_cache"},
+                           {out, "out"}, {lse, "lse"}, {workspace, "workspace"}})
+      check_ptr(p, name);
+    if (cache_lens != nullptr) check_ptr(cache_lens, "cache_lens");
+    const DecodeWorkspace w = decode_workspace(c);
+    if (workspace_bytes < w.total)
+      fail(XATTN_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, w.total);
+    const size_t es = io_size(c.io);
+    const size_t qb = (size_t)c.q_elems * es, nb = (size_t)c.kv_new_elems * es;
+    const size_t cb = (size_t)c.cache_elems * es, hdb = (size_t)c.d.head_dim * 4;
+    const size_t tb = (size_t)c.d.capacity * (c.d.head_dim / 2) * 4;
+    check_no_overlap({{k_cache, cb, "k_cache"}, {v_cache, cb, "v_cache"}, {out, qb, "out"},
+                      {lse, (size_t)c.rows_q * 4, "lse"}, {workspace, w.total, "workspace"}},
+                     {{xq, qb, "xq"}, {xk, nb, "xk"}, {v, nb, "v"}, {gamma_q, hdb, "gamma_q"},
+                      {gamma_k, hdb, "gamma_k"}, {cos_tab, tb, "cos_tab"},
+                      {sin_tab, tb, "sin_tab"},
+                      {cache_lens, cache_lens ? (size_t)c.d.batch * 4 : 0, "cache_lens"}});
+    char* ws = static_cast<char*>(workspace);
+    xattn::DecodeBufs b;
+    b.xq = xq, b.xk = xk, b.v = v, b.gamma_q = gamma_q, b.gamma_k = gamma_k;
+    b.cos_tab = cos_tab, b.sin_tab = sin_tab, b.k_cache = k_cache, b.v_cache = v_cache;
+    b.out = out, b.lse = lse;
+    b.part_o = reinterpret_cast<float*>(ws + w.part_o);
+    b.part_ml = reinterpret_cast<float*>(ws + w.part_ml);
+    b.cache_lens = cache_lens;
+    hip_check(xattn::launch_decode(c.io, c.d, b, (hipStream_t)stream), "decode launch");
+  });
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -790,34 +828,22 @@ xattn_status xattn_decode(const xattn_decode_dims* dims, const void* xq, const v
                           const float* cos_tab, const float* sin_tab, float eps, void* k_cache,
                           void* v_cache, void* out, float* lse, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  return guarded([&] {
-    const DecodeChecked c = check_decode_dims(dims, eps);
-    for (auto [p, name] : {std::pair<const void*, const char*>{xq, "xq"}, {xk, "xk"}, {v, "v"},
-                           {gamma_q, "gamma_q"}, {gamma_k, "gamma_k"}, {cos_tab, "cos_tab"},
-                           {sin_tab, "sin_tab"}, {k_cache, "k_cache"}, {v_cache, "v_cache"},
-                           {out, "out"}, {lse, "lse"}, {workspace, "workspace"}})
-      check_ptr(p, name);
-    const DecodeWorkspace w = decode_workspace(c);
-    if (workspace_bytes < w.total)
-      fail(XATTN_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, w.total);
-    const size_t es = io_size(c.io);
-    const size_t qb = (size_t)c.q_elems * es, nb = (size_t)c.kv_new_elems * es;
-    const size_t cb = (size_t)c.cache_elems * es, hdb = (size_t)c.d.head_dim * 4;
-    const size_t tb = (size_t)c.d.capacity * (c.d.head_dim / 2) * 4;
-    check_no_overlap({{k_cache, cb, "k_cache"}, {v_cache, cb, "v_cache"}, {out, qb, "out"},
-                      {lse, (size_t)c.rows_q * 4, "lse"}, {workspace, w.total, "workspace"}},
-                     {{xq, qb, "xq"}, {xk, nb, "xk"}, {v, nb, "v"}, {gamma_q, hdb, "gamma_q"},
-                      {gamma_k, hdb, "gamma_k"}, {cos_tab, tb, "cos_tab"},
-                      {sin_tab, tb, "sin_tab"}});
-    char* ws = static_cast<char*>(workspace);
-    xattn::DecodeBufs b;
-    b.xq = xq, b.xk = xk, b.v = v, b.gamma_q = gamma_q, b.gamma_k = gamma_k;
-    b.cos_tab = cos_tab, b.sin_tab = sin_tab, b.k_cache = k_cache, b.v_cache = v_cache;
-    b.out = out, b.lse = lse;
-    b.part_o = reinterpret_cast<float*>(ws + w.part_o);
-    b.part_ml = reinterpret_cast<float*>(ws + w.part_ml);
-    hip_check(xattn::launch_decode(c.io, c.d, b, (hipStream_t)stream), "decode launch");
-  });
+  return decode_impl(dims, nullptr, xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, eps, k_cache,
+                     v_cache, out, lse, workspace, workspace_bytes, stream);
+}
+
+xattn_status xattn_decode_varlen(const xattn_decode_dims* dims, const int32_t* cache_lens,
+                                 const void* xq, const void* xk, const void* v,
+                                 const float* gamma_q, const float* gamma_k,
+                                 const float* cos_tab, const float* sin_tab, float eps,
+                                 void* k_cache, void* v_cache, void* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (cache_lens == nullptr) {
+    xattn::set_last_error("cache_lens is NULL");
+    return XATTN_ERR_INVALID_ARG;
+  }
+  return decode_impl(dims, cache_lens, xq, xk, v, gamma_q, gamma_k, cos_tab, sin_tab, eps,
+                     k_cache, v_cache, out, lse, workspace, workspace_bytes, stream);
 }
 
 size_t xattn_bwd_workspace_bytes(const xattn_dims* dims, int with_prologue) {

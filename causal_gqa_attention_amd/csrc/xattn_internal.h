@@ -129,12 +129,11 @@ struct DecodeBufs {
   float* lse;
   float* part_o;   // workspace: [B*Hkv][splits][group*Sq][hd]
   float* part_ml;  // workspace: [B*Hkv][splits][group*Sq][2]
+  const int* cache_lens = nullptr;  // [B] cached rows per sequence (null: cache_len for all)
 };
 struct DecodePlan {
   int nsplit, ks;  // key ranges per KV head and keys per range
 };
-// Largest group * q_len the split kernel holds in registers for this io dtype.
-int decode_rows_limit(IoType io);
 int decode_max_splits(int batch, int num_kv_heads, int cache_rows);
 DecodePlan decode_plan(const DecodeShape& d, int cache_rows);
 hipError_t launch_decode(IoType io, const DecodeShape& d, const DecodeBufs& bufs,

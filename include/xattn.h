@@ -321,14 +321,29 @@ size_t xattn_decode_workspace_bytes(const xattn_decode_dims* dims);
  * cos_tab, sin_tab: [capacity, hd/2] from xattn_rope_cache(capacity); k_cache, v_cache:
  * [B*Hkv, capacity, hd] io dtype, rows [0, cache_len) hold the previous tokens' rotated keys
  * and values (read), rows [cache_len, cache_len + q_len) are written, the rest untouched;
- * out: [B*H, q_len, hd]; lse: [B*H*q_len] fp32.  (H / Hkv) * q_len must not exceed 16 for
- * fp32 io, 8 for bf16 (XATTN_ERR_UNSUPPORTED otherwise).  The key ranges are summed in a
- * fixed order: bitwise reproducible run to run. */
+ * out: [B*H, q_len, hd]; lse: [B*H*q_len] fp32.  Any (H / Hkv) * q_len: the query rows of
+ * a KV head are handled in chunks (8 rows for bf16 io, 16 for fp32) that each stream the
+ * cache.  The key ranges are summed in a fixed order: bitwise reproducible run to run. */
 xattn_status xattn_decode(const xattn_decode_dims* dims, const void* xq, const void* xk,
                           const void* v, const float* gamma_q, const float* gamma_k,
                           const float* cos_tab, const float* sin_tab, float eps, void* k_cache,
                           void* v_cache, void* out, float* lse, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* KV-cache decode with one cache length per sequence ([MINT] 10.3 for each sequence): as
+ * xattn_decode, except that sequence b has cache_lens[b] tokens cached (device int32
+ * [batch]) and its new tokens sit at positions cache_lens[b] + i (RoPE angle, cache rows
+ * written, causal limit).  dims->cache_len must be the largest cache_lens[b] (it sizes the
+ * key ranges, and the workspace query does not depend on it).  Each cache_lens[b] is clamped
+ * into [0, capacity - q_len] on the device: a length outside it, or above dims->cache_len,
+ * gives wrong results but no access outside the tensors.  cache_lens is read-only and must
+ * not overlap the outputs. */
+xattn_status xattn_decode_varlen(const xattn_decode_dims* dims, const int32_t* cache_lens,
+                                 const void* xq, const void* xk, const void* v,
+                                 const float* gamma_q, const float* gamma_k,
+                                 const float* cos_tab, const float* sin_tab, float eps,
+                                 void* k_cache, void* v_cache, void* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- Instrumentation (no effect on results) ---------------------------------------------
  * Per-kernel timing with HIP events: between xattn_profile_start and xattn_profile_stop,

@@ -125,8 +125,13 @@ int main() {
   // decode
   xattn_decode_dims dec{2, 8, 2, 64, XATTN_BF16, 3, 10, 64};
   expect_status(xattn_decode(&dec, at(0), at(1), at(2), fat(3), fat(4), fat(5), fat(6), 1e-5f,
-                             at(7), at(8), at(9), fat(10), at(11), 1 << 20, nullptr),
-                XATTN_ERR_UNSUPPORTED, "decode rows beyond the limit", "exceeds");
+                             at(7), at(8), at(9), fat(10), at(11), 16, nullptr),
+                XATTN_ERR_INVALID_ARG, "decode rows in chunks, small workspace",
+                "workspace too small");
+  expect_status(xattn_decode_varlen(&dec, nullptr, at(0), at(1), at(2), fat(3), fat(4), fat(5),
+                                    fat(6), 1e-5f, at(7), at(8), at(9), fat(10), at(11),
+                                    1 << 20, nullptr),
+                XATTN_ERR_INVALID_ARG, "decode_varlen NULL lengths", "cache_lens is NULL");
   dec.q_len = 1;
   const size_t dw = xattn_decode_workspace_bytes(&dec);
   expect(dw > 0, "decode workspace");

@@ -33,7 +33,7 @@ def lib():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     for n in names:
         assert hasattr(lib, n), n
     assert "gfx950" in X.xattn_version()
@@ -151,9 +151,6 @@ def test_decode_validation(lib):
     assert "cache_len" in last(lib)
     assert decode_call(lib, ddims(q_len=0), ws_bytes=1 << 20) == INVALID and "q_len" in last(lib)
     assert decode_call(lib, ddims(H=6, Hkv=4), ws_bytes=1 << 20) == INVALID
-    # bf16: group * q_len = 4 * 3 = 12 > 8 rows held per KV head
-    assert decode_call(lib, ddims(q_len=3), ws_bytes=1 << 20) == UNSUPPORTED
-    assert "exceeds 8" in last(lib)
     assert decode_call(lib, ddims(hd=48), ws_bytes=1 << 20) == UNSUPPORTED
     assert decode_call(lib, ddims(), eps=-1.0) == INVALID and "eps" in last(lib)
     assert decode_call(lib, ddims(), xq=None) == INVALID and "xq is NULL" in last(lib)
@@ -165,13 +162,30 @@ def test_decode_validation(lib):
     assert decode_call(lib, d, v_cache=A + 7 * MB + 256) == INVALID and "overlap" in last(lib)
 
 
-def test_decode_fp32_allows_sixteen_rows(lib):
-    # fp32: group * q_len up to 16 passes the row check and fails only on the fake pointers'
-    # workspace size (given too small on purpose), before any launch
-    d = ddims(dt=0, q_len=4)
+@pytest.mark.parametrize("dt,q_len", [(1, 3), (1, 16), (0, 5), (0, 48)])
+def test_decode_any_rows_per_kv_head(lib, dt, q_len):
+    # group * q_len beyond one wave's rows (8 bf16, 16 fp32) passes the shape checks and
+    # fails only on the workspace size (given too small on purpose), before any launch
+    d = ddims(dt=dt, q_len=q_len)
     assert decode_call(lib, d, ws_bytes=16) == INVALID and "workspace too small" in last(lib)
-    d = ddims(dt=0, q_len=5)
-    assert decode_call(lib, d, ws_bytes=16) == UNSUPPORTED and "exceeds 16" in last(lib)
+
+
+def test_decode_varlen_validation(lib):
+    def call(d, cache_lens, **kw):
+        names = ["xq", "xk", "v", "gamma_q", "gamma_k", "cos_tab", "sin_tab", "k_cache",
+                 "v_cache", "out", "lse", "workspace"]
+        p = {n: A + i * MB for i, n in enumerate(names)}
+        p.update(kw)
+        ws = lib.xattn_decode_workspace_bytes(ctypes.byref(d))
+        return lib.xattn_decode_varlen(
+            ctypes.byref(d), cache_lens, p["xq"], p["xk"], p["v"], p["gamma_q"], p["gamma_k"],
+            p["cos_tab"], p["sin_tab"], 1e-5, p["k_cache"], p["v_cache"], p["out"], p["lse"],
+            p["workspace"], ws, None)
+    assert call(ddims(), None) == INVALID and "cache_lens is NULL" in last(lib)
+    assert call(ddims(), A + 20 * MB + 4) == INVALID and "aligned" in last(lib)
+    assert call(ddims(), A + 20 * MB, lse=A + 20 * MB) == INVALID
+    assert "overlaps input cache_lens" in last(lib)
+    assert call(ddims(cache_len=64), A + 20 * MB) == INVALID and "exceeds capacity" in last(lib)
 
 
 def test_document_arrays_validation(lib):
