@@ -537,10 +537,10 @@ DECODE_METRIC = "KV-cache decode step: cache bytes streamed per second (HBM GB/s
 
 def decode_ranges(bkv, rows):
     """Key ranges per KV head of the library's decode plan: ranges of at least 64 keys, at
-    most ceil(2048 / bkv) of them, equal length."""
-    cap_splits = 1 if bkv >= 2048 else -(-2048 // bkv)
+    most 1024 // bkv of them, each a whole number of 16-key tiles."""
+    cap_splits = 1 if bkv >= 1024 else 1024 // bkv
     n = max(1, min(-(-rows // 64), cap_splits))
-    ks = -(-rows // n)
+    ks = -(-(-(-rows // n)) // 16) * 16
     return -(-rows // ks)
 
 
