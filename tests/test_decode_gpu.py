@@ -132,12 +132,11 @@ def test_full_size_decode_last_tokens(w, q_len):
 QWEN_HEADS = dict(num_heads=32, num_kv_heads=8, head_dim=128, theta=1e6, eps=1e-6)
 
 
-def _varlen_inputs(prefill, steps, q_len, index):
+def _varlen_inputs(prefill, steps, q_len, index, dtype="bf16", heads=QWEN_HEADS):
     B = len(prefill)
     S = max(prefill) + steps * q_len
-    w = R("bf16", QWEN_HEADS["head_dim"], S, B, QWEN_HEADS["num_heads"],
-          QWEN_HEADS["num_kv_heads"], theta=QWEN_HEADS["theta"], eps=QWEN_HEADS["eps"],
-          index=index)
+    w = R(dtype, heads["head_dim"], S, B, heads["num_heads"], heads["num_kv_heads"],
+          theta=heads["theta"], eps=heads["eps"], index=index)
     return w, W.make_inputs(w)
 
 
@@ -197,6 +196,38 @@ def test_varlen_decode_matches_full_sequences():
     again = _varlen_stepwise(w, x, prefill, steps, q_len, cap)
     for u, v in zip((out, lse, kc, vc), again):
         np.testing.assert_array_equal(u, v)  # bitwise reproducible
+
+
+# The other split kernels with per-sequence lengths: fp32 (VALU), bf16 hd 64 (matrix cores),
+# bf16 hd 16 / 32 (dot2), with row chunks where group * q_len passes one wave's rows.
+VARLEN_KERNELS = [
+    ("f32", dict(num_heads=8, num_kv_heads=2, head_dim=64, theta=1e4, eps=1e-5), [0, 9, 30], 3, 2),
+    ("bf16", dict(num_heads=12, num_kv_heads=4, head_dim=64, theta=1e4, eps=1e-6), [5, 0, 41], 4, 3),
+    ("bf16", dict(num_heads=16, num_kv_heads=2, head_dim=32, theta=1e6, eps=1e-6), [17, 3], 3, 4),
+    ("f32", dict(num_heads=4, num_kv_heads=2, head_dim=16, theta=1e4, eps=1e-5), [0, 7, 2, 19], 5, 3),
+]
+
+
+@pytest.mark.parametrize("dt,heads,prefill,steps,q_len", VARLEN_KERNELS,
+                         ids=[f"{v[0]}_hd{v[1]['head_dim']}_g{v[1]['num_heads'] // v[1]['num_kv_heads']}"
+                              f"_q{v[4]}" for v in VARLEN_KERNELS])
+def test_varlen_decode_other_kernels_match_full_sequences(dt, heads, prefill, steps, q_len):
+    w, x = _varlen_inputs(prefill, steps, q_len, 430 + len(prefill), dt, heads)
+    cap = w.seq_len + 3
+    note(f"varlen decode {dt} {heads} prefill={prefill} steps={steps} q_len={q_len}")
+    out, lse, kc, vc = _varlen_stepwise(w, x, prefill, steps, q_len, cap)
+    f = oracle.forward(x.xq, x.xk, x.v, x.gamma_q, x.gamma_k, w.num_heads, w.num_kv_heads,
+                       w.eps, w.theta)
+    n = steps * q_len
+    H, Hkv = w.num_heads, w.num_kv_heads
+    tol = TOL[dt]
+    assert_close("out", out, _gather_rows(f["out"], H, prefill, n), tol)
+    assert_close("lse", lse, _gather_rows(f["lse"][..., None], H, prefill, n)[..., 0], tol)
+    for b, p in enumerate(prefill):
+        rows, end = slice(b * Hkv, (b + 1) * Hkv), p + n
+        assert_close(f"k_cache{b}", kc[rows, :end], f["yk"][rows, :end], tol)
+        np.testing.assert_array_equal(vc[rows, :end], x.v[rows, :end].astype(np.float64))
+        assert not kc[rows, end:].any() and not vc[rows, end:].any()
 
 
 def test_full_size_varlen_decode_mixed_cache_lengths():
