@@ -135,7 +135,7 @@ def test_step_shared_dkdv_path_matches_oracle(w):
     _compare_step(w, g, f, b)
 
 
-@pytest.mark.parametrize("idx", [3, 4, 5])
+@pytest.mark.parametrize("idx", [3, 4, 5, 6])
 def test_full_size_step_every_head(idx):
     """The workload at full size, in the configuration the benchmark times: every output of
     the step (prologue, attention forward, dq / dk / dv with the fused prologue backward,
@@ -154,7 +154,7 @@ def test_full_size_step_every_head(idx):
     _compare_step(w, g, f, b)
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6])
 def test_prologue_matches_oracle_every_row(idx):
     """QK-norm + RoPE forward and backward on every row of the workload's Q and K, with
     the seeded dout (for Q) and v (for K) standing in for the upstream gradients."""

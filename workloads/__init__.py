@@ -74,6 +74,9 @@ WORKLOADS = {
     3: Workload(3, "dim768_mha_bf16", 32, 1024, 12, 12, 64, "bf16", "ones", 1e-5, 1e4),
     4: Workload(4, "dim768_gqa_g3_bf16", 32, 1024, 12, 4, 64, "bf16", "perturbed", 1e-6, 1e4),
     5: Workload(5, "qwen3_long_gqa_g4_bf16", 1, 4096, 32, 8, 128, "bf16", "perturbed", 1e-6, 1e6),
+    # The pages' own dim768 attention (24 heads of head_dim 32, sequence 256, per-rank batch
+    # 32; xtrain "Phase T12", dim768 results table): an extra measured shape.
+    6: Workload(6, "dim768_pages_hd32_bf16", 32, 256, 24, 24, 32, "bf16", "perturbed", 1e-5, 1e4),
 }
 
 
