@@ -322,8 +322,11 @@ size_t xattn_decode_workspace_bytes(const xattn_decode_dims* dims);
  * [B*Hkv, capacity, hd] io dtype, rows [0, cache_len) hold the previous tokens' rotated keys
  * and values (read), rows [cache_len, cache_len + q_len) are written, the rest untouched;
  * out: [B*H, q_len, hd]; lse: [B*H*q_len] fp32.  Any (H / Hkv) * q_len: the query rows of
- * a KV head are handled in chunks (8 rows for bf16 io, 16 for fp32) that each stream the
- * cache.  The key ranges are summed in a fixed order: bitwise reproducible run to run. */
+ * a KV head are handled in chunks (16 rows for fp32 io and for bf16 with hd 64 / 128, 8 for
+ * bf16 with hd 16 / 32) that each stream the cache.  bf16 io rounds the rotated queries and
+ * the softmax probabilities to bf16 before the products (fp32 accumulation), as the training
+ * forward does.  The key ranges are summed in a fixed order: bitwise reproducible run to
+ * run. */
 xattn_status xattn_decode(const xattn_decode_dims* dims, const void* xq, const void* xk,
                           const void* v, const float* gamma_q, const float* gamma_k,
                           const float* cos_tab, const float* sin_tab, float eps, void* k_cache,
