@@ -348,6 +348,239 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 }
 
 // --------------------------------------------------------------------------------------
+// forward and dq for small grids (fewer 128-query workgroups than CUs): one workgroup per
+// (batch*head, 32-query tile); wave w walks the key stages w, w + 4, ... (32 keys each)
+// through its own LDS tiles, and the four waves' partial states are merged in wave order at
+// the end.  Each wave's chain of products is a quarter as long as in the kernels above, and
+// four times as many workgroups share the machine; the merge order depends on the shape
+// only, so results stay bitwise reproducible.
+// --------------------------------------------------------------------------------------
+constexpr int kSplitKeys = 32;  // keys per wave stage in the split kernels
+constexpr int kSplitM = 32;     // queries per split workgroup
+
+template <typename T, int HD>
+struct SplitLds {
+  using C = Tile<T, HD>;
+  static constexpr int TILE = kSplitKeys * C::LDS_ROW;  // elements per staged tile
+  static constexpr int STAGE_BYTES = kWaves * 2 * TILE * (int)sizeof(T);
+  static constexpr int PER = 16 * C::NDT + 2;           // merged floats per lane
+  static constexpr int MERGE_BYTES = (kWaves - 1) * 64 * PER * (int)sizeof(float);
+  static constexpr int BYTES = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
+};
+
+// Copies the wave's 32-row K and V stages (the wave's own lanes only), then orders the
+// copies before the wave's reads of them.
+template <typename T, int HD>
+__device__ __forceinline__ void split_stage(T* ks, T* vs, const T* kp, const T* vp, int kb,
+                                            int S, int lane) {
+  stage_rows<T, HD>(ks, kp, kb, kSplitKeys, S, lane, 64);
+  stage_rows<T, HD>(vs, vp, kb, kSplitKeys, S, lane, 64);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_fwd_split_kernel(const T* __restrict__ q,
+                                                             const T* __restrict__ k,
+                                                             const T* __restrict__ v,
+                                                             T* __restrict__ out,
+                                                             float* __restrict__ lse, int S,
+                                                             int H, int Hkv, float scale_log2,
+                                                             const int* __restrict__ seg_lo) {
+  using C = Tile<T, HD>;
+  using L = SplitLds<T, HD>;
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.x;
+  const int qt = gridDim.y - 1 - blockIdx.y;  // heaviest query tiles first
+  const int b = bh / H, qh = bh - b * H;
+  const int kvbh = b * Hkv + qh / (H / Hkv);
+  const T* kp = k + (size_t)kvbh * S * HD;
+  const T* vp = v + (size_t)kvbh * S * HD;
+  const int q0 = qt * kSplitM, qrow = q0 + c32;
+  T* ks = reinterpret_cast<T*>(lds) + (2 * w) * L::TILE;
+  T* vs = ks + L::TILE;
+
+  vec16_t<T> qf[C::NCH];
+  load_fragment<T, HD>(qf, q + (size_t)bh * S * HD, qrow, S, h);
+  f32x16 o[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) o[dt] = zero16();
+  float m_run = -INFINITY, l_run = 0.f;
+  const bool docs = seg_lo != nullptr;
+  const int lo_row = doc_lo(seg_lo, qrow, S), lo_wave = doc_lo(seg_lo, q0, S);
+  const int ntiles = (min(S, q0 + kSplitM) + kSplitKeys - 1) / kSplitKeys;
+  for (int kt = lo_wave / kSplitKeys + w; kt < ntiles; kt += kWaves) {
+    const int kb = kt * kSplitKeys;  // <= q0 + 31 and < S: every stage has visible keys
+    split_stage<T, HD>(ks, vs, kp, vp, kb, S, lane);
+    f32x16 st = contract_hd<T, HD>(ks, 0, qf, lane);
+    const bool edge = (kb + 31 > q0) || (kb + 31 >= S) || docs;
+    float sv[16];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float x = st[i] * scale_log2;
+      if (edge) {
+        const int key = kb + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (key > qrow || key >= S || key < lo_row) x = -INFINITY;
+      }
+      sv[i] = x;
+      tmax = fmaxf(tmax, x);
+    }
+    tmax = fmaxf(tmax, xor_lanes<32>(tmax));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // no visible key yet: stays empty
+    const float alpha = fast_exp2(m_run - m_ref);
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sv[i] = fast_exp2(sv[i] - m_ref);
+      psum += sv[i];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) o[dt] *= alpha;
+    accumulate_transposed<T, HD>(o, vs, 0, sv, lane);
+    __builtin_amdgcn_wave_barrier();  // the tiles' reads stay before the next stage's copy
+  }
+
+  // merge: waves 1..3 hand their (max, per-half sum, output) to wave 0 through LDS
+  __syncthreads();
+  float* mg = reinterpret_cast<float*>(lds);
+  if (w > 0) {
+    float* dst = mg + ((w - 1) * 64 + lane) * L::PER;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[16 * dt + i] = o[dt][i];
+    dst[16 * C::NDT] = m_run;
+    dst[16 * C::NDT + 1] = l_run;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  float M = m_run;
+#pragma unroll
+  for (int u = 1; u < kWaves; ++u) M = fmaxf(M, mg[((u - 1) * 64 + lane) * L::PER + 16 * C::NDT]);
+  const float ref = M == -INFINITY ? 0.f : M;
+  const float f0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - ref);
+  float l = l_run * f0;
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) o[dt] *= f0;
+#pragma unroll
+  for (int u = 1; u < kWaves; ++u) {  // wave order
+    const float* src = mg + ((u - 1) * 64 + lane) * L::PER;
+    const float mu = src[16 * C::NDT];
+    const float f = mu == -INFINITY ? 0.f : fast_exp2(mu - ref);
+    l += src[16 * C::NDT + 1] * f;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] += src[16 * dt + i] * f;
+  }
+  l += xor_lanes<32>(l);
+  if (qrow < S) {
+    store_column<T, HD, C::NDT>(out + ((size_t)bh * S + qrow) * HD, o, 1.0f / l, h);
+    if (h == 0) lse[(size_t)bh * S + qrow] = (M + log2f(l)) * kLn2;
+  }
+}
+
+template <typename T, int HD, typename TG>
+__global__ __launch_bounds__(256) void attn_bwd_dq_split_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ out, const T* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ delta, TG* __restrict__ dq, int S, int H, int Hkv, float scale_log2,
+    float scale, const int* __restrict__ seg_lo) {
+  using C = Tile<T, HD>;
+  using L = SplitLds<T, HD>;
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.x;
+  const int qt = gridDim.y - 1 - blockIdx.y;
+  const int b = bh / H, qh = bh - b * H;
+  const int kvbh = b * Hkv + qh / (H / Hkv);
+  const T* kp = k + (size_t)kvbh * S * HD;
+  const T* vp = v + (size_t)kvbh * S * HD;
+  const int q0 = qt * kSplitM, qrow = q0 + c32;
+  const size_t head_off = (size_t)bh * S * HD;
+  T* ks = reinterpret_cast<T*>(lds) + (2 * w) * L::TILE;
+  T* vs = ks + L::TILE;
+
+  vec16_t<T> qf[C::NCH], df[C::NCH];
+  load_fragment<T, HD>(qf, q + head_off, qrow, S, h);
+  load_fragment<T, HD>(df, dout + head_off, qrow, S, h);
+  float dsum = 0.f;
+  {
+    vec16_t<T> of[C::NCH];
+    load_fragment<T, HD>(of, out + head_off, qrow, S, h);
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c)
+#pragma unroll
+      for (int j = 0; j < C::VEC; ++j) dsum += to_f32(df[c][j]) * to_f32(of[c][j]);
+  }
+  const float D = dsum + xor_lanes<32>(dsum);
+  const float lse2 = qrow < S ? lse[(size_t)bh * S + qrow] * kLog2e : 0.f;
+  if (w == 0 && qrow < S && h == 0) delta[(size_t)bh * S + qrow] = D;
+
+  f32x16 acc[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) acc[dt] = zero16();
+  const bool docs = seg_lo != nullptr;
+  const int lo_row = doc_lo(seg_lo, qrow, S), lo_wave = doc_lo(seg_lo, q0, S);
+  const int ntiles = (min(S, q0 + kSplitM) + kSplitKeys - 1) / kSplitKeys;
+  for (int kt = lo_wave / kSplitKeys + w; kt < ntiles; kt += kWaves) {
+    const int kb = kt * kSplitKeys;
+    split_stage<T, HD>(ks, vs, kp, vp, kb, S, lane);
+    const f32x16 st = contract_hd<T, HD>(ks, 0, qf, lane);   // S^T: keys x queries
+    const f32x16 dpt = contract_hd<T, HD>(vs, 0, df, lane);  // dP^T
+    const bool edge = (kb + 31 > q0) || (kb + 31 >= S) || docs;
+    float dsv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float p = fast_exp2(st[i] * scale_log2 - lse2);
+      if (edge) {
+        const int key = kb + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (key > qrow || key >= S || key < lo_row) p = 0.f;
+      }
+      dsv[i] = p * (dpt[i] - D);
+    }
+    accumulate_transposed<T, HD>(acc, ks, 0, dsv, lane);  // dQ^T += K^T dS^T
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // merge: the waves' partial dQ added in wave order by wave 0
+  __syncthreads();
+  float* mg = reinterpret_cast<float*>(lds);
+  if (w > 0) {
+    float* dst = mg + ((w - 1) * 64 + lane) * L::PER;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[16 * dt + i] = acc[dt][i];
+  }
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll
+  for (int u = 1; u < kWaves; ++u) {
+    const float* src = mg + ((u - 1) * 64 + lane) * L::PER;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[dt][i] += src[16 * dt + i];
+  }
+  if (qrow < S) store_column<TG, HD, C::NDT>(dq + ((size_t)bh * S + qrow) * HD, acc, scale, h);
+}
+
+// The split kernels serve shapes whose 128-query workgroups would not cover the CUs.
+static inline bool use_split(const AttnShape& s) {
+  const long long wg = (long long)s.batch * s.num_heads * ((s.seq_len + kBlockM - 1) / kBlockM);
+  return wg < 256;
+}
+
+// --------------------------------------------------------------------------------------
 // backward, dk/dv: one workgroup owns 32*KW keys of one KV head; QS query splits
 // (QS * KW = 4 waves) walk interleaved 32-query tiles of every query head of the group,
 // r ascending; the split partials are added in split order at the end.  Every dk/dv
@@ -355,14 +588,17 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 // --------------------------------------------------------------------------------------
 constexpr int kBlockMQ = 32;  // queries per LDS stage in dk/dv
 
+// Waves of a dk/dv workgroup: four, or QS when the query walk is split eight ways.
+constexpr int dkdv_waves(int qs) { return qs > kWaves ? qs : kWaves; }
+
 template <typename T, int HD, typename TG, int QS>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * dkdv_waves(QS)) void attn_bwd_dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, TG* __restrict__ dk, T* __restrict__ dv, int S, int H,
     int Hkv, float scale_log2, float scale, const int* __restrict__ seg_hi) {
   using C = Tile<T, HD>;
-  constexpr int KW = kWaves / QS;
+  constexpr int KW = dkdv_waves(QS) / QS;
   constexpr int BNK = 32 * KW;
   constexpr int TILE = kBlockMQ * C::LDS_ROW;
   // Q tiles of the QS splits, then their dO tiles (one buffer so that the split
@@ -483,8 +719,15 @@ static inline float scale_of(int hd) { return 1.0f / sqrtf((float)hd); }
 template <typename T, int HD>
 static hipError_t fwd_impl(const AttnShape& s, const void* q, const void* k, const void* v,
                            void* out, float* lse, hipStream_t stream) {
-  const dim3 grid(s.batch * s.num_heads, (s.seq_len + kBlockM - 1) / kBlockM);
   ProfScope prof("attn_fwd", stream);
+  if (use_split(s)) {
+    const dim3 grid(s.batch * s.num_heads, (s.seq_len + kSplitM - 1) / kSplitM);
+    hipLaunchKernelGGL((attn_fwd_split_kernel<T, HD>), grid, dim3(256), 0, stream,
+                       (const T*)q, (const T*)k, (const T*)v, (T*)out, lse, s.seq_len,
+                       s.num_heads, s.num_kv_heads, scale_of(HD) * kLog2e, s.seg_lo);
+    return hipPeekAtLastError();
+  }
+  const dim3 grid(s.batch * s.num_heads, (s.seq_len + kBlockM - 1) / kBlockM);
   hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(256), 0, stream, (const T*)q,
                      (const T*)k, (const T*)v, (T*)out, lse, s.seq_len, s.num_heads,
                      s.num_kv_heads, scale_of(HD) * kLog2e, s.seg_lo);
@@ -507,8 +750,10 @@ hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const v
 }
 
 // Query splits for the dk/dv kernel: split the query walk only when there are too few
-// key tiles to fill the machine (256 CUs).  Depends on the shape only, so results stay
-// bitwise reproducible for a given shape.
+// key tiles to fill the machine (256 CUs); eight splits (eight waves of 32 keys each) when
+// four still leave it short and the staged tiles fit in LDS.  Depends on the shape only, so
+// results stay bitwise reproducible for a given shape.
+template <typename T, int HD>
 static int dkdv_splits(const AttnShape& s) {
   const long long bkv = (long long)s.batch * s.num_kv_heads;
   for (int qs = 1; qs <= 4; qs *= 2) {
@@ -516,17 +761,20 @@ static int dkdv_splits(const AttnShape& s) {
     const long long blocks = bkv * ((s.seq_len + bnk - 1) / bnk);
     if (blocks >= 1024) return qs;
   }
-  return 4;
+  constexpr size_t stage8 = 2 * 8 * (size_t)kBlockMQ * Tile<T, HD>::LDS_ROW * sizeof(T);
+  const long long blocks4 = bkv * ((s.seq_len + 31) / 32);
+  return (blocks4 < 256 && stage8 <= 144 * 1024) ? 8 : 4;
 }
 
 template <typename T, int HD, typename TG, int QS>
 static void launch_dkdv(const AttnShape& s, const void* q, const void* k, const void* v,
                         const void* dout, const float* lse, const float* delta, void* dk,
                         void* dv, hipStream_t stream) {
-  constexpr int BNK = 32 * (kWaves / QS);
+  constexpr int BNK = 32 * (dkdv_waves(QS) / QS);
   const dim3 grid(s.batch * s.num_kv_heads, (s.seq_len + BNK - 1) / BNK);
   ProfScope prof("attn_bwd_dkdv", stream);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD, TG, QS>), grid, dim3(256), 0, stream,
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD, TG, QS>), grid, dim3(64 * dkdv_waves(QS)), 0,
+                     stream,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta,
                      (TG*)dk, (T*)dv, s.seq_len, s.num_heads, s.num_kv_heads,
                      scale_of(HD) * kLog2e, scale_of(HD), s.seg_hi);
@@ -536,19 +784,33 @@ template <typename T, int HD, typename TG>
 static hipError_t bwd_impl(const AttnShape& s, const void* q, const void* k, const void* v,
                            const void* out, const float* lse, const void* dout, void* dq,
                            void* dk, void* dv, float* delta, hipStream_t stream) {
-  const dim3 grid(s.batch * s.num_heads, (s.seq_len + kBlockM - 1) / kBlockM);
   {
     ProfScope prof("attn_bwd_dq", stream);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD, TG>), grid, dim3(256), 0, stream,
-                       (const T*)q, (const T*)k, (const T*)v, (const T*)out, (const T*)dout,
-                       lse, delta, (TG*)dq, s.seq_len, s.num_heads, s.num_kv_heads,
-                       scale_of(HD) * kLog2e, scale_of(HD), s.seg_lo);
+    if (use_split(s)) {
+      const dim3 grid(s.batch * s.num_heads, (s.seq_len + kSplitM - 1) / kSplitM);
+      hipLaunchKernelGGL((attn_bwd_dq_split_kernel<T, HD, TG>), grid, dim3(256), 0, stream,
+                         (const T*)q, (const T*)k, (const T*)v, (const T*)out,
+                         (const T*)dout, lse, delta, (TG*)dq, s.seq_len, s.num_heads,
+                         s.num_kv_heads, scale_of(HD) * kLog2e, scale_of(HD), s.seg_lo);
+    } else {
+      const dim3 grid(s.batch * s.num_heads, (s.seq_len + kBlockM - 1) / kBlockM);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD, TG>), grid, dim3(256), 0, stream,
+                         (const T*)q, (const T*)k, (const T*)v, (const T*)out,
+                         (const T*)dout, lse, delta, (TG*)dq, s.seq_len, s.num_heads,
+                         s.num_kv_heads, scale_of(HD) * kLog2e, scale_of(HD), s.seg_lo);
+    }
   }
   hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess) return e;
-  switch (dkdv_splits(s)) {
+  switch (dkdv_splits<T, HD>(s)) {
     case 1: launch_dkdv<T, HD, TG, 1>(s, q, k, v, dout, lse, delta, dk, dv, stream); break;
     case 2: launch_dkdv<T, HD, TG, 2>(s, q, k, v, dout, lse, delta, dk, dv, stream); break;
+    case 8:
+      if constexpr (2 * 8 * (size_t)kBlockMQ * Tile<T, HD>::LDS_ROW * sizeof(T) <= 144 * 1024) {
+        launch_dkdv<T, HD, TG, 8>(s, q, k, v, dout, lse, delta, dk, dv, stream);
+        break;
+      }
+      [[fallthrough]];
     default: launch_dkdv<T, HD, TG, 4>(s, q, k, v, dout, lse, delta, dk, dv, stream); break;
   }
   return hipPeekAtLastError();

@@ -37,6 +37,10 @@ SMALL = [
     # 64-key block; group 8 with the sequence exactly one 64-key block
     R("bf16", 128, 161, 2, 2, 2, theta=1e6, eps=1e-6, index=214),
     R("bf16", 128, 64, 1, 16, 2, index=215),
+    # grids of >= 256 query workgroups: the generic forward / dq kernels without the key split
+    # (the shapes above with fp32 or head_dim 16 / 32 run the split kernels)
+    R("f32", 64, 300, 4, 24, 6, index=216),
+    R("bf16", 16, 260, 8, 16, 4, index=217),
 ]
 SMALL_IDS = [w.name if w.index < 100 else f"{w.dtype}_hd{w.head_dim}_S{w.seq_len}_"
              f"B{w.batch}_H{w.num_heads}_kv{w.num_kv_heads}" for w in SMALL]
