@@ -636,24 +636,59 @@ __global__ __launch_bounds__(64 * dkdv_waves(QS)) void attn_bwd_dkdv_kernel(
   const int nsteps = max(0, (nqt - qt_first + QS - 1) / QS);
   const bool wave_live = kw0 < S;
 
-  for (int r = 0; r < group; ++r) {
-    const int bh = b * H + kvh * group + r;
-    const T* qp = q + (size_t)bh * S * HD;
-    const T* dop = dout + (size_t)bh * S * HD;
-    for (int step = 0; step < nsteps; ++step) {
-      const int qt = qt_first + step * QS + sp;
-      const int q0 = qt * kBlockMQ;
-      __syncthreads();
-      if (qt < nqt) {
-        stage_rows<T, HD>(qtile, qp, q0, kBlockMQ, S, st_tid, 64 * KW);
-        stage_rows<T, HD>(dtile, dop, q0, kBlockMQ, S, st_tid, 64 * KW);
-        for (int i = st_tid; i < kBlockMQ; i += 64 * KW) {
-          const int qi = q0 + i;
-          lse_s[sp][i] = qi < S ? lse[(size_t)bh * S + qi] * kLog2e : INFINITY;
-          del_s[sp][i] = qi < S ? delta[(size_t)bh * S + qi] : 0.f;
-        }
+  // Step u = (query head r = u / nsteps, split step u % nsteps).  The next step's Q / dO rows
+  // and row statistics are loaded into registers while the current step computes, and stored
+  // into LDS between the step's two barriers.
+  constexpr int CH = kBlockMQ * C::CPR;                  // 16-byte chunks per tile
+  constexpr int NPT = (CH + 64 * KW - 1) / (64 * KW);    // per staging thread
+  vec16_t<T> pq[NPT], pd[NPT];
+  float plse = INFINITY, pdel = 0.f;  // staging threads st_tid < kBlockMQ: one row each
+  const int nall = group * nsteps;
+  auto fetch = [&](int u) {
+    const int r = u / nsteps, step = u - r * nsteps;
+    const size_t bh = (size_t)(b * H + kvh * group + r);
+    const int q0 = (qt_first + step * QS + sp) * kBlockMQ;
+    const bool real = qt_first + step * QS + sp < nqt;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      const int idx = st_tid + j * 64 * KW;
+      const int gr = q0 + idx / C::CPR, cc = (idx % C::CPR) * C::VEC;
+      pq[j] = vzero<T>();
+      pd[j] = vzero<T>();
+      if (real && idx < CH && gr < S && cc < HD) {
+        pq[j] = load16(q + (bh * S + gr) * HD + cc);
+        pd[j] = load16(dout + (bh * S + gr) * HD + cc);
       }
-      __syncthreads();
+    }
+    if (st_tid < kBlockMQ) {
+      const int qi = q0 + st_tid;
+      const bool in = real && qi < S;
+      plse = in ? lse[bh * S + qi] * kLog2e : INFINITY;
+      pdel = in ? delta[bh * S + qi] : 0.f;
+    }
+  };
+  if (nall > 0) fetch(0);
+  for (int u = 0; u < nall; ++u) {
+    const int step = u % nsteps;
+    const int qt = qt_first + step * QS + sp;
+    const int q0 = qt * kBlockMQ;
+    __syncthreads();  // every wave is done with the previous step's tiles
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      const int idx = st_tid + j * 64 * KW;
+      if (idx < CH) {
+        const int rr = idx / C::CPR, cc = (idx % C::CPR) * C::VEC;
+        store16(qtile + rr * C::LDS_ROW + cc, pq[j]);
+        store16(dtile + rr * C::LDS_ROW + cc, pd[j]);
+      }
+    }
+    if (st_tid < kBlockMQ) {
+      lse_s[sp][st_tid] = plse;
+      del_s[sp][st_tid] = pdel;
+    }
+    __syncthreads();
+    if (u + 1 < nall) fetch(u + 1);  // in flight under this step's products
+    {
       if (qt >= nqt || !wave_live || q0 + kBlockMQ - 1 < kw0) continue;
 
       const f32x16 st = contract_hd<T, HD>(qtile, 0, kf, lane);   // S: queries x keys
