@@ -122,20 +122,33 @@ __device__ __forceinline__ void load_fragment(vec16_t<T> (&frag)[NCH], const T* 
                       : vzero<T>();
 }
 
-// Copy rows r0..r0+nrows-1 of a [S, HD] matrix into a zero-padded LDS tile, using
-// `nthr` threads starting at thread index `t`.
-template <typename T, int HD>
-__device__ __forceinline__ void stage_rows(T* tile, const T* src, int r0, int nrows, int S,
-                                           int t, int nthr) {
+// Copy of rows r0..r0+ROWS-1 of a [S, HD] matrix into a zero-padded LDS tile, in two halves
+// so that the next tile's global reads can be in flight while the current tile is used:
+// load() brings the rows into the thread's registers (zero past the end and in the padding),
+// store() writes them to the tile.  NTHR threads, t the thread's index.
+template <typename T, int HD, int ROWS, int NTHR>
+struct RowPrefetch {
   using C = Tile<T, HD>;
-  for (int idx = t; idx < nrows * C::CPR; idx += nthr) {
-    const int r = idx / C::CPR, cc = (idx % C::CPR) * C::VEC;
-    const int gr = r0 + r;
-    vec16_t<T> x = vzero<T>();
-    if (gr < S && cc < HD) x = load16(src + (size_t)gr * HD + cc);
-    store16(tile + r * C::LDS_ROW + cc, x);
+  static constexpr int CH = ROWS * C::CPR;            // 16-byte chunks of the tile
+  static constexpr int N = (CH + NTHR - 1) / NTHR;    // per thread
+  vec16_t<T> x[N];
+  __device__ __forceinline__ void load(const T* src, int r0, int S, int t) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int idx = t + j * NTHR;
+      const int gr = r0 + idx / C::CPR, cc = (idx % C::CPR) * C::VEC;
+      x[j] = vzero<T>();
+      if (idx < CH && gr < S && cc < HD) x[j] = load16(src + (size_t)gr * HD + cc);
+    }
   }
-}
+  __device__ __forceinline__ void store(T* tile, int t) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int idx = t + j * NTHR;
+      if (idx < CH) store16(tile + (idx / C::CPR) * C::LDS_ROW + (idx % C::CPR) * C::VEC, x[j]);
+    }
+  }
+};
 
 // Store the lane's column of a 32-row-tiled [HD] accumulator (rows d = 32*dt + 8*g + 4*h
 // + 0..3) as row `row` of an [S, HD] output, times `mul`.
@@ -216,12 +229,23 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ q,
 
   const int kend = min(S, q0 + kBlockM);
   const int ntiles = (kend + kBlockN - 1) / kBlockN;
-  for (int kt = doc_lo(seg_lo, q0, S) / kBlockN; kt < ntiles; ++kt) {
+  // the next stage's K / V rows are loaded into registers under the current stage
+  RowPrefetch<T, HD, kBlockN, 256> pk, pv;
+  const int kt0 = doc_lo(seg_lo, q0, S) / kBlockN;
+  if (kt0 < ntiles) {
+    pk.load(kp, kt0 * kBlockN, S, tid);
+    pv.load(vp, kt0 * kBlockN, S, tid);
+  }
+  for (int kt = kt0; kt < ntiles; ++kt) {
     const int k0 = kt * kBlockN;
     __syncthreads();
-    stage_rows<T, HD>(ks, kp, k0, kBlockN, S, tid, 256);
-    stage_rows<T, HD>(vs, vp, k0, kBlockN, S, tid, 256);
+    pk.store(ks, tid);
+    pv.store(vs, tid);
     __syncthreads();
+    if (kt + 1 < ntiles) {
+      pk.load(kp, k0 + kBlockN, S, tid);
+      pv.load(vp, k0 + kBlockN, S, tid);
+    }
 #pragma unroll
     for (int s = 0; s < kBlockN / 32; ++s) {
       const int kb = k0 + 32 * s;
@@ -317,12 +341,23 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const int lo_row = doc_lo(seg_lo, qrow, S), lo_wave = doc_lo(seg_lo, qw0, S);
   const int kend = min(S, q0 + kBlockM);
   const int ntiles = (kend + kBlockN - 1) / kBlockN;
-  for (int kt = doc_lo(seg_lo, q0, S) / kBlockN; kt < ntiles; ++kt) {
+  // the next stage's K / V rows are loaded into registers under the current stage
+  RowPrefetch<T, HD, kBlockN, 256> pk, pv;
+  const int kt0 = doc_lo(seg_lo, q0, S) / kBlockN;
+  if (kt0 < ntiles) {
+    pk.load(kp, kt0 * kBlockN, S, tid);
+    pv.load(vp, kt0 * kBlockN, S, tid);
+  }
+  for (int kt = kt0; kt < ntiles; ++kt) {
     const int k0 = kt * kBlockN;
     __syncthreads();
-    stage_rows<T, HD>(ks, kp, k0, kBlockN, S, tid, 256);
-    stage_rows<T, HD>(vs, vp, k0, kBlockN, S, tid, 256);
+    pk.store(ks, tid);
+    pv.store(vs, tid);
     __syncthreads();
+    if (kt + 1 < ntiles) {
+      pk.load(kp, k0 + kBlockN, S, tid);
+      pv.load(vp, k0 + kBlockN, S, tid);
+    }
 #pragma unroll
     for (int s = 0; s < kBlockN / 32; ++s) {
       const int kb = k0 + 32 * s;
@@ -368,17 +403,24 @@ struct SplitLds {
   static constexpr int BYTES = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
 };
 
-// Copies the wave's 32-row K and V stages (the wave's own lanes only), then orders the
-// copies before the wave's reads of them.
+// A wave's own 32-row K and V stages: the stage's rows, loaded into registers one stage
+// ahead, are written to the wave's LDS tiles, and the writes ordered before the wave's reads;
+// then the wave's next stage is loaded (in flight under this stage's products).
 template <typename T, int HD>
-__device__ __forceinline__ void split_stage(T* ks, T* vs, const T* kp, const T* vp, int kb,
-                                            int S, int lane) {
-  stage_rows<T, HD>(ks, kp, kb, kSplitKeys, S, lane, 64);
-  stage_rows<T, HD>(vs, vp, kb, kSplitKeys, S, lane, 64);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+struct SplitStager {
+  RowPrefetch<T, HD, kSplitKeys, 64> pk, pv;
+  __device__ __forceinline__ void load(const T* kp, const T* vp, int kb, int S, int lane) {
+    pk.load(kp, kb, S, lane);
+    pv.load(vp, kb, S, lane);
+  }
+  __device__ __forceinline__ void commit(T* ks, T* vs, int lane) {
+    pk.store(ks, lane);
+    pv.store(vs, lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+};
 
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_fwd_split_kernel(const T* __restrict__ q,
@@ -412,9 +454,13 @@ __global__ __launch_bounds__(256) void attn_fwd_split_kernel(const T* __restrict
   const bool docs = seg_lo != nullptr;
   const int lo_row = doc_lo(seg_lo, qrow, S), lo_wave = doc_lo(seg_lo, q0, S);
   const int ntiles = (min(S, q0 + kSplitM) + kSplitKeys - 1) / kSplitKeys;
-  for (int kt = lo_wave / kSplitKeys + w; kt < ntiles; kt += kWaves) {
+  SplitStager<T, HD> stg;
+  const int kt0 = lo_wave / kSplitKeys + w;
+  if (kt0 < ntiles) stg.load(kp, vp, kt0 * kSplitKeys, S, lane);
+  for (int kt = kt0; kt < ntiles; kt += kWaves) {
     const int kb = kt * kSplitKeys;  // <= q0 + 31 and < S: every stage has visible keys
-    split_stage<T, HD>(ks, vs, kp, vp, kb, S, lane);
+    stg.commit(ks, vs, lane);
+    if (kt + kWaves < ntiles) stg.load(kp, vp, kb + kWaves * kSplitKeys, S, lane);
     f32x16 st = contract_hd<T, HD>(ks, 0, qf, lane);
     const bool edge = (kb + 31 > q0) || (kb + 31 >= S) || docs;
     float sv[16];
@@ -531,9 +577,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_split_kernel(
   const bool docs = seg_lo != nullptr;
   const int lo_row = doc_lo(seg_lo, qrow, S), lo_wave = doc_lo(seg_lo, q0, S);
   const int ntiles = (min(S, q0 + kSplitM) + kSplitKeys - 1) / kSplitKeys;
-  for (int kt = lo_wave / kSplitKeys + w; kt < ntiles; kt += kWaves) {
+  SplitStager<T, HD> stg;
+  const int kt0 = lo_wave / kSplitKeys + w;
+  if (kt0 < ntiles) stg.load(kp, vp, kt0 * kSplitKeys, S, lane);
+  for (int kt = kt0; kt < ntiles; kt += kWaves) {
     const int kb = kt * kSplitKeys;
-    split_stage<T, HD>(ks, vs, kp, vp, kb, S, lane);
+    stg.commit(ks, vs, lane);
+    if (kt + kWaves < ntiles) stg.load(kp, vp, kb + kWaves * kSplitKeys, S, lane);
     const f32x16 st = contract_hd<T, HD>(ks, 0, qf, lane);   // S^T: keys x queries
     const f32x16 dpt = contract_hd<T, HD>(vs, 0, df, lane);  // dP^T
     const bool edge = (kb + 31 > q0) || (kb + 31 >= S) || docs;
