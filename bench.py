@@ -305,6 +305,27 @@ def pmc_means(folder):
             for k, a in acc.items()}
 
 
+def min_traffic(w):
+    """Least HBM bytes of attention fwd + bwd, each tensor read or written once: the forward
+    reads q, k, v and writes out and lse (fp32); the backward reads q, k, v, out, dO, lse and
+    D and writes dq, dk, dv."""
+    esz = 2 if w.dtype == "bf16" else 4
+    q_el, kv_el = w.bh * w.seq_len * w.head_dim, w.bkv * w.seq_len * w.head_dim
+    rows = w.bh * w.seq_len
+    fwd = esz * (2 * q_el + 2 * kv_el) + 4 * rows
+    bwd = esz * (4 * q_el + 4 * kv_el) + 8 * rows
+    return fwd + bwd
+
+
+def attainable(flop, min_bytes, value, peak):
+    """Roofline bound of the step from its least HBM traffic: intensity = FLOP / bytes, the
+    bound min(peak, intensity x HBM peak) in TFLOP/s, and the measured rate's share of it."""
+    ai = flop / min_bytes
+    bound = min(peak, ai * PEAK_HBM_GBS / 1e3)
+    return {"min_bytes": min_bytes, "flop_per_byte": ai, "tflops": bound,
+            "pct": 100.0 * value / bound}
+
+
 def stats_summary(out_name, folder, bench_args):
     """profiles/<out_name>.md: the kernel statistics rocprofv3 wrote (calls, total, average,
     min and max duration per kernel) as a table, with the command that made them."""
@@ -719,6 +740,7 @@ def main():
     units_per_head = doc_pairs(w, docs) * w.bh
     flops = {"fwd": 4 * w.head_dim * units_per_head, "bwd": 8 * w.head_dim * units_per_head,
              "total": 12 * w.head_dim * units_per_head}
+    min_bytes = min_traffic(w)
 
     settled = settle(step.run, args.settle_ms) if args.settle_ms > 0 else None
     for _ in range(args.warmup):
@@ -816,6 +838,11 @@ def main():
                    **({"documents": docs} if docs else {})},
         "pct_of_peak": 100.0 * value / PEAK_TFLOPS[w.dtype],
         "attention_kernels_tflops": flops["total"] / (attn_ms * 1e-3) / 1e12 if attn_ms else None,
+        # the same step counted the FlashAttention way (backward = 2.5 x forward: 14 hd per
+        # pair), for comparison with figures quoted in that convention
+        "fa_convention_tflops": 14 * w.head_dim * units_per_head / (ms * 1e-3) / 1e12,
+        # attainable bound min(MFMA peak, intensity x HBM peak) over the least traffic
+        "attainable": attainable(flops["total"], min_bytes, value, PEAK_TFLOPS[w.dtype]),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,

@@ -112,3 +112,20 @@ def test_executed_work_counts_the_recomputation(bench):
     # the step's headline counts 12 * hd per causal pair: forward + dk/dv + dq algorithmic
     total = sum(alg[k][1] for k in ("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq"))
     assert total == 12 * w.head_dim * w.causal_pairs() * w.bh
+
+
+def test_attainable_bound_from_the_least_traffic(bench):
+    """The least-traffic bytes and the attainable bound of the dim768 MHA shape: 202.9 MB
+    forward + 405.8 MB backward, 254 FLOP per byte, min(2500, 254 x 8 TB/s) = 2.03 PFLOP/s
+    (below the bf16 ridge); the Qwen3 shape (84.4 + 168.8 MB) is bound by the MFMA peak."""
+    import workloads as W
+    w3, w5 = W.WORKLOADS[3], W.WORKLOADS[5]
+    assert bench.min_traffic(w3) == pytest.approx(608.7e6, rel=2e-4)
+    assert bench.min_traffic(w5) == pytest.approx(253.2e6, rel=2e-4)
+    flop3 = 12 * w3.head_dim * w3.causal_pairs() * w3.bh
+    a = bench.attainable(flop3, bench.min_traffic(w3), 500.0, 2500.0)
+    assert a["flop_per_byte"] == pytest.approx(254.26, rel=1e-3)
+    assert a["tflops"] == pytest.approx(2034.1, rel=1e-3)
+    assert a["pct"] == pytest.approx(100.0 * 500.0 / a["tflops"])
+    flop5 = 12 * w5.head_dim * w5.causal_pairs() * w5.bh
+    assert bench.attainable(flop5, bench.min_traffic(w5), 1.0, 2500.0)["tflops"] == 2500.0
