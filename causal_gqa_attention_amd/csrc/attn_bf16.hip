@@ -376,42 +376,63 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Prologue backward of tile rows r0 .. r0 + NROWS - 1, the gradient w.r.t. y at positions
-// t0 + r of the head whose rows start at head_row0; writes dx rows into dx_head + t * HD
-// and adds the lane's dgamma terms (its 16 columns) into dg.  Rows t >= S store and
-// contribute nothing.  Every load of the NROWS rows is issued before the arithmetic, so
-// the passes share one memory round trip.
+// Global inputs of the prologue backward of rows r0 .. r0 + NROWS - 1 (positions t0 + r of
+// the head whose rows start at head_row0): gamma, rstd, the raw rows x and their cos / sin
+// entries.  Nothing in the attention kernels writes these arrays, so the loads may be
+// issued before the epilogue's barriers and reductions and stay in flight across them.
 template <int HD, int NROWS>
-__device__ __forceinline__ void pro_rows(float* tile, int r0, bf16* __restrict__ dx_head,
-                                         const ProBwd& pb, size_t head_row0, int t0, int S,
-                                         int lane, float (&dg)[16]) {
-  constexpr int HALF = HD / 2, LPR = HD / 16, RPI = 64 / LPR, NIT = NROWS / RPI;
+struct ProRowsIn {
+  static constexpr int HALF = HD / 2, LPR = HD / 16, RPI = 64 / LPR, NIT = NROWS / RPI;
   static_assert(NROWS % RPI == 0, "whole row passes");
-  const int part = lane % LPR, slot = lane / LPR;
-  const int c1 = 8 * part;
   float g[16];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    g[e] = pb.gamma[c1 + e];
-    g[8 + e] = pb.gamma[HALF + c1 + e];
-  }
   float rr[NIT];
   bf16x8 x1[NIT], x2[NIT];
-  f32x4 cs[NIT][2], sn[NIT][2], d1[NIT][2], d2[NIT][2];
+  f32x4 cs[NIT][2], sn[NIT][2];
+
+  __device__ __forceinline__ void load(const ProBwd& pb, size_t head_row0, int r0, int t0,
+                                       int S, int lane) {
+    const int c1 = 8 * (lane % LPR), slot = lane / LPR;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      g[e] = pb.gamma[c1 + e];
+      g[8 + e] = pb.gamma[HALF + c1 + e];
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int t = t0 + r0 + it * RPI + slot;
+      const int tc = t < S ? t : S - 1;
+      const size_t row = head_row0 + tc;
+      rr[it] = pb.rstd[row];
+      x1[it] = *reinterpret_cast<const bf16x8*>(pb.x + row * HD + c1);
+      x2[it] = *reinterpret_cast<const bf16x8*>(pb.x + row * HD + HALF + c1);
+      const float* cr = pb.cos_tab + (size_t)tc * HALF + c1;
+      const float* sr = pb.sin_tab + (size_t)tc * HALF + c1;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        cs[it][u] = *reinterpret_cast<const f32x4*>(cr + 4 * u);
+        sn[it][u] = *reinterpret_cast<const f32x4*>(sr + 4 * u);
+      }
+    }
+  }
+};
+
+// Prologue backward of tile rows r0 .. r0 + NROWS - 1, the gradient w.r.t. y at positions
+// t0 + r, with the rows' global inputs already loaded (`in`, same r0 and t0); writes dx
+// rows into dx_head + t * HD and adds the lane's dgamma terms (its 16 columns) into dg.
+// Rows t >= S store and contribute nothing.
+template <int HD, int NROWS>
+__device__ __forceinline__ void pro_rows(const ProRowsIn<HD, NROWS>& in, float* tile, int r0,
+                                         bf16* __restrict__ dx_head, int t0, int S, int lane,
+                                         float (&dg)[16]) {
+  using In = ProRowsIn<HD, NROWS>;
+  constexpr int HALF = In::HALF, LPR = In::LPR, RPI = In::RPI, NIT = In::NIT;
+  const int c1 = 8 * (lane % LPR), slot = lane / LPR;
+  f32x4 d1[NIT][2], d2[NIT][2];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    const int r = r0 + it * RPI + slot, t = t0 + r;
-    const int tc = t < S ? t : S - 1;
-    const size_t row = head_row0 + tc;
-    rr[it] = pb.rstd[row];
-    x1[it] = *reinterpret_cast<const bf16x8*>(pb.x + row * HD + c1);
-    x2[it] = *reinterpret_cast<const bf16x8*>(pb.x + row * HD + HALF + c1);
-    const float* cr = pb.cos_tab + (size_t)tc * HALF + c1;
-    const float* sr = pb.sin_tab + (size_t)tc * HALF + c1;
+    const int r = r0 + it * RPI + slot;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      cs[it][u] = *reinterpret_cast<const f32x4*>(cr + 4 * u);
-      sn[it][u] = *reinterpret_cast<const f32x4*>(sr + 4 * u);
       d1[it][u] = *epi_chunk<HD>(tile, r, c1 / 4 + u);
       d2[it][u] = *epi_chunk<HD>(tile, r, (HALF + c1) / 4 + u);
     }
@@ -425,20 +446,20 @@ __device__ __forceinline__ void pro_rows(float* tile, int r0, bf16* __restrict__
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float a = d1[it][e / 4][e % 4], b = d2[it][e / 4][e % 4];
-      const float c = cs[it][e / 4][e % 4], sv = sn[it][e / 4][e % 4];
+      const float c = in.cs[it][e / 4][e % 4], sv = in.sn[it][e / 4][e % 4];
       n[e] = a * c + b * sv;  // rotation by the negative angle
       n[8 + e] = b * c - a * sv;
-      xf[e] = (float)x1[it][e];
-      xf[8 + e] = (float)x2[it][e];
-      dot += g[e] * n[e] * xf[e] + g[8 + e] * n[8 + e] * xf[8 + e];
+      xf[e] = (float)in.x1[it][e];
+      xf[8 + e] = (float)in.x2[it][e];
+      dot += in.g[e] * n[e] * xf[e] + in.g[8 + e] * n[8 + e] * xf[8 + e];
     }
     dot = group_sum<LPR>(dot);
-    const float r = rr[it];
+    const float r = in.rr[it];
     const float coef = dot * r * r * r * (1.0f / (float)HD);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      o1[it][e] = (bf16)(g[e] * n[e] * r - xf[e] * coef);
-      o2[it][e] = (bf16)(g[8 + e] * n[8 + e] * r - xf[8 + e] * coef);
+      o1[it][e] = (bf16)(in.g[e] * n[e] * r - xf[e] * coef);
+      o2[it][e] = (bf16)(in.g[8 + e] * n[8 + e] * r - xf[8 + e] * coef);
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) dg[e] += valid ? n[e] * xf[e] * r : 0.f;
@@ -943,11 +964,13 @@ __global__ __launch_bounds__(64 * kQW, HD == 64 ? 4 : 1) void dq_kernel(
   q_stage_loop(doc, seg_lo != nullptr, min(q0 / kBN, S / kBN), ntiles, S, stage);
   if constexpr (PRO) {
     static_assert(sizeof(lds) >= kQW * 32 * HD * sizeof(float), "epilogue tiles fit");
+    ProRowsIn<HD, 32> pin;  // in flight across the barrier and the tile write
+    pin.load(pro, (size_t)bh * S, 0, qw0, S, lane);
     lds_barrier();  // every wave is done with the staged tiles
     float* tile = reinterpret_cast<float*>(lds) + wv * 32 * HD;
     acc_to_tile<HD>(tile, acc, scale, lane);
     float dg[16] = {};
-    pro_rows<HD, 32>(tile, 0, dq + hoff, pro, (size_t)bh * S, qw0, S, lane, dg);
+    pro_rows<HD, 32>(pin, tile, 0, dq + hoff, qw0, S, lane, dg);
     asm volatile("" ::: "memory");
     pro_partial<HD, kQW>(dg, reinterpret_cast<float*>(lds), 32 * HD, pro, bh * nqt + mp.qt, wv,
                          lane, tid);
@@ -1181,8 +1204,9 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_shared_kernel(
     float dg[16] = {};
     if (kw0 < S) {
       acc_to_tile<HD>(tile, dkt, scale, lane);
-      pro_rows<HD, 32>(tile, 0, dk + (size_t)kvbh * S * HD, pro, (size_t)kvbh * S, kw0, S,
-                       lane, dg);
+      ProRowsIn<HD, 32> pin;
+      pin.load(pro, (size_t)kvbh * S, 0, kw0, S, lane);
+      pro_rows<HD, 32>(pin, tile, 0, dk + (size_t)kvbh * S * HD, kw0, S, lane, dg);
     }
     asm volatile("" ::: "memory");
     pro_partial<HD>(dg, reinterpret_cast<float*>(lds), 32 * HD, pro, kvbh * nkt + kt, wv, lane,
@@ -1324,9 +1348,11 @@ __global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void dkdv_private_kernel(
     lds_barrier();
     constexpr int RPW = 64 / (HD / 16);  // rows per wave: one row-major pass
     float dg[16] = {};
-    if (wv * RPW < 32)
-      pro_rows<HD, RPW>(tile, wv * RPW, dk + (size_t)kvbh * S * HD, pro, (size_t)kvbh * S,
-                        kw0, S, lane, dg);
+    if (wv * RPW < 32) {
+      ProRowsIn<HD, RPW> pin;
+      pin.load(pro, (size_t)kvbh * S, wv * RPW, kw0, S, lane);
+      pro_rows<HD, RPW>(pin, tile, wv * RPW, dk + (size_t)kvbh * S * HD, kw0, S, lane, dg);
+    }
     pro_partial<HD>(dg, reinterpret_cast<float*>(lds + RED_AT), HD, pro, kvbh * nkt + kt, wv,
                     lane, tid);
     return;
@@ -1560,8 +1586,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_kernel(
     lds_barrier();
     constexpr int RPW = 64 / (HD / 16);  // rows per wave pass
     float dg[16] = {};
-    pro_rows<HD, 2 * RPW>(tile, wv * 2 * RPW, dk + (size_t)kvbh * S * HD, pro, (size_t)kvbh * S,
-                          k0, S, lane, dg);
+    ProRowsIn<HD, 2 * RPW> pin;
+    pin.load(pro, (size_t)kvbh * S, wv * 2 * RPW, k0, S, lane);
+    pro_rows<HD, 2 * RPW>(pin, tile, wv * 2 * RPW, dk + (size_t)kvbh * S * HD, k0, S, lane, dg);
     pro_partial<HD>(dg, reinterpret_cast<float*>(lds + RED_AT), HD, pro, kvbh * nkt + kt, wv,
                     lane, tid);
     return;
