@@ -61,28 +61,51 @@ __device__ __forceinline__ int find_job(const KArgs& g, int& bid) {
   return j;
 }
 
-// Per-lane chunk offsets of one wave's four 1 KiB copies of a staged operand tile.
-// K-contiguous tile: copy c (0..15 over the workgroup) holds rows 8c .. 8c+7, lane l the
-// physical chunk l & 7 of row 8c + l / 8, i.e. the logical chunk (l & 7) ^ swizzle.
-// M/N-contiguous tile: copy c holds k-rows 4c .. 4c+3, lane l the physical chunk l & 15 of
-// row 4c + l / 16.
+// Per-lane copy cursor of one operand over the K steps of one segment: the lane's byte
+// offset of each of its wave's four 1 KiB copies at k = 0 (kOutside for rows past the
+// matrix), the chunk's k position inside the tile (for the ragged last step) and the byte
+// step per K step.  K-contiguous tile: copy c (0..15 over the workgroup) holds rows 8c ..
+// 8c+7, lane l the physical chunk l & 7 of row 8c + l / 8, i.e. the logical chunk
+// (l & 7) ^ swizzle.  M/N-contiguous tile: copy c holds k-rows 4c .. 4c+3, lane l the
+// physical chunk l & 15 of row 4c + l / 16.  Operand buffers stay below 2^31 bytes, so an
+// offset at or past kOutside plus any in-matrix step stays past the buffer's range (and
+// reads zeros).
+struct OpCursor {
+  uint32_t off[4];
+  int kin[4];
+  uint32_t kstep;
+};
 template <bool KC>
-__device__ __forceinline__ void tile_offsets(uint32_t (&off)[4], const GemmMat& a, int rows,
-                                             int kdim, int r0, int k0, int wv, int lane) {
+__device__ __forceinline__ void cursor_init(OpCursor& cu, const GemmMat& a, int rows, int r0,
+                                            int wv, int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * wv + i;
     if constexpr (KC) {
       const int row = 8 * c + (lane >> 3);
       const int lc = (lane & 7) ^ (4 * (c & 1) + (lane >> 4));
-      const int rg = r0 + row, kg = k0 + 8 * lc;
-      off[i] = (rg < rows && kg < kdim) ? (uint32_t)(((size_t)rg * a.ld + kg) * 2) : kOutside;
+      const int rg = r0 + row;
+      cu.kin[i] = 8 * lc;
+      cu.off[i] = rg < rows ? (uint32_t)(((size_t)rg * a.ld + 8 * lc) * 2) : kOutside;
     } else {
       const int kr = 4 * c + (lane >> 4);
       const int lc = (lane & 15) ^ (4 * ((lane >> 4) & 3));
-      const int kg = k0 + kr, rg = r0 + 8 * lc;
-      off[i] = (kg < kdim && rg < rows) ? (uint32_t)(((size_t)kg * a.ld + rg) * 2) : kOutside;
+      const int rg = r0 + 8 * lc;
+      cu.kin[i] = kr;
+      cu.off[i] = rg < rows ? (uint32_t)(((size_t)kr * a.ld + rg) * 2) : kOutside;
     }
+  }
+  cu.kstep = KC ? (uint32_t)(kTK * 2) : (uint32_t)kTK * (uint32_t)a.ld * 2u;
+}
+// Offsets of the copies of the K step starting at k0 (kd = its byte step from k = 0): the
+// chunks at or past kdim (only in a ragged last step) read zeros.
+__device__ __forceinline__ void cursor_offsets(uint32_t (&off)[4], const OpCursor& cu,
+                                               uint32_t kd, int k0, int kdim) {
+  const bool ragged = k0 + kTK > kdim;  // uniform
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    off[i] = cu.off[i] + kd;
+    if (ragged && k0 + cu.kin[i] >= kdim) off[i] = kOutside;
   }
 }
 
@@ -138,18 +161,33 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(KArgs g) {
     st_begin = split * kj.steps_per_split;
     st_end = min(steps, st_begin + kj.steps_per_split);
   }
-  int iseg = 0, ik0 = st_begin * kTK;  // issue cursor
+  // issue cursor: segment, k inside it, and the segment's operands and lane offsets (set
+  // once per segment; a K step then only adds its byte step)
+  // (a split job has one segment, so only an unsplit job crosses segments, from k = 0)
+  int iseg = 0, ik0 = st_begin * kTK;
+  GemmSeg sg = jb.seg[0];
+  while (ik0 >= sg.k) {
+    ik0 = 0;
+    sg = jb.seg[++iseg];
+  }
+  OpCursor ca, cb;
+  cursor_init<AK>(ca, sg.a, jb.m, m0, wv, lane);
+  cursor_init<BK>(cb, sg.b, jb.n, n0, wv, lane);
   auto issue = [&](int buf) {
-    while (ik0 >= jb.seg[iseg].k) {  // uniform: the cursor moves to the next segment
-      ik0 = 0;
-      ++iseg;
+    if (ik0 >= sg.k) {  // uniform: the cursor moves to the next segment
+      do {
+        ik0 = 0;
+        sg = jb.seg[++iseg];
+      } while (ik0 >= sg.k);
+      cursor_init<AK>(ca, sg.a, jb.m, m0, wv, lane);
+      cursor_init<BK>(cb, sg.b, jb.n, n0, wv, lane);
     }
-    const GemmSeg& sg = jb.seg[iseg];
     char* dst = lds + buf * 2 * kOpBytes + wv * 4 * 1024;
+    const uint32_t kst = (uint32_t)(ik0 / kTK);
     uint32_t off[4];
-    tile_offsets<AK>(off, sg.a, jb.m, sg.k, m0, ik0, wv, lane);
+    cursor_offsets(off, ca, kst * ca.kstep, ik0, sg.k);
     dma16_rows<4>(dst, static_cast<const char*>(sg.a.p), sg.a.bytes, off);
-    tile_offsets<BK>(off, sg.b, jb.n, sg.k, n0, ik0, wv, lane);
+    cursor_offsets(off, cb, kst * cb.kstep, ik0, sg.k);
     dma16_rows<4>(dst + kOpBytes, static_cast<const char*>(sg.b.p), sg.b.bytes, off);
     ik0 += kTK;
   };
