@@ -13,12 +13,14 @@
 // summation order (bitwise reproducible run to run).
 //
 // bf16 kernel (gfx950):
-//   * 128 x 128 output tile per 256-thread workgroup, four waves of 64 x 64 (2 x 2
-//     v_mfma_f32_32x32x16_bf16 blocks), K in steps of 64, two workgroups per CU.
+//   * 128 x 256 output tile per 512-thread workgroup, eight waves of 64 x 64 (2 x 2
+//     v_mfma_f32_32x32x16_bf16 blocks), K in steps of 64, one workgroup per CU (the
+//     128 x 128 four-wave shape with two workgroups per CU remains as GemmShape<1>).
 //   * Both operand tiles go HBM -> LDS with direct-to-LDS buffer loads (no register round
-//     trip), one K step ahead of the MFMAs.  A chunk that lies outside its matrix gets a
-//     byte offset past the buffer's range, which the hardware turns into zeros, so ragged
-//     m, n and k need no other handling.
+//     trip), two K steps ahead of the MFMAs (three staged steps, 144 KiB).  A lane's copy
+//     offsets are set once per K segment and advanced by a uniform step.  A chunk that
+//     lies outside its matrix gets a byte offset past the buffer's range, which the
+//     hardware turns into zeros, so ragged m, n and k need no other handling.
 //   * K-contiguous tiles ([128][64]: rows of 128 bytes) are read with ds_read_b128; the
 //     16-byte chunks of row r are XOR-swizzled by (r >> 1) & 7 so that the 16 rows one
 //     read phase touches sit on 16 distinct bank groups.  M/N-contiguous tiles ([64][128]:
@@ -37,10 +39,26 @@
 namespace xattn {
 namespace {
 
-constexpr int kTM = 128, kTN = 128, kTK = 64;
-constexpr int kOpBytes = kTM * kTK * 2;  // one staged operand tile: 16 KiB
-constexpr int kGemmBuf = 2;              // staged K steps
+constexpr int kTM = 128, kTK = 64;
+constexpr int kOpBytes = kTM * kTK * 2;  // one staged 128-row operand tile: 16 KiB
 constexpr uint32_t kOutside = 0x80000000u;  // a byte offset past every operand buffer
+
+// Workgroup shapes of the bf16 kernel, by the number NBT of 128-column B tiles: NBT = 1 is a
+// 128 x 128 output tile of four waves, two K steps staged, two workgroups per CU; NBT = 2
+// a 128 x 256 tile of eight waves (2 x 4, each 64 x 64 as before), three K steps staged
+// (144 KiB), one workgroup per CU: the copies are issued two steps ahead, and each staged
+// A tile feeds twice the MFMAs.
+template <int NBT>
+struct GemmShape {
+  static constexpr int kWaves = 4 * NBT;
+  static constexpr int kTN = kTM * NBT;                // output columns per workgroup
+  static constexpr int kNB = NBT == 1 ? 2 : 3;         // staged K steps
+  static constexpr int kStage = (1 + NBT) * kOpBytes;  // A tile + NBT B tiles
+  static constexpr int kCopyA = 16 / kWaves;           // 1 KiB copies per wave and step
+  static constexpr int kCopyB = 16 * NBT / kWaves;
+  static constexpr int kPerBlock = NBT == 1 ? 2 : 1;   // resident workgroups per CU
+};
+constexpr int kGemmNBT = 2;  // the bf16 workgroup shape the launcher uses
 
 // Jobs as the kernels see them: the host-side description plus the tile bookkeeping.
 struct KJob {
@@ -70,17 +88,19 @@ __device__ __forceinline__ int find_job(const KArgs& g, int& bid) {
 // physical chunk l & 15 of row 4c + l / 16.  Operand buffers stay below 2^31 bytes, so an
 // offset at or past kOutside plus any in-matrix step stays past the buffer's range (and
 // reads zeros).
+template <int NC>
 struct OpCursor {
-  uint32_t off[4];
-  int kin[4];
+  uint32_t off[NC];
+  int kin[NC];
   uint32_t kstep;
 };
-template <bool KC>
-__device__ __forceinline__ void cursor_init(OpCursor& cu, const GemmMat& a, int rows, int r0,
-                                            int wv, int lane) {
+// The wave's copies c0 .. c0 + NC - 1 of a 128-row (or 128-column) tile starting at r0.
+template <bool KC, int NC>
+__device__ __forceinline__ void cursor_init(OpCursor<NC>& cu, const GemmMat& a, int rows,
+                                            int r0, int c0, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = 4 * wv + i;
+  for (int i = 0; i < NC; ++i) {
+    const int c = c0 + i;
     if constexpr (KC) {
       const int row = 8 * c + (lane >> 3);
       const int lc = (lane & 7) ^ (4 * (c & 1) + (lane >> 4));
@@ -99,11 +119,12 @@ __device__ __forceinline__ void cursor_init(OpCursor& cu, const GemmMat& a, int 
 }
 // Offsets of the copies of the K step starting at k0 (kd = its byte step from k = 0): the
 // chunks at or past kdim (only in a ragged last step) read zeros.
-__device__ __forceinline__ void cursor_offsets(uint32_t (&off)[4], const OpCursor& cu,
+template <int NC>
+__device__ __forceinline__ void cursor_offsets(uint32_t (&off)[NC], const OpCursor<NC>& cu,
                                                uint32_t kd, int k0, int kdim) {
   const bool ragged = k0 + kTK > kdim;  // uniform
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NC; ++i) {
     off[i] = cu.off[i] + kd;
     if (ragged && k0 + cu.kin[i] >= kdim) off[i] = kOutside;
   }
@@ -139,19 +160,26 @@ __device__ __forceinline__ bf16x8 frag(lptr tile, uint32_t ln, int blk32, int c)
   }
 }
 
-template <int FORM, int OUT>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(KArgs g) {
+template <int FORM, int OUT, int NBT>
+__global__ __launch_bounds__(64 * GemmShape<NBT>::kWaves, GemmShape<NBT>::kPerBlock)
+void gemm_bf16_kernel(KArgs g) {
+  using G = GemmShape<NBT>;
   constexpr bool AK = FORM != GEMM_TN;  // A K-contiguous
   constexpr bool BK = FORM == GEMM_NT;  // B K-contiguous
-  __shared__ __attribute__((aligned(1024))) char lds[kGemmBuf * 2 * kOpBytes];
+  constexpr int NB = G::kNB, CA = G::kCopyA, CB = G::kCopyB;
+  __shared__ __attribute__((aligned(1024))) char lds[NB * G::kStage];
   int bid = blockIdx.x;
   const KJob& kj = g.job[find_job(g, bid)];
   const GemmJob& jb = kj.j;
   const int split = bid / kj.tiles, t = bid - split * kj.tiles;
   const int tm = t / kj.tiles_n, tn = t - tm * kj.tiles_n;
-  const int m0 = tm * kTM, n0 = tn * kTN;
+  const int m0 = tm * kTM, n0 = tn * G::kTN;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wv >> 1, wn = wv & 1;
+  // waves: 2 rows x 2 NBT columns of 64 x 64 outputs; wave wv copies A chunks CA wv ..
+  // CA wv + CA - 1 and B chunks cb0 .. cb0 + CB - 1 of B tile bt (each tile 16 copies)
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv / (2 * NBT), wn = wv % (2 * NBT);
+  const int bt = wv / 4, cb0 = CB * (wv % 4);
 
   // the K steps of this workgroup over the segments (a split job has one segment)
   int steps = 0;
@@ -170,25 +198,27 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(KArgs g) {
     ik0 = 0;
     sg = jb.seg[++iseg];
   }
-  OpCursor ca, cb;
-  cursor_init<AK>(ca, sg.a, jb.m, m0, wv, lane);
-  cursor_init<BK>(cb, sg.b, jb.n, n0, wv, lane);
+  OpCursor<CA> ca;
+  OpCursor<CB> cb;
+  cursor_init<AK>(ca, sg.a, jb.m, m0, CA * wv, lane);
+  cursor_init<BK>(cb, sg.b, jb.n, n0 + kTM * bt, cb0, lane);
   auto issue = [&](int buf) {
     if (ik0 >= sg.k) {  // uniform: the cursor moves to the next segment
       do {
         ik0 = 0;
         sg = jb.seg[++iseg];
       } while (ik0 >= sg.k);
-      cursor_init<AK>(ca, sg.a, jb.m, m0, wv, lane);
-      cursor_init<BK>(cb, sg.b, jb.n, n0, wv, lane);
+      cursor_init<AK>(ca, sg.a, jb.m, m0, CA * wv, lane);
+      cursor_init<BK>(cb, sg.b, jb.n, n0 + kTM * bt, cb0, lane);
     }
-    char* dst = lds + buf * 2 * kOpBytes + wv * 4 * 1024;
+    char* stage = lds + buf * G::kStage;
     const uint32_t kst = (uint32_t)(ik0 / kTK);
-    uint32_t off[4];
-    cursor_offsets(off, ca, kst * ca.kstep, ik0, sg.k);
-    dma16_rows<4>(dst, static_cast<const char*>(sg.a.p), sg.a.bytes, off);
-    cursor_offsets(off, cb, kst * cb.kstep, ik0, sg.k);
-    dma16_rows<4>(dst + kOpBytes, static_cast<const char*>(sg.b.p), sg.b.bytes, off);
+    uint32_t oa[CA], ob[CB];
+    cursor_offsets(oa, ca, kst * ca.kstep, ik0, sg.k);
+    dma16_rows<CA>(stage + CA * wv * 1024, static_cast<const char*>(sg.a.p), sg.a.bytes, oa);
+    cursor_offsets(ob, cb, kst * cb.kstep, ik0, sg.k);
+    dma16_rows<CB>(stage + (1 + bt) * kOpBytes + cb0 * 1024, static_cast<const char*>(sg.b.p),
+                   sg.b.bytes, ob);
     ik0 += kTK;
   };
 
@@ -199,21 +229,25 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(KArgs g) {
   const uint32_t lb = BK ? kc_lane(lane) : mn_lane(lane);
   const lptr lbase = to_lds(lds);
   const int nst = st_end - st_begin;
-  if (nst > 0) issue(0);
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u)
+    if (u < nst) issue(u);
   for (int s = 0; s < nst; ++s) {
-    wait_vm<0>();  // step s has landed (this wave's copies)
+    // step s has landed (this wave's copies; later steps may stay in flight) ...
+    if (s + NB - 1 <= nst) wait_vm<(NB - 2) * (CA + CB)>();
+    else wait_vm<0>();
     __builtin_amdgcn_s_barrier();  // ... and every wave's; step s - 1's reads are done
     lds_acquire();
-    if (s + 1 < nst) issue((s + 1) % kGemmBuf);
-    const lptr ta = lbase + (s % kGemmBuf) * 2 * kOpBytes;
-    const lptr tb = ta + kOpBytes;
+    if (s + NB - 1 < nst) issue((s + NB - 1) % NB);
+    const lptr ta = lbase + (s % NB) * G::kStage;
+    const lptr tb = ta + (1 + wn / 2) * kOpBytes;  // the B tile of the wave's columns
     bf16x8 fa[2][4], fb[2][4];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         fa[i][c] = frag<AK>(ta, la, 2 * wm + i, c);
-        fb[i][c] = frag<BK>(tb, lb, 2 * wn + i, c);
+        fb[i][c] = frag<BK>(tb, lb, 2 * (wn % 2) + i, c);
       }
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -371,34 +405,41 @@ template <int FORM>
 hipError_t launch_form(IoType io, int out, const KArgs& a, int blocks, dim3 block,
                        hipStream_t stream) {
 #define XATTN_GEMM(K, O) hipLaunchKernelGGL((K<FORM, O>), dim3(blocks), block, 0, stream, a)
+#define XATTN_GEMM16(O)                                                                   \
+  hipLaunchKernelGGL((gemm_bf16_kernel<FORM, O, kGemmNBT>), dim3(blocks),                \
+                     dim3(64 * GemmShape<kGemmNBT>::kWaves), 0, stream, a)
   if (io == IO_BF16) {
-    if (out == GEMM_OUT_IO_ROWS) XATTN_GEMM(gemm_bf16_kernel, GEMM_OUT_IO_ROWS);
-    else if (out == GEMM_OUT_IO_HEADS) XATTN_GEMM(gemm_bf16_kernel, GEMM_OUT_IO_HEADS);
-    else XATTN_GEMM(gemm_bf16_kernel, GEMM_OUT_F32);
+    if (out == GEMM_OUT_IO_ROWS) XATTN_GEMM16(GEMM_OUT_IO_ROWS);
+    else if (out == GEMM_OUT_IO_HEADS) XATTN_GEMM16(GEMM_OUT_IO_HEADS);
+    else XATTN_GEMM16(GEMM_OUT_F32);
   } else {
     if (out == GEMM_OUT_IO_ROWS) XATTN_GEMM(gemm_f32_kernel, GEMM_OUT_IO_ROWS);
     else if (out == GEMM_OUT_IO_HEADS) XATTN_GEMM(gemm_f32_kernel, GEMM_OUT_IO_HEADS);
     else XATTN_GEMM(gemm_f32_kernel, GEMM_OUT_F32);
   }
 #undef XATTN_GEMM
+#undef XATTN_GEMM16
   return hipPeekAtLastError();
 }
 
 // Tile bookkeeping shared by the launcher and the workspace query.
 int plan_jobs(IoType io, const GemmJob* jobs, int njobs, KArgs* out) {
-  const int tile = io == IO_BF16 ? kTM : 64, kstep = io == IO_BF16 ? kTK : 16;
+  using G = GemmShape<kGemmNBT>;
+  const bool b16 = io == IO_BF16;
+  const int tm = b16 ? kTM : 64, tn = b16 ? G::kTN : 64, kstep = b16 ? kTK : 16;
+  const int fill = b16 ? 256 * G::kPerBlock : 512;  // workgroups resident on the chip
   int blocks = 0;
   for (int q = 0; q < njobs; ++q) {
     KJob& k = out->job[q];
     k.j = jobs[q];
-    k.tiles_n = (k.j.n + tile - 1) / tile;
-    k.tiles = ((k.j.m + tile - 1) / tile) * k.tiles_n;
+    k.tiles_n = (k.j.n + tn - 1) / tn;
+    k.tiles = ((k.j.m + tm - 1) / tm) * k.tiles_n;
     int steps = 0;
     for (int s = 0; s < k.j.nseg; ++s) steps += (k.j.seg[s].k + kstep - 1) / kstep;
     // fp32 outputs with few tiles split K (at least 8 steps per split) to fill the chip
     k.splits = 1;
-    if (k.j.part != nullptr && k.j.nseg == 1 && k.tiles < 512)
-      k.splits = std::max(1, std::min(steps / 8, (512 + k.tiles - 1) / k.tiles));
+    if (k.j.part != nullptr && k.j.nseg == 1 && k.tiles < fill)
+      k.splits = std::max(1, std::min(steps / 8, (fill + k.tiles - 1) / k.tiles));
     k.steps_per_split = (steps + k.splits - 1) / k.splits;
     k.splits = (steps + k.steps_per_split - 1) / k.steps_per_split;  // no empty split
     k.block_begin = blocks;
