@@ -92,12 +92,26 @@ template <int NC>
 struct OpCursor {
   uint32_t off[NC];
   int kin[NC];
-  uint32_t kstep;
+  uint32_t kstep;    // row-major: bytes per K step
+  int heads, S, hd;  // head-major matrices (GemmMat::heads > 0)
+  // Byte offset of the K step starting at k0 (uniform).  Row-major: k0 / kTK steps.
+  // Head-major, K-contiguous (k = features): the head k0 / hd, column k0 % hd.  Head-major,
+  // M/N-contiguous (k = tokens; the step's tokens share one sequence): sequence k0 / S,
+  // position k0 % S.
+  template <bool KC>
+  __device__ __forceinline__ uint32_t step(int k0) const {
+    if (heads == 0) return (uint32_t)(k0 / kTK) * kstep;
+    if constexpr (KC) return (uint32_t)(((k0 / hd) * S * hd + k0 % hd) * 2);
+    else return (uint32_t)(((size_t)(k0 / S) * heads * S * hd + (size_t)(k0 % S) * hd) * 2);
+  }
 };
 // The wave's copies c0 .. c0 + NC - 1 of a 128-row (or 128-column) tile starting at r0.
 template <bool KC, int NC>
 __device__ __forceinline__ void cursor_init(OpCursor<NC>& cu, const GemmMat& a, int rows,
-                                            int r0, int c0, int lane) {
+                                            int r0, int c0, int lane, int S, int hd) {
+  cu.heads = a.heads;
+  cu.S = S;
+  cu.hd = hd;
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
     const int c = c0 + i;
@@ -106,13 +120,27 @@ __device__ __forceinline__ void cursor_init(OpCursor<NC>& cu, const GemmMat& a, 
       const int lc = (lane & 7) ^ (4 * (c & 1) + (lane >> 4));
       const int rg = r0 + row;
       cu.kin[i] = 8 * lc;
-      cu.off[i] = rg < rows ? (uint32_t)(((size_t)rg * a.ld + 8 * lc) * 2) : kOutside;
+      size_t at;
+      if (a.heads == 0) {
+        at = (size_t)rg * a.ld + 8 * lc;
+      } else {  // token rg = (b, s): row (b * heads) * S + s of the head-major tensor
+        const size_t b = (size_t)rg / S;
+        at = (b * a.heads * S + (rg - b * S)) * hd + 8 * lc;
+      }
+      cu.off[i] = rg < rows ? (uint32_t)(at * 2) : kOutside;
     } else {
       const int kr = 4 * c + (lane >> 4);
       const int lc = (lane & 15) ^ (4 * ((lane >> 4) & 3));
       const int rg = r0 + 8 * lc;
       cu.kin[i] = kr;
-      cu.off[i] = rg < rows ? (uint32_t)(((size_t)kr * a.ld + rg) * 2) : kOutside;
+      size_t at;
+      if (a.heads == 0) {
+        at = (size_t)kr * a.ld + rg;
+      } else {  // feature rg = (h, e); token k0 + kr at position kr after the step's
+        const int h = rg / hd;
+        at = ((size_t)h * S + kr) * hd + (rg - h * hd);
+      }
+      cu.off[i] = rg < rows ? (uint32_t)(at * 2) : kOutside;
     }
   }
   cu.kstep = KC ? (uint32_t)(kTK * 2) : (uint32_t)kTK * (uint32_t)a.ld * 2u;
@@ -200,23 +228,22 @@ void gemm_bf16_kernel(KArgs g) {
   }
   OpCursor<CA> ca;
   OpCursor<CB> cb;
-  cursor_init<AK>(ca, sg.a, jb.m, m0, CA * wv, lane);
-  cursor_init<BK>(cb, sg.b, jb.n, n0 + kTM * bt, cb0, lane);
+  cursor_init<AK>(ca, sg.a, jb.m, m0, CA * wv, lane, g.S, g.hd);
+  cursor_init<BK>(cb, sg.b, jb.n, n0 + kTM * bt, cb0, lane, g.S, g.hd);
   auto issue = [&](int buf) {
     if (ik0 >= sg.k) {  // uniform: the cursor moves to the next segment
       do {
         ik0 = 0;
         sg = jb.seg[++iseg];
       } while (ik0 >= sg.k);
-      cursor_init<AK>(ca, sg.a, jb.m, m0, CA * wv, lane);
-      cursor_init<BK>(cb, sg.b, jb.n, n0 + kTM * bt, cb0, lane);
+      cursor_init<AK>(ca, sg.a, jb.m, m0, CA * wv, lane, g.S, g.hd);
+      cursor_init<BK>(cb, sg.b, jb.n, n0 + kTM * bt, cb0, lane, g.S, g.hd);
     }
     char* stage = lds + buf * G::kStage;
-    const uint32_t kst = (uint32_t)(ik0 / kTK);
     uint32_t oa[CA], ob[CB];
-    cursor_offsets(oa, ca, kst * ca.kstep, ik0, sg.k);
+    cursor_offsets(oa, ca, ca.template step<AK>(ik0), ik0, sg.k);
     dma16_rows<CA>(stage + CA * wv * 1024, static_cast<const char*>(sg.a.p), sg.a.bytes, oa);
-    cursor_offsets(ob, cb, kst * cb.kstep, ik0, sg.k);
+    cursor_offsets(ob, cb, cb.template step<BK>(ik0), ik0, sg.k);
     dma16_rows<CB>(stage + (1 + bt) * kOpBytes + cb0 * 1024, static_cast<const char*>(sg.b.p),
                    sg.b.bytes, ob);
     ik0 += kTK;
@@ -428,17 +455,23 @@ int plan_jobs(IoType io, const GemmJob* jobs, int njobs, KArgs* out) {
   const bool b16 = io == IO_BF16;
   const int tm = b16 ? kTM : 64, tn = b16 ? G::kTN : 64, kstep = b16 ? kTK : 16;
   const int fill = b16 ? 256 * G::kPerBlock : 512;  // workgroups resident on the chip
-  int blocks = 0;
+  int blocks = 0, all_tiles = 0;
   for (int q = 0; q < njobs; ++q) {
     KJob& k = out->job[q];
     k.j = jobs[q];
     k.tiles_n = (k.j.n + tn - 1) / tn;
     k.tiles = ((k.j.m + tm - 1) / tm) * k.tiles_n;
+    all_tiles += k.tiles;
+  }
+  for (int q = 0; q < njobs; ++q) {
+    KJob& k = out->job[q];
     int steps = 0;
     for (int s = 0; s < k.j.nseg; ++s) steps += (k.j.seg[s].k + kstep - 1) / kstep;
-    // fp32 outputs with few tiles split K (at least 8 steps per split) to fill the chip
+    // fp32 outputs split K (at least 8 steps per split) when the launch's tiles cannot fill
+    // the chip; a job never gets more splits than it would alone (the workspace query
+    // plans one job)
     k.splits = 1;
-    if (k.j.part != nullptr && k.j.nseg == 1 && k.tiles < fill)
+    if (k.j.part != nullptr && k.j.nseg == 1 && all_tiles < fill)
       k.splits = std::max(1, std::min(steps / 8, (fill + k.tiles - 1) / k.tiles));
     k.steps_per_split = (steps + k.splits - 1) / k.splits;
     k.splits = (steps + k.steps_per_split - 1) / k.steps_per_split;  // no empty split

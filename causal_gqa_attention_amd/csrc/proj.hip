@@ -49,8 +49,22 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(ColsumJobs jobs, in
   const T* src = static_cast<const T*>(jb.src);
   const size_t r0 = (size_t)p * chunk, r1 = min((size_t)jb.rows, r0 + chunk);
   float s = 0.f;
+  if (jb.heads == 0) {
 #pragma unroll 8
-  for (size_t r = r0; r < r1; ++r) s += to_f32(src[r * jb.cols + c]);
+    for (size_t r = r0; r < r1; ++r) s += to_f32(src[r * jb.cols + c]);
+  } else {  // head-major source: column c = (h, e), row r = (b, t), walked t by t
+    const int hd = jb.cols / jb.heads, h = c / hd, e = c - h * hd;
+    size_t b = r0 / jb.S, t = r0 - b * jb.S;
+    for (size_t r = r0; r < r1;) {
+      const size_t n = min(r1 - r, (size_t)jb.S - t);  // rows left in this sequence
+      const T* q = src + ((b * jb.heads + h) * jb.S + t) * hd + e;
+#pragma unroll 8
+      for (size_t i = 0; i < n; ++i) s += to_f32(q[i * hd]);
+      r += n;
+      ++b;
+      t = 0;
+    }
+  }
   jb.partial[(size_t)p * jb.cols + c] = s;
 }
 

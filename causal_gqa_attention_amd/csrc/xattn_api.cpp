@@ -208,7 +208,17 @@ ProjChecked check_proj(const xattn_dims* dims, int64_t model_dim) {
 // The projection GEMMs' jobs (gemm.hip).  Operands are row-major; `w` below is the io
 // dtype's size.  Token rows: x, y, dx [M, d]; merged heads [M, n].
 xattn::GemmMat mat(const void* p, int rows, int ld, size_t w) {
-  return {p, ld, (uint32_t)((size_t)rows * ld * w)};
+  return {p, ld, (uint32_t)((size_t)rows * ld * w), 0};
+}
+// The token rows [M, heads*hd] of a head-major tensor [B*heads, S, hd], read in place.
+xattn::GemmMat mat_heads(const void* p, int rows, int heads, int hd, size_t w) {
+  return {p, heads * hd, (uint32_t)((size_t)rows * heads * hd * w), heads};
+}
+// The bf16 GEMMs read head-major operands in place when every K step of 64 stays inside
+// one head (hd % 64 == 0) and inside one sequence (S % 64 == 0); otherwise the tensors are
+// merged into token rows first.
+bool heads_in_place(const ProjChecked& p) {
+  return p.c.io == xattn::IO_BF16 && p.c.s.head_dim % 64 == 0 && p.c.s.seq_len % 64 == 0;
 }
 xattn::GemmJob job1(xattn::GemmMat a, xattn::GemmMat b, int k, int m, int n, void* c, int ldc,
                     int c_heads, const float* bias, float* part) {
@@ -218,17 +228,21 @@ xattn::GemmJob job1(xattn::GemmMat a, xattn::GemmMat b, int k, int m, int n, voi
   j.m = m, j.n = n, j.c = c, j.ldc = ldc, j.c_heads = c_heads, j.bias = bias, j.part = part;
   return j;
 }
-// dW = x^T g: A = x stored [M, d], B = g stored [M, n]
+// dW = x^T g: A = x stored [M, d], B = g stored [M, n] (heads > 0: g head-major with that
+// many heads)
 xattn::GemmJob dw_job(const ProjChecked& p, const void* x, const void* g, int n, float* dw,
-                      float* part) {
-  return job1(mat(x, p.M, p.d, p.io), mat(g, p.M, n, p.io), p.M, p.d, n, dw, n, 0, nullptr,
-              part);
+                      float* part, int heads = 0) {
+  const xattn::GemmMat gm =
+      heads > 0 ? mat_heads(g, p.M, heads, p.c.s.head_dim, p.io) : mat(g, p.M, n, p.io);
+  return job1(mat(x, p.M, p.d, p.io), gm, p.M, p.d, n, dw, n, 0, nullptr, part);
 }
-// dWo = merge(out)^T dy: A = merged out [M, nq], B = dy [M, d]
+// dWo = merge(out)^T dy: A = out [M, nq] (merged rows, or head-major when heads > 0),
+// B = dy [M, d]
 xattn::GemmJob dwo_job(const ProjChecked& p, const void* om, const void* dy, float* dwo,
-                       float* part) {
-  return job1(mat(om, p.M, p.nq, p.io), mat(dy, p.M, p.d, p.io), p.M, p.nq, p.d, dwo, p.d, 0,
-              nullptr, part);
+                       float* part, int heads = 0) {
+  const xattn::GemmMat am =
+      heads > 0 ? mat_heads(om, p.M, heads, p.c.s.head_dim, p.io) : mat(om, p.M, p.nq, p.io);
+  return job1(am, mat(dy, p.M, p.d, p.io), p.M, p.nq, p.d, dwo, p.d, 0, nullptr, part);
 }
 
 // Workspace regions of the projection calls (each call uses a prefix of its own plan).
@@ -698,11 +712,16 @@ xattn_status xattn_out_proj_fwd(const xattn_dims* dims, const xattn_proj* pr, co
     const hipStream_t st = (hipStream_t)stream;
     Carver w{static_cast<char*>(workspace)};
     void* om = w.take<char>(M * p.nq * p.io);
-    xattn::MergeJobs mj{{{out, om, p.M, p.nq}}, 1};
-    hip_check(xattn::launch_merge_heads(p.c.io, mj, p.c.s.seq_len, p.c.s.head_dim, st),
-              "merge_heads launch");
-    const xattn::GemmJob j = job1(mat(om, p.M, p.nq, p.io), mat(pr->wo, p.nq, p.d, p.io), p.nq,
-                                  p.M, p.d, y, p.d, 0, pr->bo, nullptr);
+    const bool direct = heads_in_place(p);
+    if (!direct) {
+      xattn::MergeJobs mj{{{out, om, p.M, p.nq}}, 1};
+      hip_check(xattn::launch_merge_heads(p.c.io, mj, p.c.s.seq_len, p.c.s.head_dim, st),
+                "merge_heads launch");
+    }
+    const xattn::GemmMat am = direct ? mat_heads(out, p.M, p.c.s.num_heads, p.c.s.head_dim, p.io)
+                                     : mat(om, p.M, p.nq, p.io);
+    const xattn::GemmJob j = job1(am, mat(pr->wo, p.nq, p.d, p.io), p.nq, p.M, p.d, y, p.d, 0,
+                                  pr->bo, nullptr);
     hip_check(xattn::launch_gemm(p.c.io, xattn::GEMM_NN, xattn::GEMM_OUT_IO_ROWS, &j, 1,
                                  p.c.s.seq_len, p.c.s.head_dim, st),
               "projection GEMM launch");
@@ -730,7 +749,9 @@ xattn_status xattn_out_proj_bwd(const xattn_dims* dims, const xattn_proj* pr, co
     Carver w{static_cast<char*>(workspace)};
     void* om = w.take<char>(M * p.nq * p.io);
     float* part = w.take<float>((size_t)xattn::colsum_parts(p.M) * p.d * 4);
-    xattn::GemmJob jw = dwo_job(p, om, dy, dwo, nullptr);
+    const bool direct = heads_in_place(p);
+    xattn::GemmJob jw = direct ? dwo_job(p, out, dy, dwo, nullptr, p.c.s.num_heads)
+                               : dwo_job(p, om, dy, dwo, nullptr);
     jw.part = w.take<float>(xattn::gemm_partial_floats(p.c.io, jw) * 4);
     // dout = split(dy Wo^T): Wo stored [nq, d] is B^T
     const xattn::GemmJob jd = job1(mat(dy, p.M, p.d, p.io), mat(pr->wo, p.nq, p.d, p.io), p.d,
@@ -739,9 +760,11 @@ xattn_status xattn_out_proj_bwd(const xattn_dims* dims, const xattn_proj* pr, co
                                  p.c.s.seq_len, p.c.s.head_dim, st),
               "projection GEMM launch");
     // dwo = merge(out)^T dy
-    xattn::MergeJobs mj{{{out, om, p.M, p.nq}}, 1};
-    hip_check(xattn::launch_merge_heads(p.c.io, mj, p.c.s.seq_len, p.c.s.head_dim, st),
-              "merge_heads launch");
+    if (!direct) {
+      xattn::MergeJobs mj{{{out, om, p.M, p.nq}}, 1};
+      hip_check(xattn::launch_merge_heads(p.c.io, mj, p.c.s.seq_len, p.c.s.head_dim, st),
+                "merge_heads launch");
+    }
     hip_check(xattn::launch_gemm(p.c.io, xattn::GEMM_TN, xattn::GEMM_OUT_F32, &jw, 1,
                                  p.c.s.seq_len, p.c.s.head_dim, st),
               "projection GEMM launch");
@@ -787,19 +810,30 @@ xattn_status xattn_qkv_proj_bwd(const xattn_dims* dims, const xattn_proj* pr, co
     float* pq = w.take<float>((size_t)xattn::colsum_parts(p.M) * p.nq * 4);
     float* pk = w.take<float>((size_t)xattn::colsum_parts(p.M) * p.nk * 4);
     float* pv = w.take<float>((size_t)xattn::colsum_parts(p.M) * p.nk * 4);
-    xattn::GemmJob jw[3] = {dw_job(p, x, gq, p.nq, dwq, nullptr),
-                            dw_job(p, x, gk, p.nk, dwk, nullptr),
-                            dw_job(p, x, gv, p.nk, dwv, nullptr)};
+    // the gradients as token rows: merged copies, or the head-major tensors read in place
+    const bool direct = heads_in_place(p);
+    const int hq = direct ? p.c.s.num_heads : 0, hk = direct ? p.c.s.num_kv_heads : 0;
+    const void* rq = direct ? dxq : gq;
+    const void* rk = direct ? dxk : gk;
+    const void* rv = direct ? dv : gv;
+    xattn::GemmJob jw[3] = {dw_job(p, x, rq, p.nq, dwq, nullptr, hq),
+                            dw_job(p, x, rk, p.nk, dwk, nullptr, hk),
+                            dw_job(p, x, rv, p.nk, dwv, nullptr, hk)};
     for (xattn::GemmJob& j : jw) j.part = w.take<float>(xattn::gemm_partial_floats(p.c.io, j) * 4);
-    xattn::MergeJobs mj{{{dxq, gq, p.M, p.nq}, {dxk, gk, p.M, p.nk}, {dv, gv, p.M, p.nk}}, 3};
-    hip_check(xattn::launch_merge_heads(p.c.io, mj, p.c.s.seq_len, p.c.s.head_dim, st),
-              "merge_heads launch");
+    if (!direct) {
+      xattn::MergeJobs mj{{{dxq, gq, p.M, p.nq}, {dxk, gk, p.M, p.nk}, {dv, gv, p.M, p.nk}}, 3};
+      hip_check(xattn::launch_merge_heads(p.c.io, mj, p.c.s.seq_len, p.c.s.head_dim, st),
+                "merge_heads launch");
+    }
+    const auto rows = [&](const void* t, int n, int heads) {
+      return heads > 0 ? mat_heads(t, p.M, heads, p.c.s.head_dim, p.io) : mat(t, p.M, n, p.io);
+    };
     // dx = gq Wq^T + gk Wk^T + gv Wv^T: one job, three K segments summed in fp32 (W stored
     // [d, n] is B^T)
     xattn::GemmJob jx{};
-    jx.seg[0] = {mat(gq, p.M, p.nq, p.io), mat(pr->wq, p.d, p.nq, p.io), p.nq};
-    jx.seg[1] = {mat(gk, p.M, p.nk, p.io), mat(pr->wk, p.d, p.nk, p.io), p.nk};
-    jx.seg[2] = {mat(gv, p.M, p.nk, p.io), mat(pr->wv, p.d, p.nk, p.io), p.nk};
+    jx.seg[0] = {rows(rq, p.nq, hq), mat(pr->wq, p.d, p.nq, p.io), p.nq};
+    jx.seg[1] = {rows(rk, p.nk, hk), mat(pr->wk, p.d, p.nk, p.io), p.nk};
+    jx.seg[2] = {rows(rv, p.nk, hk), mat(pr->wv, p.d, p.nk, p.io), p.nk};
     jx.nseg = 3;
     jx.m = p.M, jx.n = p.d, jx.c = dx, jx.ldc = p.d;
     hip_check(xattn::launch_gemm(p.c.io, xattn::GEMM_NT, xattn::GEMM_OUT_IO_ROWS, &jx, 1,
@@ -810,9 +844,9 @@ xattn_status xattn_qkv_proj_bwd(const xattn_dims* dims, const xattn_proj* pr, co
                                  p.c.s.seq_len, p.c.s.head_dim, st),
               "projection GEMM launch");
     xattn::ColsumJobs cj{};
-    if (dbq != nullptr) cj.job[cj.n++] = {gq, pq, dbq, p.M, p.nq};
-    if (dbk != nullptr) cj.job[cj.n++] = {gk, pk, dbk, p.M, p.nk};
-    if (dbv != nullptr) cj.job[cj.n++] = {gv, pv, dbv, p.M, p.nk};
+    if (dbq != nullptr) cj.job[cj.n++] = {rq, pq, dbq, p.M, p.nq, hq, p.c.s.seq_len};
+    if (dbk != nullptr) cj.job[cj.n++] = {rk, pk, dbk, p.M, p.nk, hk, p.c.s.seq_len};
+    if (dbv != nullptr) cj.job[cj.n++] = {rv, pv, dbv, p.M, p.nk, hk, p.c.s.seq_len};
     if (cj.n > 0) hip_check(xattn::launch_colsum(p.c.io, cj, st), "bias gradient launch");
   });
 }

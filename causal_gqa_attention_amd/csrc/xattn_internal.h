@@ -158,6 +158,8 @@ struct ColsumJob {
   float* partial;  // [colsum_parts(rows)][cols] scratch
   float* out;      // [cols]
   int rows, cols;
+  int heads;       // 0: src is [rows, cols] row-major; else head-major [B*heads, S, hd]
+  int S;           // sequence length of a head-major src (rows = B*S, cols = heads*hd)
 };
 struct ColsumJobs {
   ColsumJob job[3];
@@ -183,6 +185,11 @@ struct GemmMat {
   const void* p;
   int ld;          // elements per stored row
   uint32_t bytes;  // size of the stored matrix
+  // 0: row-major with ld.  Else the matrix is the token-row view [B*S, heads*hd] of a
+  // head-major tensor [B*heads, S, hd] (element (b*S + s, h*hd + e) at ((b*heads + h)*S +
+  // s)*hd + e; S and hd from the launch), read in place (bf16 only; hd % 64 == 0, and
+  // S % 64 == 0 when tokens run along K)
+  int heads;
 };
 struct GemmSeg {
   GemmMat a, b;

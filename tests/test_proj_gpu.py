@@ -24,6 +24,8 @@ SHAPES = [
     ("bf16", 1, 4096, 32, 8, 128, 4096, True),  # Qwen3-shaped heads, d = 4096
     ("bf16", 3, 50, 6, 2, 32, 200, True),       # ragged rows, columns and K in every GEMM
     ("bf16", 2, 33, 4, 4, 16, 40, False),       # hd 16: 4-column output runs inside a head
+    ("bf16", 3, 128, 4, 2, 64, 200, True),      # head-major operands read in place, 3 sequences
+    ("bf16", 2, 192, 2, 1, 128, 136, True),     # ... at hd 128, ragged model dim
     ("f32", 3, 50, 6, 2, 32, 200, False),
 ]
 IDS = [f"{s[0]}_B{s[1]}_S{s[2]}_H{s[3]}_kv{s[4]}_hd{s[5]}_d{s[6]}_{'bias' if s[7] else 'nobias'}"
