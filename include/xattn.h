@@ -243,7 +243,9 @@ xattn_status xattn_bwd_noalloc(const xattn_dims* dims, const void* q, const void
  * before Wo; [T12]: GEMMs take the io dtype with fp32 accumulation, the weight and bias
  * gradients are fp32.  Token rows: x, y, dx [B*S, d], row b*S + s.  The GEMMs are the
  * library's own kernels (bf16: MFMA), with the head split, bias and rounding in their
- * epilogues; weight gradients are summed in a fixed order (bitwise reproducible).
+ * epilogues, and (bf16, hd and S multiples of 64) the head-major tensors read in place
+ * instead of merged into a copy; weight gradients are summed in a fixed order (bitwise
+ * reproducible).
  * Requires d % 8 == 0 and every operand below 2^31 bytes.  The segment fields of dims are
  * ignored. */
 typedef struct {
