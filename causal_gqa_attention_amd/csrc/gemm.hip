@@ -14,8 +14,7 @@
 //
 // bf16 kernel (gfx950):
 //   * 128 x 256 output tile per 512-thread workgroup, eight waves of 64 x 64 (2 x 2
-//     v_mfma_f32_32x32x16_bf16 blocks), K in steps of 64, one workgroup per CU (the
-//     128 x 128 four-wave shape with two workgroups per CU remains as GemmShape<1>).
+//     v_mfma_f32_32x32x16_bf16 blocks), K in steps of 64, one workgroup per CU.
 //   * Both operand tiles go HBM -> LDS with direct-to-LDS buffer loads (no register round
 //     trip), two K steps ahead of the MFMAs (three staged steps, 144 KiB).  A lane's copy
 //     offsets are set once per K segment and advanced by a uniform step.  A chunk that
@@ -43,22 +42,30 @@ constexpr int kTM = 128, kTK = 64;
 constexpr int kOpBytes = kTM * kTK * 2;  // one staged 128-row operand tile: 16 KiB
 constexpr uint32_t kOutside = 0x80000000u;  // a byte offset past every operand buffer
 
-// Workgroup shapes of the bf16 kernel, by the number NBT of 128-column B tiles: NBT = 1 is a
-// 128 x 128 output tile of four waves, two K steps staged, two workgroups per CU; NBT = 2
-// a 128 x 256 tile of eight waves (2 x 4, each 64 x 64 as before), three K steps staged
-// (144 KiB), one workgroup per CU: the copies are issued two steps ahead, and each staged
-// A tile feeds twice the MFMAs.
-template <int NBT>
-struct GemmShape {
-  static constexpr int kWaves = 4 * NBT;
-  static constexpr int kTN = kTM * NBT;                // output columns per workgroup
-  static constexpr int kNB = NBT == 1 ? 2 : 3;         // staged K steps
-  static constexpr int kStage = (1 + NBT) * kOpBytes;  // A tile + NBT B tiles
-  static constexpr int kCopyA = 16 / kWaves;           // 1 KiB copies per wave and step
+// Workgroup shape of the bf16 kernel: NAT x NBT staged 128-row operand tiles (A, B) per K
+// step, a WM x WN grid of waves, each wave BM x BN blocks of 32 x 32 outputs.  The one in
+// use (GemmShape<2>) is 128 x 256 with eight waves of 64 x 64 and three K steps staged
+// (144 KiB, one workgroup per CU): the copies run two steps ahead and each staged A tile
+// feeds twice the MFMAs of a 128 x 128 tile.
+template <int NAT_, int NBT_, int WM_, int WN_, int BM_, int BN_, int NB_, int PER_>
+struct GemmShapeT {
+  static constexpr int NAT = NAT_, NBT = NBT_, WM = WM_, WN = WN_, BM = BM_, BN = BN_;
+  static constexpr int kNB = NB_, kPerBlock = PER_;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kTMW = kTM * NAT, kTN = kTM * NBT;  // output rows / columns
+  static constexpr int kStage = (NAT + NBT) * kOpBytes;
+  static constexpr int kCopyA = 16 * NAT / kWaves;  // 1 KiB copies per wave and step
   static constexpr int kCopyB = 16 * NBT / kWaves;
-  static constexpr int kPerBlock = NBT == 1 ? 2 : 1;   // resident workgroups per CU
+  static_assert(32 * BM * WM == kTMW && 32 * BN * WN == kTN, "waves cover the tile");
+  static_assert(kCopyA >= 1 && kCopyB >= 1 && 16 % kCopyA == 0 && 16 % kCopyB == 0,
+                "whole copies per wave, inside one tile");
+  static_assert(kNB * kStage <= 160 * 1024, "staged steps fit the LDS");
 };
-constexpr int kGemmNBT = 2;  // the bf16 workgroup shape the launcher uses
+template <int ID>
+struct GemmShape;
+template <>
+struct GemmShape<2> : GemmShapeT<1, 2, 2, 4, 2, 2, 3, 1> {};
+constexpr int kGemmShape = 2;  // the bf16 workgroup shape the launcher uses
 
 // Jobs as the kernels see them: the host-side description plus the tile bookkeeping.
 struct KJob {
@@ -188,10 +195,11 @@ __device__ __forceinline__ bf16x8 frag(lptr tile, uint32_t ln, int blk32, int c)
   }
 }
 
-template <int FORM, int OUT, int NBT>
-__global__ __launch_bounds__(64 * GemmShape<NBT>::kWaves, GemmShape<NBT>::kPerBlock)
+template <int FORM, int OUT, int ID>
+__global__ __launch_bounds__(64 * GemmShape<ID>::kWaves, GemmShape<ID>::kPerBlock)
 void gemm_bf16_kernel(KArgs g) {
-  using G = GemmShape<NBT>;
+  using G = GemmShape<ID>;
+  constexpr int NAT = G::NAT, BM = G::BM, BN = G::BN;
   constexpr bool AK = FORM != GEMM_TN;  // A K-contiguous
   constexpr bool BK = FORM == GEMM_NT;  // B K-contiguous
   constexpr int NB = G::kNB, CA = G::kCopyA, CB = G::kCopyB;
@@ -201,13 +209,18 @@ void gemm_bf16_kernel(KArgs g) {
   const GemmJob& jb = kj.j;
   const int split = bid / kj.tiles, t = bid - split * kj.tiles;
   const int tm = t / kj.tiles_n, tn = t - tm * kj.tiles_n;
-  const int m0 = tm * kTM, n0 = tn * G::kTN;
+  const int m0 = tm * G::kTMW, n0 = tn * G::kTN;
   const int tid = threadIdx.x, lane = tid & 63;
-  // waves: 2 rows x 2 NBT columns of 64 x 64 outputs; wave wv copies A chunks CA wv ..
-  // CA wv + CA - 1 and B chunks cb0 .. cb0 + CB - 1 of B tile bt (each tile 16 copies)
+  // wave (wm, wn) of the WM x WN grid owns rows 32 BM wm .. and columns 32 BN wn ..; it
+  // copies chunks ca0 .. ca0 + CA - 1 of A tile cat and cb0 .. cb0 + CB - 1 of B tile cbt
+  // (16 chunks of 1 KiB per 128-row tile)
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv / (2 * NBT), wn = wv % (2 * NBT);
-  const int bt = wv / 4, cb0 = CB * (wv % 4);
+  const int wm = wv / G::WN, wn = wv % G::WN;
+  const int cat = CA * wv / 16, ca0 = CA * wv % 16;
+  const int cbt = CB * wv / 16, cb0 = CB * wv % 16;
+  // the tile and first 32-block of the wave's rows (A) and columns (B)
+  const int rat = 32 * BM * wm / kTM, rab = 32 * BM * wm % kTM / 32;
+  const int rbt = 32 * BN * wn / kTM, rbb = 32 * BN * wn % kTM / 32;
 
   // the K steps of this workgroup over the segments (a split job has one segment)
   int steps = 0;
@@ -228,30 +241,33 @@ void gemm_bf16_kernel(KArgs g) {
   }
   OpCursor<CA> ca;
   OpCursor<CB> cb;
-  cursor_init<AK>(ca, sg.a, jb.m, m0, CA * wv, lane, g.S, g.hd);
-  cursor_init<BK>(cb, sg.b, jb.n, n0 + kTM * bt, cb0, lane, g.S, g.hd);
+  cursor_init<AK>(ca, sg.a, jb.m, m0 + kTM * cat, ca0, lane, g.S, g.hd);
+  cursor_init<BK>(cb, sg.b, jb.n, n0 + kTM * cbt, cb0, lane, g.S, g.hd);
   auto issue = [&](int buf) {
     if (ik0 >= sg.k) {  // uniform: the cursor moves to the next segment
       do {
         ik0 = 0;
         sg = jb.seg[++iseg];
       } while (ik0 >= sg.k);
-      cursor_init<AK>(ca, sg.a, jb.m, m0, CA * wv, lane, g.S, g.hd);
-      cursor_init<BK>(cb, sg.b, jb.n, n0 + kTM * bt, cb0, lane, g.S, g.hd);
+      cursor_init<AK>(ca, sg.a, jb.m, m0 + kTM * cat, ca0, lane, g.S, g.hd);
+      cursor_init<BK>(cb, sg.b, jb.n, n0 + kTM * cbt, cb0, lane, g.S, g.hd);
     }
     char* stage = lds + buf * G::kStage;
     uint32_t oa[CA], ob[CB];
     cursor_offsets(oa, ca, ca.template step<AK>(ik0), ik0, sg.k);
-    dma16_rows<CA>(stage + CA * wv * 1024, static_cast<const char*>(sg.a.p), sg.a.bytes, oa);
+    dma16_rows<CA>(stage + cat * kOpBytes + ca0 * 1024, static_cast<const char*>(sg.a.p),
+                   sg.a.bytes, oa);
     cursor_offsets(ob, cb, cb.template step<BK>(ik0), ik0, sg.k);
-    dma16_rows<CB>(stage + (1 + bt) * kOpBytes + cb0 * 1024, static_cast<const char*>(sg.b.p),
-                   sg.b.bytes, ob);
+    dma16_rows<CB>(stage + (NAT + cbt) * kOpBytes + cb0 * 1024,
+                   static_cast<const char*>(sg.b.p), sg.b.bytes, ob);
     ik0 += kTK;
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[BM][BN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = zero16();
+  for (int i = 0; i < BM; ++i)
+#pragma unroll
+    for (int j = 0; j < BN; ++j) acc[i][j] = zero16();
   const uint32_t la = AK ? kc_lane(lane) : mn_lane(lane);
   const uint32_t lb = BK ? kc_lane(lane) : mn_lane(lane);
   const lptr lbase = to_lds(lds);
@@ -266,30 +282,30 @@ void gemm_bf16_kernel(KArgs g) {
     __builtin_amdgcn_s_barrier();  // ... and every wave's; step s - 1's reads are done
     lds_acquire();
     if (s + NB - 1 < nst) issue((s + NB - 1) % NB);
-    const lptr ta = lbase + (s % NB) * G::kStage;
-    const lptr tb = ta + (1 + wn / 2) * kOpBytes;  // the B tile of the wave's columns
-    bf16x8 fa[2][4], fb[2][4];
+    const lptr st0 = lbase + (s % NB) * G::kStage;
+    const lptr ta = st0 + rat * kOpBytes, tb = st0 + (NAT + rbt) * kOpBytes;
+    bf16x8 fa[BM][4], fb[BN][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int i = 0; i < BM; ++i) fa[i][c] = frag<AK>(ta, la, rab + i, c);
+#pragma unroll
+      for (int j = 0; j < BN; ++j) fb[j][c] = frag<BK>(tb, lb, rbb + j, c);
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        fa[i][c] = frag<AK>(ta, la, 2 * wm + i, c);
-        fb[i][c] = frag<BK>(tb, lb, 2 * (wn % 2) + i, c);
-      }
+      for (int i = 0; i < BM; ++i)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(fb[j][c], fa[i][c], acc[i][j]);
+        for (int j = 0; j < BN; ++j) acc[i][j] = mfma_bf16(fb[j][c], fa[i][c], acc[i][j]);
   }
 
-  // epilogue: lane row m0 + 64 wm + 32 i + lane % 32, columns n0 + 64 wn + 32 j + 8 q +
-  // 4 h + {0..3} in acc[i][j][4q .. 4q+3]
+  // epilogue: lane row m0 + 32 BM wm + 32 i + lane % 32, columns n0 + 32 BN wn + 32 j +
+  // 8 q + 4 h + {0..3} in acc[i][j][4q .. 4q+3]
   const int h = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = m0 + 64 * wm + 32 * i + (lane & 31);
+  for (int i = 0; i < BM; ++i) {
+    const int row = m0 + 32 * BM * wm + 32 * i + (lane & 31);
     if (row >= jb.m) continue;
     int b = 0, sq = row;
     if constexpr (OUT == GEMM_OUT_IO_HEADS) {
@@ -297,10 +313,10 @@ void gemm_bf16_kernel(KArgs g) {
       sq = row - b * g.S;
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < BN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = n0 + 64 * wn + 32 * j + 8 * q + 4 * h;
+        const int col = n0 + 32 * BN * wn + 32 * j + 8 * q + 4 * h;
         if (col >= jb.n) continue;
         f32x4 v;
 #pragma unroll
@@ -433,8 +449,8 @@ hipError_t launch_form(IoType io, int out, const KArgs& a, int blocks, dim3 bloc
                        hipStream_t stream) {
 #define XATTN_GEMM(K, O) hipLaunchKernelGGL((K<FORM, O>), dim3(blocks), block, 0, stream, a)
 #define XATTN_GEMM16(O)                                                                   \
-  hipLaunchKernelGGL((gemm_bf16_kernel<FORM, O, kGemmNBT>), dim3(blocks),                \
-                     dim3(64 * GemmShape<kGemmNBT>::kWaves), 0, stream, a)
+  hipLaunchKernelGGL((gemm_bf16_kernel<FORM, O, kGemmShape>), dim3(blocks),              \
+                     dim3(64 * GemmShape<kGemmShape>::kWaves), 0, stream, a)
   if (io == IO_BF16) {
     if (out == GEMM_OUT_IO_ROWS) XATTN_GEMM16(GEMM_OUT_IO_ROWS);
     else if (out == GEMM_OUT_IO_HEADS) XATTN_GEMM16(GEMM_OUT_IO_HEADS);
@@ -451,9 +467,9 @@ hipError_t launch_form(IoType io, int out, const KArgs& a, int blocks, dim3 bloc
 
 // Tile bookkeeping shared by the launcher and the workspace query.
 int plan_jobs(IoType io, const GemmJob* jobs, int njobs, KArgs* out) {
-  using G = GemmShape<kGemmNBT>;
+  using G = GemmShape<kGemmShape>;
   const bool b16 = io == IO_BF16;
-  const int tm = b16 ? kTM : 64, tn = b16 ? G::kTN : 64, kstep = b16 ? kTK : 16;
+  const int tm = b16 ? G::kTMW : 64, tn = b16 ? G::kTN : 64, kstep = b16 ? kTK : 16;
   const int fill = b16 ? 256 * G::kPerBlock : 512;  // workgroups resident on the chip
   int blocks = 0, all_tiles = 0;
   for (int q = 0; q < njobs; ++q) {
