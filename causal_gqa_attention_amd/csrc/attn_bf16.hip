@@ -1624,10 +1624,9 @@ hipError_t fwd_launch(const AttnShape& s, const void* q, const void* k, const vo
 // machine; else, at head_dim 128, the pipelined one (64 keys per workgroup), else the
 // private one (32 keys per workgroup).
 bool dkdv_shared(int BKV, int S) { return (long long)BKV * ((S + 127) / 128) >= 1024; }
-constexpr bool kDkdvPipe = true;
 int dkdv_keys_per_block(int BKV, int S, int HD) {
   if (dkdv_shared(BKV, S)) return 128;
-  return (kDkdvPipe && HD == 128) ? 64 : 32;
+  return HD == 128 ? 64 : 32;
 }
 
 template <int HD, bool PRO>
@@ -1658,13 +1657,13 @@ hipError_t bwd_launch(const AttnShape& s, const void* q, const void* k, const vo
                        (const bf16*)dout, (const float*)lse2, (const float*)delta, (bf16*)dk,
                        (bf16*)dv, S, s.num_heads, s.num_kv_heads, sl2, scale, nkt, xcd, pk,
                        s.seg_hi);
-  } else if (dkdv_keys_per_block(BKV, S, HD) == 64) {
+  } else if constexpr (HD == 128) {  // 64 keys per workgroup
     const int nkt = (S + 63) / 64;
     hipLaunchKernelGGL((dkdv_pipe_kernel<HD, PRO>), dim3(BKV * nkt), dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
                        (const float*)lse2, (const float*)delta, (bf16*)dk, (bf16*)dv, S,
                        s.num_heads, s.num_kv_heads, sl2, scale, nkt, xcd, pk, s.seg_hi);
-  } else {
+  } else {  // 32 keys per workgroup
     const int nkt = (S + 31) / 32;
     hipLaunchKernelGGL((dkdv_private_kernel<HD, kDkdvPrivateBuf, PRO>), dim3(BKV * nkt),
                        dim3(256), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
