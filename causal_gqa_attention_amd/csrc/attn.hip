@@ -821,6 +821,7 @@ static hipError_t fwd_impl(const AttnShape& s, const void* q, const void* k, con
 
 hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const void* k,
                            const void* v, void* out, float* lse, hipStream_t stream) {
+  // bf16 at head_dim 64 / 128 always runs the attn_bf16.hip kernels
   if (io == IO_BF16 && fast_bf16_supported(s.head_dim))
     return launch_attn_fwd_bf16_fast(s, q, k, v, out, lse, nullptr, stream);
 #define XATTN_CASE(T, HD) \
@@ -828,7 +829,7 @@ hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const v
   if (io == IO_F32) {
     XATTN_CASE(float, 16) XATTN_CASE(float, 32) XATTN_CASE(float, 64) XATTN_CASE(float, 128)
   } else {
-    XATTN_CASE(bf16, 16) XATTN_CASE(bf16, 32) XATTN_CASE(bf16, 64) XATTN_CASE(bf16, 128)
+    XATTN_CASE(bf16, 16) XATTN_CASE(bf16, 32)
   }
 #undef XATTN_CASE
   return hipErrorInvalidValue;
@@ -905,9 +906,13 @@ hipError_t launch_attn_bwd(IoType io, const AttnShape& s, const void* q, const v
                            const void* v, const void* out, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, float* delta,
                            float* lse2, bool grads_f32, hipStream_t stream) {
-  if (io == IO_BF16 && fast_bf16_supported(s.head_dim) && !grads_f32)
+  // bf16 at head_dim 64 / 128 always runs the attn_bf16.hip kernels (with fp32 gradients
+  // never requested there: that path applies the prologue backward in its own stores)
+  if (io == IO_BF16 && fast_bf16_supported(s.head_dim)) {
+    if (grads_f32) return hipErrorInvalidValue;
     return launch_attn_bwd_bf16_fast(s, q, k, v, out, lse, dout, dq, dk, dv, delta, lse2,
                                      nullptr, stream);
+  }
 #define XATTN_CASE(T, HD, TG)                                                          \
   if (s.head_dim == HD)                                                                \
     return bwd_impl<T, HD, TG>(s, q, k, v, out, lse, dout, dq, dk, dv, delta, stream);
@@ -915,11 +920,9 @@ hipError_t launch_attn_bwd(IoType io, const AttnShape& s, const void* q, const v
     XATTN_CASE(float, 16, float) XATTN_CASE(float, 32, float) XATTN_CASE(float, 64, float)
     XATTN_CASE(float, 128, float)
   } else if (grads_f32) {
-    XATTN_CASE(bf16, 16, float) XATTN_CASE(bf16, 32, float) XATTN_CASE(bf16, 64, float)
-    XATTN_CASE(bf16, 128, float)
+    XATTN_CASE(bf16, 16, float) XATTN_CASE(bf16, 32, float)
   } else {
-    XATTN_CASE(bf16, 16, bf16) XATTN_CASE(bf16, 32, bf16) XATTN_CASE(bf16, 64, bf16)
-    XATTN_CASE(bf16, 128, bf16)
+    XATTN_CASE(bf16, 16, bf16) XATTN_CASE(bf16, 32, bf16)
   }
 #undef XATTN_CASE
   return hipErrorInvalidValue;

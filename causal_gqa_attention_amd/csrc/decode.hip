@@ -917,19 +917,20 @@ hipError_t split_launch(int R, DecodeArgs a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_split_mfma_kernel<HD>), dim3((waves + 3) / 4), dim3(256), 0,
                        stream, a);
     return hipSuccess;
+  } else {
+    if constexpr (RMV < decode_rows_max<T>()) {
+      if (R > RMV) return split_launch<T, HD, 2 * RMV>(R, a, stream);
+    }
+    a.nchunk = (R + RMV - 1) / RMV;
+    const int waves = a.B * a.Hkv * a.nchunk * a.nsplit;
+    if constexpr (std::is_same_v<T, bf16>)
+      hipLaunchKernelGGL((decode_split_bf16_kernel<HD, RMV>), dim3((waves + 3) / 4),
+                         dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<T, HD, RMV>), dim3((waves + 3) / 4), dim3(256),
+                         0, stream, a);
+    return hipSuccess;
   }
-  if constexpr (RMV < decode_rows_max<T>()) {
-    if (R > RMV) return split_launch<T, HD, 2 * RMV>(R, a, stream);
-  }
-  a.nchunk = (R + RMV - 1) / RMV;
-  const int waves = a.B * a.Hkv * a.nchunk * a.nsplit;
-  if constexpr (std::is_same_v<T, bf16>)
-    hipLaunchKernelGGL((decode_split_bf16_kernel<HD, RMV>), dim3((waves + 3) / 4), dim3(256),
-                       0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<T, HD, RMV>), dim3((waves + 3) / 4), dim3(256), 0,
-                       stream, a);
-  return hipSuccess;
 }
 
 template <typename T, int HD>
