@@ -1550,28 +1550,41 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_kernel(
   }
   wait_vm<0>();
 
-  // stream-ordered combination of the two partials of each key half
-  float* red = reinterpret_cast<float*>(lds);
+  // stream-ordered combination of the two partials of each key half: once every wave is done
+  // with the staged tiles (and their copies have landed), stream 1 parks its dK / dV partials
+  // in LDS as 16-byte slots, element-major (slot index, then lane: conflict-free), above the
+  // epilogue tile; after one barrier stream 0 adds them to its own.
+  {
+    constexpr int NT = HD / 32, SLOTS = 2 * NT * 4;  // f32x4 slots per lane: dK then dV
+    constexpr int RED_AT = 65536;
+    static_assert(RED_AT + 2 * SLOTS * 64 * 16 <= (int)sizeof(lds), "partials fit");
+    f32x4* red = reinterpret_cast<f32x4*>(lds + RED_AT) + kb * SLOTS * 64 + lane;
+    __syncthreads();
+    if (st == 1) {
 #pragma unroll
-  for (int which = 0; which < 2; ++which) {
+      for (int which = 0; which < 2; ++which)
 #pragma unroll
-    for (int dt = 0; dt < HD / 32; ++dt) {
-      __syncthreads();
-      if (st == 1) {
-        float* slot = red + (kb * 64 + lane) * 16;
-        const f32x16& src = which == 0 ? dkt[dt] : dvt[dt];
+        for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) slot[e] = src[e];
-      }
-      __syncthreads();
-      if (st == 0) {
-        const float* slot = red + (kb * 64 + lane) * 16;
+          for (int q = 0; q < 4; ++q) {
+            const f32x16& a = which == 0 ? dkt[dt] : dvt[dt];
+            red[((which * NT + dt) * 4 + q) * 64] =
+                f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+          }
+    }
+    __syncthreads();
+    if (st == 0) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          if (which == 0) dkt[dt][e] += slot[e];
-          else dvt[dt][e] += slot[e];
-        }
-      }
+      for (int which = 0; which < 2; ++which)
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 b = red[((which * NT + dt) * 4 + q) * 64];
+            f32x16& a = which == 0 ? dkt[dt] : dvt[dt];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[4 * q + e] += b[e];
+          }
     }
   }
   if constexpr (PRO) {
