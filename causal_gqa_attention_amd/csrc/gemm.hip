@@ -29,6 +29,11 @@
 //   * The MFMA takes the B fragment as its A operand, so each accumulator holds a block of
 //     C^T: a lane owns one output row and runs of four adjacent columns, which the
 //     epilogue stores as 8- or 16-byte vectors (with the bias add and the rounding).
+//   * An operand may be the token-row view of a head-major tensor [B*heads, S, hd] (the
+//     attention output, the gradients w.r.t. q, k, v): the lane's chunk offset then holds
+//     its token's or feature's head coordinates and a K step adds a uniform offset of the
+//     next head (k = features) or the next 64 positions of a sequence (k = tokens), so the
+//     tensor is read in place instead of being merged into token rows first.
 #include <algorithm>
 
 #include "lds_copy.h"
