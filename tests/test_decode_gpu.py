@@ -28,11 +28,12 @@ STEPWISE = [
     (R("bf16", 64, 50, 2, 6, 2, index=405), 2, 3),                     # g3, R = 6
     (R("bf16", 32, 20, 1, 4, 4, index=406), 5, 0),                     # MHA, 5 at a time
     (R("bf16", 16, 9, 1, 2, 1, index=407), 4, 1),                      # hd 16, ragged last
-    # more rows per KV head than one wave holds (8 bf16, 16 fp32): row chunks
+    # rows per KV head against what one wave holds (16 for fp32 and for bf16 at hd 64 / 128,
+    # 8 for bf16 at hd 16 / 32): beyond it, row chunks
     (R("bf16", 128, 70, 1, 32, 8, theta=1e6, eps=1e-6, index=409), 4, 2),  # Qwen3 heads, R 16
     (R("f32", 64, 40, 1, 16, 2, index=410), 4, 0),                     # g8, R = 32
     (R("bf16", 64, 50, 1, 8, 1, index=411), 3, 1),                     # MQA g8, R = 24, ragged
-    (R("bf16", 128, 48, 1, 4, 1, index=412), 16, 0),                   # R = 64, 8 chunks
+    (R("bf16", 128, 48, 1, 4, 1, index=412), 16, 0),                   # R = 64, 4 chunks
 ]
 IDS = [f"{w.dtype}_hd{w.head_dim}_S{w.seq_len}_H{w.num_heads}_kv{w.num_kv_heads}_q{q}"
        for w, q, _ in STEPWISE]
