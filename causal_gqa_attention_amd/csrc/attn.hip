@@ -23,6 +23,7 @@
 //     transposing LDS read, so no transposed copy is ever stored.
 //   * Online softmax in the exp2 domain with log2(e)/sqrt(hd) folded into one multiply.
 //   * Work order: the heaviest causal tiles are dispatched first.
+#include <algorithm>
 #include <type_traits>
 
 #include "xattn_device.h"
@@ -641,12 +642,17 @@ constexpr int kBlockMQ = 32;  // queries per LDS stage in dk/dv
 // Waves of a dk/dv workgroup: four, or QS when the query walk is split eight ways.
 constexpr int dkdv_waves(int qs) { return qs > kWaves ? qs : kWaves; }
 
+// With gsplit > 1 the group's query heads are split over blockIdx.z (heads
+// z*group/gsplit .. (z+1)*group/gsplit - 1, ascending) and each workgroup writes its fp32
+// partial dK (unscaled) and dV to part instead of dk / dv; dkdv_group_sum_kernel then adds
+// the gsplit partials in z order.
 template <typename T, int HD, typename TG, int QS>
 __global__ __launch_bounds__(64 * dkdv_waves(QS)) void attn_bwd_dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, TG* __restrict__ dk, T* __restrict__ dv, int S, int H,
-    int Hkv, float scale_log2, float scale, const int* __restrict__ seg_hi) {
+    int Hkv, float scale_log2, float scale, const int* __restrict__ seg_hi, int gsplit,
+    float* __restrict__ part) {
   using C = Tile<T, HD>;
   constexpr int KW = dkdv_waves(QS) / QS;
   constexpr int BNK = 32 * KW;
@@ -663,6 +669,8 @@ __global__ __launch_bounds__(64 * dkdv_waves(QS)) void attn_bwd_dkdv_kernel(
   const int kvbh = blockIdx.x;
   const int b = kvbh / Hkv, kvh = kvbh - b * Hkv;
   const int group = H / Hkv;
+  const int r_lo = (int)blockIdx.z * group / gsplit;  // the workgroup's query heads
+  const int nr = ((int)blockIdx.z + 1) * group / gsplit - r_lo;
   const int k0 = blockIdx.y * BNK;  // lowest key tiles (most work) dispatched first
   const int kw0 = k0 + 32 * kw;
   const int key = kw0 + c32;
@@ -693,9 +701,9 @@ __global__ __launch_bounds__(64 * dkdv_waves(QS)) void attn_bwd_dkdv_kernel(
   constexpr int NPT = (CH + 64 * KW - 1) / (64 * KW);    // per staging thread
   vec16_t<T> pq[NPT], pd[NPT];
   float plse = INFINITY, pdel = 0.f;  // staging threads st_tid < kBlockMQ: one row each
-  const int nall = group * nsteps;
+  const int nall = nr * nsteps;
   auto fetch = [&](int u) {
-    const int r = u / nsteps, step = u - r * nsteps;
+    const int r = r_lo + u / nsteps, step = u - (u / nsteps) * nsteps;
     const size_t bh = (size_t)(b * H + kvh * group + r);
     const int q0 = (qt_first + step * QS + sp) * kBlockMQ;
     const bool real = qt_first + step * QS + sp < nqt;
@@ -791,8 +799,42 @@ __global__ __launch_bounds__(64 * dkdv_waves(QS)) void attn_bwd_dkdv_kernel(
     }
   }
   if (sp == 0 && key < S) {
-    store_column<TG, HD, C::NDT>(dk + ((size_t)kvbh * S + key) * HD, dkt, scale, h);
-    store_column<T, HD, C::NDT>(dv + ((size_t)kvbh * S + key) * HD, dvt, 1.0f, h);
+    if (part != nullptr) {  // group split: fp32 partials, dK unscaled
+      const size_t per = (size_t)gridDim.x * S * HD;  // one partial tensor
+      float* pk = part + (size_t)blockIdx.z * 2 * per + ((size_t)kvbh * S + key) * HD;
+      store_column<float, HD, C::NDT>(pk, dkt, 1.0f, h);
+      store_column<float, HD, C::NDT>(pk + per, dvt, 1.0f, h);
+    } else {
+      store_column<TG, HD, C::NDT>(dk + ((size_t)kvbh * S + key) * HD, dkt, scale, h);
+      store_column<T, HD, C::NDT>(dv + ((size_t)kvbh * S + key) * HD, dvt, 1.0f, h);
+    }
+  }
+}
+
+// dk = scale * (sum over z ascending of the partial dK), dv = the sum of the partial dV;
+// partials [gsplit][2][n] fp32, four elements per thread.
+template <typename T, typename TG>
+__global__ __launch_bounds__(256) void dkdv_group_sum_kernel(const float* __restrict__ part,
+                                                             TG* __restrict__ dk,
+                                                             T* __restrict__ dv, size_t n,
+                                                             int gsplit, float scale) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 sk = *reinterpret_cast<const f32x4*>(part + i);
+  f32x4 sv = *reinterpret_cast<const f32x4*>(part + n + i);
+  for (int z = 1; z < gsplit; ++z) {
+    const f32x4 ak = *reinterpret_cast<const f32x4*>(part + (size_t)z * 2 * n + i);
+    const f32x4 av = *reinterpret_cast<const f32x4*>(part + (size_t)z * 2 * n + n + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sk[e] += ak[e];
+      sv[e] += av[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    dk[i + e] = from_f32<TG>(sk[e] * scale);
+    dv[i + e] = from_f32<T>(sv[e]);
   }
 }
 
@@ -852,24 +894,45 @@ static int dkdv_splits(const AttnShape& s) {
   return (blocks4 < 256 && stage8 <= 144 * 1024) ? 8 : 4;
 }
 
+// Group splits of the dk/dv kernel: when even the split query walk leaves fewer than 256
+// workgroups, the group's query heads are spread over up to `group` workgroups per key
+// block (fp32 partials added afterwards in a fixed order).  Shape only, like the splits.
+template <int QS>
+static int dkdv_gsplit(const AttnShape& s) {
+  constexpr int BNK = 32 * (dkdv_waves(QS) / QS);
+  const long long blocks =
+      (long long)s.batch * s.num_kv_heads * ((s.seq_len + BNK - 1) / BNK);
+  const int group = s.num_heads / s.num_kv_heads;
+  if (blocks >= 256 || group == 1) return 1;
+  return (int)std::min<long long>(group, (256 + blocks - 1) / blocks);
+}
+
 template <typename T, int HD, typename TG, int QS>
 static void launch_dkdv(const AttnShape& s, const void* q, const void* k, const void* v,
                         const void* dout, const float* lse, const float* delta, void* dk,
-                        void* dv, hipStream_t stream) {
+                        void* dv, float* part, hipStream_t stream) {
   constexpr int BNK = 32 * (dkdv_waves(QS) / QS);
-  const dim3 grid(s.batch * s.num_kv_heads, (s.seq_len + BNK - 1) / BNK);
+  const int gs = dkdv_gsplit<QS>(s);
+  const dim3 grid(s.batch * s.num_kv_heads, (s.seq_len + BNK - 1) / BNK, gs);
   ProfScope prof("attn_bwd_dkdv", stream);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD, TG, QS>), grid, dim3(64 * dkdv_waves(QS)), 0,
                      stream,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta,
                      (TG*)dk, (T*)dv, s.seq_len, s.num_heads, s.num_kv_heads,
-                     scale_of(HD) * kLog2e, scale_of(HD), s.seg_hi);
+                     scale_of(HD) * kLog2e, scale_of(HD), s.seg_hi, gs,
+                     gs > 1 ? part : nullptr);
+  if (gs > 1) {
+    const size_t n = (size_t)s.batch * s.num_kv_heads * s.seq_len * HD;
+    hipLaunchKernelGGL((dkdv_group_sum_kernel<T, TG>), dim3((unsigned)((n / 4 + 255) / 256)),
+                       dim3(256), 0, stream, (const float*)part, (TG*)dk, (T*)dv, n, gs,
+                       scale_of(HD));
+  }
 }
 
 template <typename T, int HD, typename TG>
 static hipError_t bwd_impl(const AttnShape& s, const void* q, const void* k, const void* v,
                            const void* out, const float* lse, const void* dout, void* dq,
-                           void* dk, void* dv, float* delta, hipStream_t stream) {
+                           void* dk, void* dv, float* delta, float* part, hipStream_t stream) {
   {
     ProfScope prof("attn_bwd_dq", stream);
     if (use_split(s)) {
@@ -889,23 +952,48 @@ static hipError_t bwd_impl(const AttnShape& s, const void* q, const void* k, con
   hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess) return e;
   switch (dkdv_splits<T, HD>(s)) {
-    case 1: launch_dkdv<T, HD, TG, 1>(s, q, k, v, dout, lse, delta, dk, dv, stream); break;
-    case 2: launch_dkdv<T, HD, TG, 2>(s, q, k, v, dout, lse, delta, dk, dv, stream); break;
+    case 1: launch_dkdv<T, HD, TG, 1>(s, q, k, v, dout, lse, delta, dk, dv, part, stream); break;
+    case 2: launch_dkdv<T, HD, TG, 2>(s, q, k, v, dout, lse, delta, dk, dv, part, stream); break;
     case 8:
       if constexpr (2 * 8 * (size_t)kBlockMQ * Tile<T, HD>::LDS_ROW * sizeof(T) <= 144 * 1024) {
-        launch_dkdv<T, HD, TG, 8>(s, q, k, v, dout, lse, delta, dk, dv, stream);
+        launch_dkdv<T, HD, TG, 8>(s, q, k, v, dout, lse, delta, dk, dv, part, stream);
         break;
       }
       [[fallthrough]];
-    default: launch_dkdv<T, HD, TG, 4>(s, q, k, v, dout, lse, delta, dk, dv, stream); break;
+    default: launch_dkdv<T, HD, TG, 4>(s, q, k, v, dout, lse, delta, dk, dv, part, stream); break;
   }
   return hipPeekAtLastError();
+}
+
+template <typename T, int HD>
+static size_t dkdv_partial_floats_impl(const AttnShape& s) {
+  int gs = 1;
+  switch (dkdv_splits<T, HD>(s)) {
+    case 1: gs = dkdv_gsplit<1>(s); break;
+    case 2: gs = dkdv_gsplit<2>(s); break;
+    case 8: gs = dkdv_gsplit<8>(s); break;
+    default: gs = dkdv_gsplit<4>(s); break;
+  }
+  return gs > 1 ? 2 * (size_t)gs * s.batch * s.num_kv_heads * s.seq_len * HD : 0;
+}
+
+size_t dkdv_partial_floats(IoType io, const AttnShape& s) {
+  if (io == IO_BF16 && fast_bf16_supported(s.head_dim)) return 0;
+#define XATTN_CASE(T, HD) \
+  if (s.head_dim == HD) return dkdv_partial_floats_impl<T, HD>(s);
+  if (io == IO_F32) {
+    XATTN_CASE(float, 16) XATTN_CASE(float, 32) XATTN_CASE(float, 64) XATTN_CASE(float, 128)
+  } else {
+    XATTN_CASE(bf16, 16) XATTN_CASE(bf16, 32)
+  }
+#undef XATTN_CASE
+  return 0;
 }
 
 hipError_t launch_attn_bwd(IoType io, const AttnShape& s, const void* q, const void* k,
                            const void* v, const void* out, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, float* delta,
-                           float* lse2, bool grads_f32, hipStream_t stream) {
+                           float* lse2, bool grads_f32, float* dkdv_part, hipStream_t stream) {
   // bf16 at head_dim 64 / 128 always runs the attn_bf16.hip kernels (with fp32 gradients
   // never requested there: that path applies the prologue backward in its own stores)
   if (io == IO_BF16 && fast_bf16_supported(s.head_dim)) {
@@ -915,7 +1003,8 @@ hipError_t launch_attn_bwd(IoType io, const AttnShape& s, const void* q, const v
   }
 #define XATTN_CASE(T, HD, TG)                                                          \
   if (s.head_dim == HD)                                                                \
-    return bwd_impl<T, HD, TG>(s, q, k, v, out, lse, dout, dq, dk, dv, delta, stream);
+    return bwd_impl<T, HD, TG>(s, q, k, v, out, lse, dout, dq, dk, dv, delta, dkdv_part,   \
+                               stream);
   if (io == IO_F32) {
     XATTN_CASE(float, 16, float) XATTN_CASE(float, 32, float) XATTN_CASE(float, 64, float)
     XATTN_CASE(float, 128, float)

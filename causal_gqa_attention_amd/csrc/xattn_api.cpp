@@ -160,6 +160,7 @@ bool fused_prologue_bwd(const DimsChecked& c) {
 
 size_t bwd_workspace(const DimsChecked& c, bool with_prologue) {
   size_t n = 2 * align256((size_t)c.rows_q * sizeof(float));  // delta, lse * log2(e)
+  n += align256(xattn::dkdv_partial_floats(c.io, c.s) * sizeof(float));  // group-split dk/dv
   if (with_prologue && fused_prologue_bwd(c)) {
     const int64_t hq = (int64_t)c.s.batch * c.s.num_heads;
     const int64_t hk = (int64_t)c.s.batch * c.s.num_kv_heads;
@@ -933,10 +934,13 @@ xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, con
     ws += align256((size_t)c.rows_q * sizeof(float));
     float* lse2 = reinterpret_cast<float*>(ws);
     ws += align256((size_t)c.rows_q * sizeof(float));
+    const size_t npart = xattn::dkdv_partial_floats(c.io, c.s);
+    float* dkdv_part = npart > 0 ? reinterpret_cast<float*>(ws) : nullptr;
+    ws += align256(npart * sizeof(float));
     const hipStream_t st = (hipStream_t)stream;
     if (pro == nullptr) {
       hip_check(xattn::launch_attn_bwd(c.io, c.s, q, k, v, out, lse, dout, dq, dk, dv, delta,
-                                       lse2, false, st),
+                                       lse2, false, dkdv_part, st),
                 "attention backward launch");
       return;
     }
@@ -964,7 +968,7 @@ xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, con
     ws += align256((size_t)xattn::qknorm_rope_bwd_blocks(c.rows_q) * c.s.head_dim * sizeof(float));
     float* part_k = reinterpret_cast<float*>(ws);
     hip_check(xattn::launch_attn_bwd(c.io, c.s, q, k, v, out, lse, dout, dyq, dyk, dv, delta,
-                                     lse2, true, st),
+                                     lse2, true, dkdv_part, st),
               "attention backward launch");
     hip_check(xattn::launch_qknorm_rope_bwd_qk(
                   xattn::IO_F32, c.io, c.s.head_dim, dyq, pro->xq, pro->gamma_q, pro->rstd_q, dq,

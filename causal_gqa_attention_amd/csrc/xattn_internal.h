@@ -112,10 +112,14 @@ hipError_t launch_attn_bwd_bf16_fast(const AttnShape& s, const void* q, const vo
 
 // grads_f32: when true, dq and dk are written as fp32 (used when the prologue backward
 // follows inside xattn_bwd); otherwise in the io dtype.  dv is always in the io dtype.
+// dkdv_part: fp32 scratch of dkdv_partial_floats(io, s) floats (the generic dk/dv kernel
+// splits the group's query heads over workgroups for shapes with few key blocks; NULL when
+// that is 0).
 hipError_t launch_attn_bwd(IoType io, const AttnShape& s, const void* q, const void* k,
                            const void* v, const void* out, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, float* delta,
-                           float* lse2, bool grads_f32, hipStream_t stream);
+                           float* lse2, bool grads_f32, float* dkdv_part, hipStream_t stream);
+size_t dkdv_partial_floats(IoType io, const AttnShape& s);
 
 // ---- KV-cache decode (decode.hip) ---------------------------------------------------
 struct DecodeShape {

@@ -41,6 +41,9 @@ SMALL = [
     # (the shapes above with fp32 or head_dim 16 / 32 run the split kernels)
     R("f32", 64, 300, 4, 24, 6, index=216),
     R("bf16", 16, 260, 8, 16, 4, index=217),
+    # the generic dk/dv with the group's query heads split over workgroups (few key blocks):
+    # group 5 over two splits, heads {0, 1} and {2, 3, 4}
+    R("f32", 32, 1000, 2, 10, 2, index=218),
 ]
 SMALL_IDS = [w.name if w.index < 100 else f"{w.dtype}_hd{w.head_dim}_S{w.seq_len}_"
              f"B{w.batch}_H{w.num_heads}_kv{w.num_kv_heads}" for w in SMALL]
