@@ -6,8 +6,9 @@
 //   out_i = sum_j p_ij v_j, lse_i = ln sum_j exp(s_ij); query head qh of batch b reads KV
 //   head b*Hkv + qh/group.  The backward is the chain rule with D_i = dO_i . out_i:
 //   dS = P (dP - D), dq = dS K / sqrt(hd), dk = sum_r dS^T Q / sqrt(hd), dv = sum_r P^T dO,
-//   where r runs over the group's query heads; each dk/dv tile has exactly one owning
-//   workgroup that sums the group in ascending r with no atomics.
+//   where r runs over the group's query heads, summed in ascending r with no atomics (by
+//   the dk/dv tile's one owning workgroup, or, for the smallest grids, by a fixed-order sum
+//   of per-workgroup partials over contiguous ranges of r).
 //
 // Design (MI355X-first, not a translation of the pages' CUDA kernels):
 //   * Tiles of 32 x 32 on v_mfma_f32_32x32x16_bf16 (fp32 io: v_mfma_f32_32x32x2_f32).
@@ -635,7 +636,8 @@ static inline bool use_split(const AttnShape& s) {
 // backward, dk/dv: one workgroup owns 32*KW keys of one KV head; QS query splits
 // (QS * KW = 4 waves) walk interleaved 32-query tiles of every query head of the group,
 // r ascending; the split partials are added in split order at the end.  Every dk/dv
-// element therefore has one owner and a fixed summation order.
+// element therefore has one owner and a fixed summation order (with the query heads also
+// split over workgroups, a fixed-order sum of their partials follows, below).
 // --------------------------------------------------------------------------------------
 constexpr int kBlockMQ = 32;  // queries per LDS stage in dk/dv
 
