@@ -179,6 +179,168 @@ __device__ __forceinline__ void store_column(TO* dst, const f32x16 (&acc)[NDT], 
   }
 }
 
+// Q side of the prologue forward applied to the lane's resident Q fragment (bf16 io,
+// head_dim 16 or 32; Mint documentation 5.4.1 and 5.5.1): raw row t of the head whose rows
+// start at head_row0, elements 16 c + 8 h + j of chunk c as load_fragment places them, is
+// normalised and rotated with the standalone prologue forward's operations in its order
+// (no multiply-add contraction; at head_dim 32 the lanes l and l ^ 32 own a row's columns
+// as its two row lanes do, at head_dim 16 each takes the other's half so that both sum the
+// whole row as its one row lane does), so the rows are bitwise those of
+// xattn_qknorm_rope_fwd.  The rotated row becomes the fragment; with `store` it also goes to
+// pro.yq and its rstd to pro.rstd_q.  Rows t >= S give a zero fragment and store nothing.
+// Every lane of the wave calls.
+template <int HD>
+__device__ __forceinline__ void q_prologue_frag(bf16x8 (&qf)[HD / 16], const QProFuse& pro,
+                                                size_t head_row0, int t, int S, bool store,
+                                                int lane) {
+#pragma clang fp contract(off)
+  static_assert(HD == 16 || HD == 32, "fragment of one or two 16-byte chunks");
+  constexpr int HALF = HD / 2;
+  const int h = lane >> 5;
+  const int f0 = HD == 32 ? 8 * h : 0;  // the lane's first-half columns f0 .. f0 + 7
+  const bool valid = t < S;
+  const int tc = valid ? t : S - 1;
+  const size_t row = head_row0 + tc;
+  const bf16* xq = static_cast<const bf16*>(pro.xq);
+  float a[8], b[8], g1[8], g2[8], cs[8], sn[8];
+  if constexpr (HD == 32) {
+    const bf16x8 xa = load16(xq + row * HD + f0), xb = load16(xq + row * HD + HALF + f0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = (float)xa[e];
+      b[e] = (float)xb[e];
+    }
+  } else {
+    const bf16x8 xo = load16(xq + row * HD + 8 * h);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float own = (float)xo[e], other = xor_lanes<32>(own);
+      a[e] = h ? other : own;
+      b[e] = h ? own : other;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const f32x4 ga = *reinterpret_cast<const f32x4*>(pro.gamma_q + f0 + 4 * u);
+    const f32x4 gb = *reinterpret_cast<const f32x4*>(pro.gamma_q + HALF + f0 + 4 * u);
+    const f32x4 ca = *reinterpret_cast<const f32x4*>(pro.cos_tab + (size_t)tc * HALF + f0 + 4 * u);
+    const f32x4 sa = *reinterpret_cast<const f32x4*>(pro.sin_tab + (size_t)tc * HALF + f0 + 4 * u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      g1[4 * u + e] = ga[e];
+      g2[4 * u + e] = gb[e];
+      cs[4 * u + e] = ca[e];
+      sn[4 * u + e] = sa[e];
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += a[e] * a[e] + b[e] * b[e];
+  if constexpr (HD == 32) ss = ss + xor_lanes<32>(ss);
+  const float r = 1.0f / sqrtf(ss * (1.0f / (float)HD) + pro.eps);
+  bf16x8 y1, y2;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float n1 = a[e] * r * g1[e];
+    const float n2 = b[e] * r * g2[e];
+    y1[e] = valid ? (bf16)(n1 * cs[e] - n2 * sn[e]) : (bf16)0.f;
+    y2[e] = valid ? (bf16)(n1 * sn[e] + n2 * cs[e]) : (bf16)0.f;
+  }
+  bf16* yq = static_cast<bf16*>(pro.yq);
+  if constexpr (HD == 32) {
+    qf[0] = y1;
+    qf[1] = y2;
+    if (store && valid) {
+      store16(yq + row * HD + f0, y1);
+      store16(yq + row * HD + HALF + f0, y2);
+    }
+  } else {
+    qf[0] = h ? y2 : y1;
+    if (store && valid) store16(yq + row * HD + 8 * h, qf[0]);
+  }
+  if (store && valid && h == 0) pro.rstd_q[row] = r;
+}
+
+// Prologue backward applied in the dq / dk stores of the kernels below (bf16 io, head_dim 16
+// or 32; the arithmetic of the standalone prologue backward, Mint documentation 5.4.4 and
+// 5.5.2), so the gradient w.r.t. the rotated rows never goes to HBM.  The lane's `mul` *
+// acc is that gradient for row t of the head whose rows start at head_row0, column
+// 8 g + 4 h + j in acc[4 g + j] (g < HD / 8): both columns of every rotation pair
+// (c, c + HD / 2) are the lane's own, and the row's other columns are in lane l ^ 32.
+// Writes dx of row t (when t < S) to dx_head + t * HD, and the dgamma terms of the wave's
+// 32 rows, summed over the rows in a fixed order (rows t >= S add nothing), to partial slot
+// `slot`.  Every lane of the wave calls.
+template <int HD>
+__device__ __forceinline__ void pro_column(const f32x16& acc, float mul, const ProBwd& pb,
+                                           size_t head_row0, int t, int S,
+                                           bf16* __restrict__ dx_head, int slot, int lane) {
+  static_assert(HD == 16 || HD == 32, "one 32-column accumulator tile");
+  constexpr int NG = HD / 8, HG = NG / 2, HALF = HD / 2;
+  const int h = lane >> 5;
+  const bool valid = t < S;
+  const size_t row = head_row0 + (valid ? t : S - 1);
+  const float r = pb.rstd[row];
+  float xf[NG][4], gm[NG][4], n[NG][4];
+  f32x4 cs[HG], sn[HG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int col = 8 * g + 4 * h;
+    const bf16x4 xv = *reinterpret_cast<const bf16x4*>(pb.x + row * HD + col);
+    const f32x4 gv = *reinterpret_cast<const f32x4*>(pb.gamma + col);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xf[g][j] = (float)xv[j];
+      gm[g][j] = gv[j];
+    }
+  }
+  const size_t trow = (size_t)(valid ? t : S - 1) * HALF;
+#pragma unroll
+  for (int g = 0; g < HG; ++g) {
+    cs[g] = *reinterpret_cast<const f32x4*>(pb.cos_tab + trow + 8 * g + 4 * h);
+    sn[g] = *reinterpret_cast<const f32x4*>(pb.sin_tab + trow + 8 * g + 4 * h);
+  }
+  float dot = 0.f;
+#pragma unroll
+  for (int g = 0; g < HG; ++g)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = acc[4 * g + j] * mul, b = acc[4 * (g + HG) + j] * mul;
+      n[g][j] = a * cs[g][j] + b * sn[g][j];  // rotation by the negative angle
+      n[g + HG][j] = b * cs[g][j] - a * sn[g][j];
+      dot += gm[g][j] * n[g][j] * xf[g][j] + gm[g + HG][j] * n[g + HG][j] * xf[g + HG][j];
+    }
+  dot += xor_lanes<32>(dot);
+  const float coef = dot * r * r * r * (1.0f / (float)HD);
+  float dg[4 * NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    bf16x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[j] = (bf16)(gm[g][j] * n[g][j] * r - xf[g][j] * coef);
+      dg[4 * g + j] = valid ? n[g][j] * xf[g][j] * r : 0.f;
+    }
+    if (valid) *reinterpret_cast<bf16x4*>(dx_head + (size_t)t * HD + 8 * g + 4 * h) = o;
+  }
+  // sum over the rows (lane bits 16 .. 1): recursive halving, then the remaining bits; the
+  // lane is left with register k of its half's columns
+  int k;
+  bool writer;
+  if constexpr (NG == 4) {
+    halving_sum<16, 16, 16, 2>(dg, lane);
+    dg[0] += xor_lanes<1>(dg[0]);
+    k = 8 * ((lane >> 4) & 1) + 4 * ((lane >> 3) & 1) + 2 * ((lane >> 2) & 1) + ((lane >> 1) & 1);
+    writer = (lane & 1) == 0;
+  } else {
+    halving_sum<8, 8, 16, 4>(dg, lane);
+    dg[0] += xor_lanes<2>(dg[0]);
+    dg[0] += xor_lanes<1>(dg[0]);
+    k = 4 * ((lane >> 4) & 1) + 2 * ((lane >> 3) & 1) + ((lane >> 2) & 1);
+    writer = (lane & 3) == 0;
+  }
+  if (writer) pb.partials[(size_t)(8 * (k >> 2) + 4 * h + (k & 3)) * pb.nparts + slot] = dg[0];
+}
+
 // Packed documents (block-causal mask): first / last row of row i's document, clamped into
 // the sequence (so a bad array gives wrong values but no access outside the tensors);
 // without documents 0 and S - 1.
@@ -196,14 +358,15 @@ constexpr int kBlockN = 64;           // keys per LDS stage in forward / dq
 // --------------------------------------------------------------------------------------
 // forward: one workgroup per (batch*head, 128-query tile); 4 waves x 32 queries.
 // --------------------------------------------------------------------------------------
-template <typename T, int HD>
+template <typename T, int HD, bool QPRO>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ q,
                                                        const T* __restrict__ k,
                                                        const T* __restrict__ v,
                                                        T* __restrict__ out,
                                                        float* __restrict__ lse, int S, int H,
                                                        int Hkv, float scale_log2,
-                                                       const int* __restrict__ seg_lo) {
+                                                       const int* __restrict__ seg_lo,
+                                                       QProFuse pro) {
   using C = Tile<T, HD>;
   __shared__ __attribute__((aligned(16))) T ks[kBlockN * C::LDS_ROW];
   __shared__ __attribute__((aligned(16))) T vs[kBlockN * C::LDS_ROW];
@@ -220,7 +383,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ q,
   const int qrow = qw0 + c32;
 
   vec16_t<T> qf[C::NCH];
-  load_fragment<T, HD>(qf, qp, qrow, S, h);
+  if constexpr (QPRO) q_prologue_frag<HD>(qf, pro, (size_t)bh * S, qrow, S, true, lane);
+  else load_fragment<T, HD>(qf, qp, qrow, S, h);
   f32x16 o[C::NDT];
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt) o[dt] = zero16();
@@ -297,12 +461,12 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ q,
 // backward, dq: one workgroup per (batch*head, 128-query tile); also writes
 // delta_i = dO_i . out_i for the dk/dv kernel.
 // --------------------------------------------------------------------------------------
-template <typename T, int HD, typename TG>
+template <typename T, int HD, typename TG, bool PRO>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ out, const T* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ delta, TG* __restrict__ dq, int S, int H, int Hkv, float scale_log2,
-    float scale, const int* __restrict__ seg_lo) {
+    float scale, const int* __restrict__ seg_lo, ProBwd pro) {
   using C = Tile<T, HD>;
   __shared__ __attribute__((aligned(16))) T ks[kBlockN * C::LDS_ROW];
   __shared__ __attribute__((aligned(16))) T vs[kBlockN * C::LDS_ROW];
@@ -381,7 +545,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
       accumulate_transposed<T, HD>(acc, ks, 32 * s, dsv, lane);  // dQ^T += K^T dS^T
     }
   }
-  if (qrow < S) store_column<TG, HD, C::NDT>(dq + ((size_t)bh * S + qrow) * HD, acc, scale, h);
+  if constexpr (PRO) {  // one dgamma slot per wave
+    static_assert(std::is_same<TG, bf16>::value, "dx in the io dtype");
+    pro_column<HD>(acc[0], scale, pro, (size_t)bh * S, qrow, S, dq + head_off,
+                   (blockIdx.x * gridDim.y + blockIdx.y) * kWaves + w, lane);
+  } else if (qrow < S) {
+    store_column<TG, HD, C::NDT>(dq + ((size_t)bh * S + qrow) * HD, acc, scale, h);
+  }
 }
 
 // --------------------------------------------------------------------------------------
@@ -424,14 +594,15 @@ struct SplitStager {
   }
 };
 
-template <typename T, int HD>
+template <typename T, int HD, bool QPRO>
 __global__ __launch_bounds__(256) void attn_fwd_split_kernel(const T* __restrict__ q,
                                                              const T* __restrict__ k,
                                                              const T* __restrict__ v,
                                                              T* __restrict__ out,
                                                              float* __restrict__ lse, int S,
                                                              int H, int Hkv, float scale_log2,
-                                                             const int* __restrict__ seg_lo) {
+                                                             const int* __restrict__ seg_lo,
+                                                             QProFuse pro) {
   using C = Tile<T, HD>;
   using L = SplitLds<T, HD>;
   __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
@@ -448,7 +619,10 @@ __global__ __launch_bounds__(256) void attn_fwd_split_kernel(const T* __restrict
   T* vs = ks + L::TILE;
 
   vec16_t<T> qf[C::NCH];
-  load_fragment<T, HD>(qf, q + (size_t)bh * S * HD, qrow, S, h);
+  if constexpr (QPRO)  // the four waves share the rows; wave 0 stores them
+    q_prologue_frag<HD>(qf, pro, (size_t)bh * S, qrow, S, w == 0, lane);
+  else
+    load_fragment<T, HD>(qf, q + (size_t)bh * S * HD, qrow, S, h);
   f32x16 o[C::NDT];
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt) o[dt] = zero16();
@@ -535,12 +709,12 @@ __global__ __launch_bounds__(256) void attn_fwd_split_kernel(const T* __restrict
   }
 }
 
-template <typename T, int HD, typename TG>
+template <typename T, int HD, typename TG, bool PRO>
 __global__ __launch_bounds__(256) void attn_bwd_dq_split_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ out, const T* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ delta, TG* __restrict__ dq, int S, int H, int Hkv, float scale_log2,
-    float scale, const int* __restrict__ seg_lo) {
+    float scale, const int* __restrict__ seg_lo, ProBwd pro) {
   using C = Tile<T, HD>;
   using L = SplitLds<T, HD>;
   __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
@@ -623,7 +797,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_split_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[dt][i] += src[16 * dt + i];
   }
-  if (qrow < S) store_column<TG, HD, C::NDT>(dq + ((size_t)bh * S + qrow) * HD, acc, scale, h);
+  if constexpr (PRO) {  // one dgamma slot per workgroup (wave 0 holds its 32 rows)
+    static_assert(std::is_same<TG, bf16>::value, "dx in the io dtype");
+    pro_column<HD>(acc[0], scale, pro, (size_t)bh * S, qrow, S, dq + head_off,
+                   blockIdx.x * gridDim.y + blockIdx.y, lane);
+  } else if (qrow < S) {
+    store_column<TG, HD, C::NDT>(dq + ((size_t)bh * S + qrow) * HD, acc, scale, h);
+  }
 }
 
 // The split kernels serve shapes whose 128-query workgroups would not cover the CUs.
@@ -648,13 +828,13 @@ constexpr int dkdv_waves(int qs) { return qs > kWaves ? qs : kWaves; }
 // z*group/gsplit .. (z+1)*group/gsplit - 1, ascending) and each workgroup writes its fp32
 // partial dK (unscaled) and dV to part instead of dk / dv; dkdv_group_sum_kernel then adds
 // the gsplit partials in z order.
-template <typename T, int HD, typename TG, int QS>
+template <typename T, int HD, typename TG, int QS, bool PRO>
 __global__ __launch_bounds__(64 * dkdv_waves(QS)) void attn_bwd_dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, TG* __restrict__ dk, T* __restrict__ dv, int S, int H,
     int Hkv, float scale_log2, float scale, const int* __restrict__ seg_hi, int gsplit,
-    float* __restrict__ part) {
+    float* __restrict__ part, ProBwd pro) {
   using C = Tile<T, HD>;
   constexpr int KW = dkdv_waves(QS) / QS;
   constexpr int BNK = 32 * KW;
@@ -800,7 +980,14 @@ __global__ __launch_bounds__(64 * dkdv_waves(QS)) void attn_bwd_dkdv_kernel(
       }
     }
   }
-  if (sp == 0 && key < S) {
+  if constexpr (PRO) {  // no group split; one dgamma slot per wave of keys
+    static_assert(std::is_same<TG, bf16>::value, "dx in the io dtype");
+    if (sp == 0) {
+      pro_column<HD>(dkt[0], scale, pro, (size_t)kvbh * S, key, S, dk + (size_t)kvbh * S * HD,
+                     (blockIdx.x * gridDim.y + blockIdx.y) * KW + kw, lane);
+      if (key < S) store_column<T, HD, C::NDT>(dv + ((size_t)kvbh * S + key) * HD, dvt, 1.0f, h);
+    }
+  } else if (sp == 0 && key < S) {
     if (part != nullptr) {  // group split: fp32 partials, dK unscaled
       const size_t per = (size_t)gridDim.x * S * HD;  // one partial tensor
       float* pk = part + (size_t)blockIdx.z * 2 * per + ((size_t)kvbh * S + key) * HD;
@@ -845,31 +1032,41 @@ __global__ __launch_bounds__(256) void dkdv_group_sum_kernel(const float* __rest
 // --------------------------------------------------------------------------------------
 static inline float scale_of(int hd) { return 1.0f / sqrtf((float)hd); }
 
-template <typename T, int HD>
+// With QPRO the Q side of the prologue runs in the kernel (q unused; pro's rows are read,
+// and yq / rstd_q written, instead).
+template <typename T, int HD, bool QPRO>
 static hipError_t fwd_impl(const AttnShape& s, const void* q, const void* k, const void* v,
-                           void* out, float* lse, hipStream_t stream) {
+                           void* out, float* lse, const QProFuse& pro, hipStream_t stream) {
   ProfScope prof("attn_fwd", stream);
   if (use_split(s)) {
     const dim3 grid(s.batch * s.num_heads, (s.seq_len + kSplitM - 1) / kSplitM);
-    hipLaunchKernelGGL((attn_fwd_split_kernel<T, HD>), grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((attn_fwd_split_kernel<T, HD, QPRO>), grid, dim3(256), 0, stream,
                        (const T*)q, (const T*)k, (const T*)v, (T*)out, lse, s.seq_len,
-                       s.num_heads, s.num_kv_heads, scale_of(HD) * kLog2e, s.seg_lo);
+                       s.num_heads, s.num_kv_heads, scale_of(HD) * kLog2e, s.seg_lo, pro);
     return hipPeekAtLastError();
   }
   const dim3 grid(s.batch * s.num_heads, (s.seq_len + kBlockM - 1) / kBlockM);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(256), 0, stream, (const T*)q,
+  hipLaunchKernelGGL((attn_fwd_kernel<T, HD, QPRO>), grid, dim3(256), 0, stream, (const T*)q,
                      (const T*)k, (const T*)v, (T*)out, lse, s.seq_len, s.num_heads,
-                     s.num_kv_heads, scale_of(HD) * kLog2e, s.seg_lo);
+                     s.num_kv_heads, scale_of(HD) * kLog2e, s.seg_lo, pro);
   return hipPeekAtLastError();
 }
 
 hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const void* k,
-                           const void* v, void* out, float* lse, hipStream_t stream) {
+                           const void* v, void* out, float* lse, const QProFuse* pro,
+                           hipStream_t stream) {
   // bf16 at head_dim 64 / 128 always runs the attn_bf16.hip kernels
   if (io == IO_BF16 && fast_bf16_supported(s.head_dim))
-    return launch_attn_fwd_bf16_fast(s, q, k, v, out, lse, nullptr, stream);
+    return launch_attn_fwd_bf16_fast(s, q, k, v, out, lse, pro, stream);
+  if (pro != nullptr) {  // bf16, head_dim 16 / 32 only
+    if (io != IO_BF16) return hipErrorInvalidValue;
+    if (s.head_dim == 16) return fwd_impl<bf16, 16, true>(s, nullptr, k, v, out, lse, *pro, stream);
+    if (s.head_dim == 32) return fwd_impl<bf16, 32, true>(s, nullptr, k, v, out, lse, *pro, stream);
+    return hipErrorInvalidValue;
+  }
+  const QProFuse none{};
 #define XATTN_CASE(T, HD) \
-  if (s.head_dim == HD) return fwd_impl<T, HD>(s, q, k, v, out, lse, stream);
+  if (s.head_dim == HD) return fwd_impl<T, HD, false>(s, q, k, v, out, lse, none, stream);
   if (io == IO_F32) {
     XATTN_CASE(float, 16) XATTN_CASE(float, 32) XATTN_CASE(float, 64) XATTN_CASE(float, 128)
   } else {
@@ -909,20 +1106,22 @@ static int dkdv_gsplit(const AttnShape& s) {
   return (int)std::min<long long>(group, (256 + blocks - 1) / blocks);
 }
 
-template <typename T, int HD, typename TG, int QS>
+// dk/dv launch; with `pro` (only where dkdv_gsplit is 1) the K side's prologue backward is
+// applied in the dk stores.
+template <typename T, int HD, typename TG, int QS, bool PRO>
 static void launch_dkdv(const AttnShape& s, const void* q, const void* k, const void* v,
                         const void* dout, const float* lse, const float* delta, void* dk,
-                        void* dv, float* part, hipStream_t stream) {
+                        void* dv, float* part, const ProBwd& pro, hipStream_t stream) {
   constexpr int BNK = 32 * (dkdv_waves(QS) / QS);
-  const int gs = dkdv_gsplit<QS>(s);
+  const int gs = PRO ? 1 : dkdv_gsplit<QS>(s);
   const dim3 grid(s.batch * s.num_kv_heads, (s.seq_len + BNK - 1) / BNK, gs);
   ProfScope prof("attn_bwd_dkdv", stream);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD, TG, QS>), grid, dim3(64 * dkdv_waves(QS)), 0,
-                     stream,
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD, TG, QS, PRO>), grid,
+                     dim3(64 * dkdv_waves(QS)), 0, stream,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, delta,
                      (TG*)dk, (T*)dv, s.seq_len, s.num_heads, s.num_kv_heads,
                      scale_of(HD) * kLog2e, scale_of(HD), s.seg_hi, gs,
-                     gs > 1 ? part : nullptr);
+                     gs > 1 ? part : nullptr, pro);
   if (gs > 1) {
     const size_t n = (size_t)s.batch * s.num_kv_heads * s.seq_len * HD;
     hipLaunchKernelGGL((dkdv_group_sum_kernel<T, TG>), dim3((unsigned)((n / 4 + 255) / 256)),
@@ -931,52 +1130,103 @@ static void launch_dkdv(const AttnShape& s, const void* q, const void* k, const 
   }
 }
 
-template <typename T, int HD, typename TG>
-static hipError_t bwd_impl(const AttnShape& s, const void* q, const void* k, const void* v,
-                           const void* out, const float* lse, const void* dout, void* dq,
-                           void* dk, void* dv, float* delta, float* part, hipStream_t stream) {
+// The dk/dv kernel's query splits (QS) and group splits for a shape.
+template <typename T, int HD>
+static void dkdv_plan(const AttnShape& s, int* qs, int* gs) {
+  *qs = dkdv_splits<T, HD>(s);
+  switch (*qs) {
+    case 1: *gs = dkdv_gsplit<1>(s); break;
+    case 2: *gs = dkdv_gsplit<2>(s); break;
+    case 8: *gs = dkdv_gsplit<8>(s); break;
+    default: *gs = dkdv_gsplit<4>(s); break;
+  }
+}
+
+template <typename T, int HD, typename TG, bool PRO>
+static hipError_t bwd_run(const AttnShape& s, const void* q, const void* k, const void* v,
+                          const void* out, const float* lse, const void* dout, void* dq,
+                          void* dk, void* dv, float* delta, float* part, const ProBwd& pq,
+                          const ProBwd& pk, hipStream_t stream) {
   {
     ProfScope prof("attn_bwd_dq", stream);
     if (use_split(s)) {
       const dim3 grid(s.batch * s.num_heads, (s.seq_len + kSplitM - 1) / kSplitM);
-      hipLaunchKernelGGL((attn_bwd_dq_split_kernel<T, HD, TG>), grid, dim3(256), 0, stream,
+      hipLaunchKernelGGL((attn_bwd_dq_split_kernel<T, HD, TG, PRO>), grid, dim3(256), 0, stream,
                          (const T*)q, (const T*)k, (const T*)v, (const T*)out,
                          (const T*)dout, lse, delta, (TG*)dq, s.seq_len, s.num_heads,
-                         s.num_kv_heads, scale_of(HD) * kLog2e, scale_of(HD), s.seg_lo);
+                         s.num_kv_heads, scale_of(HD) * kLog2e, scale_of(HD), s.seg_lo, pq);
     } else {
       const dim3 grid(s.batch * s.num_heads, (s.seq_len + kBlockM - 1) / kBlockM);
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD, TG>), grid, dim3(256), 0, stream,
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD, TG, PRO>), grid, dim3(256), 0, stream,
                          (const T*)q, (const T*)k, (const T*)v, (const T*)out,
                          (const T*)dout, lse, delta, (TG*)dq, s.seq_len, s.num_heads,
-                         s.num_kv_heads, scale_of(HD) * kLog2e, scale_of(HD), s.seg_lo);
+                         s.num_kv_heads, scale_of(HD) * kLog2e, scale_of(HD), s.seg_lo, pq);
     }
   }
   hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess) return e;
-  switch (dkdv_splits<T, HD>(s)) {
-    case 1: launch_dkdv<T, HD, TG, 1>(s, q, k, v, dout, lse, delta, dk, dv, part, stream); break;
-    case 2: launch_dkdv<T, HD, TG, 2>(s, q, k, v, dout, lse, delta, dk, dv, part, stream); break;
+  int qs, gs;
+  dkdv_plan<T, HD>(s, &qs, &gs);
+  if (PRO && gs != 1) return hipErrorInvalidValue;
+  switch (qs) {
+    case 1:
+      launch_dkdv<T, HD, TG, 1, PRO>(s, q, k, v, dout, lse, delta, dk, dv, part, pk, stream);
+      break;
+    case 2:
+      launch_dkdv<T, HD, TG, 2, PRO>(s, q, k, v, dout, lse, delta, dk, dv, part, pk, stream);
+      break;
     case 8:
       if constexpr (2 * 8 * (size_t)kBlockMQ * Tile<T, HD>::LDS_ROW * sizeof(T) <= 144 * 1024) {
-        launch_dkdv<T, HD, TG, 8>(s, q, k, v, dout, lse, delta, dk, dv, part, stream);
+        launch_dkdv<T, HD, TG, 8, PRO>(s, q, k, v, dout, lse, delta, dk, dv, part, pk, stream);
         break;
       }
       [[fallthrough]];
-    default: launch_dkdv<T, HD, TG, 4>(s, q, k, v, dout, lse, delta, dk, dv, part, stream); break;
+    default:
+      launch_dkdv<T, HD, TG, 4, PRO>(s, q, k, v, dout, lse, delta, dk, dv, part, pk, stream);
+      break;
   }
   return hipPeekAtLastError();
 }
 
+template <typename T, int HD, typename TG>
+static hipError_t bwd_impl(const AttnShape& s, const void* q, const void* k, const void* v,
+                           const void* out, const float* lse, const void* dout, void* dq,
+                           void* dk, void* dv, float* delta, float* part, hipStream_t stream) {
+  const ProBwd none{};
+  return bwd_run<T, HD, TG, false>(s, q, k, v, out, lse, dout, dq, dk, dv, delta, part, none,
+                                   none, stream);
+}
+
 template <typename T, int HD>
 static size_t dkdv_partial_floats_impl(const AttnShape& s) {
-  int gs = 1;
-  switch (dkdv_splits<T, HD>(s)) {
-    case 1: gs = dkdv_gsplit<1>(s); break;
-    case 2: gs = dkdv_gsplit<2>(s); break;
-    case 8: gs = dkdv_gsplit<8>(s); break;
-    default: gs = dkdv_gsplit<4>(s); break;
-  }
+  int qs, gs;
+  dkdv_plan<T, HD>(s, &qs, &gs);
   return gs > 1 ? 2 * (size_t)gs * s.batch * s.num_kv_heads * s.seq_len * HD : 0;
+}
+
+// Partial slots of the fused prologue backward in the kernels above: one per dq wave (four
+// per 128-query workgroup, or one per 32-query workgroup of the split kernel) and one per
+// final dk wave (KW per key block).  False where the shape runs unfused: a dk/dv launch that
+// splits the group's query heads over workgroups.
+template <typename T, int HD>
+static bool generic_pro_parts_impl(const AttnShape& s, int* nq, int* nk) {
+  int qs, gs;
+  dkdv_plan<T, HD>(s, &qs, &gs);
+  if (gs != 1) return false;
+  const int bh = s.batch * s.num_heads;
+  *nq = use_split(s) ? bh * ((s.seq_len + kSplitM - 1) / kSplitM)
+                     : bh * ((s.seq_len + kBlockM - 1) / kBlockM) * kWaves;
+  const int kw = dkdv_waves(qs) / qs, bnk = 32 * kw;
+  *nk = s.batch * s.num_kv_heads * ((s.seq_len + bnk - 1) / bnk) * kw;
+  return true;
+}
+
+bool generic_pro_parts(IoType io, const AttnShape& s, int* nq, int* nk) {
+  *nq = *nk = 0;
+  if (io != IO_BF16) return false;
+  if (s.head_dim == 16) return generic_pro_parts_impl<bf16, 16>(s, nq, nk);
+  if (s.head_dim == 32) return generic_pro_parts_impl<bf16, 32>(s, nq, nk);
+  return false;
 }
 
 size_t dkdv_partial_floats(IoType io, const AttnShape& s) {
@@ -995,13 +1245,31 @@ size_t dkdv_partial_floats(IoType io, const AttnShape& s) {
 hipError_t launch_attn_bwd(IoType io, const AttnShape& s, const void* q, const void* k,
                            const void* v, const void* out, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, float* delta,
-                           float* lse2, bool grads_f32, float* dkdv_part, hipStream_t stream) {
+                           float* lse2, bool grads_f32, float* dkdv_part, const ProFuse* pro,
+                           hipStream_t stream) {
   // bf16 at head_dim 64 / 128 always runs the attn_bf16.hip kernels (with fp32 gradients
   // never requested there: that path applies the prologue backward in its own stores)
   if (io == IO_BF16 && fast_bf16_supported(s.head_dim)) {
-    if (grads_f32) return hipErrorInvalidValue;
+    if (grads_f32 || pro != nullptr) return hipErrorInvalidValue;
     return launch_attn_bwd_bf16_fast(s, q, k, v, out, lse, dout, dq, dk, dv, delta, lse2,
                                      nullptr, stream);
+  }
+  if (pro != nullptr) {  // bf16, head_dim 16 / 32: the prologue backward in the stores
+    int nq, nk;
+    if (grads_f32 || !generic_pro_parts(io, s, &nq, &nk)) return hipErrorInvalidValue;
+    const ProBwd pq{static_cast<const bf16*>(pro->xq), pro->gamma_q, pro->rstd_q,
+                    pro->cos_tab, pro->sin_tab, pro->partials_q, nq};
+    const ProBwd pk{static_cast<const bf16*>(pro->xk), pro->gamma_k, pro->rstd_k,
+                    pro->cos_tab, pro->sin_tab, pro->partials_k, nk};
+    const hipError_t e =
+        s.head_dim == 16
+            ? bwd_run<bf16, 16, bf16, true>(s, q, k, v, out, lse, dout, dq, dk, dv, delta,
+                                            nullptr, pq, pk, stream)
+            : bwd_run<bf16, 32, bf16, true>(s, q, k, v, out, lse, dout, dq, dk, dv, delta,
+                                            nullptr, pq, pk, stream);
+    if (e != hipSuccess) return e;
+    return launch_dgamma_reduce_qk(s.head_dim, pro->partials_q, nq, pro->dgamma_q,
+                                   pro->partials_k, nk, pro->dgamma_k, stream);
   }
 #define XATTN_CASE(T, HD, TG)                                                          \
   if (s.head_dim == HD)                                                                \

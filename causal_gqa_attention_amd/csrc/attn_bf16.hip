@@ -299,16 +299,6 @@ __device__ __forceinline__ void store_col(TO* dst, const f32x16 (&acc)[HD / 32],
 // the row sum over the HD/16 lanes.  The dgamma terms of a workgroup's rows are summed in
 // a fixed order into one partial slot per workgroup, reduced by a separate launch.
 // ---------------------------------------------------------------------------------------
-struct ProBwd {
-  const bf16* x;         // pre-norm rows, indexed like the gradient ([rows, S, HD])
-  const float* gamma;    // [HD]
-  const float* rstd;     // [rows * S], from the prologue forward
-  const float* cos_tab;  // [S, HD / 2]
-  const float* sin_tab;  // [S, HD / 2]
-  float* partials;       // [HD][nparts] column-major, one slot per workgroup
-  int nparts;
-};
-
 // LDS tile of fp32 rows of HD: row r, 16-byte chunk c at chunk position c ^ (r & 15)
 // (the rows a b128 access phase touches fall on distinct bank groups).
 template <int HD>
@@ -331,23 +321,6 @@ __device__ __forceinline__ void acc_to_tile(float* tile, const f32x16 (&acc)[HD 
       for (int j = 0; j < 4; ++j) o[j] = acc[dt][4 * g + j] * mul;
       *epi_chunk<HD>(tile, c32, 8 * dt + 2 * g + h) = o;
     }
-}
-
-// Sums v[0..N) over the lanes that differ in lane bits M, M/2, .., MLAST by recursive
-// halving: at the step for bit m the lane keeps one half of its remaining values (the upper
-// one if its bit m is set), sends the other half to lane ^ m and adds what that lane sends.
-// Fixed order, so bitwise reproducible.
-template <int NV, int N, int M, int MLAST>
-__device__ __forceinline__ void halving_sum(float (&v)[NV], int lane) {
-  constexpr int H = N / 2;
-  const bool up = (lane & M) != 0;
-#pragma unroll
-  for (int k = 0; k < H; ++k) {
-    const float keep = up ? v[k + H] : v[k];
-    const float send = up ? v[k] : v[k + H];
-    v[k] = keep + xor_lanes<M>(send);
-  }
-  if constexpr (M > MLAST) halving_sum<NV, H, M / 2, MLAST>(v, lane);
 }
 
 // s_waitcnt lgkmcnt(0) + workgroup barrier + LDS acquire; outstanding global stores are

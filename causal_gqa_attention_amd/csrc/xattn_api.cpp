@@ -158,6 +158,12 @@ bool fused_prologue_bwd(const DimsChecked& c) {
   return c.io == xattn::IO_BF16 && xattn::fast_bf16_supported(c.s.head_dim);
 }
 
+// So do the generic bf16 kernels (head_dim 16 / 32) where the dk/dv launch does not split
+// the group's query heads; nq / nk: their dgamma partial slots.
+bool generic_fused_prologue_bwd(const DimsChecked& c, int* nq, int* nk) {
+  return xattn::generic_pro_parts(c.io, c.s, nq, nk);
+}
+
 size_t bwd_workspace(const DimsChecked& c, bool with_prologue) {
   size_t n = 2 * align256((size_t)c.rows_q * sizeof(float));  // delta, lse * log2(e)
   n += align256(xattn::dkdv_partial_floats(c.io, c.s) * sizeof(float));  // group-split dk/dv
@@ -167,6 +173,9 @@ size_t bwd_workspace(const DimsChecked& c, bool with_prologue) {
     const size_t col = (size_t)c.s.head_dim * sizeof(float);  // dgamma partials per slot
     n += align256((size_t)xattn::fused_pro_parts_q(hq, c.s.seq_len) * col);
     n += align256((size_t)xattn::fused_pro_parts_k(hk, c.s.seq_len) * col);
+  } else if (int nq, nk; with_prologue && generic_fused_prologue_bwd(c, &nq, &nk)) {
+    const size_t col = (size_t)c.s.head_dim * sizeof(float);
+    n += align256((size_t)nq * col) + align256((size_t)nk * col);
   } else if (with_prologue) {
     const int64_t rows_k = (int64_t)c.s.batch * c.s.num_kv_heads * c.s.seq_len;
     n += align256((size_t)c.q_elems * sizeof(float));      // dq w.r.t. the rotated q
@@ -605,7 +614,7 @@ xattn_status xattn_fwd(const xattn_dims* dims, const void* q, const void* k, con
     check_no_overlap({{out, qb, "out"}, {lse, (size_t)c.rows_q * 4, "lse"}},
                      {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, seg_lo_range(c),
                       seg_hi_range(c)});
-    hip_check(xattn::launch_attn_fwd(c.io, c.s, q, k, v, out, lse, (hipStream_t)stream),
+    hip_check(xattn::launch_attn_fwd(c.io, c.s, q, k, v, out, lse, nullptr, (hipStream_t)stream),
               "attention forward launch");
   });
 }
@@ -633,11 +642,11 @@ xattn_status xattn_fwd_qnorm(const xattn_dims* dims, const xattn_fwd_prologue* p
                       {pro->cos_tab, tb, "pro->cos_tab"}, {pro->sin_tab, tb, "pro->sin_tab"},
                       {k, kb, "k"}, {v, kb, "v"}, seg_lo_range(c), seg_hi_range(c)});
     const hipStream_t st = (hipStream_t)stream;
-    if (c.io == xattn::IO_BF16 && xattn::fast_bf16_supported(c.s.head_dim)) {
+    if (c.io == xattn::IO_BF16) {  // every bf16 head_dim: one pass
       xattn::QProFuse pf;
       pf.xq = pro->xq, pf.gamma_q = pro->gamma_q, pf.cos_tab = pro->cos_tab;
       pf.sin_tab = pro->sin_tab, pf.yq = pro->yq, pf.rstd_q = pro->rstd_q, pf.eps = pro->eps;
-      hip_check(xattn::launch_attn_fwd_bf16_fast(c.s, nullptr, k, v, out, lse, &pf, st),
+      hip_check(xattn::launch_attn_fwd(c.io, c.s, nullptr, k, v, out, lse, &pf, st),
                 "attention forward launch");
       return;
     }
@@ -645,7 +654,7 @@ xattn_status xattn_fwd_qnorm(const xattn_dims* dims, const xattn_fwd_prologue* p
                                             pro->cos_tab, pro->sin_tab, pro->yq, pro->rstd_q,
                                             (int)c.rows_q, c.s.seq_len, pro->eps, st),
               "prologue forward launch");
-    hip_check(xattn::launch_attn_fwd(c.io, c.s, pro->yq, k, v, out, lse, st),
+    hip_check(xattn::launch_attn_fwd(c.io, c.s, pro->yq, k, v, out, lse, nullptr, st),
               "attention forward launch");
   });
 }
@@ -940,16 +949,16 @@ xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, con
     const hipStream_t st = (hipStream_t)stream;
     if (pro == nullptr) {
       hip_check(xattn::launch_attn_bwd(c.io, c.s, q, k, v, out, lse, dout, dq, dk, dv, delta,
-                                       lse2, false, dkdv_part, st),
+                                       lse2, false, dkdv_part, nullptr, st),
                 "attention backward launch");
       return;
     }
+    xattn::ProFuse pf;
+    pf.xq = pro->xq, pf.xk = pro->xk, pf.gamma_q = pro->gamma_q, pf.gamma_k = pro->gamma_k;
+    pf.rstd_q = pro->rstd_q, pf.rstd_k = pro->rstd_k;
+    pf.cos_tab = pro->cos_tab, pf.sin_tab = pro->sin_tab;
+    pf.dgamma_q = pro->dgamma_q, pf.dgamma_k = pro->dgamma_k;
     if (fused_prologue_bwd(c)) {
-      xattn::ProFuse pf;
-      pf.xq = pro->xq, pf.xk = pro->xk, pf.gamma_q = pro->gamma_q, pf.gamma_k = pro->gamma_k;
-      pf.rstd_q = pro->rstd_q, pf.rstd_k = pro->rstd_k;
-      pf.cos_tab = pro->cos_tab, pf.sin_tab = pro->sin_tab;
-      pf.dgamma_q = pro->dgamma_q, pf.dgamma_k = pro->dgamma_k;
       const int64_t hq = (int64_t)c.s.batch * c.s.num_heads;
       pf.partials_q = reinterpret_cast<float*>(ws);
       ws += align256((size_t)xattn::fused_pro_parts_q(hq, c.s.seq_len) * c.s.head_dim *
@@ -957,6 +966,15 @@ xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, con
       pf.partials_k = reinterpret_cast<float*>(ws);
       hip_check(xattn::launch_attn_bwd_bf16_fast(c.s, q, k, v, out, lse, dout, dq, dk, dv,
                                                  delta, lse2, &pf, st),
+                "attention backward launch");
+      return;
+    }
+    if (int nq, nk; generic_fused_prologue_bwd(c, &nq, &nk)) {
+      pf.partials_q = reinterpret_cast<float*>(ws);
+      ws += align256((size_t)nq * c.s.head_dim * sizeof(float));
+      pf.partials_k = reinterpret_cast<float*>(ws);
+      hip_check(xattn::launch_attn_bwd(c.io, c.s, q, k, v, out, lse, dout, dq, dk, dv, delta,
+                                       lse2, false, dkdv_part, &pf, st),
                 "attention backward launch");
       return;
     }
@@ -968,7 +986,7 @@ xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, con
     ws += align256((size_t)xattn::qknorm_rope_bwd_blocks(c.rows_q) * c.s.head_dim * sizeof(float));
     float* part_k = reinterpret_cast<float*>(ws);
     hip_check(xattn::launch_attn_bwd(c.io, c.s, q, k, v, out, lse, dout, dyq, dyk, dv, delta,
-                                     lse2, true, dkdv_part, st),
+                                     lse2, true, dkdv_part, nullptr, st),
               "attention backward launch");
     hip_check(xattn::launch_qknorm_rope_bwd_qk(
                   xattn::IO_F32, c.io, c.s.head_dim, dyq, pro->xq, pro->gamma_q, pro->rstd_q, dq,

@@ -140,4 +140,34 @@ __device__ __forceinline__ float xor_sum_down(float v) {
   else return v;
 }
 
+// Sums v[0..N) over the lanes that differ in lane bits M, M/2, .., MLAST by recursive
+// halving: at the step for bit m the lane keeps one half of its remaining values (the upper
+// one if its bit m is set), sends the other half to lane ^ m and adds what that lane sends.
+// Fixed order, so bitwise reproducible.
+template <int NV, int N, int M, int MLAST>
+__device__ __forceinline__ void halving_sum(float (&v)[NV], int lane) {
+  constexpr int H = N / 2;
+  const bool up = (lane & M) != 0;
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const float keep = up ? v[k + H] : v[k];
+    const float send = up ? v[k] : v[k + H];
+    v[k] = keep + xor_lanes<M>(send);
+  }
+  if constexpr (M > MLAST) halving_sum<NV, H, M / 2, MLAST>(v, lane);
+}
+
+// Inputs and dgamma output of a prologue backward applied in an attention kernel's dq / dk
+// stores (bf16 io): the gradient w.r.t. the rotated rows stays in the kernel, and the
+// dgamma terms of each workgroup (or wave) go to one partial slot, reduced by a later launch.
+struct ProBwd {
+  const bf16* x;         // pre-norm rows, indexed like the gradient ([rows, S, HD])
+  const float* gamma;    // [HD]
+  const float* rstd;     // [rows * S], from the prologue forward
+  const float* cos_tab;  // [S, HD / 2]
+  const float* sin_tab;  // [S, HD / 2]
+  float* partials;       // [HD][nparts] column-major, one slot per workgroup or wave
+  int nparts;
+};
+
 }  // namespace xattn

@@ -72,8 +72,6 @@ struct AttnShape {
   const int* seg_hi = nullptr;
 };
 
-hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const void* k,
-                           const void* v, void* out, float* lse, hipStream_t stream);
 
 // gfx950 fast path (bf16 io, head_dim 64 or 128), attn_bf16.hip.  The backward also
 // writes -lse * log2(e) and -D (D = dO . out) per query row (workspace) for its dk/dv kernel.
@@ -91,6 +89,11 @@ struct QProFuse {
 hipError_t launch_attn_fwd_bf16_fast(const AttnShape& s, const void* q, const void* k,
                                      const void* v, void* out, float* lse,
                                      const QProFuse* pro, hipStream_t stream);
+// Any io / head_dim.  `pro` (bf16 only; q unused) as for launch_attn_fwd_bf16_fast: the Q
+// side of the prologue runs inside the forward, at head_dim 16 / 32 too.
+hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const void* k,
+                           const void* v, void* out, float* lse, const QProFuse* pro,
+                           hipStream_t stream);
 //
 // With `pro` non-null the prologue backward is applied in the dq and dk stores: dq, dk
 // receive the gradients w.r.t. the raw xq, xk (io dtype) and dgamma_q, dgamma_k are
@@ -110,16 +113,23 @@ hipError_t launch_attn_bwd_bf16_fast(const AttnShape& s, const void* q, const vo
                                      float* delta, float* lse2, const ProFuse* pro,
                                      hipStream_t stream);
 
-// grads_f32: when true, dq and dk are written as fp32 (used when the prologue backward
-// follows inside xattn_bwd); otherwise in the io dtype.  dv is always in the io dtype.
-// dkdv_part: fp32 scratch of dkdv_partial_floats(io, s) floats (the generic dk/dv kernel
-// splits the group's query heads over workgroups for shapes with few key blocks; NULL when
-// that is 0).
+// grads_f32: when true, dq and dk are written as fp32 (used when the standalone prologue
+// backward follows inside xattn_bwd); otherwise in the io dtype.  dv is always in the io
+// dtype.  dkdv_part: fp32 scratch of dkdv_partial_floats(io, s) floats (the generic dk/dv
+// kernel splits the group's query heads over workgroups for shapes with few key blocks; NULL
+// when that is 0).  pro (only where generic_pro_parts(io, s) holds; grads_f32 false): the
+// prologue backward is applied in the dq and dk stores as in launch_attn_bwd_bf16_fast, with
+// generic_pro_parts' nq / nk partial slots of head_dim floats in partials_q / partials_k.
 hipError_t launch_attn_bwd(IoType io, const AttnShape& s, const void* q, const void* k,
                            const void* v, const void* out, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, float* delta,
-                           float* lse2, bool grads_f32, float* dkdv_part, hipStream_t stream);
+                           float* lse2, bool grads_f32, float* dkdv_part, const ProFuse* pro,
+                           hipStream_t stream);
 size_t dkdv_partial_floats(IoType io, const AttnShape& s);
+// Whether the generic kernels (bf16, head_dim 16 / 32) apply the prologue backward in their
+// stores for this shape (not where the dk/dv launch splits the group's query heads), and
+// their dgamma partial slot counts.
+bool generic_pro_parts(IoType io, const AttnShape& s, int* nq, int* nk);
 
 // ---- KV-cache decode (decode.hip) ---------------------------------------------------
 struct DecodeShape {

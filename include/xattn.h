@@ -183,10 +183,11 @@ typedef struct {
 
 /* Attention forward with the Q side of the prologue fused ([T9] Decision 1, [MINT] 5.4.1,
  * 5.4.4, 5.5.1 and 5.3.1): the same results as xattn_qknorm_rope_fwd(pro->xq) into
- * pro->yq / pro->rstd_q followed by xattn_fwd(pro->yq, k, v).  For bf16 io at hd 64 / 128
- * it is one pass: the attention reads the raw Q rows it keeps resident and normalises and
- * rotates them itself (yq and rstd_q are still written, as xattn_bwd needs them);
- * otherwise the two calls run in sequence.  k must already be normalised and rotated
+ * pro->yq / pro->rstd_q followed by xattn_fwd(pro->yq, k, v).  For bf16 io it is one pass:
+ * the attention reads the raw Q rows it keeps resident and normalises and rotates them
+ * itself (yq and rstd_q are still written, as xattn_bwd needs them; at hd 16 / 32 bitwise
+ * the rows xattn_qknorm_rope_fwd gives, at hd 64 / 128 within one rounding of them, the
+ * mean square being summed in another order); for fp32 the two calls run in sequence.  k must already be normalised and rotated
  * (xattn_qknorm_rope_fwd): every query tile reads every K tile before it, so K is
  * prepared once.  out, lse as in xattn_fwd. */
 xattn_status xattn_fwd_qnorm(const xattn_dims* dims, const xattn_fwd_prologue* pro,
@@ -209,8 +210,10 @@ size_t xattn_bwd_workspace_bytes(const xattn_dims* dims, int with_prologue);
  * pro != NULL: the prologue backward runs too; dq, dk are then gradients w.r.t. the raw
  * pro->xq, pro->xk and pro->dgamma_q / dgamma_k are written (the arithmetic of
  * xattn_qknorm_rope_bwd; dgamma summed in a fixed order, bitwise reproducible).  For bf16
- * io at hd 64 / 128 it is applied inside the dq and dk stores (the gradients w.r.t. the
- * rotated q, k never reach memory); otherwise as a separate pass over fp32 gradients.
+ * io it is applied inside the dq and dk stores (the gradients w.r.t. the rotated q, k never
+ * reach memory), except at hd 16 / 32 for shapes so small that the dk/dv pass spreads a
+ * group's query heads over several workgroups; there, and for fp32, it is a separate pass
+ * over fp32 gradients.
  * q, out, dout, dq: [B*H, S, hd]; k, v, dk, dv: [B*Hkv, S, hd]; lse: [B*H*S] fp32 from
  * xattn_fwd.  workspace: device memory of at least xattn_bwd_workspace_bytes bytes. */
 xattn_status xattn_bwd(const xattn_dims* dims, const void* q, const void* k, const void* v,

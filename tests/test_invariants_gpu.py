@@ -76,8 +76,9 @@ def test_causal_no_peeking_bitwise(dtype, hd):
 
 # (workload, replaced fields): workloads 3 and 4 at full size run the shared-tile dk/dv
 # kernel, workload 4 at batch 4 the private one, workload 5 the pipelined one, workload 2
-# the generic fp32 kernels.
-DETERMINISM = [(2, {}), (3, {}), (4, {}), (4, dict(batch=4)), (5, {})]
+# the generic fp32 kernels, workload 6 the generic bf16 kernels with the prologue backward
+# in their dq / dk stores.
+DETERMINISM = [(2, {}), (3, {}), (4, {}), (4, dict(batch=4)), (5, {}), (6, {})]
 
 
 @pytest.mark.parametrize("idx,kw", DETERMINISM,
@@ -200,17 +201,30 @@ def test_fused_prologue_backward_equals_separate_calls_f32():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("wi,dtype", [(5, "bf16"), (4, "bf16"), (2, "f32")])
-def test_forward_with_fused_q_prologue_matches_separate_calls(wi, dtype):
+# (workload, whether yq / rstd_q must equal the standalone prologue's bit for bit): the
+# hd 64 / 128 bf16 forward sums the mean square in another order; fp32 runs the two calls
+# in sequence; the generic bf16 forward (hd 16 / 32, key-split and unsplit kernels) repeats
+# the standalone kernel's operations in its order.
+QNORM_CASES = [
+    (W.WORKLOADS[5].replace(seq_len=1000), False),
+    (W.WORKLOADS[4].replace(batch=2, seq_len=300), False),
+    (W.WORKLOADS[2], True),
+    (W.WORKLOADS[6], True),
+    (W.small_ragged("bf16", 16, 77, 2, 4, 2, index=305), True),
+    (W.small_ragged("bf16", 16, 260, 8, 16, 4, index=306), True),
+    (W.small_ragged("bf16", 32, 100, 1, 3, 1, index=307), True),
+]
+
+
+@pytest.mark.parametrize("w,bitwise", QNORM_CASES,
+                         ids=[f"{w.dtype}_hd{w.head_dim}_S{w.seq_len}_B{w.batch}"
+                              for w, _ in QNORM_CASES])
+def test_forward_with_fused_q_prologue_matches_separate_calls(w, bitwise):
     """xattn_fwd_qnorm: out and lse are bitwise those of xattn_fwd on the yq it wrote, and
-    yq / rstd_q match xattn_qknorm_rope_fwd (bitwise for fp32, where the two calls run in
-    sequence; for bf16 the in-kernel mean square sums in another order, so rstd may differ
-    in the last bits and yq by one rounding)."""
-    w = W.WORKLOADS[wi]
-    if wi == 5:
-        w = w.replace(seq_len=1000)
-    if wi == 4:
-        w = w.replace(batch=2, seq_len=300)
+    yq / rstd_q match xattn_qknorm_rope_fwd: bit for bit where the same operations run in
+    the same order, else (bf16 at hd 64 / 128, whose in-kernel mean square sums in another
+    order) rstd within a few ulp and yq within one rounding."""
+    dtype = w.dtype
     x = W.make_inputs(w)
     note(f"fused Q prologue forward {w}")
     cos, sin = X.rope_cache(w.seq_len, w.head_dim, w.theta)
@@ -223,7 +237,7 @@ def test_forward_with_fused_q_prologue_matches_separate_calls(wi, dtype):
     yq2, rq2 = X.qknorm_rope_fwd(txq, gq, cos, sin, w.eps)
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
-    if dtype == "f32":
+    if bitwise:
         assert torch.equal(yq, yq2) and torch.equal(rq, rq2)
     else:
         np.testing.assert_allclose(host(rq), host(rq2), rtol=2e-6, atol=0)

@@ -44,6 +44,10 @@ SMALL = [
     # the generic dk/dv with the group's query heads split over workgroups (few key blocks):
     # group 5 over two splits, heads {0, 1} and {2, 3, 4}
     R("f32", 32, 1000, 2, 10, 2, index=218),
+    # bf16 head_dim 16 / 32 apply the prologue backward in the dq / dk stores unless the
+    # group is split as above: here with the dk/dv query walk split two ways (32 keys of 64
+    # per wave); 207 and 217 cover the eight- and four-way splits, workload 6 the unsplit one
+    R("bf16", 32, 520, 8, 32, 16, index=219),
 ]
 SMALL_IDS = [w.name if w.index < 100 else f"{w.dtype}_hd{w.head_dim}_S{w.seq_len}_"
              f"B{w.batch}_H{w.num_heads}_kv{w.num_kv_heads}" for w in SMALL]

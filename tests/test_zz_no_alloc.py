@@ -50,14 +50,17 @@ def _run(step, with_prologue, noalloc):
 
 
 # (larger, smaller) pairs: bf16 with the prologue fused into the gradient stores (hd 64,
-# then hd 128), and the fp32 kernels with the separate prologue backward.
+# then hd 128; the generic kernels at hd 32, then hd 16), and the fp32 kernels with the
+# separate prologue backward.
 PAIRS = [
     (W.WORKLOADS[4].replace(batch=8, index=601), W.WORKLOADS[5].replace(seq_len=300, index=602)),
+    (W.WORKLOADS[6].replace(batch=4, index=605), W.small_ragged("bf16", 16, 260, 8, 16, 4, index=606)),
     (W.WORKLOADS[2].replace(index=603), W.small_ragged("f32", 32, 77, 2, 6, 2, index=604)),
 ]
 
 
-@pytest.mark.parametrize("big,small", PAIRS, ids=["bf16_fused_prologue", "f32"])
+@pytest.mark.parametrize("big,small", PAIRS, ids=["bf16_fused_prologue", "bf16_generic_fused",
+                                                  "f32"])
 @pytest.mark.parametrize("with_prologue", [True, False], ids=["prologue", "attention_only"])
 def test_noalloc_backward_matches_workspace_backward(big, small, with_prologue):
     (xb, sb), (xs, ss) = _forward(big), _forward(small)
