@@ -154,17 +154,18 @@ def kernel_units(w, docs=None):
     hd = w.head_dim
     io = 2 if w.dtype == "bf16" else 4
     rows_q, rows_k = w.bh * w.seq_len, w.bkv * w.seq_len
-    fused_q = w.dtype == "bf16" and hd in (64, 128)
+    fused_q = w.dtype == "bf16"
     return {
         "attn_fwd": ("mfma", 4 * hd * pairs, "QK^T and PV: 4*hd per causal pair"),
         "attn_bwd_dkdv": ("mfma", 6 * hd * pairs, "dP, dV, dK: 6*hd per causal pair"),
         "attn_bwd_dq": ("mfma", 2 * hd * pairs, "dQ: 2*hd per causal pair"),
-        # prologue forward: K alone when the Q side runs inside attn_fwd (bf16, hd 64/128),
-        # else the per-launch average over the Q launch and the K launch
+        # prologue forward: K alone when the Q side runs inside attn_fwd (bf16), else the
+        # per-launch average over the Q launch and the K launch
         "qknorm_rope_fwd": ("hbm", (rows_k if fused_q else (rows_q + rows_k) / 2)
                             * (hd * 2 * io + 4), "read x, write y (io dtype), write rstd"),
-        # standalone prologue backward (fp32 io; bf16 io fuses it into attn_bwd_dq / dkdv):
-        # one launch for Q and K together
+        # standalone prologue backward (fp32 io, and bf16 shapes whose dk/dv launch splits
+        # the group's query heads; bf16 io otherwise fuses it into attn_bwd_dq / dkdv): one
+        # launch for Q and K together
         "qknorm_rope_bwd": ("hbm", (rows_q + rows_k) * (hd * (4 + 2 * io) + 4),
                             "read fp32 dy, read x, write dx (io dtype), read rstd"),
     }
