@@ -154,15 +154,13 @@ def kernel_units(w, docs=None):
     hd = w.head_dim
     io = 2 if w.dtype == "bf16" else 4
     rows_q, rows_k = w.bh * w.seq_len, w.bkv * w.seq_len
-    fused_q = w.dtype == "bf16"
     return {
         "attn_fwd": ("mfma", 4 * hd * pairs, "QK^T and PV: 4*hd per causal pair"),
         "attn_bwd_dkdv": ("mfma", 6 * hd * pairs, "dP, dV, dK: 6*hd per causal pair"),
         "attn_bwd_dq": ("mfma", 2 * hd * pairs, "dQ: 2*hd per causal pair"),
-        # prologue forward: K alone when the Q side runs inside attn_fwd (bf16), else the
-        # per-launch average over the Q launch and the K launch
-        "qknorm_rope_fwd": ("hbm", (rows_k if fused_q else (rows_q + rows_k) / 2)
-                            * (hd * 2 * io + 4), "read x, write y (io dtype), write rstd"),
+        # prologue forward: K alone (the Q side runs inside attn_fwd)
+        "qknorm_rope_fwd": ("hbm", rows_k * (hd * 2 * io + 4),
+                            "read x, write y (io dtype), write rstd"),
         # standalone prologue backward (fp32 io, and bf16 shapes whose dk/dv launch splits
         # the group's query heads; bf16 io otherwise fuses it into attn_bwd_dq / dkdv): one
         # launch for Q and K together

@@ -261,6 +261,70 @@ __device__ __forceinline__ void q_prologue_frag(bf16x8 (&qf)[HD / 16], const QPr
   if (store && valid && h == 0) pro.rstd_q[row] = r;
 }
 
+// The same for fp32 io at any head_dim (Mint documentation 5.4.1 and 5.5.1).  The fragment
+// holds columns 8 c + 4 h + j of chunk c: lane half h owns the standalone kernel's 4-column
+// parts p = 2 c + h of the first half (chunks c < HD / 16) with their second-half partners
+// (chunk c + HD / 16).  The standalone kernel sums each part's squares in its lane, then
+// adds the parts by a butterfly over its HD / 8 row lanes (pairs (2c, 2c + 1) first, then
+// pairs of pairs, ...); here each part pair is one cross-half exchange and the upper levels
+// are added in the same tree, so the rows and rstd are bitwise those of
+// xattn_qknorm_rope_fwd.  Rows t >= S give a zero fragment and store nothing.
+template <int HD>
+__device__ __forceinline__ void q_prologue_frag(f32x4 (&qf)[HD / 8], const QProFuse& pro,
+                                                size_t head_row0, int t, int S, bool store,
+                                                int lane) {
+#pragma clang fp contract(off)
+  constexpr int HALF = HD / 2, NP = HD / 16;  // first-half parts per lane
+  const int h = lane >> 5;
+  const bool valid = t < S;
+  const int tc = valid ? t : S - 1;
+  const size_t row = head_row0 + tc;
+  const float* xr = static_cast<const float*>(pro.xq) + row * HD + 4 * h;
+  f32x4 a[NP], b[NP], g1[NP], g2[NP], cs[NP], sn[NP];
+#pragma unroll
+  for (int c = 0; c < NP; ++c) {
+    const int f = 8 * c + 4 * h;  // the part's first column
+    a[c] = *reinterpret_cast<const f32x4*>(xr + 8 * c);
+    b[c] = *reinterpret_cast<const f32x4*>(xr + HALF + 8 * c);
+    g1[c] = *reinterpret_cast<const f32x4*>(pro.gamma_q + f);
+    g2[c] = *reinterpret_cast<const f32x4*>(pro.gamma_q + HALF + f);
+    cs[c] = *reinterpret_cast<const f32x4*>(pro.cos_tab + (size_t)tc * HALF + f);
+    sn[c] = *reinterpret_cast<const f32x4*>(pro.sin_tab + (size_t)tc * HALF + f);
+  }
+  float tr[NP];
+#pragma unroll
+  for (int c = 0; c < NP; ++c) {
+    float sp = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sp += a[c][e] * a[c][e] + b[c][e] * b[c][e];
+    tr[c] = sp + xor_lanes<32>(sp);  // parts 2c and 2c + 1
+  }
+#pragma unroll
+  for (int n = NP; n > 1; n /= 2)
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) tr[i] = tr[2 * i] + tr[2 * i + 1];
+  const float r = 1.0f / sqrtf(tr[0] * (1.0f / (float)HD) + pro.eps);
+  float* yr = static_cast<float*>(pro.yq) + row * HD + 4 * h;
+#pragma unroll
+  for (int c = 0; c < NP; ++c) {
+    f32x4 y1, y2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float n1 = a[c][e] * r * g1[c][e];
+      const float n2 = b[c][e] * r * g2[c][e];
+      y1[e] = valid ? n1 * cs[c][e] - n2 * sn[c][e] : 0.f;
+      y2[e] = valid ? n1 * sn[c][e] + n2 * cs[c][e] : 0.f;
+    }
+    qf[c] = y1;
+    qf[c + NP] = y2;
+    if (store && valid) {
+      *reinterpret_cast<f32x4*>(yr + 8 * c) = y1;
+      *reinterpret_cast<f32x4*>(yr + HALF + 8 * c) = y2;
+    }
+  }
+  if (store && valid && h == 0) pro.rstd_q[row] = r;
+}
+
 // Prologue backward applied in the dq / dk stores of the kernels below (bf16 io, head_dim 16
 // or 32; the arithmetic of the standalone prologue backward, Mint documentation 5.4.4 and
 // 5.5.2), so the gradient w.r.t. the rotated rows never goes to HBM.  The lane's `mul` *
@@ -1058,10 +1122,15 @@ hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const v
   // bf16 at head_dim 64 / 128 always runs the attn_bf16.hip kernels
   if (io == IO_BF16 && fast_bf16_supported(s.head_dim))
     return launch_attn_fwd_bf16_fast(s, q, k, v, out, lse, pro, stream);
-  if (pro != nullptr) {  // bf16, head_dim 16 / 32 only
-    if (io != IO_BF16) return hipErrorInvalidValue;
-    if (s.head_dim == 16) return fwd_impl<bf16, 16, true>(s, nullptr, k, v, out, lse, *pro, stream);
-    if (s.head_dim == 32) return fwd_impl<bf16, 32, true>(s, nullptr, k, v, out, lse, *pro, stream);
+  if (pro != nullptr) {  // the Q side of the prologue inside the forward
+#define XATTN_CASE(T, HD) \
+    if (s.head_dim == HD) return fwd_impl<T, HD, true>(s, nullptr, k, v, out, lse, *pro, stream);
+    if (io == IO_F32) {
+      XATTN_CASE(float, 16) XATTN_CASE(float, 32) XATTN_CASE(float, 64) XATTN_CASE(float, 128)
+    } else {
+      XATTN_CASE(bf16, 16) XATTN_CASE(bf16, 32)
+    }
+#undef XATTN_CASE
     return hipErrorInvalidValue;
   }
   const QProFuse none{};

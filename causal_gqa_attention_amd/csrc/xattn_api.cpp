@@ -641,20 +641,11 @@ xattn_status xattn_fwd_qnorm(const xattn_dims* dims, const xattn_fwd_prologue* p
                      {{pro->xq, qb, "pro->xq"}, {pro->gamma_q, hdb, "pro->gamma_q"},
                       {pro->cos_tab, tb, "pro->cos_tab"}, {pro->sin_tab, tb, "pro->sin_tab"},
                       {k, kb, "k"}, {v, kb, "v"}, seg_lo_range(c), seg_hi_range(c)});
-    const hipStream_t st = (hipStream_t)stream;
-    if (c.io == xattn::IO_BF16) {  // every bf16 head_dim: one pass
-      xattn::QProFuse pf;
-      pf.xq = pro->xq, pf.gamma_q = pro->gamma_q, pf.cos_tab = pro->cos_tab;
-      pf.sin_tab = pro->sin_tab, pf.yq = pro->yq, pf.rstd_q = pro->rstd_q, pf.eps = pro->eps;
-      hip_check(xattn::launch_attn_fwd(c.io, c.s, nullptr, k, v, out, lse, &pf, st),
-                "attention forward launch");
-      return;
-    }
-    hip_check(xattn::launch_qknorm_rope_fwd(c.io, c.s.head_dim, pro->xq, pro->gamma_q,
-                                            pro->cos_tab, pro->sin_tab, pro->yq, pro->rstd_q,
-                                            (int)c.rows_q, c.s.seq_len, pro->eps, st),
-              "prologue forward launch");
-    hip_check(xattn::launch_attn_fwd(c.io, c.s, pro->yq, k, v, out, lse, nullptr, st),
+    xattn::QProFuse pf;  // one pass: the forward normalises and rotates its own Q rows
+    pf.xq = pro->xq, pf.gamma_q = pro->gamma_q, pf.cos_tab = pro->cos_tab;
+    pf.sin_tab = pro->sin_tab, pf.yq = pro->yq, pf.rstd_q = pro->rstd_q, pf.eps = pro->eps;
+    hip_check(xattn::launch_attn_fwd(c.io, c.s, nullptr, k, v, out, lse, &pf,
+                                     (hipStream_t)stream),
               "attention forward launch");
   });
 }

@@ -89,8 +89,8 @@ struct QProFuse {
 hipError_t launch_attn_fwd_bf16_fast(const AttnShape& s, const void* q, const void* k,
                                      const void* v, void* out, float* lse,
                                      const QProFuse* pro, hipStream_t stream);
-// Any io / head_dim.  `pro` (bf16 only; q unused) as for launch_attn_fwd_bf16_fast: the Q
-// side of the prologue runs inside the forward, at head_dim 16 / 32 too.
+// Any io / head_dim.  `pro` (q unused) as for launch_attn_fwd_bf16_fast: the Q side of the
+// prologue runs inside the forward, for every io dtype and head_dim.
 hipError_t launch_attn_fwd(IoType io, const AttnShape& s, const void* q, const void* k,
                            const void* v, void* out, float* lse, const QProFuse* pro,
                            hipStream_t stream);

@@ -183,11 +183,11 @@ typedef struct {
 
 /* Attention forward with the Q side of the prologue fused ([T9] Decision 1, [MINT] 5.4.1,
  * 5.4.4, 5.5.1 and 5.3.1): the same results as xattn_qknorm_rope_fwd(pro->xq) into
- * pro->yq / pro->rstd_q followed by xattn_fwd(pro->yq, k, v).  For bf16 io it is one pass:
- * the attention reads the raw Q rows it keeps resident and normalises and rotates them
- * itself (yq and rstd_q are still written, as xattn_bwd needs them; at hd 16 / 32 bitwise
- * the rows xattn_qknorm_rope_fwd gives, at hd 64 / 128 within one rounding of them, the
- * mean square being summed in another order); for fp32 the two calls run in sequence.  k must already be normalised and rotated
+ * pro->yq / pro->rstd_q followed by xattn_fwd(pro->yq, k, v), in one pass: the attention
+ * reads the raw Q rows it keeps resident and normalises and rotates them itself (yq and
+ * rstd_q are still written, as xattn_bwd needs them; bitwise the rows xattn_qknorm_rope_fwd
+ * gives, except bf16 at hd 64 / 128: within one rounding of them, the mean square being
+ * summed in another order).  k must already be normalised and rotated
  * (xattn_qknorm_rope_fwd): every query tile reads every K tile before it, so K is
  * prepared once.  out, lse as in xattn_fwd. */
 xattn_status xattn_fwd_qnorm(const xattn_dims* dims, const xattn_fwd_prologue* pro,

@@ -202,9 +202,9 @@ def test_fused_prologue_backward_equals_separate_calls_f32():
 
 
 # (workload, whether yq / rstd_q must equal the standalone prologue's bit for bit): the
-# hd 64 / 128 bf16 forward sums the mean square in another order; fp32 runs the two calls
-# in sequence; the generic bf16 forward (hd 16 / 32, key-split and unsplit kernels) repeats
-# the standalone kernel's operations in its order.
+# hd 64 / 128 bf16 forward sums the mean square in another order; the generic forward (bf16
+# hd 16 / 32, fp32 every hd; key-split and unsplit kernels) repeats the standalone kernel's
+# operations in its order.
 QNORM_CASES = [
     (W.WORKLOADS[5].replace(seq_len=1000), False),
     (W.WORKLOADS[4].replace(batch=2, seq_len=300), False),
@@ -213,6 +213,10 @@ QNORM_CASES = [
     (W.small_ragged("bf16", 16, 77, 2, 4, 2, index=305), True),
     (W.small_ragged("bf16", 16, 260, 8, 16, 4, index=306), True),
     (W.small_ragged("bf16", 32, 100, 1, 3, 1, index=307), True),
+    (W.small_ragged("f32", 16, 77, 2, 4, 2, index=308), True),
+    (W.small_ragged("f32", 32, 300, 4, 24, 6, index=309), True),
+    (W.small_ragged("f32", 64, 300, 4, 24, 6, index=310), True),
+    (W.small_ragged("f32", 128, 100, 1, 4, 2, theta=1e6, eps=1e-6, index=311), True),
 ]
 
 
