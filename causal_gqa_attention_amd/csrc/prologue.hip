@@ -329,8 +329,9 @@ static hipError_t fwd_table_dispatch(const void* x, const float* gamma, const in
   constexpr int HALF = HD / 2;
   constexpr int NG = 256 / (HALF / V16<T>::n);  // rows per block
   // positions per block: as many as leave one row group per head row (at most one table
-  // entry per thread); head rows per block: the rest of the block
-  const int P = std::max(1, std::min(256 / HALF, NG / heads));
+  // entry per thread), and at head_dim <= 32 (rows of 64 bytes or less) at least enough
+  // for 8 heads' rows to form contiguous runs; head rows per block: the rest of the block
+  const int P = std::max(1, std::min(256 / HALF, NG / (HD <= 32 ? std::min(heads, 8) : heads)));
   const int HB = std::max(1, NG / P);
   const dim3 grid((seq_len + P - 1) / P, (heads + HB - 1) / HB);
   ProfScope prof("qknorm_rope_fwd", stream);

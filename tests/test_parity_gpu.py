@@ -48,6 +48,8 @@ SMALL = [
     # group is split as above: here with the dk/dv query walk split two ways (32 keys of 64
     # per wave); 207 and 217 cover the eight- and four-way splits, workload 6 the unsplit one
     R("bf16", 32, 520, 8, 32, 16, index=219),
+    # a single token through both fused prologue halves of the generic bf16 kernels
+    R("bf16", 16, 1, 3, 2, 2, index=220),
 ]
 SMALL_IDS = [w.name if w.index < 100 else f"{w.dtype}_hd{w.head_dim}_S{w.seq_len}_"
              f"B{w.batch}_H{w.num_heads}_kv{w.num_kv_heads}" for w in SMALL]
