@@ -27,8 +27,11 @@ CASES = [
     (R("f32", 64, 150, 2, 4, 2, index=505), [10, 70, 1, 69]),
     (R("f32", 16, 40, 1, 2, 1, index=506), [1] * 40),
     (R("bf16", 32, 77, 1, 4, 2, index=507), [30, 47]),
-    # bf16 head_dim 32 with the prologue backward in the dq / dk stores (MHA: no group split)
+    # bf16 head_dim 16 / 32 with the prologue backward in the dq / dk stores (no group
+    # split): MHA, and GQA group 2 on the unsplit dq kernel
     (R("bf16", 32, 150, 2, 4, 4, index=513), [1, 60, 89]),
+    (R("bf16", 16, 90, 2, 4, 4, index=514), [45, 2, 43]),
+    (R("bf16", 32, 300, 12, 8, 4, index=515), [128, 100, 72]),
 ]
 IDS = [f"{w.dtype}_hd{w.head_dim}_S{w.seq_len}_B{w.batch}_docs{len(d)}" for w, d in CASES]
 
