@@ -42,9 +42,10 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X published dense MFMA pea
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "causal_gqa_attention_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
-# sources whose text decides the attention kernels' code: counter summaries taken on other
-# text are stale and not reported
-KERNEL_SOURCES = ["attn.hip", "attn_bf16.hip", "prologue.hip", "lds_copy.h", "xattn_device.h"]
+# sources whose text decides the attention kernels' code (the build script holds their
+# compile flags): counter summaries taken on other text are stale and not reported
+KERNEL_SOURCES = ["attn.hip", "attn_bf16.hip", "prologue.hip", "lds_copy.h", "xattn_device.h",
+                  os.path.join("..", "build.py")]
 # counters of one rocprofv3 --pmc pass (8 SQ counters and one GRBM counter fit one pass)
 SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA",
                "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_VALU",

@@ -20,9 +20,10 @@ LIB = os.path.join(PKG, "libxattn.so")
 SOURCES = ["attn.hip", "attn_bf16.hip", "prologue.hip", "decode.hip", "proj.hip", "gemm.hip",
            "xattn_api.cpp", "profile.cpp", "noalloc.hip"]
 LINK_LIBS: list = []
-# Per-source extra flags.  attn_bf16.hip, decode.hip: MFMA results go to VGPRs (the score
-# tiles are consumed by VALU right away; AGPR results would need a copy per element).
+# Per-source extra flags.  The attention and decode kernels: MFMA results go to VGPRs (the
+# score tiles are consumed by VALU right away; AGPR results would need a copy per element).
 SOURCE_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                 "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
